@@ -1,0 +1,48 @@
+"""CPU oracle for the weight-only quantized decode linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(the HIP library and its Python binding) never imports or calls it, and it
+imports nothing from the product: the two share only the seeded input
+generators in ``wqd_inputs``.
+
+It computes, plainly and slowly, what the decode linear layer computes:
+
+* ``formats``: bfloat16 / float16 / FP8-E4M3 rounding and decoding, in float64;
+* ``quant``:   the three weight formats (bf16, FP8-E4M3 + per-row fp32 scale,
+  W4A16 = uint4 codes in groups of 128 with an fp16 scale and a uint4 zero
+  point) and their exact dequantisation;
+* ``gemm``:    y = x . dequant(W)^T in float64, rounded once to bf16.
+
+Pins (tests marked ``not gpu``): exhaustive E4M3 decode against its closed
+form and against the printed maximum 448; a brute-force nearest-value encoder;
+bf16/fp16 rounding against torch's and numpy's conversions and hand-built
+boundary cases; W4A16 codes against a brute-force argmin over the 16 grid
+points; the products against exact rational arithmetic on tiny shapes and
+against special cases (integer matmul, identity, zero).  No function here is
+"parity unpinned".
+"""
+from .formats import (  # noqa: F401
+    BF16_MAX,
+    E4M3_MAX,
+    bf16_bits_from_value,
+    bf16_bits_to_f64,
+    bf16_round,
+    bf16_to_bits,
+    e4m3_decode,
+    e4m3_encode,
+    fp16_round_f32,
+)
+from .gemm import qgemm_exact, qgemm_ref  # noqa: F401
+from .quant import (  # noqa: F401
+    FMTS,
+    GROUP,
+    dequant_exact,
+    dequant_f32,
+    fp8_row_scales,
+    quantize,
+    quantize_bf16,
+    quantize_fp8,
+    quantize_w4a16,
+    w4a16_group_params,
+)

@@ -1,0 +1,35 @@
+"""Reference product y = x . dequant(W)^T for the decode linear layer.
+
+Test infrastructure only (see ``oracle/__init__.py``).
+
+The method reaches exactly (up to the order of accumulation) a plain dense
+matmul with dequantised weights: a weight-only kernel multiplies the quantised
+matrix by a full-precision activation vector, dequantising on the fly, and the
+activations are never quantised ("Making each token cheaper", section "What
+quantization saves": the GPTQ decode kernel; CS336 lecture 10 notes, section
+5.2: "simulated quantisation" is quantise, dequantise, then a dense matmul).
+So the oracle is that definition: x (bf16 values) times the exact dequantised
+weights, in float64, then one rounding to bf16.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import bf16_bits_to_f64, bf16_to_bits
+from .quant import dequant_exact
+
+
+def qgemm_exact(x_bits, qw: dict) -> np.ndarray:
+    """y64[M, N] = x[M, K] . Wd[N, K]^T in float64 (x given as bf16 bit patterns)."""
+    x = bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16))
+    Wd = dequant_exact(qw)
+    if x.shape[1] != Wd.shape[1]:
+        raise ValueError("K mismatch")
+    return x @ Wd.T
+
+
+def qgemm_ref(x_bits, qw: dict) -> dict:
+    """Reference output: the float64 product and its bf16 rounding (bit patterns)."""
+    y64 = qgemm_exact(x_bits, qw)
+    return {"y64": y64, "y_bits": bf16_to_bits(y64)}
+
