@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark: weight-stream GB/s and microseconds per layer-stack step.
+
+Default workload: the 70B-class decode stack (80 layers x q, k, v, o, gate, up,
+down; hidden 8192, GQA 8 KV heads of 128, FFN 28672) with W4A16-g128 weights,
+M = 1 activation row.  One step = the 560 y = x . dequant(W)^T calls of the
+stack, replayed from one HIP graph; weights (~35.6 GB packed) are resident in
+HBM before timing starts and the stack is far larger than the 256 MB
+last-level cache, so every step streams the weights from HBM.
+
+Prints ONE JSON line.  Other workloads: --workload fp8_70b | bf16_7b |
+gemv4096 | verify:<fmt>:<mat>, with --m for the activation rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor peak
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="w4a16_70b")
+    ap.add_argument("--m", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    return ap.parse_args()
+
+
+def make_workload(args):
+    from weight_only_quantized_decode_amd import workloads as WL
+
+    w = args.workload
+    if w == "w4a16_70b":
+        return WL.stack_70b("w4a16", args.m, args.layers or 80)
+    if w == "fp8_70b":
+        return WL.stack_70b("fp8", args.m, args.layers or 80)
+    if w == "bf16_7b":
+        return WL.stack_7b_bf16(args.m, args.layers or 32)
+    if w == "gemv4096":
+        return WL.gemv_4096_w4a16()
+    if w.startswith("verify:"):
+        _, fmt, mat = w.split(":")
+        return WL.verify_matrix(fmt, mat, args.m)
+    raise SystemExit(f"unknown workload {w!r}")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def build_stack(wl):
+    """Pack every weight matrix of the workload on the device (untimed setup)."""
+    import torch
+
+    import weight_only_quantized_decode_amd as wqd
+    import wqd_inputs as I
+
+    dev = torch.device("cuda", 0)
+    packed = []
+    t0 = time.time()
+    for layer in range(wl.layers):
+        row = []
+        for mi, (name, N, K) in enumerate(wl.mats):
+            W = I.w_device(I.stack_seed(wl.cfg, layer, mi), N, K, device=dev)
+            row.append(wqd.pack_weights(wl.fmt, W))
+            del W
+        packed.append(row)
+        if layer % 10 == 0:
+            torch.cuda.synchronize()
+            log(f"[bench] packed layer {layer}/{wl.layers} ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    xs, ys = {}, {}
+    for name, N, K in wl.mats:
+        if K not in xs:
+            xb = I.x_bf16(I.x_seed(wl.cfg, wl.M, K), wl.M, K, outliers=wl.outliers)
+            xs[K] = xb.to(dev)
+        if N not in ys:
+            ys[N] = torch.empty((wl.M, N), dtype=torch.bfloat16, device=dev)
+    need = max(wqd.workspace_bytes(wl.fmt, wl.M, N, K) for _, N, K in wl.mats)
+    ws = wqd.get_workspace(need, dev)
+    return packed, xs, ys, ws
+
+
+def hbm_ceiling(gib=4, reps=10):
+    """Measured HBM read and copy bandwidth (GB/s) with the library's stream kernels."""
+    import torch
+
+    import weight_only_quantized_decode_amd as wqd
+
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    dst = torch.empty(n // 2, dtype=torch.uint8, device="cuda")
+    sink = wqd.stream_read(buf)
+    wqd.stream_copy(dst, buf[: n // 2])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        wqd.stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    read = n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    e0.record()
+    for _ in range(reps):
+        wqd.stream_copy(dst, buf[: n // 2])
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2 * (n // 2) * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del buf, dst
+    torch.cuda.empty_cache()
+    return read, copy
+
+
+def cpu_baseline(wl):
+    """The oracle (as it stands) on a bounded sample of the same workload, on the host cores."""
+    import numpy as np
+
+    import oracle
+    import wqd_inputs as I
+    from weight_only_quantized_decode_amd import workloads as WL
+
+    name, N, K = max(wl.mats, key=lambda m: m[1] * m[2]) if wl.layers == 1 else wl.mats[0]
+    W = I.w_host(I.stack_seed(wl.cfg, 0, 0), N, K)
+    qw = oracle.quantize(wl.fmt, W)
+    x = I.x_bf16_bits(I.x_seed(wl.cfg, wl.M, K), wl.M, K, outliers=wl.outliers)
+    reps, t_total = 0, 0.0
+    while t_total < 10.0 and reps < 50:
+        t0 = time.perf_counter()
+        oracle.qgemm_exact(x, qw)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per_call = t_total / reps
+    gbps = WL.call_bytes(wl.fmt, wl.M, N, K) / per_call / 1e9
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    return {
+        "value": round(gbps, 3),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{reps} calls of the float64 oracle (exact dequant + matmul + bf16 rounding) on one "
+                  f"{name} matrix {N}x{K} {wl.fmt}, M={wl.M}; {per_call * 1e3:.1f} ms per call; "
+                  f"host {platform.processor() or platform.machine()}, {os.cpu_count()} logical CPUs",
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this decode layer is measured on a single MI355X "
+              "(multi-GPU sharding is a design note, not part of this build).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import weight_only_quantized_decode_amd as wqd
+    from weight_only_quantized_decode_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    wqd.lib()
+    wl = make_workload(args)
+    log(f"[bench] workload {wl.name}: {wl.launches} launches/step, {wl.step_bytes() / 1e9:.3f} GB/step")
+    ceiling = (None, None) if args.no_ceiling else hbm_ceiling()
+    if ceiling[0]:
+        log(f"[bench] HBM ceiling: read {ceiling[0]:.0f} GB/s, copy {ceiling[1]:.0f} GB/s")
+    packed, xs, ys, ws = build_stack(wl)
+
+    stream = torch.cuda.Stream()
+
+    def step():
+        for layer in range(wl.layers):
+            for (name, N, K), pw in zip(wl.mats, packed[layer]):
+                wqd.qgemm(xs[K], pw, y=ys[N], workspace=ws)
+
+    with torch.cuda.stream(stream):
+        step()  # eager warm-up (also loads the kernels)
+        torch.cuda.synchronize()
+        graph = None
+        if not args.no_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                step()
+        run = graph.replay if graph is not None else step
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    step_bytes = wl.step_bytes()
+    gbps = step_bytes / (ms / 1e3) / 1e9
+    per_launch_bytes = step_bytes / wl.launches
+    avg_launch_us = ms * 1e3 / wl.launches
+    achieved = per_launch_bytes / (avg_launch_us / 1e6) / 1e9
+    out = {
+        "metric": "weight-stream GB/s (% of HBM peak) & us per layer-stack step, 70B W4A16/FP8/BF16",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "us_per_step": round(ms * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"w4a16": "u4+bf16", "fp8": "e4m3+bf16", "bf16": "bf16"}[wl.fmt],
+        "data": "synthetic",
+        "config": {"workload": wl.name, "fmt": wl.fmt, "M": wl.M, "layers": wl.layers,
+                   "launches_per_step": wl.launches, "graph": graph is not None,
+                   "algorithmic_bytes_per_step": step_bytes},
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "hbm_read_ceiling_GBps": None if ceiling[0] is None else round(ceiling[0], 1),
+        "hbm_copy_ceiling_GBps": None if ceiling[1] is None else round(ceiling[1], 1),
+        "pct_measured_read_ceiling": None if ceiling[0] is None else round(100 * gbps / ceiling[0], 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": f"gemv_kernel<{wl.fmt}, M={min(wl.M, 8)}>",
+                     "avg_launch_us": round(avg_launch_us, 3)},
+    }
+    if wl.M >= 16:
+        tflops = wl.step_flops() / (ms / 1e3) / 1e12
+        out["mfma_util_pct"] = round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * wqd.h - C ABI of the weight-only quantized decode linear layer for MI355X (gfx950).
+ *
+ * The layer is y[M, N] = x[M, K] . W[N, K]^T for the few activation rows of a
+ * decode step (M = batch x verify width), with W streamed from HBM in one of
+ * three storage formats and dequantised in registers on the fly; activations
+ * stay bfloat16 and are never quantised.  Sources for the operation:
+ *   - "降低每個 Token 的生成成本" (Making each token cheaper), section
+ *     "量化省下什麼" (What quantization saves): a weight-only decode kernel
+ *     multiplies the quantised matrix by a full-precision vector, dequantising
+ *     the weights on the fly, without quantising activations;
+ *   - same page, "權重量化 / 格式" (Weight quantization / Formats): values are
+ *     stored in fewer bits with a scale that maps them back; FP8-E4M3 (largest
+ *     normal 448); weight-only INT4 with one scale per group of 128 along K,
+ *     dequantised to 16 bits before the multiply-accumulate;
+ *   - same page, "完整範例" (Worked example: weight bytes per format): one
+ *     32-bit scale per row for FP8;
+ *   - CS336 lecture 10 notes, section 5.2 "量化": a scale and a zero point per
+ *     group; real speed needs kernels that read the low-bit weights directly.
+ *
+ * Conventions common to every entry point
+ *   - Tensor pointers marked "device" are HIP device pointers owned by the
+ *     caller.  The library never allocates, frees or retains them.  All must be
+ *     16-byte aligned.  Row-major means the last index is contiguous.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Every call that touches the device only enqueues work on `stream` and
+ *     returns; results are valid once the stream has synchronised.
+ *   - Every function returns a wqd_status.  Arguments are validated on the host
+ *     before anything is enqueued, so a non-OK return leaves no partial writes.
+ *     A failing HIP call returns WQD_E_HIP; wqd_last_hip_error() then gives the
+ *     hipError_t of the calling thread.  Nothing prints, throws or aborts.
+ *   - Results are bitwise reproducible for the same (fmt, M, N, K) on gfx950:
+ *     there are no floating-point atomics.
+ *
+ * Formats (fmt):
+ *   WQD_FMT_BF16       each weight bfloat16 (round to nearest even).
+ *   WQD_FMT_FP8_E4M3   OCP E4M3FN codes, one float32 scale per output row:
+ *                      s_n = max_k |W[n,k]| / 448 (1 for an all-zero row, at
+ *                      least 2^-126), code = nearest E4M3 of W/s_n (ties to
+ *                      even, saturating at 448); weight = e4m3(code) * s_n.
+ *   WQD_FMT_W4A16_G128 unsigned 4-bit codes q in groups of 128 consecutive k,
+ *                      each group with an fp16 scale s and a uint4 zero point z:
+ *                      lo = min(0, min W_g), hi = max(0, max W_g),
+ *                      s = fp16(fp32(hi - lo) / 15) (2^-24 if that is 0, 65504
+ *                      if it overflows, 1 for an all-zero group),
+ *                      z = clamp(rint(-lo / s), 0, 15),
+ *                      q = clamp(rint(W / s) + z, 0, 15); weight = (q - z) * s.
+ *                      All divisions float32, rint ties to even.
+ *
+ * Packed layout (private to the library; read it back only through
+ * wqd_dequant / wqd_unpack): weights are stored in tiles of 64 output rows x
+ * 4 KiB, so each lane of a 64-wide wavefront issues 16-byte loads that are
+ * contiguous across the wavefront.  wqd_packed_sizes gives the buffer sizes.
+ */
+#ifndef WQD_H
+#define WQD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum wqd_fmt {
+    WQD_FMT_BF16 = 0,
+    WQD_FMT_FP8_E4M3 = 1,
+    WQD_FMT_W4A16_G128 = 2
+};
+
+enum wqd_status {
+    WQD_OK = 0,
+    WQD_E_ARG = 1,          /* null pointer, unknown fmt, negative size */
+    WQD_E_SHAPE = 2,        /* shape not supported by fmt (e.g. K % 128 != 0 for W4A16) */
+    WQD_E_ALIGN = 3,        /* a pointer is not 16-byte aligned */
+    WQD_E_WORKSPACE = 4,    /* workspace missing or smaller than wqd_workspace_bytes */
+    WQD_E_HIP = 5,          /* a HIP runtime call failed; see wqd_last_hip_error() */
+    WQD_E_UNSUPPORTED = 6   /* a valid request this build cannot serve */
+};
+
+/* Library version as major*10000 + minor*100 + patch. */
+int wqd_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* wqd_status_str(int status);
+
+/* hipError_t of the last failing HIP call made by this thread (0 if none). */
+int wqd_last_hip_error(void);
+
+/*
+ * Host-only: byte sizes of the three packed buffers for an N x K weight in
+ * `fmt` (tiles padded to 64 rows and to whole K tiles).  scale_bytes and
+ * zero_bytes are 0 where the format has none.  Any output pointer may be NULL.
+ * Errors: WQD_E_ARG (fmt, N < 1, K < 1), WQD_E_SHAPE (K % 128 != 0 for W4A16,
+ * K % 8 != 0 for the others).
+ */
+int wqd_packed_sizes(int fmt, int64_t N, int64_t K,
+                     size_t* w_bytes, size_t* scale_bytes, size_t* zero_bytes);
+
+/*
+ * Host-only: bytes of scratch workspace wqd_qgemm needs for this shape (may
+ * be 0).  The workspace holds split-K partial sums and per-tile arrival
+ * counters.  It must be zero-filled before its first use; every call returns
+ * it to that state when it completes.  One workspace must not be used by two
+ * calls that can run at the same time.
+ */
+int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes);
+
+/*
+ * Setup (not on the decode hot path): quantise W (device, float32 [N, K]
+ * row-major, finite values) to `fmt` and write the packed weights, scales and
+ * zero points (device buffers of the sizes wqd_packed_sizes gives; scales and
+ * zeros may be NULL where the format has none).  Deterministic.
+ */
+int wqd_pack_weights(int fmt, const float* W, int64_t N, int64_t K,
+                     void* w_packed, void* scales, void* zeros, void* stream);
+
+/*
+ * Hot path: y[M, N] = x[M, K] . dequant(W)^T.
+ *   x  device bfloat16 [M, K] row-major;   y  device bfloat16 [M, N] row-major.
+ * Products are formed from exactly dequantised weights and accumulated in
+ * float32 (each W4A16 group and each FP8 row scale applied in float32); y is
+ * the float32 sum rounded to nearest even bfloat16.  M >= 1; any M is
+ * accepted, M <= 8 takes the wavefront-per-64-rows streaming kernel, larger M
+ * the matrix-core kernel.  workspace: device, >= wqd_workspace_bytes bytes
+ * (may be NULL when that is 0).
+ */
+int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K,
+              const void* w_packed, const void* scales, const void* zeros,
+              void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Parity: dequantised weights in logical order, W_out device float32 [N, K]
+ * row-major.  bf16 and W4A16 values are exact; FP8 values are the float32
+ * product e4m3(code) * s_n rounded once.
+ */
+int wqd_dequant(int fmt, const void* w_packed, const void* scales, const void* zeros,
+                int64_t N, int64_t K, float* W_out, void* stream);
+
+/*
+ * Parity: the logical codes behind a packed weight.
+ *   codes_out  device [N, K] row-major: uint16 bf16 bit patterns (BF16), uint8
+ *              E4M3 codes (FP8) or uint8 q in [0, 15] (W4A16);
+ *   scales_out device float32 [N] (FP8) or float16 bits [N, K/128] (W4A16);
+ *   zeros_out  device uint8 [N, K/128] (W4A16).
+ * Outputs a format does not have must be NULL or are ignored.
+ */
+int wqd_unpack(int fmt, const void* w_packed, const void* scales, const void* zeros,
+               int64_t N, int64_t K, void* codes_out, void* scales_out, void* zeros_out,
+               void* stream);
+
+/*
+ * Parity: decode n E4M3 codes (device uint8) to float32 (device) with the same
+ * device conversion the FP8 weight path uses (the exhaustive 256-code check).
+ */
+int wqd_decode_e4m3(const uint8_t* codes, float* out, int64_t n, void* stream);
+
+/*
+ * Measurement: read `bytes` (multiple of 16) from device `src` with 16-byte
+ * loads and write one 32-bit checksum per workgroup to `sink` (device,
+ * >= wqd_stream_sink_words(bytes) words).  The HBM read ceiling.
+ */
+int wqd_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+size_t wqd_stream_sink_words(size_t bytes);
+
+/* Measurement: device copy of `bytes` (multiple of 16) with 16-byte loads/stores. */
+int wqd_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQD_H */

@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/wqd.h, answers the host-only queries, and rejects bad
+arguments with the documented status codes before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_quantized_decode_amd as wqd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wqd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(wqd.LIB_PATH), reason="libwqd.so not built")
+
+OK, E_ARG, E_SHAPE, E_ALIGN, E_WS = 0, 1, 2, 3, 4
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(wqd_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) >= 13
+    L = ctypes.CDLL(wqd.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(wqd.exported_symbols()) == names
+
+
+def test_version_and_status_strings():
+    L = wqd.lib()
+    assert L.wqd_version() >= 100
+    for s in range(7):
+        assert L.wqd_status_str(s)
+    assert L.wqd_status_str(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("fmt,N,K", [("bf16", 4096, 4096), ("fp8", 8192, 8192), ("w4a16", 4096, 4096),
+                                     ("w4a16", 100, 256), ("fp8", 65, 24), ("bf16", 1, 8)])
+def test_packed_sizes(fmt, N, K):
+    # 1 KiB tiles of 16 rows x 64 bytes of K; W4A16 metadata stored 4 groups per row together
+    w, s, z = wqd.packed_sizes(fmt, N, K)
+    NB = -(-N // 16)
+    tk = {"bf16": 32, "fp8": 64, "w4a16": 128}[fmt]
+    KT = -(-K // tk)
+    assert w == NB * KT * 1024
+    if fmt == "bf16":
+        assert s == 0 and z == 0
+    elif fmt == "fp8":
+        assert s == NB * 16 * 4 and z == 0
+    else:
+        G4 = -(-(K // 128) // 4)
+        assert s == NB * 16 * G4 * 4 * 2 and z == NB * 16 * G4 * 2
+    if N % 16 == 0 and (fmt != "w4a16" or (K // 128) % 4 == 0) and K % tk == 0:
+        # no padding: the packed size is exactly the algorithmic byte count
+        from weight_only_quantized_decode_amd import workloads as WL
+        wb = WL.weight_bytes(fmt, N, K)
+        assert (w, s, z) == (wb["w"], wb["s"], wb["z"])
+
+
+def test_w4a16_4096_square_sizes_match_page_byte_count():
+    # CS336 lecture 10 notes, exercise 4: 4096x4096 INT4, groups of 128, fp16
+    # scale -> 4.125 bits/weight = 8,650,752 bytes; our format adds a uint4 zero.
+    w, s, z = wqd.packed_sizes("w4a16", 4096, 4096)
+    assert w + s == 8_650_752
+    assert z == 4096 * 4096 // 128 // 2
+
+
+def test_packed_sizes_errors():
+    L = wqd.lib()
+    n = ctypes.c_size_t()
+    assert L.wqd_packed_sizes(3, 64, 128, None, None, None) == E_ARG
+    assert L.wqd_packed_sizes(2, 0, 128, None, None, None) == E_ARG
+    assert L.wqd_packed_sizes(2, 64, 100, None, None, None) == E_SHAPE
+    assert L.wqd_packed_sizes(1, 64, 12, None, None, None) == E_SHAPE
+    assert L.wqd_packed_sizes(0, 64, 16, ctypes.byref(n), None, None) == OK and n.value == 4096  # 4 blocks x 1 tile
+
+
+def test_workspace_query():
+    for fmt in ("bf16", "fp8", "w4a16"):
+        for M in (1, 4, 8, 16, 1024):
+            assert wqd.workspace_bytes(fmt, M, 8192, 8192) == 0
+    L = wqd.lib()
+    assert L.wqd_workspace_bytes(2, 1, 64, 128, None) == E_ARG
+    b = ctypes.c_size_t()
+    assert L.wqd_workspace_bytes(2, 0, 64, 128, ctypes.byref(b)) == E_ARG
+
+
+def test_qgemm_rejects_bad_arguments_before_enqueue():
+    L = wqd.lib()
+    A = 0x10000  # 16-byte aligned fake address: never dereferenced, validation fails first
+    args = dict(fmt=2, x=A, M=1, N=64, K=128, w=A, s=A, z=A, y=A, ws=A, wsb=1 << 20, st=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.wqd_qgemm(a["fmt"], a["x"], a["M"], a["N"], a["K"], a["w"], a["s"], a["z"], a["y"], a["ws"],
+                           a["wsb"], a["st"])
+
+    assert call(M=0) == E_ARG
+    assert call(fmt=9) == E_ARG
+    assert call(N=0) == E_ARG
+    assert call(K=100) == E_SHAPE
+    assert call(x=None) == E_ARG
+    assert call(y=None) == E_ARG
+    assert call(w=None) == E_ARG
+    assert call(s=None) == E_ARG
+    assert call(z=None) == E_ARG
+    assert call(x=A + 2) == E_ALIGN
+    assert call(w=A + 8) == E_ALIGN
+    assert call(fmt=1, K=12) == E_SHAPE
+    assert wqd.workspace_bytes("w4a16", 1, 64 * 200, 128 * 64) == 0
+
+
+def test_other_entry_points_reject_bad_arguments():
+    L = wqd.lib()
+    A = 0x10000
+    assert L.wqd_pack_weights(2, None, 64, 128, A, A, A, None) == E_ARG
+    assert L.wqd_pack_weights(2, A, 64, 100, A, A, A, None) == E_SHAPE
+    assert L.wqd_pack_weights(1, A, 64, 128, A, None, None, None) == E_ARG
+    assert L.wqd_pack_weights(0, A + 4, 64, 128, A, None, None, None) == E_ALIGN
+    assert L.wqd_dequant(2, A, A, None, 64, 128, A, None) == E_ARG
+    assert L.wqd_dequant(2, A, A, A, 64, 128, None, None) == E_ARG
+    assert L.wqd_unpack(1, A, A, None, 64, 128, None, None, None, None) == E_ARG
+    assert L.wqd_decode_e4m3(None, None, 5, None) == E_ARG
+    assert L.wqd_decode_e4m3(None, None, 0, None) == OK
+    assert L.wqd_stream_read(A, 17, A, None) == E_ARG
+    assert L.wqd_stream_copy(A, A + 8, 32, None) == E_ALIGN
+    assert L.wqd_stream_sink_words(1 << 30) >= 1

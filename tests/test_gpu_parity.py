@@ -1,0 +1,173 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer work (codes, scales, zero points, dequantised weights) is compared
+bit for bit; y within the tolerance in tests/parity.py.  Small cases span
+several 64-row tiles, several K tiles and ragged tails in N and K; the
+full-size cases use the exact shapes and launch plans of the benchmark and
+check sampled output channels, which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_quantized_decode_amd as wqd
+import wqd_inputs as I
+from tests.parity import bf16_bits, compare_y
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ("bf16", "fp8", "w4a16")
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def x_dev(x_bits):
+    return to_dev(x_bits.view(np.int16)).view(torch.bfloat16)
+
+
+def small_shapes(fmt):
+    # (N, K): several tiles, ragged N; ragged K tiles where the format allows it
+    if fmt == "w4a16":
+        return [(357, 896), (64, 128), (1, 128), (130, 512), (200, 4096)]
+    return [(357, 904), (64, 64), (1, 8), (130, 512), (200, 4096)]
+
+
+def check_unpack(fmt, pw, qw):
+    codes, scales, zeros = wqd.unpack(pw)
+    torch.cuda.synchronize()
+    if fmt == "bf16":
+        assert np.array_equal(codes.cpu().numpy().view(np.uint16), qw["codes"])
+    elif fmt == "fp8":
+        assert np.array_equal(codes.cpu().numpy(), qw["codes"])
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), qw["scales"].view(np.uint32))
+    else:
+        assert np.array_equal(codes.cpu().numpy(), qw["codes"])
+        assert np.array_equal(scales.cpu().numpy().view(np.uint16), qw["scales"].view(np.uint16))
+        assert np.array_equal(zeros.cpu().numpy(), qw["zeros"])
+
+
+# --------------------------------------------------------------------------- formats
+def test_decode_e4m3_exhaustive():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).to(dev())
+    got = wqd.decode_e4m3(codes).cpu().numpy().astype(np.float64)
+    ref = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    assert np.nanmax(got) == 448.0
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_pack_unpack_and_dequant_bitexact(fmt):
+    for N, K in small_shapes(fmt):
+        print(f"pack/unpack/dequant {fmt} N={N} K={K}", flush=True)
+        W = I.w_host(11 + N + K, N, K)
+        qw = oracle.quantize(fmt, W)
+        pw = wqd.pack_weights(fmt, to_dev(W))
+        check_unpack(fmt, pw, qw)
+        Wd = wqd.dequant(pw).cpu().numpy()
+        assert np.array_equal(Wd.view(np.uint32), oracle.dequant_f32(qw).view(np.uint32)), (fmt, N, K)
+
+
+def test_pack_degenerate_groups_and_rows():
+    rng = np.random.default_rng(3)
+    W = I.w_host(5, 70, 384)
+    W[0, :] = 0.0                             # zero row (fp8 scale 1) and zero groups
+    W[1, :128] = np.abs(W[1, :128])           # z = 0
+    W[2, 128:256] = -np.abs(W[2, 128:256])    # z = 15
+    W[3, 256:] = 1e-9                         # tiny groups: fp16 scale floors at 2^-24
+    W[4, :] = np.float32(3.0)                 # constant row
+    W[5, :128] = rng.integers(-7, 8, 128).astype(np.float32) * np.float32(0.25)  # exact ties
+    W[6, :] = -0.0
+    W[7, 5] = np.float32(1e4)                 # one outlier inflating its group / row scale
+    for fmt in FMTS:
+        qw = oracle.quantize(fmt, W)
+        pw = wqd.pack_weights(fmt, to_dev(W))
+        check_unpack(fmt, pw, qw)
+        Wd = wqd.dequant(pw).cpu().numpy()
+        assert np.array_equal(Wd.view(np.uint32), oracle.dequant_f32(qw).view(np.uint32)), fmt
+
+
+# --------------------------------------------------------------------------- qgemm small
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 33])
+def test_qgemm_small_shapes(fmt, M):
+    for N, K in small_shapes(fmt):
+        print(f"qgemm {fmt} M={M} N={N} K={K}", flush=True)
+        W = I.w_host(1000 + N + K, N, K)
+        qw = oracle.quantize(fmt, W)
+        pw = wqd.pack_weights(fmt, to_dev(W))
+        x = I.x_bf16_bits(7 * M + K, M, K)
+        y = wqd.qgemm(x_dev(x), pw)
+        torch.cuda.synchronize()
+        compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_one_hot_probes_exact(fmt):
+    """x = e_k gives y[:, n] = bf16(Wd[n, k]) exactly: ties the kernel's own dequant to the oracle.
+
+    Wd is the float32 dequantised weight (exact for bf16 and W4A16; for FP8 the
+    kernel applies the row scale in float32, so the single float32 product
+    e4m3 * s_n is the value it rounds to bf16)."""
+    N, K = 200, 512
+    W = I.w_host(77, N, K)
+    qw = oracle.quantize(fmt, W)
+    Wd = oracle.dequant_f32(qw).astype(np.float64)
+    pw = wqd.pack_weights(fmt, to_dev(W))
+    ks = [0, 1, 7, 8, 63, 64, 127, 128, 300, 511]
+    x = np.zeros((len(ks), K), np.uint16)
+    for i, k in enumerate(ks):
+        x[i, k] = 0x3F80  # 1.0
+    for M0 in range(0, len(ks), 8):
+        xb = x[M0:M0 + 8]
+        y = bf16_bits(wqd.qgemm(x_dev(xb), pw))
+        for i in range(xb.shape[0]):
+            assert np.array_equal(y[i], oracle.bf16_to_bits(Wd[:, ks[M0 + i]])), (fmt, ks[M0 + i])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_zero_weights_give_exact_zero(fmt):
+    N, K = 130, 512
+    pw = wqd.pack_weights(fmt, torch.zeros((N, K), dtype=torch.float32, device=dev()))
+    y = wqd.qgemm(x_dev(I.x_bf16_bits(3, 4, K)), pw)
+    torch.cuda.synchronize()
+    assert (y.float() == 0).all()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_deterministic_and_every_output_written(fmt):
+    N, K = 1000, 2048
+    W = I.w_host(9, N, K)
+    pw = wqd.pack_weights(fmt, to_dev(W))
+    for M in (1, 5, 8):
+        x = x_dev(I.x_bf16_bits(10 + M, M, K))
+        y1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+        y2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+        wqd.qgemm(x, pw, y=y1)
+        wqd.qgemm(x, pw, y=y2)
+        torch.cuda.synchronize()
+        assert torch.isfinite(y1.float()).all()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_no_workspace_needed():
+    """The streaming kernel keeps every partial sum inside its workgroup."""
+    fmt, N, K = "w4a16", 640, 4096
+    for M in (1, 8, 3, 40):
+        assert wqd.workspace_bytes(fmt, M, N, K) == 0
+    W = I.w_host(1, N, K)
+    qw = oracle.quantize(fmt, W)
+    pw = wqd.pack_weights(fmt, to_dev(W))
+    x = I.x_bf16_bits(5, 3, K)
+    y = wqd.qgemm(x_dev(x), pw, workspace=None)
+    torch.cuda.synchronize()
+    compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), "no workspace")

@@ -1,0 +1,259 @@
+"""Weight-only quantized decode linear layer for MI355X (gfx950).
+
+A thin ctypes binding over ``libwqd.so`` (C ABI in ``include/wqd.h``).  It only
+marshals arguments: torch provides device memory and the current HIP stream,
+and every step of the computation runs in the library's HIP kernels.  If the
+library is missing, every call raises: there is no fallback.
+
+    import weight_only_quantized_decode_amd as wqd
+    pw = wqd.pack_weights("w4a16", W)        # W: cuda float32 [N, K]
+    y = wqd.qgemm(x, pw)                     # x: cuda bfloat16 [M, K] -> y [M, N]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwqd.so")
+
+FMT = {"bf16": 0, "fp8": 1, "w4a16": 2}
+FMT_NAMES = {v: k for k, v in FMT.items()}
+GROUP = 128
+
+_lib = None
+
+
+class WqdError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{where}: {lib().wqd_status_str(status).decode()} (status {status})"
+        if hip_error:
+            msg += f", hipError {hip_error}"
+        super().__init__(msg)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m weight_only_quantized_decode_amd.build` "
+                "(the decode path has no fallback)"
+            )
+        L = ctypes.CDLL(LIB_PATH)
+        i64, sz, vp, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+        psz = ctypes.POINTER(ctypes.c_size_t)
+        sig = {
+            "wqd_version": (i32, []),
+            "wqd_status_str": (ctypes.c_char_p, [i32]),
+            "wqd_last_hip_error": (i32, []),
+            "wqd_packed_sizes": (i32, [i32, i64, i64, psz, psz, psz]),
+            "wqd_workspace_bytes": (i32, [i32, i64, i64, i64, psz]),
+            "wqd_pack_weights": (i32, [i32, vp, i64, i64, vp, vp, vp, vp]),
+            "wqd_qgemm": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
+            "wqd_dequant": (i32, [i32, vp, vp, vp, i64, i64, vp, vp]),
+            "wqd_unpack": (i32, [i32, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
+            "wqd_decode_e4m3": (i32, [vp, vp, i64, vp]),
+            "wqd_stream_read": (i32, [vp, sz, vp, vp]),
+            "wqd_stream_sink_words": (sz, [sz]),
+            "wqd_stream_copy": (i32, [vp, vp, sz, vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    """Names of the C entry points this binding declares (all must resolve)."""
+    lib()
+    return [
+        "wqd_version", "wqd_status_str", "wqd_last_hip_error", "wqd_packed_sizes", "wqd_workspace_bytes",
+        "wqd_pack_weights", "wqd_qgemm", "wqd_dequant", "wqd_unpack", "wqd_decode_e4m3", "wqd_stream_read",
+        "wqd_stream_sink_words", "wqd_stream_copy",
+    ]
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise WqdError(status, where, lib().wqd_last_hip_error() if status == 5 else 0)
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        if fmt not in FMT:
+            raise ValueError(f"unknown format {fmt!r}; expected one of {sorted(FMT)}")
+        return FMT[fmt]
+    return int(fmt)
+
+
+def _stream(stream=None):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+# ----------------------------------------------------------------------------- host queries
+def packed_sizes(fmt, N: int, K: int):
+    w, s, z = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().wqd_packed_sizes(_fmt(fmt), N, K, ctypes.byref(w), ctypes.byref(s), ctypes.byref(z)),
+           "wqd_packed_sizes")
+    return w.value, s.value, z.value
+
+
+def workspace_bytes(fmt, M: int, N: int, K: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().wqd_workspace_bytes(_fmt(fmt), M, N, K, ctypes.byref(b)), "wqd_workspace_bytes")
+    return b.value
+
+
+# ----------------------------------------------------------------------------- packed weights
+@dataclass
+class PackedWeight:
+    fmt: str
+    N: int
+    K: int
+    w: "object"                 # torch uint8 device tensor
+    scales: "Optional[object]"  # torch uint8 device tensor (or None)
+    zeros: "Optional[object]"
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() for t in (self.w, self.scales, self.zeros) if t is not None)
+
+
+def alloc_packed(fmt, N: int, K: int, device="cuda") -> PackedWeight:
+    import torch
+
+    wb, sb, zb = packed_sizes(fmt, N, K)
+    w = torch.empty(wb, dtype=torch.uint8, device=device)
+    s = torch.empty(sb, dtype=torch.uint8, device=device) if sb else None
+    z = torch.empty(zb, dtype=torch.uint8, device=device) if zb else None
+    return PackedWeight(FMT_NAMES[_fmt(fmt)], N, K, w, s, z)
+
+
+def pack_weights(fmt, W, out: Optional[PackedWeight] = None, stream=None) -> PackedWeight:
+    """Quantise float32 W[N, K] (cuda) into the packed layout."""
+    import torch
+
+    if W.dtype != torch.float32 or not W.is_cuda or W.dim() != 2:
+        raise ValueError("W must be a cuda float32 [N, K] tensor")
+    W = W.contiguous()
+    N, K = W.shape
+    pw = out if out is not None else alloc_packed(fmt, N, K, W.device)
+    _check(lib().wqd_pack_weights(_fmt(fmt), W.data_ptr(), N, K, _ptr(pw.w), _ptr(pw.scales), _ptr(pw.zeros),
+                                  _stream(stream)), "wqd_pack_weights")
+    return pw
+
+
+# ----------------------------------------------------------------------------- workspace
+_ws_cache = {}
+
+
+def get_workspace(nbytes: int, device=None):
+    """A zero-filled workspace of at least nbytes, cached per device (grow-only).
+
+    The library returns it to all-zero state after every call, so the cache can
+    be reused by consecutive calls on one stream.
+    """
+    import torch
+
+    if nbytes == 0:
+        return None
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    cur = _ws_cache.get(dev)
+    if cur is None or cur.numel() < nbytes:
+        cur = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _ws_cache[dev] = cur
+    return cur
+
+
+def qgemm(x, pw: PackedWeight, y=None, workspace=None, stream=None):
+    """y[M, N] (bfloat16) = x[M, K] (bfloat16) . dequant(W)^T."""
+    import torch
+
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 [M, K] tensor")
+    M, K = x.shape
+    if K != pw.K:
+        raise ValueError(f"K mismatch: x has {K}, weights have {pw.K}")
+    if y is None:
+        y = torch.empty((M, pw.N), dtype=torch.bfloat16, device=x.device)
+    need = workspace_bytes(pw.fmt, M, pw.N, K)
+    if workspace is None:
+        workspace = get_workspace(need, x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().wqd_qgemm(_fmt(pw.fmt), x.data_ptr(), M, pw.N, K, _ptr(pw.w), _ptr(pw.scales), _ptr(pw.zeros),
+                           y.data_ptr(), _ptr(workspace), wsb, _stream(stream)), "wqd_qgemm")
+    return y
+
+
+def dequant(pw: PackedWeight, out=None, stream=None):
+    import torch
+
+    if out is None:
+        out = torch.empty((pw.N, pw.K), dtype=torch.float32, device=pw.w.device)
+    _check(lib().wqd_dequant(_fmt(pw.fmt), _ptr(pw.w), _ptr(pw.scales), _ptr(pw.zeros), pw.N, pw.K, out.data_ptr(),
+                             _stream(stream)), "wqd_dequant")
+    return out
+
+
+def unpack(pw: PackedWeight, stream=None):
+    """Logical (codes, scales, zeros) of a packed weight, as device tensors."""
+    import torch
+
+    dev = pw.w.device
+    G = pw.K // GROUP
+    if pw.fmt == "bf16":
+        codes = torch.empty((pw.N, pw.K), dtype=torch.int16, device=dev)
+        scales = zeros = None
+    elif pw.fmt == "fp8":
+        codes = torch.empty((pw.N, pw.K), dtype=torch.uint8, device=dev)
+        scales = torch.empty((pw.N,), dtype=torch.float32, device=dev)
+        zeros = None
+    else:
+        codes = torch.empty((pw.N, pw.K), dtype=torch.uint8, device=dev)
+        scales = torch.empty((pw.N, G), dtype=torch.int16, device=dev)
+        zeros = torch.empty((pw.N, G), dtype=torch.uint8, device=dev)
+    _check(lib().wqd_unpack(_fmt(pw.fmt), _ptr(pw.w), _ptr(pw.scales), _ptr(pw.zeros), pw.N, pw.K,
+                            codes.data_ptr(), _ptr(scales), _ptr(zeros), _stream(stream)), "wqd_unpack")
+    return codes, scales, zeros
+
+
+def decode_e4m3(codes, stream=None):
+    import torch
+
+    out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    _check(lib().wqd_decode_e4m3(codes.data_ptr(), out.data_ptr(), codes.numel(), _stream(stream)),
+           "wqd_decode_e4m3")
+    return out
+
+
+def stream_read(buf, sink=None, stream=None):
+    import torch
+
+    nbytes = buf.numel() * buf.element_size()
+    words = lib().wqd_stream_sink_words(nbytes)
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=buf.device)
+    _check(lib().wqd_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(stream)), "wqd_stream_read")
+    return sink
+
+
+def stream_copy(dst, src, stream=None):
+    nbytes = src.numel() * src.element_size()
+    _check(lib().wqd_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream)), "wqd_stream_copy")
+    return dst

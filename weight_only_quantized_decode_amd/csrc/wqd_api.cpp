@@ -1,0 +1,147 @@
+// extern "C" entry points declared in include/wqd.h: validate on the host,
+// plan, then enqueue on the caller's stream.  No allocation, no host sync.
+#include <hip/hip_runtime.h>
+
+#include "../../include/wqd.h"
+#include "wqd_internal.h"
+#include "wqd_plan.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return WQD_OK;
+  g_last_hip_error = int(e);
+  return WQD_E_HIP;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool need_scales(int fmt) { return fmt != wqd::kFmtBF16; }
+bool need_zeros(int fmt) { return fmt == wqd::kFmtW4; }
+
+int check_packed_ptrs(int fmt, const void* wp, const void* scales, const void* zeros) {
+  if (!wp) return WQD_E_ARG;
+  if (need_scales(fmt) && !scales) return WQD_E_ARG;
+  if (need_zeros(fmt) && !zeros) return WQD_E_ARG;
+  if (!wqd::aligned16(wp)) return WQD_E_ALIGN;
+  if (need_scales(fmt) && !wqd::aligned16(scales)) return WQD_E_ALIGN;
+  if (need_zeros(fmt) && !wqd::aligned16(zeros)) return WQD_E_ALIGN;
+  return WQD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wqd_version(void) { return 100; }
+
+const char* wqd_status_str(int status) {
+  switch (status) {
+    case WQD_OK: return "ok";
+    case WQD_E_ARG: return "invalid argument (null pointer, unknown format or bad size)";
+    case WQD_E_SHAPE: return "shape not supported by this format";
+    case WQD_E_ALIGN: return "pointer not 16-byte aligned";
+    case WQD_E_WORKSPACE: return "workspace missing or too small";
+    case WQD_E_HIP: return "HIP runtime error";
+    case WQD_E_UNSUPPORTED: return "unsupported request";
+    default: return "unknown status";
+  }
+}
+
+int wqd_last_hip_error(void) { return g_last_hip_error; }
+
+int wqd_packed_sizes(int fmt, int64_t N, int64_t K, size_t* w_bytes, size_t* scale_bytes, size_t* zero_bytes) {
+  wqd::PackedSizes ps;
+  const int st = wqd::packed_sizes(fmt, N, K, &ps);
+  if (st != wqd::kOK) return st;
+  if (w_bytes) *w_bytes = ps.w_bytes;
+  if (scale_bytes) *scale_bytes = ps.s_bytes;
+  if (zero_bytes) *zero_bytes = ps.z_bytes;
+  return WQD_OK;
+}
+
+int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return WQD_E_ARG;
+  return wqd::workspace_bytes(fmt, M, N, K, bytes);
+}
+
+int wqd_pack_weights(int fmt, const float* W, int64_t N, int64_t K, void* w_packed, void* scales, void* zeros,
+                     void* stream) {
+  wqd::PackedSizes ps;
+  int st = wqd::packed_sizes(fmt, N, K, &ps);
+  if (st != wqd::kOK) return st;
+  if (!W) return WQD_E_ARG;
+  if (!wqd::aligned16(W)) return WQD_E_ALIGN;
+  st = check_packed_ptrs(fmt, w_packed, scales, zeros);
+  if (st != WQD_OK) return st;
+  return hip_status(wqd::launch_pack(fmt, W, N, K, ps, w_packed, scales, zeros, as_stream(stream)));
+}
+
+int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const void* w_packed, const void* scales,
+              const void* zeros, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 1) return WQD_E_ARG;
+  wqd::GemvPlan plan;
+  int st = wqd::plan_gemv(fmt, M, N, K, &plan);
+  if (st != wqd::kOK) return st;
+  if (!x || !y) return WQD_E_ARG;
+  if (!wqd::aligned16(x) || !wqd::aligned16(y)) return WQD_E_ALIGN;
+  st = check_packed_ptrs(fmt, w_packed, scales, zeros);
+  if (st != WQD_OK) return st;
+  size_t need = 0;
+  st = wqd::workspace_bytes(fmt, M, N, K, &need);
+  if (st != wqd::kOK) return st;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return WQD_E_WORKSPACE;
+    if (!wqd::aligned16(workspace)) return WQD_E_ALIGN;
+  }
+  return hip_status(wqd::launch_gemv(fmt, plan, x, M, N, K, w_packed, scales, zeros, y, as_stream(stream)));
+}
+
+int wqd_dequant(int fmt, const void* w_packed, const void* scales, const void* zeros, int64_t N, int64_t K,
+                float* W_out, void* stream) {
+  wqd::PackedSizes ps;
+  int st = wqd::packed_sizes(fmt, N, K, &ps);
+  if (st != wqd::kOK) return st;
+  if (!W_out) return WQD_E_ARG;
+  st = check_packed_ptrs(fmt, w_packed, scales, zeros);
+  if (st != WQD_OK) return st;
+  return hip_status(wqd::launch_dequant(fmt, w_packed, scales, zeros, N, K, ps, W_out, as_stream(stream)));
+}
+
+int wqd_unpack(int fmt, const void* w_packed, const void* scales, const void* zeros, int64_t N, int64_t K,
+               void* codes_out, void* scales_out, void* zeros_out, void* stream) {
+  wqd::PackedSizes ps;
+  int st = wqd::packed_sizes(fmt, N, K, &ps);
+  if (st != wqd::kOK) return st;
+  if (!codes_out) return WQD_E_ARG;
+  st = check_packed_ptrs(fmt, w_packed, scales, zeros);
+  if (st != WQD_OK) return st;
+  if (fmt == wqd::kFmtBF16) scales_out = zeros_out = nullptr;
+  if (fmt == wqd::kFmtFP8) zeros_out = nullptr;
+  return hip_status(wqd::launch_unpack(fmt, w_packed, scales, zeros, N, K, ps, codes_out, scales_out, zeros_out,
+                                       as_stream(stream)));
+}
+
+int wqd_decode_e4m3(const uint8_t* codes, float* out, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && (!codes || !out))) return WQD_E_ARG;
+  if (n == 0) return WQD_OK;
+  return hip_status(wqd::launch_decode_e4m3(codes, out, n, as_stream(stream)));
+}
+
+size_t wqd_stream_sink_words(size_t bytes) { return wqd::stream_sink_words(bytes); }
+
+int wqd_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16) return WQD_E_ARG;
+  if (!wqd::aligned16(src)) return WQD_E_ALIGN;
+  return hip_status(wqd::launch_stream_read(src, bytes, sink, as_stream(stream)));
+}
+
+int wqd_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!src || !dst || bytes == 0 || bytes % 16) return WQD_E_ARG;
+  if (!wqd::aligned16(src) || !wqd::aligned16(dst)) return WQD_E_ALIGN;
+  return hip_status(wqd::launch_stream_copy(dst, src, bytes, as_stream(stream)));
+}
+
+}  // extern "C"

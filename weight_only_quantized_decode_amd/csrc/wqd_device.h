@@ -1,0 +1,54 @@
+// Device helpers shared by the gfx950 kernels: number-format conversions and
+// the in-register dequantisation primitives.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace wqd {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// float32 -> bfloat16 bits, round to nearest even (finite inputs; subnormals kept).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Two FP8-E4M3 codes (bytes 0,1 or bytes 2,3 of `w`) -> two bf16 in one register.
+// gfx950's conversion decodes the OCP E4M3FN encoding; every E4M3 value is
+// exactly representable in bf16, and a scale of 1 leaves it unchanged.
+template <bool HI>
+__device__ __forceinline__ bf16x2_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  bf16x2_t v = e4m3x2_to_bf16x2<false>(code & 0xFFu);
+  return bf16_bits_to_f32(__builtin_bit_cast(uint32_t, v) & 0xFFFFu);
+}
+
+// W4A16 nibble order inside a packed 32-bit word: nibble t (bits 4t..4t+3)
+// holds element kNibElem[t] of the word's 8 consecutive k, so that
+// (w >> 4t) & 0x000F000F yields elements (2t, 2t+1) in the low and high half.
+__device__ __forceinline__ int nib_elem(int t) { return (t & 3) * 2 + (t >> 2); }
+
+// Elements (2t, 2t+1) of a packed word as bf16 (128 + q0, 128 + q1): OR-ing a
+// 4-bit code into the low mantissa bits of 128.0 (0x4300) gives 128 + q exactly.
+template <int T>
+__device__ __forceinline__ bf16x2_t u4x2_to_bf16x2_offset128(uint32_t w) {
+  uint32_t v = ((w >> (4 * T)) & 0x000F000Fu) | 0x43004300u;
+  return __builtin_bit_cast(bf16x2_t, v);
+}
+
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+
+}  // namespace wqd

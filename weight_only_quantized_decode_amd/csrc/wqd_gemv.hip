@@ -1,0 +1,289 @@
+// Streaming decode kernel for M <= 8 activation rows: y = x . dequant(W)^T.
+//
+// Decode moves every weight byte once per step at about one FLOP per byte, so
+// this kernel is bound by HBM ("Making each token cheaper", section "Why
+// decode is usually bandwidth bound").  Design for gfx950:
+//   * one workgroup owns one 16-row block over ALL of K, so no partial sums
+//     ever leave the workgroup: no split-K workspace and no device-scope
+//     fences (on a multi-XCD part those write back and invalidate L2);
+//   * its W wavefronts take contiguous quarter (or eighth) shares of K.  Lane
+//     l = 16 kb + n of a wavefront owns slice kb of row n of every tile in its
+//     share: one 16-byte load per lane, 1 KiB contiguous per wavefront;
+//   * each wavefront stages its own x range in a private LDS region (chunked
+//     when it does not fit) and reads it back as 16-byte broadcast reads; no
+//     workgroup barrier is needed until the final reduction;
+//   * weight tiles are loaded a group of 4 tiles ahead of the arithmetic;
+//   * dequantisation in registers: W4A16 nibble pairs become bf16 (128 + q)
+//     with one AND-OR, FP8 codes become bf16 with the hardware conversion;
+//     v_dot2_f32_bf16 forms exact bf16 x bf16 products summed in float32.
+//     A W4A16 slice contributes s * (sum x (128 + q) - (128 + z) * sum x),
+//     where sum x comes from the same dot2 chain against (1, 1), so q == z
+//     == 0 cancels exactly;
+//   * the 4 lanes of a row and the W wavefronts are reduced in a fixed order
+//     (deterministic, no atomics).
+#include "wqd_device.h"
+#include "wqd_internal.h"
+#include "wqd_plan.h"
+
+namespace wqd {
+
+struct GemvArgs {
+  const uint16_t* x;
+  uint16_t* y;
+  const uint4* w;
+  const void* scales;
+  const uint16_t* zeros;
+  int64_t N, K, NB, KT, G4;
+};
+
+template <int FMT>
+struct FmtC {
+  static constexpr int TK = FMT == kFmtBF16 ? 32 : FMT == kFmtFP8 ? 64 : 128;  // K per tile
+  static constexpr int SLK = TK / 4;                                             // K per slice
+  static constexpr int SLU = SLK / 8;                                            // x uint4 per slice
+  static constexpr int SLS = SLU + (FMT == kFmtW4 ? 1 : 0);  // padded LDS stride: spreads the 4 slices over banks
+};
+
+constexpr int kGroupTiles = 4;  // tiles per prefetch group (= one W4A16 scale quad)
+
+// Tiles of x one wavefront stages per chunk: about 4 KiB of x, whole groups.
+template <int FMT, int MR>
+constexpr int chunk_tiles() {
+  constexpr int t = 2048 / (MR * FmtC<FMT>::TK) / kGroupTiles * kGroupTiles;
+  return t < kGroupTiles ? kGroupTiles : t;
+}
+
+template <int FMT>
+struct Group {
+  uint4 w[kGroupTiles];
+  uint2 s;     // W4A16: 4 fp16 scales (one per tile of the group)
+  uint32_t z;  // W4A16: 4 zero nibbles
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_group(Group<FMT>& g, const GemvArgs& a, int64_t nb, int64_t kt, int64_t kt_end,
+                                           int lane) {
+  const uint4* p = a.w + (nb * a.KT + kt) * (kTileBytes / 16) + lane;
+#pragma unroll
+  for (int i = 0; i < kGroupTiles; ++i)
+    if (kt + i < kt_end) g.w[i] = p[i * (kTileBytes / 16)];
+  if (FMT == kFmtW4) {
+    const int n = lane & 15;
+    const int64_t q = (nb * a.G4 + kt / kScaleQuad) * kTileRows + n;
+    g.s = reinterpret_cast<const uint2*>(a.scales)[q];
+    g.z = a.zeros[q];
+  }
+}
+
+// One tile for every activation row: acc[m] += row-n slice-kb partial product.
+template <int FMT, int MR, int CT>
+__device__ __forceinline__ void tile_dot(const uint4 w, int i, const Group<FMT>& g, int kb,
+                                         const uint4* __restrict__ xs, const float* __restrict__ xsum, int tl,
+                                         float (&acc)[MR]) {
+  using C = FmtC<FMT>;
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  const int sl = tl * 4 + kb;  // slice index inside the staged chunk
+  if (FMT == kFmtW4) {
+    const uint32_t sbits = (i < 2 ? g.s.x : g.s.y) >> (16 * (i & 1));
+    const float s = __half2float(__ushort_as_half(uint16_t(sbits & 0xFFFFu)));
+    const float zc = 128.0f + float((g.z >> (4 * i)) & 0xFu);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const uint4* xp = xs + (m * CT * 4 + sl) * C::SLS;
+      float P = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 xv = xp[q];
+        P = dot2_bf16(u4x2_to_bf16x2_offset128<0>(wd[q]), as_bf16x2(xv.x), P);
+        P = dot2_bf16(u4x2_to_bf16x2_offset128<1>(wd[q]), as_bf16x2(xv.y), P);
+        P = dot2_bf16(u4x2_to_bf16x2_offset128<2>(wd[q]), as_bf16x2(xv.z), P);
+        P = dot2_bf16(u4x2_to_bf16x2_offset128<3>(wd[q]), as_bf16x2(xv.w), P);
+      }
+      const float D = fmaf(-zc, xsum[m * CT * 4 + sl], P);
+      acc[m] = fmaf(s, D, acc[m]);
+    }
+  } else if (FMT == kFmtFP8) {
+    const bf16x2_t b0 = e4m3x2_to_bf16x2<false>(wd[0]), b1 = e4m3x2_to_bf16x2<true>(wd[0]);
+    const bf16x2_t b2 = e4m3x2_to_bf16x2<false>(wd[1]), b3 = e4m3x2_to_bf16x2<true>(wd[1]);
+    const bf16x2_t b4 = e4m3x2_to_bf16x2<false>(wd[2]), b5 = e4m3x2_to_bf16x2<true>(wd[2]);
+    const bf16x2_t b6 = e4m3x2_to_bf16x2<false>(wd[3]), b7 = e4m3x2_to_bf16x2<true>(wd[3]);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const uint4* xp = xs + (m * CT * 4 + sl) * C::SLS;
+      const uint4 x0 = xp[0], x1 = xp[1];
+      float a0 = acc[m];
+      a0 = dot2_bf16(b0, as_bf16x2(x0.x), a0);
+      a0 = dot2_bf16(b1, as_bf16x2(x0.y), a0);
+      a0 = dot2_bf16(b2, as_bf16x2(x0.z), a0);
+      a0 = dot2_bf16(b3, as_bf16x2(x0.w), a0);
+      a0 = dot2_bf16(b4, as_bf16x2(x1.x), a0);
+      a0 = dot2_bf16(b5, as_bf16x2(x1.y), a0);
+      a0 = dot2_bf16(b6, as_bf16x2(x1.z), a0);
+      a0 = dot2_bf16(b7, as_bf16x2(x1.w), a0);
+      acc[m] = a0;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const uint4 xv = xs[(m * CT * 4 + sl) * C::SLS];
+      float a0 = acc[m];
+      a0 = dot2_bf16(as_bf16x2(wd[0]), as_bf16x2(xv.x), a0);
+      a0 = dot2_bf16(as_bf16x2(wd[1]), as_bf16x2(xv.y), a0);
+      a0 = dot2_bf16(as_bf16x2(wd[2]), as_bf16x2(xv.z), a0);
+      a0 = dot2_bf16(as_bf16x2(wd[3]), as_bf16x2(xv.w), a0);
+      acc[m] = a0;
+    }
+  }
+}
+
+// Stage x for tiles [kt0, kt0 + nt) of this wavefront's share into its LDS
+// region; W4A16 also gets the per-slice x sums.  Wavefront-private: LDS
+// operations of one wavefront complete in order, so only compiler ordering
+// is needed around it.
+template <int FMT, int MR, int CT>
+__device__ __forceinline__ void stage_x(const GemvArgs& a, int64_t kt0, int nt, int lane, uint4* __restrict__ xs,
+                                        float* __restrict__ xsum) {
+  using C = FmtC<FMT>;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int per_m = nt * 4;  // slices per activation row in this chunk
+  for (int i = lane; i < MR * per_m; i += 64) {
+    const int m = i / per_m, sl = i - m * per_m;
+    const int64_t k = (kt0 + sl / 4) * C::TK + (sl & 3) * C::SLK;
+    uint4 v[C::SLU];
+#pragma unroll
+    for (int u = 0; u < C::SLU; ++u) {
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (k + 8 * u < a.K) v[u] = *reinterpret_cast<const uint4*>(a.x + int64_t(m) * a.K + k + 8 * u);
+    }
+    uint4* dst = xs + (m * CT * 4 + sl) * C::SLS;
+#pragma unroll
+    for (int u = 0; u < C::SLU; ++u) dst[u] = v[u];
+    if (FMT == kFmtW4) {
+      const bf16x2_t ones = as_bf16x2(0x3F803F80u);
+      float X = 0.f;
+#pragma unroll
+      for (int u = 0; u < C::SLU; ++u) {
+        X = dot2_bf16(ones, as_bf16x2(v[u].x), X);
+        X = dot2_bf16(ones, as_bf16x2(v[u].y), X);
+        X = dot2_bf16(ones, as_bf16x2(v[u].z), X);
+        X = dot2_bf16(ones, as_bf16x2(v[u].w), X);
+      }
+      xsum[m * CT * 4 + sl] = X;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int FMT, int MR, int W>
+__global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a) {
+  using C = FmtC<FMT>;
+  constexpr int CT = chunk_tiles<FMT, MR>();
+  __shared__ uint4 s_x[W][MR * CT * 4 * C::SLS];
+  __shared__ float s_xsum[W][FMT == kFmtW4 ? MR * CT * 4 : 1];
+  __shared__ float s_red[W][MR][kTileRows];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, kb = lane >> 4, n = lane & 15;
+  const int64_t nb = blockIdx.x;
+  // contiguous share of K tiles for this wavefront, in whole groups
+  const int64_t per_wave = (a.KT + int64_t(W) * kGroupTiles - 1) / (int64_t(W) * kGroupTiles) * kGroupTiles;
+  const int64_t kt_begin = wave * per_wave;
+  const int64_t kt_end = min(a.KT, kt_begin + per_wave);
+  uint4* xs = s_x[wave];
+  float* xsum = s_xsum[wave];
+
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+
+  if (kt_begin < kt_end) {
+    Group<FMT> cur, nxt;
+    load_group<FMT>(cur, a, nb, kt_begin, kt_end, lane);
+    for (int64_t c0 = kt_begin; c0 < kt_end; c0 += CT) {
+      const int nt = int(min<int64_t>(CT, kt_end - c0));
+      stage_x<FMT, MR, CT>(a, c0, nt, lane, xs, xsum);
+      for (int g0 = 0; g0 < nt; g0 += kGroupTiles) {
+        const int64_t kt = c0 + g0;
+        if (kt + kGroupTiles < kt_end) load_group<FMT>(nxt, a, nb, kt + kGroupTiles, kt_end, lane);
+#pragma unroll
+        for (int i = 0; i < kGroupTiles; ++i)
+          if (kt + i < kt_end) tile_dot<FMT, MR, CT>(cur.w[i], i, cur, kb, xs, xsum, g0 + i, acc);
+        cur = nxt;
+      }
+    }
+  }
+
+  // the 4 slices of a row (lanes n, n+16, n+32, n+48), then the W wavefronts
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    float v = acc[m];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (kb == 0) s_red[wave][m][n] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < MR * kTileRows) {
+    const int m = threadIdx.x / kTileRows, r = threadIdx.x % kTileRows;
+    float v = s_red[0][m][r];
+#pragma unroll
+    for (int w = 1; w < W; ++w) v += s_red[w][m][r];
+    const int64_t row = nb * kTileRows + r;
+    if (row < a.N) {
+      if (FMT == kFmtFP8) v *= reinterpret_cast<const float*>(a.scales)[row];
+      a.y[int64_t(m) * a.N + row] = uint16_t(f32_to_bf16_rne(v));
+    }
+  }
+}
+
+template <int FMT, int W, int MR>
+static hipError_t launch_fmt(const GemvArgs& a, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((gemv_kernel<FMT, MR, W>), dim3(grid), dim3(64 * W), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_waves(const GemvArgs& a, int mr, int waves, unsigned grid, hipStream_t st) {
+  // 8 wavefronts only for up to 2 activation rows (their LDS share fits)
+  if (waves == 8 && mr == 1) return launch_fmt<FMT, 8, 1>(a, grid, st);
+  if (waves == 8 && mr == 2) return launch_fmt<FMT, 8, 2>(a, grid, st);
+  switch (mr) {
+    case 1: return launch_fmt<FMT, 4, 1>(a, grid, st);
+    case 2: return launch_fmt<FMT, 4, 2>(a, grid, st);
+    case 3: return launch_fmt<FMT, 4, 3>(a, grid, st);
+    case 4: return launch_fmt<FMT, 4, 4>(a, grid, st);
+    case 5: return launch_fmt<FMT, 4, 5>(a, grid, st);
+    case 6: return launch_fmt<FMT, 4, 6>(a, grid, st);
+    case 7: return launch_fmt<FMT, 4, 7>(a, grid, st);
+    case 8: return launch_fmt<FMT, 4, 8>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemv(int fmt, const GemvPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
+                       const void* scales, const void* zeros, void* y, hipStream_t st) {
+  GemvArgs a;
+  a.w = reinterpret_cast<const uint4*>(wp);
+  a.scales = scales;
+  a.zeros = reinterpret_cast<const uint16_t*>(zeros);
+  a.N = N;
+  a.K = K;
+  a.NB = p.NB;
+  a.KT = p.KT;
+  a.G4 = fmt == kFmtW4 ? ceil_div(K / kGroup, kScaleQuad) : 0;
+  const unsigned grid = unsigned(p.NB);
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int64_t m0 = int64_t(c) * kGemvMaxM;
+    const int mr = int(M - m0 < kGemvMaxM ? M - m0 : int64_t(kGemvMaxM));
+    a.x = reinterpret_cast<const uint16_t*>(x) + m0 * K;
+    a.y = reinterpret_cast<uint16_t*>(y) + m0 * N;
+    hipError_t e;
+    if (fmt == kFmtBF16) e = launch_waves<kFmtBF16>(a, mr, p.waves, grid, st);
+    else if (fmt == kFmtFP8) e = launch_waves<kFmtFP8>(a, mr, p.waves, grid, st);
+    else e = launch_waves<kFmtW4>(a, mr, p.waves, grid, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace wqd

@@ -1,0 +1,24 @@
+// Launchers shared between the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wqd_plan.h"
+
+namespace wqd {
+
+hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, const PackedSizes& ps, void* wp, void* scales,
+                       void* zeros, hipStream_t st);
+hipError_t launch_dequant(int fmt, const void* wp, const void* scales, const void* zeros, int64_t N, int64_t K,
+                          const PackedSizes& ps, float* out, hipStream_t st);
+hipError_t launch_unpack(int fmt, const void* wp, const void* scales, const void* zeros, int64_t N, int64_t K,
+                         const PackedSizes& ps, void* codes, void* scales_out, void* zeros_out, hipStream_t st);
+hipError_t launch_decode_e4m3(const uint8_t* codes, float* out, int64_t n, hipStream_t st);
+hipError_t launch_gemv(int fmt, const GemvPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
+                       const void* scales, const void* zeros, void* y, hipStream_t st);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
+size_t stream_sink_words(size_t bytes);
+
+}  // namespace wqd

@@ -1,0 +1,61 @@
+// Packed layout geometry, argument validation and launch planning.
+// Pure host C++: no HIP headers, so it is the same code on a GPU-less host.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wqd {
+
+// A tile is 16 output rows x 4 slices x 16 bytes = 1 KiB.  Inside a tile,
+// slice j of row r sits at byte (16 j + r) * 16, so lane l = 16 j + r of a
+// 64-wide wavefront loads 16 bytes at l * 16: one fully contiguous 1 KiB load
+// per wavefront.  The same lane order is the B-operand order of the bf16
+// matrix-core instructions (lane = 16 * k_block + column).  Each row holds
+// 64 bytes of K per tile; tiles of one 16-row block are consecutive along K.
+constexpr int kTileRows = 16;
+constexpr int kSlices = 4;
+constexpr int kSliceBytes = 16;
+constexpr int kTileBytes = kTileRows * kSlices * kSliceBytes;  // 1024
+constexpr int kGroup = 128;  // W4A16 group length along K (= one tile's K extent)
+constexpr int kScaleQuad = 4;  // W4A16 scales / zeros are stored 4 groups per row together
+
+constexpr int kFmtBF16 = 0;
+constexpr int kFmtFP8 = 1;
+constexpr int kFmtW4 = 2;
+
+// K elements covered by one tile: 64 bytes per row.
+inline int tile_k(int fmt) { return fmt == kFmtBF16 ? 32 : fmt == kFmtFP8 ? 64 : 128; }
+inline bool fmt_ok(int fmt) { return fmt == kFmtBF16 || fmt == kFmtFP8 || fmt == kFmtW4; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct PackedSizes {
+  int64_t NB;     // 16-row blocks
+  int64_t KT;     // tiles along K
+  int64_t G4;     // W4A16: groups of 4 K-groups (scale / zero storage unit)
+  size_t w_bytes, s_bytes, z_bytes;
+};
+
+// Status codes mirror enum wqd_status in include/wqd.h.
+enum { kOK = 0, kEArg = 1, kEShape = 2, kEAlign = 3, kEWorkspace = 4, kEHip = 5, kEUnsupported = 6 };
+
+int packed_sizes(int fmt, int64_t N, int64_t K, PackedSizes* out);
+
+// Streaming kernel (M <= 8): one workgroup per 16-row block over all of K.
+constexpr int kGemvMaxM = 8;
+
+struct GemvPlan {
+  int64_t NB, KT;
+  int mrows;    // rows per launch (M, or kGemvMaxM when M is processed in chunks)
+  int nchunks;  // launches over M
+  int waves;    // wavefronts per workgroup (each takes a contiguous share of K)
+};
+
+int plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, GemvPlan* out);
+
+// Workspace bytes for wqd_qgemm (0: no path needs scratch memory).
+int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace wqd

@@ -1,0 +1,84 @@
+"""Decode workloads (layer stacks and single matrices) and their algorithmic byte counts.
+
+Algorithmic bytes of one y[M, N] = x[M, K] . W[N, K]^T call: packed weights +
+scales + zero points + x + y, each counted once:
+  bf16   2 B/weight;
+  fp8    1 B/weight + 4 B per output row (one 32-bit scale per row);
+  w4a16  0.5 B/weight + (2 B scale + 0.5 B zero) per 128-weight group,
+         i.e. 4 + 16/128 + 4/128 = 4.15625 bits/weight;
+  x      2 B * M * K;   y  2 B * M * N.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import wqd_inputs as I
+
+WEIGHT_BITS = {"bf16": 16.0, "fp8": 8.0, "w4a16": 4.0}
+
+
+def weight_bytes(fmt: str, N: int, K: int) -> dict:
+    if fmt == "bf16":
+        return {"w": 2 * N * K, "s": 0, "z": 0}
+    if fmt == "fp8":
+        return {"w": N * K, "s": 4 * N, "z": 0}
+    if fmt == "w4a16":
+        g = N * (K // 128)
+        return {"w": N * K // 2, "s": 2 * g, "z": g // 2}
+    raise ValueError(fmt)
+
+
+def call_bytes(fmt: str, M: int, N: int, K: int) -> int:
+    wb = weight_bytes(fmt, N, K)
+    return wb["w"] + wb["s"] + wb["z"] + 2 * M * K + 2 * M * N
+
+
+def call_flops(M: int, N: int, K: int) -> int:
+    return 2 * M * N * K
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    fmt: str
+    M: int
+    layers: int
+    mats: tuple  # ((name, N, K), ...) per layer
+    outliers: bool
+    cfg: int
+
+    @property
+    def launches(self) -> int:
+        return self.layers * len(self.mats)
+
+    def step_bytes(self) -> int:
+        return self.layers * sum(call_bytes(self.fmt, self.M, N, K) for _, N, K in self.mats)
+
+    def step_flops(self) -> int:
+        return self.layers * sum(call_flops(self.M, N, K) for _, N, K in self.mats)
+
+    def weight_stream_bytes(self) -> int:
+        return self.layers * sum(sum(weight_bytes(self.fmt, N, K).values()) for _, N, K in self.mats)
+
+
+def stack_70b(fmt: str, M: int, layers: int = 80) -> Workload:
+    cfg = 3 if fmt == "fp8" else 4
+    return Workload(f"70b_{fmt}_stack_{layers}l_m{M}", fmt, M, layers, I.LAYER_70B, fmt == "w4a16", cfg)
+
+
+def stack_7b_bf16(M: int = 1, layers: int = 32) -> Workload:
+    return Workload(f"llama2_7b_bf16_stack_{layers}l_m{M}", "bf16", M, layers, I.LAYER_7B, False, 2)
+
+
+def gemv_4096_w4a16() -> Workload:
+    return Workload("w4a16_gemv_4096x4096_m1", "w4a16", 1, 1, (("w", 4096, 4096),), False, 1)
+
+
+def verify_matrix(fmt: str, mat: str, M: int) -> Workload:
+    shapes = {"q": (8192, 8192), "o": (8192, 8192), "gate": (28672, 8192), "up": (28672, 8192),
+              "down": (8192, 28672)}
+    N, K = shapes[mat]
+    return Workload(f"verify_{fmt}_{mat}_m{M}", fmt, M, 1, ((mat, N, K),), True, 5)
+
+
+VERIFY_M = (6, 16, 48, 128, 192, 384, 512, 1024)
