@@ -9,6 +9,13 @@
 namespace wqd {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed data that is read once).
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // float32 -> bfloat16 bits, round to nearest even (finite inputs; subnormals kept).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -43,6 +50,15 @@ template <int T>
 __device__ __forceinline__ bf16x2_t u4x2_to_bf16x2_offset128(uint32_t w) {
   uint32_t v = ((w >> (4 * T)) & 0x000F000Fu) | 0x43004300u;
   return __builtin_bit_cast(bf16x2_t, v);
+}
+
+// (a & mask) | orv in one VOP3 instruction.  Both constants must sit in
+// VGPRs: a gfx9 VOP3 instruction takes no literal and one scalar operand, so
+// left to itself the compiler splits this into v_and + v_or.
+__device__ __forceinline__ uint32_t and_or_v(uint32_t a, uint32_t mask, uint32_t orv) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(mask), "v"(orv));
+  return d;
 }
 
 __device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float c) {

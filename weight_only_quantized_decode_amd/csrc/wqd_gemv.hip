@@ -12,7 +12,10 @@
 //   * each wavefront stages its own x range in a private LDS region (chunked
 //     when it does not fit) and reads it back as 16-byte broadcast reads; no
 //     workgroup barrier is needed until the final reduction;
-//   * weight tiles are loaded a group of 4 tiles ahead of the arithmetic;
+//   * weight tiles stream in groups of 4 with the next group in flight during
+//     the arithmetic; loads are branch-free (clamped at the end of a share)
+//     so the in-order load counter lets the arithmetic wait for exactly the
+//     group it needs; non-temporal loads (every byte is read once per step);
 //   * dequantisation in registers: W4A16 nibble pairs become bf16 (128 + q)
 //     with one AND-OR, FP8 codes become bf16 with the hardware conversion;
 //     v_dot2_f32_bf16 forms exact bf16 x bf16 products summed in float32.
@@ -60,80 +63,117 @@ struct Group {
   uint32_t z;  // W4A16: 4 zero nibbles
 };
 
+// Load one group of 4 tiles of this wavefront's rows: lane l reads its 16
+// bytes of tile t at wbase + t * 64 (uint4 units), t = t0 .. t0 + 3 clamped
+// to the last tile of the share, so every load is issued unconditionally
+// (no branch: the in-order load counter stays exact) and stays in bounds;
+// clamped tiles are never multiplied.  Weights are read once per decode
+// step, so the loads are non-temporal.
 template <int FMT>
-__device__ __forceinline__ void load_group(Group<FMT>& g, const GemvArgs& a, int64_t nb, int64_t kt, int64_t kt_end,
-                                           int lane) {
-  const uint4* p = a.w + (nb * a.KT + kt) * (kTileBytes / 16) + lane;
+__device__ __forceinline__ void load_group(Group<FMT>& g, const uint4* wbase, const uint2* sbase,
+                                           const uint16_t* zbase, int t0, int last) {
 #pragma unroll
-  for (int i = 0; i < kGroupTiles; ++i)
-    if (kt + i < kt_end) g.w[i] = p[i * (kTileBytes / 16)];
+  for (int i = 0; i < kGroupTiles; ++i) g.w[i] = load_nt(wbase + min(t0 + i, last) * (kTileBytes / 16));
   if (FMT == kFmtW4) {
-    const int n = lane & 15;
-    const int64_t q = (nb * a.G4 + kt / kScaleQuad) * kTileRows + n;
-    g.s = reinterpret_cast<const uint2*>(a.scales)[q];
-    g.z = a.zeros[q];
+    const int q = min(t0, last) / kScaleQuad;
+    g.s = sbase[q * kTileRows];
+    g.z = zbase[q * kTileRows];
   }
 }
 
-// One tile for every activation row: acc[m] += row-n slice-kb partial product.
-template <int FMT, int MR, int CT>
-__device__ __forceinline__ void tile_dot(const uint4 w, int i, const Group<FMT>& g, int kb,
-                                         const uint4* __restrict__ xs, const float* __restrict__ xsum, int tl,
-                                         float (&acc)[MR]) {
+// acc[m] += the products of the first NT tiles of a group (NT = 4 on the fast
+// path: no per-tile branches).  One dot2 chain per tile and activation row;
+// dependent VALU instructions issue back to back on CDNA, and other
+// wavefronts fill the LDS wait.  tl0 is the index of the group's first tile
+// inside the staged x chunk.
+template <int FMT, int MR, int CT, int NT>
+__device__ __forceinline__ void group_dot(const Group<FMT>& g, int kb, const uint4* __restrict__ xs,
+                                          const float* __restrict__ xsum, int tl0, float (&acc)[MR]) {
   using C = FmtC<FMT>;
-  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-  const int sl = tl * 4 + kb;  // slice index inside the staged chunk
   if (FMT == kFmtW4) {
-    const uint32_t sbits = (i < 2 ? g.s.x : g.s.y) >> (16 * (i & 1));
-    const float s = __half2float(__ushort_as_half(uint16_t(sbits & 0xFFFFu)));
-    const float zc = 128.0f + float((g.z >> (4 * i)) & 0xFu);
+    const uint32_t mask = 0x000F000Fu, magic = 0x43004300u;
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const uint4* xp = xs + (m * CT * 4 + sl) * C::SLS;
-      float P = 0.f;
+    for (int i = 0; i < NT; ++i) {
+      const uint32_t wd[4] = {g.w[i].x, g.w[i].y, g.w[i].z, g.w[i].w};
+      const int sl = (tl0 + i) * 4 + kb;
+      float P[MR];
+#pragma unroll
+      for (int m = 0; m < MR; ++m) P[m] = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 xv = xp[q];
-        P = dot2_bf16(u4x2_to_bf16x2_offset128<0>(wd[q]), as_bf16x2(xv.x), P);
-        P = dot2_bf16(u4x2_to_bf16x2_offset128<1>(wd[q]), as_bf16x2(xv.y), P);
-        P = dot2_bf16(u4x2_to_bf16x2_offset128<2>(wd[q]), as_bf16x2(xv.z), P);
-        P = dot2_bf16(u4x2_to_bf16x2_offset128<3>(wd[q]), as_bf16x2(xv.w), P);
+        const bf16x2_t b0 = as_bf16x2(and_or_v(wd[q], mask, magic));  // (128 + q) pairs
+        const bf16x2_t b1 = as_bf16x2(and_or_v(wd[q] >> 4, mask, magic));
+        const bf16x2_t b2 = as_bf16x2(and_or_v(wd[q] >> 8, mask, magic));
+        const bf16x2_t b3 = as_bf16x2(and_or_v(wd[q] >> 12, mask, magic));
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          const uint4 xv = xs[(m * CT * 4 + sl) * C::SLS + q];
+          P[m] = dot2_bf16(b0, as_bf16x2(xv.x), P[m]);
+          P[m] = dot2_bf16(b1, as_bf16x2(xv.y), P[m]);
+          P[m] = dot2_bf16(b2, as_bf16x2(xv.z), P[m]);
+          P[m] = dot2_bf16(b3, as_bf16x2(xv.w), P[m]);
+        }
       }
-      const float D = fmaf(-zc, xsum[m * CT * 4 + sl], P);
-      acc[m] = fmaf(s, D, acc[m]);
+      const uint32_t sbits = (i < 2 ? g.s.x : g.s.y) >> (16 * (i & 1));
+      const float s = __half2float(__ushort_as_half(uint16_t(sbits & 0xFFFFu)));
+      const float zc = 128.0f + float((g.z >> (4 * i)) & 0xFu);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const float D = fmaf(-zc, xsum[m * CT * 4 + sl], P[m]);
+        acc[m] = fmaf(s, D, acc[m]);
+      }
     }
   } else if (FMT == kFmtFP8) {
-    const bf16x2_t b0 = e4m3x2_to_bf16x2<false>(wd[0]), b1 = e4m3x2_to_bf16x2<true>(wd[0]);
-    const bf16x2_t b2 = e4m3x2_to_bf16x2<false>(wd[1]), b3 = e4m3x2_to_bf16x2<true>(wd[1]);
-    const bf16x2_t b4 = e4m3x2_to_bf16x2<false>(wd[2]), b5 = e4m3x2_to_bf16x2<true>(wd[2]);
-    const bf16x2_t b6 = e4m3x2_to_bf16x2<false>(wd[3]), b7 = e4m3x2_to_bf16x2<true>(wd[3]);
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const uint4* xp = xs + (m * CT * 4 + sl) * C::SLS;
-      const uint4 x0 = xp[0], x1 = xp[1];
-      float a0 = acc[m];
-      a0 = dot2_bf16(b0, as_bf16x2(x0.x), a0);
-      a0 = dot2_bf16(b1, as_bf16x2(x0.y), a0);
-      a0 = dot2_bf16(b2, as_bf16x2(x0.z), a0);
-      a0 = dot2_bf16(b3, as_bf16x2(x0.w), a0);
-      a0 = dot2_bf16(b4, as_bf16x2(x1.x), a0);
-      a0 = dot2_bf16(b5, as_bf16x2(x1.y), a0);
-      a0 = dot2_bf16(b6, as_bf16x2(x1.z), a0);
-      a0 = dot2_bf16(b7, as_bf16x2(x1.w), a0);
-      acc[m] = a0;
+    for (int i = 0; i < NT; ++i) {
+      const uint32_t wd[4] = {g.w[i].x, g.w[i].y, g.w[i].z, g.w[i].w};
+      const int sl = (tl0 + i) * 4 + kb;
+      bf16x2_t b[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        b[2 * q] = e4m3x2_to_bf16x2<false>(wd[q]);
+        b[2 * q + 1] = e4m3x2_to_bf16x2<true>(wd[q]);
+      }
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const uint4 x0 = xs[(m * CT * 4 + sl) * C::SLS], x1 = xs[(m * CT * 4 + sl) * C::SLS + 1];
+        float a0 = acc[m];
+        a0 = dot2_bf16(b[0], as_bf16x2(x0.x), a0);
+        a0 = dot2_bf16(b[1], as_bf16x2(x0.y), a0);
+        a0 = dot2_bf16(b[2], as_bf16x2(x0.z), a0);
+        a0 = dot2_bf16(b[3], as_bf16x2(x0.w), a0);
+        a0 = dot2_bf16(b[4], as_bf16x2(x1.x), a0);
+        a0 = dot2_bf16(b[5], as_bf16x2(x1.y), a0);
+        a0 = dot2_bf16(b[6], as_bf16x2(x1.z), a0);
+        a0 = dot2_bf16(b[7], as_bf16x2(x1.w), a0);
+        acc[m] = a0;
+      }
     }
   } else {
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const uint4 xv = xs[(m * CT * 4 + sl) * C::SLS];
-      float a0 = acc[m];
-      a0 = dot2_bf16(as_bf16x2(wd[0]), as_bf16x2(xv.x), a0);
-      a0 = dot2_bf16(as_bf16x2(wd[1]), as_bf16x2(xv.y), a0);
-      a0 = dot2_bf16(as_bf16x2(wd[2]), as_bf16x2(xv.z), a0);
-      a0 = dot2_bf16(as_bf16x2(wd[3]), as_bf16x2(xv.w), a0);
-      acc[m] = a0;
+    for (int i = 0; i < NT; ++i) {
+      const int sl = (tl0 + i) * 4 + kb;
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const uint4 xv = xs[(m * CT * 4 + sl) * C::SLS];
+        float a0 = acc[m];
+        a0 = dot2_bf16(as_bf16x2(g.w[i].x), as_bf16x2(xv.x), a0);
+        a0 = dot2_bf16(as_bf16x2(g.w[i].y), as_bf16x2(xv.y), a0);
+        a0 = dot2_bf16(as_bf16x2(g.w[i].z), as_bf16x2(xv.z), a0);
+        a0 = dot2_bf16(as_bf16x2(g.w[i].w), as_bf16x2(xv.w), a0);
+        acc[m] = a0;
+      }
     }
   }
+}
+
+// Tail group with 1..3 tiles.
+template <int FMT, int MR, int CT>
+__device__ __forceinline__ void group_dot_tail(const Group<FMT>& g, int kb, const uint4* __restrict__ xs,
+                                               const float* __restrict__ xsum, int tl0, int n, float (&acc)[MR]) {
+  if (n == 1) group_dot<FMT, MR, CT, 1>(g, kb, xs, xsum, tl0, acc);
+  else if (n == 2) group_dot<FMT, MR, CT, 2>(g, kb, xs, xsum, tl0, acc);
+  else group_dot<FMT, MR, CT, 3>(g, kb, xs, xsum, tl0, acc);
 }
 
 // Stage x for tiles [kt0, kt0 + nt) of this wavefront's share into its LDS
@@ -197,20 +237,36 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a) {
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = 0.f;
 
-  if (kt_begin < kt_end) {
-    Group<FMT> cur, nxt;
-    load_group<FMT>(cur, a, nb, kt_begin, kt_end, lane);
-    for (int64_t c0 = kt_begin; c0 < kt_end; c0 += CT) {
-      const int nt = int(min<int64_t>(CT, kt_end - c0));
-      stage_x<FMT, MR, CT>(a, c0, nt, lane, xs, xsum);
-      for (int g0 = 0; g0 < nt; g0 += kGroupTiles) {
-        const int64_t kt = c0 + g0;
-        if (kt + kGroupTiles < kt_end) load_group<FMT>(nxt, a, nb, kt + kGroupTiles, kt_end, lane);
-#pragma unroll
-        for (int i = 0; i < kGroupTiles; ++i)
-          if (kt + i < kt_end) tile_dot<FMT, MR, CT>(cur.w[i], i, cur, kb, xs, xsum, g0 + i, acc);
-        cur = nxt;
-      }
+  const int total = int(max<int64_t>(0, kt_end - kt_begin));
+  if (total > 0) {
+    // weight, scale and zero streams of this lane
+    const uint4* wbase = a.w + (nb * a.KT + kt_begin) * (kTileBytes / 16) + lane;
+    const int64_t q0 = FMT == kFmtW4 ? (nb * a.G4 + kt_begin / kScaleQuad) * kTileRows + n : 0;
+    const uint2* sbase = reinterpret_cast<const uint2*>(a.scales) + q0;
+    const uint16_t* zbase = a.zeros + q0;
+    int issued = 0;  // first tile of the next group to load
+    auto issue = [&](Group<FMT>& g) {
+      load_group<FMT>(g, wbase, sbase, zbase, issued, total - 1);
+      issued += kGroupTiles;
+    };
+    // One group in flight ahead of the one being multiplied (measured faster
+    // than two on gfx950: fewer registers, more resident wavefronts).  The
+    // buffers alternate by unrolling the loop two ways (no register copies):
+    // step(cur, dst) refills dst, the buffer consumed one step earlier.
+    Group<FMT> g0, g1;
+    int t = 0;  // tiles multiplied so far
+    auto step = [&](Group<FMT>& cur, Group<FMT>& dst) -> bool {
+      if (t >= total) return false;
+      if (t % CT == 0) stage_x<FMT, MR, CT>(a, kt_begin + t, min(CT, total - t), lane, xs, xsum);
+      issue(dst);
+      const int left = total - t;
+      if (left >= kGroupTiles) group_dot<FMT, MR, CT, kGroupTiles>(cur, kb, xs, xsum, t % CT, acc);
+      else group_dot_tail<FMT, MR, CT>(cur, kb, xs, xsum, t % CT, left, acc);
+      t += kGroupTiles;
+      return true;
+    };
+    issue(g0);
+    while (step(g0, g1) && step(g1, g0)) {
     }
   }
 

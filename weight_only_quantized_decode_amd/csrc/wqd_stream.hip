@@ -1,23 +1,33 @@
 // HBM ceiling kernels: a read-only stream (16-byte loads folded into a
 // checksum so the loads cannot be dropped) and a 16-byte copy.  They give the
 // measured bandwidth that the decode kernels are compared against.
+#include "wqd_device.h"
 #include "wqd_internal.h"
 
 namespace wqd {
 
 static constexpr unsigned kStreamBlocks = 2048;  // 8 workgroups per compute unit on 256 CUs
+static constexpr int kUnroll = 8;                // independent 16-byte loads per thread in flight
 
+// Each workgroup reads one contiguous range; per iteration its 256 threads
+// issue 8 loads each (32 KiB of the range, 1 KiB contiguous per wavefront
+// load), all independent, before folding them into the checksum.
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, size_t n16,
                                                           uint32_t* __restrict__ sink) {
   __shared__ uint32_t red[4];
+  const size_t per_block = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t begin = size_t(blockIdx.x) * per_block;
+  const size_t end = begin + per_block < n16 ? begin + per_block : n16;
   uint32_t acc = 0;
-  const size_t stride = size_t(gridDim.x) * 256;
-  size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  size_t i = begin + threadIdx.x;
+  for (; i + (kUnroll - 1) * 256 < end; i += kUnroll * 256) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = load_nt(src + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < end; i += 256) {
     const uint4 a = src[i];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
