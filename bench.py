@@ -4,12 +4,14 @@
 Default workload: the 70B-class decode stack (80 layers x q, k, v, o, gate, up,
 down; hidden 8192, GQA 8 KV heads of 128, FFN 28672) with W4A16-g128 weights,
 M = 1 activation row.  One step = the 560 y = x . dequant(W)^T calls of the
-stack, replayed from one HIP graph; weights (~35.6 GB packed) are resident in
-HBM before timing starts and the stack is far larger than the 256 MB
+stack, replayed from one HIP graph; the packed weights (~35.6 GB) are resident
+in HBM before timing starts, and the stack is far larger than the 256 MB
 last-level cache, so every step streams the weights from HBM.
 
-Prints ONE JSON line.  Other workloads: --workload fp8_70b | bf16_7b |
-gemv4096 | verify:<fmt>:<mat>, with --m for the activation rows.
+Prints ONE JSON line.  Options: --workload w4a16_70b | fp8_70b | bf16_7b |
+gemv4096 | verify:<fmt>:<mat>; --m (activation rows); --fused (q/k/v and
+gate/up concatenated, 4 launches per layer, identical bytes and results);
+--pmc-probe (a short fixed launch sequence for hardware-counter runs).
 """
 from __future__ import annotations
 
@@ -22,6 +24,7 @@ import time
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor peak
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+MAT_INDEX = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "w": 0}
 
 
 def parse():
@@ -32,9 +35,13 @@ def parse():
     ap.add_argument("--workload", default="w4a16_70b")
     ap.add_argument("--m", type=int, default=1)
     ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--fused", action="store_true", help="q/k/v and gate/up as one matrix each")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape timing breakdown")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run 8 x 1 GiB copies and 16 launches of the dominant kernel, then exit")
     return ap.parse_args()
 
 
@@ -43,11 +50,11 @@ def make_workload(args):
 
     w = args.workload
     if w == "w4a16_70b":
-        return WL.stack_70b("w4a16", args.m, args.layers or 80)
+        return WL.stack_70b("w4a16", args.m, args.layers or 80, args.fused)
     if w == "fp8_70b":
-        return WL.stack_70b("fp8", args.m, args.layers or 80)
+        return WL.stack_70b("fp8", args.m, args.layers or 80, args.fused)
     if w == "bf16_7b":
-        return WL.stack_7b_bf16(args.m, args.layers or 32)
+        return WL.stack_7b_bf16(args.m, args.layers or 32, args.fused)
     if w == "gemv4096":
         return WL.gemv_4096_w4a16()
     if w.startswith("verify:"):
@@ -58,6 +65,24 @@ def make_workload(args):
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def weight_for(wl, layer, name, N, K, dev):
+    """The float32 weights of one matrix; fused matrices concatenate their parts'
+    draws, so fused and separate stacks hold identical weights."""
+    import torch
+
+    import wqd_inputs as I
+    from weight_only_quantized_decode_amd import workloads as WL
+
+    if name in WL.FUSED_PARTS:
+        shapes = {n: (Nn, Kn) for n, Nn, Kn in (I.LAYER_70B if K == 8192 else I.LAYER_7B)}
+        parts = [I.w_device(I.stack_seed(wl.cfg, layer, MAT_INDEX[p]), shapes[p][0], K, device=dev)
+                 for p in WL.FUSED_PARTS[name]]
+        W = torch.cat(parts, dim=0)
+        assert W.shape == (N, K)
+        return W
+    return I.w_device(I.stack_seed(wl.cfg, layer, MAT_INDEX[name]), N, K, device=dev)
 
 
 def build_stack(wl):
@@ -72,8 +97,8 @@ def build_stack(wl):
     t0 = time.time()
     for layer in range(wl.layers):
         row = []
-        for mi, (name, N, K) in enumerate(wl.mats):
-            W = I.w_device(I.stack_seed(wl.cfg, layer, mi), N, K, device=dev)
+        for name, N, K in wl.mats:
+            W = weight_for(wl, layer, name, N, K, dev)
             row.append(wqd.pack_weights(wl.fmt, W))
             del W
         packed.append(row)
@@ -124,16 +149,43 @@ def hbm_ceiling(gib=4, reps=10):
     return read, copy
 
 
+def shape_breakdown(wl, packed, xs, ys, ws, stream):
+    """Per-matrix timing: each matrix type launched once per layer (every launch
+    on a different layer's weights, so HBM-cold), timed with events on the
+    launch stream."""
+    import torch
+
+    import weight_only_quantized_decode_amd as wqd
+    from weight_only_quantized_decode_amd import workloads as WL
+
+    out = {}
+    with torch.cuda.stream(stream):
+        for j, (name, N, K) in enumerate(wl.mats):
+            for layer in range(wl.layers):
+                wqd.qgemm(xs[K], packed[layer][j], y=ys[N], workspace=ws)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for layer in range(wl.layers):
+                wqd.qgemm(xs[K], packed[layer][j], y=ys[N], workspace=ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / wl.layers
+            b = WL.call_bytes(wl.fmt, wl.M, N, K)
+            out[name] = {"N": N, "K": K, "us": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1)}
+    return out
+
+
 def cpu_baseline(wl):
     """The oracle (as it stands) on a bounded sample of the same workload, on the host cores."""
-    import numpy as np
-
     import oracle
     import wqd_inputs as I
     from weight_only_quantized_decode_amd import workloads as WL
 
     name, N, K = max(wl.mats, key=lambda m: m[1] * m[2]) if wl.layers == 1 else wl.mats[0]
-    W = I.w_host(I.stack_seed(wl.cfg, 0, 0), N, K)
+    if name in WL.FUSED_PARTS:  # time the first part of a fused matrix (the q matrix)
+        name = WL.FUSED_PARTS[name][0]
+        N = {n: Nn for n, Nn, _ in (I.LAYER_70B if K == 8192 else I.LAYER_7B)}[name]
+    W = I.w_host(I.stack_seed(wl.cfg, 0, MAT_INDEX.get(name, 0)), N, K)
     qw = oracle.quantize(wl.fmt, W)
     x = I.x_bf16_bits(I.x_seed(wl.cfg, wl.M, K), wl.M, K, outliers=wl.outliers)
     reps, t_total = 0, 0.0
@@ -155,10 +207,41 @@ def cpu_baseline(wl):
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{reps} calls of the float64 oracle (exact dequant + matmul + bf16 rounding) on one "
-                  f"{name} matrix {N}x{K} {wl.fmt}, M={wl.M}; {per_call * 1e3:.1f} ms per call; "
-                  f"host {platform.processor() or platform.machine()}, {os.cpu_count()} logical CPUs",
+        "sample": f"{reps} calls of the float64 oracle (exact dequant, matmul, bf16 rounding) on one "
+                  f"{name} matrix {N}x{K} {wl.fmt}, M={wl.M}: {per_call * 1e3:.1f} ms per call; "
+                  f"host {platform.machine()}, {os.cpu_count()} logical CPUs, BLAS threads {threads}",
     }
+
+
+def pmc_probe():
+    """Fixed sequence for counter runs: 8 copies of 1 GiB (known traffic: 1 GiB
+    read + 1 GiB written each), then 16 launches of the W4A16 M=1 kernel on
+    16 different 28672 x 8192 matrices (HBM-cold)."""
+    import torch
+
+    import weight_only_quantized_decode_amd as wqd
+    import wqd_inputs as I
+
+    dev = torch.device("cuda", 0)
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(8):
+        wqd.stream_copy(dst, src)
+    torch.cuda.synchronize()
+    del src, dst
+    N, K = 28672, 8192
+    pws = []
+    for i in range(16):
+        W = I.w_device(900 + i, N, K, device=dev)
+        pws.append(wqd.pack_weights("w4a16", W))
+        del W
+    x = I.x_bf16(1, 1, K).to(dev)
+    y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    for pw in pws:
+        wqd.qgemm(x, pw, y=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_probe": "done", "copy_bytes_each": 2 << 30, "gemv_launches": 16, "N": N, "K": K}))
 
 
 def main():
@@ -171,12 +254,14 @@ def main():
     import torch
 
     import weight_only_quantized_decode_amd as wqd
-    from weight_only_quantized_decode_amd import workloads as WL
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     wqd.lib()
+    if args.pmc_probe:
+        pmc_probe()
+        return
     wl = make_workload(args)
     log(f"[bench] workload {wl.name}: {wl.launches} launches/step, {wl.step_bytes() / 1e9:.3f} GB/step")
     ceiling = (None, None) if args.no_ceiling else hbm_ceiling()
@@ -203,6 +288,7 @@ def main():
         for _ in range(args.warmup):
             run()
         torch.cuda.synchronize()
+        log(f"[bench] timing {args.steps} steps")
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
@@ -215,6 +301,8 @@ def main():
     per_launch_bytes = step_bytes / wl.launches
     avg_launch_us = ms * 1e3 / wl.launches
     achieved = per_launch_bytes / (avg_launch_us / 1e6) / 1e9
+    shapes = None if args.no_shapes else shape_breakdown(wl, packed, xs, ys, ws, stream)
+    mr = min(wl.M, 8)
     out = {
         "metric": "weight-stream GB/s (% of HBM peak) & us per layer-stack step, 70B W4A16/FP8/BF16",
         "value": round(gbps, 2),
@@ -230,7 +318,7 @@ def main():
         "dtype": {"w4a16": "u4+bf16", "fp8": "e4m3+bf16", "bf16": "bf16"}[wl.fmt],
         "data": "synthetic",
         "config": {"workload": wl.name, "fmt": wl.fmt, "M": wl.M, "layers": wl.layers,
-                   "launches_per_step": wl.launches, "graph": graph is not None,
+                   "launches_per_step": wl.launches, "graph": graph is not None, "fused": args.fused,
                    "algorithmic_bytes_per_step": step_bytes},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "hbm_read_ceiling_GBps": None if ceiling[0] is None else round(ceiling[0], 1),
@@ -238,9 +326,12 @@ def main():
         "pct_measured_read_ceiling": None if ceiling[0] is None else round(100 * gbps / ceiling[0], 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": f"gemv_kernel<{wl.fmt}, M={min(wl.M, 8)}>",
-                     "avg_launch_us": round(avg_launch_us, 3)},
+                     "kernel": f"gemv_kernel<{wl.fmt}, M={mr}> (every launch of the timed step)",
+                     "avg_launch_us": round(avg_launch_us, 3),
+                     "bytes_per_launch": round(per_launch_bytes)},
     }
+    if shapes is not None:
+        out["shapes"] = shapes
     if wl.M >= 16:
         tflops = wl.step_flops() / (ms / 1e3) / 1e12
         out["mfma_util_pct"] = round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2)

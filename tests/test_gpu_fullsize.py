@@ -1,0 +1,81 @@
+"""GPU parity at the full sizes of the decode workloads, in the launch plans the
+benchmark uses.  The weights are drawn on the device; the oracle quantises and
+multiplies a sample of output channels (every format is row-local: a row's
+codes depend only on that row), so it checks those outputs one by one.
+
+Workloads (hidden 8192, GQA 8 KV heads x 128, FFN 28672 for the 70B-class
+layer; Llama-2-7B for the BF16 stack):
+  * W4A16-g128 GEMV 4096 x 4096, M = 1 (all 4096 outputs checked);
+  * 7B BF16 layer shapes, M = 1;
+  * 70B FP8-E4M3 layer shapes, M = 1, 8, 32;
+  * 70B W4A16 layer shapes with 6 outlier hidden channels at 20x, M = 1, 4, 16, 32;
+  * speculative-verify widths M = batch x (k + 1) on q / gate / down shapes in
+    W4A16 and BF16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_quantized_decode_amd as wqd
+import wqd_inputs as I
+from tests.parity import bf16_bits, compare_y
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+N_SAMPLE = 40
+
+
+def sample_rows(N, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(N, size=min(N, N_SAMPLE - 4), replace=False).tolist())
+    rows |= {0, 15, N - 16, N - 1}  # first / last 16-row blocks
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+def run_case(fmt, N, K, Ms, seed, outliers, full=False):
+    W = I.w_device(seed, N, K, device=DEV)
+    pw = wqd.pack_weights(fmt, W)
+    rows = np.arange(N) if full else sample_rows(N, seed)
+    W_rows = W[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    del W
+    qw = oracle.quantize(fmt, W_rows)
+    # dequantised weights of the sampled rows, bit for bit
+    Wd = wqd.dequant(pw)
+    Wd_rows = Wd[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    del Wd
+    assert np.array_equal(Wd_rows.view(np.uint32), oracle.dequant_f32(qw).view(np.uint32)), (fmt, N, K)
+    for M in Ms:
+        print(f"fullsize {fmt} N={N} K={K} M={M}", flush=True)
+        x = I.x_bf16_bits(I.x_seed(0, M, K), M, K, outliers=outliers)
+        xd = torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+        y = wqd.qgemm(xd, pw)
+        torch.cuda.synchronize()
+        yb = bf16_bits(y)[:, rows]
+        compare_y(yb, oracle.qgemm_exact(x, qw), f"{fmt} N={N} K={K} M={M}")
+
+
+def test_w4a16_gemv_4096_all_outputs():
+    run_case("w4a16", 4096, 4096, [1], 101, outliers=False, full=True)
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (11008, 4096), (4096, 11008)])
+def test_llama7b_bf16_shapes(N, K):
+    run_case("bf16", N, K, [1], 200 + N % 97, outliers=False)
+
+
+@pytest.mark.parametrize("N,K", [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)])
+def test_70b_fp8_shapes(N, K):
+    run_case("fp8", N, K, [1, 8, 32], 300 + N % 97 + K % 89, outliers=False)
+
+
+@pytest.mark.parametrize("N,K", [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)])
+def test_70b_w4a16_shapes_with_outliers(N, K):
+    run_case("w4a16", N, K, [1, 4, 16, 32], 400 + N % 97 + K % 89, outliers=True)
+
+
+@pytest.mark.parametrize("fmt", ["w4a16", "bf16"])
+@pytest.mark.parametrize("N,K", [(8192, 8192), (28672, 8192), (8192, 28672)])
+def test_verify_widths(fmt, N, K):
+    run_case(fmt, N, K, [6, 16, 48, 128, 1024], 500 + N % 97 + K % 89, outliers=True)

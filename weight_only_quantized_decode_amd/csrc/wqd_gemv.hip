@@ -6,16 +6,20 @@
 //   * one workgroup owns one 16-row block over ALL of K, so no partial sums
 //     ever leave the workgroup: no split-K workspace and no device-scope
 //     fences (on a multi-XCD part those write back and invalidate L2);
-//   * its W wavefronts take contiguous quarter (or eighth) shares of K.  Lane
-//     l = 16 kb + n of a wavefront owns slice kb of row n of every tile in its
-//     share: one 16-byte load per lane, 1 KiB contiguous per wavefront;
+//   * its W wavefronts take contiguous shares of K.  Lane l = 16 kb + n of a
+//     wavefront owns slice kb of row n of every tile in its share: one
+//     16-byte load per lane, 1 KiB contiguous per wavefront;
 //   * each wavefront stages its own x range in a private LDS region (chunked
 //     when it does not fit) and reads it back as 16-byte broadcast reads; no
-//     workgroup barrier is needed until the final reduction;
-//   * weight tiles stream in groups of 4 with the next group in flight during
-//     the arithmetic; loads are branch-free (clamped at the end of a share)
-//     so the in-order load counter lets the arithmetic wait for exactly the
-//     group it needs; non-temporal loads (every byte is read once per step);
+//     workgroup barrier is needed until the final reduction.  The x loads are
+//     issued ahead of the first two weight groups, so the start-up costs one
+//     memory round trip, not two;
+//   * weight tiles stream in groups of GT (4 or 8) with the next group in
+//     flight during the arithmetic: the bytes in flight per compute unit are
+//     what sets the bandwidth (Little's law).  Loads are branch-free (clamped
+//     at the end of a share) so the in-order load counter lets the arithmetic
+//     wait for exactly the group it needs; they are non-temporal (every byte
+//     is read once per step);
 //   * dequantisation in registers: W4A16 nibble pairs become bf16 (128 + q)
 //     with one AND-OR, FP8 codes become bf16 with the hardware conversion;
 //     v_dot2_f32_bf16 forms exact bf16 x bf16 products summed in float32.
@@ -47,169 +51,178 @@ struct FmtC {
   static constexpr int SLS = SLU + (FMT == kFmtW4 ? 1 : 0);  // padded LDS stride: spreads the 4 slices over banks
 };
 
-constexpr int kGroupTiles = 4;  // tiles per prefetch group (= one W4A16 scale quad)
-
-// Tiles of x one wavefront stages per chunk: about 4 KiB of x, whole groups.
+// x staged per wavefront and chunk: about 4 KiB (2048 k per activation row
+// at M = 1).  Tiles per group: 8 for BF16 when the chunk holds 8 tiles (its
+// arithmetic per byte is light, so more bytes in flight pay), else 4 (a
+// W4A16 scale quad; W4A16 and FP8 measured faster with the smaller register
+// footprint).  Tiles per chunk: a whole number of groups.  SPL: x slices each
+// lane stages per chunk.
 template <int FMT, int MR>
-constexpr int chunk_tiles() {
-  constexpr int t = 2048 / (MR * FmtC<FMT>::TK) / kGroupTiles * kGroupTiles;
-  return t < kGroupTiles ? kGroupTiles : t;
-}
-
-template <int FMT>
-struct Group {
-  uint4 w[kGroupTiles];
-  uint2 s;     // W4A16: 4 fp16 scales (one per tile of the group)
-  uint32_t z;  // W4A16: 4 zero nibbles
+struct Plan {
+  static constexpr int raw = 2048 / (MR * FmtC<FMT>::TK);
+  static constexpr int GT = (FMT == kFmtBF16 && raw >= 8) ? 8 : 4;
+  static constexpr int CT = raw / GT * GT < GT ? GT : raw / GT * GT;
+  static constexpr int SPL = (MR * CT * 4 + 63) / 64;
 };
 
-// Load one group of 4 tiles of this wavefront's rows: lane l reads its 16
-// bytes of tile t at wbase + t * 64 (uint4 units), t = t0 .. t0 + 3 clamped
-// to the last tile of the share, so every load is issued unconditionally
-// (no branch: the in-order load counter stays exact) and stays in bounds;
-// clamped tiles are never multiplied.  Weights are read once per decode
-// step, so the loads are non-temporal.
-template <int FMT>
-__device__ __forceinline__ void load_group(Group<FMT>& g, const uint4* wbase, const uint2* sbase,
+template <int FMT, int GT>
+struct Group {
+  uint4 w[GT];
+  uint2 s[GT / 4];     // W4A16: fp16 scales, 4 tiles per quad
+  uint32_t z[GT / 4];  // W4A16: 4 zero nibbles per quad
+};
+
+// Load one group of GT tiles of this wavefront's rows: lane l reads its 16
+// bytes of tile t at wbase + t * 64 (uint4 units), t = t0 .. t0 + GT - 1
+// clamped to the last tile of the share, so every load is issued
+// unconditionally (no branch: the in-order load counter stays exact) and
+// stays in bounds; clamped tiles are never multiplied.  Non-temporal: weights
+// are read once per decode step.
+template <int FMT, int GT>
+__device__ __forceinline__ void load_group(Group<FMT, GT>& g, const uint4* wbase, const uint2* sbase,
                                            const uint16_t* zbase, int t0, int last) {
 #pragma unroll
-  for (int i = 0; i < kGroupTiles; ++i) g.w[i] = load_nt(wbase + min(t0 + i, last) * (kTileBytes / 16));
+  for (int i = 0; i < GT; ++i) g.w[i] = load_nt(wbase + min(t0 + i, last) * (kTileBytes / 16));
   if (FMT == kFmtW4) {
-    const int q = min(t0, last) / kScaleQuad;
-    g.s = sbase[q * kTileRows];
-    g.z = zbase[q * kTileRows];
+#pragma unroll
+    for (int j = 0; j < GT / 4; ++j) {
+      const int q = min(t0 + 4 * j, last) / kScaleQuad;
+      g.s[j] = sbase[q * kTileRows];
+      g.z[j] = zbase[q * kTileRows];
+    }
   }
 }
 
-// acc[m] += the products of the first NT tiles of a group (NT = 4 on the fast
-// path: no per-tile branches).  One dot2 chain per tile and activation row;
-// dependent VALU instructions issue back to back on CDNA, and other
-// wavefronts fill the LDS wait.  tl0 is the index of the group's first tile
-// inside the staged x chunk.
-template <int FMT, int MR, int CT, int NT>
-__device__ __forceinline__ void group_dot(const Group<FMT>& g, int kb, const uint4* __restrict__ xs,
-                                          const float* __restrict__ xsum, int tl0, float (&acc)[MR]) {
+// acc[m] += the products of tile i of a group for every activation row.  One
+// dot2 chain per tile and row: dependent VALU instructions issue back to back
+// on CDNA and other wavefronts fill the LDS wait.  sl = slice index of this
+// lane's part of the tile inside the staged x chunk.
+template <int FMT, int MR, int CT, int GT>
+__device__ __forceinline__ void tile_dot(const Group<FMT, GT>& g, int i, int sl, const uint4* __restrict__ xs,
+                                         const float* __restrict__ xsum, float (&acc)[MR]) {
   using C = FmtC<FMT>;
+  const uint32_t wd[4] = {g.w[i].x, g.w[i].y, g.w[i].z, g.w[i].w};
   if (FMT == kFmtW4) {
     const uint32_t mask = 0x000F000Fu, magic = 0x43004300u;
+    float P[MR];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const uint32_t wd[4] = {g.w[i].x, g.w[i].y, g.w[i].z, g.w[i].w};
-      const int sl = (tl0 + i) * 4 + kb;
-      float P[MR];
+    for (int m = 0; m < MR; ++m) P[m] = 0.f;
 #pragma unroll
-      for (int m = 0; m < MR; ++m) P[m] = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x2_t b0 = as_bf16x2(and_or_v(wd[q], mask, magic));  // (128 + q) pairs
-        const bf16x2_t b1 = as_bf16x2(and_or_v(wd[q] >> 4, mask, magic));
-        const bf16x2_t b2 = as_bf16x2(and_or_v(wd[q] >> 8, mask, magic));
-        const bf16x2_t b3 = as_bf16x2(and_or_v(wd[q] >> 12, mask, magic));
-#pragma unroll
-        for (int m = 0; m < MR; ++m) {
-          const uint4 xv = xs[(m * CT * 4 + sl) * C::SLS + q];
-          P[m] = dot2_bf16(b0, as_bf16x2(xv.x), P[m]);
-          P[m] = dot2_bf16(b1, as_bf16x2(xv.y), P[m]);
-          P[m] = dot2_bf16(b2, as_bf16x2(xv.z), P[m]);
-          P[m] = dot2_bf16(b3, as_bf16x2(xv.w), P[m]);
-        }
-      }
-      const uint32_t sbits = (i < 2 ? g.s.x : g.s.y) >> (16 * (i & 1));
-      const float s = __half2float(__ushort_as_half(uint16_t(sbits & 0xFFFFu)));
-      const float zc = 128.0f + float((g.z >> (4 * i)) & 0xFu);
+    for (int q = 0; q < 4; ++q) {
+      const bf16x2_t b0 = as_bf16x2(and_or_v(wd[q], mask, magic));  // (128 + q) pairs
+      const bf16x2_t b1 = as_bf16x2(and_or_v(wd[q] >> 4, mask, magic));
+      const bf16x2_t b2 = as_bf16x2(and_or_v(wd[q] >> 8, mask, magic));
+      const bf16x2_t b3 = as_bf16x2(and_or_v(wd[q] >> 12, mask, magic));
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        const float D = fmaf(-zc, xsum[m * CT * 4 + sl], P[m]);
-        acc[m] = fmaf(s, D, acc[m]);
+        const uint4 xv = xs[(m * CT * 4 + sl) * C::SLS + q];
+        P[m] = dot2_bf16(b0, as_bf16x2(xv.x), P[m]);
+        P[m] = dot2_bf16(b1, as_bf16x2(xv.y), P[m]);
+        P[m] = dot2_bf16(b2, as_bf16x2(xv.z), P[m]);
+        P[m] = dot2_bf16(b3, as_bf16x2(xv.w), P[m]);
       }
     }
+    const uint2 sq = g.s[i / 4];
+    const uint32_t sbits = ((i & 3) < 2 ? sq.x : sq.y) >> (16 * (i & 1));
+    const float s = __half2float(__ushort_as_half(uint16_t(sbits & 0xFFFFu)));
+    const float zc = 128.0f + float((g.z[i / 4] >> (4 * (i & 3))) & 0xFu);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float D = fmaf(-zc, xsum[m * CT * 4 + sl], P[m]);
+      acc[m] = fmaf(s, D, acc[m]);
+    }
   } else if (FMT == kFmtFP8) {
+    bf16x2_t b[8];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const uint32_t wd[4] = {g.w[i].x, g.w[i].y, g.w[i].z, g.w[i].w};
-      const int sl = (tl0 + i) * 4 + kb;
-      bf16x2_t b[8];
+    for (int q = 0; q < 4; ++q) {
+      b[2 * q] = e4m3x2_to_bf16x2<false>(wd[q]);
+      b[2 * q + 1] = e4m3x2_to_bf16x2<true>(wd[q]);
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        b[2 * q] = e4m3x2_to_bf16x2<false>(wd[q]);
-        b[2 * q + 1] = e4m3x2_to_bf16x2<true>(wd[q]);
-      }
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        const uint4 x0 = xs[(m * CT * 4 + sl) * C::SLS], x1 = xs[(m * CT * 4 + sl) * C::SLS + 1];
-        float a0 = acc[m];
-        a0 = dot2_bf16(b[0], as_bf16x2(x0.x), a0);
-        a0 = dot2_bf16(b[1], as_bf16x2(x0.y), a0);
-        a0 = dot2_bf16(b[2], as_bf16x2(x0.z), a0);
-        a0 = dot2_bf16(b[3], as_bf16x2(x0.w), a0);
-        a0 = dot2_bf16(b[4], as_bf16x2(x1.x), a0);
-        a0 = dot2_bf16(b[5], as_bf16x2(x1.y), a0);
-        a0 = dot2_bf16(b[6], as_bf16x2(x1.z), a0);
-        a0 = dot2_bf16(b[7], as_bf16x2(x1.w), a0);
-        acc[m] = a0;
-      }
+    for (int m = 0; m < MR; ++m) {
+      const uint4 x0 = xs[(m * CT * 4 + sl) * C::SLS], x1 = xs[(m * CT * 4 + sl) * C::SLS + 1];
+      float a0 = acc[m];
+      a0 = dot2_bf16(b[0], as_bf16x2(x0.x), a0);
+      a0 = dot2_bf16(b[1], as_bf16x2(x0.y), a0);
+      a0 = dot2_bf16(b[2], as_bf16x2(x0.z), a0);
+      a0 = dot2_bf16(b[3], as_bf16x2(x0.w), a0);
+      a0 = dot2_bf16(b[4], as_bf16x2(x1.x), a0);
+      a0 = dot2_bf16(b[5], as_bf16x2(x1.y), a0);
+      a0 = dot2_bf16(b[6], as_bf16x2(x1.z), a0);
+      a0 = dot2_bf16(b[7], as_bf16x2(x1.w), a0);
+      acc[m] = a0;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int sl = (tl0 + i) * 4 + kb;
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        const uint4 xv = xs[(m * CT * 4 + sl) * C::SLS];
-        float a0 = acc[m];
-        a0 = dot2_bf16(as_bf16x2(g.w[i].x), as_bf16x2(xv.x), a0);
-        a0 = dot2_bf16(as_bf16x2(g.w[i].y), as_bf16x2(xv.y), a0);
-        a0 = dot2_bf16(as_bf16x2(g.w[i].z), as_bf16x2(xv.z), a0);
-        a0 = dot2_bf16(as_bf16x2(g.w[i].w), as_bf16x2(xv.w), a0);
-        acc[m] = a0;
-      }
+    for (int m = 0; m < MR; ++m) {
+      const uint4 xv = xs[(m * CT * 4 + sl) * C::SLS];
+      float a0 = acc[m];
+      a0 = dot2_bf16(as_bf16x2(wd[0]), as_bf16x2(xv.x), a0);
+      a0 = dot2_bf16(as_bf16x2(wd[1]), as_bf16x2(xv.y), a0);
+      a0 = dot2_bf16(as_bf16x2(wd[2]), as_bf16x2(xv.z), a0);
+      a0 = dot2_bf16(as_bf16x2(wd[3]), as_bf16x2(xv.w), a0);
+      acc[m] = a0;
     }
   }
 }
 
-// Tail group with 1..3 tiles.
+// Staging of x for tiles [kt0, kt0 + nt) of this wavefront's share, in two
+// halves: load_x issues the global loads into registers, commit_x writes
+// them to the wavefront's LDS region (and, for W4A16, the per-slice x sums).
+// Weight loads issued between the two halves stay in flight: loads complete
+// in issue order, so commit_x waits for x alone.  The region is private to
+// the wavefront and LDS operations of one wavefront complete in order, so
+// only compiler ordering is needed around it.
 template <int FMT, int MR, int CT>
-__device__ __forceinline__ void group_dot_tail(const Group<FMT>& g, int kb, const uint4* __restrict__ xs,
-                                               const float* __restrict__ xsum, int tl0, int n, float (&acc)[MR]) {
-  if (n == 1) group_dot<FMT, MR, CT, 1>(g, kb, xs, xsum, tl0, acc);
-  else if (n == 2) group_dot<FMT, MR, CT, 2>(g, kb, xs, xsum, tl0, acc);
-  else group_dot<FMT, MR, CT, 3>(g, kb, xs, xsum, tl0, acc);
+struct XStage {
+  uint4 v[Plan<FMT, MR>::SPL][FmtC<FMT>::SLU];
+};
+
+template <int FMT, int MR, int CT>
+__device__ __forceinline__ void load_x(XStage<FMT, MR, CT>& xr, const GemvArgs& a, int64_t kt0, int nt, int lane) {
+  using C = FmtC<FMT>;
+  const int per_m = nt * 4;  // slices per activation row in this chunk
+#pragma unroll
+  for (int j = 0; j < Plan<FMT, MR>::SPL; ++j) {
+    const int i = lane + 64 * j;
+    const int m = i / per_m, sl = i - m * per_m;
+    const int64_t k = (kt0 + sl / 4) * C::TK + (sl & 3) * C::SLK;
+#pragma unroll
+    for (int u = 0; u < C::SLU; ++u) {
+      xr.v[j][u] = make_uint4(0, 0, 0, 0);
+      if (i < MR * per_m && k + 8 * u < a.K)
+        xr.v[j][u] = *reinterpret_cast<const uint4*>(a.x + int64_t(m) * a.K + k + 8 * u);
+    }
+  }
 }
 
-// Stage x for tiles [kt0, kt0 + nt) of this wavefront's share into its LDS
-// region; W4A16 also gets the per-slice x sums.  Wavefront-private: LDS
-// operations of one wavefront complete in order, so only compiler ordering
-// is needed around it.
 template <int FMT, int MR, int CT>
-__device__ __forceinline__ void stage_x(const GemvArgs& a, int64_t kt0, int nt, int lane, uint4* __restrict__ xs,
-                                        float* __restrict__ xsum) {
+__device__ __forceinline__ void commit_x(const XStage<FMT, MR, CT>& xr, int nt, int lane, uint4* __restrict__ xs,
+                                         float* __restrict__ xsum) {
   using C = FmtC<FMT>;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const int per_m = nt * 4;  // slices per activation row in this chunk
-  for (int i = lane; i < MR * per_m; i += 64) {
-    const int m = i / per_m, sl = i - m * per_m;
-    const int64_t k = (kt0 + sl / 4) * C::TK + (sl & 3) * C::SLK;
-    uint4 v[C::SLU];
+  const int per_m = nt * 4;
 #pragma unroll
-    for (int u = 0; u < C::SLU; ++u) {
-      v[u] = make_uint4(0, 0, 0, 0);
-      if (k + 8 * u < a.K) v[u] = *reinterpret_cast<const uint4*>(a.x + int64_t(m) * a.K + k + 8 * u);
-    }
-    uint4* dst = xs + (m * CT * 4 + sl) * C::SLS;
+  for (int j = 0; j < Plan<FMT, MR>::SPL; ++j) {
+    const int i = lane + 64 * j;
+    if (i < MR * per_m) {
+      const int m = i / per_m, sl = i - m * per_m;
+      uint4* dst = xs + (m * CT * 4 + sl) * C::SLS;
 #pragma unroll
-    for (int u = 0; u < C::SLU; ++u) dst[u] = v[u];
-    if (FMT == kFmtW4) {
-      const bf16x2_t ones = as_bf16x2(0x3F803F80u);
-      float X = 0.f;
+      for (int u = 0; u < C::SLU; ++u) dst[u] = xr.v[j][u];
+      if (FMT == kFmtW4) {
+        const bf16x2_t ones = as_bf16x2(0x3F803F80u);
+        float X = 0.f;
 #pragma unroll
-      for (int u = 0; u < C::SLU; ++u) {
-        X = dot2_bf16(ones, as_bf16x2(v[u].x), X);
-        X = dot2_bf16(ones, as_bf16x2(v[u].y), X);
-        X = dot2_bf16(ones, as_bf16x2(v[u].z), X);
-        X = dot2_bf16(ones, as_bf16x2(v[u].w), X);
+        for (int u = 0; u < C::SLU; ++u) {
+          X = dot2_bf16(ones, as_bf16x2(xr.v[j][u].x), X);
+          X = dot2_bf16(ones, as_bf16x2(xr.v[j][u].y), X);
+          X = dot2_bf16(ones, as_bf16x2(xr.v[j][u].z), X);
+          X = dot2_bf16(ones, as_bf16x2(xr.v[j][u].w), X);
+        }
+        xsum[m * CT * 4 + sl] = X;
       }
-      xsum[m * CT * 4 + sl] = X;
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -219,7 +232,8 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, int64_t kt0, int nt, 
 template <int FMT, int MR, int W>
 __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a) {
   using C = FmtC<FMT>;
-  constexpr int CT = chunk_tiles<FMT, MR>();
+  constexpr int GT = Plan<FMT, MR>::GT;
+  constexpr int CT = Plan<FMT, MR>::CT;
   __shared__ uint4 s_x[W][MR * CT * 4 * C::SLS];
   __shared__ float s_xsum[W][FMT == kFmtW4 ? MR * CT * 4 : 1];
   __shared__ float s_red[W][MR][kTileRows];
@@ -227,7 +241,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, kb = lane >> 4, n = lane & 15;
   const int64_t nb = blockIdx.x;
   // contiguous share of K tiles for this wavefront, in whole groups
-  const int64_t per_wave = (a.KT + int64_t(W) * kGroupTiles - 1) / (int64_t(W) * kGroupTiles) * kGroupTiles;
+  const int64_t per_wave = (a.KT + int64_t(W) * GT - 1) / (int64_t(W) * GT) * GT;
   const int64_t kt_begin = wave * per_wave;
   const int64_t kt_end = min(a.KT, kt_begin + per_wave);
   uint4* xs = s_x[wave];
@@ -245,26 +259,39 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a) {
     const uint2* sbase = reinterpret_cast<const uint2*>(a.scales) + q0;
     const uint16_t* zbase = a.zeros + q0;
     int issued = 0;  // first tile of the next group to load
-    auto issue = [&](Group<FMT>& g) {
-      load_group<FMT>(g, wbase, sbase, zbase, issued, total - 1);
-      issued += kGroupTiles;
+    auto issue = [&](Group<FMT, GT>& g) {
+      load_group<FMT, GT>(g, wbase, sbase, zbase, issued, total - 1);
+      issued += GT;
     };
-    // One group in flight ahead of the one being multiplied (measured faster
-    // than two on gfx950: fewer registers, more resident wavefronts).  The
+    // One group in flight ahead of the one being multiplied.  The two
     // buffers alternate by unrolling the loop two ways (no register copies):
-    // step(cur, dst) refills dst, the buffer consumed one step earlier.
-    Group<FMT> g0, g1;
+    // step(cur, dst) refills dst, the buffer consumed one step earlier.  At a
+    // chunk boundary the x loads go out before dst's weight loads, so the
+    // first step has x, group 0 and group 1 in flight together.
+    Group<FMT, GT> g0, g1;
+    XStage<FMT, MR, CT> xr;
     int t = 0;  // tiles multiplied so far
-    auto step = [&](Group<FMT>& cur, Group<FMT>& dst) -> bool {
+    auto step = [&](Group<FMT, GT>& cur, Group<FMT, GT>& dst) -> bool {
       if (t >= total) return false;
-      if (t % CT == 0) stage_x<FMT, MR, CT>(a, kt_begin + t, min(CT, total - t), lane, xs, xsum);
+      const bool stage = t % CT == 0;
+      const int nt = min(CT, total - t);
+      if (stage && t > 0) load_x<FMT, MR, CT>(xr, a, kt_begin + t, nt, lane);
       issue(dst);
+      if (stage) commit_x<FMT, MR, CT>(xr, nt, lane, xs, xsum);
       const int left = total - t;
-      if (left >= kGroupTiles) group_dot<FMT, MR, CT, kGroupTiles>(cur, kb, xs, xsum, t % CT, acc);
-      else group_dot_tail<FMT, MR, CT>(cur, kb, xs, xsum, t % CT, left, acc);
-      t += kGroupTiles;
+      const int tl0 = t % CT;
+      if (left >= GT) {
+#pragma unroll
+        for (int i = 0; i < GT; ++i) tile_dot<FMT, MR, CT, GT>(cur, i, (tl0 + i) * 4 + kb, xs, xsum, acc);
+      } else {
+#pragma unroll
+        for (int i = 0; i < GT; ++i)
+          if (i < left) tile_dot<FMT, MR, CT, GT>(cur, i, (tl0 + i) * 4 + kb, xs, xsum, acc);
+      }
+      t += GT;
       return true;
     };
+    load_x<FMT, MR, CT>(xr, a, kt_begin, min(CT, total), lane);
     issue(g0);
     while (step(g0, g1) && step(g1, g0)) {
     }

@@ -61,13 +61,39 @@ class Workload:
         return self.layers * sum(sum(weight_bytes(self.fmt, N, K).values()) for _, N, K in self.mats)
 
 
-def stack_70b(fmt: str, M: int, layers: int = 80) -> Workload:
+def fuse_layer(mats) -> tuple:
+    """q/k/v and gate/up concatenated along N (they share their input x).
+
+    Row-concatenation leaves every row's codes, scales and zero points
+    unchanged (all three formats quantise row-locally), so a fused matrix
+    holds exactly the bytes of its parts and computes their outputs side by
+    side, in one launch instead of several.
+    """
+    d = {name: (N, K) for name, N, K in mats}
+    out = []
+    if all(n in d for n in ("q", "k", "v")):
+        out.append(("qkv", d["q"][0] + d["k"][0] + d["v"][0], d["q"][1]))
+    out.append(("o", *d["o"]))
+    if "gate" in d and "up" in d:
+        out.append(("gate_up", d["gate"][0] + d["up"][0], d["gate"][1]))
+    out.append(("down", *d["down"]))
+    return tuple(out)
+
+
+FUSED_PARTS = {"qkv": ("q", "k", "v"), "gate_up": ("gate", "up")}
+
+
+def stack_70b(fmt: str, M: int, layers: int = 80, fused: bool = False) -> Workload:
     cfg = 3 if fmt == "fp8" else 4
-    return Workload(f"70b_{fmt}_stack_{layers}l_m{M}", fmt, M, layers, I.LAYER_70B, fmt == "w4a16", cfg)
+    mats = fuse_layer(I.LAYER_70B) if fused else I.LAYER_70B
+    tag = "_fused" if fused else ""
+    return Workload(f"70b_{fmt}_stack_{layers}l_m{M}{tag}", fmt, M, layers, mats, fmt == "w4a16", cfg)
 
 
-def stack_7b_bf16(M: int = 1, layers: int = 32) -> Workload:
-    return Workload(f"llama2_7b_bf16_stack_{layers}l_m{M}", "bf16", M, layers, I.LAYER_7B, False, 2)
+def stack_7b_bf16(M: int = 1, layers: int = 32, fused: bool = False) -> Workload:
+    mats = fuse_layer(I.LAYER_7B) if fused else I.LAYER_7B
+    tag = "_fused" if fused else ""
+    return Workload(f"llama2_7b_bf16_stack_{layers}l_m{M}{tag}", "bf16", M, layers, mats, False, 2)
 
 
 def gemv_4096_w4a16() -> Workload:
