@@ -82,8 +82,12 @@ def test_packed_sizes_errors():
 
 def test_workspace_query():
     for fmt in ("bf16", "fp8", "w4a16"):
-        for M in (1, 4, 8, 16, 1024):
-            assert wqd.workspace_bytes(fmt, M, 8192, 8192) == 0
+        for M in (1, 4, 8):
+            assert wqd.workspace_bytes(fmt, M, 8192, 8192) == 0  # streaming kernel: none
+        # matrix-core path: split-K partials only when the tile grid is small
+        assert wqd.workspace_bytes(fmt, 1024, 28672, 8192) == 0
+        ws = wqd.workspace_bytes(fmt, 16, 8192, 8192)
+        assert ws > 0 and ws % (16 * 8192 * 4) == 0
     L = wqd.lib()
     assert L.wqd_workspace_bytes(2, 1, 64, 128, None) == E_ARG
     b = ctypes.c_size_t()
@@ -113,6 +117,9 @@ def test_qgemm_rejects_bad_arguments_before_enqueue():
     assert call(w=A + 8) == E_ALIGN
     assert call(fmt=1, K=12) == E_SHAPE
     assert wqd.workspace_bytes("w4a16", 1, 64 * 200, 128 * 64) == 0
+    need = wqd.workspace_bytes("w4a16", 16, 8192, 8192)
+    assert call(M=16, N=8192, K=8192, ws=None) == E_WS
+    assert call(M=16, N=8192, K=8192, wsb=need - 1) == E_WS
 
 
 def test_other_entry_points_reject_bad_arguments():

@@ -96,7 +96,13 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const voi
     if (!workspace || workspace_bytes < need) return WQD_E_WORKSPACE;
     if (!wqd::aligned16(workspace)) return WQD_E_ALIGN;
   }
-  return hip_status(wqd::launch_gemv(fmt, plan, x, M, N, K, w_packed, scales, zeros, y, as_stream(stream)));
+  if (M <= wqd::kGemvMaxM)
+    return hip_status(wqd::launch_gemv(fmt, plan, x, M, N, K, w_packed, scales, zeros, y, as_stream(stream)));
+  wqd::MfmaPlan mp;
+  st = wqd::plan_mfma(fmt, M, N, K, &mp);
+  if (st != wqd::kOK) return st;
+  return hip_status(
+      wqd::launch_mfma(fmt, mp, M, N, K, x, w_packed, scales, zeros, y, workspace, as_stream(stream)));
 }
 
 int wqd_dequant(int fmt, const void* w_packed, const void* scales, const void* zeros, int64_t N, int64_t K,

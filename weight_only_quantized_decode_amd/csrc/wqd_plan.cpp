@@ -45,11 +45,54 @@ int plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, GemvPlan* out) {
   return kOK;
 }
 
+// Tiles per chunk of the matrix-core kernel: the staged x chunk is 16 KiB
+// (16 * BMS rows), at most 8 tiles.
+static int mfma_tpc(int fmt, int bms) {
+  const int raw = 8192 / (16 * bms * tile_k(fmt));
+  return raw > 8 ? 8 : (raw < 1 ? 1 : raw);
+}
+
+int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out) {
+  PackedSizes ps;
+  int st = packed_sizes(fmt, N, K, &ps);
+  if (st != kOK) return st;
+  if (M < 1) return kEArg;
+  MfmaPlan p{};
+  p.BMS = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  p.BNT = (M > 64 && fmt != kFmtBF16) ? 2 : 1;
+  p.TPC = mfma_tpc(fmt, p.BMS);
+  p.NB = ps.NB;
+  p.KT = ps.KT;
+  p.NBB = ceil_div(p.NB, 4 * p.BNT);
+  p.MB = ceil_div(M, 16 * p.BMS);
+  p.chunks = ceil_div(p.KT, p.TPC);
+  const int64_t wgs = p.NBB * p.MB;
+  const int64_t target = 512;  // two workgroups per compute unit
+  int64_t S = wgs >= target ? 1 : ceil_div(target, wgs);
+  // every split keeps at least 4 chunks
+  const int64_t max_s = p.chunks / 4 > 1 ? p.chunks / 4 : 1;
+  if (S > max_s) S = max_s;
+  if (S > 16) S = 16;
+  p.chunks_per_split = ceil_div(p.chunks, S);
+  S = ceil_div(p.chunks, p.chunks_per_split);
+  p.S = int(S);
+  p.ws_bytes = p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;
+  *out = p;
+  return kOK;
+}
+
 int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out) {
   GemvPlan g;
   int st = plan_gemv(fmt, M, N, K, &g);
   if (st != kOK) return st;
-  *out = 0;
+  if (M <= kGemvMaxM) {
+    *out = 0;
+    return kOK;
+  }
+  MfmaPlan p;
+  st = plan_mfma(fmt, M, N, K, &p);
+  if (st != kOK) return st;
+  *out = p.ws_bytes;
   return kOK;
 }
 

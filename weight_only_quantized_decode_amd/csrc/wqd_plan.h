@@ -53,6 +53,22 @@ struct GemvPlan {
 
 int plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, GemvPlan* out);
 
+// Matrix-core kernel (M > 8): workgroup tile = 16 * BMS rows of x times
+// 4 wavefronts x BNT 16-column tiles; the K loop advances in chunks of TPC
+// tiles.  When that leaves fewer than ~2 workgroups per compute unit, K is
+// split S ways over workgroups; the S float32 partial tiles go to the
+// workspace and a second kernel adds them in split order (deterministic, no
+// atomics, no device-scope fences).
+struct MfmaPlan {
+  int BMS, BNT, TPC;
+  int64_t NB, KT, NBB, MB, chunks;
+  int S;                // K splits
+  int64_t chunks_per_split;
+  size_t ws_bytes;      // S * M * N * 4 when S > 1
+};
+
+int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out);
+
 // Workspace bytes for wqd_qgemm (0: no path needs scratch memory).
 int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out);
 
