@@ -175,6 +175,27 @@ def shape_breakdown(wl, packed, xs, ys, ws, stream):
     return out
 
 
+def profiled_traffic(wl):
+    """HBM bytes per launch from the committed counter summary of this workload
+    (profiles/traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE runs scaled by
+    a copy kernel of known size), or None when there is none or the kernel
+    sources changed since the counters were taken."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"traffic_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    csrc = os.path.join(root, "weight_only_quantized_decode_amd", "csrc")
+    for fn, digest in d.get("kernel_sources_sha256_16", {}).items():
+        with open(os.path.join(csrc, fn), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
+                return None
+    return d["traffic_bytes_per_launch"]
+
+
 def cpu_baseline(wl):
     """The oracle (as it stands) on a bounded sample of the same workload, on the host cores."""
     import oracle
@@ -325,7 +346,7 @@ def main():
         "hbm_copy_ceiling_GBps": None if ceiling[1] is None else round(ceiling[1], 1),
         "pct_measured_read_ceiling": None if ceiling[0] is None else round(100 * gbps / ceiling[0], 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(wl),
                      "kernel": f"gemv_kernel<{wl.fmt}, M={mr}> (every launch of the timed step)",
                      "avg_launch_us": round(avg_launch_us, 3),
                      "bytes_per_launch": round(per_launch_bytes)},
