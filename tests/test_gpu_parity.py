@@ -111,8 +111,34 @@ def test_qgemm_small_shapes(fmt, M):
         compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
+def bcast_shapes(fmt):
+    # (N, K) for the 1-2 row kernel: shares of 1, 3, 5 (partial groups), 16
+    # tiles, 4 / 8 / 16 wavefronts per block, and K long enough that it falls
+    # back to the staged kernel (more than 256 tiles)
+    if fmt == "w4a16":
+        return [(16, 128), (40, 384), (200, 640), (72, 2176), (1024, 8192), (96, 12800), (64, 28672), (16, 32896)]
+    if fmt == "fp8":
+        return [(16, 8), (40, 72), (200, 1000), (1024, 8192), (64, 16384), (16, 16448)]
+    return [(16, 8), (40, 72), (200, 1000), (1024, 8192), (16, 8200)]
+
+
 @pytest.mark.parametrize("fmt", FMTS)
-def test_one_hot_probes_exact(fmt):
+@pytest.mark.parametrize("M", [1, 2])
+def test_qgemm_one_two_rows(fmt, M):
+    for N, K in bcast_shapes(fmt):
+        print(f"qgemm {fmt} M={M} N={N} K={K}", flush=True)
+        W = I.w_host(2000 + N + K, N, K)
+        qw = oracle.quantize(fmt, W)
+        pw = wqd.pack_weights(fmt, to_dev(W))
+        x = I.x_bf16_bits(11 * M + K, M, K)
+        y = wqd.qgemm(x_dev(x), pw)
+        torch.cuda.synchronize()
+        compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rows", [1, 2, 8])
+def test_one_hot_probes_exact(fmt, rows):
     """x = e_k gives y[:, n] = bf16(Wd[n, k]) exactly: ties the kernel's own dequant to the oracle.
 
     Wd is the float32 dequantised weight (exact for bf16 and W4A16; for FP8 the
@@ -127,8 +153,8 @@ def test_one_hot_probes_exact(fmt):
     x = np.zeros((len(ks), K), np.uint16)
     for i, k in enumerate(ks):
         x[i, k] = 0x3F80  # 1.0
-    for M0 in range(0, len(ks), 8):
-        xb = x[M0:M0 + 8]
+    for M0 in range(0, len(ks), rows):
+        xb = x[M0:M0 + rows]
         y = bf16_bits(wqd.qgemm(x_dev(xb), pw))
         for i in range(xb.shape[0]):
             assert np.array_equal(y[i], oracle.bf16_to_bits(Wd[:, ks[M0 + i]])), (fmt, ks[M0 + i])
@@ -138,9 +164,10 @@ def test_one_hot_probes_exact(fmt):
 def test_zero_weights_give_exact_zero(fmt):
     N, K = 130, 512
     pw = wqd.pack_weights(fmt, torch.zeros((N, K), dtype=torch.float32, device=dev()))
-    y = wqd.qgemm(x_dev(I.x_bf16_bits(3, 4, K)), pw)
-    torch.cuda.synchronize()
-    assert (y.float() == 0).all()
+    for M in (1, 2, 4, 16):
+        y = wqd.qgemm(x_dev(I.x_bf16_bits(3 + M, M, K)), pw)
+        torch.cuda.synchronize()
+        assert (y.float() == 0).all(), M
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -96,6 +96,9 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const voi
     if (!workspace || workspace_bytes < need) return WQD_E_WORKSPACE;
     if (!wqd::aligned16(workspace)) return WQD_E_ALIGN;
   }
+  wqd::BcastPlan bp;
+  if (M <= wqd::kBcastMaxM && wqd::plan_bcast(fmt, M, N, K, &bp) == wqd::kOK)
+    return hip_status(wqd::launch_gemv_bcast(fmt, bp, x, M, N, K, w_packed, scales, zeros, y, as_stream(stream)));
   if (M <= wqd::kGemvMaxM)
     return hip_status(wqd::launch_gemv(fmt, plan, x, M, N, K, w_packed, scales, zeros, y, as_stream(stream)));
   wqd::MfmaPlan mp;

@@ -45,6 +45,29 @@ int plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, GemvPlan* out) {
   return kOK;
 }
 
+// Wavefronts per workgroup: the fewest whose shares hold at most 16 tiles,
+// then doubled while the whole launch has fewer than 4096 wavefronts (16 per
+// compute unit) and each still gets at least one group of 4 tiles.
+int plan_bcast(int fmt, int64_t M, int64_t N, int64_t K, BcastPlan* out) {
+  PackedSizes ps;
+  int st = packed_sizes(fmt, N, K, &ps);
+  if (st != kOK) return st;
+  if (M < 1) return kEArg;
+  if (M > kBcastMaxM) return kEUnsupported;
+  auto share = [&](int w) { return ceil_div(ps.KT, 4 * int64_t(w)) * 4; };
+  int w = 4;
+  while (w < 16 && share(w) > 16) w *= 2;
+  if (share(w) > 16) return kEUnsupported;
+  while (w < 16 && ps.NB * w < 4096 && ceil_div(ps.KT, 4) >= 2 * w) w *= 2;
+  BcastPlan p{};
+  p.NB = ps.NB;
+  p.KT = ps.KT;
+  p.waves = w;
+  p.per_wave = int(share(w));
+  *out = p;
+  return kOK;
+}
+
 // Tiles per chunk of the matrix-core kernel: the staged x chunk is 16 KiB
 // (16 * BMS rows), at most 8 tiles.
 static int mfma_tpc(int fmt, int bms) {
