@@ -175,6 +175,14 @@ def shape_breakdown(wl, packed, xs, ys, ws, stream):
     return out
 
 
+def kernel_label(wl):
+    """Kernel family and waves per workgroup of every launch in the step."""
+    import weight_only_quantized_decode_amd as wqd
+
+    fams = sorted({"%s(%d waves)" % wqd.kernel_path(wl.fmt, wl.M, N, K) for _, N, K in wl.mats})
+    return f"{'+'.join(fams)} {wl.fmt} M={wl.M} (every launch of the timed step)"
+
+
 def profiled_traffic(wl):
     """HBM bytes per launch from the committed counter summary of this workload
     (profiles/traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE runs scaled by
@@ -189,7 +197,10 @@ def profiled_traffic(wl):
     with open(path) as f:
         d = json.load(f)
     csrc = os.path.join(root, "weight_only_quantized_decode_amd", "csrc")
-    for fn, digest in d.get("kernel_sources_sha256_16", {}).items():
+    recorded = d.get("kernel_sources_sha256_16", {})
+    if sorted(recorded) != sorted(os.listdir(csrc)):  # every source file, no more, no fewer
+        return None
+    for fn, digest in recorded.items():
         with open(os.path.join(csrc, fn), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
                 return None
@@ -323,7 +334,6 @@ def main():
     avg_launch_us = ms * 1e3 / wl.launches
     achieved = per_launch_bytes / (avg_launch_us / 1e6) / 1e9
     shapes = None if args.no_shapes else shape_breakdown(wl, packed, xs, ys, ws, stream)
-    mr = min(wl.M, 8)
     out = {
         "metric": "weight-stream GB/s (% of HBM peak) & us per layer-stack step, 70B W4A16/FP8/BF16",
         "value": round(gbps, 2),
@@ -347,7 +357,7 @@ def main():
         "pct_measured_read_ceiling": None if ceiling[0] is None else round(100 * gbps / ceiling[0], 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(wl),
-                     "kernel": f"gemv_kernel<{wl.fmt}, M={mr}> (every launch of the timed step)",
+                     "kernel": kernel_label(wl),
                      "avg_launch_us": round(avg_launch_us, 3),
                      "bytes_per_launch": round(per_launch_bytes)},
     }

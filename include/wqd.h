@@ -99,12 +99,27 @@ int wqd_packed_sizes(int fmt, int64_t N, int64_t K,
 
 /*
  * Host-only: bytes of scratch workspace wqd_qgemm needs for this shape (may
- * be 0).  The workspace holds split-K partial sums and per-tile arrival
- * counters.  It must be zero-filled before its first use; every call returns
- * it to that state when it completes.  One workspace must not be used by two
+ * be 0).  Only the matrix-core path (M > 8) uses one, when it splits K over
+ * workgroups: it holds their float32 partial tiles, which a second kernel
+ * adds in split order.  Its contents on entry do not matter (every byte read
+ * is written first in the same call).  One workspace must not be used by two
  * calls that can run at the same time.
  */
 int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes);
+
+/* Kernel families behind wqd_qgemm (wqd_kernel_path). */
+enum wqd_path {
+    WQD_PATH_BCAST = 0,   /* M <= 2: streaming, x broadcast across DPP rows */
+    WQD_PATH_STAGED = 1,  /* M <= 8: streaming, x staged in LDS */
+    WQD_PATH_MFMA = 2     /* M > 8: bf16 matrix cores, dequant on load */
+};
+
+/*
+ * Host-only: which kernel family wqd_qgemm launches for this shape (written
+ * to *path), and the wavefronts per workgroup it uses (to *waves; may be
+ * NULL).  Same validation as wqd_qgemm's shape checks.
+ */
+int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* waves);
 
 /*
  * Setup (not on the decode hot path): quantise W (device, float32 [N, K]

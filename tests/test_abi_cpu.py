@@ -94,6 +94,30 @@ def test_workspace_query():
     assert L.wqd_workspace_bytes(2, 0, 64, 128, ctypes.byref(b)) == E_ARG
 
 
+def test_kernel_path_choice():
+    """Which kernel family serves each decode shape (host planning only)."""
+    # one or two rows: the broadcast streaming kernel, more wavefronts for small N
+    assert wqd.kernel_path("w4a16", 1, 8192, 8192) == ("bcast", 4)
+    assert wqd.kernel_path("w4a16", 1, 28672, 8192) == ("bcast", 4)
+    assert wqd.kernel_path("w4a16", 1, 1024, 8192) == ("bcast", 16)
+    assert wqd.kernel_path("w4a16", 1, 8192, 28672) == ("bcast", 8)   # 224 tiles: shares of 28
+    assert wqd.kernel_path("w4a16", 2, 8192, 28672) == ("bcast", 16)  # two rows: shares of at most 16
+    assert wqd.kernel_path("fp8", 1, 28672, 8192)[0] == "bcast"
+    assert wqd.kernel_path("bf16", 2, 4096, 11008) == ("bcast", 16)   # 344 tiles: shares of 24
+    assert wqd.kernel_path("bf16", 1, 16, 16416)[0] == "staged"       # 513 tiles
+    assert wqd.kernel_path("w4a16", 1, 16, 65664)[0] == "staged"      # 513 tiles
+    assert wqd.kernel_path("w4a16", 2, 16, 32896)[0] == "staged"      # 257 tiles, two rows
+    for M in (3, 8):
+        assert wqd.kernel_path("fp8", M, 8192, 8192)[0] == "staged"
+    for M in (9, 16, 1024):
+        assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "mfma"
+    L = wqd.lib()
+    p = ctypes.c_int()
+    assert L.wqd_kernel_path(2, 1, 64, 128, None, None) == E_ARG
+    assert L.wqd_kernel_path(2, 1, 64, 100, ctypes.byref(p), None) == E_SHAPE
+    assert L.wqd_kernel_path(2, 1, 64, 128, ctypes.byref(p), None) == 0 and p.value == 0
+
+
 def test_qgemm_rejects_bad_arguments_before_enqueue():
     L = wqd.lib()
     A = 0x10000  # 16-byte aligned fake address: never dereferenced, validation fails first

@@ -114,12 +114,13 @@ def test_qgemm_small_shapes(fmt, M):
 def bcast_shapes(fmt):
     # (N, K) for the 1-2 row kernel: shares of 1, 3, 5 (partial groups), 16
     # tiles, 4 / 8 / 16 wavefronts per block, and K long enough that it falls
-    # back to the staged kernel (more than 256 tiles)
+    # back to the staged kernel (more than 512 tiles; 256 for two W4A16 rows)
     if fmt == "w4a16":
-        return [(16, 128), (40, 384), (200, 640), (72, 2176), (1024, 8192), (96, 12800), (64, 28672), (16, 32896)]
+        return [(16, 128), (40, 384), (200, 640), (72, 2176), (1024, 8192), (96, 12800), (64, 28672), (16, 32896),
+                (16, 65664)]
     if fmt == "fp8":
-        return [(16, 8), (40, 72), (200, 1000), (1024, 8192), (64, 16384), (16, 16448)]
-    return [(16, 8), (40, 72), (200, 1000), (1024, 8192), (16, 8200)]
+        return [(16, 8), (40, 72), (200, 1000), (1024, 8192), (64, 16384), (16, 16448), (16, 32832)]
+    return [(16, 8), (40, 72), (200, 1000), (1024, 8192), (16, 8200), (16, 16416)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -134,6 +135,21 @@ def test_qgemm_one_two_rows(fmt, M):
         y = wqd.qgemm(x_dev(x), pw)
         torch.cuda.synchronize()
         compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("fmt,N,K", [("w4a16", 4096, 20608), ("fp8", 4096, 12352), ("bf16", 4096, 6176)])
+def test_qgemm_long_shares(fmt, N, K):
+    """One row, 8 waves per block with 24-28 tile shares (two x-sum registers
+    for W4A16), a partial last group and an idle last wavefront."""
+    assert wqd.kernel_path(fmt, 1, N, K) == ("bcast", 8)
+    print(f"qgemm {fmt} M=1 N={N} K={K}", flush=True)
+    W = I.w_host(3000 + K, N, K)
+    qw = oracle.quantize(fmt, W)
+    pw = wqd.pack_weights(fmt, to_dev(W))
+    x = I.x_bf16_bits(17 + K, 1, K)
+    y = wqd.qgemm(x_dev(x), pw)
+    torch.cuda.synchronize()
+    compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M=1 N={N} K={K}")
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -36,6 +36,9 @@ class WqdError(RuntimeError):
         super().__init__(msg)
 
 
+_SIGNATURE_NAMES: list = []
+
+
 def lib() -> ctypes.CDLL:
     """The loaded C library (raises if it has not been built)."""
     global _lib
@@ -54,6 +57,7 @@ def lib() -> ctypes.CDLL:
             "wqd_last_hip_error": (i32, []),
             "wqd_packed_sizes": (i32, [i32, i64, i64, psz, psz, psz]),
             "wqd_workspace_bytes": (i32, [i32, i64, i64, i64, psz]),
+            "wqd_kernel_path": (i32, [i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "wqd_pack_weights": (i32, [i32, vp, i64, i64, vp, vp, vp, vp]),
             "wqd_qgemm": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
             "wqd_dequant": (i32, [i32, vp, vp, vp, i64, i64, vp, vp]),
@@ -63,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "wqd_stream_sink_words": (sz, [sz]),
             "wqd_stream_copy": (i32, [vp, vp, sz, vp]),
         }
+        _SIGNATURE_NAMES[:] = list(sig)
         for name, (res, args) in sig.items():
             f = getattr(L, name)
             f.restype = res
@@ -74,11 +79,7 @@ def lib() -> ctypes.CDLL:
 def exported_symbols():
     """Names of the C entry points this binding declares (all must resolve)."""
     lib()
-    return [
-        "wqd_version", "wqd_status_str", "wqd_last_hip_error", "wqd_packed_sizes", "wqd_workspace_bytes",
-        "wqd_pack_weights", "wqd_qgemm", "wqd_dequant", "wqd_unpack", "wqd_decode_e4m3", "wqd_stream_read",
-        "wqd_stream_sink_words", "wqd_stream_copy",
-    ]
+    return list(_SIGNATURE_NAMES)
 
 
 def _check(status: int, where: str):
@@ -118,6 +119,16 @@ def workspace_bytes(fmt, M: int, N: int, K: int) -> int:
     b = ctypes.c_size_t()
     _check(lib().wqd_workspace_bytes(_fmt(fmt), M, N, K, ctypes.byref(b)), "wqd_workspace_bytes")
     return b.value
+
+
+KERNEL_PATHS = ("bcast", "staged", "mfma")
+
+
+def kernel_path(fmt, M: int, N: int, K: int):
+    """(family, wavefronts per workgroup) of the kernel qgemm launches for this shape."""
+    p, w = ctypes.c_int(), ctypes.c_int()
+    _check(lib().wqd_kernel_path(_fmt(fmt), M, N, K, ctypes.byref(p), ctypes.byref(w)), "wqd_kernel_path")
+    return KERNEL_PATHS[p.value], w.value
 
 
 # ----------------------------------------------------------------------------- packed weights

@@ -67,6 +67,25 @@ int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes)
   return wqd::workspace_bytes(fmt, M, N, K, bytes);
 }
 
+int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* waves) {
+  if (!path) return WQD_E_ARG;
+  wqd::GemvPlan g;
+  int st = wqd::plan_gemv(fmt, M, N, K, &g);
+  if (st != wqd::kOK) return st;
+  wqd::BcastPlan bp;
+  if (M <= wqd::kBcastMaxM && wqd::plan_bcast(fmt, M, N, K, &bp) == wqd::kOK) {
+    *path = WQD_PATH_BCAST;
+    if (waves) *waves = bp.waves;
+  } else if (M <= wqd::kGemvMaxM) {
+    *path = WQD_PATH_STAGED;
+    if (waves) *waves = g.waves;
+  } else {
+    *path = WQD_PATH_MFMA;
+    if (waves) *waves = 4;
+  }
+  return WQD_OK;
+}
+
 int wqd_pack_weights(int fmt, const float* W, int64_t N, int64_t K, void* w_packed, void* scales, void* zeros,
                      void* stream) {
   wqd::PackedSizes ps;

@@ -20,9 +20,9 @@
 // W4A16 zero points: a tile contributes s * (P - (128 + z) * X) with
 // P = sum x (128 + q) over a lane's slice and X = sum x over the same slice
 // from an identical dot2 chain (so q == z == 0 cancels exactly).  X depends
-// on (tile, slice) only: at the start each lane (kb, n) computes X for tile n
-// of its wavefront's share (at most 16 tiles), and the correction reads it
-// back with the same row broadcast (v_fmac_f32 with DPP on X).
+// on (tile, slice) only: at the start each lane (kb, n) computes X for tiles
+// n, 16 + n of its wavefront's share (at most 32 tiles), and the correction
+// reads it back with the same row broadcast (v_fmac_f32 with DPP on X).
 //
 // DPP wait states.  The DPP instructions live in inline assembly, where the
 // compiler's hazard tracking cannot see them, so each block keeps its own
@@ -209,10 +209,10 @@ __device__ __forceinline__ void dot4_bcast(float& acc, uint32_t x, uint4 w) {
 
 // ---- per-tile arithmetic ---------------------------------------------------
 
-// Tile I of a group; CI = its position in the wavefront's share modulo 16
-// (the lane holding its W4A16 x sums).
-template <int FMT, int MR, int I, int CI>
-__device__ __forceinline__ void btile(const BGroup<FMT, MR>& g, const float (&X)[MR], float (&acc)[MR]) {
+// Tile I of a group; CI = its position in the wavefront's share (register
+// CI / 16 of the W4A16 x sums holds it, in lane CI % 16 of each row).
+template <int FMT, int MR, int XC, int I, int CI>
+__device__ __forceinline__ void btile(const BGroup<FMT, MR>& g, const float (&X)[MR][XC], float (&acc)[MR]) {
   using C = BcC<FMT>;
   const uint4 wv = g.w[I];
   constexpr int R = I / C::TPX;               // x register of this tile
@@ -238,7 +238,7 @@ __device__ __forceinline__ void btile(const BGroup<FMT, MR>& g, const float (&X)
     }
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      fmac_bcast<CI>(P[m], X[m], nz);
+      fmac_bcast<CI % 16>(P[m], X[m][CI / 16], nz);
       acc[m] = fmaf(s, P[m], acc[m]);
     }
   } else if constexpr (FMT == kFmtFP8) {
@@ -257,39 +257,80 @@ __device__ __forceinline__ void btile(const BGroup<FMT, MR>& g, const float (&X)
   }
 }
 
-// Load the group after `cur` into `dst` (unless LAST), then multiply `cur`
-// (tiles t .. t + 3; fewer at the end of the share).  Returns whether tiles
-// remain.  The steps are straight-line code (a share holds at most 16
-// tiles), so no loop-carried registers with loads in flight: the compiler's
-// wait before each tile counts exactly the loads issued after it.
-template <int FMT, int MR, int CB, bool LAST>
-__device__ __forceinline__ bool bstep(const BGroup<FMT, MR>& cur, BGroup<FMT, MR>& dst, int& t, int total,
-                                      const BcastArgs& a, __amdgpu_buffer_rsrc_t wres, const uint2* sbase,
-                                      const uint16_t* zbase, int64_t kt_begin, int lane, int kb, int n,
-                                      const float (&X)[MR], float (&acc)[MR]) {
-  if (!LAST) bload<FMT, MR>(dst, a, wres, sbase, zbase, kt_begin, t + 4, total - 1, lane, kb, n);
+// Multiply group `g` (tiles t .. t + 3; fewer at the end of the share), then
+// (unless LAST) refill it with the group two ahead, so two groups stay in
+// flight.  Refills past the share read nothing from memory (the weight
+// buffer resource ends with the share; x, scale and zero reads are clamped),
+// which keeps every load unconditional and the compiler's waits exact.
+// Returns whether tiles remain.
+template <int FMT, int MR, int XC, int CB, bool LAST>
+__device__ __forceinline__ bool bstep(BGroup<FMT, MR>& g, int& t, int total, const BcastArgs& a,
+                                      __amdgpu_buffer_rsrc_t wres, const uint2* sbase, const uint16_t* zbase,
+                                      int64_t kt_begin, int lane, int kb, int n, const float (&X)[MR][XC],
+                                      float (&acc)[MR]) {
   const int left = total - t;
   if (left >= 4) {
-    btile<FMT, MR, 0, CB + 0>(cur, X, acc);
-    btile<FMT, MR, 1, CB + 1>(cur, X, acc);
-    btile<FMT, MR, 2, CB + 2>(cur, X, acc);
-    btile<FMT, MR, 3, CB + 3>(cur, X, acc);
+    btile<FMT, MR, XC, 0, CB + 0>(g, X, acc);
+    btile<FMT, MR, XC, 1, CB + 1>(g, X, acc);
+    btile<FMT, MR, XC, 2, CB + 2>(g, X, acc);
+    btile<FMT, MR, XC, 3, CB + 3>(g, X, acc);
+    if (!LAST) bload<FMT, MR>(g, a, wres, sbase, zbase, kt_begin, t + 8, total - 1, lane, kb, n);
     t += 4;
     return t < total;
   }
-  btile<FMT, MR, 0, CB + 0>(cur, X, acc);
-  if (left > 1) btile<FMT, MR, 1, CB + 1>(cur, X, acc);
-  if (left > 2) btile<FMT, MR, 2, CB + 2>(cur, X, acc);
+  btile<FMT, MR, XC, 0, CB + 0>(g, X, acc);
+  if (left > 1) btile<FMT, MR, XC, 1, CB + 1>(g, X, acc);
+  if (left > 2) btile<FMT, MR, XC, 2, CB + 2>(g, X, acc);
   return false;
 }
 
-template <int FMT, int MR, int W>
+// The x sums of one register (16 tiles): the dot2 chain of x against ones,
+// in the order of the products' chain.
+template <int FMT, int MR, int XC>
+__device__ __forceinline__ void xsums(float (&X)[MR][XC], const uint4 (&xs)[MR][4], int c) {
+  const bf16x2_t ones = as_bf16x2(0x3F803F80u);
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    float v = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v = dot2_bf16(as_bf16x2(xs[m][u].x), ones, v);
+      v = dot2_bf16(as_bf16x2(xs[m][u].y), ones, v);
+      v = dot2_bf16(as_bf16x2(xs[m][u].z), ones, v);
+      v = dot2_bf16(as_bf16x2(xs[m][u].w), ones, v);
+    }
+    X[m][c] = v;
+  }
+}
+
+// Steps S .. NG - 1 as straight-line code with early exits (no loop, so no
+// loop-carried registers with loads in flight): groups alternate between the
+// two buffers, and the last two steps have nothing left to refill.  The
+// second register of W4A16 x sums is formed just before its first tile, from
+// loads issued after the first one's chain.
+template <int FMT, int MR, int XC, int NG, int S>
+__device__ __forceinline__ void bsteps(BGroup<FMT, MR>& g0, BGroup<FMT, MR>& g1, int& t, int total,
+                                       const BcastArgs& a, __amdgpu_buffer_rsrc_t wres, const uint2* sbase,
+                                       const uint16_t* zbase, int64_t kt_begin, int lane, int kb, int n,
+                                       float (&X)[MR][XC], const uint4 (&xs)[MR][4], float (&acc)[MR]) {
+  if constexpr (S < NG) {
+    if constexpr (FMT == kFmtW4 && XC == 2 && S == 4) xsums<FMT, MR, XC>(X, xs, 1);
+    BGroup<FMT, MR>& g = S % 2 == 0 ? g0 : g1;
+    if (bstep<FMT, MR, XC, 4 * S, (S >= NG - 2)>(g, t, total, a, wres, sbase, zbase, kt_begin, lane, kb, n, X, acc))
+      bsteps<FMT, MR, XC, NG, S + 1>(g0, g1, t, total, a, wres, sbase, zbase, kt_begin, lane, kb, n, X, xs, acc);
+  }
+}
+
+// NG: groups of 4 tiles per wavefront share (4 or 8).  XC: registers of
+// W4A16 x sums, 16 tiles each.
+template <int FMT, int MR, int W, int NG>
 __global__ __launch_bounds__(64 * W) void gemv_bcast_kernel(BcastArgs a) {
   using C = BcC<FMT>;
+  constexpr int XC = FMT == kFmtW4 ? NG / 4 : 1;
   __shared__ float s_red[W][MR][kTileRows];
 
   const int lane = threadIdx.x & 63, kb = lane >> 4, n = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar control flow
   const int64_t nb = blockIdx.x;
   const int64_t kt_begin = int64_t(wave) * a.per_wave;
   const int64_t rem = a.KT - kt_begin;
@@ -307,40 +348,36 @@ __global__ __launch_bounds__(64 * W) void gemv_bcast_kernel(BcastArgs a) {
     const uint2* sbase = reinterpret_cast<const uint2*>(a.scales) + q0;
     const uint16_t* zbase = a.zeros + q0;
 
-    // W4A16 x sums: lane (kb, n) sums slice kb of tile n of the share (the
-    // share holds at most 16 tiles), with the dot2 chain of the products.
-    uint4 xs[MR][FMT == kFmtW4 ? 4 : 1];
-    if constexpr (FMT == kFmtW4) {
-      const int64_t k0 = (kt_begin + min(n, last)) * C::TK + kb * C::SLK;
+    // W4A16 x sums: lane (kb, n) of register c sums slice kb of tile 16 c + n
+    // of the share.  Its 32 x values are loaded as 4 x 16 bytes per row.
+    uint4 xs[MR][4];
+    auto load_xs = [&](int c) {
+      const int64_t k0 = (kt_begin + min(16 * c + n, last)) * C::TK + kb * C::SLK;
 #pragma unroll
       for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int u = 0; u < 4; ++u) xs[m][u] = *reinterpret_cast<const uint4*>(a.x + int64_t(m) * a.K + k0 + 8 * u);
-    }
+    };
+    if constexpr (FMT == kFmtW4) load_xs(0);
     BGroup<FMT, MR> g0, g1;
     bload<FMT, MR>(g0, a, wres, sbase, zbase, kt_begin, 0, last, lane, kb, n);
-    float X[MR];
+    bload<FMT, MR>(g1, a, wres, sbase, zbase, kt_begin, 4, last, lane, kb, n);
+    // keep every prologue load ahead of the first wait (the x sums wait for
+    // their own loads; the scheduler would otherwise start them earlier)
+    __builtin_amdgcn_sched_barrier(0);
+    float X[MR][XC];
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      X[m] = 0.f;
-      if constexpr (FMT == kFmtW4) {
-        const bf16x2_t ones = as_bf16x2(0x3F803F80u);
+    for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          X[m] = dot2_bf16(as_bf16x2(xs[m][u].x), ones, X[m]);
-          X[m] = dot2_bf16(as_bf16x2(xs[m][u].y), ones, X[m]);
-          X[m] = dot2_bf16(as_bf16x2(xs[m][u].z), ones, X[m]);
-          X[m] = dot2_bf16(as_bf16x2(xs[m][u].w), ones, X[m]);
-        }
-      }
+      for (int c = 0; c < XC; ++c) X[m][c] = 0.f;
+    if constexpr (FMT == kFmtW4) {
+      xsums<FMT, MR, XC>(X, xs, 0);
+      if constexpr (XC == 2) load_xs(1);
     }
-    // One group in flight ahead of the one being multiplied, at most four
-    // groups per share.
+    // Groups 0 and 1 are in flight; each step multiplies one and refills it
+    // with the group two ahead.
     int t = 0;
-    if (bstep<FMT, MR, 0, false>(g0, g1, t, total, a, wres, sbase, zbase, kt_begin, lane, kb, n, X, acc) &&
-        bstep<FMT, MR, 4, false>(g1, g0, t, total, a, wres, sbase, zbase, kt_begin, lane, kb, n, X, acc) &&
-        bstep<FMT, MR, 8, false>(g0, g1, t, total, a, wres, sbase, zbase, kt_begin, lane, kb, n, X, acc))
-      bstep<FMT, MR, 12, true>(g1, g0, t, total, a, wres, sbase, zbase, kt_begin, lane, kb, n, X, acc);
+    bsteps<FMT, MR, XC, NG, 0>(g0, g1, t, total, a, wres, sbase, zbase, kt_begin, lane, kb, n, X, xs, acc);
   }
 
   // the 4 slices of a row (lanes n, n+16, n+32, n+48), then the W wavefronts
@@ -365,20 +402,22 @@ __global__ __launch_bounds__(64 * W) void gemv_bcast_kernel(BcastArgs a) {
   }
 }
 
-template <int FMT, int MR>
+template <int FMT, int MR, int NG>
 static hipError_t launch_bc_w(const BcastArgs& a, int waves, unsigned grid, hipStream_t st) {
   switch (waves) {
-    case 4: hipLaunchKernelGGL((gemv_bcast_kernel<FMT, MR, 4>), dim3(grid), dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((gemv_bcast_kernel<FMT, MR, 8>), dim3(grid), dim3(512), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((gemv_bcast_kernel<FMT, MR, 16>), dim3(grid), dim3(1024), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gemv_bcast_kernel<FMT, MR, 4, NG>), dim3(grid), dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((gemv_bcast_kernel<FMT, MR, 8, NG>), dim3(grid), dim3(512), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((gemv_bcast_kernel<FMT, MR, 16, NG>), dim3(grid), dim3(1024), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int FMT>
-static hipError_t launch_bc_fmt(const BcastArgs& a, int mr, int waves, unsigned grid, hipStream_t st) {
-  return mr == 1 ? launch_bc_w<FMT, 1>(a, waves, grid, st) : launch_bc_w<FMT, 2>(a, waves, grid, st);
+static hipError_t launch_bc_fmt(const BcastArgs& a, int mr, int waves, int ng, unsigned grid, hipStream_t st) {
+  if (ng == 4) return mr == 1 ? launch_bc_w<FMT, 1, 4>(a, waves, grid, st) : launch_bc_w<FMT, 2, 4>(a, waves, grid, st);
+  if (ng == 8) return mr == 1 ? launch_bc_w<FMT, 1, 8>(a, waves, grid, st) : launch_bc_w<FMT, 2, 8>(a, waves, grid, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv_bcast(int fmt, const BcastPlan& p, const void* x, int64_t M, int64_t N, int64_t K,
@@ -397,9 +436,9 @@ hipError_t launch_gemv_bcast(int fmt, const BcastPlan& p, const void* x, int64_t
   a.per_wave = p.per_wave;
   const unsigned grid = unsigned(p.NB);
   const int mr = int(M);
-  if (fmt == kFmtBF16) return launch_bc_fmt<kFmtBF16>(a, mr, p.waves, grid, st);
-  if (fmt == kFmtFP8) return launch_bc_fmt<kFmtFP8>(a, mr, p.waves, grid, st);
-  return launch_bc_fmt<kFmtW4>(a, mr, p.waves, grid, st);
+  if (fmt == kFmtBF16) return launch_bc_fmt<kFmtBF16>(a, mr, p.waves, p.groups, grid, st);
+  if (fmt == kFmtFP8) return launch_bc_fmt<kFmtFP8>(a, mr, p.waves, p.groups, grid, st);
+  return launch_bc_fmt<kFmtW4>(a, mr, p.waves, p.groups, grid, st);
 }
 
 }  // namespace wqd
