@@ -137,11 +137,12 @@ def test_qgemm_one_two_rows(fmt, M):
         compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("fmt,N,K", [("w4a16", 4096, 20608), ("fp8", 4096, 12352), ("bf16", 4096, 6176)])
-def test_qgemm_long_shares(fmt, N, K):
-    """One row, 8 waves per block with 24-28 tile shares (two x-sum registers
-    for W4A16), a partial last group and an idle last wavefront."""
-    assert wqd.kernel_path(fmt, 1, N, K) == ("bcast", 8)
+@pytest.mark.parametrize("fmt,N,K,waves", [("w4a16", 4096, 20608, 8), ("fp8", 4096, 12352, 8),
+                                           ("bf16", 2048, 10976, 16)])
+def test_qgemm_long_shares(fmt, N, K, waves):
+    """One row, shares of 24-28 tiles (eight groups; two x-sum registers for
+    W4A16), a partial last group and an idle last wavefront."""
+    assert wqd.kernel_path(fmt, 1, N, K) == ("bcast", waves)
     print(f"qgemm {fmt} M=1 N={N} K={K}", flush=True)
     W = I.w_host(3000 + K, N, K)
     qw = oracle.quantize(fmt, W)
