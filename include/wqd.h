@@ -109,8 +109,8 @@ int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes)
 
 /* Kernel families behind wqd_qgemm (wqd_kernel_path). */
 enum wqd_path {
-    WQD_PATH_BCAST = 0,   /* M <= 2: streaming, x broadcast across DPP rows */
-    WQD_PATH_STAGED = 1,  /* M <= 8: streaming, x staged in LDS */
+    WQD_PATH_BCAST = 0,   /* M <= 2 (W4A16) or M <= 8: streaming, x broadcast across DPP rows */
+    WQD_PATH_STAGED = 1,  /* M <= 8 otherwise (e.g. W4A16 M >= 3): streaming, x staged in LDS */
     WQD_PATH_MFMA = 2     /* M > 8: bf16 matrix cores, dequant on load */
 };
 

@@ -108,7 +108,10 @@ def test_kernel_path_choice():
     assert wqd.kernel_path("w4a16", 1, 16, 65664)[0] == "staged"      # 513 tiles
     assert wqd.kernel_path("w4a16", 2, 16, 32896)[0] == "staged"      # 257 tiles, two rows
     for M in (3, 8):
-        assert wqd.kernel_path("fp8", M, 8192, 8192)[0] == "staged"
+        assert wqd.kernel_path("fp8", M, 8192, 8192)[0] == "bcast"    # FP8 / BF16: up to 8 rows
+        assert wqd.kernel_path("bf16", M, 4096, 4096)[0] == "bcast"
+        assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "staged"
+    assert wqd.kernel_path("fp8", 3, 8192, 28672)[0] == "staged"       # 448 tiles: 3+ rows keep 16-tile shares
     for M in (9, 16, 1024):
         assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "mfma"
     L = wqd.lib()

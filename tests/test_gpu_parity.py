@@ -112,7 +112,7 @@ def test_qgemm_small_shapes(fmt, M):
 
 
 def bcast_shapes(fmt):
-    # (N, K) for the 1-2 row kernel: shares of 1, 3, 5 (partial groups), 16
+    # (N, K) for the broadcast kernel: shares of 1, 3, 5 (partial groups), 16
     # tiles, 4 / 8 / 16 wavefronts per block, and K long enough that it falls
     # back to the staged kernel (more than 512 tiles; 256 for two W4A16 rows)
     if fmt == "w4a16":
@@ -124,8 +124,8 @@ def bcast_shapes(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M", [1, 2])
-def test_qgemm_one_two_rows(fmt, M):
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+def test_qgemm_broadcast_rows(fmt, M):
     for N, K in bcast_shapes(fmt):
         print(f"qgemm {fmt} M={M} N={N} K={K}", flush=True)
         W = I.w_host(2000 + N + K, N, K)

@@ -73,7 +73,7 @@ int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* wa
   int st = wqd::plan_gemv(fmt, M, N, K, &g);
   if (st != wqd::kOK) return st;
   wqd::BcastPlan bp;
-  if (M <= wqd::kBcastMaxM && wqd::plan_bcast(fmt, M, N, K, &bp) == wqd::kOK) {
+  if (wqd::plan_bcast(fmt, M, N, K, &bp) == wqd::kOK) {
     *path = WQD_PATH_BCAST;
     if (waves) *waves = bp.waves;
   } else if (M <= wqd::kGemvMaxM) {
@@ -116,7 +116,7 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const voi
     if (!wqd::aligned16(workspace)) return WQD_E_ALIGN;
   }
   wqd::BcastPlan bp;
-  if (M <= wqd::kBcastMaxM && wqd::plan_bcast(fmt, M, N, K, &bp) == wqd::kOK)
+  if (wqd::plan_bcast(fmt, M, N, K, &bp) == wqd::kOK)
     return hip_status(wqd::launch_gemv_bcast(fmt, bp, x, M, N, K, w_packed, scales, zeros, y, as_stream(stream)));
   if (M <= wqd::kGemvMaxM)
     return hip_status(wqd::launch_gemv(fmt, plan, x, M, N, K, w_packed, scales, zeros, y, as_stream(stream)));

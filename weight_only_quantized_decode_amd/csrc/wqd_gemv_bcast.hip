@@ -1,4 +1,5 @@
-// Streaming decode kernel for one or two activation rows, x broadcast by DPP.
+// Streaming decode kernel for few activation rows (1-2 for W4A16, up to 8 for
+// FP8 and BF16), x broadcast by DPP.
 //
 // Same work split as the LDS-staged streaming kernel (one workgroup per
 // 16-row block over all of K, W wavefronts on contiguous shares of K, fixed
@@ -413,16 +414,38 @@ static hipError_t launch_bc_w(const BcastArgs& a, int waves, unsigned grid, hipS
   return hipGetLastError();
 }
 
+// Rows per launch: 1..2 for every format (four or eight groups per share);
+// FP8 and BF16 also 3..8 (four groups: the x registers grow with the rows).
 template <int FMT>
 static hipError_t launch_bc_fmt(const BcastArgs& a, int mr, int waves, int ng, unsigned grid, hipStream_t st) {
-  if (ng == 4) return mr == 1 ? launch_bc_w<FMT, 1, 4>(a, waves, grid, st) : launch_bc_w<FMT, 2, 4>(a, waves, grid, st);
-  if (ng == 8) return mr == 1 ? launch_bc_w<FMT, 1, 8>(a, waves, grid, st) : launch_bc_w<FMT, 2, 8>(a, waves, grid, st);
+  if (ng == 8) {
+    if (mr == 1) return launch_bc_w<FMT, 1, 8>(a, waves, grid, st);
+    if (mr == 2) return launch_bc_w<FMT, 2, 8>(a, waves, grid, st);
+    return hipErrorInvalidValue;
+  }
+  if (ng != 4) return hipErrorInvalidValue;
+  switch (mr) {
+    case 1: return launch_bc_w<FMT, 1, 4>(a, waves, grid, st);
+    case 2: return launch_bc_w<FMT, 2, 4>(a, waves, grid, st);
+    default: break;
+  }
+  if constexpr (FMT != kFmtW4) {
+    switch (mr) {
+      case 3: return launch_bc_w<FMT, 3, 4>(a, waves, grid, st);
+      case 4: return launch_bc_w<FMT, 4, 4>(a, waves, grid, st);
+      case 5: return launch_bc_w<FMT, 5, 4>(a, waves, grid, st);
+      case 6: return launch_bc_w<FMT, 6, 4>(a, waves, grid, st);
+      case 7: return launch_bc_w<FMT, 7, 4>(a, waves, grid, st);
+      case 8: return launch_bc_w<FMT, 8, 4>(a, waves, grid, st);
+      default: break;
+    }
+  }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv_bcast(int fmt, const BcastPlan& p, const void* x, int64_t M, int64_t N, int64_t K,
                              const void* wp, const void* scales, const void* zeros, void* y, hipStream_t st) {
-  if (M < 1 || M > kBcastMaxM) return hipErrorInvalidValue;
+  if (M < 1 || M > (fmt == kFmtW4 ? kBcastMaxMW4 : kBcastMaxM)) return hipErrorInvalidValue;
   BcastArgs a;
   a.x = reinterpret_cast<const uint16_t*>(x);
   a.y = reinterpret_cast<uint16_t*>(y);

@@ -50,17 +50,17 @@ int plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, GemvPlan* out) {
 // doubled while the launch has fewer wavefronts than the target (8 per
 // compute unit; 16 for BF16) and each still gets at least one group of 4
 // tiles.  Fewer, longer shares amortise each wavefront's start (its x sums
-// and first loads).  Measured on the 70B and 7B shapes.  Two W4A16 rows keep
-// shares of at most 16 tiles (registers).
+// and first loads).  Measured on the 70B and 7B shapes.  Three or more rows,
+// and two W4A16 rows, keep shares of at most 16 tiles (registers).
 int plan_bcast(int fmt, int64_t M, int64_t N, int64_t K, BcastPlan* out) {
   PackedSizes ps;
   int st = packed_sizes(fmt, N, K, &ps);
   if (st != kOK) return st;
   if (M < 1) return kEArg;
-  if (M > kBcastMaxM) return kEUnsupported;
+  if (M > (fmt == kFmtW4 ? kBcastMaxMW4 : kBcastMaxM)) return kEUnsupported;
   auto share = [&](int w) { return ceil_div(ps.KT, 4 * int64_t(w)) * 4; };
   const int64_t pref = fmt == kFmtBF16 ? 16 : 32;
-  const int64_t cap = (fmt == kFmtW4 && M == 2) ? 16 : 32;
+  const int64_t cap = (M >= 3 || (fmt == kFmtW4 && M == 2)) ? 16 : 32;
   const int64_t target = fmt == kFmtBF16 ? 4096 : 2048;
   int w = 4;
   while (w < 16 && share(w) > (pref < cap ? pref : cap)) w *= 2;

@@ -53,13 +53,15 @@ struct GemvPlan {
 
 int plan_gemv(int fmt, int64_t M, int64_t N, int64_t K, GemvPlan* out);
 
-// Row-broadcast streaming kernel (M <= 2): like the above, but x is read
-// from L2 per tile and broadcast across the lanes of a DPP row, so no LDS
-// staging.  W wavefronts (4, 8 or 16) per 16-row block, each on a share of
-// per_wave tiles (a multiple of 4, at most 32: straight-line code over
-// `groups` = 4 or 8 groups of 4 tiles); kEUnsupported when K is too long for
-// that (more than 512 tiles).
-constexpr int kBcastMaxM = 2;
+// Row-broadcast streaming kernel (M <= 2 for W4A16, M <= 8 for FP8 and
+// BF16): like the above, but x is read from L2 per tile and broadcast across
+// the lanes of a DPP row, so no LDS staging.  W wavefronts (4, 8 or 16) per
+// 16-row block, each on a share of per_wave tiles (a multiple of 4, at most
+// 32: straight-line code over `groups` = 4 or 8 groups of 4 tiles; at most 16
+// tiles for three or more rows, or two W4A16 rows); kEUnsupported when K is
+// too long for that.
+constexpr int kBcastMaxM = 8;
+constexpr int kBcastMaxMW4 = 2;
 
 struct BcastPlan {
   int64_t NB, KT;
