@@ -107,11 +107,17 @@ int wqd_packed_sizes(int fmt, int64_t N, int64_t K,
  */
 int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes);
 
-/* Kernel families behind wqd_qgemm (wqd_kernel_path). */
+/* Kernel families behind wqd_qgemm (wqd_kernel_path).  Which one serves a
+ * shape: the broadcast kernel up to 2 W4A16 rows or 4 FP8 / BF16 rows; the
+ * streaming matrix-core kernel up to 8 rows; otherwise, up to 8 rows, the
+ * broadcast kernel, then the staged one; above 8 rows the LDS matrix-core
+ * kernel.  Each streaming kernel also needs K short enough for its shares
+ * (hundreds of 16-row tiles). */
 enum wqd_path {
-    WQD_PATH_BCAST = 0,   /* M <= 2 (W4A16) or M <= 8: streaming, x broadcast across DPP rows */
-    WQD_PATH_STAGED = 1,  /* M <= 8 otherwise (e.g. W4A16 M >= 3): streaming, x staged in LDS */
-    WQD_PATH_MFMA = 2     /* M > 8: bf16 matrix cores, dequant on load */
+    WQD_PATH_BCAST = 0,   /* streaming, x read per tile and broadcast across DPP rows */
+    WQD_PATH_STAGED = 1,  /* streaming, x staged in LDS, dot2 products */
+    WQD_PATH_MFMA = 2,    /* bf16 matrix cores, x staged in LDS, dequant on load */
+    WQD_PATH_MC = 3       /* streaming, bf16 matrix cores, x fragments read per tile */
 };
 
 /*

@@ -96,22 +96,26 @@ def test_workspace_query():
 
 def test_kernel_path_choice():
     """Which kernel family serves each decode shape (host planning only)."""
-    # one or two rows: the broadcast streaming kernel, more wavefronts for small N
+    # broadcast kernel: 1-2 W4A16 rows, 1-4 FP8 / BF16 rows; more waves for small N
     assert wqd.kernel_path("w4a16", 1, 8192, 8192) == ("bcast", 4)
     assert wqd.kernel_path("w4a16", 1, 28672, 8192) == ("bcast", 4)
     assert wqd.kernel_path("w4a16", 1, 1024, 8192) == ("bcast", 16)
     assert wqd.kernel_path("w4a16", 1, 8192, 28672) == ("bcast", 8)   # 224 tiles: shares of 28
     assert wqd.kernel_path("w4a16", 2, 8192, 28672) == ("bcast", 16)  # two rows: shares of at most 16
-    assert wqd.kernel_path("fp8", 1, 28672, 8192)[0] == "bcast"
+    assert wqd.kernel_path("fp8", 4, 28672, 8192)[0] == "bcast"
     assert wqd.kernel_path("bf16", 2, 4096, 11008) == ("bcast", 16)   # 344 tiles: shares of 24
-    assert wqd.kernel_path("bf16", 1, 16, 16416)[0] == "staged"       # 513 tiles
-    assert wqd.kernel_path("w4a16", 1, 16, 65664)[0] == "staged"      # 513 tiles
-    assert wqd.kernel_path("w4a16", 2, 16, 32896)[0] == "staged"      # 257 tiles, two rows
+    # streaming matrix-core kernel: 3-8 W4A16 rows, 5-8 FP8 / BF16 rows
     for M in (3, 8):
-        assert wqd.kernel_path("fp8", M, 8192, 8192)[0] == "bcast"    # FP8 / BF16: up to 8 rows
-        assert wqd.kernel_path("bf16", M, 4096, 4096)[0] == "bcast"
-        assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "staged"
-    assert wqd.kernel_path("fp8", 3, 8192, 28672)[0] == "staged"       # 448 tiles: 3+ rows keep 16-tile shares
+        assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "mc"
+    for M in (5, 8):
+        assert wqd.kernel_path("fp8", M, 8192, 8192)[0] == "mc"
+        assert wqd.kernel_path("bf16", M, 4096, 4096)[0] == "mc"
+    assert wqd.kernel_path("fp8", 3, 8192, 28672)[0] == "mc"           # 448 tiles: too long for 3-row shares
+    # too long for either streaming kernel: the staged one
+    assert wqd.kernel_path("bf16", 1, 16, 16416)[0] == "staged"       # 513 tiles
+    assert wqd.kernel_path("w4a16", 1, 16, 65664)[0] == "staged"
+    assert wqd.kernel_path("w4a16", 5, 16, 65664)[0] == "staged"
+    # above 8 rows: the LDS matrix-core kernel
     for M in (9, 16, 1024):
         assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "mfma"
     L = wqd.lib()

@@ -121,7 +121,7 @@ def workspace_bytes(fmt, M: int, N: int, K: int) -> int:
     return b.value
 
 
-KERNEL_PATHS = ("bcast", "staged", "mfma")
+KERNEL_PATHS = ("bcast", "staged", "mfma", "mc")
 
 
 def kernel_path(fmt, M: int, N: int, K: int):

@@ -69,19 +69,15 @@ int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes)
 
 int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* waves) {
   if (!path) return WQD_E_ARG;
-  wqd::GemvPlan g;
-  int st = wqd::plan_gemv(fmt, M, N, K, &g);
+  wqd::Choice c;
+  int st = wqd::choose_path(fmt, M, N, K, &c);
   if (st != wqd::kOK) return st;
-  wqd::BcastPlan bp;
-  if (wqd::plan_bcast(fmt, M, N, K, &bp) == wqd::kOK) {
-    *path = WQD_PATH_BCAST;
-    if (waves) *waves = bp.waves;
-  } else if (M <= wqd::kGemvMaxM) {
-    *path = WQD_PATH_STAGED;
-    if (waves) *waves = g.waves;
-  } else {
-    *path = WQD_PATH_MFMA;
-    if (waves) *waves = 4;
+  *path = c.path;  // enum wqd_path and wqd::Path share their values
+  if (waves) {
+    *waves = c.path == wqd::kPathBcast ? c.bcast.waves
+           : c.path == wqd::kPathMc    ? c.mc.waves
+           : c.path == wqd::kPathStaged ? c.gemv.waves
+                                        : 4;
   }
   return WQD_OK;
 }
@@ -101,30 +97,29 @@ int wqd_pack_weights(int fmt, const float* W, int64_t N, int64_t K, void* w_pack
 int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const void* w_packed, const void* scales,
               const void* zeros, void* y, void* workspace, size_t workspace_bytes, void* stream) {
   if (M < 1) return WQD_E_ARG;
-  wqd::GemvPlan plan;
-  int st = wqd::plan_gemv(fmt, M, N, K, &plan);
+  wqd::Choice c;
+  int st = wqd::choose_path(fmt, M, N, K, &c);
   if (st != wqd::kOK) return st;
   if (!x || !y) return WQD_E_ARG;
   if (!wqd::aligned16(x) || !wqd::aligned16(y)) return WQD_E_ALIGN;
   st = check_packed_ptrs(fmt, w_packed, scales, zeros);
   if (st != WQD_OK) return st;
-  size_t need = 0;
-  st = wqd::workspace_bytes(fmt, M, N, K, &need);
-  if (st != wqd::kOK) return st;
+  const size_t need = c.path == wqd::kPathMfma ? c.mfma.ws_bytes : 0;
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return WQD_E_WORKSPACE;
     if (!wqd::aligned16(workspace)) return WQD_E_ALIGN;
   }
-  wqd::BcastPlan bp;
-  if (wqd::plan_bcast(fmt, M, N, K, &bp) == wqd::kOK)
-    return hip_status(wqd::launch_gemv_bcast(fmt, bp, x, M, N, K, w_packed, scales, zeros, y, as_stream(stream)));
-  if (M <= wqd::kGemvMaxM)
-    return hip_status(wqd::launch_gemv(fmt, plan, x, M, N, K, w_packed, scales, zeros, y, as_stream(stream)));
-  wqd::MfmaPlan mp;
-  st = wqd::plan_mfma(fmt, M, N, K, &mp);
-  if (st != wqd::kOK) return st;
-  return hip_status(
-      wqd::launch_mfma(fmt, mp, M, N, K, x, w_packed, scales, zeros, y, workspace, as_stream(stream)));
+  hipStream_t s = as_stream(stream);
+  switch (c.path) {
+    case wqd::kPathBcast:
+      return hip_status(wqd::launch_gemv_bcast(fmt, c.bcast, x, M, N, K, w_packed, scales, zeros, y, s));
+    case wqd::kPathMc:
+      return hip_status(wqd::launch_gemv_mc(fmt, c.mc, x, M, N, K, w_packed, scales, zeros, y, s));
+    case wqd::kPathStaged:
+      return hip_status(wqd::launch_gemv(fmt, c.gemv, x, M, N, K, w_packed, scales, zeros, y, s));
+    default:
+      return hip_status(wqd::launch_mfma(fmt, c.mfma, M, N, K, x, w_packed, scales, zeros, y, workspace, s));
+  }
 }
 
 int wqd_dequant(int fmt, const void* w_packed, const void* scales, const void* zeros, int64_t N, int64_t K,

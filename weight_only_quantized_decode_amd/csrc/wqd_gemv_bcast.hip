@@ -276,6 +276,9 @@ __device__ __forceinline__ bool bstep(BGroup<FMT, MR>& g, int& t, int total, con
     btile<FMT, MR, XC, 2, CB + 2>(g, X, acc);
     btile<FMT, MR, XC, 3, CB + 3>(g, X, acc);
     if (!LAST) bload<FMT, MR>(g, a, wres, sbase, zbase, kt_begin, t + 8, total - 1, lane, kb, n);
+    // issue the refill here: left to itself the scheduler sinks loads to just
+    // before their use, which would leave one group in flight instead of two
+    __builtin_amdgcn_sched_barrier(0);
     t += 4;
     return t < total;
   }

@@ -19,6 +19,8 @@ hipError_t launch_gemv(int fmt, const GemvPlan& p, const void* x, int64_t M, int
                        const void* scales, const void* zeros, void* y, hipStream_t st);
 hipError_t launch_gemv_bcast(int fmt, const BcastPlan& p, const void* x, int64_t M, int64_t N, int64_t K,
                              const void* wp, const void* scales, const void* zeros, void* y, hipStream_t st);
+hipError_t launch_gemv_mc(int fmt, const McPlan& p, const void* x, int64_t M, int64_t N, int64_t K,
+                          const void* wp, const void* scales, const void* zeros, void* y, hipStream_t st);
 hipError_t launch_mfma(int fmt, const MfmaPlan& p, int64_t M, int64_t N, int64_t K, const void* x, const void* wp,
                        const void* scales, const void* zeros, void* y, void* ws, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);

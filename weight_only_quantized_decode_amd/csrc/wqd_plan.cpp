@@ -76,6 +76,29 @@ int plan_bcast(int fmt, int64_t M, int64_t N, int64_t K, BcastPlan* out) {
   return kOK;
 }
 
+// Wavefronts per workgroup as for the broadcast kernel: the fewest whose
+// shares hold at most 32 tiles, doubled while the launch has fewer than 2048
+// wavefronts and each keeps at least one group of 4 tiles.
+int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out) {
+  PackedSizes ps;
+  int st = packed_sizes(fmt, N, K, &ps);
+  if (st != kOK) return st;
+  if (M < 1) return kEArg;
+  if (M > kMcMaxM || M * K * 2 >= (int64_t(1) << 31)) return kEUnsupported;
+  auto share = [&](int w) { return ceil_div(ps.KT, 4 * int64_t(w)) * 4; };
+  int w = 4;
+  while (w < 16 && share(w) > 32) w *= 2;
+  if (share(w) > 32) return kEUnsupported;
+  while (w < 16 && ps.NB * w < 2048 && ceil_div(ps.KT, 4) >= 2 * w) w *= 2;
+  McPlan p{};
+  p.NB = ps.NB;
+  p.KT = ps.KT;
+  p.waves = w;
+  p.per_wave = int(share(w));
+  *out = p;
+  return kOK;
+}
+
 // Tiles per chunk of the matrix-core kernel: the staged x chunk is 16 KiB
 // (16 * BMS rows), at most 8 tiles.
 static int mfma_tpc(int fmt, int bms) {
@@ -112,18 +135,33 @@ int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out) {
   return kOK;
 }
 
-int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out) {
-  GemvPlan g;
-  int st = plan_gemv(fmt, M, N, K, &g);
+int choose_path(int fmt, int64_t M, int64_t N, int64_t K, Choice* out) {
+  Choice c{};
+  int st = plan_gemv(fmt, M, N, K, &c.gemv);
   if (st != kOK) return st;
-  if (M <= kGemvMaxM) {
-    *out = 0;
-    return kOK;
+  const int64_t bcast_first = fmt == kFmtW4 ? 2 : 4;
+  if (M <= bcast_first && plan_bcast(fmt, M, N, K, &c.bcast) == kOK) {
+    c.path = kPathBcast;
+  } else if (M <= kGemvMaxM && plan_mc(fmt, M, N, K, &c.mc) == kOK) {
+    c.path = kPathMc;
+  } else if (M <= kGemvMaxM && plan_bcast(fmt, M, N, K, &c.bcast) == kOK) {
+    c.path = kPathBcast;
+  } else if (M <= kGemvMaxM) {
+    c.path = kPathStaged;
+  } else {
+    st = plan_mfma(fmt, M, N, K, &c.mfma);
+    if (st != kOK) return st;
+    c.path = kPathMfma;
   }
-  MfmaPlan p;
-  st = plan_mfma(fmt, M, N, K, &p);
+  *out = c;
+  return kOK;
+}
+
+int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out) {
+  Choice c;
+  int st = choose_path(fmt, M, N, K, &c);
   if (st != kOK) return st;
-  *out = p.ws_bytes;
+  *out = c.path == kPathMfma ? c.mfma.ws_bytes : 0;
   return kOK;
 }
 

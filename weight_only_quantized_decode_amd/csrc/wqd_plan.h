@@ -70,6 +70,21 @@ struct BcastPlan {
 
 int plan_bcast(int fmt, int64_t M, int64_t N, int64_t K, BcastPlan* out);
 
+// Streaming matrix-core kernel (M <= 16): the same work split, with the
+// products on bf16 matrix cores (x fragments read from L2 per tile).  Shares
+// of at most 32 tiles; kEUnsupported when K is too long for that or the x
+// rows span 2 GiB or more.
+constexpr int kMcMaxM = 16;
+
+struct McPlan {
+  int64_t NB, KT;
+  int waves, per_wave;
+};
+
+int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out);
+
+
+
 // Matrix-core kernel (M > 8): workgroup tile = 16 * BMS rows of x times
 // 4 wavefronts x BNT 16-column tiles; the K loop advances in chunks of TPC
 // tiles.  When that leaves fewer than ~2 workgroups per compute unit, K is
@@ -85,6 +100,23 @@ struct MfmaPlan {
 };
 
 int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out);
+
+// The kernel family for a shape, in order of preference (measured on the
+// 70B shapes): the broadcast kernel for up to 2 W4A16 rows or 4 FP8 / BF16
+// rows; the streaming matrix-core kernel up to 8 rows; the broadcast kernel
+// again, then the staged one, up to 8 rows where the former cannot take the
+// shape; the LDS matrix-core kernel above 8 rows.
+enum Path { kPathBcast = 0, kPathStaged = 1, kPathMfma = 2, kPathMc = 3 };
+
+struct Choice {
+  int path;
+  GemvPlan gemv;
+  BcastPlan bcast;
+  McPlan mc;
+  MfmaPlan mfma;
+};
+
+int choose_path(int fmt, int64_t M, int64_t N, int64_t K, Choice* out);
 
 // Workspace bytes for wqd_qgemm (0: no path needs scratch memory).
 int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out);
