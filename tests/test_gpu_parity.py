@@ -154,6 +154,22 @@ def test_qgemm_long_shares(fmt, N, K, waves):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_qgemm_two_blocks_per_wave(fmt):
+    """Streaming matrix-core kernel with two 16-row blocks per wavefront, an odd
+    block count (the last workgroup's second block is past N) and a ragged N."""
+    N, K, M = 16392, 1024, 6
+    assert wqd.kernel_path(fmt, M, N, K)[0] == "mc"
+    print(f"qgemm {fmt} M={M} N={N} K={K}", flush=True)
+    W = I.w_host(4000 + N, N, K)
+    qw = oracle.quantize(fmt, W)
+    pw = wqd.pack_weights(fmt, to_dev(W))
+    x = I.x_bf16_bits(23, M, K)
+    y = wqd.qgemm(x_dev(x), pw)
+    torch.cuda.synchronize()
+    compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("rows", [1, 2, 8])
 def test_one_hot_probes_exact(fmt, rows):
     """x = e_k gives y[:, n] = bf16(Wd[n, k]) exactly: ties the kernel's own dequant to the oracle.

@@ -52,14 +52,18 @@ __device__ __forceinline__ bf16x2_t u4x2_to_bf16x2_offset128(uint32_t w) {
   return __builtin_bit_cast(bf16x2_t, v);
 }
 
-// (a & mask) | orv in one VOP3 instruction.  Both constants must sit in
-// VGPRs: a gfx9 VOP3 instruction takes no literal and one scalar operand, so
-// left to itself the compiler splits this into v_and + v_or.
-__device__ __forceinline__ uint32_t and_or_v(uint32_t a, uint32_t mask, uint32_t orv) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(mask), "v"(orv));
-  return d;
+// (a & mask) | orv, which the compiler turns into one v_and_or_b32 when both
+// constants sit in VGPRs: a gfx9 VOP3 instruction takes no literal and one
+// scalar operand, so with literal constants it would split the operation
+// into v_and + v_or.  vgpr_const() makes a constant opaque so that it stays in
+// a VGPR.  Plain code (no inline assembly) keeps the result visible to the
+// compiler's hazard tracking, e.g. before a matrix-core instruction reads it.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  asm volatile("" : "+v"(c));
+  return c;
 }
+
+__device__ __forceinline__ uint32_t and_or_v(uint32_t a, uint32_t mask, uint32_t orv) { return (a & mask) | orv; }
 
 __device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);

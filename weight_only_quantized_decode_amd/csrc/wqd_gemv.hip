@@ -103,7 +103,7 @@ __device__ __forceinline__ void tile_dot(const Group<FMT, GT>& g, int i, int sl,
   using C = FmtC<FMT>;
   const uint32_t wd[4] = {g.w[i].x, g.w[i].y, g.w[i].z, g.w[i].w};
   if (FMT == kFmtW4) {
-    const uint32_t mask = 0x000F000Fu, magic = 0x43004300u;
+    const uint32_t mask = vgpr_const(0x000F000Fu), magic = vgpr_const(0x43004300u);
     float P[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m) P[m] = 0.f;

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int t = 0; t < TPC; ++t) {
       if (FMT == kFmtW4) {
-        const uint32_t mask = 0x000F000Fu, magic = 0x43004300u;
+        const uint32_t mask = vgpr_const(0x000F000Fu), magic = vgpr_const(0x43004300u);
         f32x4_t ag[BMS][BNT], xsum[BMS];
 #pragma unroll
         for (int i = 0; i < BMS; ++i) {
