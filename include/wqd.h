@@ -108,7 +108,7 @@ int wqd_packed_sizes(int fmt, int64_t N, int64_t K,
 int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes);
 
 /* Kernel families behind wqd_qgemm (wqd_kernel_path).  Which one serves a
- * shape: the broadcast kernel up to 2 W4A16 rows or 4 FP8 / BF16 rows; the
+ * shape: the broadcast kernel for 1 W4A16 row or up to 4 FP8 / BF16 rows; the
  * streaming matrix-core kernel up to 8 rows; otherwise, up to 8 rows, the
  * broadcast kernel, then the staged one; above 8 rows the LDS matrix-core
  * kernel.  Each streaming kernel also needs K short enough for its shares

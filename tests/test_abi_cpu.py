@@ -96,16 +96,16 @@ def test_workspace_query():
 
 def test_kernel_path_choice():
     """Which kernel family serves each decode shape (host planning only)."""
-    # broadcast kernel: 1-2 W4A16 rows, 1-4 FP8 / BF16 rows; more waves for small N
+    # broadcast kernel: 1 W4A16 row, 1-4 FP8 / BF16 rows; more waves for small N
     assert wqd.kernel_path("w4a16", 1, 8192, 8192) == ("bcast", 4)
     assert wqd.kernel_path("w4a16", 1, 28672, 8192) == ("bcast", 4)
     assert wqd.kernel_path("w4a16", 1, 1024, 8192) == ("bcast", 16)
     assert wqd.kernel_path("w4a16", 1, 8192, 28672) == ("bcast", 8)   # 224 tiles: shares of 28
-    assert wqd.kernel_path("w4a16", 2, 8192, 28672) == ("bcast", 16)  # two rows: shares of at most 16
     assert wqd.kernel_path("fp8", 4, 28672, 8192)[0] == "bcast"
     assert wqd.kernel_path("bf16", 2, 4096, 11008) == ("bcast", 16)   # 344 tiles: shares of 24
-    # streaming matrix-core kernel: 3-8 W4A16 rows, 5-8 FP8 / BF16 rows
-    for M in (3, 8):
+    # streaming matrix-core kernel: 2-8 W4A16 rows, 5-8 FP8 / BF16 rows
+    assert wqd.kernel_path("w4a16", 4, 57344, 8192) == ("mc", 4)
+    for M in (2, 3, 8):
         assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "mc"
     for M in (5, 8):
         assert wqd.kernel_path("fp8", M, 8192, 8192)[0] == "mc"

@@ -146,7 +146,7 @@ int choose_path(int fmt, int64_t M, int64_t N, int64_t K, Choice* out) {
   Choice c{};
   int st = plan_gemv(fmt, M, N, K, &c.gemv);
   if (st != kOK) return st;
-  const int64_t bcast_first = fmt == kFmtW4 ? 2 : 4;
+  const int64_t bcast_first = fmt == kFmtW4 ? 1 : 4;
   if (M <= bcast_first && plan_bcast(fmt, M, N, K, &c.bcast) == kOK) {
     c.path = kPathBcast;
   } else if (M <= kGemvMaxM && plan_mc(fmt, M, N, K, &c.mc) == kOK) {

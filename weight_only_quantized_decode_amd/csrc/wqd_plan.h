@@ -70,9 +70,9 @@ struct BcastPlan {
 
 int plan_bcast(int fmt, int64_t M, int64_t N, int64_t K, BcastPlan* out);
 
-// Streaming matrix-core kernel (M <= 16): the same work split, with the
-// products on bf16 matrix cores (x fragments read from L2 per tile).  Shares
-// of at most 32 tiles; kEUnsupported when K is too long for that or the x
+// Streaming matrix-core kernel (M <= 16): the same work split (4, 8 or 16
+// wavefronts per workgroup), with the products on bf16 matrix cores (x
+// fragments read from L2 per tile).  Shares of at most 32 tiles; kEUnsupported when K is too long for that or the x
 // rows span 2 GiB or more.
 constexpr int kMcMaxM = 16;
 
@@ -103,7 +103,7 @@ struct MfmaPlan {
 int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out);
 
 // The kernel family for a shape, in order of preference (measured on the
-// 70B shapes): the broadcast kernel for up to 2 W4A16 rows or 4 FP8 / BF16
+// 70B shapes): the broadcast kernel for 1 W4A16 row or up to 4 FP8 / BF16
 // rows; the streaming matrix-core kernel up to 8 rows; the broadcast kernel
 // again, then the staged one, up to 8 rows where the former cannot take the
 // shape; the LDS matrix-core kernel above 8 rows.
