@@ -3,14 +3,18 @@
 
 Default workload: the 70B-class decode stack (80 layers x q, k, v, o, gate, up,
 down; hidden 8192, GQA 8 KV heads of 128, FFN 28672) with W4A16-g128 weights,
-M = 1 activation row.  One step = the 560 y = x . dequant(W)^T calls of the
-stack, replayed from one HIP graph; the packed weights (~35.6 GB) are resident
-in HBM before timing starts, and the stack is far larger than the 256 MB
-last-level cache, so every step streams the weights from HBM.
+M = 1 activation row, in the fused layout a decode engine uses: q/k/v and
+gate/up each concatenated along N into one matrix (the same weights, bytes and
+results; 4 launches per layer instead of 7).  One step = every
+y = x . dequant(W)^T call of the stack, replayed from one HIP graph; the packed
+weights (~35.6 GB) are resident in HBM before timing starts, and the stack is
+far larger than the 256 MB last-level cache, so every step streams the
+weights from HBM.  The same stack in the separate layout (7 launches per
+layer) is timed in the same run and reported as "separate_layout".
 
 Prints ONE JSON line.  Options: --workload w4a16_70b | fp8_70b | bf16_7b |
-gemv4096 | verify:<fmt>:<mat>; --m (activation rows); --fused (q/k/v and
-gate/up concatenated, 4 launches per layer, identical bytes and results);
+gemv4096 | verify:<fmt>:<mat>; --m (activation rows); --separate (time the
+separate layout as the headline); --no-alt (skip the other layout);
 --pmc-probe (a short fixed launch sequence for hardware-counter runs).
 """
 from __future__ import annotations
@@ -35,7 +39,9 @@ def parse():
     ap.add_argument("--workload", default="w4a16_70b")
     ap.add_argument("--m", type=int, default=1)
     ap.add_argument("--layers", type=int, default=None)
-    ap.add_argument("--fused", action="store_true", help="q/k/v and gate/up as one matrix each")
+    ap.add_argument("--fused", action="store_true", help="q/k/v and gate/up as one matrix each (the default)")
+    ap.add_argument("--separate", action="store_true", help="q, k, v, gate, up as separate matrices")
+    ap.add_argument("--no-alt", action="store_true", help="do not also time the other layout")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
@@ -276,31 +282,16 @@ def pmc_probe():
     print(json.dumps({"pmc_probe": "done", "copy_bytes_each": 2 << 30, "gemv_launches": 16, "N": N, "K": K}))
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this decode layer is measured on a single MI355X "
-              "(multi-GPU sharding is a design note, not part of this build).", file=sys.stderr)
-        sys.exit(2)
+def time_stack(wl, args, with_shapes):
+    """Build the packed stack of `wl`, replay its step args.steps times after
+    args.warmup untimed steps (HIP events on the launch stream) and free it.
+    Returns (ms per step, whether a graph was replayed, per-shape breakdown)."""
     import torch
 
     import weight_only_quantized_decode_amd as wqd
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    wqd.lib()
-    if args.pmc_probe:
-        pmc_probe()
-        return
-    wl = make_workload(args)
     log(f"[bench] workload {wl.name}: {wl.launches} launches/step, {wl.step_bytes() / 1e9:.3f} GB/step")
-    ceiling = (None, None) if args.no_ceiling else hbm_ceiling()
-    if ceiling[0]:
-        log(f"[bench] HBM ceiling: read {ceiling[0]:.0f} GB/s, copy {ceiling[1]:.0f} GB/s")
     packed, xs, ys, ws = build_stack(wl)
-
     stream = torch.cuda.Stream()
 
     def step():
@@ -328,12 +319,53 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    shapes = shape_breakdown(wl, packed, xs, ys, ws, stream) if with_shapes else None
+    del graph, packed, xs, ys, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return ms, not args.no_graph, shapes
+
+
+def main():
+    args = parse()
+    args.fused = not args.separate
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this decode layer is measured on a single MI355X "
+              "(multi-GPU sharding is a design note, not part of this build).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import weight_only_quantized_decode_amd as wqd
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    wqd.lib()
+    if args.pmc_probe:
+        pmc_probe()
+        return
+    wl = make_workload(args)
+    ceiling = (None, None) if args.no_ceiling else hbm_ceiling()
+    if ceiling[0]:
+        log(f"[bench] HBM ceiling: read {ceiling[0]:.0f} GB/s, copy {ceiling[1]:.0f} GB/s")
+    ms, graph_used, shapes = time_stack(wl, args, with_shapes=not args.no_shapes)
+    alt = None
+    if not args.no_alt and wl.layers > 1 and args.workload in ("w4a16_70b", "fp8_70b", "bf16_7b"):
+        alt_args = argparse.Namespace(**vars(args))
+        alt_args.fused = not args.fused
+        alt_wl = make_workload(alt_args)
+        alt_ms, _, _ = time_stack(alt_wl, alt_args, with_shapes=False)
+        alt_gbps = alt_wl.step_bytes() / (alt_ms / 1e3) / 1e9
+        alt = {"workload": alt_wl.name, "launches_per_step": alt_wl.launches, "value": round(alt_gbps, 2),
+               "ms_per_step": round(alt_ms, 4), "kernel": kernel_label(alt_wl),
+               "pct_measured_read_ceiling": None if ceiling[0] is None else round(100 * alt_gbps / ceiling[0], 2)}
     step_bytes = wl.step_bytes()
     gbps = step_bytes / (ms / 1e3) / 1e9
     per_launch_bytes = step_bytes / wl.launches
     avg_launch_us = ms * 1e3 / wl.launches
     achieved = per_launch_bytes / (avg_launch_us / 1e6) / 1e9
-    shapes = None if args.no_shapes else shape_breakdown(wl, packed, xs, ys, ws, stream)
+    graph = graph_used
     out = {
         "metric": "weight-stream GB/s (% of HBM peak) & us per layer-stack step, 70B W4A16/FP8/BF16",
         "value": round(gbps, 2),
@@ -349,7 +381,7 @@ def main():
         "dtype": {"w4a16": "u4+bf16", "fp8": "e4m3+bf16", "bf16": "bf16"}[wl.fmt],
         "data": "synthetic",
         "config": {"workload": wl.name, "fmt": wl.fmt, "M": wl.M, "layers": wl.layers,
-                   "launches_per_step": wl.launches, "graph": graph is not None, "fused": args.fused,
+                   "launches_per_step": wl.launches, "graph": graph, "fused": args.fused,
                    "algorithmic_bytes_per_step": step_bytes},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "hbm_read_ceiling_GBps": None if ceiling[0] is None else round(ceiling[0], 1),
@@ -361,6 +393,8 @@ def main():
                      "avg_launch_us": round(avg_launch_us, 3),
                      "bytes_per_launch": round(per_launch_bytes)},
     }
+    if alt is not None:
+        out["separate_layout" if args.fused else "fused_layout"] = alt
     if shapes is not None:
         out["shapes"] = shapes
     if wl.M >= 16:
