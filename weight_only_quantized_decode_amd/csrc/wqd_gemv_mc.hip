@@ -11,8 +11,8 @@
 //
 // x fragments are read from L2 per tile through a buffer resource: lanes of
 // rows j >= M get an out-of-range offset and read zeros without touching
-// memory.  Weights run seven tiles ahead of the arithmetic and x two tiles
-// ahead; every load is unconditional (weights past the share are out of
+// memory.  Weights run seven tiles ahead of the arithmetic (three with two
+// row blocks per wavefront) and x two tiles ahead; every load is unconditional (weights past the share are out of
 // range of their buffer resource, x reads are clamped to the share) and the
 // tile steps are straight-line code, so the compiler's waits are exact.
 //
@@ -50,7 +50,7 @@ struct McC {
   static constexpr int SLK = TK / 4;                                             // K per slice
   static constexpr int XU = SLK / 8;  // x uint4 per lane and tile = matrix-core steps per tile
   static constexpr int LW = RB == 1 ? 7 : 3;  // tile steps whose weights are loaded ahead
-  static constexpr int LX = RB == 1 ? 2 : 1;  // x tiles loaded ahead
+  static constexpr int LX = 2;                // x tiles loaded ahead
   static constexpr int RW = LW + 1;           // ring sizes
   static constexpr int RX = LX + 1;
 };
