@@ -99,9 +99,9 @@ int wqd_packed_sizes(int fmt, int64_t N, int64_t K,
 
 /*
  * Host-only: bytes of scratch workspace wqd_qgemm needs for this shape (may
- * be 0).  Only the matrix-core path (M > 8) uses one, when it splits K over
- * workgroups: it holds their float32 partial tiles, which a second kernel
- * adds in split order.  Its contents on entry do not matter (every byte read
+ * be 0).  Only the matrix-core paths above 8 rows use one, when they split K
+ * over workgroups: it holds their float32 partial tiles (S * M * N * 4
+ * bytes), which a second kernel adds in split order.  Its contents on entry do not matter (every byte read
  * is written first in the same call).  One workspace must not be used by two
  * calls that can run at the same time.
  */
@@ -110,14 +110,17 @@ int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes)
 /* Kernel families behind wqd_qgemm (wqd_kernel_path).  Which one serves a
  * shape: the broadcast kernel for 1 W4A16 row or up to 4 FP8 / BF16 rows; the
  * streaming matrix-core kernel up to 8 rows; otherwise, up to 8 rows, the
- * broadcast kernel, then the staged one; above 8 rows the LDS matrix-core
- * kernel.  Each streaming kernel also needs K short enough for its shares
- * (hundreds of 16-row tiles). */
+ * broadcast kernel, then the staged one; from 9 to 32 rows the skinny
+ * matrix-core kernel (K a whole number of tiles: 128 W4A16, 64 FP8, 32 BF16);
+ * above that, or where the skinny kernel cannot take the shape, the LDS
+ * matrix-core kernel.  Each streaming kernel also needs K short enough for
+ * its shares (hundreds of 16-row tiles). */
 enum wqd_path {
     WQD_PATH_BCAST = 0,   /* streaming, x read per tile and broadcast across DPP rows */
     WQD_PATH_STAGED = 1,  /* streaming, x staged in LDS, dot2 products */
     WQD_PATH_MFMA = 2,    /* bf16 matrix cores, x staged in LDS, dequant on load */
-    WQD_PATH_MC = 3       /* streaming, bf16 matrix cores, x fragments read per tile */
+    WQD_PATH_MC = 3,      /* streaming, bf16 matrix cores, x fragments read per tile */
+    WQD_PATH_SKINNY = 4   /* bf16 matrix cores, x staged in LDS by a producer wavefront, shared by 8 row blocks */
 };
 
 /*

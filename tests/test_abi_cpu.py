@@ -84,10 +84,13 @@ def test_workspace_query():
     for fmt in ("bf16", "fp8", "w4a16"):
         for M in (1, 4, 8):
             assert wqd.workspace_bytes(fmt, M, 8192, 8192) == 0  # streaming kernel: none
-        # matrix-core path: split-K partials only when the tile grid is small
+        # matrix-core paths: split-K partials only when the row blocks give too few workgroups
         assert wqd.workspace_bytes(fmt, 1024, 28672, 8192) == 0
+        assert wqd.workspace_bytes(fmt, 16, 57344, 8192) == 0
         ws = wqd.workspace_bytes(fmt, 16, 8192, 8192)
-        assert ws > 0 and ws % (16 * 8192 * 4) == 0
+        assert ws > 0 and ws % (16 * 8192 * 4) == 0 and ws // (16 * 8192 * 4) <= 8
+        ws = wqd.workspace_bytes(fmt, 80, 8192, 8192)
+        assert ws > 0 and ws % (80 * 8192 * 4) == 0
     L = wqd.lib()
     assert L.wqd_workspace_bytes(2, 1, 64, 128, None) == E_ARG
     b = ctypes.c_size_t()
@@ -115,8 +118,13 @@ def test_kernel_path_choice():
     assert wqd.kernel_path("bf16", 1, 16, 16416)[0] == "staged"       # 513 tiles
     assert wqd.kernel_path("w4a16", 1, 16, 65664)[0] == "staged"
     assert wqd.kernel_path("w4a16", 5, 16, 65664)[0] == "staged"
-    # above 8 rows: the LDS matrix-core kernel
-    for M in (9, 16, 1024):
+    # 9 to 32 rows: the skinny matrix-core kernel (4 consumer wavefronts and a producer)
+    for M in (9, 16, 17, 32):
+        for fmt in ("w4a16", "fp8", "bf16"):
+            assert wqd.kernel_path(fmt, M, 8192, 8192) == ("skinny", 5)
+    assert wqd.kernel_path("fp8", 16, 8192, 8208)[0] == "mfma"          # K not a whole number of 64-k tiles
+    # above 32 rows: the LDS matrix-core kernel
+    for M in (33, 1024):
         assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "mfma"
     L = wqd.lib()
     p = ctypes.c_int()

@@ -169,8 +169,36 @@ def test_qgemm_two_blocks_per_wave(fmt):
     compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
+def skinny_shapes(fmt):
+    # (N, K) for the skinny matrix-core kernel, in tiles of TK k: 13 tiles (a
+    # share shorter than one loop body, few workgroups), 5 tiles over 385
+    # workgroups (no K split; the last workgroup has one live row block of 8),
+    # 4- and 8-way K splits (257 row blocks: a ragged last group), and a 7-way
+    # split whose last split is short (28 of 32 tiles)
+    tk = {"w4a16": 128, "fp8": 64, "bf16": 32}[fmt]
+    return [(2000, 13 * tk), (49160, 5 * tk), (4104, 64 * tk), (1000, 8192), (300, 220 * tk)]
+
+
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("rows", [1, 2, 8])
+def test_qgemm_skinny(fmt):
+    """x staged in LDS by a producer wavefront and shared by 4 consumer
+    wavefronts (two 16-row blocks each), K split over
+    workgroups with the fixed-order partial sum."""
+    for N, K in skinny_shapes(fmt):
+        W = I.w_host(5000 + N + K, N, K)
+        qw = oracle.quantize(fmt, W)
+        pw = wqd.pack_weights(fmt, to_dev(W))
+        for M in (9, 16, 17, 32):
+            assert wqd.kernel_path(fmt, M, N, K)[0] == "skinny"
+            print(f"qgemm {fmt} M={M} N={N} K={K} ws={wqd.workspace_bytes(fmt, M, N, K)}", flush=True)
+            x = I.x_bf16_bits(29 * M + K, M, K)
+            y = wqd.qgemm(x_dev(x), pw)
+            torch.cuda.synchronize()
+            compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rows", [1, 2, 8, 10, 16])
 def test_one_hot_probes_exact(fmt, rows):
     """x = e_k gives y[:, n] = bf16(Wd[n, k]) exactly: ties the kernel's own dequant to the oracle.
 
@@ -197,7 +225,7 @@ def test_one_hot_probes_exact(fmt, rows):
 def test_zero_weights_give_exact_zero(fmt):
     N, K = 130, 512
     pw = wqd.pack_weights(fmt, torch.zeros((N, K), dtype=torch.float32, device=dev()))
-    for M in (1, 2, 4, 16):
+    for M in (1, 2, 4, 16, 40, 64):
         y = wqd.qgemm(x_dev(I.x_bf16_bits(3 + M, M, K)), pw)
         torch.cuda.synchronize()
         assert (y.float() == 0).all(), M
@@ -208,7 +236,7 @@ def test_deterministic_and_every_output_written(fmt):
     N, K = 1000, 2048
     W = I.w_host(9, N, K)
     pw = wqd.pack_weights(fmt, to_dev(W))
-    for M in (1, 5, 8):
+    for M in (1, 5, 8, 24, 40):
         x = x_dev(I.x_bf16_bits(10 + M, M, K))
         y1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
         y2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())

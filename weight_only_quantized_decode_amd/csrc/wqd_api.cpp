@@ -77,6 +77,7 @@ int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* wa
     *waves = c.path == wqd::kPathBcast ? c.bcast.waves
            : c.path == wqd::kPathMc    ? c.mc.waves
            : c.path == wqd::kPathStaged ? c.gemv.waves
+           : c.path == wqd::kPathSkinny ? c.sk.waves + 1
                                         : 4;
   }
   return WQD_OK;
@@ -104,7 +105,7 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const voi
   if (!wqd::aligned16(x) || !wqd::aligned16(y)) return WQD_E_ALIGN;
   st = check_packed_ptrs(fmt, w_packed, scales, zeros);
   if (st != WQD_OK) return st;
-  const size_t need = c.path == wqd::kPathMfma ? c.mfma.ws_bytes : 0;
+  const size_t need = c.path == wqd::kPathMfma ? c.mfma.ws_bytes : c.path == wqd::kPathSkinny ? c.sk.ws_bytes : 0;
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return WQD_E_WORKSPACE;
     if (!wqd::aligned16(workspace)) return WQD_E_ALIGN;
@@ -117,6 +118,8 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const voi
       return hip_status(wqd::launch_gemv_mc(fmt, c.mc, x, M, N, K, w_packed, scales, zeros, y, s));
     case wqd::kPathStaged:
       return hip_status(wqd::launch_gemv(fmt, c.gemv, x, M, N, K, w_packed, scales, zeros, y, s));
+    case wqd::kPathSkinny:
+      return hip_status(wqd::launch_gemv_sk(fmt, c.sk, x, M, N, K, w_packed, scales, zeros, y, workspace, s));
     default:
       return hip_status(wqd::launch_mfma(fmt, c.mfma, M, N, K, x, w_packed, scales, zeros, y, workspace, s));
   }

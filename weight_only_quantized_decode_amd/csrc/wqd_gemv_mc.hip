@@ -160,6 +160,18 @@ __device__ __forceinline__ void mc_compute(McState<FMT, RB>& st) {
   }
 }
 
+// Prologue: weight tiles 0 .. LW - 1 and x tiles 0 .. LX - 1, the weights and
+// x of one tile issued together (loads complete in issue order).
+template <int FMT, int RB, int NT, int T>
+__device__ __forceinline__ void mc_prologue(McState<FMT, RB>& st) {
+  using C = McC<FMT, RB>;
+  if constexpr (T < NT && (T < C::LW || T < C::LX)) {
+    if constexpr (T < C::LW) mc_load_w<FMT, RB, T>(st);
+    if constexpr (T < C::LX) mc_load_x<FMT, RB, T>(st);
+    mc_prologue<FMT, RB, NT, T + 1>(st);
+  }
+}
+
 // Tiles T .. NT - 1 as straight-line code with early exits: each step loads
 // the weights LW tiles ahead, x LX tiles ahead and (W4A16, every fourth tile)
 // the scale / zero quad two ahead, then multiplies tile T.
@@ -223,15 +235,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mc_kernel(McArgs a) {
       mc_load_sz<FMT, RB, 0>(st);
       if constexpr (NT > 4) mc_load_sz<FMT, RB, 1>(st);
     }
-    mc_load_w<FMT, RB, 0>(st);
-    mc_load_x<FMT, RB, 0>(st);
-    if constexpr (NT > 1) mc_load_w<FMT, RB, 1>(st);
-    if constexpr (NT > 1) mc_load_x<FMT, RB, 1>(st);
-    if constexpr (NT > 2) mc_load_w<FMT, RB, 2>(st);
-    if constexpr (C::LW > 3 && NT > 3) mc_load_w<FMT, RB, 3>(st);
-    if constexpr (C::LW > 4 && NT > 4) mc_load_w<FMT, RB, 4>(st);
-    if constexpr (C::LW > 5 && NT > 5) mc_load_w<FMT, RB, 5>(st);
-    if constexpr (C::LW > 6 && NT > 6) mc_load_w<FMT, RB, 6>(st);
+    mc_prologue<FMT, RB, NT, 0>(st);
     __builtin_amdgcn_sched_barrier(0);
     mc_tiles<FMT, RB, NT, 0>(st);
   }

@@ -291,6 +291,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   y[i] = uint16_t(f32_to_bf16_rne(v));
 }
 
+hipError_t launch_splitk_reduce(int fmt, const float* part, int S, int64_t M, int64_t N, const void* scales, void* y,
+                                hipStream_t st) {
+  const int64_t total = M * N;
+  const dim3 grid(unsigned((total + 255) / 256));
+  const float* cs = reinterpret_cast<const float*>(scales);
+  uint16_t* yo = reinterpret_cast<uint16_t*>(y);
+  if (fmt == kFmtFP8)
+    hipLaunchKernelGGL(splitk_reduce_kernel<kFmtFP8>, grid, dim3(256), 0, st, part, S, M, N, cs, yo);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<kFmtBF16>, grid, dim3(256), 0, st, part, S, M, N, cs, yo);
+  return hipGetLastError();
+}
+
 template <int FMT, int BMS, int BNT>
 static hipError_t launch_mf(MfmaArgs a, hipStream_t st) {
   const int64_t nbb8 = ceil_div(a.NBB, 8) * 8;
@@ -298,10 +311,7 @@ static hipError_t launch_mf(MfmaArgs a, hipStream_t st) {
   hipLaunchKernelGGL((mfma_kernel<FMT, BMS, BNT>), dim3(unsigned(grid), unsigned(a.S)), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.S == 1) return e;
-  const int64_t total = a.M * a.N;
-  hipLaunchKernelGGL(splitk_reduce_kernel<FMT>, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st, a.part, a.S,
-                     a.M, a.N, reinterpret_cast<const float*>(a.scales), a.y);
-  return hipGetLastError();
+  return launch_splitk_reduce(FMT, a.part, a.S, a.M, a.N, a.scales, a.y, st);
 }
 
 template <int FMT>

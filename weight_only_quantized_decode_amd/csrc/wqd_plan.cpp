@@ -106,6 +106,47 @@ int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out) {
   return kOK;
 }
 
+// Skinny kernel: 4 consumer wavefronts per workgroup, two row blocks each
+// (x fragments reused in registers); a ring of 8 weight
+// tiles per row block and x chunks of 4 tiles, triple-buffered for 16 rows
+// (so a chunk's x loads have two chunks of time to land), double-buffered
+// for 32 (LDS).  K is split while the launch has fewer than ~1.5 workgroups per
+// compute unit, keeping every split at least 2 rings long and at most 8
+// splits (each adds M * N * 8 bytes of partial traffic).
+int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
+  PackedSizes ps;
+  int st = packed_sizes(fmt, N, K, &ps);
+  if (st != kOK) return st;
+  if (M < 1) return kEArg;
+  if (M > kSkMaxM || M * K * 2 >= (int64_t(1) << 31)) return kEUnsupported;
+  if (K % tile_k(fmt) != 0) return kEUnsupported;
+  SkPlan p{};
+  p.NB = ps.NB;
+  p.KT = ps.KT;
+  p.mf = int(ceil_div(M, 16));
+  p.rb = 2;
+  p.waves = 4;
+  p.ring = 8;
+  p.ct = 4;
+  p.nx = p.mf == 1 ? 3 : 2;
+  p.groups = ceil_div(p.NB, int64_t(p.waves) * p.rb);
+  const int64_t body = p.ring;
+  int64_t S = 1;
+  const int64_t target = 384;
+  if (p.groups < target) {
+    S = ceil_div(target, p.groups);
+    const int64_t max_s = p.KT / (2 * body) > 1 ? p.KT / (2 * body) : 1;
+    if (S > max_s) S = max_s;
+    if (S > 8) S = 8;
+  }
+  const int64_t per = ceil_div(ceil_div(p.KT, S), body) * body;
+  p.per_split = int(per);
+  p.S = int(ceil_div(p.KT, per));
+  p.ws_bytes = p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;
+  *out = p;
+  return kOK;
+}
+
 // Tiles per chunk of the matrix-core kernel: the staged x chunk is 16 KiB
 // (16 * BMS rows), at most 8 tiles.
 static int mfma_tpc(int fmt, int bms) {
@@ -155,6 +196,8 @@ int choose_path(int fmt, int64_t M, int64_t N, int64_t K, Choice* out) {
     c.path = kPathBcast;
   } else if (M <= kGemvMaxM) {
     c.path = kPathStaged;
+  } else if (M <= kSkMaxM && plan_skinny(fmt, M, N, K, &c.sk) == kOK) {
+    c.path = kPathSkinny;
   } else {
     st = plan_mfma(fmt, M, N, K, &c.mfma);
     if (st != kOK) return st;
@@ -168,7 +211,7 @@ int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out) {
   Choice c;
   int st = choose_path(fmt, M, N, K, &c);
   if (st != kOK) return st;
-  *out = c.path == kPathMfma ? c.mfma.ws_bytes : 0;
+  *out = c.path == kPathMfma ? c.mfma.ws_bytes : c.path == kPathSkinny ? c.sk.ws_bytes : 0;
   return kOK;
 }
 

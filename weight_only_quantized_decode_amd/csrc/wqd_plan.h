@@ -84,7 +84,24 @@ struct McPlan {
 
 int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out);
 
+// Skinny matrix-core kernel (9 to 32 rows): a workgroup of `waves` consumer
+// wavefronts (plus one that stages x in LDS) owns waves x rb 16-row blocks
+// (`groups` workgroups cover the matrix), mf 16-row blocks of x, and chunks
+// of ct tiles.  K is split S ways (per_split tiles each, a multiple of ring)
+// when the row blocks alone give too few workgroups; the S float32 partials
+// then need S * M * N * 4 bytes of workspace.  kEUnsupported above 32 rows,
+// for x rows spanning 2 GiB or more, and for K not a whole number of tiles.
+constexpr int kSkMaxM = 32;
 
+struct SkPlan {
+  int64_t NB, KT, groups;
+  int mf, rb, waves;
+  int ring, ct, nx;  // weight ring slots (tiles), tiles per x chunk, x chunk buffers
+  int S, per_split;
+  size_t ws_bytes;
+};
+
+int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out);
 
 // Matrix-core kernel (M > 8): workgroup tile = 16 * BMS rows of x times
 // 4 wavefronts x BNT 16-column tiles; the K loop advances in chunks of TPC
@@ -106,14 +123,17 @@ int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out);
 // 70B shapes): the broadcast kernel for 1 W4A16 row or up to 4 FP8 / BF16
 // rows; the streaming matrix-core kernel up to 8 rows; the broadcast kernel
 // again, then the staged one, up to 8 rows where the former cannot take the
-// shape; the LDS matrix-core kernel above 8 rows.
-enum Path { kPathBcast = 0, kPathStaged = 1, kPathMfma = 2, kPathMc = 3 };
+// shape; the skinny matrix-core kernel from 9 to 32 rows; the LDS
+// matrix-core kernel above that (or where the skinny one cannot take the
+// shape).
+enum Path { kPathBcast = 0, kPathStaged = 1, kPathMfma = 2, kPathMc = 3, kPathSkinny = 4 };
 
 struct Choice {
   int path;
   GemvPlan gemv;
   BcastPlan bcast;
   McPlan mc;
+  SkPlan sk;
   MfmaPlan mfma;
 };
 
