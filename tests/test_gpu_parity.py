@@ -170,13 +170,15 @@ def test_qgemm_two_blocks_per_wave(fmt):
 
 
 def skinny_shapes(fmt):
-    # (N, K) for the skinny matrix-core kernel, in tiles of TK k: 13 tiles (a
-    # share shorter than one loop body, few workgroups), 5 tiles over 385
-    # workgroups (no K split; the last workgroup has one live row block of 8),
-    # 4- and 8-way K splits (257 row blocks: a ragged last group), and a 7-way
-    # split whose last split is short (28 of 32 tiles)
+    # (N, K) for the skinny matrix-core kernel, in tiles of TK k.  With the
+    # planner's choices: 13 tiles (shares shorter than one loop body; 7
+    # consumers of one row block), 5 tiles over 3073 row blocks (7 consumers
+    # of two row blocks, no K split, a half-live last workgroup), 512 row blocks
+    # of 64 tiles (4 consumers of two row blocks, 4-way K split), 257 and 63 row
+    # blocks (ragged last groups, K splits), and a 7-way split whose last split
+    # is short (28 of 32 tiles)
     tk = {"w4a16": 128, "fp8": 64, "bf16": 32}[fmt]
-    return [(2000, 13 * tk), (49160, 5 * tk), (4104, 64 * tk), (1000, 8192), (300, 220 * tk)]
+    return [(2000, 13 * tk), (49160, 5 * tk), (8192, 64 * tk), (4104, 64 * tk), (1000, 8192), (300, 220 * tk)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)

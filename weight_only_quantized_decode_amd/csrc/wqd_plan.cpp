@@ -106,13 +106,44 @@ int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out) {
   return kOK;
 }
 
-// Skinny kernel: 4 consumer wavefronts per workgroup, two row blocks each
-// (x fragments reused in registers); a ring of 8 weight
-// tiles per row block and x chunks of 4 tiles, triple-buffered for 16 rows
-// (so a chunk's x loads have two chunks of time to land), double-buffered
-// for 32 (LDS).  K is split while the launch has fewer than ~1.5 workgroups per
-// compute unit, keeping every split at least 2 rings long and at most 8
-// splits (each adds M * N * 8 bytes of partial traffic).
+// Skinny kernel: consumer wavefronts per workgroup and row blocks per consumer
+// from (7, 2), (7, 1), (4, 2) (x chunks shared by 14, 7 or 8 row blocks); a
+// ring of 8 weight tiles per row block; x chunks of 4 tiles (2 for 32 rows of
+// W4A16, which would otherwise need 100 KiB of LDS), three buffers.  K is
+// split so that the launch has about as many workgroups as compute units
+// (S = units / groups: a second workgroup on only some units would make them
+// the tail), keeping every split at least 2 rings long and at most 8 splits
+// (each adds M * N * 8 bytes of partial traffic).  The configuration whose
+// workgroups fill whole multiples of the compute units best wins; near ties
+// go to the earlier one (measured on the 70B shapes).
+constexpr int64_t kComputeUnits = 256;  // MI355X
+
+static int plan_skinny_with(int fmt, int64_t M, const PackedSizes& ps, int waves, int rb, int64_t S, SkPlan* out) {
+  SkPlan p{};
+  p.NB = ps.NB;
+  p.KT = ps.KT;
+  p.mf = int(ceil_div(M, 16));
+  p.rb = rb;
+  p.waves = waves;
+  p.ring = 8;
+  p.ct = (fmt == kFmtW4 && p.mf == 2) ? 2 : 4;
+  p.nx = 3;
+  p.groups = ceil_div(p.NB, int64_t(p.waves) * p.rb);
+  const int64_t body = p.ring;
+  if (S < 1) {
+    S = kComputeUnits / p.groups;
+    const int64_t max_s = p.KT / (2 * body);
+    if (S > max_s) S = max_s;
+    if (S > 8) S = 8;
+    if (S < 1) S = 1;
+  }
+  const int64_t per = ceil_div(ceil_div(p.KT, S), body) * body;
+  p.per_split = int(per);
+  p.S = int(ceil_div(p.KT, per));
+  *out = p;
+  return kOK;
+}
+
 int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
   PackedSizes ps;
   int st = packed_sizes(fmt, N, K, &ps);
@@ -120,28 +151,20 @@ int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
   if (M < 1) return kEArg;
   if (M > kSkMaxM || M * K * 2 >= (int64_t(1) << 31)) return kEUnsupported;
   if (K % tile_k(fmt) != 0) return kEUnsupported;
+  if (ps.s_bytes >= (size_t(1) << 31) || ps.z_bytes >= (size_t(1) << 31)) return kEUnsupported;
+  static const int kCfg[3][2] = {{7, 2}, {7, 1}, {4, 2}};
   SkPlan p{};
-  p.NB = ps.NB;
-  p.KT = ps.KT;
-  p.mf = int(ceil_div(M, 16));
-  p.rb = 2;
-  p.waves = 4;
-  p.ring = 8;
-  p.ct = 4;
-  p.nx = p.mf == 1 ? 3 : 2;
-  p.groups = ceil_div(p.NB, int64_t(p.waves) * p.rb);
-  const int64_t body = p.ring;
-  int64_t S = 1;
-  const int64_t target = 384;
-  if (p.groups < target) {
-    S = ceil_div(target, p.groups);
-    const int64_t max_s = p.KT / (2 * body) > 1 ? p.KT / (2 * body) : 1;
-    if (S > max_s) S = max_s;
-    if (S > 8) S = 8;
+  double best = -1.0;
+  for (const auto& cfg : kCfg) {
+    SkPlan q;
+    plan_skinny_with(fmt, M, ps, cfg[0], cfg[1], 0, &q);
+    const int64_t W = q.groups * q.S;
+    const double fill = double(W) / double(ceil_div(W, kComputeUnits) * kComputeUnits);
+    if (fill > best + 0.02) {
+      best = fill;
+      p = q;
+    }
   }
-  const int64_t per = ceil_div(ceil_div(p.KT, S), body) * body;
-  p.per_split = int(per);
-  p.S = int(ceil_div(p.KT, per));
   p.ws_bytes = p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;
   *out = p;
   return kOK;

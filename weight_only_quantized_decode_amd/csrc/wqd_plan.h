@@ -85,7 +85,8 @@ struct McPlan {
 int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out);
 
 // Skinny matrix-core kernel (9 to 32 rows): a workgroup of `waves` consumer
-// wavefronts (plus one that stages x in LDS) owns waves x rb 16-row blocks
+// wavefronts (plus a producer that stages x, scales and zero points in LDS
+// and computes the W4A16 x sums) owns waves x rb 16-row blocks
 // (`groups` workgroups cover the matrix), mf 16-row blocks of x, and chunks
 // of ct tiles.  K is split S ways (per_split tiles each, a multiple of ring)
 // when the row blocks alone give too few workgroups; the S float32 partials

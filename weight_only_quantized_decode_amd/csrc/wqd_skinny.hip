@@ -10,28 +10,34 @@
 // wavefront.  Design for gfx950:
 //   * a workgroup owns WN x RB consecutive 16-row blocks over a range of K.
 //     WN consumer wavefronts each stream RB row blocks; one producer
-//     wavefront stages x;
-//   * x is staged per chunk of CT tiles in LDS (NX buffers: the producer
-//     runs NX - 1 chunks ahead) by the producer
+//     wavefront does everything else;
+//   * the producer stages x per chunk of CT tiles in LDS (NX = 3 buffers)
 //     with direct-to-LDS buffer loads, already in matrix-core fragment order:
 //     fragment (tile t, row block of x i, K-step s) is 1 KiB, lane
 //     16 kb + j holding the 8 k of activation row 16 i + j that the bf16
 //     instruction v_mfma_f32_16x16x32_bf16 pairs with slice kb of the weight
-//     tile.  Consumers read it back as one conflict-free 16-byte LDS read
-//     per lane.  Rows at or past M read zeros (out-of-range buffer offsets),
+//     tile, read back by the consumers as one conflict-free 16-byte LDS read
+//     per lane.  Rows at or past M read zeros (out-of-range buffer offsets)
 //     and only feed output rows that are never stored;
-//   * the producer waits on its own load counter before each chunk barrier.
-//     Consumers never issue x loads, so their in-order load counter holds
-//     weights only and the arithmetic waits for exactly the tile it needs;
+//   * W4A16: the producer also stages the fp16 scales and uint4 zero points
+//     of the workgroup's row blocks (one 4-group quad at a time) and computes
+//     X = x . 1 per tile with the all-ones B operand, so that a tile
+//     contributes s * (P - (128 + z) * X) with P = x . (128 + q) from the
+//     consumers' identical chain of matrix-core steps (q == z == 0 cancels
+//     exactly).  Consumers thus issue nothing but weight loads: their in-order
+//     load counter holds weights only, so the arithmetic waits for exactly the
+//     tile it needs;
+//   * the producer works one chunk ahead: between the barriers that open
+//     chunks c - 1 and c it computes X of chunk c (landed) and issues the
+//     loads of chunk c + 1;
 //   * consumers keep R weight tiles per row block in a register ring, R - 1
 //     of them in flight (loads past the range are out of range of their
-//     buffer resource: no traffic, zeros); the loop body is one ring (a whole
-//     number of chunks), so every ring slot is a compile-time constant;
-//   * products and dequantisation as in the streaming matrix-core kernel:
-//     W4A16 nibble pairs become bf16 (128 + q) with one AND-OR, a tile
-//     contributes s * (P - (128 + z) * X) with X = x . 1 from a chain of the
-//     same shape (exact cancellation for q == z == 0); FP8 codes convert
-//     exactly, the row scale is applied once at the end; BF16 feeds as is;
+//     buffer resource: no traffic, zeros; the tile offset rides in the scalar
+//     offset, so a load costs no vector arithmetic); the loop body is one
+//     ring (a whole number of chunks), so every ring slot is a compile-time
+//     constant;
+//   * FP8 codes convert exactly to bf16 and the row scale is applied once at
+//     the end; BF16 feeds the matrix cores as loaded;
 //   * when the row blocks alone give too few workgroups, K is split S ways
 //     over grid y; the float32 partials go to the workspace and the fixed-order
 //     split-K sum of the matrix-core path finishes them (deterministic, no
@@ -50,6 +56,8 @@ __device__ __forceinline__ sk_f32x4_t sk_mfma(uint4 a, uint4 b, sk_f32x4_t c) {
                                                  __builtin_bit_cast(sk_bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) void* sk_lds_ptr;
+
 struct SkArgs {
   const uint16_t* x;
   uint16_t* y;
@@ -58,7 +66,7 @@ struct SkArgs {
   const void* scales;
   const uint16_t* zeros;
   int64_t M, N, K, KT, G4, NB;
-  int per_split;  // tiles per split, a multiple of the ring size
+  int per_split;  // tiles per split, a multiple of the ring size and of 4
   int S;
 };
 
@@ -69,75 +77,57 @@ struct SkF {
   static constexpr int STEPS = SLK / 8;  // 32-k matrix-core steps per tile
 };
 
-template <int FMT, int MF, int CT>
+// LDS layout, in uint4 units: NX x chunks, then (W4A16) NX x-sum buffers
+// (16 bytes per tile, x row block and slice) and 3 scale / zero quad buffers
+// (BR = WN * RB row blocks x 16 rows: 8 bytes of scales, 2 of zeros; room
+// for a whole number of 8-row-block groups, one staging load each).
+template <int FMT, int MF, int CT, int NX, int BR>
 struct SkL {
   static constexpr int FRAGS = CT * MF * SkF<FMT>::STEPS;  // 1 KiB fragments per chunk
-  static constexpr int BUF = FRAGS * 64;                    // uint4 per LDS buffer
+  static constexpr int XBUF = FRAGS * 64;
+  static constexpr int SBUF = CT * MF * 4;
+  static constexpr int QG = (BR + 7) / 8;  // groups of 8 row blocks
+  static constexpr int QS = QG * 64, QZ = QG * 16, QBUF = QS + QZ;
+  static constexpr int X0 = 0, XS0 = NX * XBUF, Q0 = XS0 + (FMT == kFmtW4 ? NX * SBUF : 0);
+  static constexpr int TOTAL = Q0 + (FMT == kFmtW4 ? 3 * QBUF : 0);
 };
-
-// Producer: stage the x fragments of tiles kt .. kt + CT - 1 into buf.
-template <int FMT, int MF, int CT>
-__device__ __forceinline__ void sk_stage(const SkArgs& a, __amdgpu_buffer_rsrc_t xres, uint4* buf, int64_t kt,
-                                         int lane) {
-  using F = SkF<FMT>;
-  const int kb = lane >> 4, j = lane & 15;
-#pragma unroll
-  for (int f = 0; f < SkL<FMT, MF, CT>::FRAGS; ++f) {
-    const int t = f / (MF * F::STEPS), i = (f / F::STEPS) % MF, s = f % F::STEPS;
-    const int64_t row = 16 * i + j;
-    const int64_t k = (kt + t) * F::TK + kb * F::SLK + 8 * s;
-    const uint32_t off = row < a.M && k < a.K ? uint32_t((row * a.K + k) * 2) : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (__attribute__((address_space(3))) void*)(buf + f * 64), 16, off,
-                                             0, 0, 0);
-  }
-}
 
 template <int FMT, int MF, int RB, int R>
 struct SkState {
-  uint4 w[R][RB];                 // ring of R weight tiles per row block
-  uint32_t sw[R][RB], zw[R][RB];  // W4A16: fp16 scale bits and zero quad of the tile's group
+  uint4 w[R][RB];  // ring of R weight tiles per row block
   sk_f32x4_t acc[MF][RB];
-  __amdgpu_buffer_rsrc_t wres[RB], sres[RB], zres[RB];
-  const uint4* xb;      // LDS buffer of the current chunk
-  uint32_t soff, zoff;  // this lane's byte offsets inside a scale / zero quad column
-  int64_t kt0;
-  int lane, total;
+  __amdgpu_buffer_rsrc_t wres[RB];
+  const uint4* xb;      // LDS: x fragments of the current chunk
+  const uint4* xs;      // LDS: x sums of the current chunk
+  const uint16_t* sq;   // LDS: scale quads of the current chunk's quad, [BR][16][4] fp16
+  const uint16_t* zq;   // LDS: zero quads, [BR][16] (4 nibbles)
+  int lane, rbl, total;  // rbl: this wavefront's first row block inside the workgroup
 };
 
-// Weights (and W4A16 scale / zero) of tile T into ring slot SLOT = T % R.
 template <int FMT, int MF, int RB, int R, int SLOT>
 __device__ __forceinline__ void sk_load(SkState<FMT, MF, RB, R>& st, int T) {
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     // cache policy 2: non-temporal (weights are read once per step)
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(st.wres[b], uint32_t(T) * kTileBytes + st.lane * 16, 0, 2);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(st.wres[b], st.lane * 16, T * kTileBytes, 2);
     st.w[SLOT][b] = make_uint4(v.x, v.y, v.z, v.w);
-    if constexpr (FMT == kFmtW4) {
-      const int64_t kt = st.kt0 + T;
-      const uint32_t q = uint32_t(kt / kScaleQuad);
-      st.sw[SLOT][b] = __builtin_amdgcn_raw_buffer_load_b16(
-          st.sres[b], (q * kTileRows) * (kScaleQuad * 2) + st.soff + uint32_t(kt % kScaleQuad) * 2, 0, 0);
-      st.zw[SLOT][b] = __builtin_amdgcn_raw_buffer_load_b16(st.zres[b], q * (kTileRows * 2) + st.zoff, 0, 0);
-    }
   }
 }
 
-// Multiply the tile in ring slot SLOT: tile SLOT % CT of the chunk in st.xb.
+// Multiply tile T in ring slot SLOT: tile SLOT % CT of the current chunk.
 template <int FMT, int MF, int RB, int R, int CT, int SLOT>
-__device__ __forceinline__ void sk_compute(SkState<FMT, MF, RB, R>& st) {
+__device__ __forceinline__ void sk_compute(SkState<FMT, MF, RB, R>& st, int T) {
   using F = SkF<FMT>;
   constexpr int t = SLOT % CT;
+  const int kb = st.lane >> 4, n = st.lane & 15;
   const uint4* xf = st.xb + (t * MF) * F::STEPS * 64 + st.lane;  // fragment (t, i, s) at xf[(i * STEPS + s) * 64]
   if constexpr (FMT == kFmtW4) {
     const uint32_t mask = vgpr_const(0x000F000Fu), magic = vgpr_const(0x43004300u);
-    const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-    sk_f32x4_t X[MF], P[MF][RB];
+    sk_f32x4_t P[MF][RB];
 #pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      X[i] = sk_f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < MF; ++i)
 #pragma unroll
       for (int b = 0; b < RB; ++b) P[i][b] = sk_f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint4 bm[RB];
@@ -151,21 +141,26 @@ __device__ __forceinline__ void sk_compute(SkState<FMT, MF, RB, R>& st) {
 #pragma unroll
       for (int i = 0; i < MF; ++i) {
         const uint4 af = xf[(i * 4 + s) * 64];
-        X[i] = sk_mfma(af, ones, X[i]);
 #pragma unroll
         for (int b = 0; b < RB; ++b) P[i][b] = sk_mfma(af, bm[b], P[i][b]);
       }
     }
     // splits start on a scale quad and R is a multiple of 4, so the tile's
-    // place in its quad is SLOT % 4
+    // place in its quad is SLOT % 4; tiles past the range get scale 0
+    const bool live = T < st.total;
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-      const float sc = __half2float(__ushort_as_half(uint16_t(st.sw[SLOT][b])));
-      const float zc = 128.0f + float((st.zw[SLOT][b] >> (4 * (SLOT % kScaleQuad))) & 0xFu);
+      const int row = (st.rbl + b) * 16 + n;
+      const float s0 = __half2float(__ushort_as_half(st.sq[row * kScaleQuad + SLOT % kScaleQuad]));
+      const float sc = live ? s0 : 0.f;
+      const float zc = 128.0f + float((uint32_t(st.zq[row]) >> (4 * (SLOT % kScaleQuad))) & 0xFu);
 #pragma unroll
-      for (int i = 0; i < MF; ++i)
+      for (int i = 0; i < MF; ++i) {
+        const uint4 xq = st.xs[(t * MF + i) * 4 + kb];
+        const sk_f32x4_t X = __builtin_bit_cast(sk_f32x4_t, xq);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st.acc[i][b][r] = fmaf(sc, fmaf(-zc, X[i][r], P[i][b][r]), st.acc[i][b][r]);
+        for (int r = 0; r < 4; ++r) st.acc[i][b][r] = fmaf(sc, fmaf(-zc, X[r], P[i][b][r]), st.acc[i][b][r]);
+      }
     }
   } else if constexpr (FMT == kFmtFP8) {
 #pragma unroll
@@ -199,22 +194,30 @@ __device__ __forceinline__ void sk_compute(SkState<FMT, MF, RB, R>& st) {
 
 // Steps I .. R - 1 of a loop body starting at tile T0.  Step T waits at the
 // chunk barrier when T starts a chunk, loads tile T + R - 1 into the slot tile
-// T - 1 has freed, then multiplies tile T; tiles past the range load zeros
-// and are not multiplied.
-template <int FMT, int MF, int RB, int R, int CT, int NX, int I>
-__device__ __forceinline__ void sk_steps(SkState<FMT, MF, RB, R>& st, uint4* s_x, int T0) {
+// T - 1 has freed, then multiplies tile T.  Tiles past the range load zeros
+// and multiply to zero (W4A16: scale 0).
+template <int FMT, int MF, int RB, int R, int CT, int NX, int BR, int I>
+__device__ __forceinline__ void sk_steps(SkState<FMT, MF, RB, R>& st, uint4* lds, int T0) {
+  using L = SkL<FMT, MF, CT, NX, BR>;
   if constexpr (I < R) {
     const int T = T0 + I;
     if constexpr (I % CT == 0) {
-      __syncthreads();  // chunk T / CT staged; everyone is done with the buffer it replaces
-      st.xb = s_x + ((T / CT) % NX) * SkL<FMT, MF, CT>::BUF;
+      __syncthreads();  // chunk T / CT staged; everyone is done with the buffers it replaces
+      const int c = T / CT, xbuf = c % NX;
+      st.xb = lds + L::X0 + xbuf * L::XBUF;
+      if constexpr (FMT == kFmtW4) {
+        st.xs = lds + L::XS0 + xbuf * L::SBUF;
+        const uint4* qb = lds + L::Q0 + ((T / kScaleQuad) % 3) * L::QBUF;
+        st.sq = reinterpret_cast<const uint16_t*>(qb);
+        st.zq = reinterpret_cast<const uint16_t*>(qb + L::QS);
+      }
     }
     sk_load<FMT, MF, RB, R, (I + R - 1) % R>(st, T + R - 1);
     // keep the loads here: left to itself the scheduler sinks them to just
     // before their use, which would leave nothing in flight during the math
     __builtin_amdgcn_sched_barrier(0);
-    if (T < st.total) sk_compute<FMT, MF, RB, R, CT, I>(st);
-    sk_steps<FMT, MF, RB, R, CT, NX, I + 1>(st, s_x, T0);
+    sk_compute<FMT, MF, RB, R, CT, I>(st, T);
+    sk_steps<FMT, MF, RB, R, CT, NX, BR, I + 1>(st, lds, T0);
   }
 }
 
@@ -227,18 +230,73 @@ __device__ __forceinline__ void sk_prologue(SkState<FMT, MF, RB, R>& st) {
   }
 }
 
-// Producer wait: at most N loads of this wavefront still in flight.
-template <int N>
-__device__ __forceinline__ void sk_wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt holds 0 .. 63");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+// Producer: issue the direct-to-LDS loads of chunk c (tiles kt0 + c CT ..):
+// its x fragments and, when it starts a scale quad, the workgroup's scale
+// and zero quads.
+template <int FMT, int MF, int CT, int NX, int BR>
+__device__ __forceinline__ void sk_stage(const SkArgs& a, __amdgpu_buffer_rsrc_t xres, __amdgpu_buffer_rsrc_t sres,
+                                         __amdgpu_buffer_rsrc_t zres, uint4* lds, int64_t kt0, int c, int64_t nbw,
+                                         int lane) {
+  using F = SkF<FMT>;
+  using L = SkL<FMT, MF, CT, NX, BR>;
+  const int kb = lane >> 4, j = lane & 15;
+  const int64_t kt = kt0 + int64_t(c) * CT;
+  uint4* xb = lds + L::X0 + (c % NX) * L::XBUF;
+#pragma unroll
+  for (int f = 0; f < L::FRAGS; ++f) {
+    const int t = f / (MF * F::STEPS), i = (f / F::STEPS) % MF, s = f % F::STEPS;
+    const int64_t row = 16 * i + j;
+    const int64_t k = (kt + t) * F::TK + kb * F::SLK + 8 * s;
+    const uint32_t off = row < a.M && k < a.K ? uint32_t((row * a.K + k) * 2) : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (sk_lds_ptr)(xb + f * 64), 16, off, 0, 0, 0);
+  }
+  if constexpr (FMT == kFmtW4) {
+    if ((c * CT) % kScaleQuad == 0) {
+      const int64_t q = kt / kScaleQuad;
+      uint4* qb = lds + L::Q0 + (int((c * CT) / kScaleQuad) % 3) * L::QBUF;
+#pragma unroll
+      for (int h = 0; h < L::QG; ++h) {
+        // lane l: row block 8 h + l / 8 of the workgroup, rows 2 (l % 8) and 2 (l % 8) + 1
+        const int rb = 8 * h + (lane >> 3);
+        const int64_t nb = nbw + rb, r0 = (lane & 7) * 2;
+        const int64_t e = (nb * a.G4 + q) * kTileRows + r0;  // (row block, quad, row) element
+        const bool ok = rb < BR && nb < a.NB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (sk_lds_ptr)(qb + 64 * h), 16, ok ? uint32_t(e * 8) : 0x80000000u,
+                                                 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(zres, (sk_lds_ptr)(qb + L::QS + 16 * h), 4,
+                                                 ok ? uint32_t(e * 2) : 0x80000000u, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Producer (W4A16): X = x . 1 of every tile and x row block of chunk c, by the
+// same chain of matrix-core steps the consumers use for P; lanes 16 kb store
+// rows 4 kb .. 4 kb + 3.
+template <int FMT, int MF, int CT, int NX, int BR>
+__device__ __forceinline__ void sk_xsums(uint4* lds, int c, int lane) {
+  using L = SkL<FMT, MF, CT, NX, BR>;
+  const uint4* xb = lds + L::X0 + (c % NX) * L::XBUF + lane;
+  uint4* xs = lds + L::XS0 + (c % NX) * L::SBUF;
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+#pragma unroll
+  for (int t = 0; t < CT; ++t)
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      sk_f32x4_t X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) X = sk_mfma(xb[((t * MF + i) * 4 + s) * 64], ones, X);
+      if ((lane & 15) == 0) xs[(t * MF + i) * 4 + (lane >> 4)] = __builtin_bit_cast(uint4, X);
+    }
 }
 
 template <int FMT, int MF, int RB, int WN, int R, int CT, int NX>
 __global__ __launch_bounds__(64 * (WN + 1)) void gemv_sk_kernel(SkArgs a) {
-  using L = SkL<FMT, MF, CT>;
-  static_assert(R % CT == 0 && R % 4 == 0 && NX >= 2 && NX <= 3, "ring, chunk and buffer counts");
-  __shared__ uint4 s_x[NX * L::BUF];
+  constexpr int BR = WN * RB;
+  using L = SkL<FMT, MF, CT, NX, BR>;
+  static_assert(R % CT == 0 && R % 4 == 0 && NX == 3 && (FMT != kFmtW4 || kScaleQuad % CT == 0),
+                "ring, chunk and buffer counts");
+  __shared__ uint4 lds[L::TOTAL];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -248,25 +306,32 @@ __global__ __launch_bounds__(64 * (WN + 1)) void gemv_sk_kernel(SkArgs a) {
   const int total = rem < a.per_split ? int(rem) : a.per_split;  // >= 1: the planner sizes S so
   const int nbody = (total + R - 1) / R;
   const int nch = nbody * (R / CT);
+  const int64_t nbw = int64_t(blockIdx.x) * BR;  // the workgroup's first row block
 
   if (wave == WN) {
-    // producer: chunks 0 .. NX - 2 up front, then chunk c + NX - 1 once
-    // barrier c has freed the buffer of chunk c - 1
+    // producer.  Between the barriers that open chunks c - 1 and c: wait for
+    // chunk c (the only loads in flight), compute its x sums, issue chunk c + 1
+    // into the buffers of chunk c - 2 (free: the consumers are on c - 1)
     const __amdgpu_buffer_rsrc_t xres =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, 0x7FFFFFF0, 0x00020000);
-    for (int q = 0; q < NX - 1 && q < nch; ++q) sk_stage<FMT, MF, CT>(a, xres, s_x + q * L::BUF, kt0 + q * CT, lane);
+    __amdgpu_buffer_rsrc_t sres = xres, zres = xres;
+    if constexpr (FMT == kFmtW4) {
+      sres = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.scales), 0,
+                                               uint32_t(a.NB * a.G4 * kTileRows * kScaleQuad * 2), 0x00020000);
+      zres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.zeros), 0, uint32_t(a.NB * a.G4 * kTileRows * 2),
+                                               0x00020000);
+    }
+    sk_stage<FMT, MF, CT, NX, BR>(a, xres, sres, zres, lds, kt0, 0, nbw, lane);
+    // chunk 0 is requested before the consumers' weights, which would
+    // otherwise queue ahead of it and leave them waiting for x
+    asm volatile("s_barrier" ::: "memory");
     for (int c = 0; c < nch; ++c) {
-      // chunk c has landed before its barrier opens it (at most chunk c + 1,
-      // issued later, is still in flight)
-      if (NX == 3 && c + 1 < nch)
-        sk_wait_vm<(NX - 2) * L::FRAGS>();
-      else
-        sk_wait_vm<0>();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (FMT == kFmtW4) sk_xsums<FMT, MF, CT, NX, BR>(lds, c, lane);
+      if (c + 1 < nch) sk_stage<FMT, MF, CT, NX, BR>(a, xres, sres, zres, lds, kt0, c + 1, nbw, lane);
       // a bare barrier: __syncthreads() would add a release fence, which waits
-      // for every direct-to-LDS load in flight (the next chunk's included)
-      asm volatile("s_barrier" ::: "memory");
-      const int nc = c + NX - 1;
-      if (nc < nch) sk_stage<FMT, MF, CT>(a, xres, s_x + (nc % NX) * L::BUF, kt0 + int64_t(nc) * CT, lane);
+      // for the direct-to-LDS loads of chunk c + 1 just issued
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     return;
   }
@@ -275,36 +340,27 @@ __global__ __launch_bounds__(64 * (WN + 1)) void gemv_sk_kernel(SkArgs a) {
   const int n = lane & 15, kb = lane >> 4;
   st.lane = lane;
   st.total = total;
-  st.kt0 = kt0;
-  st.xb = s_x;
-  const int64_t nb0 = (int64_t(blockIdx.x) * WN + wave) * RB;
+  st.rbl = wave * RB;
+  st.xb = st.xs = lds;
+  st.sq = st.zq = reinterpret_cast<const uint16_t*>(lds);
+  const int64_t nb0 = nbw + wave * RB;
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
-    // a row block past the matrix gets empty resources: its loads read zeros
-    // and its outputs are never stored
+    // a row block past the matrix gets an empty resource: its loads read
+    // zeros and its outputs are never stored
     const bool live = nb0 + b < a.NB;
     const int64_t nb = live ? nb0 + b : 0;
     st.wres[b] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(a.w + (nb * a.KT + kt0) * (kTileBytes / 16)), 0,
                                                    live ? uint32_t(total) * kTileBytes : 0u, 0x00020000);
-    if constexpr (FMT == kFmtW4) {
-      const uint16_t* sb = reinterpret_cast<const uint16_t*>(a.scales) + nb * a.G4 * kTileRows * kScaleQuad;
-      const uint16_t* zb = a.zeros + nb * a.G4 * kTileRows;
-      st.sres[b] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(sb), 0,
-                                                     live ? uint32_t(a.G4 * kTileRows * kScaleQuad * 2) : 0u,
-                                                     0x00020000);
-      st.zres[b] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(zb), 0,
-                                                     live ? uint32_t(a.G4 * kTileRows * 2) : 0u, 0x00020000);
-    }
 #pragma unroll
     for (int i = 0; i < MF; ++i) st.acc[i][b] = sk_f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  st.soff = uint32_t(n) * (kScaleQuad * 2);
-  st.zoff = uint32_t(n) * 2;
 
   // prologue: tiles 0 .. R - 2 into slots 0 .. R - 2, in tile order (the
   // waits of the first loop pass assume it)
+  asm volatile("s_barrier" ::: "memory");  // the producer has requested x of chunk 0
   sk_prologue<FMT, MF, RB, R, 0>(st);
-  for (int it = 0; it < nbody; ++it) sk_steps<FMT, MF, RB, R, CT, NX, 0>(st, s_x, it * R);
+  for (int it = 0; it < nbody; ++it) sk_steps<FMT, MF, RB, R, CT, NX, BR, 0>(st, lds, it * R);
 
   // lane (kb, n) holds activation rows 16 i + 4 kb + r of column n of each block
 #pragma unroll
@@ -326,23 +382,29 @@ __global__ __launch_bounds__(64 * (WN + 1)) void gemv_sk_kernel(SkArgs a) {
   }
 }
 
-template <int FMT, int MF, int RB, int R, int CT, int NX>
+template <int FMT, int MF, int RB, int WN>
 static hipError_t launch_sk_cfg(const SkArgs& a, const SkPlan& p, hipStream_t st) {
-  constexpr int WN = 4;
-  if (p.waves != WN) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemv_sk_kernel<FMT, MF, RB, WN, R, CT, NX>), dim3(unsigned(p.groups), unsigned(p.S)),
+  constexpr int CT = (FMT == kFmtW4 && MF == 2) ? 2 : 4;
+  if (p.ring != 8 || p.ct != CT || p.nx != 3) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemv_sk_kernel<FMT, MF, RB, WN, 8, CT, 3>), dim3(unsigned(p.groups), unsigned(p.S)),
                      dim3(64 * (WN + 1)), 0, st, a);
   return hipGetLastError();
 }
 
-// The configurations the planner chooses from (mf, rb, ring, chunk, buffers).
+// The configurations the planner chooses from: x row blocks, weight row
+// blocks per consumer, consumers per workgroup.
 template <int FMT>
 static hipError_t launch_sk_fmt(const SkArgs& a, const SkPlan& p, hipStream_t st) {
-#define WQD_SK_CFG(MF, RB, R, CT, NX)                                                  \
-  if (p.mf == MF && p.rb == RB && p.ring == R && p.ct == CT && p.nx == NX) \
-    return launch_sk_cfg<FMT, MF, RB, R, CT, NX>(a, p, st);
-  WQD_SK_CFG(1, 2, 8, 4, 3)
-  WQD_SK_CFG(2, 2, 8, 4, 2)
+#define WQD_SK_CFG(MF, RB, WN) \
+  if (p.mf == MF && p.rb == RB && p.waves == WN) return launch_sk_cfg<FMT, MF, RB, WN>(a, p, st);
+  WQD_SK_CFG(1, 2, 4)
+  WQD_SK_CFG(1, 2, 5)
+  WQD_SK_CFG(1, 1, 7)
+  WQD_SK_CFG(1, 2, 7)
+  WQD_SK_CFG(2, 2, 4)
+  WQD_SK_CFG(2, 2, 5)
+  WQD_SK_CFG(2, 1, 7)
+  WQD_SK_CFG(2, 2, 7)
 #undef WQD_SK_CFG
   return hipErrorInvalidValue;
 }
