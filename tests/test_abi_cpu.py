@@ -82,8 +82,8 @@ def test_packed_sizes_errors():
 
 def test_workspace_query():
     for fmt in ("bf16", "fp8", "w4a16"):
-        for M in (1, 4, 8):
-            assert wqd.workspace_bytes(fmt, M, 8192, 8192) == 0  # streaming kernel: none
+        for M in (1, 4):
+            assert wqd.workspace_bytes(fmt, M, 8192, 8192) == 0  # streaming kernels: none
         # matrix-core paths: split-K partials only when the row blocks give too few workgroups
         assert wqd.workspace_bytes(fmt, 1024, 28672, 8192) == 0
         assert wqd.workspace_bytes(fmt, 16, 57344, 8192) == 0
@@ -106,8 +106,14 @@ def test_kernel_path_choice():
     assert wqd.kernel_path("w4a16", 1, 8192, 28672) == ("bcast", 8)   # 224 tiles: shares of 28
     assert wqd.kernel_path("fp8", 4, 28672, 8192)[0] == "bcast"
     assert wqd.kernel_path("bf16", 2, 4096, 11008) == ("bcast", 16)   # 344 tiles: shares of 24
-    # streaming matrix-core kernel: 2-8 W4A16 rows, 5-8 FP8 / BF16 rows
-    assert wqd.kernel_path("w4a16", 4, 57344, 8192) == ("mc", 4)
+    # up to 8 rows, long unsplit K shares (large N): the skinny kernel (7 consumers + producer)
+    for M in (2, 4, 8):
+        assert wqd.kernel_path("w4a16", M, 57344, 8192) == ("skinny", 8)
+    assert wqd.kernel_path("fp8", 8, 57344, 8192) == ("skinny", 8)
+    assert wqd.kernel_path("w4a16", 8, 8192, 28672)[0] == "skinny"    # K split: only at 8 rows
+    assert wqd.kernel_path("w4a16", 4, 8192, 28672)[0] == "mc"
+    # streaming matrix-core kernel: 2-8 W4A16 rows, 5-8 FP8 / BF16 rows otherwise
+    assert wqd.kernel_path("w4a16", 4, 10240, 8192) == ("mc", 4)
     for M in (2, 3, 8):
         assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "mc"
     for M in (5, 8):

@@ -211,15 +211,22 @@ int choose_path(int fmt, int64_t M, int64_t N, int64_t K, Choice* out) {
   int st = plan_gemv(fmt, M, N, K, &c.gemv);
   if (st != kOK) return st;
   const int64_t bcast_first = fmt == kFmtW4 ? 1 : 4;
+  const bool sk_ok = plan_skinny(fmt, M, N, K, &c.sk) == kOK;
+  // up to 8 rows the skinny kernel pays off where its shares are long (its
+  // start and, with a K split, the second launch are amortised), measured
+  // on the 70B shapes: gate/up from 2 rows, down at 8
+  const bool sk_long = sk_ok && c.sk.per_split >= 48 && (c.sk.S == 1 || M >= kGemvMaxM);
   if (M <= bcast_first && plan_bcast(fmt, M, N, K, &c.bcast) == kOK) {
     c.path = kPathBcast;
+  } else if (M <= kGemvMaxM && sk_long) {
+    c.path = kPathSkinny;
   } else if (M <= kGemvMaxM && plan_mc(fmt, M, N, K, &c.mc) == kOK) {
     c.path = kPathMc;
   } else if (M <= kGemvMaxM && plan_bcast(fmt, M, N, K, &c.bcast) == kOK) {
     c.path = kPathBcast;
   } else if (M <= kGemvMaxM) {
     c.path = kPathStaged;
-  } else if (M <= kSkMaxM && plan_skinny(fmt, M, N, K, &c.sk) == kOK) {
+  } else if (M <= kSkMaxM && sk_ok) {
     c.path = kPathSkinny;
   } else {
     st = plan_mfma(fmt, M, N, K, &c.mfma);

@@ -122,11 +122,12 @@ int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out);
 
 // The kernel family for a shape, in order of preference (measured on the
 // 70B shapes): the broadcast kernel for 1 W4A16 row or up to 4 FP8 / BF16
-// rows; the streaming matrix-core kernel up to 8 rows; the broadcast kernel
-// again, then the staged one, up to 8 rows where the former cannot take the
-// shape; the skinny matrix-core kernel from 9 to 32 rows; the LDS
-// matrix-core kernel above that (or where the skinny one cannot take the
-// shape).
+// rows; up to 8 rows the skinny matrix-core kernel where its K shares are
+// at least 48 tiles long and unsplit (or split, at 8 rows), else the
+// streaming matrix-core kernel; the broadcast kernel again, then the staged
+// one, up to 8 rows where those cannot take the shape; the skinny kernel
+// from 9 to 32 rows; the LDS matrix-core kernel above that (or where the
+// skinny one cannot take the shape).
 enum Path { kPathBcast = 0, kPathStaged = 1, kPathMfma = 2, kPathMc = 3, kPathSkinny = 4 };
 
 struct Choice {
