@@ -111,7 +111,7 @@ int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes)
  * shape: the broadcast kernel for 1 W4A16 row or up to 4 FP8 / BF16 rows; up
  * to 8 rows the skinny matrix-core kernel for long shares of K (large N, or
  * long K at 8 rows), else the streaming matrix-core kernel; otherwise, up to
- * 8 rows, the broadcast kernel, then the staged one; from 9 to 32 rows the skinny
+ * 8 rows, the broadcast kernel, then the staged one; from 9 to 64 rows the skinny
  * matrix-core kernel (K a whole number of tiles: 128 W4A16, 64 FP8, 32 BF16);
  * above that, or where the skinny kernel cannot take the shape, the LDS
  * matrix-core kernel.  Each streaming kernel also needs K short enough for

@@ -124,13 +124,13 @@ def test_kernel_path_choice():
     assert wqd.kernel_path("bf16", 1, 16, 16416)[0] == "staged"       # 513 tiles
     assert wqd.kernel_path("w4a16", 1, 16, 65664)[0] == "staged"
     assert wqd.kernel_path("w4a16", 5, 16, 65664)[0] == "staged"
-    # 9 to 32 rows: the skinny matrix-core kernel (4 consumer wavefronts and a producer)
-    for M in (9, 16, 17, 32):
+    # 9 to 64 rows: the skinny matrix-core kernel (4 consumer wavefronts and a producer)
+    for M in (9, 16, 17, 32, 33, 64):
         for fmt in ("w4a16", "fp8", "bf16"):
             assert wqd.kernel_path(fmt, M, 8192, 8192) == ("skinny", 5)
     assert wqd.kernel_path("fp8", 16, 8192, 8208)[0] == "mfma"          # K not a whole number of 64-k tiles
-    # above 32 rows: the LDS matrix-core kernel
-    for M in (33, 1024):
+    # above 64 rows: the LDS matrix-core kernel
+    for M in (65, 1024):
         assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "mfma"
     L = wqd.lib()
     p = ctypes.c_int()

@@ -190,7 +190,7 @@ def test_qgemm_skinny(fmt):
         W = I.w_host(5000 + N + K, N, K)
         qw = oracle.quantize(fmt, W)
         pw = wqd.pack_weights(fmt, to_dev(W))
-        for M in (9, 16, 17, 32):
+        for M in (9, 16, 17, 32, 40, 64):
             assert wqd.kernel_path(fmt, M, N, K)[0] == "skinny"
             print(f"qgemm {fmt} M={M} N={N} K={K} ws={wqd.workspace_bytes(fmt, M, N, K)}", flush=True)
             x = I.x_bf16_bits(29 * M + K, M, K)

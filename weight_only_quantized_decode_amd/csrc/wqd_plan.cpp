@@ -108,8 +108,9 @@ int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out) {
 
 // Skinny kernel: consumer wavefronts per workgroup and row blocks per consumer
 // from (7, 2), (7, 1), (4, 2) (x chunks shared by 14, 7 or 8 row blocks); a
-// ring of 8 weight tiles per row block; x chunks of 4 tiles (2 for 32 rows of
-// W4A16, which would otherwise need 100 KiB of LDS), three buffers.  K is
+// ring of 8 weight tiles per row block; x chunks of 4 tiles (2 for W4A16 from
+// 17 rows and for everything from 33, whose chunks would otherwise need up to
+// 200 KiB of LDS), three buffers.  K is
 // split so that the launch has about as many workgroups as compute units
 // (S = units / groups: a second workgroup on only some units would make them
 // the tail), keeping every split at least 2 rings long and at most 8 splits
@@ -126,7 +127,7 @@ static int plan_skinny_with(int fmt, int64_t M, const PackedSizes& ps, int waves
   p.rb = rb;
   p.waves = waves;
   p.ring = 8;
-  p.ct = (fmt == kFmtW4 && p.mf == 2) ? 2 : 4;
+  p.ct = (fmt == kFmtW4 && p.mf >= 2) || p.mf >= 3 ? 2 : 4;
   p.nx = 3;
   p.groups = ceil_div(p.NB, int64_t(p.waves) * p.rb);
   const int64_t body = p.ring;

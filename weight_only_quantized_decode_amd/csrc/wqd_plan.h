@@ -84,15 +84,15 @@ struct McPlan {
 
 int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out);
 
-// Skinny matrix-core kernel (9 to 32 rows): a workgroup of `waves` consumer
+// Skinny matrix-core kernel (9 to 64 rows): a workgroup of `waves` consumer
 // wavefronts (plus a producer that stages x, scales and zero points in LDS
 // and computes the W4A16 x sums) owns waves x rb 16-row blocks
 // (`groups` workgroups cover the matrix), mf 16-row blocks of x, and chunks
 // of ct tiles.  K is split S ways (per_split tiles each, a multiple of ring)
 // when the row blocks alone give too few workgroups; the S float32 partials
-// then need S * M * N * 4 bytes of workspace.  kEUnsupported above 32 rows,
+// then need S * M * N * 4 bytes of workspace.  kEUnsupported above 64 rows,
 // for x rows spanning 2 GiB or more, and for K not a whole number of tiles.
-constexpr int kSkMaxM = 32;
+constexpr int kSkMaxM = 64;
 
 struct SkPlan {
   int64_t NB, KT, groups;
@@ -126,7 +126,7 @@ int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out);
 // at least 48 tiles long and unsplit (or split, at 8 rows), else the
 // streaming matrix-core kernel; the broadcast kernel again, then the staged
 // one, up to 8 rows where those cannot take the shape; the skinny kernel
-// from 9 to 32 rows; the LDS matrix-core kernel above that (or where the
+// from 9 to 64 rows; the LDS matrix-core kernel above that (or where the
 // skinny one cannot take the shape).
 enum Path { kPathBcast = 0, kPathStaged = 1, kPathMfma = 2, kPathMc = 3, kPathSkinny = 4 };
 

@@ -1,4 +1,4 @@
-// Skinny matrix-core decode kernel for 9 to 32 activation rows:
+// Skinny matrix-core decode kernel for 9 to 64 activation rows:
 // y = x . dequant(W)^T.
 //
 // Between a handful of rows and the compute-bound verify widths the layer is
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(64 * (WN + 1)) void gemv_sk_kernel(SkArgs a) {
 
 template <int FMT, int MF, int RB, int WN>
 static hipError_t launch_sk_cfg(const SkArgs& a, const SkPlan& p, hipStream_t st) {
-  constexpr int CT = (FMT == kFmtW4 && MF == 2) ? 2 : 4;
+  constexpr int CT = (FMT == kFmtW4 && MF >= 2) || MF >= 3 ? 2 : 4;
   if (p.ring != 8 || p.ct != CT || p.nx != 3) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemv_sk_kernel<FMT, MF, RB, WN, 8, CT, 3>), dim3(unsigned(p.groups), unsigned(p.S)),
                      dim3(64 * (WN + 1)), 0, st, a);
@@ -405,6 +405,12 @@ static hipError_t launch_sk_fmt(const SkArgs& a, const SkPlan& p, hipStream_t st
   WQD_SK_CFG(2, 2, 5)
   WQD_SK_CFG(2, 1, 7)
   WQD_SK_CFG(2, 2, 7)
+  WQD_SK_CFG(3, 2, 4)
+  WQD_SK_CFG(3, 1, 7)
+  WQD_SK_CFG(3, 2, 7)
+  WQD_SK_CFG(4, 2, 4)
+  WQD_SK_CFG(4, 1, 7)
+  WQD_SK_CFG(4, 2, 7)
 #undef WQD_SK_CFG
   return hipErrorInvalidValue;
 }
