@@ -113,15 +113,18 @@ int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes)
  * long K at 8 rows), else the streaming matrix-core kernel; otherwise, up to
  * 8 rows, the broadcast kernel, then the staged one; from 9 to 64 rows the skinny
  * matrix-core kernel (K a whole number of tiles: 128 W4A16, 64 FP8, 32 BF16);
- * above that, or where the skinny kernel cannot take the shape, the LDS
- * matrix-core kernel.  Each streaming kernel also needs K short enough for
- * its shares (hundreds of 16-row tiles). */
+ * above 64 rows the tiled matrix-core kernel for FP8 / BF16 beyond 256 rows,
+ * else the LDS matrix-core kernel (also where the others cannot take the
+ * shape: x rows spanning 2 GiB or more, or a ragged K below 65 rows).  Each
+ * streaming kernel also needs K short enough for its shares (hundreds of
+ * 16-row tiles). */
 enum wqd_path {
     WQD_PATH_BCAST = 0,   /* streaming, x read per tile and broadcast across DPP rows */
     WQD_PATH_STAGED = 1,  /* streaming, x staged in LDS, dot2 products */
     WQD_PATH_MFMA = 2,    /* bf16 matrix cores, x staged in LDS, dequant on load */
     WQD_PATH_MC = 3,      /* streaming, bf16 matrix cores, x fragments read per tile */
-    WQD_PATH_SKINNY = 4   /* bf16 matrix cores, x staged in LDS by a producer wavefront, shared by 8 row blocks */
+    WQD_PATH_SKINNY = 4,  /* bf16 matrix cores, x staged in LDS by a producer wavefront, shared by 7-14 row blocks */
+    WQD_PATH_GEMM = 5     /* bf16 matrix cores, 128 x 256 tiles of y, x staged in LDS, dequant on load */
 };
 
 /*

@@ -129,9 +129,15 @@ def test_kernel_path_choice():
         for fmt in ("w4a16", "fp8", "bf16"):
             assert wqd.kernel_path(fmt, M, 8192, 8192) == ("skinny", 5)
     assert wqd.kernel_path("fp8", 16, 8192, 8208)[0] == "mfma"          # K not a whole number of 64-k tiles
-    # above 64 rows: the LDS matrix-core kernel
+    # above 256 rows, FP8 / BF16: the tiled matrix-core kernel (8 wavefronts)
+    assert wqd.kernel_path("bf16", 257, 8192, 8192) == ("gemm", 8)
+    assert wqd.kernel_path("fp8", 1024, 28672, 8192) == ("gemm", 8)
+    # otherwise above 64 rows (and W4A16): the LDS matrix-core kernel
     for M in (65, 1024):
         assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "mfma"
+    assert wqd.kernel_path("bf16", 256, 8192, 8192)[0] == "mfma"
+    # x rows spanning 2 GiB: the LDS matrix-core kernel
+    assert wqd.kernel_path("bf16", 65536, 64, 16384)[0] == "mfma"
     L = wqd.lib()
     p = ctypes.c_int()
     assert L.wqd_kernel_path(2, 1, 64, 128, None, None) == E_ARG

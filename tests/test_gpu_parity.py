@@ -199,6 +199,29 @@ def test_qgemm_skinny(fmt):
             compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
+def tiled_shapes():
+    # (N, K) for the tiled matrix-core kernel: a partial column block, odd
+    # chunk counts (5, 9), K splits over few workgroups, and a K that ends
+    # inside a tile (x past K reads as zero)
+    return [(300, 648), (1000, 1160), (4104, 4096)]
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "bf16"])
+def test_qgemm_tiled(fmt):
+    """Wide verify batches: 128-row tiles of y with a ragged last row block."""
+    for N, K in tiled_shapes():
+        W = I.w_host(6000 + N + K, N, K)
+        qw = oracle.quantize(fmt, W)
+        pw = wqd.pack_weights(fmt, to_dev(W))
+        for M in (257, 300, 384):
+            assert wqd.kernel_path(fmt, M, N, K)[0] == "gemm"
+            print(f"qgemm {fmt} M={M} N={N} K={K} ws={wqd.workspace_bytes(fmt, M, N, K)}", flush=True)
+            x = I.x_bf16_bits(31 * M + K, M, K)
+            y = wqd.qgemm(x_dev(x), pw)
+            torch.cuda.synchronize()
+            compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("rows", [1, 2, 8, 10, 16])
 def test_one_hot_probes_exact(fmt, rows):
@@ -227,7 +250,7 @@ def test_one_hot_probes_exact(fmt, rows):
 def test_zero_weights_give_exact_zero(fmt):
     N, K = 130, 512
     pw = wqd.pack_weights(fmt, torch.zeros((N, K), dtype=torch.float32, device=dev()))
-    for M in (1, 2, 4, 16, 40, 64):
+    for M in (1, 2, 4, 16, 40, 64, 100):
         y = wqd.qgemm(x_dev(I.x_bf16_bits(3 + M, M, K)), pw)
         torch.cuda.synchronize()
         assert (y.float() == 0).all(), M
@@ -238,7 +261,7 @@ def test_deterministic_and_every_output_written(fmt):
     N, K = 1000, 2048
     W = I.w_host(9, N, K)
     pw = wqd.pack_weights(fmt, to_dev(W))
-    for M in (1, 5, 8, 24, 40):
+    for M in (1, 5, 8, 24, 40, 150):
         x = x_dev(I.x_bf16_bits(10 + M, M, K))
         y1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
         y2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())

@@ -121,7 +121,7 @@ def workspace_bytes(fmt, M: int, N: int, K: int) -> int:
     return b.value
 
 
-KERNEL_PATHS = ("bcast", "staged", "mfma", "mc", "skinny")
+KERNEL_PATHS = ("bcast", "staged", "mfma", "mc", "skinny", "gemm")
 
 
 def kernel_path(fmt, M: int, N: int, K: int):

@@ -78,6 +78,7 @@ int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* wa
            : c.path == wqd::kPathMc    ? c.mc.waves
            : c.path == wqd::kPathStaged ? c.gemv.waves
            : c.path == wqd::kPathSkinny ? c.sk.waves + 1
+           : c.path == wqd::kPathGemm   ? 4 * c.gm.wm
                                         : 4;
   }
   return WQD_OK;
@@ -105,7 +106,9 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const voi
   if (!wqd::aligned16(x) || !wqd::aligned16(y)) return WQD_E_ALIGN;
   st = check_packed_ptrs(fmt, w_packed, scales, zeros);
   if (st != WQD_OK) return st;
-  const size_t need = c.path == wqd::kPathMfma ? c.mfma.ws_bytes : c.path == wqd::kPathSkinny ? c.sk.ws_bytes : 0;
+  size_t need = 0;
+  st = wqd::workspace_bytes(fmt, M, N, K, &need);
+  if (st != wqd::kOK) return st;
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return WQD_E_WORKSPACE;
     if (!wqd::aligned16(workspace)) return WQD_E_ALIGN;
@@ -118,6 +121,8 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const voi
       return hip_status(wqd::launch_gemv_mc(fmt, c.mc, x, M, N, K, w_packed, scales, zeros, y, s));
     case wqd::kPathStaged:
       return hip_status(wqd::launch_gemv(fmt, c.gemv, x, M, N, K, w_packed, scales, zeros, y, s));
+    case wqd::kPathGemm:
+      return hip_status(wqd::launch_gemm(fmt, c.gm, x, M, N, K, w_packed, scales, zeros, y, workspace, s));
     case wqd::kPathSkinny:
       return hip_status(wqd::launch_gemv_sk(fmt, c.sk, x, M, N, K, w_packed, scales, zeros, y, workspace, s));
     default:

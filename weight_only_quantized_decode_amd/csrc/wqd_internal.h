@@ -23,6 +23,8 @@ hipError_t launch_gemv_mc(int fmt, const McPlan& p, const void* x, int64_t M, in
                           const void* wp, const void* scales, const void* zeros, void* y, hipStream_t st);
 hipError_t launch_gemv_sk(int fmt, const SkPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
                           const void* scales, const void* zeros, void* y, void* ws, hipStream_t st);
+hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
+                       const void* scales, const void* zeros, void* y, void* ws, hipStream_t st);
 // y = sum over s < S of part[s] (float32 [S][M][N], added in split order), FP8
 // scaled per column, rounded to bfloat16.
 hipError_t launch_splitk_reduce(int fmt, const float* part, int S, int64_t M, int64_t N, const void* scales, void* y,

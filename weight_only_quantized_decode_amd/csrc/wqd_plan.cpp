@@ -171,6 +171,42 @@ int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
   return kOK;
 }
 
+// Tiled kernel (FP8 / BF16 above kGmMinM rows, where it measured faster than
+// the LDS matrix-core kernel on the 70B verify shapes): 128-row blocks (64 up
+// to 96 rows, for more workgroups, and
+// for W4A16, whose per-group partials and x sums need the register file of a
+// single wavefront per SIMD); K
+// split while the tiles give fewer workgroups than compute units, keeping
+// every split at least 4 chunks long and at most 8 splits.
+int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
+  PackedSizes ps;
+  int st = packed_sizes(fmt, N, K, &ps);
+  if (st != kOK) return st;
+  if (M < 1) return kEArg;
+  if (M * K * 2 >= (int64_t(1) << 31)) return kEUnsupported;
+  if (ps.s_bytes >= (size_t(1) << 31) || ps.z_bytes >= (size_t(1) << 31)) return kEUnsupported;
+  GmPlan p{};
+  p.NB = ps.NB;
+  p.KT = ps.KT;
+  p.wm = (M <= 96 || fmt == kFmtW4) ? 1 : 2;
+  p.NBN = ceil_div(p.NB, 16);
+  p.MB = ceil_div(M, 64 * p.wm);
+  p.nchunks = ceil_div(K, 128);
+  const int64_t wgs = p.NBN * p.MB;
+  int64_t S = 1;
+  if (wgs < kComputeUnits) {
+    S = ceil_div(kComputeUnits, wgs);
+    const int64_t max_s = p.nchunks / 4 > 1 ? p.nchunks / 4 : 1;
+    if (S > max_s) S = max_s;
+    if (S > 8) S = 8;
+  }
+  p.cps = ceil_div(p.nchunks, S);
+  p.S = int(ceil_div(p.nchunks, p.cps));
+  p.ws_bytes = p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;
+  *out = p;
+  return kOK;
+}
+
 // Tiles per chunk of the matrix-core kernel: the staged x chunk is 16 KiB
 // (16 * BMS rows), at most 8 tiles.
 static int mfma_tpc(int fmt, int bms) {
@@ -229,6 +265,8 @@ int choose_path(int fmt, int64_t M, int64_t N, int64_t K, Choice* out) {
     c.path = kPathStaged;
   } else if (M <= kSkMaxM && sk_ok) {
     c.path = kPathSkinny;
+  } else if (M > kGmMinM && fmt != kFmtW4 && plan_gemm(fmt, M, N, K, &c.gm) == kOK) {
+    c.path = kPathGemm;
   } else {
     st = plan_mfma(fmt, M, N, K, &c.mfma);
     if (st != kOK) return st;
@@ -242,7 +280,10 @@ int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out) {
   Choice c;
   int st = choose_path(fmt, M, N, K, &c);
   if (st != kOK) return st;
-  *out = c.path == kPathMfma ? c.mfma.ws_bytes : c.path == kPathSkinny ? c.sk.ws_bytes : 0;
+  *out = c.path == kPathMfma     ? c.mfma.ws_bytes
+         : c.path == kPathSkinny ? c.sk.ws_bytes
+         : c.path == kPathGemm   ? c.gm.ws_bytes
+                                 : 0;
   return kOK;
 }
 

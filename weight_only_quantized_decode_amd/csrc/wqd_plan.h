@@ -104,6 +104,22 @@ struct SkPlan {
 
 int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out);
 
+// Tiled matrix-core kernel (more than 64 rows): a workgroup of 4 wm
+// wavefronts computes a (64 wm) x 256 tile of y; NBN column blocks x MB row
+// blocks of workgroups (XCD-aware order), K in chunks of 128 split S ways
+// (cps chunks per split) when that leaves fewer than one workgroup per
+// compute unit; the S float32 partials need S * M * N * 4 bytes of workspace.
+// kEUnsupported for x rows spanning 2 GiB or more.
+constexpr int kGmMinM = 256;
+
+struct GmPlan {
+  int64_t NB, KT, NBN, MB, nchunks, cps;
+  int wm, S;
+  size_t ws_bytes;
+};
+
+int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out);
+
 // Matrix-core kernel (M > 8): workgroup tile = 16 * BMS rows of x times
 // 4 wavefronts x BNT 16-column tiles; the K loop advances in chunks of TPC
 // tiles.  When that leaves fewer than ~2 workgroups per compute unit, K is
@@ -126,9 +142,9 @@ int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out);
 // at least 48 tiles long and unsplit (or split, at 8 rows), else the
 // streaming matrix-core kernel; the broadcast kernel again, then the staged
 // one, up to 8 rows where those cannot take the shape; the skinny kernel
-// from 9 to 64 rows; the LDS matrix-core kernel above that (or where the
-// skinny one cannot take the shape).
-enum Path { kPathBcast = 0, kPathStaged = 1, kPathMfma = 2, kPathMc = 3, kPathSkinny = 4 };
+// from 9 to 64 rows; above that the tiled matrix-core kernel for FP8 / BF16
+// beyond 256 rows, else the LDS matrix-core kernel.
+enum Path { kPathBcast = 0, kPathStaged = 1, kPathMfma = 2, kPathMc = 3, kPathSkinny = 4, kPathGemm = 5 };
 
 struct Choice {
   int path;
@@ -136,6 +152,7 @@ struct Choice {
   BcastPlan bcast;
   McPlan mc;
   SkPlan sk;
+  GmPlan gm;
   MfmaPlan mfma;
 };
 
