@@ -365,6 +365,18 @@ def main():
     per_launch_bytes = step_bytes / wl.launches
     avg_launch_us = ms * 1e3 / wl.launches
     achieved = per_launch_bytes / (avg_launch_us / 1e6) / 1e9
+    # the bound of the step: HBM bytes at the vendor bandwidth, or bf16
+    # matrix-core FLOPs at the vendor dense peak, whichever takes longer
+    flops_per_launch = wl.step_flops() / wl.launches
+    if flops_per_launch / (BF16_MFMA_PEAK_TFLOPS * 1e12) > per_launch_bytes / (HBM_PEAK_GBPS * 1e9):
+        tf = flops_per_launch / (avg_launch_us / 1e6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": profiled_traffic(wl)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(wl)}
+    roofline.update({"kernel": kernel_label(wl), "avg_launch_us": round(avg_launch_us, 3),
+                     "bytes_per_launch": round(per_launch_bytes), "flops_per_launch": round(flops_per_launch)})
     graph = graph_used
     out = {
         "metric": "weight-stream GB/s (% of HBM peak) & us per layer-stack step, 70B W4A16/FP8/BF16",
@@ -387,11 +399,7 @@ def main():
         "hbm_read_ceiling_GBps": None if ceiling[0] is None else round(ceiling[0], 1),
         "hbm_copy_ceiling_GBps": None if ceiling[1] is None else round(ceiling[1], 1),
         "pct_measured_read_ceiling": None if ceiling[0] is None else round(100 * gbps / ceiling[0], 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(wl),
-                     "kernel": kernel_label(wl),
-                     "avg_launch_us": round(avg_launch_us, 3),
-                     "bytes_per_launch": round(per_launch_bytes)},
+        "roofline": roofline,
     }
     if alt is not None:
         out["separate_layout" if args.fused else "fused_layout"] = alt
