@@ -1,32 +1,28 @@
-// Tiled matrix-core kernel for wide verify batches (more than 64 activation
-// rows): y = x . dequant(W)^T as a dense contraction.
+// Tiled matrix-core kernel for wide verify batches (FP8 / BF16 weights, many
+// activation rows): y = x . dequant(W)^T as a dense contraction.
 //
 // With speculative verification the layer multiplies batch x (k + 1) rows
 // ("Making each token cheaper", sections "Speculative decoding" and the lab
 // on verify width; CS336 lecture 10 notes, 3.2-3.3: the MLP's arithmetic
-// intensity grows with the batch), and from roughly a hundred W4A16 rows the
-// matrix cores, not HBM, set the time.  Design for gfx950:
+// intensity grows with the batch), and from a few hundred rows the matrix
+// cores, not HBM, set the time.  Design for gfx950:
 //   * a workgroup computes a BM x 256 tile of y (BM = 64 WM rows) with 4 WM
 //     wavefronts, WM x 4, each owning 64 rows x 4 weight row blocks: 16
 //     accumulators of v_mfma_f32_16x16x32_bf16 per wavefront;
 //   * the packed 1 KiB weight tile is already the B-operand order (lane
 //     16 kb + n: slice kb of weight row n), so weights go from memory straight
-//     into registers, dequantised there (W4A16 nibble pairs become
-//     bf16 128 + q with one AND-OR; FP8 codes convert exactly; BF16 as is),
-//     each B fragment feeding 4 x row blocks;
-//   * x is staged per chunk of 128 k in LDS (two buffers, one barrier per
-//     chunk) in fragment order: fragment (tile, x row block i, K-step s) is
-//     1 KiB, lane 16 kb + j holding the 8 k of row 16 i + j that pair with
-//     slice kb of the weights; every wavefront loads 4 fragments of the next
-//     chunk into registers while the current one is multiplied, then writes
-//     them.  Reads back are conflict-free 16-byte LDS reads;
-//   * weights and (W4A16) scale / zero of the next chunk are loaded during
-//     the current one (two register sets, static indices: the loop body is
-//     two chunks);
-//   * W4A16 groups are 128 k, one chunk: P = x . (128 + q) and X = x . 1 come
-//     from matrix-core chains of the same shape (so q == z == 0 cancels
-//     exactly) and acc += s * (P - (128 + z) * X) in float32; FP8 applies the
-//     row scale at the end.  Dequantised weights are never rounded;
+//     into registers (FP8 codes convert exactly to bf16, BF16 feeds as is),
+//     each B fragment feeding 4 x row blocks; the FP8 row scale is applied
+//     once at the end;
+//   * K advances in chunks of 64 through a three-stage pipeline: while chunk
+//     c is multiplied, the weights and x of chunk c + 2 are in flight (three
+//     register sets for the weights, three for this wavefront's x fragments)
+//     and the x of chunk c + 1 is written into its LDS buffer (three buffers,
+//     one barrier per chunk).  The loop body is three chunks, so every index
+//     is a compile-time constant.  x sits in LDS in fragment order: fragment
+//     (tile, x row block i, K-step s) is 1 KiB, lane 16 kb + j holding the 8 k
+//     of row 16 i + j that pair with slice kb of the weights; reads are
+//     conflict-free 16-byte LDS reads;
 //   * XCD-aware order: consecutive workgroups of one XCD (dispatch is
 //     round-robin over the 8 XCDs) take the row blocks of x of one column
 //     block, so its weights come from HBM once and then from that XCD's L2;
@@ -56,7 +52,7 @@ struct GmArgs {
   const uint16_t* zeros;
   int64_t M, N, K, KT, G4, NB;
   int NBN, MB;  // 256-column blocks, BM-row blocks
-  int nchunks;  // chunks of 128 k
+  int nchunks;  // chunks of 64 k
   int cps;      // chunks per split
   int S;
 };
@@ -64,43 +60,44 @@ struct GmArgs {
 constexpr int kGmMF = 4;   // x row blocks per wavefront
 constexpr int kGmRB = 4;   // weight row blocks per wavefront
 constexpr int kGmWN = 4;   // wavefronts along N
-constexpr int kGmKC = 128;  // k per chunk
+constexpr int kGmKC = 64;  // k per chunk
+constexpr int kGmNS = 3;   // stages: chunks c, c + 1 (x in registers), c + 2 (loads in flight)
 
 template <int FMT>
 struct GmF {
-  static constexpr int TK = FMT == kFmtBF16 ? 32 : FMT == kFmtFP8 ? 64 : 128;  // K per tile
-  static constexpr int SLK = TK / 4;                                             // K per slice
-  static constexpr int STEPS = SLK / 8;                                          // 32-k steps per tile
-  static constexpr int TPC = kGmKC / TK;                                         // tiles per chunk
+  static_assert(FMT != kFmtW4, "W4A16 takes the LDS matrix-core kernel");
+  static constexpr int TK = FMT == kFmtBF16 ? 32 : 64;  // K per tile
+  static constexpr int SLK = TK / 4;                    // K per slice
+  static constexpr int STEPS = SLK / 8;                 // 32-k steps per tile
+  static constexpr int TPC = kGmKC / TK;                // tiles per chunk
 };
 
 template <int FMT, int WM>
 struct GmL {
-  static constexpr int XB = 4 * WM;                          // x row blocks per workgroup
-  static constexpr int FRAGS = GmF<FMT>::TPC * XB * GmF<FMT>::STEPS;  // 1 KiB fragments per chunk (4 XB)
-  static constexpr int BUF = FRAGS * 64;                      // uint4 per LDS buffer
-  static constexpr int XPW = FRAGS / (WM * kGmWN);           // fragments each wavefront stages
+  static constexpr int XB = 4 * WM;                                   // x row blocks per workgroup
+  static constexpr int FRAGS = GmF<FMT>::TPC * XB * GmF<FMT>::STEPS;  // 1 KiB fragments per chunk (2 XB)
+  static constexpr int BUF = FRAGS * 64;                               // uint4 per LDS buffer
+  static constexpr int XPW = FRAGS / (WM * kGmWN);                    // fragments each wavefront stages
   static_assert(XPW * WM * kGmWN == FRAGS, "whole fragments per wavefront");
 };
 
-template <int FMT>
+template <int FMT, int WM>
 struct GmState {
   using F = GmF<FMT>;
-  uint4 w[2][kGmRB][F::TPC];
-  uint32_t sw[2][kGmRB], zw[2][kGmRB];  // W4A16: fp16 scale bits and zero quad of the chunk's group
-  uint4 xr[kGmMF];                      // x fragments of the next chunk (XPW == kGmMF)
+  uint4 w[kGmNS][kGmRB][F::TPC];           // weights of chunks c, c + 1, c + 2
+  uint4 xr[kGmNS][GmL<FMT, WM>::XPW];      // x fragments loaded two chunks ahead
   gm_f32x4_t acc[kGmMF][kGmRB];
-  __amdgpu_buffer_rsrc_t wres[kGmRB], sres[kGmRB], zres[kGmRB], xres;
+  __amdgpu_buffer_rsrc_t wres[kGmRB], xres;
   int64_t kt0, m0;
-  int lane, wave, wm, nch;
+  int lane, wave, wm;
 };
 
-// Weights (and W4A16 scale / zero) of chunk c of the split into set H.
-template <int FMT, int H>
-__device__ __forceinline__ void gm_load_w(GmState<FMT>& st, int c) {
+// Weights of chunk c of the split into set H.
+template <int FMT, int WM, int H>
+__device__ __forceinline__ void gm_load_w(GmState<FMT, WM>& st, int c) {
   using F = GmF<FMT>;
 #pragma unroll
-  for (int b = 0; b < kGmRB; ++b) {
+  for (int b = 0; b < kGmRB; ++b)
 #pragma unroll
     for (int t = 0; t < F::TPC; ++t) {
       // cache policy 2: non-temporal (each weight byte is read by the few
@@ -109,21 +106,12 @@ __device__ __forceinline__ void gm_load_w(GmState<FMT>& st, int c) {
           __builtin_amdgcn_raw_buffer_load_b128(st.wres[b], st.lane * 16, (c * F::TPC + t) * kTileBytes, 2);
       st.w[H][b][t] = make_uint4(v.x, v.y, v.z, v.w);
     }
-    if constexpr (FMT == kFmtW4) {
-      const int64_t kt = st.kt0 + c;
-      const int q = int(kt / kScaleQuad), j = int(kt % kScaleQuad);
-      const int n = st.lane & 15;
-      st.sw[H][b] = __builtin_amdgcn_raw_buffer_load_b16(st.sres[b], n * (kScaleQuad * 2),
-                                                         q * (kTileRows * kScaleQuad * 2) + j * 2, 0);
-      st.zw[H][b] = __builtin_amdgcn_raw_buffer_load_b16(st.zres[b], n * 2, q * (kTileRows * 2), 0);
-    }
-  }
 }
 
-// x fragments this wavefront stages for chunk c: fragment f = wave * XPW + u
-// of (tile t, x row block i, step s) order.
-template <int FMT, int WM>
-__device__ __forceinline__ void gm_load_x(GmState<FMT>& st, const GmArgs& a, int c) {
+// x fragments this wavefront stages for chunk c into set H: fragment
+// f = wave * XPW + u of (tile t, x row block i, step s) order.
+template <int FMT, int WM, int H>
+__device__ __forceinline__ void gm_load_x(GmState<FMT, WM>& st, const GmArgs& a, int c) {
   using F = GmF<FMT>;
   using L = GmL<FMT, WM>;
   const int kb = st.lane >> 4, j = st.lane & 15;
@@ -135,65 +123,24 @@ __device__ __forceinline__ void gm_load_x(GmState<FMT>& st, const GmArgs& a, int
     const int64_t k = (st.kt0 + int64_t(c) * F::TPC + t) * F::TK + kb * F::SLK + 8 * s;
     const uint32_t off = row < a.M && k < a.K ? uint32_t((row * a.K + k) * 2) : 0x80000000u;
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(st.xres, off, 0, 0);
-    st.xr[u] = make_uint4(v.x, v.y, v.z, v.w);
+    st.xr[H][u] = make_uint4(v.x, v.y, v.z, v.w);
   }
 }
 
-template <int FMT, int WM>
-__device__ __forceinline__ void gm_store_x(const GmState<FMT>& st, uint4* buf) {
+template <int FMT, int WM, int H>
+__device__ __forceinline__ void gm_store_x(const GmState<FMT, WM>& st, uint4* buf) {
   using L = GmL<FMT, WM>;
 #pragma unroll
-  for (int u = 0; u < L::XPW; ++u) buf[(st.wave * L::XPW + u) * 64 + st.lane] = st.xr[u];
+  for (int u = 0; u < L::XPW; ++u) buf[(st.wave * L::XPW + u) * 64 + st.lane] = st.xr[H][u];
 }
 
-// Multiply chunk c (x in buf, weights in set H).
+// Multiply the chunk in buf with the weights of set H.
 template <int FMT, int WM, int H>
-__device__ __forceinline__ void gm_compute(GmState<FMT>& st, const uint4* buf, int c) {
+__device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, const uint4* buf) {
   using F = GmF<FMT>;
   using L = GmL<FMT, WM>;
   const uint4* xf = buf + st.lane;
-  if constexpr (FMT == kFmtW4) {
-    const uint32_t mask = vgpr_const(0x000F000Fu), magic = vgpr_const(0x43004300u);
-    const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-    gm_f32x4_t X[kGmMF], P[kGmMF][kGmRB];
-#pragma unroll
-    for (int i = 0; i < kGmMF; ++i) {
-      X[i] = gm_f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int b = 0; b < kGmRB; ++b) P[i][b] = gm_f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 bm[kGmRB];
-#pragma unroll
-      for (int b = 0; b < kGmRB; ++b) {
-        const uint4 wv = st.w[H][b][0];
-        const uint32_t wd = s == 0 ? wv.x : s == 1 ? wv.y : s == 2 ? wv.z : wv.w;
-        bm[b] = make_uint4(and_or_v(wd, mask, magic), and_or_v(wd >> 4, mask, magic), and_or_v(wd >> 8, mask, magic),
-                           and_or_v(wd >> 12, mask, magic));
-      }
-#pragma unroll
-      for (int i = 0; i < kGmMF; ++i) {
-        const uint4 af = xf[((st.wm * kGmMF + i) * 4 + s) * 64];
-        X[i] = gm_mfma(af, ones, X[i]);
-#pragma unroll
-        for (int b = 0; b < kGmRB; ++b) P[i][b] = gm_mfma(af, bm[b], P[i][b]);
-      }
-    }
-    // the chunk is one group; chunks past the split get scale 0
-    const int jq = int((st.kt0 + c) % kScaleQuad);
-    const bool live = c < st.nch;
-#pragma unroll
-    for (int b = 0; b < kGmRB; ++b) {
-      const float s0 = __half2float(__ushort_as_half(uint16_t(st.sw[H][b])));
-      const float sc = live ? s0 : 0.f;
-      const float zc = 128.0f + float((st.zw[H][b] >> (4 * jq)) & 0xFu);
-#pragma unroll
-      for (int i = 0; i < kGmMF; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st.acc[i][b][r] = fmaf(sc, fmaf(-zc, X[i][r], P[i][b][r]), st.acc[i][b][r]);
-    }
-  } else if constexpr (FMT == kFmtFP8) {
+  if constexpr (FMT == kFmtFP8) {
 #pragma unroll
     for (int t = 0; t < F::TPC; ++t)
 #pragma unroll
@@ -227,12 +174,30 @@ __device__ __forceinline__ void gm_compute(GmState<FMT>& st, const uint4* buf, i
   }
 }
 
+// Step for chunk c = 3 it + H: request chunk c + 2 (x first: its wait comes
+// first), multiply chunk c, write the x of chunk c + 1 (loaded a chunk ago)
+// into its LDS buffer (that of chunk c - 2, released by the last barrier).
+// Loads and stores are unconditional: chunks past the split read zero weights
+// (out of range of the weight resources), so no register of the ring is ever
+// a merge of an old and a new value, which would make the compiler copy it
+// (and wait for its load) at the loop's back edge.
+template <int FMT, int WM, int H>
+__device__ __forceinline__ void gm_step(GmState<FMT, WM>& st, const GmArgs& a, uint4 (*s_x)[GmL<FMT, WM>::BUF],
+                                        int c) {
+  constexpr int H1 = (H + 1) % kGmNS, H2 = (H + 2) % kGmNS;
+  gm_load_x<FMT, WM, H2>(st, a, c + 2);
+  gm_load_w<FMT, WM, H2>(st, c + 2);
+  __builtin_amdgcn_sched_barrier(0);
+  gm_compute<FMT, WM, H>(st, s_x[H]);
+  gm_store_x<FMT, WM, H1>(st, s_x[H1]);
+  __syncthreads();
+}
+
 template <int FMT, int WM>
 __global__ __launch_bounds__(64 * WM * kGmWN) void gemm_kernel(GmArgs a) {
   using F = GmF<FMT>;
   using L = GmL<FMT, WM>;
-  static_assert(L::XPW == kGmMF, "x staging registers");
-  __shared__ uint4 s_x[2][L::BUF];
+  __shared__ uint4 s_x[kGmNS][L::BUF];
 
   // XCD-aware order: the workgroups of one XCD sweep the row blocks of x of
   // one column block back to back
@@ -240,59 +205,42 @@ __global__ __launch_bounds__(64 * WM * kGmWN) void gemm_kernel(GmArgs a) {
   const int nbn = (wi / a.MB) * 8 + xcd, mb = wi % a.MB;
   if (nbn >= a.NBN) return;  // whole workgroup, before any barrier
 
-  GmState<FMT> st;
+  GmState<FMT, WM> st;
   st.lane = threadIdx.x & 63;
   st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   st.wm = st.wave / kGmWN;
   const int wn = st.wave % kGmWN;
   const int split = blockIdx.y;
   const int c0 = split * a.cps;
-  st.nch = a.nchunks - c0 < a.cps ? a.nchunks - c0 : a.cps;  // >= 1: the planner sizes S so
+  const int nch = a.nchunks - c0 < a.cps ? a.nchunks - c0 : a.cps;  // >= 1: the planner sizes S so
+  const int nchp = (nch + kGmNS - 1) / kGmNS * kGmNS;  // padded: chunks past the split read zero weights
   st.kt0 = int64_t(c0) * F::TPC;
   st.m0 = int64_t(mb) * 64 * WM;
-  const int64_t tiles = a.KT - st.kt0 < int64_t(st.nch) * F::TPC ? a.KT - st.kt0 : int64_t(st.nch) * F::TPC;
+  const int64_t tiles = a.KT - st.kt0 < int64_t(nch) * F::TPC ? a.KT - st.kt0 : int64_t(nch) * F::TPC;
   const int64_t nb0 = int64_t(nbn) * 16 + wn * kGmRB;
 #pragma unroll
   for (int b = 0; b < kGmRB; ++b) {
-    // row blocks past the matrix get empty resources: zeros, never stored
+    // row blocks past the matrix and tiles past the split read zeros
     const bool live = nb0 + b < a.NB;
     const int64_t nb = live ? nb0 + b : 0;
     st.wres[b] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(a.w + (nb * a.KT + st.kt0) * (kTileBytes / 16)),
                                                    0, live ? uint32_t(tiles) * kTileBytes : 0u, 0x00020000);
-    if constexpr (FMT == kFmtW4) {
-      const uint16_t* sb = reinterpret_cast<const uint16_t*>(a.scales) + nb * a.G4 * kTileRows * kScaleQuad;
-      const uint16_t* zb = a.zeros + nb * a.G4 * kTileRows;
-      st.sres[b] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(sb), 0,
-                                                     live ? uint32_t(a.G4 * kTileRows * kScaleQuad * 2) : 0u,
-                                                     0x00020000);
-      st.zres[b] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(zb), 0,
-                                                     live ? uint32_t(a.G4 * kTileRows * 2) : 0u, 0x00020000);
-    }
 #pragma unroll
     for (int i = 0; i < kGmMF; ++i) st.acc[i][b] = gm_f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   st.xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, 0x7FFFFFF0, 0x00020000);
 
-  // chunk 0 staged, its weights requested
-  gm_load_x<FMT, WM>(st, a, 0);
-  gm_load_w<FMT, 0>(st, 0);
-  gm_store_x<FMT, WM>(st, s_x[0]);
+  // prologue: chunk 0 staged, chunk 1's x in registers, weights of 0 and 1 requested
+  gm_load_x<FMT, WM, 0>(st, a, 0);
+  gm_load_w<FMT, WM, 0>(st, 0);
+  gm_load_x<FMT, WM, 1>(st, a, 1);
+  gm_load_w<FMT, WM, 1>(st, 1);
+  gm_store_x<FMT, WM, 0>(st, s_x[0]);
   __syncthreads();
-  const int nch2 = (st.nch + 1) & ~1;
-  for (int c = 0; c < nch2; c += 2) {
-    // chunk c + 1 requested (x first: its wait comes first), chunk c multiplied
-    gm_load_x<FMT, WM>(st, a, c + 1);
-    gm_load_w<FMT, 1>(st, c + 1);
-    gm_compute<FMT, WM, 0>(st, s_x[0], c);
-    gm_store_x<FMT, WM>(st, s_x[1]);  // buffer 1 held chunk c - 1: released by the last barrier
-    __syncthreads();
-    if (c + 2 < nch2) {
-      gm_load_x<FMT, WM>(st, a, c + 2);
-      gm_load_w<FMT, 0>(st, c + 2);
-    }
-    gm_compute<FMT, WM, 1>(st, s_x[1], c + 1);
-    if (c + 2 < nch2) gm_store_x<FMT, WM>(st, s_x[0]);
-    __syncthreads();
+  for (int c = 0; c < nchp; c += kGmNS) {
+    gm_step<FMT, WM, 0>(st, a, s_x, c);
+    gm_step<FMT, WM, 1>(st, a, s_x, c + 1);
+    gm_step<FMT, WM, 2>(st, a, s_x, c + 2);
   }
 
   // lane (kb, n) holds rows 4 kb + r of each x row block, column n of each row block
@@ -319,9 +267,8 @@ __global__ __launch_bounds__(64 * WM * kGmWN) void gemm_kernel(GmArgs a) {
 template <int FMT>
 static hipError_t launch_gm_fmt(const GmArgs& a, const GmPlan& p, hipStream_t st) {
   const unsigned grid = unsigned(ceil_div(p.NBN, 8) * 8 * p.MB);
-  if (p.wm == 2 && FMT != kFmtW4)
-    hipLaunchKernelGGL((gemm_kernel<FMT, FMT != kFmtW4 ? 2 : 1>), dim3(grid, unsigned(p.S)), dim3(64 * 2 * kGmWN), 0,
-                       st, a);
+  if (p.wm == 2)
+    hipLaunchKernelGGL((gemm_kernel<FMT, 2>), dim3(grid, unsigned(p.S)), dim3(64 * 2 * kGmWN), 0, st, a);
   else if (p.wm == 1)
     hipLaunchKernelGGL((gemm_kernel<FMT, 1>), dim3(grid, unsigned(p.S)), dim3(64 * 1 * kGmWN), 0, st, a);
   else
@@ -342,7 +289,7 @@ hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64
   a.N = N;
   a.K = K;
   a.KT = p.KT;
-  a.G4 = fmt == kFmtW4 ? ceil_div(K / kGroup, kScaleQuad) : 0;
+  a.G4 = 0;
   a.NB = p.NB;
   a.NBN = int(p.NBN);
   a.MB = int(p.MB);
@@ -355,7 +302,7 @@ hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64
   else if (fmt == kFmtFP8)
     e = launch_gm_fmt<kFmtFP8>(a, p, st);
   else
-    e = launch_gm_fmt<kFmtW4>(a, p, st);
+    return hipErrorInvalidValue;  // W4A16 takes the LDS matrix-core kernel
   if (e != hipSuccess || p.S == 1) return e;
   return launch_splitk_reduce(fmt, a.part, p.S, M, N, scales, y, st);
 }

@@ -172,26 +172,23 @@ int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
 }
 
 // Tiled kernel (FP8 / BF16 above kGmMinM rows, where it measured faster than
-// the LDS matrix-core kernel on the 70B verify shapes): 128-row blocks (64 up
-// to 96 rows, for more workgroups, and
-// for W4A16, whose per-group partials and x sums need the register file of a
-// single wavefront per SIMD); K
-// split while the tiles give fewer workgroups than compute units, keeping
-// every split at least 4 chunks long and at most 8 splits.
+// the LDS matrix-core kernel on the 70B verify shapes; W4A16 is not
+// supported): 128-row blocks (64 up to 96 rows, for more workgroups), K in
+// chunks of 64, split while the tiles give fewer workgroups than compute
+// units, keeping every split at least 4 chunks long and at most 8 splits.
 int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   PackedSizes ps;
   int st = packed_sizes(fmt, N, K, &ps);
   if (st != kOK) return st;
   if (M < 1) return kEArg;
-  if (M * K * 2 >= (int64_t(1) << 31)) return kEUnsupported;
-  if (ps.s_bytes >= (size_t(1) << 31) || ps.z_bytes >= (size_t(1) << 31)) return kEUnsupported;
+  if (fmt == kFmtW4 || M * K * 2 >= (int64_t(1) << 31)) return kEUnsupported;
   GmPlan p{};
   p.NB = ps.NB;
   p.KT = ps.KT;
-  p.wm = (M <= 96 || fmt == kFmtW4) ? 1 : 2;
+  p.wm = M <= 96 ? 1 : 2;
   p.NBN = ceil_div(p.NB, 16);
   p.MB = ceil_div(M, 64 * p.wm);
-  p.nchunks = ceil_div(K, 128);
+  p.nchunks = ceil_div(K, 64);
   const int64_t wgs = p.NBN * p.MB;
   int64_t S = 1;
   if (wgs < kComputeUnits) {
