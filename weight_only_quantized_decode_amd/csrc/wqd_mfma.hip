@@ -278,23 +278,63 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
 }
 
 // y = sum of the S split partials, added in split order; FP8 applies the
-// per-column scale after the sum, as the single-pass epilogue does.
+// per-column scale after the sum, as the single-pass epilogue does.  Each
+// thread owns 4 consecutive outputs and requests all S partials before the
+// first add, so the kernel costs one memory round trip, not S.
+constexpr int kMaxSplits = 16;
+
+template <int FMT>
+__device__ __forceinline__ float reduce_scale(float v, const float* __restrict__ colscale, int64_t i, int64_t N) {
+  return FMT == kFmtFP8 ? v * colscale[i % N] : v;
+}
+
 template <int FMT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t M,
                                                             int64_t N, const float* __restrict__ colscale,
                                                             uint16_t* __restrict__ y) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= M * N) return;
-  float v = part[i];
-  for (int s = 1; s < S; ++s) v += part[int64_t(s) * M * N + i];
-  if (FMT == kFmtFP8) v *= colscale[i % N];
-  y[i] = uint16_t(f32_to_bf16_rne(v));
+  const int64_t MN = M * N;
+  const int64_t i0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i0 >= MN) return;
+  if ((MN & 3) == 0) {
+    float4 v[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+      if (s < S) v[s] = *reinterpret_cast<const float4*>(part + int64_t(s) * MN + i0);
+    float4 a = v[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSplits; ++s)
+      if (s < S) {
+        a.x += v[s].x;
+        a.y += v[s].y;
+        a.z += v[s].z;
+        a.w += v[s].w;
+      }
+    const uint32_t lo = f32_to_bf16_rne(reduce_scale<FMT>(a.x, colscale, i0, N)) |
+                        (f32_to_bf16_rne(reduce_scale<FMT>(a.y, colscale, i0 + 1, N)) << 16);
+    const uint32_t hi = f32_to_bf16_rne(reduce_scale<FMT>(a.z, colscale, i0 + 2, N)) |
+                        (f32_to_bf16_rne(reduce_scale<FMT>(a.w, colscale, i0 + 3, N)) << 16);
+    *reinterpret_cast<uint2*>(y + i0) = make_uint2(lo, hi);
+    return;
+  }
+  const int n = MN - i0 < 4 ? int(MN - i0) : 4;
+  for (int e = 0; e < n; ++e) {
+    float v[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+      if (s < S) v[s] = part[int64_t(s) * MN + i0 + e];
+    float a = v[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSplits; ++s)
+      if (s < S) a += v[s];
+    y[i0 + e] = uint16_t(f32_to_bf16_rne(reduce_scale<FMT>(a, colscale, i0 + e, N)));
+  }
 }
 
 hipError_t launch_splitk_reduce(int fmt, const float* part, int S, int64_t M, int64_t N, const void* scales, void* y,
                                 hipStream_t st) {
-  const int64_t total = M * N;
-  const dim3 grid(unsigned((total + 255) / 256));
+  if (S < 1 || S > kMaxSplits) return hipErrorInvalidValue;
+  const int64_t quads = (M * N + 3) / 4;
+  const dim3 grid(unsigned((quads + 255) / 256));
   const float* cs = reinterpret_cast<const float*>(scales);
   uint16_t* yo = reinterpret_cast<uint16_t*>(y);
   if (fmt == kFmtFP8)
