@@ -14,15 +14,17 @@
 //     into registers (FP8 codes convert exactly to bf16, BF16 feeds as is),
 //     each B fragment feeding 4 x row blocks; the FP8 row scale is applied
 //     once at the end;
-//   * K advances in chunks of 64 through a three-stage pipeline: while chunk
-//     c is multiplied, the weights and x of chunk c + 2 are in flight (three
-//     register sets for the weights, three for this wavefront's x fragments)
-//     and the x of chunk c + 1 is written into its LDS buffer (three buffers,
-//     one barrier per chunk).  The loop body is three chunks, so every index
-//     is a compile-time constant.  x sits in LDS in fragment order: fragment
+//   * K advances in chunks of 64 through an NS-stage pipeline (3 for BF16, 4
+//     for FP8, whose weights take half the registers): while chunk c is
+//     multiplied, the weights and x of chunks up to c + NS - 1 are in flight
+//     (NS register sets for the weights, NS for this wavefront's x
+//     fragments) and the x of chunk c + 1 is written into its LDS buffer (one
+//     barrier per chunk).  The loop body is NS chunks, so every index is a
+//     compile-time constant.  x sits in LDS in fragment order: fragment
 //     (tile, x row block i, K-step s) is 1 KiB, lane 16 kb + j holding the 8 k
 //     of row 16 i + j that pair with slice kb of the weights; reads are
-//     conflict-free 16-byte LDS reads;
+//     conflict-free 16-byte LDS reads, all of a chunk's issued before its
+//     first multiply;
 //   * XCD-aware order: consecutive workgroups of one XCD (dispatch is
 //     round-robin over the 8 XCDs) take the row blocks of x of one column
 //     block, so its weights come from HBM once and then from that XCD's L2;
@@ -61,7 +63,6 @@ constexpr int kGmMF = 4;   // x row blocks per wavefront
 constexpr int kGmRB = 4;   // weight row blocks per wavefront
 constexpr int kGmWN = 4;   // wavefronts along N
 constexpr int kGmKC = 64;  // k per chunk
-constexpr int kGmNS = 3;   // stages: chunks c, c + 1 (x in registers), c + 2 (loads in flight)
 
 template <int FMT>
 struct GmF {
@@ -70,6 +71,9 @@ struct GmF {
   static constexpr int SLK = TK / 4;                    // K per slice
   static constexpr int STEPS = SLK / 8;                 // 32-k steps per tile
   static constexpr int TPC = kGmKC / TK;                // tiles per chunk
+  // pipeline stages: chunk c is multiplied while chunks up to c + NS - 1 are
+  // in flight (FP8 weights take half the registers, so one more stage fits)
+  static constexpr int NS = FMT == kFmtFP8 ? 4 : 3;
 };
 
 template <int FMT, int WM>
@@ -84,8 +88,8 @@ struct GmL {
 template <int FMT, int WM>
 struct GmState {
   using F = GmF<FMT>;
-  uint4 w[kGmNS][kGmRB][F::TPC];           // weights of chunks c, c + 1, c + 2
-  uint4 xr[kGmNS][GmL<FMT, WM>::XPW];      // x fragments loaded two chunks ahead
+  uint4 w[F::NS][kGmRB][F::TPC];       // weights of chunks c .. c + NS - 1
+  uint4 xr[F::NS][GmL<FMT, WM>::XPW];  // x fragments loaded NS - 1 chunks ahead
   gm_f32x4_t acc[kGmMF][kGmRB];
   __amdgpu_buffer_rsrc_t wres[kGmRB], xres;
   int64_t kt0, m0;
@@ -100,10 +104,11 @@ __device__ __forceinline__ void gm_load_w(GmState<FMT, WM>& st, int c) {
   for (int b = 0; b < kGmRB; ++b)
 #pragma unroll
     for (int t = 0; t < F::TPC; ++t) {
-      // cache policy 2: non-temporal (each weight byte is read by the few
-      // workgroups of its column block, then not again)
+      // default cache policy: every x row block of the column block (and both
+      // of its wavefront rows) reads these bytes, so they must stay in L2
+      // (streaming them non-temporally cost 5-20% on the 70B verify shapes)
       const u32x4_t v =
-          __builtin_amdgcn_raw_buffer_load_b128(st.wres[b], st.lane * 16, (c * F::TPC + t) * kTileBytes, 2);
+          __builtin_amdgcn_raw_buffer_load_b128(st.wres[b], st.lane * 16, (c * F::TPC + t) * kTileBytes, 0);
       st.w[H][b][t] = make_uint4(v.x, v.y, v.z, v.w);
     }
 }
@@ -134,61 +139,80 @@ __device__ __forceinline__ void gm_store_x(const GmState<FMT, WM>& st, uint4* bu
   for (int u = 0; u < L::XPW; ++u) buf[(st.wave * L::XPW + u) * 64 + st.lane] = st.xr[H][u];
 }
 
-// Multiply the chunk in buf with the weights of set H.
-template <int FMT, int WM, int H>
-__device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, const uint4* buf) {
+// x fragments of the chunk in buf that this wavefront multiplies: 32-k step
+// q, x row block i.
+template <int FMT>
+struct GmFrag {
+  static constexpr int NQ = GmF<FMT>::TPC * GmF<FMT>::STEPS;  // 32-k steps per chunk (2)
+  uint4 a[NQ][kGmMF];
+};
+
+template <int FMT, int WM>
+__device__ __forceinline__ void gm_read_x(const GmState<FMT, WM>& st, const uint4* buf, GmFrag<FMT>& f) {
   using F = GmF<FMT>;
   using L = GmL<FMT, WM>;
   const uint4* xf = buf + st.lane;
+#pragma unroll
+  for (int q = 0; q < GmFrag<FMT>::NQ; ++q)
+#pragma unroll
+    for (int i = 0; i < kGmMF; ++i) {
+      const int t = q / F::STEPS, s = q % F::STEPS;
+      f.a[q][i] = xf[((t * L::XB + st.wm * kGmMF + i) * F::STEPS + s) * 64];
+    }
+}
+
+// Multiply the x fragments with the weights of set H.
+template <int FMT, int WM, int H>
+__device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, const GmFrag<FMT>& f) {
+  using F = GmF<FMT>;
   if constexpr (FMT == kFmtFP8) {
 #pragma unroll
-    for (int t = 0; t < F::TPC; ++t)
+    for (int s = 0; s < 2; ++s) {
+      uint4 bm[kGmRB];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        uint4 bm[kGmRB];
-#pragma unroll
-        for (int b = 0; b < kGmRB; ++b) {
-          const uint4 wv = st.w[H][b][t];
-          const uint32_t w0 = s == 0 ? wv.x : wv.z, w1 = s == 0 ? wv.y : wv.w;
-          bm[b] = make_uint4(__builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(w0)),
-                             __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(w0)),
-                             __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(w1)),
-                             __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(w1)));
-        }
-#pragma unroll
-        for (int i = 0; i < kGmMF; ++i) {
-          const uint4 af = xf[((t * L::XB + st.wm * kGmMF + i) * 2 + s) * 64];
-#pragma unroll
-          for (int b = 0; b < kGmRB; ++b) st.acc[i][b] = gm_mfma(af, bm[b], st.acc[i][b]);
-        }
+      for (int b = 0; b < kGmRB; ++b) {
+        const uint4 wv = st.w[H][b][0];
+        const uint32_t w0 = s == 0 ? wv.x : wv.z, w1 = s == 0 ? wv.y : wv.w;
+        bm[b] = make_uint4(__builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(w0)),
+                           __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(w0)),
+                           __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(w1)),
+                           __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(w1)));
       }
+#pragma unroll
+      for (int i = 0; i < kGmMF; ++i)
+#pragma unroll
+        for (int b = 0; b < kGmRB; ++b) st.acc[i][b] = gm_mfma(f.a[s][i], bm[b], st.acc[i][b]);
+    }
   } else {
 #pragma unroll
     for (int t = 0; t < F::TPC; ++t)
 #pragma unroll
-      for (int i = 0; i < kGmMF; ++i) {
-        const uint4 af = xf[(t * L::XB + st.wm * kGmMF + i) * 64];
+      for (int i = 0; i < kGmMF; ++i)
 #pragma unroll
-        for (int b = 0; b < kGmRB; ++b) st.acc[i][b] = gm_mfma(af, st.w[H][b][t], st.acc[i][b]);
-      }
+        for (int b = 0; b < kGmRB; ++b) st.acc[i][b] = gm_mfma(f.a[t][i], st.w[H][b][t], st.acc[i][b]);
   }
 }
 
-// Step for chunk c = 3 it + H: request chunk c + 2 (x first: its wait comes
-// first), multiply chunk c, write the x of chunk c + 1 (loaded a chunk ago)
-// into its LDS buffer (that of chunk c - 2, released by the last barrier).
-// Loads and stores are unconditional: chunks past the split read zero weights
-// (out of range of the weight resources), so no register of the ring is ever
-// a merge of an old and a new value, which would make the compiler copy it
-// (and wait for its load) at the loop's back edge.
+// Step for chunk c = 3 it + H: read this wavefront's x fragments of chunk c
+// from LDS, request chunk c + 2 (x first: its wait comes first; the LDS reads
+// land meanwhile), multiply chunk c, write the x of chunk c + 1 (loaded a
+// chunk ago) into its LDS buffer (that of chunk c - 2, released by the last
+// barrier).  Loads and stores are unconditional: chunks past the split read
+// zero weights (out of range of the weight resources), so no register of the
+// ring is ever a merge of an old and a new value, which would make the
+// compiler copy it (and wait for its load) at the loop's back edge.
 template <int FMT, int WM, int H>
 __device__ __forceinline__ void gm_step(GmState<FMT, WM>& st, const GmArgs& a, uint4 (*s_x)[GmL<FMT, WM>::BUF],
                                         int c) {
-  constexpr int H1 = (H + 1) % kGmNS, H2 = (H + 2) % kGmNS;
-  gm_load_x<FMT, WM, H2>(st, a, c + 2);
-  gm_load_w<FMT, WM, H2>(st, c + 2);
+  constexpr int NS = GmF<FMT>::NS;
+  constexpr int H1 = (H + 1) % NS, HL = (H + NS - 1) % NS;
+  GmFrag<FMT> f;
+  gm_read_x<FMT, WM>(st, s_x[H], f);
   __builtin_amdgcn_sched_barrier(0);
-  gm_compute<FMT, WM, H>(st, s_x[H]);
+  gm_load_x<FMT, WM, HL>(st, a, c + NS - 1);
+  gm_load_w<FMT, WM, HL>(st, c + NS - 1);
+  __builtin_amdgcn_sched_barrier(0);
+  gm_compute<FMT, WM, H>(st, f);
   gm_store_x<FMT, WM, H1>(st, s_x[H1]);
   __syncthreads();
 }
@@ -197,7 +221,8 @@ template <int FMT, int WM>
 __global__ __launch_bounds__(64 * WM * kGmWN) void gemm_kernel(GmArgs a) {
   using F = GmF<FMT>;
   using L = GmL<FMT, WM>;
-  __shared__ uint4 s_x[kGmNS][L::BUF];
+  constexpr int NS = F::NS;
+  __shared__ uint4 s_x[NS][L::BUF];
 
   // XCD-aware order: the workgroups of one XCD sweep the row blocks of x of
   // one column block back to back
@@ -213,7 +238,7 @@ __global__ __launch_bounds__(64 * WM * kGmWN) void gemm_kernel(GmArgs a) {
   const int split = blockIdx.y;
   const int c0 = split * a.cps;
   const int nch = a.nchunks - c0 < a.cps ? a.nchunks - c0 : a.cps;  // >= 1: the planner sizes S so
-  const int nchp = (nch + kGmNS - 1) / kGmNS * kGmNS;  // padded: chunks past the split read zero weights
+  const int nchp = (nch + NS - 1) / NS * NS;  // padded: chunks past the split read zero weights
   st.kt0 = int64_t(c0) * F::TPC;
   st.m0 = int64_t(mb) * 64 * WM;
   const int64_t tiles = a.KT - st.kt0 < int64_t(nch) * F::TPC ? a.KT - st.kt0 : int64_t(nch) * F::TPC;
@@ -230,17 +255,22 @@ __global__ __launch_bounds__(64 * WM * kGmWN) void gemm_kernel(GmArgs a) {
   }
   st.xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, 0x7FFFFFF0, 0x00020000);
 
-  // prologue: chunk 0 staged, chunk 1's x in registers, weights of 0 and 1 requested
+  // prologue: chunks 0 .. NS - 2 requested, chunk 0 staged
   gm_load_x<FMT, WM, 0>(st, a, 0);
   gm_load_w<FMT, WM, 0>(st, 0);
   gm_load_x<FMT, WM, 1>(st, a, 1);
   gm_load_w<FMT, WM, 1>(st, 1);
+  if constexpr (NS > 3) {
+    gm_load_x<FMT, WM, 2>(st, a, 2);
+    gm_load_w<FMT, WM, 2>(st, 2);
+  }
   gm_store_x<FMT, WM, 0>(st, s_x[0]);
   __syncthreads();
-  for (int c = 0; c < nchp; c += kGmNS) {
+  for (int c = 0; c < nchp; c += NS) {
     gm_step<FMT, WM, 0>(st, a, s_x, c);
     gm_step<FMT, WM, 1>(st, a, s_x, c + 1);
     gm_step<FMT, WM, 2>(st, a, s_x, c + 2);
+    if constexpr (NS > 3) gm_step<FMT, WM, 3 % NS>(st, a, s_x, c + 3);
   }
 
   // lane (kb, n) holds rows 4 kb + r of each x row block, column n of each row block
