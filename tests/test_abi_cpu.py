@@ -129,13 +129,24 @@ def test_kernel_path_choice():
         for fmt in ("w4a16", "fp8", "bf16"):
             assert wqd.kernel_path(fmt, M, 8192, 8192) == ("skinny", 5)
     assert wqd.kernel_path("fp8", 16, 8192, 8208)[0] == "mfma"          # K not a whole number of 64-k tiles
-    # above 256 rows, FP8 / BF16: the tiled matrix-core kernel (8 wavefronts)
-    assert wqd.kernel_path("bf16", 257, 8192, 8192) == ("gemm", 8)
+    # above 64 rows, FP8 / BF16 with at least 16 column blocks of 256: the tiled
+    # matrix-core kernel (4 wavefronts up to 128 rows, 8 above)
+    assert wqd.kernel_path("bf16", 65, 8192, 8192) == ("gemm", 4)
+    assert wqd.kernel_path("fp8", 128, 4096, 8192) == ("gemm", 4)
+    assert wqd.kernel_path("bf16", 129, 8192, 8192) == ("gemm", 8)
     assert wqd.kernel_path("fp8", 1024, 28672, 8192) == ("gemm", 8)
-    # otherwise above 64 rows (and W4A16): the LDS matrix-core kernel
+    # otherwise above 64 rows (W4A16, or N under 16 x 256): the LDS matrix-core kernel
     for M in (65, 1024):
         assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "mfma"
-    assert wqd.kernel_path("bf16", 256, 8192, 8192)[0] == "mfma"
+    assert wqd.kernel_path("bf16", 256, 1024, 8192)[0] == "mfma"
+    assert wqd.kernel_path("fp8", 256, 3840, 8192)[0] == "mfma"
+    # the tiled kernel's K split: whole splits of M x N float32 partials, at most 8
+    for fmt, M, N, K in (("bf16", 128, 8192, 28672), ("fp8", 384, 8192, 8192), ("bf16", 1024, 28672, 8192),
+                         ("fp8", 96, 4096, 4096)):
+        ws = wqd.workspace_bytes(fmt, M, N, K)
+        assert ws % (M * N * 4) == 0 and ws // (M * N * 4) in (0, 2, 3, 4, 5, 6, 7, 8)
+    assert wqd.workspace_bytes("bf16", 128, 8192, 28672) == 4 * 128 * 8192 * 4  # 64 tiles: 4 splits fill the GPU
+    assert wqd.workspace_bytes("bf16", 1024, 28672, 8192) == 0                  # 896 tiles: no split
     # x rows spanning 2 GiB: the LDS matrix-core kernel
     assert wqd.kernel_path("bf16", 65536, 64, 16384)[0] == "mfma"
     L = wqd.lib()

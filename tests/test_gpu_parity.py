@@ -200,23 +200,48 @@ def test_qgemm_skinny(fmt):
 
 
 def tiled_shapes():
-    # (N, K) for the tiled matrix-core kernel: a partial column block, odd
-    # chunk counts (5, 9), K splits over few workgroups, and a K that ends
-    # inside a tile (x past K reads as zero)
-    return [(300, 648), (1000, 1160), (4104, 4096)]
+    # (N, K) for the tiled matrix-core kernel (at least 16 column blocks of
+    # 256): a partial column block, odd chunk counts (11, 19), K splits over
+    # few workgroups, and a K that ends inside a tile (x past K reads as zero)
+    return [(3900, 648), (4000, 1160), (4104, 4096)]
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "bf16"])
 def test_qgemm_tiled(fmt):
-    """Wide verify batches: 128-row tiles of y with a ragged last row block."""
+    """Wide verify batches: 64- and 128-row tiles of y with a ragged last row block."""
     for N, K in tiled_shapes():
         W = I.w_host(6000 + N + K, N, K)
         qw = oracle.quantize(fmt, W)
         pw = wqd.pack_weights(fmt, to_dev(W))
-        for M in (257, 300, 384):
+        for M in (65, 100, 128, 129, 257, 300, 384):
             assert wqd.kernel_path(fmt, M, N, K)[0] == "gemm"
             print(f"qgemm {fmt} M={M} N={N} K={K} ws={wqd.workspace_bytes(fmt, M, N, K)}", flush=True)
             x = I.x_bf16_bits(31 * M + K, M, K)
+            y = wqd.qgemm(x_dev(x), pw)
+            torch.cuda.synchronize()
+            compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
+
+
+def mfma_wide_shapes(fmt):
+    # (N, K) that the LDS matrix-core kernel takes above 64 rows (every format
+    # below 16 column blocks of 256; W4A16 always): ragged N, ragged K tiles
+    # where the format allows them, and a K split
+    if fmt == "w4a16":
+        return [(357, 896), (1000, 1152), (3840, 512), (8200, 1024)]
+    return [(357, 904), (1000, 1160), (3840, 512)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_qgemm_mfma_wide(fmt):
+    """Wide batches on narrow matrices: 16 to 64 rows per block of the LDS kernel."""
+    for N, K in mfma_wide_shapes(fmt):
+        W = I.w_host(7000 + N + K, N, K)
+        qw = oracle.quantize(fmt, W)
+        pw = wqd.pack_weights(fmt, to_dev(W))
+        for M in (65, 100, 200, 300):
+            assert wqd.kernel_path(fmt, M, N, K)[0] == "mfma"
+            print(f"qgemm {fmt} M={M} N={N} K={K} ws={wqd.workspace_bytes(fmt, M, N, K)}", flush=True)
+            x = I.x_bf16_bits(37 * M + K, M, K)
             y = wqd.qgemm(x_dev(x), pw)
             torch.cuda.synchronize()
             compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")

@@ -172,10 +172,15 @@ int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
 }
 
 // Tiled kernel (FP8 / BF16 above kGmMinM rows, where it measured faster than
-// the LDS matrix-core kernel on the 70B verify shapes; W4A16 is not
-// supported): 128-row blocks (64 up to 96 rows, for more workgroups), K in
-// chunks of 64, split while the tiles give fewer workgroups than compute
-// units, keeping every split at least 4 chunks long and at most 8 splits.
+// the LDS matrix-core kernel on the 70B verify shapes once N gives at least
+// kGmMinNBN column blocks; W4A16 is not supported): 64-row blocks up to 128
+// rows, 128-row blocks above, K in chunks of 64.  The K split comes from a
+// time model fitted to the kernel on those shapes: with one workgroup per
+// compute unit, the launch runs ceil(W / 256) rounds of cps chunks each (W =
+// tiles x splits), about 1.46 us per chunk for BF16 and 1.1 for FP8 (0.8 of
+// that with 64-row blocks), and every split adds M x N float32 partials
+// written and read once at about 4 TB/s.  The cheapest S from 1 to 8 (each
+// split at least 4 chunks) wins; within 2% the smaller S.
 int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   PackedSizes ps;
   int st = packed_sizes(fmt, N, K, &ps);
@@ -185,17 +190,24 @@ int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   GmPlan p{};
   p.NB = ps.NB;
   p.KT = ps.KT;
-  p.wm = M <= 96 ? 1 : 2;
+  p.wm = M <= 128 ? 1 : 2;
   p.NBN = ceil_div(p.NB, 16);
   p.MB = ceil_div(M, 64 * p.wm);
   p.nchunks = ceil_div(K, 64);
-  const int64_t wgs = p.NBN * p.MB;
+  const int64_t tiles = p.NBN * p.MB;
+  const double t_chunk = (fmt == kFmtFP8 ? 1.1 : 1.46) * (p.wm == 1 ? 0.8 : 1.0);  // us
+  const double part_us = double(M) * double(N) * 8.0 / 4.0e6;  // one split's partials, us
+  const int64_t max_s = p.nchunks / 4 < 1 ? 1 : (p.nchunks / 4 > 8 ? 8 : p.nchunks / 4);
+  double best = 0.0;
   int64_t S = 1;
-  if (wgs < kComputeUnits) {
-    S = ceil_div(kComputeUnits, wgs);
-    const int64_t max_s = p.nchunks / 4 > 1 ? p.nchunks / 4 : 1;
-    if (S > max_s) S = max_s;
-    if (S > 8) S = 8;
+  for (int64_t s = 1; s <= max_s; ++s) {
+    const int64_t cps = ceil_div(p.nchunks, s), se = ceil_div(p.nchunks, cps);
+    const double t = double(ceil_div(tiles * se, kComputeUnits)) * double(cps) * t_chunk +
+                     (se > 1 ? double(se) * part_us : 0.0);
+    if (s == 1 || t < 0.98 * best) {
+      best = t;
+      S = se;
+    }
   }
   p.cps = ceil_div(p.nchunks, S);
   p.S = int(ceil_div(p.nchunks, p.cps));
@@ -262,7 +274,8 @@ int choose_path(int fmt, int64_t M, int64_t N, int64_t K, Choice* out) {
     c.path = kPathStaged;
   } else if (M <= kSkMaxM && sk_ok) {
     c.path = kPathSkinny;
-  } else if (M > kGmMinM && fmt != kFmtW4 && plan_gemm(fmt, M, N, K, &c.gm) == kOK) {
+  } else if (M > kGmMinM && fmt != kFmtW4 && ceil_div(N, int64_t(256)) >= kGmMinNBN &&
+             plan_gemm(fmt, M, N, K, &c.gm) == kOK) {
     c.path = kPathGemm;
   } else {
     st = plan_mfma(fmt, M, N, K, &c.mfma);

@@ -104,13 +104,15 @@ struct SkPlan {
 
 int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out);
 
-// Tiled matrix-core kernel (FP8 / BF16, more than 64 rows): a workgroup of
-// 4 wm wavefronts computes a (64 wm) x 256 tile of y; NBN column blocks x MB
-// row blocks of workgroups (XCD-aware order), K in chunks of 64 split S ways
-// (cps chunks per split) when that leaves fewer than one workgroup per
-// compute unit; the S float32 partials need S * M * N * 4 bytes of workspace.
-// kEUnsupported for W4A16 and for x rows spanning 2 GiB or more.
-constexpr int kGmMinM = 256;
+// Tiled matrix-core kernel (FP8 / BF16, more than kGmMinM rows and at least
+// kGmMinNBN column blocks): a workgroup of 4 wm wavefronts computes a
+// (64 wm) x 256 tile of y; NBN column blocks x MB row blocks of workgroups
+// (XCD-aware order), K in chunks of 64 split S ways (cps chunks per split) as
+// a time model of the kernel picks; the S float32 partials need
+// S * M * N * 4 bytes of workspace.  kEUnsupported for W4A16 and for x rows
+// spanning 2 GiB or more.
+constexpr int kGmMinM = 64;
+constexpr int64_t kGmMinNBN = 16;
 
 struct GmPlan {
   int64_t NB, KT, NBN, MB, nchunks, cps;
