@@ -84,12 +84,15 @@ def test_workspace_query():
     for fmt in ("bf16", "fp8", "w4a16"):
         for M in (1, 4):
             assert wqd.workspace_bytes(fmt, M, 8192, 8192) == 0  # streaming kernels: none
-        # matrix-core paths: split-K partials only when the row blocks give too few workgroups
-        assert wqd.workspace_bytes(fmt, 1024, 28672, 8192) == 0
+        # matrix-core paths: split-K partials only when the row blocks give too
+        # few workgroups; the tiled kernel's W4A16 x sums, float32 per (group,
+        # row of the 64-row blocks), before them
+        xs = lambda M, K: (K // 128) * (-(-M // 64) * 64) * 4 if fmt == "w4a16" else 0
+        assert wqd.workspace_bytes(fmt, 1024, 28672, 8192) == xs(1024, 8192)
         assert wqd.workspace_bytes(fmt, 16, 57344, 8192) == 0
         ws = wqd.workspace_bytes(fmt, 16, 8192, 8192)
         assert ws > 0 and ws % (16 * 8192 * 4) == 0 and ws // (16 * 8192 * 4) <= 8
-        ws = wqd.workspace_bytes(fmt, 80, 8192, 8192)
+        ws = wqd.workspace_bytes(fmt, 80, 8192, 8192) - xs(80, 8192)
         assert ws > 0 and ws % (80 * 8192 * 4) == 0
     L = wqd.lib()
     assert L.wqd_workspace_bytes(2, 1, 64, 128, None) == E_ARG
@@ -129,15 +132,16 @@ def test_kernel_path_choice():
         for fmt in ("w4a16", "fp8", "bf16"):
             assert wqd.kernel_path(fmt, M, 8192, 8192) == ("skinny", 5)
     assert wqd.kernel_path("fp8", 16, 8192, 8208)[0] == "mfma"          # K not a whole number of 64-k tiles
-    # above 64 rows, FP8 / BF16 with at least 16 column blocks of 256: the tiled
-    # matrix-core kernel (4 wavefronts up to 128 rows, 8 above)
+    # above 64 rows with at least 16 column blocks of 256: the tiled matrix-core
+    # kernel (FP8 / BF16: 4 wavefronts up to 128 rows, 8 above; W4A16: 8)
     assert wqd.kernel_path("bf16", 65, 8192, 8192) == ("gemm", 4)
     assert wqd.kernel_path("fp8", 128, 4096, 8192) == ("gemm", 4)
     assert wqd.kernel_path("bf16", 129, 8192, 8192) == ("gemm", 8)
     assert wqd.kernel_path("fp8", 1024, 28672, 8192) == ("gemm", 8)
-    # otherwise above 64 rows (W4A16, or N under 16 x 256): the LDS matrix-core kernel
     for M in (65, 1024):
-        assert wqd.kernel_path("w4a16", M, 8192, 8192)[0] == "mfma"
+        assert wqd.kernel_path("w4a16", M, 8192, 8192) == ("gemm", 8)
+    # otherwise above 64 rows (N under 16 x 256): the LDS matrix-core kernel
+    assert wqd.kernel_path("w4a16", 256, 3840, 8192)[0] == "mfma"
     assert wqd.kernel_path("bf16", 256, 1024, 8192)[0] == "mfma"
     assert wqd.kernel_path("fp8", 256, 3840, 8192)[0] == "mfma"
     # the tiled kernel's K split: whole splits of M x N float32 partials, at most 8

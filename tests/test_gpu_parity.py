@@ -199,17 +199,20 @@ def test_qgemm_skinny(fmt):
             compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
-def tiled_shapes():
+def tiled_shapes(fmt):
     # (N, K) for the tiled matrix-core kernel (at least 16 column blocks of
-    # 256): a partial column block, odd chunk counts (11, 19), K splits over
-    # few workgroups, and a K that ends inside a tile (x past K reads as zero)
+    # 256): a partial column block, odd chunk counts (11, 19; W4A16 5, 9), K
+    # splits over few workgroups, and a K that ends inside a tile (x past K
+    # reads as zero; W4A16 K is whole groups)
+    if fmt == "w4a16":
+        return [(3900, 640), (4000, 1152), (4104, 4096)]
     return [(3900, 648), (4000, 1160), (4104, 4096)]
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "bf16"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_qgemm_tiled(fmt):
     """Wide verify batches: 64- and 128-row tiles of y with a ragged last row block."""
-    for N, K in tiled_shapes():
+    for N, K in tiled_shapes(fmt):
         W = I.w_host(6000 + N + K, N, K)
         qw = oracle.quantize(fmt, W)
         pw = wqd.pack_weights(fmt, to_dev(W))
@@ -223,11 +226,11 @@ def test_qgemm_tiled(fmt):
 
 
 def mfma_wide_shapes(fmt):
-    # (N, K) that the LDS matrix-core kernel takes above 64 rows (every format
-    # below 16 column blocks of 256; W4A16 always): ragged N, ragged K tiles
-    # where the format allows them, and a K split
+    # (N, K) that the LDS matrix-core kernel takes above 64 rows (below 16
+    # column blocks of 256): ragged N, ragged K tiles where the format allows
+    # them, and a K split
     if fmt == "w4a16":
-        return [(357, 896), (1000, 1152), (3840, 512), (8200, 1024)]
+        return [(357, 896), (1000, 1152), (3840, 1024)]
     return [(357, 904), (1000, 1160), (3840, 512)]
 
 

@@ -171,31 +171,34 @@ int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
   return kOK;
 }
 
-// Tiled kernel (FP8 / BF16 above kGmMinM rows, where it measured faster than
-// the LDS matrix-core kernel on the 70B verify shapes once N gives at least
-// kGmMinNBN column blocks; W4A16 is not supported): 64-row blocks up to 128
-// rows, 128-row blocks above, K in chunks of 64.  The K split comes from a
-// time model fitted to the kernel on those shapes: with one workgroup per
-// compute unit, the launch runs ceil(W / 256) rounds of cps chunks each (W =
-// tiles x splits), about 1.46 us per chunk for BF16 and 1.1 for FP8 (0.8 of
-// that with 64-row blocks), and every split adds M x N float32 partials
-// written and read once at about 4 TB/s.  The cheapest S from 1 to 8 (each
-// split at least 4 chunks) wins; within 2% the smaller S.
+// Tiled kernel (above kGmMinM rows, where it measured faster than the LDS
+// matrix-core kernel on the 70B verify shapes once N gives at least kGmMinNBN
+// column blocks): BF16 / FP8 64-row blocks up to 128 rows, 128-row blocks
+// above; W4A16 64-row blocks.  The K split comes from a time model fitted to
+// the kernel on those shapes: with one workgroup per compute unit, the launch
+// runs ceil(W / 256) rounds of cps chunks each (W = tiles x splits), about
+// 1.46 us per 64-k chunk for BF16, 1.1 for FP8 (0.8 of that with 64-row
+// blocks) and 1.42 per 128-k chunk for W4A16, and every split adds M x N
+// float32 partials written and read once at about 4 TB/s.  The cheapest S
+// from 1 to 8 (each split at least 4 chunks) wins; within 2% the smaller S.
 int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   PackedSizes ps;
   int st = packed_sizes(fmt, N, K, &ps);
   if (st != kOK) return st;
   if (M < 1) return kEArg;
-  if (fmt == kFmtW4 || M * K * 2 >= (int64_t(1) << 31)) return kEUnsupported;
+  if (M * K * 2 >= (int64_t(1) << 31)) return kEUnsupported;
   GmPlan p{};
   p.NB = ps.NB;
   p.KT = ps.KT;
-  p.wm = M <= 128 ? 1 : 2;
+  p.wm = fmt == kFmtW4 || M <= 128 ? 1 : 2;
   p.NBN = ceil_div(p.NB, 16);
   p.MB = ceil_div(M, 64 * p.wm);
-  p.nchunks = ceil_div(K, 64);
+  p.Mp = p.MB * 64 * p.wm;
+  p.nchunks = fmt == kFmtW4 ? p.KT : ceil_div(K, 64);
+  if (fmt == kFmtW4 && p.KT * p.Mp * 4 >= (int64_t(1) << 31)) return kEUnsupported;
+  p.xs_bytes = fmt == kFmtW4 ? (size_t(p.KT) * size_t(p.Mp) * sizeof(float) + 255) / 256 * 256 : 0;
   const int64_t tiles = p.NBN * p.MB;
-  const double t_chunk = (fmt == kFmtFP8 ? 1.1 : 1.46) * (p.wm == 1 ? 0.8 : 1.0);  // us
+  const double t_chunk = fmt == kFmtW4 ? 1.42 : (fmt == kFmtFP8 ? 1.1 : 1.46) * (p.wm == 1 ? 0.8 : 1.0);  // us
   const double part_us = double(M) * double(N) * 8.0 / 4.0e6;  // one split's partials, us
   const int64_t max_s = p.nchunks / 4 < 1 ? 1 : (p.nchunks / 4 > 8 ? 8 : p.nchunks / 4);
   double best = 0.0;
@@ -211,7 +214,7 @@ int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   }
   p.cps = ceil_div(p.nchunks, S);
   p.S = int(ceil_div(p.nchunks, p.cps));
-  p.ws_bytes = p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;
+  p.ws_bytes = p.xs_bytes + (p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0);
   *out = p;
   return kOK;
 }
@@ -274,8 +277,7 @@ int choose_path(int fmt, int64_t M, int64_t N, int64_t K, Choice* out) {
     c.path = kPathStaged;
   } else if (M <= kSkMaxM && sk_ok) {
     c.path = kPathSkinny;
-  } else if (M > kGmMinM && fmt != kFmtW4 && ceil_div(N, int64_t(256)) >= kGmMinNBN &&
-             plan_gemm(fmt, M, N, K, &c.gm) == kOK) {
+  } else if (M > kGmMinM && ceil_div(N, int64_t(256)) >= kGmMinNBN && plan_gemm(fmt, M, N, K, &c.gm) == kOK) {
     c.path = kPathGemm;
   } else {
     st = plan_mfma(fmt, M, N, K, &c.mfma);

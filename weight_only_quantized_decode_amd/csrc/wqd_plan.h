@@ -104,20 +104,22 @@ struct SkPlan {
 
 int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out);
 
-// Tiled matrix-core kernel (FP8 / BF16, more than kGmMinM rows and at least
-// kGmMinNBN column blocks): a workgroup of 4 wm wavefronts computes a
-// (64 wm) x 256 tile of y; NBN column blocks x MB row blocks of workgroups
-// (XCD-aware order), K in chunks of 64 split S ways (cps chunks per split) as
-// a time model of the kernel picks; the S float32 partials need
-// S * M * N * 4 bytes of workspace.  kEUnsupported for W4A16 and for x rows
-// spanning 2 GiB or more.
+// Tiled matrix-core kernel (more than kGmMinM rows and at least kGmMinNBN
+// column blocks): a workgroup of 8 wavefronts (BF16 / FP8 above 128 rows:
+// wm = 2, 8 wavefronts of 64 x 64; otherwise wm = 1: BF16 / FP8 4 of 64 x 64,
+// W4A16 8 of 64 x 32) computes a (64 wm) x 256 tile of y; NBN column blocks x
+// MB row blocks of workgroups (XCD-aware order), K in chunks (64; W4A16 128)
+// split S ways (cps chunks per split) as a time model of the kernel picks.
+// Workspace: W4A16 x sums, float32 [KT][Mp] (Mp = 64 MB rows), xs_bytes
+// rounded up to 256; then the S float32 partials, S * M * N * 4 bytes when
+// S > 1.  kEUnsupported for x rows spanning 2 GiB or more.
 constexpr int kGmMinM = 64;
 constexpr int64_t kGmMinNBN = 16;
 
 struct GmPlan {
-  int64_t NB, KT, NBN, MB, nchunks, cps;
+  int64_t NB, KT, NBN, MB, nchunks, cps, Mp;
   int wm, S;
-  size_t ws_bytes;
+  size_t xs_bytes, ws_bytes;
 };
 
 int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out);
