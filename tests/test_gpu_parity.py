@@ -175,10 +175,12 @@ def skinny_shapes(fmt):
     # consumers of one row block), 5 tiles over 3073 row blocks (7 consumers
     # of two row blocks, no K split, a half-live last workgroup), 512 row blocks
     # of 64 tiles (4 consumers of two row blocks, 4-way K split), 257 and 63 row
-    # blocks (ragged last groups, K splits), and a 7-way split whose last split
-    # is short (28 of 32 tiles)
+    # blocks (ragged last groups, K splits), a 7-way split whose last split
+    # is short (28 of 32 tiles), and 640 row blocks of 64 tiles (5 consumers
+    # of two row blocks, 4-way K split)
     tk = {"w4a16": 128, "fp8": 64, "bf16": 32}[fmt]
-    return [(2000, 13 * tk), (49160, 5 * tk), (8192, 64 * tk), (4104, 64 * tk), (1000, 8192), (300, 220 * tk)]
+    return [(2000, 13 * tk), (49160, 5 * tk), (8192, 64 * tk), (4104, 64 * tk), (1000, 8192), (300, 220 * tk),
+            (10240, 64 * tk)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -107,7 +107,8 @@ int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out) {
 }
 
 // Skinny kernel: consumer wavefronts per workgroup and row blocks per consumer
-// from (7, 2), (7, 1), (4, 2) (x chunks shared by 14, 7 or 8 row blocks); a
+// from (7, 2), (7, 1), (4, 2), (5, 2) (x chunks shared by 14, 7, 8 or 10 row
+// blocks; 10 fills the compute units for N = 10240 with 4 splits); a
 // ring of 8 weight tiles per row block; x chunks of 4 tiles (2 for W4A16 from
 // 17 rows and for everything from 33, whose chunks would otherwise need up to
 // 200 KiB of LDS), three buffers.  K is
@@ -153,10 +154,9 @@ int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
   if (M > kSkMaxM || M * K * 2 >= (int64_t(1) << 31)) return kEUnsupported;
   if (K % tile_k(fmt) != 0) return kEUnsupported;
   if (ps.s_bytes >= (size_t(1) << 31) || ps.z_bytes >= (size_t(1) << 31)) return kEUnsupported;
-  static const int kCfg[3][2] = {{7, 2}, {7, 1}, {4, 2}};
   SkPlan p{};
   double best = -1.0;
-  for (const auto& cfg : kCfg) {
+  for (const auto& cfg : kSkCfg) {
     SkPlan q;
     plan_skinny_with(fmt, M, ps, cfg[0], cfg[1], 0, &q);
     const int64_t W = q.groups * q.S;

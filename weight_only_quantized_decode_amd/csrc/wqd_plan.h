@@ -102,6 +102,12 @@ struct SkPlan {
   size_t ws_bytes;
 };
 
+// The skinny kernel's (consumer wavefronts, row blocks per consumer)
+// configurations: the planner chooses among them and the kernel file
+// instantiates every one for 1 to 4 x row blocks.
+constexpr int kSkCfgCount = 4;
+constexpr int kSkCfg[kSkCfgCount][2] = {{7, 2}, {7, 1}, {4, 2}, {5, 2}};
+
 int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out);
 
 // Tiled matrix-core kernel (more than kGmMinM rows and at least kGmMinNBN

@@ -391,28 +391,28 @@ static hipError_t launch_sk_cfg(const SkArgs& a, const SkPlan& p, hipStream_t st
   return hipGetLastError();
 }
 
-// The configurations the planner chooses from: x row blocks, weight row
-// blocks per consumer, consumers per workgroup.
+// Every configuration the planner chooses from (kSkCfg: consumers, weight row
+// blocks per consumer), for 1 to 4 x row blocks.
+template <int FMT, int MF, int I>
+static hipError_t launch_sk_try(const SkArgs& a, const SkPlan& p, hipStream_t st) {
+  if constexpr (I == kSkCfgCount) {
+    return hipErrorInvalidValue;
+  } else {
+    constexpr int WN = kSkCfg[I][0], RB = kSkCfg[I][1];
+    if (p.waves == WN && p.rb == RB) return launch_sk_cfg<FMT, MF, RB, WN>(a, p, st);
+    return launch_sk_try<FMT, MF, I + 1>(a, p, st);
+  }
+}
+
 template <int FMT>
 static hipError_t launch_sk_fmt(const SkArgs& a, const SkPlan& p, hipStream_t st) {
-#define WQD_SK_CFG(MF, RB, WN) \
-  if (p.mf == MF && p.rb == RB && p.waves == WN) return launch_sk_cfg<FMT, MF, RB, WN>(a, p, st);
-  WQD_SK_CFG(1, 2, 4)
-  WQD_SK_CFG(1, 2, 5)
-  WQD_SK_CFG(1, 1, 7)
-  WQD_SK_CFG(1, 2, 7)
-  WQD_SK_CFG(2, 2, 4)
-  WQD_SK_CFG(2, 2, 5)
-  WQD_SK_CFG(2, 1, 7)
-  WQD_SK_CFG(2, 2, 7)
-  WQD_SK_CFG(3, 2, 4)
-  WQD_SK_CFG(3, 1, 7)
-  WQD_SK_CFG(3, 2, 7)
-  WQD_SK_CFG(4, 2, 4)
-  WQD_SK_CFG(4, 1, 7)
-  WQD_SK_CFG(4, 2, 7)
-#undef WQD_SK_CFG
-  return hipErrorInvalidValue;
+  switch (p.mf) {
+    case 1: return launch_sk_try<FMT, 1, 0>(a, p, st);
+    case 2: return launch_sk_try<FMT, 2, 0>(a, p, st);
+    case 3: return launch_sk_try<FMT, 3, 0>(a, p, st);
+    case 4: return launch_sk_try<FMT, 4, 0>(a, p, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gemv_sk(int fmt, const SkPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
