@@ -99,11 +99,14 @@ int wqd_packed_sizes(int fmt, int64_t N, int64_t K,
 
 /*
  * Host-only: bytes of scratch workspace wqd_qgemm needs for this shape (may
- * be 0).  Only the matrix-core paths above 8 rows use one, when they split K
- * over workgroups: it holds their float32 partial tiles (S * M * N * 4
- * bytes), which a second kernel adds in split order.  Its contents on entry do not matter (every byte read
- * is written first in the same call).  One workspace must not be used by two
- * calls that can run at the same time.
+ * be 0).  The matrix-core paths use one when they split K over workgroups:
+ * it holds their float32 partial tiles (S * M * N * 4 bytes), which a second
+ * kernel adds in split order.  W4A16 on the tiled matrix-core kernel also
+ * keeps the x sums of each 128-k group there (float32, K / 128 x M rounded
+ * up to 64 rows, first), written by a first kernel of the same call.  Its
+ * contents on entry do not matter (every byte read is written first in the
+ * same call).  One workspace must not be used by two calls that can run at
+ * the same time.
  */
 int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes);
 
@@ -113,9 +116,10 @@ int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes)
  * long K at 8 rows), else the streaming matrix-core kernel; otherwise, up to
  * 8 rows, the broadcast kernel, then the staged one; from 9 to 64 rows the skinny
  * matrix-core kernel (K a whole number of tiles: 128 W4A16, 64 FP8, 32 BF16);
- * above 64 rows the tiled matrix-core kernel for FP8 / BF16 beyond 256 rows,
- * else the LDS matrix-core kernel (also where the others cannot take the
- * shape: x rows spanning 2 GiB or more, or a ragged K below 65 rows).  Each
+ * above 64 rows the tiled matrix-core kernel where N > 3840 (16 or more
+ * 256-column blocks), else the LDS matrix-core kernel (also where the others
+ * cannot take the shape: x rows spanning 2 GiB or more, or a ragged K below
+ * 65 rows).  Each
  * streaming kernel also needs K short enough for its shares (hundreds of
  * 16-row tiles). */
 enum wqd_path {
@@ -124,7 +128,7 @@ enum wqd_path {
     WQD_PATH_MFMA = 2,    /* bf16 matrix cores, x staged in LDS, dequant on load */
     WQD_PATH_MC = 3,      /* streaming, bf16 matrix cores, x fragments read per tile */
     WQD_PATH_SKINNY = 4,  /* bf16 matrix cores, x staged in LDS by a producer wavefront, shared by 7-14 row blocks */
-    WQD_PATH_GEMM = 5     /* bf16 matrix cores, 128 x 256 tiles of y, x staged in LDS, dequant on load */
+    WQD_PATH_GEMM = 5     /* bf16 matrix cores, 64 or 128 x 256 tiles of y, x staged in LDS, dequant on load */
 };
 
 /*
