@@ -115,7 +115,9 @@ int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes)
  * to 8 rows the skinny matrix-core kernel for long shares of K (large N, or
  * long K at 8 rows), else the streaming matrix-core kernel; otherwise, up to
  * 8 rows, the broadcast kernel, then the staged one; from 9 to 64 rows the skinny
- * matrix-core kernel (K a whole number of tiles: 128 W4A16, 64 FP8, 32 BF16);
+ * matrix-core kernel (K a whole number of tiles: 128 W4A16, 64 FP8, 32 BF16),
+ * except up to 16 rows on matrices up to 8192 x 8192 that it would split over
+ * K, which take the streaming matrix-core kernel;
  * above 64 rows the tiled matrix-core kernel where N > 3840 (16 or more
  * 256-column blocks), else the LDS matrix-core kernel (also where the others
  * cannot take the shape: x rows spanning 2 GiB or more, or a ragged K below

@@ -90,8 +90,9 @@ def test_workspace_query():
         xs = lambda M, K: (K // 128) * (-(-M // 64) * 64) * 4 if fmt == "w4a16" else 0
         assert wqd.workspace_bytes(fmt, 1024, 28672, 8192) == xs(1024, 8192)
         assert wqd.workspace_bytes(fmt, 16, 57344, 8192) == 0
-        ws = wqd.workspace_bytes(fmt, 16, 8192, 8192)
-        assert ws > 0 and ws % (16 * 8192 * 4) == 0 and ws // (16 * 8192 * 4) <= 8
+        ws = wqd.workspace_bytes(fmt, 16, 10240, 8192)
+        assert ws > 0 and ws % (16 * 10240 * 4) == 0 and ws // (16 * 10240 * 4) <= 8
+        assert wqd.workspace_bytes(fmt, 16, 8192, 8192) == 0  # streaming matrix-core kernel
         ws = wqd.workspace_bytes(fmt, 80, 8192, 8192) - xs(80, 8192)
         assert ws > 0 and ws % (80 * 8192 * 4) == 0
     L = wqd.lib()
@@ -127,10 +128,18 @@ def test_kernel_path_choice():
     assert wqd.kernel_path("bf16", 1, 16, 16416)[0] == "staged"       # 513 tiles
     assert wqd.kernel_path("w4a16", 1, 16, 65664)[0] == "staged"
     assert wqd.kernel_path("w4a16", 5, 16, 65664)[0] == "staged"
-    # 9 to 64 rows: the skinny matrix-core kernel (4 consumer wavefronts and a producer)
-    for M in (9, 16, 17, 32, 33, 64):
+    # 9 to 64 rows: the skinny matrix-core kernel (4 consumer wavefronts and a producer) ...
+    for M in (17, 32, 33, 64):
         for fmt in ("w4a16", "fp8", "bf16"):
             assert wqd.kernel_path(fmt, M, 8192, 8192) == ("skinny", 5)
+    for M in (9, 16):
+        for fmt in ("w4a16", "fp8", "bf16"):
+            assert wqd.kernel_path(fmt, M, 10240, 8192) == ("skinny", 6)  # 5 consumers of two row blocks
+            assert wqd.kernel_path(fmt, M, 8192, 28672) == ("skinny", 5)
+            # ... except up to 16 rows on matrices up to 8192 x 8192 that it would
+            # split: the streaming matrix-core kernel
+            assert wqd.kernel_path(fmt, M, 8192, 8192)[0] == "mc"
+            assert wqd.kernel_path(fmt, M, 4096, 4096)[0] == "mc"
     assert wqd.kernel_path("fp8", 16, 8192, 8208)[0] == "mfma"          # K not a whole number of 64-k tiles
     # above 64 rows with at least 16 column blocks of 256: the tiled matrix-core
     # kernel (FP8 / BF16: 4 wavefronts up to 128 rows, 8 above; W4A16: 8)
@@ -183,9 +192,10 @@ def test_qgemm_rejects_bad_arguments_before_enqueue():
     assert call(w=A + 8) == E_ALIGN
     assert call(fmt=1, K=12) == E_SHAPE
     assert wqd.workspace_bytes("w4a16", 1, 64 * 200, 128 * 64) == 0
-    need = wqd.workspace_bytes("w4a16", 16, 8192, 8192)
-    assert call(M=16, N=8192, K=8192, ws=None) == E_WS
-    assert call(M=16, N=8192, K=8192, wsb=need - 1) == E_WS
+    need = wqd.workspace_bytes("w4a16", 16, 10240, 8192)
+    assert need > 0
+    assert call(M=16, N=10240, K=8192, ws=None) == E_WS
+    assert call(M=16, N=10240, K=8192, wsb=need - 1) == E_WS
 
 
 def test_other_entry_points_reject_bad_arguments():

@@ -193,9 +193,34 @@ def test_qgemm_skinny(fmt):
         qw = oracle.quantize(fmt, W)
         pw = wqd.pack_weights(fmt, to_dev(W))
         for M in (9, 16, 17, 32, 40, 64):
-            assert wqd.kernel_path(fmt, M, N, K)[0] == "skinny"
+            # up to 16 rows, matrices up to 8192 x 8192 that it would split go to
+            # the streaming matrix-core kernel (tested below)
+            assert wqd.kernel_path(fmt, M, N, K)[0] in (("skinny", "mc") if M <= 16 else ("skinny",))
             print(f"qgemm {fmt} M={M} N={N} K={K} ws={wqd.workspace_bytes(fmt, M, N, K)}", flush=True)
             x = I.x_bf16_bits(29 * M + K, M, K)
+            y = wqd.qgemm(x_dev(x), pw)
+            torch.cuda.synchronize()
+            compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
+
+
+def mc_wide_row_shapes(fmt):
+    # (N, K) that take the streaming matrix-core kernel from 9 to 16 rows: a
+    # ragged N of 63 row blocks with long shares (16 wavefronts for BF16), 129
+    # row blocks, and 257 row blocks over the longest K it takes
+    return [(1000, 8192), (2056, 4096), (4104, 8192)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_qgemm_mc_rows_9_to_16(fmt):
+    """9 to 16 activation rows in one 16-row x block of the streaming matrix-core kernel."""
+    for N, K in mc_wide_row_shapes(fmt):
+        W = I.w_host(9000 + N + K, N, K)
+        qw = oracle.quantize(fmt, W)
+        pw = wqd.pack_weights(fmt, to_dev(W))
+        for M in (9, 12, 16):
+            assert wqd.kernel_path(fmt, M, N, K)[0] == "mc"
+            print(f"qgemm {fmt} M={M} N={N} K={K}", flush=True)
+            x = I.x_bf16_bits(41 * M + K, M, K)
             y = wqd.qgemm(x_dev(x), pw)
             torch.cuda.synchronize()
             compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
