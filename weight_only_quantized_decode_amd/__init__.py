@@ -175,10 +175,11 @@ _ws_cache = {}
 
 
 def get_workspace(nbytes: int, device=None):
-    """A zero-filled workspace of at least nbytes, cached per device (grow-only).
+    """A workspace of at least nbytes, cached per device (grow-only).
 
-    The library returns it to all-zero state after every call, so the cache can
-    be reused by consecutive calls on one stream.
+    Its contents on entry do not matter to wqd_qgemm (every byte it reads was
+    written earlier in the same call), so consecutive calls on one stream can
+    share it; calls that may run at the same time must not.
     """
     import torch
 
