@@ -151,9 +151,11 @@ int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out);
 // rows; up to 8 rows the skinny matrix-core kernel where its K shares are
 // at least 48 tiles long and unsplit (or split, at 8 rows), else the
 // streaming matrix-core kernel; the broadcast kernel again, then the staged
-// one, up to 8 rows where those cannot take the shape; the skinny kernel
-// from 9 to 64 rows; above that the tiled matrix-core kernel for FP8 / BF16
-// beyond 256 rows, else the LDS matrix-core kernel.
+// one, up to 8 rows where those cannot take the shape; from 9 to 16 rows
+// the streaming matrix-core kernel on matrices up to 8192 x 8192 that the
+// skinny kernel would split over K; the skinny kernel otherwise up to 64
+// rows; above that the tiled matrix-core kernel where N has at least
+// kGmMinNBN column blocks of 256, else the LDS matrix-core kernel.
 enum Path { kPathBcast = 0, kPathStaged = 1, kPathMfma = 2, kPathMc = 3, kPathSkinny = 4, kPathGemm = 5 };
 
 struct Choice {
