@@ -20,6 +20,10 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}"]
 # Keep the compiler from forming packed-FP32 (v_pk_*_f32) instructions.
 NO_PACKED_F32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-file flags: the tiled matrix-core kernel keeps its accumulators in VGPRs
+# (in AGPRs the compiler copied them at every loop edge, and the 4-wavefront
+# instances needed over 256 registers).
+EXTRA = {"wqd_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -31,7 +35,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, *NO_PACKED_F32, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *NO_PACKED_F32, *EXTRA.get(src, []), "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

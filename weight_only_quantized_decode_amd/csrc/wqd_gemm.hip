@@ -87,9 +87,21 @@ struct GmF {
   static constexpr int NS = FMT == kFmtFP8 ? 4 : FMT == kFmtW4 ? 2 : 3;
 };
 
+// Per (format, wavefront rows): BF16 with two wavefront rows takes 128-row
+// wavefront tiles (8 x row blocks, 256 rows per workgroup; the accumulators
+// then need the registers of a third pipeline stage and of the second
+// step's x fragments, which are read after the first step's multiplies).
+template <int FMT, int WM>
+struct GmT : GmF<FMT> {
+  static constexpr bool WIDE = FMT == kFmtBF16 && WM == 2;
+  static constexpr int MF = WIDE ? 8 : GmF<FMT>::MF;
+  static constexpr int NS = WIDE ? 2 : GmF<FMT>::NS;
+  static constexpr int NA = GmF<FMT>::W4 || WIDE ? 1 : GmF<FMT>::NQ;  // 32-k steps read before the multiplies
+};
+
 template <int FMT, int WM>
 struct GmL {
-  using F = GmF<FMT>;
+  using F = GmT<FMT, WM>;
   static constexpr int XB = F::MF * WM;                 // x row blocks per workgroup
   static constexpr int FRAGS = F::TPC * XB * F::STEPS;  // 1 KiB fragments per chunk
   static constexpr int XS = F::W4 ? 4 * XB : 0;         // uint4 of group x sums per chunk (16 rows per block)
@@ -102,7 +114,7 @@ struct GmL {
 
 template <int FMT, int WM>
 struct GmState {
-  using F = GmF<FMT>;
+  using F = GmT<FMT, WM>;
   uint4 w[F::NS][F::RB][F::TPC];         // weights of chunks c .. c + NS - 1
   uint4 xr[F::NS][GmL<FMT, WM>::XPW];    // x fragments loaded NS - 1 chunks ahead
   uint4 xsr[F::NS];                      // W4A16: x sums (lanes below XS)
@@ -120,7 +132,7 @@ struct GmState {
 // zeros).
 template <int FMT, int WM, int H>
 __device__ __forceinline__ void gm_load_w(GmState<FMT, WM>& st, const GmArgs& a, int c) {
-  using F = GmF<FMT>;
+  using F = GmT<FMT, WM>;
 #pragma unroll
   for (int b = 0; b < F::RB; ++b)
 #pragma unroll
@@ -163,7 +175,7 @@ __device__ __forceinline__ void gm_load_sz(GmState<FMT, WM>& st, int c) {
 // first one stores them).
 template <int FMT, int WM, int H>
 __device__ __forceinline__ void gm_load_x(GmState<FMT, WM>& st, const GmArgs& a, int c) {
-  using F = GmF<FMT>;
+  using F = GmT<FMT, WM>;
   using L = GmL<FMT, WM>;
   if constexpr (F::W4) {
     // K is a whole number of groups, so a chunk is either inside x or past it
@@ -205,20 +217,20 @@ __device__ __forceinline__ void gm_store_x(const GmState<FMT, WM>& st, uint4* bu
 // x fragments of the chunk in buf that this wavefront multiplies: 32-k step
 // q, x row block i (W4A16: step 0; the rest, and the x sums of rows
 // 4 kb .. 4 kb + 3 of each block, are read as they are needed).
-template <int FMT>
+template <int FMT, int WM>
 struct GmFrag {
-  static constexpr int NA = GmF<FMT>::W4 ? 1 : GmF<FMT>::NQ;  // steps read before the multiplies
-  uint4 a[NA][GmF<FMT>::MF];
-  uint4 xs[GmF<FMT>::W4 ? GmF<FMT>::MF : 1];
+  static constexpr int NA = GmT<FMT, WM>::NA;
+  uint4 a[NA][GmT<FMT, WM>::MF];
+  uint4 xs[GmF<FMT>::W4 ? GmT<FMT, WM>::MF : 1];
 };
 
 template <int FMT, int WM>
-__device__ __forceinline__ void gm_read_x(const GmState<FMT, WM>& st, const uint4* buf, GmFrag<FMT>& f) {
-  using F = GmF<FMT>;
+__device__ __forceinline__ void gm_read_x(const GmState<FMT, WM>& st, const uint4* buf, GmFrag<FMT, WM>& f) {
+  using F = GmT<FMT, WM>;
   using L = GmL<FMT, WM>;
   const uint4* xf = buf + st.lane;
 #pragma unroll
-  for (int q = 0; q < GmFrag<FMT>::NA; ++q)
+  for (int q = 0; q < GmFrag<FMT, WM>::NA; ++q)
 #pragma unroll
     for (int i = 0; i < F::MF; ++i) {
       const int t = q / F::STEPS, s = q % F::STEPS;
@@ -228,8 +240,8 @@ __device__ __forceinline__ void gm_read_x(const GmState<FMT, WM>& st, const uint
 
 // Multiply the x fragments with the weights of set H (chunk c).
 template <int FMT, int WM, int H>
-__device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, GmFrag<FMT>& f, const uint4* buf, int c) {
-  using F = GmF<FMT>;
+__device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, GmFrag<FMT, WM>& f, const uint4* buf, int c) {
+  using F = GmT<FMT, WM>;
   if constexpr (FMT == kFmtW4) {
     using L = GmL<FMT, WM>;
     const uint32_t mask = vgpr_const(0x000F000Fu), magic = vgpr_const(0x43004300u);
@@ -295,12 +307,21 @@ __device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, GmFrag<FMT>& f,
         for (int b = 0; b < F::RB; ++b) st.acc[i][b] = gm_mfma(f.a[s][i], bm[b], st.acc[i][b]);
     }
   } else {
+    using L = GmL<FMT, WM>;
 #pragma unroll
-    for (int t = 0; t < F::TPC; ++t)
+    for (int t = 0; t < F::TPC; ++t) {
+      if (t >= F::NA) {
+        // a later step's fragments replace the first step's once those are
+        // multiplied
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < F::MF; ++i) f.a[t % F::NA][i] = buf[(t * L::XB + st.wm * F::MF + i) * 64 + st.lane];
+      }
 #pragma unroll
       for (int i = 0; i < F::MF; ++i)
 #pragma unroll
-        for (int b = 0; b < F::RB; ++b) st.acc[i][b] = gm_mfma(f.a[t][i], st.w[H][b][t], st.acc[i][b]);
+        for (int b = 0; b < F::RB; ++b) st.acc[i][b] = gm_mfma(f.a[t % F::NA][i], st.w[H][b][t], st.acc[i][b]);
+    }
   }
 }
 
@@ -316,9 +337,9 @@ __device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, GmFrag<FMT>& f,
 template <int FMT, int WM, int H>
 __device__ __forceinline__ void gm_step(GmState<FMT, WM>& st, const GmArgs& a, uint4 (*s_x)[GmL<FMT, WM>::BUF],
                                         int c) {
-  constexpr int NS = GmF<FMT>::NS;
+  constexpr int NS = GmT<FMT, WM>::NS;
   constexpr int H1 = (H + 1) % NS, HL = (H + NS - 1) % NS;
-  GmFrag<FMT> f;
+  GmFrag<FMT, WM> f;
   gm_read_x<FMT, WM>(st, s_x[H], f);
   __builtin_amdgcn_sched_barrier(0);
   gm_load_sz<FMT, WM, H1>(st, c + 1);
@@ -332,7 +353,7 @@ __device__ __forceinline__ void gm_step(GmState<FMT, WM>& st, const GmArgs& a, u
 
 template <int FMT, int WM>
 __global__ __launch_bounds__(64 * WM * GmF<FMT>::WN) void gemm_kernel(GmArgs a) {
-  using F = GmF<FMT>;
+  using F = GmT<FMT, WM>;
   using L = GmL<FMT, WM>;
   constexpr int NS = F::NS;
   __shared__ uint4 s_x[NS][L::BUF];
@@ -354,7 +375,7 @@ __global__ __launch_bounds__(64 * WM * GmF<FMT>::WN) void gemm_kernel(GmArgs a) 
   const int nchp = (nch + NS - 1) / NS * NS;  // padded: chunks past the split read zero weights
   st.nch = nch;
   st.kt0 = int64_t(c0) * F::TPC;
-  st.m0 = int64_t(mb) * 64 * WM;
+  st.m0 = int64_t(mb) * 16 * F::MF * WM;
   const int64_t tiles = a.KT - st.kt0 < int64_t(nch) * F::TPC ? a.KT - st.kt0 : int64_t(nch) * F::TPC;
   st.nb0 = int64_t(nbn) * 16 + wn * F::RB;
 #pragma unroll

@@ -185,6 +185,8 @@ int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
 // blocks) and 1.42 per 128-k chunk for W4A16, and every split adds M x N
 // float32 partials written and read once at about 4 TB/s.  The cheapest S
 // from 1 to 8 (each split at least 4 chunks) wins; within 2% the smaller S.
+static constexpr double kGmWideChunkUs = 2.5;
+
 int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   PackedSizes ps;
   int st = packed_sizes(fmt, N, K, &ps);
@@ -194,15 +196,17 @@ int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   GmPlan p{};
   p.NB = ps.NB;
   p.KT = ps.KT;
-  p.wm = fmt == kFmtW4 || M <= 128 ? 1 : 2;
+  p.wm = fmt == kFmtW4 || M <= (fmt == kFmtBF16 ? 256 : 128) ? 1 : 2;
+  const bool wide = fmt == kFmtBF16 && p.wm == 2;  // 128-row wavefront tiles
+  const int64_t rows = wide ? 256 : 64 * p.wm;     // per workgroup
   p.NBN = ceil_div(p.NB, 16);
-  p.MB = ceil_div(M, 64 * p.wm);
-  p.Mp = p.MB * 64 * p.wm;
+  p.MB = ceil_div(M, rows);
+  p.Mp = p.MB * rows;
   p.nchunks = fmt == kFmtW4 ? p.KT : ceil_div(K, 64);
   if (fmt == kFmtW4 && p.KT * p.Mp * 4 >= (int64_t(1) << 31)) return kEUnsupported;
   p.xs_bytes = fmt == kFmtW4 ? (size_t(p.KT) * size_t(p.Mp) * sizeof(float) + 255) / 256 * 256 : 0;
   const int64_t tiles = p.NBN * p.MB;
-  const double t_chunk = fmt == kFmtW4 ? 1.42 : (fmt == kFmtFP8 ? 1.1 : 1.46) * (p.wm == 1 ? 0.8 : 1.0);  // us
+  const double t_chunk = fmt == kFmtW4 ? 1.42 : wide ? kGmWideChunkUs : (fmt == kFmtFP8 ? 1.1 : 1.46) * (p.wm == 1 ? 0.8 : 1.0);  // us
   const double part_us = double(M) * double(N) * 8.0 / 4.0e6;  // one split's partials, us
   const int64_t max_s = p.nchunks / 4 < 1 ? 1 : (p.nchunks / 4 > 8 ? 8 : p.nchunks / 4);
   double best = 0.0;
