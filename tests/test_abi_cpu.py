@@ -142,13 +142,13 @@ def test_kernel_path_choice():
             assert wqd.kernel_path(fmt, M, 4096, 4096)[0] == "mc"
     assert wqd.kernel_path("fp8", 16, 8192, 8208)[0] == "mfma"          # K not a whole number of 64-k tiles
     # above 64 rows with at least 16 column blocks of 256: the tiled matrix-core
-    # kernel (FP8: 4 wavefronts up to 128 rows, 8 above; BF16: 4 up to 256
-    # rows, then 8 of 128-row tiles; W4A16: 8)
+    # kernel (FP8 / BF16: 4 wavefronts up to 256 rows, then 8 of 128-row
+    # tiles; W4A16: 8)
     assert wqd.kernel_path("bf16", 65, 8192, 8192) == ("gemm", 4)
     assert wqd.kernel_path("fp8", 128, 4096, 8192) == ("gemm", 4)
-    assert wqd.kernel_path("fp8", 129, 8192, 8192) == ("gemm", 8)
-    assert wqd.kernel_path("bf16", 256, 8192, 8192) == ("gemm", 4)
-    assert wqd.kernel_path("bf16", 257, 8192, 8192) == ("gemm", 8)
+    for fmt in ("fp8", "bf16"):
+        assert wqd.kernel_path(fmt, 256, 8192, 8192) == ("gemm", 4)
+        assert wqd.kernel_path(fmt, 257, 8192, 8192) == ("gemm", 8)
     assert wqd.kernel_path("fp8", 1024, 28672, 8192) == ("gemm", 8)
     for M in (65, 1024):
         assert wqd.kernel_path("w4a16", M, 8192, 8192) == ("gemm", 8)

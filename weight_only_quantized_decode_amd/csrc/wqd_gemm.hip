@@ -87,13 +87,14 @@ struct GmF {
   static constexpr int NS = FMT == kFmtFP8 ? 4 : FMT == kFmtW4 ? 2 : 3;
 };
 
-// Per (format, wavefront rows): BF16 with two wavefront rows takes 128-row
-// wavefront tiles (8 x row blocks, 256 rows per workgroup; the accumulators
-// then need the registers of a third pipeline stage and of the second
-// step's x fragments, which are read after the first step's multiplies).
+// Per (format, wavefront rows): BF16 and FP8 with two wavefront rows take
+// 128-row wavefront tiles (8 x row blocks, 256 rows per workgroup; the
+// accumulators then need the registers of further pipeline stages and of the
+// second step's x fragments, which are read after the first step's
+// multiplies).
 template <int FMT, int WM>
 struct GmT : GmF<FMT> {
-  static constexpr bool WIDE = FMT == kFmtBF16 && WM == 2;
+  static constexpr bool WIDE = (FMT == kFmtBF16 || FMT == kFmtFP8) && WM == 2;
   static constexpr int MF = WIDE ? 8 : GmF<FMT>::MF;
   static constexpr int NS = WIDE ? 2 : GmF<FMT>::NS;
   static constexpr int NA = GmF<FMT>::W4 || WIDE ? 1 : GmF<FMT>::NQ;  // 32-k steps read before the multiplies
@@ -289,8 +290,14 @@ __device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, GmFrag<FMT, WM>
       }
     }
   } else if constexpr (FMT == kFmtFP8) {
+    using L = GmL<FMT, WM>;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      if (s >= F::NA) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < F::MF; ++i) f.a[s % F::NA][i] = buf[((st.wm * F::MF + i) * F::STEPS + s) * 64 + st.lane];
+      }
       uint4 bm[F::RB];
 #pragma unroll
       for (int b = 0; b < F::RB; ++b) {
@@ -304,7 +311,7 @@ __device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, GmFrag<FMT, WM>
 #pragma unroll
       for (int i = 0; i < F::MF; ++i)
 #pragma unroll
-        for (int b = 0; b < F::RB; ++b) st.acc[i][b] = gm_mfma(f.a[s][i], bm[b], st.acc[i][b]);
+        for (int b = 0; b < F::RB; ++b) st.acc[i][b] = gm_mfma(f.a[s % F::NA][i], bm[b], st.acc[i][b]);
     }
   } else {
     using L = GmL<FMT, WM>;

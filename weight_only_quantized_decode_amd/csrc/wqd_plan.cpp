@@ -177,16 +177,15 @@ int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
 
 // Tiled kernel (above kGmMinM rows, where it measured faster than the LDS
 // matrix-core kernel on the 70B verify shapes once N gives at least kGmMinNBN
-// column blocks): BF16 / FP8 64-row blocks up to 128 rows, 128-row blocks
-// above; W4A16 64-row blocks.  The K split comes from a time model fitted to
-// the kernel on those shapes: with one workgroup per compute unit, the launch
-// runs ceil(W / 256) rounds of cps chunks each (W = tiles x splits), about
-// 1.46 us per 64-k chunk for BF16, 1.1 for FP8 (0.8 of that with 64-row
-// blocks) and 1.42 per 128-k chunk for W4A16, and every split adds M x N
-// float32 partials written and read once at about 4 TB/s.  The cheapest S
-// from 1 to 8 (each split at least 4 chunks) wins; within 2% the smaller S.
-static constexpr double kGmWideChunkUs = 2.5;
-
+// column blocks): 64-row blocks (4 wavefronts for BF16 / FP8, 8 for W4A16) up
+// to 256 rows and for W4A16 throughout, 256-row blocks of 8 wavefronts above.
+// The K split comes from a time model fitted to the kernel on those shapes:
+// with one workgroup per compute unit, the launch runs ceil(W / 256) rounds of
+// cps chunks each (W = tiles x splits); a 64-k chunk costs 1.17 us for BF16
+// and 0.88 for FP8 with 64-row blocks, 2.5 and 1.83 with 256-row blocks, a
+// 128-k W4A16 chunk 1.42; every split adds M x N float32 partials written and
+// read once at about 4 TB/s.  The cheapest S from 1 to 8 (each split at least
+// 4 chunks) wins; within 2% the smaller S.
 int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   PackedSizes ps;
   int st = packed_sizes(fmt, N, K, &ps);
@@ -196,8 +195,8 @@ int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   GmPlan p{};
   p.NB = ps.NB;
   p.KT = ps.KT;
-  p.wm = fmt == kFmtW4 || M <= (fmt == kFmtBF16 ? 256 : 128) ? 1 : 2;
-  const bool wide = fmt == kFmtBF16 && p.wm == 2;  // 128-row wavefront tiles
+  p.wm = fmt == kFmtW4 || M <= 256 ? 1 : 2;
+  const bool wide = p.wm == 2;  // 128-row wavefront tiles
   const int64_t rows = wide ? 256 : 64 * p.wm;     // per workgroup
   p.NBN = ceil_div(p.NB, 16);
   p.MB = ceil_div(M, rows);
@@ -206,7 +205,7 @@ int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   if (fmt == kFmtW4 && p.KT * p.Mp * 4 >= (int64_t(1) << 31)) return kEUnsupported;
   p.xs_bytes = fmt == kFmtW4 ? (size_t(p.KT) * size_t(p.Mp) * sizeof(float) + 255) / 256 * 256 : 0;
   const int64_t tiles = p.NBN * p.MB;
-  const double t_chunk = fmt == kFmtW4 ? 1.42 : wide ? kGmWideChunkUs : (fmt == kFmtFP8 ? 1.1 : 1.46) * (p.wm == 1 ? 0.8 : 1.0);  // us
+  const double t_chunk = fmt == kFmtW4 ? 1.42 : wide ? (fmt == kFmtFP8 ? 1.83 : 2.5) : (fmt == kFmtFP8 ? 0.88 : 1.17);  // us
   const double part_us = double(M) * double(N) * 8.0 / 4.0e6;  // one split's partials, us
   const int64_t max_s = p.nchunks / 4 < 1 ? 1 : (p.nchunks / 4 > 8 ? 8 : p.nchunks / 4);
   double best = 0.0;
