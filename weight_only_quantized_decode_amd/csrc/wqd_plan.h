@@ -111,9 +111,9 @@ constexpr int kSkCfg[kSkCfgCount][2] = {{7, 2}, {7, 1}, {4, 2}, {5, 2}};
 int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out);
 
 // Tiled matrix-core kernel (more than kGmMinM rows and at least kGmMinNBN
-// column blocks): a workgroup of 8 wavefronts (BF16 / FP8 above 128 rows:
-// wm = 2, 8 wavefronts of 64 x 64; otherwise wm = 1: BF16 / FP8 4 of 64 x 64,
-// W4A16 8 of 64 x 32) computes a (64 wm) x 256 tile of y; NBN column blocks x
+// column blocks): wm = 1, a 64 x 256 tile of y (BF16 / FP8 up to 256 rows: 4
+// wavefronts of 64 x 64; W4A16: 8 of 64 x 32), or wm = 2 for BF16 / FP8 above
+// 256 rows, a 256 x 256 tile (8 wavefronts of 128 x 64); NBN column blocks x
 // MB row blocks of workgroups (XCD-aware order), K in chunks (64; W4A16 128)
 // split S ways (cps chunks per split) as a time model of the kernel picks.
 // Workspace: W4A16 x sums, float32 [KT][Mp] (Mp = 64 MB rows), xs_bytes
