@@ -159,6 +159,27 @@ int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
   if (K % tile_k(fmt) != 0) return kEUnsupported;
   if (ps.s_bytes >= (size_t(1) << 31) || ps.z_bytes >= (size_t(1) << 31)) return kEUnsupported;
   SkPlan p{};
+  if (fmt == kFmtW4 && M > 16 && ps.KT >= 128) {
+    // W4A16 from 17 rows on long K: the dequantisation and group corrections
+    // make the kernel compute-heavy and more resident wavefronts pay
+    // (measured on 8192 x 28672 at 17-64 rows, 17-27% faster than the
+    // choice below): two x row blocks take 4 consumers with twice the
+    // splits (two workgroups per compute unit), three or four take 7
+    // consumers of two row blocks (one workgroup per compute unit).
+    if (ceil_div(M, 16) == 2) {
+      const int64_t groups = ceil_div(ps.NB, int64_t(8));
+      int64_t S = 2 * kComputeUnits / groups;
+      const int64_t max_s = ps.KT / 16;
+      S = S > 8 ? 8 : S;
+      S = S > max_s ? max_s : S;
+      plan_skinny_with(fmt, M, ps, 4, 2, S < 1 ? 1 : S, &p);
+    } else {
+      plan_skinny_with(fmt, M, ps, 7, 2, 0, &p);
+    }
+    p.ws_bytes = p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;
+    *out = p;
+    return kOK;
+  }
   double best = -1.0;
   for (const auto& cfg : kSkCfg) {
     SkPlan q;
