@@ -20,19 +20,24 @@
 //     definition of the dequantised weight, s (q - z): a chunk is one 128-k
 //     group, its product P = sum x (128 + q) is formed in fresh accumulators,
 //     and acc += s (P - (128 + z) X) with X the group's x sum, which a small
-//     first kernel writes to the workspace ([group][row], float32) and the
-//     kernel stages with the x tile;
-//   * K advances in chunks (64 k; W4A16 128) through an NS-stage pipeline (3
-//     for BF16, 4 for FP8, whose weights take half the registers, 2 for
-//     W4A16, whose chunks are twice as long):
-//     while chunk c is multiplied, the weights (and W4A16 scales, zero points
-//     and x sums) and x of chunks up to c + NS - 1 are in flight and the x of
-//     chunk c + 1 is written into its LDS buffer (one barrier per chunk).  The
-//     loop body is NS chunks, so every index is a compile-time constant.  x
-//     sits in LDS in fragment order: fragment (tile, x row block i, K-step s)
-//     is 1 KiB, lane 16 kb + j holding the 8 k of row 16 i + j that pair with
-//     slice kb of the weights; reads are conflict-free 16-byte LDS reads, all
-//     of a chunk's issued before its first multiply;
+//     first kernel writes to the workspace ([group][row], float32);
+//   * x goes from memory straight into LDS (16-byte loads that write LDS
+//     instead of registers), in fragment order: fragment (tile, x row block
+//     i, K-step s) is 1 KiB, lane 16 kb + j holding the 8 k of row 16 i + j
+//     that pair with slice kb of the weights, which is exactly the lane order
+//     in which one such load writes LDS; reads are conflict-free 16-byte LDS
+//     reads.  W4A16 scales, zero words and x sums take the same way into a
+//     slot of each wavefront, so no register carries them across a chunk;
+//   * K advances in chunks (64 k; W4A16 128) through an NS-stage pipeline: one
+//     LDS buffer per stage, and while chunk c is multiplied the loads of
+//     chunks up to c + NS - 1 are in flight.  Each step ends with an explicit
+//     wait for this wavefront's x of chunk c + 1 (loads complete in issue
+//     order, so the count of later loads is exact) and a bare barrier; a
+//     barrier with a memory fence would make the compiler wait for every
+//     pending load into LDS, including those of chunks c + 2 ...  Each stage
+//     buffer is its own LDS array, which lets the compiler see that reading
+//     one does not wait for loads into another.  The loop body is NS chunks,
+//     so every index is a compile-time constant;
 //   * weights are read with the default cache policy: every x row block of a
 //     column block re-reads them, and XCD-aware order keeps them in one L2:
 //     consecutive workgroups of one XCD (dispatch is round-robin over the 8
@@ -81,17 +86,15 @@ struct GmF {
   static constexpr int MF = 4;                                                 // x row blocks per wavefront
   static constexpr int RB = W4 ? 2 : 4;                                        // weight row blocks per wavefront
   static constexpr int WN = 16 / RB;                                           // wavefronts along N
-  // pipeline stages: FP8 weights take half the registers of BF16, so one
-  // more fits; W4A16 chunks are twice as long and its group partials need
-  // the registers, so one fewer
-  static constexpr int NS = FMT == kFmtFP8 ? 4 : FMT == kFmtW4 ? 2 : 3;
+  // pipeline stages (measured: the kernel is bound by its multiply, dequant
+  // and LDS issue, so one more stage changes the time by a few percent)
+  static constexpr int NS = FMT == kFmtFP8 ? 4 : 3;
 };
 
 // Per (format, wavefront rows): BF16 and FP8 with two wavefront rows take
-// 128-row wavefront tiles (8 x row blocks, 256 rows per workgroup; the
-// accumulators then need the registers of further pipeline stages and of the
-// second step's x fragments, which are read after the first step's
-// multiplies).
+// 128-row wavefront tiles (8 x row blocks, 256 rows per workgroup; two
+// pipeline stages, as the accumulators take the registers of the others; the
+// second step's x fragments are read after the first step's multiplies).
 template <int FMT, int WM>
 struct GmT : GmF<FMT> {
   static constexpr bool WIDE = (FMT == kFmtBF16 || FMT == kFmtFP8) && WM == 2;
@@ -105,29 +108,36 @@ struct GmL {
   using F = GmT<FMT, WM>;
   static constexpr int XB = F::MF * WM;                 // x row blocks per workgroup
   static constexpr int FRAGS = F::TPC * XB * F::STEPS;  // 1 KiB fragments per chunk
-  static constexpr int XS = F::W4 ? 4 * XB : 0;         // uint4 of group x sums per chunk (16 rows per block)
-  static constexpr int BUF = FRAGS * 64 + XS;           // uint4 per LDS buffer
   static constexpr int NW = WM * F::WN;                 // wavefronts per workgroup
   static constexpr int XPW = FRAGS / NW;                // fragments each wavefront stages
+  // W4A16: each wavefront's slot after the fragments, 1 KiB per load (lanes
+  // out of range may write zeros where their bytes would go): the group's x
+  // sums of the workgroup's rows, the 128-byte scale quads of the wavefront's
+  // row blocks, their 32-byte zero words
+  static constexpr int SLOT = 192, SL_XS = 0, SL_S = 64, SL_Z = 128;  // uint4
+  static constexpr int BUF = FRAGS * 64 + (F::W4 ? NW * SLOT : 0);  // uint4 per LDS buffer
   static_assert(XPW * NW == FRAGS, "whole fragments per wavefront");
-  static_assert(XS <= 64, "one wavefront stages the x sums");
+  static_assert(!F::W4 || (4 * XB <= 64 && 8 * F::RB <= 64), "one load holds the x sums and the scale quads");
 };
 
 template <int FMT, int WM>
 struct GmState {
   using F = GmT<FMT, WM>;
-  uint4 w[F::NS][F::RB][F::TPC];         // weights of chunks c .. c + NS - 1
-  uint4 xr[F::NS][GmL<FMT, WM>::XPW];    // x fragments loaded NS - 1 chunks ahead
-  uint4 xsr[F::NS];                      // W4A16: x sums (lanes below XS)
-  uint32_t sc16[F::NS][F::RB];           // W4A16: fp16 scale bits of this lane's column
-  uint32_t zq16[F::NS][F::RB];           // W4A16: the 4 zero nibbles of its scale quad
+  uint4 w[F::NS][F::RB][F::TPC];  // weights of chunks c .. c + NS - 1
   gm_f32x4_t acc[F::MF][F::RB];
-  __amdgpu_buffer_rsrc_t wres[F::RB], xres, sres[F::W4 ? F::RB : 1], zres[F::W4 ? F::RB : 1], xsres;
+  __amdgpu_buffer_rsrc_t wres[F::RB], xres, sres, zres, xsres;
   uint32_t xvo[GmL<FMT, WM>::XPW];  // W4A16: this lane's x byte offsets (chunk 0 of the matrix)
   uint32_t xsvo;                    // W4A16: this lane's x-sum byte offset (group 0)
+  uint32_t svo, zvo;                // W4A16: this lane's scale / zero-word byte offsets (quad 0)
   int64_t kt0, m0, nb0;
-  int lane, wave, wm, nch;
+  int lane, wave, wm;
 };
+
+// 16 bytes per lane from r into LDS: lane i's bytes land at dst + 16 i.
+template <int FMT, int WM>
+__device__ __forceinline__ void gm_dma(__amdgpu_buffer_rsrc_t r, uint4* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
 
 // Weights of chunk c of the split into set H (chunks past the split read
 // zeros).
@@ -147,49 +157,37 @@ __device__ __forceinline__ void gm_load_w(GmState<FMT, WM>& st, const GmArgs& a,
     }
 }
 
-// W4A16: scales and zero words of chunk c (one group) into set H, requested
-// one chunk ahead (before that chunk's x and weights, so waiting for them
-// does not wait for those): the row block's scales [quad][row][4] and zero
-// words [quad][row], the lane's row in the vector offset, the group in the
-// scalar one (past the split: beyond the resource, so 0).
-template <int FMT, int WM, int H>
-__device__ __forceinline__ void gm_load_sz(GmState<FMT, WM>& st, int c) {
+// W4A16: the scale quads ([quad][row][4] fp16, 128 bytes per row block) and
+// zero words ([quad][row], 32 bytes) holding chunk c's group, for this
+// wavefront's row blocks, into its slot of buf; the quad goes in the scalar
+// offset.  Chunks past the split are multiplied with scale 0 whatever lands.
+template <int FMT, int WM>
+__device__ __forceinline__ void gm_load_sz(GmState<FMT, WM>& st, int c, uint4* buf) {
   if constexpr (GmF<FMT>::W4) {
-    const int g = int(st.kt0) + c;
-    const bool ok = c < st.nch;
-    const uint32_t so = ok ? uint32_t(((g / kScaleQuad) * kTileRows * kScaleQuad + g % kScaleQuad) * 2) : 0x40000000u;
-    const uint32_t zo = ok ? uint32_t((g / kScaleQuad) * kTileRows * 2) : 0x40000000u;
-    const int n = st.lane & 15;
-#pragma unroll
-    for (int b = 0; b < GmF<FMT>::RB; ++b) {
-      // kept apart until the group is multiplied: combining them here would
-      // wait for the loads
-      st.sc16[H][b] = __builtin_amdgcn_raw_buffer_load_b16(st.sres[b], n * kScaleQuad * 2, so, 0);
-      st.zq16[H][b] = __builtin_amdgcn_raw_buffer_load_b16(st.zres[b], n * 2, zo, 0);
-    }
+    using L = GmL<FMT, WM>;
+    static_assert(kScaleQuad == 4, "four groups per scale quad");
+    const uint32_t q = (uint32_t(st.kt0) + uint32_t(c)) >> 2;
+    uint4* slot = buf + L::FRAGS * 64 + st.wave * L::SLOT;
+    gm_dma<FMT, WM>(st.sres, slot + L::SL_S, st.svo, q * (kTileRows * kScaleQuad * 2));
+    gm_dma<FMT, WM>(st.zres, slot + L::SL_Z, st.zvo, q * (kTileRows * 2));
   }
 }
 
-// x fragments this wavefront stages for chunk c into set H: fragment
-// f = wave * XPW + u of (tile t, x row block i, step s) order; W4A16: the
-// group's x sums of the workgroup's rows too (each wavefront loads them, the
-// first one stores them).
-template <int FMT, int WM, int H>
-__device__ __forceinline__ void gm_load_x(GmState<FMT, WM>& st, const GmArgs& a, int c) {
+// x of chunk c into buf: this wavefront's fragments f = wave * XPW + u of
+// (tile t, x row block i, step s) order (rows past M and k past K are out of
+// range of the resource); W4A16: first the group's x sums into its slot.
+template <int FMT, int WM>
+__device__ __forceinline__ void gm_load_x(GmState<FMT, WM>& st, const GmArgs& a, int c, uint4* buf) {
   using F = GmT<FMT, WM>;
   using L = GmL<FMT, WM>;
   if constexpr (F::W4) {
     // K is a whole number of groups, so a chunk is either inside x or past it
     const int64_t g = st.kt0 + c;
     const uint32_t so = g < a.KT ? uint32_t(g * kGroup * 2) : 0x7FFFFFF0u;
-#pragma unroll
-    for (int u = 0; u < L::XPW; ++u) {
-      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(st.xres, st.xvo[u], so, 0);
-      st.xr[H][u] = make_uint4(v.x, v.y, v.z, v.w);
-    }
     const uint32_t sso = g < a.KT ? uint32_t(g * a.Mp * 4) : 0x7FFFFFF0u;
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(st.xsres, st.xsvo, sso, 0);
-    st.xsr[H] = make_uint4(v.x, v.y, v.z, v.w);
+    gm_dma<FMT, WM>(st.xsres, buf + L::FRAGS * 64 + st.wave * L::SLOT + L::SL_XS, st.xsvo, sso);
+#pragma unroll
+    for (int u = 0; u < L::XPW; ++u) gm_dma<FMT, WM>(st.xres, buf + (st.wave * L::XPW + u) * 64, st.xvo[u], so);
     return;
   }
   const int kb = st.lane >> 4, j = st.lane & 15;
@@ -200,19 +198,46 @@ __device__ __forceinline__ void gm_load_x(GmState<FMT, WM>& st, const GmArgs& a,
     const int64_t row = st.m0 + 16 * i + j;
     const int64_t k = (st.kt0 + int64_t(c) * F::TPC + t) * F::TK + kb * F::SLK + 8 * s;
     const uint32_t off = row < a.M && k < a.K ? uint32_t((row * a.K + k) * 2) : 0x80000000u;
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(st.xres, off, 0, 0);
-    st.xr[H][u] = make_uint4(v.x, v.y, v.z, v.w);
+    gm_dma<FMT, WM>(st.xres, buf + f * 64, off, 0);
   }
 }
 
+// All loads of chunk c, in a fixed order that the wait below counts on: W4A16
+// scale quads, zero words and x sums, then x, then weights.
 template <int FMT, int WM, int H>
-__device__ __forceinline__ void gm_store_x(const GmState<FMT, WM>& st, uint4* buf) {
+__device__ __forceinline__ void gm_load_group(GmState<FMT, WM>& st, const GmArgs& a, int c, uint4* buf) {
+  gm_load_sz<FMT, WM>(st, c, buf);
+  gm_load_x<FMT, WM>(st, a, c, buf);
+  __builtin_amdgcn_sched_barrier(0);
+  gm_load_w<FMT, WM, H>(st, a, c);
+}
+
+// End of a step that requested nothing: wait for everything in flight.
+__device__ __forceinline__ void gm_wait_all() {
+  __builtin_amdgcn_s_waitcnt(0x7 << 4);  // vmcnt(0) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// End of a step: wait until this wavefront's loads into LDS for chunk c + 1
+// (requested NS - 2 steps ago) have landed and its LDS reads of chunk c are
+// done, then meet the other wavefronts.  Loads complete in issue order; after
+// chunk c + 1's x this wavefront has issued that chunk's weights and, in each
+// later step, a whole group (W4A16 scale quads, zero words and x sums, then
+// x, then weights).  The barrier carries no memory fence: with one the
+// compiler would also wait for the loads of chunks c + 2 ... into LDS.
+template <int FMT, int WM>
+__device__ __forceinline__ void gm_wait_step() {
+  using F = GmT<FMT, WM>;
   using L = GmL<FMT, WM>;
-#pragma unroll
-  for (int u = 0; u < L::XPW; ++u) buf[(st.wave * L::XPW + u) * 64 + st.lane] = st.xr[H][u];
-  if constexpr (GmF<FMT>::W4) {
-    if (st.wave == 0 && st.lane < L::XS) buf[L::FRAGS * 64 + st.lane] = st.xsr[H];
-  }
+  constexpr int RBT = F::RB * F::TPC, SZ = F::W4 ? 3 : 0;
+  constexpr int N = RBT + (F::NS - 2) * (SZ + L::XPW + RBT);
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));  // vmcnt(N) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // x fragments of the chunk in buf that this wavefront multiplies: 32-k step
@@ -270,18 +295,35 @@ __device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, GmFrag<FMT, WM>
         for (int b = 0; b < F::RB; ++b)
           P[i][b] = gm_mfma(f.a[0][i], bm[b], s == 0 ? gm_f32x4_t{0.f, 0.f, 0.f, 0.f} : P[i][b]);
     }
-    // acc += s (P - (128 + z) X): the group's zero point is nibble g % 4 of
-    // the quad's zero word; the x sums are read only now (held through the
-    // multiplies they would not leave room for the accumulators)
+    // acc += s (P - (128 + z) X): the group is entry g % 4 of the scale quad
+    // and nibble g % 4 of the zero word; the x sums are read only now (held
+    // through the multiplies they would not leave room for the accumulators)
     __builtin_amdgcn_sched_barrier(0);
     const int kb = st.lane >> 4;
 #pragma unroll
-    for (int i = 0; i < F::MF; ++i) f.xs[i] = buf[L::FRAGS * 64 + (st.wm * F::MF + i) * 4 + kb];
-    const int zsh = 4 * int((st.kt0 + c) % kScaleQuad);
+    for (int i = 0; i < F::MF; ++i) f.xs[i] = buf[L::FRAGS * 64 + st.wave * L::SLOT + L::SL_XS + (st.wm * F::MF + i) * 4 + kb];
+    const int zsh = 4 * int((uint32_t(st.kt0) + uint32_t(c)) & 3u);
+    // this lane's row n in each row block: its 4 scales (8 bytes) and its
+    // zero word (half of a dword), read one at a time: the compiler merges
+    // adjacent reads into one that no longer shows which LDS array it reads,
+    // and then waits for every load into LDS in flight
+    const int n = st.lane & 15;
+    uint2 sqv[F::RB];
+    uint32_t zwv[F::RB];
 #pragma unroll
     for (int b = 0; b < F::RB; ++b) {
-      const float sc = __half2float(__ushort_as_half(uint16_t(st.sc16[H][b])));
-      const float zc = 128.0f + float((st.zq16[H][b] >> zsh) & 0xFu);
+      sqv[b] = reinterpret_cast<const uint2*>(buf + L::FRAGS * 64 + st.wave * L::SLOT + L::SL_S)[b * 16 + n];
+      __builtin_amdgcn_sched_barrier(0);
+      zwv[b] = reinterpret_cast<const uint32_t*>(buf + L::FRAGS * 64 + st.wave * L::SLOT + L::SL_Z)[b * 8 + (n >> 1)];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int b = 0; b < F::RB; ++b) {
+      const uint2 sq = sqv[b];
+      const uint32_t zw = zwv[b];
+      const uint32_t sw = ((zsh & 8) ? sq.y : sq.x) >> (4 * (zsh & 4));
+      const float sc = __half2float(__ushort_as_half(uint16_t(sw & 0xFFFFu)));
+      const float zc = 128.0f + float(((zw >> (16 * (n & 1))) >> zsh) & 0xFu);
 #pragma unroll
       for (int i = 0; i < F::MF; ++i) {
         const gm_f32x4_t X = __builtin_bit_cast(gm_f32x4_t, f.xs[i]);
@@ -333,29 +375,32 @@ __device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, GmFrag<FMT, WM>
 }
 
 // Step for chunk c = NS it + H: read this wavefront's x fragments of chunk c
-// from LDS, request chunk c + NS - 1 (x first: its wait comes first; the LDS
-// reads land meanwhile), multiply chunk c, write the x of chunk c + 1 (loaded
-// NS - 2 chunks ago) into its LDS buffer (that of chunk c + 1 - NS, released
-// by the last barrier).  Loads and stores are unconditional: chunks past the
+// from LDS, request chunk c + NS - 1 into the buffer of chunk c - 1 (released
+// by the last barrier; the LDS reads land meanwhile), multiply chunk c, wait
+// for chunk c + 1.  Every step issues the same loads in the same order, as
+// the prologue does for its chunks, so the compiler's count of loads in
+// flight is exact at every wait.  Loads are unconditional: chunks past the
 // split read zero weights (out of range of the weight resources), so no
 // register of the ring is ever a merge of an old and a new value, which
 // would make the compiler copy it (and wait for its load) at the loop's back
-// edge.
-template <int FMT, int WM, int H>
-__device__ __forceinline__ void gm_step(GmState<FMT, WM>& st, const GmArgs& a, uint4 (*s_x)[GmL<FMT, WM>::BUF],
-                                        int c) {
+// edge.  The steps after the loop (TAIL) request nothing: the compiler would
+// drop their weight loads, whose values are never used, and the count of
+// loads that the wait relies on would be wrong.
+template <int FMT, int WM, int H, bool TAIL = false>
+__device__ __forceinline__ void gm_step(GmState<FMT, WM>& st, const GmArgs& a, uint4* const* s_x, int c) {
   constexpr int NS = GmT<FMT, WM>::NS;
-  constexpr int H1 = (H + 1) % NS, HL = (H + NS - 1) % NS;
+  constexpr int HL = (H + NS - 1) % NS;
   GmFrag<FMT, WM> f;
   gm_read_x<FMT, WM>(st, s_x[H], f);
   __builtin_amdgcn_sched_barrier(0);
-  gm_load_sz<FMT, WM, H1>(st, c + 1);
-  gm_load_x<FMT, WM, HL>(st, a, c + NS - 1);
-  gm_load_w<FMT, WM, HL>(st, a, c + NS - 1);
+  if constexpr (!TAIL) gm_load_group<FMT, WM, HL>(st, a, c + NS - 1, s_x[HL]);
   __builtin_amdgcn_sched_barrier(0);
   gm_compute<FMT, WM, H>(st, f, s_x[H], c);
-  gm_store_x<FMT, WM, H1>(st, s_x[H1]);
-  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (TAIL)
+    gm_wait_all();
+  else
+    gm_wait_step<FMT, WM>();
 }
 
 template <int FMT, int WM>
@@ -363,7 +408,9 @@ __global__ __launch_bounds__(64 * WM * GmF<FMT>::WN) void gemm_kernel(GmArgs a) 
   using F = GmT<FMT, WM>;
   using L = GmL<FMT, WM>;
   constexpr int NS = F::NS;
-  __shared__ uint4 s_x[NS][L::BUF];
+  // one LDS array per pipeline stage (see gm_wait_step)
+  __shared__ uint4 s_x0[L::BUF], s_x1[L::BUF], s_x2[NS > 2 ? L::BUF : 1], s_x3[NS > 3 ? L::BUF : 1];
+  uint4* const s_x[4] = {s_x0, s_x1, s_x2, s_x3};
 
   // XCD-aware order: the workgroups of one XCD sweep the row blocks of x of
   // one column block back to back
@@ -379,8 +426,6 @@ __global__ __launch_bounds__(64 * WM * GmF<FMT>::WN) void gemm_kernel(GmArgs a) 
   const int split = blockIdx.y;
   const int c0 = split * a.cps;
   const int nch = a.nchunks - c0 < a.cps ? a.nchunks - c0 : a.cps;  // >= 1: the planner sizes S so
-  const int nchp = (nch + NS - 1) / NS * NS;  // padded: chunks past the split read zero weights
-  st.nch = nch;
   st.kt0 = int64_t(c0) * F::TPC;
   st.m0 = int64_t(mb) * 16 * F::MF * WM;
   const int64_t tiles = a.KT - st.kt0 < int64_t(nch) * F::TPC ? a.KT - st.kt0 : int64_t(nch) * F::TPC;
@@ -398,15 +443,16 @@ __global__ __launch_bounds__(64 * WM * GmF<FMT>::WN) void gemm_kernel(GmArgs a) 
   st.xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, 0x7FFFFFF0, 0x00020000);
   if constexpr (F::W4) {
     const int64_t qb = a.G4 * kTileRows;  // (scale quad, row) entries per row block
-#pragma unroll
-    for (int b = 0; b < F::RB; ++b) {
-      const bool live = st.nb0 + b < a.NB;
-      const int64_t nb = live ? st.nb0 + b : 0;
-      st.sres[b] = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.scales) + nb * qb * kScaleQuad), 0,
-          live ? uint32_t(qb * kScaleQuad * 2) : 0u, 0x00020000);
-      st.zres[b] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.zeros + nb * qb), 0,
-                                                     live ? uint32_t(qb * 2) : 0u, 0x00020000);
+    // lanes 0-15: the 128-byte scale quads of this wavefront's two row
+    // blocks (8 lanes each); lanes 0-3: their 32-byte zero words (2 each);
+    // row blocks past the matrix are out of range
+    st.sres = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.scales), 0, uint32_t(a.NB * qb * kScaleQuad * 2),
+                                                0x00020000);
+    st.zres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.zeros), 0, uint32_t(a.NB * qb * 2), 0x00020000);
+    {
+      const int64_t nbs = st.nb0 + (st.lane >> 3), nbz = st.nb0 + (st.lane >> 1);
+      st.svo = st.lane < 8 * F::RB && nbs < a.NB ? uint32_t(nbs * qb * kScaleQuad * 2 + (st.lane & 7) * 16) : 0x7FFFFFF0u;
+      st.zvo = st.lane < 2 * F::RB && nbz < a.NB ? uint32_t(nbz * qb * 2 + (st.lane & 1) * 16) : 0x7FFFFFF0u;
     }
     st.xsres = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.xsum), 0, uint32_t(a.KT * a.Mp * 4), 0x00020000);
     const int kb = st.lane >> 4, j = st.lane & 15;
@@ -418,28 +464,38 @@ __global__ __launch_bounds__(64 * WM * GmF<FMT>::WN) void gemm_kernel(GmArgs a) 
       const int64_t row = st.m0 + 16 * i + j;
       st.xvo[u] = row < a.M ? uint32_t((row * a.K + int64_t(kb) * F::SLK + 8 * sx) * 2) : 0x7FFFFFF0u;
     }
-    st.xsvo = st.lane < L::XS ? uint32_t((st.m0 + 4 * st.lane) * 4) : 0x7FFFFFF0u;
+    st.xsvo = st.lane < 4 * L::XB ? uint32_t((st.m0 + 4 * st.lane) * 4) : 0x7FFFFFF0u;
   }
 
-  // prologue: chunks 0 .. NS - 2 requested, chunk 0 staged
-  gm_load_sz<FMT, WM, 0>(st, 0);
-  gm_load_x<FMT, WM, 0>(st, a, 0);
-  gm_load_w<FMT, WM, 0>(st, a, 0);
-  if constexpr (NS > 2) {
-    gm_load_x<FMT, WM, 1>(st, a, 1);
-    gm_load_w<FMT, WM, 1>(st, a, 1);
+  // prologue: chunks 0 .. NS - 2 requested, chunk 0 in LDS
+  {
+    // the buffers start as zeros: lanes out of range of their resource may
+    // leave their LDS bytes unwritten (those bytes then only ever hold zeros
+    // or earlier values of the same rows, never NaN)
+#pragma unroll
+    for (int h = 0; h < NS; ++h)
+      for (int i = threadIdx.x; i < L::BUF; i += 64 * L::NW) s_x[h][i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
   }
-  if constexpr (NS > 3) {
-    gm_load_x<FMT, WM, 2>(st, a, 2);
-    gm_load_w<FMT, WM, 2>(st, a, 2);
-  }
-  gm_store_x<FMT, WM, 0>(st, s_x[0]);
+  gm_load_group<FMT, WM, 0>(st, a, 0, s_x[0]);
+  if constexpr (NS > 2) gm_load_group<FMT, WM, 1>(st, a, 1, s_x[1]);
+  if constexpr (NS > 3) gm_load_group<FMT, WM, 2>(st, a, 2, s_x[2]);
   __syncthreads();
-  for (int c = 0; c < nchp; c += NS) {
+  int c = 0;
+  for (; c + NS <= nch; c += NS) {
     gm_step<FMT, WM, 0>(st, a, s_x, c);
     gm_step<FMT, WM, 1>(st, a, s_x, c + 1);
     if constexpr (NS > 2) gm_step<FMT, WM, 2 % NS>(st, a, s_x, c + 2);
     if constexpr (NS > 3) gm_step<FMT, WM, 3 % NS>(st, a, s_x, c + 3);
+  }
+  // the last nch % NS chunks, already requested
+  const int rest = nch - c;
+  if (rest > 0) gm_step<FMT, WM, 0, true>(st, a, s_x, c);
+  if constexpr (NS > 2) {
+    if (rest > 1) gm_step<FMT, WM, 1, true>(st, a, s_x, c + 1);
+  }
+  if constexpr (NS > 3) {
+    if (rest > 2) gm_step<FMT, WM, 2, true>(st, a, s_x, c + 2);
   }
 
   // lane (kb, n) holds rows 4 kb + r of each x row block, column n of each row block
