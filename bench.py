@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--no-alt", action="store_true", help="do not also time the other layout")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the measured HBM (and, for M >= 16, matrix-core) ceilings")
     ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape timing breakdown")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run 8 x 1 GiB copies and 16 launches of the dominant kernel, then exit")
@@ -144,6 +144,24 @@ def build_stack(wl):
     need = max(wqd.workspace_bytes(wl.fmt, wl.M, N, K) for _, N, K in wl.mats)
     ws = wqd.get_workspace(need, dev)
     return packed, xs, ys, ws
+
+
+def mfma_ceiling(iters=20000):
+    """Measured matrix-core throughput (TFLOP/s): back-to-back bf16 multiplies
+    from registers on every SIMD (the library's ceiling kernel)."""
+    import torch
+
+    import weight_only_quantized_decode_amd as wqd
+
+    sink = torch.empty(wqd.mfma_peak_sink_words(), dtype=torch.float32, device="cuda")
+    wqd.mfma_peak(100, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    flops = wqd.mfma_peak(iters, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    return flops / (e0.elapsed_time(e1) / 1e3) / 1e12
 
 
 def hbm_ceiling(gib=4, reps=10):
@@ -435,6 +453,11 @@ def main():
     if wl.M >= 16:
         tflops = wl.step_flops() / (ms / 1e3) / 1e12
         out["mfma_util_pct"] = round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2)
+        if not args.no_ceiling:
+            peak = mfma_ceiling()
+            log(f"[bench] matrix-core ceiling: {peak:.0f} TFLOP/s")
+            out["mfma_ceiling_TFLOPs"] = round(peak, 1)
+            out["mfma_util_pct_measured_ceiling"] = round(100 * tflops / peak, 2)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl)

@@ -200,6 +200,19 @@ size_t wqd_stream_sink_words(size_t bytes);
 /* Measurement: device copy of `bytes` (multiple of 16) with 16-byte loads/stores. */
 int wqd_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/*
+ * Measurement: the matrix-core ceiling.  Every SIMD runs four wavefronts, each
+ * issuing `iters` x 16 independent v_mfma_f32_16x16x32_bf16 on operands held
+ * in registers, and one float per workgroup goes to `sink` (device, >=
+ * wqd_mfma_peak_sink_words() floats).  wqd_mfma_peak_flops(iters) is the FLOP
+ * count of one launch (host only); divided by the launch's time it gives the
+ * throughput the wide verify batches are compared against.  iters >= 1, else
+ * WQD_E_ARG.
+ */
+int wqd_mfma_peak(int64_t iters, float* sink, void* stream);
+size_t wqd_mfma_peak_sink_words(void);
+double wqd_mfma_peak_flops(int64_t iters);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ OK, E_ARG, E_SHAPE, E_ALIGN, E_WS = 0, 1, 2, 3, 4
 
 def header_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(wqd_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|double|const char\*)\s+(wqd_\w+)\s*\(", text, re.M)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -216,3 +216,9 @@ def test_other_entry_points_reject_bad_arguments():
     assert L.wqd_stream_read(A, 17, A, None) == E_ARG
     assert L.wqd_stream_copy(A, A + 8, 32, None) == E_ALIGN
     assert L.wqd_stream_sink_words(1 << 30) >= 1
+    assert L.wqd_mfma_peak(0, A, None) == E_ARG
+    assert L.wqd_mfma_peak(5, None, None) == E_ARG
+    assert L.wqd_mfma_peak_sink_words() == 512
+    # 512 workgroups x 8 wavefronts x 16 multiplies of 16 x 16 x 32 per iteration
+    assert L.wqd_mfma_peak_flops(3) == 3 * 512 * 8 * 16 * (2 * 16 * 16 * 32)
+    assert L.wqd_mfma_peak_flops(0) == 0.0

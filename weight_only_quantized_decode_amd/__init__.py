@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
             "wqd_stream_read": (i32, [vp, sz, vp, vp]),
             "wqd_stream_sink_words": (sz, [sz]),
             "wqd_stream_copy": (i32, [vp, vp, sz, vp]),
+            "wqd_mfma_peak": (i32, [i64, vp, vp]),
+            "wqd_mfma_peak_sink_words": (sz, []),
+            "wqd_mfma_peak_flops": (ctypes.c_double, [i64]),
         }
         _SIGNATURE_NAMES[:] = list(sig)
         for name, (res, args) in sig.items():
@@ -269,3 +272,14 @@ def stream_copy(dst, src, stream=None):
     nbytes = src.numel() * src.element_size()
     _check(lib().wqd_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream)), "wqd_stream_copy")
     return dst
+
+
+def mfma_peak(iters, sink, stream=None):
+    """Launch the matrix-core ceiling kernel (`iters` x 16 multiplies per
+    wavefront, see wqd_mfma_peak); returns the FLOP count of the launch."""
+    _check(lib().wqd_mfma_peak(int(iters), sink.data_ptr(), _stream(stream)), "wqd_mfma_peak")
+    return lib().wqd_mfma_peak_flops(int(iters))
+
+
+def mfma_peak_sink_words():
+    return lib().wqd_mfma_peak_sink_words()

@@ -175,4 +175,13 @@ int wqd_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
   return hip_status(wqd::launch_stream_copy(dst, src, bytes, as_stream(stream)));
 }
 
+size_t wqd_mfma_peak_sink_words(void) { return wqd::mfma_peak_sink_words(); }
+
+double wqd_mfma_peak_flops(int64_t iters) { return iters < 1 ? 0.0 : wqd::mfma_peak_flops(iters); }
+
+int wqd_mfma_peak(int64_t iters, float* sink, void* stream) {
+  if (!sink || iters < 1) return WQD_E_ARG;
+  return hip_status(wqd::launch_mfma_peak(iters, sink, as_stream(stream)));
+}
+
 }  // extern "C"

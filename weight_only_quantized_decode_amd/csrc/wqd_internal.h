@@ -34,5 +34,8 @@ hipError_t launch_mfma(int fmt, const MfmaPlan& p, int64_t M, int64_t N, int64_t
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 size_t stream_sink_words(size_t bytes);
+hipError_t launch_mfma_peak(int64_t iters, float* sink, hipStream_t st);
+size_t mfma_peak_sink_words();
+double mfma_peak_flops(int64_t iters);
 
 }  // namespace wqd

@@ -1,6 +1,8 @@
-// HBM ceiling kernels: a read-only stream (16-byte loads folded into a
-// checksum so the loads cannot be dropped) and a 16-byte copy.  They give the
-// measured bandwidth that the decode kernels are compared against.
+// Ceiling kernels: a read-only stream (16-byte loads folded into a checksum
+// so the loads cannot be dropped) and a 16-byte copy give the measured HBM
+// bandwidth that the decode kernels are compared against; back-to-back
+// matrix-core multiplies from registers give the measured matrix-core
+// throughput that the wide verify batches are compared against.
 #include "wqd_device.h"
 #include "wqd_internal.h"
 
@@ -54,6 +56,48 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hip
   const size_t n16 = bytes / 16;
   hipLaunchKernelGGL(stream_read_kernel, dim3(unsigned(stream_sink_words(bytes))), dim3(256), 0, st,
                      reinterpret_cast<const uint4*>(src), n16, sink);
+  return hipGetLastError();
+}
+
+// Matrix-core ceiling: every wavefront keeps 16 independent accumulators and
+// issues iters x 16 v_mfma_f32_16x16x32_bf16 on operands that stay in
+// registers; four wavefronts per SIMD (two 8-wavefront workgroups per compute
+// unit).  The accumulators are folded into one float per workgroup so the
+// multiplies cannot be dropped.
+static constexpr unsigned kPeakBlocks = 2 * 256;  // two workgroups on each of the 256 compute units
+static constexpr int kPeakThreads = 512, kPeakAcc = 16;
+
+typedef __bf16 pk_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float pk_f32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kPeakThreads) void mfma_peak_kernel(float* __restrict__ sink, int64_t iters) {
+  pk_bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = __bf16(float(threadIdx.x & 63) * 0.001f + float(i));
+    b[i] = __bf16(float(i) * 0.5f + float(blockIdx.x & 7));
+  }
+  pk_f32x4_t acc[kPeakAcc];
+#pragma unroll
+  for (int i = 0; i < kPeakAcc; ++i) acc[i] = pk_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < kPeakAcc; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPeakAcc; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  if (threadIdx.x == 0) sink[blockIdx.x] = s;
+}
+
+size_t mfma_peak_sink_words() { return kPeakBlocks; }
+
+double mfma_peak_flops(int64_t iters) {
+  return double(kPeakBlocks) * (kPeakThreads / 64) * double(iters) * kPeakAcc * (2.0 * 16 * 16 * 32);
+}
+
+hipError_t launch_mfma_peak(int64_t iters, float* sink, hipStream_t st) {
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(kPeakBlocks), dim3(kPeakThreads), 0, st, sink, iters);
   return hipGetLastError();
 }
 
