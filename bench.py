@@ -280,6 +280,13 @@ def cpu_baseline(wl):
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count()
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     return {
         "value": round(gbps, 3),
         "unit": "GB/s",
@@ -287,7 +294,8 @@ def cpu_baseline(wl):
         "kind": "oracle",
         "sample": f"{reps} calls of the float64 oracle (exact dequant, matmul, bf16 rounding) on one "
                   f"{name} matrix {N}x{K} {wl.fmt}, M={wl.M}: {per_call * 1e3:.1f} ms per call; "
-                  f"host {platform.machine()}, {os.cpu_count()} logical CPUs, BLAS threads {threads}",
+                  f"host {model} ({platform.machine()}), {os.cpu_count()} logical CPUs, {affinity} in this "
+                  f"process's affinity mask, BLAS threads {threads}",
     }
 
 
@@ -444,6 +452,7 @@ def main():
         "hbm_read_ceiling_GBps": None if ceiling[0] is None else round(ceiling[0], 1),
         "hbm_copy_ceiling_GBps": None if ceiling[1] is None else round(ceiling[1], 1),
         "pct_measured_read_ceiling": None if ceiling[0] is None else round(100 * gbps / ceiling[0], 2),
+        "pct_measured_copy_ceiling": None if ceiling[1] is None else round(100 * gbps / ceiling[1], 2),
         "roofline": roofline,
     }
     if alt is not None:
