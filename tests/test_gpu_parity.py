@@ -169,6 +169,25 @@ def test_qgemm_two_blocks_per_wave(fmt):
     compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("fmt", ["w4a16", "fp8"])
+def test_qgemm_three_blocks_per_wave(fmt):
+    """Streaming matrix-core kernel with three 16-row blocks per wavefront (640
+    row blocks: 214 workgroups instead of 320 of two), and a ragged N whose
+    last workgroup holds one partial block and two past N."""
+    for N in (10240, 10232):
+        K = 1024
+        W = I.w_host(4100 + N, N, K)
+        qw = oracle.quantize(fmt, W)
+        pw = wqd.pack_weights(fmt, to_dev(W))
+        for M in ((2, 6, 8) if fmt == "w4a16" else (6, 8)):
+            assert wqd.kernel_path(fmt, M, N, K) == ("mc", 4)
+            print(f"qgemm {fmt} M={M} N={N} K={K}", flush=True)
+            x = I.x_bf16_bits(29 + M, M, K)
+            y = wqd.qgemm(x_dev(x), pw)
+            torch.cuda.synchronize()
+            compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
+
+
 def skinny_shapes(fmt):
     # (N, K) for the skinny matrix-core kernel, in tiles of TK k.  With the
     # planner's choices: 13 tiles (shares shorter than one loop body; 7

@@ -49,7 +49,7 @@ struct McC {
   static constexpr int TK = FMT == kFmtBF16 ? 32 : FMT == kFmtFP8 ? 64 : 128;  // K per tile
   static constexpr int SLK = TK / 4;                                             // K per slice
   static constexpr int XU = SLK / 8;  // x uint4 per lane and tile = matrix-core steps per tile
-  static constexpr int LW = RB == 1 ? 7 : 3;  // tile steps whose weights are loaded ahead
+  static constexpr int LW = RB == 1 ? 7 : 3;  // tile steps whose weights are loaded ahead (RB = 2, 3: 3)
   static constexpr int LX = 2;                // x tiles loaded ahead
   static constexpr int RW = LW + 1;           // ring sizes
   static constexpr int RX = LX + 1;
@@ -266,7 +266,11 @@ static hipError_t launch_mc_w(const McArgs& a, int waves, unsigned grid, hipStre
   switch (waves) {
     case 4: hipLaunchKernelGGL((gemv_mc_kernel<FMT, 4, NT, RB>), dim3(grid), dim3(256), 0, st, a); break;
     case 8: hipLaunchKernelGGL((gemv_mc_kernel<FMT, 8, NT, RB>), dim3(grid), dim3(512), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((gemv_mc_kernel<FMT, 16, NT, RB>), dim3(grid), dim3(1024), 0, st, a); break;
+    case 16:
+      // three row blocks do not fit the 128 registers of a 16-wavefront workgroup
+      if constexpr (RB == 3) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL((gemv_mc_kernel<FMT, 16, NT, RB>), dim3(grid), dim3(1024), 0, st, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -281,6 +285,9 @@ static hipError_t launch_mc_fmt(const McArgs& a, const McPlan& p, hipStream_t st
   } else if (p.rb == 2) {
     if (p.per_wave <= 16) return launch_mc_w<FMT, 16, 2>(a, p.waves, grid, st);
     if (p.per_wave <= 32) return launch_mc_w<FMT, 32, 2>(a, p.waves, grid, st);
+  } else if (p.rb == 3) {
+    if (p.per_wave <= 16) return launch_mc_w<FMT, 16, 3>(a, p.waves, grid, st);
+    if (p.per_wave <= 32) return launch_mc_w<FMT, 32, 3>(a, p.waves, grid, st);
   }
   return hipErrorInvalidValue;
 }

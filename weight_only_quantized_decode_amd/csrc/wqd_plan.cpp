@@ -79,6 +79,8 @@ int plan_bcast(int fmt, int64_t M, int64_t N, int64_t K, BcastPlan* out) {
 // Wavefronts per workgroup as for the broadcast kernel: the fewest whose
 // shares hold at most 32 tiles, doubled while the launch has fewer than 2048
 // wavefronts and each keeps at least one group of 4 tiles.
+constexpr int64_t kComputeUnits = 256;  // MI355X
+
 int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out) {
   PackedSizes ps;
   int st = packed_sizes(fmt, N, K, &ps);
@@ -94,12 +96,20 @@ int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out) {
   // keep the fewest wavefronts whose shares fit (measured on 8192^2 and
   // 4096^2: 5-12% faster than doubling them).
   const bool wide = M > kGemvMaxM && fmt != kFmtBF16;
-  const int rb = ps.NB >= 128 && (fmt == kFmtW4 || ps.KT >= 256 || wide) ? 2 : 1;
+  int rb = ps.NB >= 128 && (fmt == kFmtW4 || ps.KT >= 256 || wide) ? 2 : 1;
+  // Three row blocks when that lowers the most row blocks any compute unit
+  // carries (one workgroup per unit is the aim: a unit running two takes
+  // their time end to end): 640 blocks (a 10240-row matrix) give 214
+  // workgroups of three instead of 320 of two.  Not with 16 wavefronts,
+  // whose 128 registers three row blocks do not fit.
+  if (rb == 2 && share(8) <= 32 &&
+      ceil_div(ceil_div(ps.NB, 3), kComputeUnits) * 3 < ceil_div(ceil_div(ps.NB, 2), kComputeUnits) * 2)
+    rb = 3;
   const int64_t units = ceil_div(ps.NB, rb);
   int w = 4;
   while (w < 16 && share(w) > 32) w *= 2;
   if (share(w) > 32) return kEUnsupported;
-  while (!wide && w < 16 && units * w < 2048 / rb && ceil_div(ps.KT, 4) >= 2 * w) w *= 2;
+  while (!wide && w < (rb == 3 ? 8 : 16) && units * w < 2048 / rb && ceil_div(ps.KT, 4) >= 2 * w) w *= 2;
   McPlan p{};
   p.NB = ps.NB;
   p.KT = ps.KT;
@@ -122,7 +132,6 @@ int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out) {
 // (each adds M * N * 8 bytes of partial traffic).  The configuration whose
 // workgroups fill whole multiples of the compute units best wins; near ties
 // go to the earlier one (measured on the 70B shapes).
-constexpr int64_t kComputeUnits = 256;  // MI355X
 
 static int plan_skinny_with(int fmt, int64_t M, const PackedSizes& ps, int waves, int rb, int64_t S, SkPlan* out) {
   SkPlan p{};

@@ -79,7 +79,7 @@ constexpr int kMcMaxM = 16;
 struct McPlan {
   int64_t NB, KT;
   int waves, per_wave;
-  int rb;  // 16-row blocks per wavefront (1 or 2): x fragments shared by rb weight tiles
+  int rb;  // 16-row blocks per wavefront (1, 2 or 3): x fragments shared by rb weight tiles
 };
 
 int plan_mc(int fmt, int64_t M, int64_t N, int64_t K, McPlan* out);
