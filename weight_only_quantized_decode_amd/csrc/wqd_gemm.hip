@@ -6,16 +6,17 @@
 // on verify width; CS336 lecture 10 notes, 3.2-3.3: the MLP's arithmetic
 // intensity grows with the batch), and from about a hundred rows the matrix
 // cores, not HBM, set the time.  Design for gfx950:
-//   * a workgroup computes a BM x 256 tile of y (BM = 64 WM rows) with WM x WN
-//     wavefronts, each owning 64 rows x RB weight row blocks (BF16 / FP8: 4
-//     row blocks, 4 x 2 wavefronts; W4A16: 2 row blocks, 8 x 1 wavefronts,
-//     whose group partials need a second set of accumulators):
-//     v_mfma_f32_16x16x32_bf16 throughout;
+//   * a workgroup computes a BM x 256 tile of y with WM x WN wavefronts, each
+//     owning 16 MF rows x RB weight row blocks: BM = 64 with 64-row wavefront
+//     tiles (BF16 / FP8: 4 row blocks, 4 wavefronts; W4A16: 2 row blocks, 8
+//     wavefronts, whose group partials need a second set of accumulators), or
+//     BM = 256 for BF16 / FP8 above 256 rows (two wavefront rows of 128-row
+//     tiles, 8 wavefronts); v_mfma_f32_16x16x32_bf16 throughout;
 //   * the packed 1 KiB weight tile is already the B-operand order (lane
 //     16 kb + n: slice kb of weight row n), so weights go from memory straight
 //     into registers and become exact bf16 B fragments there (FP8 codes by the
 //     hardware conversion, W4A16 codes as 128 + q by OR-ing them into the
-//     mantissa of 128.0, BF16 as is), each feeding 4 x row blocks.  The FP8
+//     mantissa of 128.0, BF16 as is), each feeding MF x row blocks.  The FP8
 //     row scale is applied once at the end.  W4A16 follows the group's
 //     definition of the dequantised weight, s (q - z): a chunk is one 128-k
 //     group, its product P = sum x (128 + q) is formed in fresh accumulators,
@@ -37,7 +38,8 @@
 //     pending load into LDS, including those of chunks c + 2 ...  Each stage
 //     buffer is its own LDS array, which lets the compiler see that reading
 //     one does not wait for loads into another.  The loop body is NS chunks,
-//     so every index is a compile-time constant;
+//     so every index is a compile-time constant; the last nch % NS chunks
+//     follow as steps that request nothing;
 //   * weights are read with the default cache policy: every x row block of a
 //     column block re-reads them, and XCD-aware order keeps them in one L2:
 //     consecutive workgroups of one XCD (dispatch is round-robin over the 8
@@ -134,7 +136,6 @@ struct GmState {
 };
 
 // 16 bytes per lane from r into LDS: lane i's bytes land at dst + 16 i.
-template <int FMT, int WM>
 __device__ __forceinline__ void gm_dma(__amdgpu_buffer_rsrc_t r, uint4* dst, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
@@ -168,8 +169,8 @@ __device__ __forceinline__ void gm_load_sz(GmState<FMT, WM>& st, int c, uint4* b
     static_assert(kScaleQuad == 4, "four groups per scale quad");
     const uint32_t q = (uint32_t(st.kt0) + uint32_t(c)) >> 2;
     uint4* slot = buf + L::FRAGS * 64 + st.wave * L::SLOT;
-    gm_dma<FMT, WM>(st.sres, slot + L::SL_S, st.svo, q * (kTileRows * kScaleQuad * 2));
-    gm_dma<FMT, WM>(st.zres, slot + L::SL_Z, st.zvo, q * (kTileRows * 2));
+    gm_dma(st.sres, slot + L::SL_S, st.svo, q * (kTileRows * kScaleQuad * 2));
+    gm_dma(st.zres, slot + L::SL_Z, st.zvo, q * (kTileRows * 2));
   }
 }
 
@@ -185,9 +186,9 @@ __device__ __forceinline__ void gm_load_x(GmState<FMT, WM>& st, const GmArgs& a,
     const int64_t g = st.kt0 + c;
     const uint32_t so = g < a.KT ? uint32_t(g * kGroup * 2) : 0x7FFFFFF0u;
     const uint32_t sso = g < a.KT ? uint32_t(g * a.Mp * 4) : 0x7FFFFFF0u;
-    gm_dma<FMT, WM>(st.xsres, buf + L::FRAGS * 64 + st.wave * L::SLOT + L::SL_XS, st.xsvo, sso);
+    gm_dma(st.xsres, buf + L::FRAGS * 64 + st.wave * L::SLOT + L::SL_XS, st.xsvo, sso);
 #pragma unroll
-    for (int u = 0; u < L::XPW; ++u) gm_dma<FMT, WM>(st.xres, buf + (st.wave * L::XPW + u) * 64, st.xvo[u], so);
+    for (int u = 0; u < L::XPW; ++u) gm_dma(st.xres, buf + (st.wave * L::XPW + u) * 64, st.xvo[u], so);
     return;
   }
   const int kb = st.lane >> 4, j = st.lane & 15;
@@ -198,7 +199,7 @@ __device__ __forceinline__ void gm_load_x(GmState<FMT, WM>& st, const GmArgs& a,
     const int64_t row = st.m0 + 16 * i + j;
     const int64_t k = (st.kt0 + int64_t(c) * F::TPC + t) * F::TK + kb * F::SLK + 8 * s;
     const uint32_t off = row < a.M && k < a.K ? uint32_t((row * a.K + k) * 2) : 0x80000000u;
-    gm_dma<FMT, WM>(st.xres, buf + f * 64, off, 0);
+    gm_dma(st.xres, buf + f * 64, off, 0);
   }
 }
 
