@@ -333,14 +333,9 @@ __device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, GmFrag<FMT, WM>
       }
     }
   } else if constexpr (FMT == kFmtFP8) {
-    using L = GmL<FMT, WM>;
+    // 64-row tiles read both steps' fragments before the multiplies (NA = 2)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if (s >= F::NA) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < F::MF; ++i) f.a[s % F::NA][i] = buf[((st.wm * F::MF + i) * F::STEPS + s) * 64 + st.lane];
-      }
       uint4 bm[F::RB];
 #pragma unroll
       for (int b = 0; b < F::RB; ++b) {
@@ -352,25 +347,31 @@ __device__ __forceinline__ void gm_compute(GmState<FMT, WM>& st, GmFrag<FMT, WM>
                            __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(w1)));
       }
 #pragma unroll
-      for (int i = 0; i < F::MF; ++i)
+      for (int i = 0; i < F::MF; ++i) {
 #pragma unroll
         for (int b = 0; b < F::RB; ++b) st.acc[i][b] = gm_mfma(f.a[s % F::NA][i], bm[b], st.acc[i][b]);
+        // 128-row tiles: the second step's fragment i replaces the first's as
+        // soon as its multiplies are issued, so the LDS reads overlap the rest
+        if constexpr (F::NA == 1) {
+          if (s == 0) f.a[0][i] = buf[((st.wm * F::MF + i) * F::STEPS + 1) * 64 + st.lane];
+        }
+      }
     }
   } else {
     using L = GmL<FMT, WM>;
+    // 64-row tiles read both tiles' fragments before the multiplies (NA = 2)
 #pragma unroll
     for (int t = 0; t < F::TPC; ++t) {
-      if (t >= F::NA) {
-        // a later step's fragments replace the first step's once those are
-        // multiplied
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < F::MF; ++i) f.a[t % F::NA][i] = buf[(t * L::XB + st.wm * F::MF + i) * 64 + st.lane];
-      }
-#pragma unroll
-      for (int i = 0; i < F::MF; ++i)
+      for (int i = 0; i < F::MF; ++i) {
 #pragma unroll
         for (int b = 0; b < F::RB; ++b) st.acc[i][b] = gm_mfma(f.a[t % F::NA][i], st.w[H][b][t], st.acc[i][b]);
+        // 128-row tiles: the next tile's fragment i replaces this one as soon
+        // as its multiplies are issued, so the LDS reads overlap the rest
+        if constexpr (F::NA == 1) {
+          if (t + 1 < F::TPC) f.a[0][i] = buf[((t + 1) * L::XB + st.wm * F::MF + i) * 64 + st.lane];
+        }
+      }
     }
   }
 }
