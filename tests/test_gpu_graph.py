@@ -22,6 +22,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("w4a16", 1, 4104, 4096, "bcast"),
     ("w4a16", 4, 8192, 2048, "mc"),
+    ("w4a16", 4, 10232, 1024, "mc"),         # three row blocks per wavefront, ragged N
     ("fp8", 16, 10240, 2048, "skinny"),      # K split: partials + second launch
     ("w4a16", 300, 4104, 4096, "gemm"),      # x sums, K split
     ("bf16", 200, 4000, 1160, "gemm"),
