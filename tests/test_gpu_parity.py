@@ -271,6 +271,24 @@ def test_qgemm_tiled(fmt):
             compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("N,K,Ms", [(16392, 640, (200,)), (16392, 2048, (65, 200)), (12296, 4096, (65,))])
+def test_qgemm_tiled_w4a16_128_rows(N, K, Ms):
+    """W4A16 on 128-row wavefront tiles (the planner's time model picks them for
+    these shapes): no K split with an odd chunk count (5) and an even one
+    (16), K splits of 3 and 5 with both remainders, and ragged rows."""
+    fmt = "w4a16"
+    W = I.w_host(6100 + N + K, N, K)
+    qw = oracle.quantize(fmt, W)
+    pw = wqd.pack_weights(fmt, to_dev(W))
+    for M in Ms:
+        assert wqd.kernel_path(fmt, M, N, K) == ("gemm", 8)
+        print(f"qgemm {fmt} M={M} N={N} K={K} ws={wqd.workspace_bytes(fmt, M, N, K)}", flush=True)
+        x = I.x_bf16_bits(37 * M + K, M, K)
+        y = wqd.qgemm(x_dev(x), pw)
+        torch.cuda.synchronize()
+        compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
+
+
 def mfma_wide_shapes(fmt):
     # (N, K) that the LDS matrix-core kernel takes above 64 rows (below 16
     # column blocks of 256): ragged N, ragged K tiles where the format allows

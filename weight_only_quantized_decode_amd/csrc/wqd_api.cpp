@@ -78,7 +78,7 @@ int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* wa
            : c.path == wqd::kPathMc    ? c.mc.waves
            : c.path == wqd::kPathStaged ? c.gemv.waves
            : c.path == wqd::kPathSkinny ? c.sk.waves + 1
-           : c.path == wqd::kPathGemm   ? (fmt == wqd::kFmtW4 ? 8 : 4) * c.gm.wm
+           : c.path == wqd::kPathGemm   ? (fmt == wqd::kFmtW4 ? 8 : 4 * c.gm.wm)
                                         : 4;
   }
   return WQD_OK;

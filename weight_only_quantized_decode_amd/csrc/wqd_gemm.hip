@@ -6,12 +6,13 @@
 // on verify width; CS336 lecture 10 notes, 3.2-3.3: the MLP's arithmetic
 // intensity grows with the batch), and from about a hundred rows the matrix
 // cores, not HBM, set the time.  Design for gfx950:
-//   * a workgroup computes a BM x 256 tile of y with WM x WN wavefronts, each
-//     owning 16 MF rows x RB weight row blocks: BM = 64 with 64-row wavefront
-//     tiles (BF16 / FP8: 4 row blocks, 4 wavefronts; W4A16: 2 row blocks, 8
-//     wavefronts, whose group partials need a second set of accumulators), or
-//     BM = 256 for BF16 / FP8 above 256 rows (two wavefront rows of 128-row
-//     tiles, 8 wavefronts); v_mfma_f32_16x16x32_bf16 throughout;
+//   * a workgroup computes a BM x 256 tile of y with WR x WN wavefronts, each
+//     owning 16 MF rows x RB weight row blocks.  WM = 1: 64-row wavefront
+//     tiles, BM = 64 (BF16 / FP8: 4 row blocks, 4 wavefronts; W4A16: 2 row
+//     blocks, 8 wavefronts, whose group partials need a second set of
+//     accumulators).  WM = 2: 128-row wavefront tiles, BM = 256 for BF16 /
+//     FP8 (two wavefront rows, 8 wavefronts) and 128 for W4A16 (one row of 8);
+//     v_mfma_f32_16x16x32_bf16 throughout;
 //   * the packed 1 KiB weight tile is already the B-operand order (lane
 //     16 kb + n: slice kb of weight row n), so weights go from memory straight
 //     into registers and become exact bf16 B fragments there (FP8 codes by the
@@ -93,14 +94,18 @@ struct GmF {
   static constexpr int NS = FMT == kFmtFP8 ? 4 : 3;
 };
 
-// Per (format, wavefront rows): BF16 and FP8 with two wavefront rows take
-// 128-row wavefront tiles (8 x row blocks, 256 rows per workgroup; two
-// pipeline stages, as the accumulators take the registers of the others; the
-// second step's x fragments are read after the first step's multiplies).
+// Per (format, WM): WM = 2 takes 128-row wavefront tiles (8 x row blocks;
+// BF16 and FP8 in two wavefront rows, 256 rows per workgroup, W4A16 in one,
+// 128 rows).  Each weight fragment then feeds 8 x row blocks, which halves
+// the weight traffic through the texture path (BF16 / FP8) and the
+// dequantisation (W4A16) per multiply.  Two pipeline stages: the
+// accumulators take the registers (and for W4A16 the 128-row x chunks the
+// LDS) of the others.
 template <int FMT, int WM>
 struct GmT : GmF<FMT> {
-  static constexpr bool WIDE = (FMT == kFmtBF16 || FMT == kFmtFP8) && WM == 2;
+  static constexpr bool WIDE = WM == 2;
   static constexpr int MF = WIDE ? 8 : GmF<FMT>::MF;
+  static constexpr int WR = GmF<FMT>::W4 ? 1 : WM;  // wavefront rows
   static constexpr int NS = WIDE ? 2 : GmF<FMT>::NS;
   static constexpr int NA = GmF<FMT>::W4 || WIDE ? 1 : GmF<FMT>::NQ;  // 32-k steps read before the multiplies
 };
@@ -108,9 +113,9 @@ struct GmT : GmF<FMT> {
 template <int FMT, int WM>
 struct GmL {
   using F = GmT<FMT, WM>;
-  static constexpr int XB = F::MF * WM;                 // x row blocks per workgroup
+  static constexpr int XB = F::MF * F::WR;              // x row blocks per workgroup
   static constexpr int FRAGS = F::TPC * XB * F::STEPS;  // 1 KiB fragments per chunk
-  static constexpr int NW = WM * F::WN;                 // wavefronts per workgroup
+  static constexpr int NW = F::WR * F::WN;              // wavefronts per workgroup
   static constexpr int XPW = FRAGS / NW;                // fragments each wavefront stages
   // W4A16: each wavefront's slot after the fragments, 1 KiB per load (lanes
   // out of range may write zeros where their bytes would go): the group's x
@@ -406,7 +411,7 @@ __device__ __forceinline__ void gm_step(GmState<FMT, WM>& st, const GmArgs& a, u
 }
 
 template <int FMT, int WM>
-__global__ __launch_bounds__(64 * WM * GmF<FMT>::WN) void gemm_kernel(GmArgs a) {
+__global__ __launch_bounds__((64 * GmT<FMT, WM>::WR * GmF<FMT>::WN)) void gemm_kernel(GmArgs a) {
   using F = GmT<FMT, WM>;
   using L = GmL<FMT, WM>;
   constexpr int NS = F::NS;
@@ -429,7 +434,7 @@ __global__ __launch_bounds__(64 * WM * GmF<FMT>::WN) void gemm_kernel(GmArgs a) 
   const int c0 = split * a.cps;
   const int nch = a.nchunks - c0 < a.cps ? a.nchunks - c0 : a.cps;  // >= 1: the planner sizes S so
   st.kt0 = int64_t(c0) * F::TPC;
-  st.m0 = int64_t(mb) * 16 * F::MF * WM;
+  st.m0 = int64_t(mb) * 16 * F::MF * F::WR;
   const int64_t tiles = a.KT - st.kt0 < int64_t(nch) * F::TPC ? a.KT - st.kt0 : int64_t(nch) * F::TPC;
   st.nb0 = int64_t(nbn) * 16 + wn * F::RB;
 #pragma unroll
@@ -549,11 +554,10 @@ template <int FMT>
 static hipError_t launch_gm_fmt(const GmArgs& a, const GmPlan& p, hipStream_t st) {
   constexpr int WN = GmF<FMT>::WN;
   const unsigned grid = unsigned(ceil_div(p.NBN, 8) * 8 * p.MB);
-  if (p.wm == 2 && FMT != kFmtW4)
-    hipLaunchKernelGGL((gemm_kernel<FMT, (FMT == kFmtW4 ? 1 : 2)>), dim3(grid, unsigned(p.S)), dim3(64 * 2 * WN), 0,
-                       st, a);
+  if (p.wm == 2)
+    hipLaunchKernelGGL((gemm_kernel<FMT, 2>), dim3(grid, unsigned(p.S)), dim3(64 * GmT<FMT, 2>::WR * WN), 0, st, a);
   else if (p.wm == 1)
-    hipLaunchKernelGGL((gemm_kernel<FMT, 1>), dim3(grid, unsigned(p.S)), dim3(64 * 1 * WN), 0, st, a);
+    hipLaunchKernelGGL((gemm_kernel<FMT, 1>), dim3(grid, unsigned(p.S)), dim3(64 * GmT<FMT, 1>::WR * WN), 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -588,7 +592,7 @@ hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64
   } else if (fmt == kFmtFP8) {
     e = launch_gm_fmt<kFmtFP8>(a, p, st);
   } else {
-    if (p.wm != 1 || p.Mp < M || p.Mp % 64 != 0) return hipErrorInvalidValue;
+    if (p.Mp < M || p.Mp % (p.wm == 2 ? 128 : 64) != 0) return hipErrorInvalidValue;
     const int64_t n = p.KT * p.Mp;
     hipLaunchKernelGGL(gm_xsum_kernel, dim3(unsigned(ceil_div(n, int64_t(256)))), dim3(256), 0, st, a.x, M, K, p.Mp,
                        p.KT, reinterpret_cast<float*>(ws));

@@ -112,11 +112,13 @@ int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out);
 
 // Tiled matrix-core kernel (more than kGmMinM rows and at least kGmMinNBN
 // column blocks): wm = 1, a 64 x 256 tile of y (BF16 / FP8 up to 256 rows: 4
-// wavefronts of 64 x 64; W4A16: 8 of 64 x 32), or wm = 2 for BF16 / FP8 above
-// 256 rows, a 256 x 256 tile (8 wavefronts of 128 x 64); NBN column blocks x
-// MB row blocks of workgroups (XCD-aware order), K in chunks (64; W4A16 128)
-// split S ways (cps chunks per split) as a time model of the kernel picks.
-// Workspace: W4A16 x sums, float32 [KT][Mp] (Mp = 64 MB rows), xs_bytes
+// wavefronts of 64 x 64; W4A16: 8 of 64 x 32), or wm = 2, 128-row wavefront
+// tiles (BF16 / FP8 above 256 rows: a 256 x 256 tile, 8 wavefronts of
+// 128 x 64; W4A16 where the time model puts it faster: 128 x 256, 8 of
+// 128 x 32); NBN column blocks x MB row blocks of workgroups (XCD-aware
+// order), K in chunks (64; W4A16 128) split S ways (cps chunks per split) as
+// the time model picks.
+// Workspace: W4A16 x sums, float32 [KT][Mp] (Mp = MB rows per block), xs_bytes
 // rounded up to 256; then the S float32 partials, S * M * N * 4 bytes when
 // S > 1.  kEUnsupported for x rows spanning 2 GiB or more.
 constexpr int kGmMinM = 64;
