@@ -10,7 +10,7 @@ layer; Llama-2-7B for the BF16 stack):
   * 70B FP8-E4M3 layer shapes, M = 1, 8, 32;
   * 70B W4A16 layer shapes with 6 outlier hidden channels at 20x, M = 1, 4, 16, 32;
   * speculative-verify widths M = batch x (k + 1) on q / gate / down shapes in
-    W4A16 and BF16.
+    W4A16, BF16 and FP8.
 """
 import numpy as np
 import pytest
@@ -75,7 +75,14 @@ def test_70b_w4a16_shapes_with_outliers(N, K):
     run_case("w4a16", N, K, [1, 4, 16, 32], 400 + N % 97 + K % 89, outliers=True)
 
 
-@pytest.mark.parametrize("fmt", ["w4a16", "bf16"])
+@pytest.mark.parametrize("fmt", ["w4a16", "bf16", "fp8"])
 @pytest.mark.parametrize("N,K", [(8192, 8192), (28672, 8192), (8192, 28672)])
 def test_verify_widths(fmt, N, K):
-    run_case(fmt, N, K, [6, 16, 48, 128, 1024], 500 + N % 97 + K % 89, outliers=True)
+    run_case(fmt, N, K, [6, 16, 48, 128, 200, 1024], 500 + N % 97 + K % 89, outliers=True)
+
+
+@pytest.mark.parametrize("fmt,N,K,M", [("bf16", 8192, 8192, 129), ("fp8", 8192, 28672, 200)])
+def test_tall_tiles_below_256_rows(fmt, N, K, M):
+    """BF16 / FP8 on 256-row tiles with padded rows and an 8-way K split."""
+    assert wqd.kernel_path(fmt, M, N, K) == ("gemm", 8)
+    run_case(fmt, N, K, [M], 600 + N % 97 + K % 89, outliers=False)

@@ -289,6 +289,21 @@ def test_qgemm_tiled_w4a16_128_rows(N, K, Ms):
         compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("fmt,N,K,M", [("bf16", 8224, 4096, 200), ("bf16", 8232, 4104, 193)])
+def test_qgemm_tiled_256_rows_padded(fmt, N, K, M):
+    """BF16 on 256-row tiles below 256 rows (the planner's time model picks them
+    for these shapes with a K split): padded rows, ragged N, ragged K."""
+    W = I.w_host(6200 + N + K, N, K)
+    qw = oracle.quantize(fmt, W)
+    pw = wqd.pack_weights(fmt, to_dev(W))
+    assert wqd.kernel_path(fmt, M, N, K) == ("gemm", 8)
+    print(f"qgemm {fmt} M={M} N={N} K={K} ws={wqd.workspace_bytes(fmt, M, N, K)}", flush=True)
+    x = I.x_bf16_bits(41 * M + K, M, K)
+    y = wqd.qgemm(x_dev(x), pw)
+    torch.cuda.synchronize()
+    compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
+
+
 def mfma_wide_shapes(fmt):
     # (N, K) that the LDS matrix-core kernel takes above 64 rows (below 16
     # column blocks of 256): ragged N, ragged K tiles where the format allows

@@ -207,15 +207,29 @@ int plan_skinny(int fmt, int64_t M, int64_t N, int64_t K, SkPlan* out) {
 
 // Tiled kernel (above kGmMinM rows, where it measured faster than the LDS
 // matrix-core kernel on the 70B verify shapes once N gives at least kGmMinNBN
-// column blocks): 64-row blocks (4 wavefronts for BF16 / FP8, 8 for W4A16) up
-// to 256 rows and for W4A16 throughout, 256-row blocks of 8 wavefronts above.
-// The K split comes from a time model fitted to the kernel on those shapes:
-// with one workgroup per compute unit, the launch runs ceil(W / 256) rounds of
-// cps chunks each (W = tiles x splits); a 64-k chunk costs 1.17 us for BF16
-// and 0.88 for FP8 with 64-row blocks, 2.5 and 1.83 with 256-row blocks, a
-// 128-k W4A16 chunk 1.42; every split adds M x N float32 partials written and
-// read once at about 4 TB/s.  The cheapest S from 1 to 8 (each split at least
-// 4 chunks) wins; within 2% the smaller S.
+// column blocks).  Tile heights: 64 rows (4 wavefronts for BF16 / FP8, 8 for
+// W4A16) or, with wm = 2, 256 rows of 8 wavefronts (BF16 / FP8) or 128 rows
+// (W4A16).  Height and K split come from time models fitted to the kernel on
+// the 7B and 70B projection shapes (W = tiles x splits workgroups, cps chunks
+// of 64 k (128 for W4A16) per workgroup, S splits):
+//  * BF16 / FP8: t = c0 + cps x (a + b x fill) x L + S x M x N x 8 B / bw,
+//    where fill is the share of real rows in the padded tiles and L = 1 for
+//    W <= 256, else r x ceil(W / 256) (r < 1 for 64-row tiles, which run two
+//    workgroups per compute unit side by side); the last term, for S > 1, is
+//    the float32 partials written and read once.  Fitted constants below
+//    (c0 in us, a and b in us per chunk, bw in TB/s); on the fitting sweep
+//    the modelled choice came within 1.3% of the best measured one in total.
+//  * W4A16: ceil(W / 256) rounds of cps chunks at 1.33 us (64 rows) or 2.26
+//    (128 rows) per chunk, plus partials at about 4 TB/s.
+// The cheapest S from 1 to 8 (each split at least 4 chunks) wins, within 2%
+// the smaller S; between heights the taller one needs a 2% margin.
+struct GmCost {
+  double c0, a, b, r, bw;
+};
+static constexpr GmCost kGmCost[2][2] = {
+    {{7.7, 0.771, 0.0, 0.941, 4.37}, {10.5, 1.649, 0.498, 1.103, 5.38}},   // BF16: 64 / 256 rows
+    {{8.4, 0.469, 0.079, 0.912, 4.49}, {11.4, 1.23, 0.394, 1.13, 6.16}},  // FP8
+};
 // One tile shape (wm) of the tiled kernel: its padded rows, x-sum bytes and
 // the K split of least modelled time (returned in *t_us).
 static int plan_gemm_wm(int fmt, int64_t M, int64_t N, int64_t K, const PackedSizes& ps, int wm, GmPlan* out,
@@ -233,17 +247,22 @@ static int plan_gemm_wm(int fmt, int64_t M, int64_t N, int64_t K, const PackedSi
   if (fmt == kFmtW4 && p.KT * p.Mp * 4 >= (int64_t(1) << 31)) return kEUnsupported;
   p.xs_bytes = fmt == kFmtW4 ? (size_t(p.KT) * size_t(p.Mp) * sizeof(float) + 255) / 256 * 256 : 0;
   const int64_t tiles = p.NBN * p.MB;
-  // us per chunk of one workgroup (fitted on the 70B shapes)
-  const double t_chunk = fmt == kFmtW4 ? (wide ? 2.26 : 1.33)
-                                       : wide ? (fmt == kFmtFP8 ? 1.83 : 2.5) : (fmt == kFmtFP8 ? 0.88 : 1.17);
-  const double part_us = double(M) * double(N) * 8.0 / 4.0e6;  // one split's partials, us
+  const double mn8 = double(M) * double(N) * 8.0;  // one split's partials, bytes
+  const double fill = double(M) / double(p.Mp);
   const int64_t max_s = p.nchunks / 4 < 1 ? 1 : (p.nchunks / 4 > 8 ? 8 : p.nchunks / 4);
   double best = 0.0;
   int64_t S = 1;
   for (int64_t s = 1; s <= max_s; ++s) {
     const int64_t cps = ceil_div(p.nchunks, s), se = ceil_div(p.nchunks, cps);
-    const double t = double(ceil_div(tiles * se, kComputeUnits)) * double(cps) * t_chunk +
-                     (se > 1 ? double(se) * part_us : 0.0);
+    const int64_t rounds = ceil_div(tiles * se, kComputeUnits);
+    double t;
+    if (fmt == kFmtW4) {
+      t = double(rounds) * double(cps) * (wide ? 2.26 : 1.33) + (se > 1 ? double(se) * mn8 / 4.0e6 : 0.0);
+    } else {
+      const GmCost& c = kGmCost[fmt == kFmtFP8][wide];
+      const double L = rounds == 1 ? 1.0 : c.r * double(rounds);
+      t = c.c0 + double(cps) * (c.a + c.b * fill) * L + (se > 1 ? double(se) * mn8 / (c.bw * 1.0e6) : 0.0);
+    }
     if (s == 1 || t < 0.98 * best) {
       best = t;
       S = se;
@@ -264,12 +283,12 @@ int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   if (M < 1) return kEArg;
   if (M * K * 2 >= (int64_t(1) << 31)) return kEUnsupported;
   double t1 = 0.0, t2 = 0.0;
-  if (fmt != kFmtW4) return plan_gemm_wm(fmt, M, N, K, ps, M <= 256 ? 1 : 2, out, &t1);
-  // W4A16: 64- or 128-row tiles, whichever the model puts faster (within 2%:
-  // 64).  128 rows halve the dequantisation per multiply but pad M and
-  // quantise the launch into rounds more coarsely (measured on the 70B
-  // shapes: 4-14% faster for gate / down from 512 rows and q from 768, up to
-  // 12% slower where the rounds fall badly, e.g. gate at 384 rows).
+  // 64-row tiles or the taller ones, whichever the model puts faster (within
+  // 2%: 64).  Taller tiles read each weight chunk for more rows (W4A16: half
+  // the dequantisation per multiply) but pad M and quantise the launch into
+  // rounds more coarsely (W4A16 on the 70B shapes: 4-14% faster for gate /
+  // down from 512 rows and q from 768, up to 12% slower where the rounds fall
+  // badly, e.g. gate at 384 rows).
   GmPlan p1, p2;
   st = plan_gemm_wm(fmt, M, N, K, ps, 1, &p1, &t1);
   if (st != kOK) return st;
