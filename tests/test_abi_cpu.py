@@ -142,14 +142,17 @@ def test_kernel_path_choice():
             assert wqd.kernel_path(fmt, M, 4096, 4096)[0] == "mc"
     assert wqd.kernel_path("fp8", 16, 8192, 8208)[0] == "mfma"          # K not a whole number of 64-k tiles
     # above 64 rows with at least 16 column blocks of 256: the tiled matrix-core
-    # kernel (FP8 / BF16: 4 wavefronts up to 256 rows, then 8 of 128-row
-    # tiles; W4A16: 8)
+    # kernel (FP8 / BF16: 4 wavefronts on 64-row tiles or 8 on 256-row tiles,
+    # whichever the time model puts faster; W4A16: 8)
     assert wqd.kernel_path("bf16", 65, 8192, 8192) == ("gemm", 4)
     assert wqd.kernel_path("fp8", 128, 4096, 8192) == ("gemm", 4)
     for fmt in ("fp8", "bf16"):
         assert wqd.kernel_path(fmt, 256, 8192, 8192) == ("gemm", 4)
-        assert wqd.kernel_path(fmt, 257, 8192, 8192) == ("gemm", 8)
-    assert wqd.kernel_path("fp8", 1024, 28672, 8192) == ("gemm", 8)
+        assert wqd.kernel_path(fmt, 257, 8192, 8192) == ("gemm", 4)   # a 5th 64-row block, no 2nd 256-row round
+        assert wqd.kernel_path(fmt, 512, 4096, 4096) == ("gemm", 4)   # 256-row tiles: too few workgroups
+    assert wqd.kernel_path("bf16", 129, 8192, 8192) == ("gemm", 8)    # 256-row tiles with an 8-way K split
+    assert wqd.kernel_path("bf16", 1024, 28672, 8192) == ("gemm", 8)
+    assert wqd.kernel_path("fp8", 1024, 28672, 8192) == ("gemm", 4)
     for M in (65, 1024):
         assert wqd.kernel_path("w4a16", M, 8192, 8192) == ("gemm", 8)
     # otherwise above 64 rows (N under 16 x 256): the LDS matrix-core kernel
