@@ -12,14 +12,19 @@ It computes, plainly and slowly, what the decode linear layer computes:
 * ``quant``:   the three weight formats (bf16, FP8-E4M3 + per-row fp32 scale,
   W4A16 = uint4 codes in groups of 128 with an fp16 scale and a uint4 zero
   point) and their exact dequantisation;
-* ``gemm``:    y = x . dequant(W)^T in float64, rounded once to bf16.
+* ``gemm``:    y = x . dequant(W)^T in float64, rounded once to bf16;
+* ``spec``:    the speculative-sampling accept / reject step over the verify
+  pass's target and draft distributions.
 
 Pins (tests marked ``not gpu``): exhaustive E4M3 decode against its closed
 form and against the printed maximum 448; a brute-force nearest-value encoder;
 bf16/fp16 rounding against torch's and numpy's conversions and hand-built
 boundary cases; W4A16 codes against a brute-force argmin over the 16 grid
 points; the products against exact rational arithmetic on tiny shapes and
-against special cases (integer matmul, identity, zero).  No function here is
+against special cases (integer matmul, identity, zero); the accept / reject
+step against the pages' worked three-token example, the theorem that its output
+is distributed as the target (integrated over a grid of the uniforms), a
+pure-Python inverse-CDF walk and its special cases.  No function here is
 "parity unpinned".
 """
 from .formats import (  # noqa: F401
@@ -46,3 +51,4 @@ from .quant import (  # noqa: F401
     quantize_w4a16,
     w4a16_group_params,
 )
+from .spec import accept, draw_units, inverse_cdf_draw, spec_accept, spec_accept_one  # noqa: F401

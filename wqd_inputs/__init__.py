@@ -3,7 +3,7 @@
 This module is shared by the CPU oracle, the tests and the benchmark.  It holds
 no arithmetic of the method itself (no quantisation, no dequantisation, no
 matmul): it only draws random numbers and stores them in the types the layer
-consumes (activations as bfloat16, weights as float32).
+consumes (activations as bfloat16, weights as float32, probabilities as float32).
 
 Recipe (all draws seeded, nothing read from disk):
 
@@ -14,6 +14,9 @@ Recipe (all draws seeded, nothing read from disk):
   section on why outliers defeat plain INT8); then rounded to bfloat16
   (round-to-nearest-even, done by torch's dtype conversion).
 * weights ``W[N, K]``: float32 from N(0, sigma=0.02).
+* speculative accept / reject inputs: target rows softmax(N(0, 2.5) logits) over
+  V tokens, draft rows softmax of the same logits plus N(0, 1) noise, draft
+  tokens drawn from the draft rows, uniforms as multiples of 2^-24 in [0, 1).
 
 Host draws use numpy's PCG64; device draws use torch's CUDA generator.  The two
 streams differ for the same seed, so a test always takes one of them and moves
@@ -117,3 +120,33 @@ def stack_seed(cfg: int, layer: int, matrix: int) -> int:
 def x_seed(cfg: int, M: int, K: int) -> int:
     """Seed of the activation rows fed to every matrix with input width K."""
     return 1000 * cfg + M + 7919 * K
+
+
+def uniform_f32(rng, shape) -> np.ndarray:
+    """Uniform float32 numbers in [0, 1): multiples of 2^-24, so none rounds up to 1."""
+    return (rng.integers(0, 1 << 24, size=shape) / float(1 << 24)).astype(np.float32)
+
+
+def spec_inputs(seed: int, B: int, k: int, V: int, noise: float = 1.0, temp: float = 2.5):
+    """Inputs of the speculative accept / reject step for B sequences of k drafts.
+
+    Target rows: softmax of N(0, temp) logits over V tokens (float32), k + 1 per
+    sequence.  Draft rows: softmax of the same logits plus N(0, noise) (a cheap
+    model close to the target), k per sequence.  Draft tokens: drawn from the
+    draft rows.  Uniforms: u_accept [B, k] and v [B] in [0, 1).
+    """
+    rng = np.random.default_rng(seed)
+    logits = rng.normal(0.0, temp, size=(B, k + 1, V))
+
+    def softmax(z):
+        e = np.exp(z - z.max(axis=-1, keepdims=True))
+        return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+    target = softmax(logits)
+    draft = softmax(logits[:, :k] + rng.normal(0.0, noise, size=(B, k, V)))
+    tokens = np.zeros((B, k), dtype=np.int32)
+    for b in range(B):
+        for i in range(k):
+            p = draft[b, i].astype(np.float64)
+            tokens[b, i] = rng.choice(V, p=p / p.sum())
+    return target, draft, tokens, uniform_f32(rng, (B, k)), uniform_f32(rng, (B,))
