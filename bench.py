@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the measured HBM (and, for M >= 16, matrix-core) ceilings")
     ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape timing breakdown")
+    ap.add_argument("--spec", action="store_true",
+                    help="also time the speculative accept / reject step (64 sequences x 4 drafts, 128256-token vocabulary)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run 8 x 1 GiB copies and 16 launches of the dominant kernel, then exit")
     return ap.parse_args()
@@ -378,6 +380,36 @@ def time_stack(wl, args, with_shapes):
     return ms, not args.no_graph, shapes
 
 
+def spec_accept_timing(B=64, k=4, V=128256, reps=50):
+    """The accept / reject step after a verify pass of k + 1 positions: HIP-event
+    time per launch and its algorithmic bytes (the accept tests' few values,
+    then one target row per sequence, plus its draft row where a draft was
+    rejected, read once)."""
+    import numpy as np
+    import torch
+
+    import weight_only_quantized_decode_amd as wqd
+    import wqd_inputs as I
+
+    log(f"[bench] speculative accept / reject: B={B} k={k} V={V}")
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).to("cuda") for a in I.spec_inputs(5, B, k, V)]
+    n, _ = wqd.spec_accept(*dev)
+    torch.cuda.synchronize()
+    n = n.cpu().numpy()
+    rows = int(np.sum(np.where(n < k, 2, 1)))
+    algo = rows * V * 4 + B * k * 16 + B * 4 + B * (k + 2) * 4
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        wqd.spec_accept(*dev)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    gbps = algo / (us * 1e-6) / 1e9
+    return {"B": B, "k": k, "V": V, "mean_kept": round(float(n.mean()), 3), "us_per_launch": round(us, 2),
+            "algorithmic_bytes": algo, "GBps": round(gbps, 1), "roofline_frac_hbm": round(gbps / 8000.0, 4)}
+
+
 def main():
     args = parse()
     args.fused = not args.separate
@@ -467,6 +499,8 @@ def main():
             log(f"[bench] matrix-core ceiling: {peak:.0f} TFLOP/s")
             out["mfma_ceiling_TFLOPs"] = round(peak, 1)
             out["mfma_util_pct_measured_ceiling"] = round(100 * tflops / peak, 2)
+    if args.spec:
+        out["spec_accept"] = spec_accept_timing()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl)

@@ -190,6 +190,36 @@ int wqd_unpack(int fmt, const void* w_packed, const void* scales, const void* ze
 int wqd_decode_e4m3(const uint8_t* codes, float* out, int64_t n, void* stream);
 
 /*
+ * Speculative-sampling accept / reject, the step after the verify pass (CS336
+ * lecture 10 notes, section 6.1, the four steps; section 6.2, why the output
+ * is an exact sample of the target).  For each of B sequences, with
+ *   target       device float32 [B, k+1, V]: the target's distributions at the
+ *                k + 1 verified positions (probabilities in [0, 1]);
+ *   draft        device float32 [B, k, V]: the draft's distributions;
+ *   draft_tokens device int32 [B, k]: the drafted tokens;
+ *   u_accept     device float32 [B, k], u_draw device float32 [B]: the
+ *                uniform numbers in [0, 1) the method draws, supplied by the
+ *                caller;
+ * draft token x_i is kept, left to right, while u_accept * draft_i(x_i) <
+ * target_i(x_i) in float32 (u < min(1, target / draft); an out-of-range token
+ * is rejected).  At the first rejection, position i, one token is drawn from
+ * max(target_i - draft_i, 0) normalised; if every draft is kept, from
+ * target_k.  A draw counts each weight in units of 2^-32 (floor(w * 2^32),
+ * exact integers), takes U = floor(u_draw * T) with T the sum (the product
+ * in double), and returns the smallest token whose prefix sum exceeds U.
+ * An empty residual draws from target_i; an all-zero row draws -1.
+ * Outputs (device, caller-owned): n_kept int32 [B] (0 .. k) and out_tokens
+ * int32 [B, k+1]: the kept drafts, the drawn token, then -1.  draft,
+ * draft_tokens and u_accept may be NULL when k = 0.  Deterministic; all
+ * arrays contiguous row-major, 4-byte aligned.
+ * Errors: WQD_E_ARG (NULL pointer, B < 1, k < 0, V < 1), WQD_E_SHAPE (k > 64,
+ * V > 2^20), WQD_E_ALIGN.
+ */
+int wqd_spec_accept(const float* target, const float* draft, const int32_t* draft_tokens,
+                    const float* u_accept, const float* u_draw, int64_t B, int64_t k, int64_t V,
+                    int32_t* n_kept, int32_t* out_tokens, void* stream);
+
+/*
  * Measurement: read `bytes` (multiple of 16) from device `src` with 16-byte
  * loads and write one 32-bit checksum per workgroup to `sink` (device,
  * >= wqd_stream_sink_words(bytes) words).  The HBM read ceiling.

@@ -225,3 +225,23 @@ def test_other_entry_points_reject_bad_arguments():
     # 512 workgroups x 8 wavefronts x 16 multiplies of 16 x 16 x 32 per iteration
     assert L.wqd_mfma_peak_flops(3) == 3 * 512 * 8 * 16 * (2 * 16 * 16 * 32)
     assert L.wqd_mfma_peak_flops(0) == 0.0
+
+
+def test_spec_accept_rejects_bad_arguments():
+    """Validation happens before any device work (no GPU needed)."""
+    L = wqd.lib()
+    A = 0x10000
+    args = [A, A, A, A, A, 4, 3, 100, A, A, None]  # target, draft, tokens, u_accept, u_draw, B, k, V, n, out
+
+    def call(**kw):
+        a = list(args)
+        names = ["target", "draft", "tokens", "u_accept", "u_draw", "B", "k", "V", "n", "out"]
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return L.wqd_spec_accept(*a)
+
+    for key in ("target", "draft", "tokens", "u_accept", "u_draw", "n", "out"):
+        assert call(**{key: None}) == E_ARG, key
+    assert call(B=0) == E_ARG and call(k=-1) == E_ARG and call(V=0) == E_ARG
+    assert call(k=65) == E_SHAPE and call(V=(1 << 20) + 1) == E_SHAPE
+    assert call(target=A + 2) == E_ALIGN and call(out=A + 1) == E_ALIGN

@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
             "wqd_dequant": (i32, [i32, vp, vp, vp, i64, i64, vp, vp]),
             "wqd_unpack": (i32, [i32, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
             "wqd_decode_e4m3": (i32, [vp, vp, i64, vp]),
+            "wqd_spec_accept": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]),
             "wqd_stream_read": (i32, [vp, sz, vp, vp]),
             "wqd_stream_sink_words": (sz, [sz]),
             "wqd_stream_copy": (i32, [vp, vp, sz, vp]),
@@ -255,6 +256,30 @@ def decode_e4m3(codes, stream=None):
     _check(lib().wqd_decode_e4m3(codes.data_ptr(), out.data_ptr(), codes.numel(), _stream(stream)),
            "wqd_decode_e4m3")
     return out
+
+
+def spec_accept(target, draft, draft_tokens, u_accept, u_draw, stream=None):
+    """Speculative accept / reject on the device (``wqd_spec_accept``).
+
+    target float32 [B, k+1, V], draft float32 [B, k, V], draft_tokens int32
+    [B, k], u_accept float32 [B, k], u_draw float32 [B], all contiguous on one
+    device.  Returns (n_kept int32 [B], out_tokens int32 [B, k+1]).
+    """
+    import torch
+
+    B, k1, V = target.shape
+    k = k1 - 1
+    want = ((target, torch.float32, (B, k1, V)), (draft, torch.float32, (B, k, V)),
+            (draft_tokens, torch.int32, (B, k)), (u_accept, torch.float32, (B, k)), (u_draw, torch.float32, (B,)))
+    for t, dt, shape in want:
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or t.device != target.device:
+            raise ValueError(f"spec_accept: expected a contiguous {dt} tensor of shape {shape} on {target.device}")
+    n_kept = torch.empty(B, dtype=torch.int32, device=target.device)
+    out = torch.empty((B, k1), dtype=torch.int32, device=target.device)
+    ptr = lambda t: t.data_ptr() if t.numel() else None  # noqa: E731
+    _check(lib().wqd_spec_accept(target.data_ptr(), ptr(draft), ptr(draft_tokens), ptr(u_accept), u_draw.data_ptr(),
+                                 B, k, V, n_kept.data_ptr(), out.data_ptr(), _stream(stream)), "wqd_spec_accept")
+    return n_kept, out
 
 
 def stream_read(buf, sink=None, stream=None):

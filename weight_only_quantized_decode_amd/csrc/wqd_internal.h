@@ -37,5 +37,8 @@ size_t stream_sink_words(size_t bytes);
 hipError_t launch_mfma_peak(int64_t iters, float* sink, hipStream_t st);
 size_t mfma_peak_sink_words();
 double mfma_peak_flops(int64_t iters);
+hipError_t launch_spec_accept(const float* target, const float* draft, const int32_t* tokens, const float* u_accept,
+                              const float* u_draw, int64_t B, int64_t k, int64_t V, int32_t* n_kept, int32_t* out,
+                              hipStream_t st);
 
 }  // namespace wqd
