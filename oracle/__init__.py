@@ -51,4 +51,4 @@ from .quant import (  # noqa: F401
     quantize_w4a16,
     w4a16_group_params,
 )
-from .spec import accept, draw_units, inverse_cdf_draw, spec_accept, spec_accept_one  # noqa: F401
+from .spec import accept, draw_units, inverse_cdf_draw, residual, spec_accept, spec_accept_one  # noqa: F401

@@ -61,6 +61,11 @@ def inverse_cdf_draw(units, v) -> int:
     return int(np.searchsorted(np.cumsum(units), U, side="right"))
 
 
+def residual(t_row, d_row) -> np.ndarray:
+    """max(t - d, 0) in float32: the weights of the draw after a rejection."""
+    return np.maximum(np.asarray(t_row, np.float32) - np.asarray(d_row, np.float32), np.float32(0))
+
+
 def accept(u, d_x, t_x) -> bool:
     """The accept test u < min(1, t/d) in float32 product form."""
     return bool(np.float32(u) * np.float32(d_x) < np.float32(t_x))
@@ -81,7 +86,7 @@ def spec_accept_one(target, draft, tokens, u_accept, v):
         if 0 <= x < V and accept(u_accept[i], draft[i, x], target[i, x]):
             out[i] = x
             continue
-        units = draw_units(np.maximum(target[i] - draft[i], np.float32(0)))
+        units = draw_units(residual(target[i], draft[i]))
         if units.sum() == 0:
             units = draw_units(target[i])
         out[i] = inverse_cdf_draw(units, v)

@@ -148,3 +148,29 @@ def test_special_cases():
     # k = 0: only the draw from t_0
     n, out = oracle.spec_accept_one(t[:1], np.zeros((0, V), np.float32), [], [], v)
     assert n == 0 and out.tolist() == [oracle.inverse_cdf_draw(oracle.draw_units(t[0]), v)]
+
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Plant plausible mistakes in the oracle's step and check that a pin fails for each."""
+    import oracle.spec as S
+
+    real_accept, real_draw, real_units, real_res = S.accept, S.inverse_cdf_draw, S.draw_units, S.residual
+    plants = [
+        # ratio inverted in the accept test: the page's acceptance 0.6 fails
+        ("accept", lambda u, d_x, t_x: bool(np.float32(u) * np.float32(t_x) < np.float32(d_x)), test_page_example_three_tokens),
+        # residual with the operands swapped: the output is no longer the target
+        ("residual", lambda t_row, d_row: real_res(d_row, t_row), test_page_example_three_tokens),
+        # inverse CDF one token early (first prefix sum >= the threshold)
+        ("inverse_cdf_draw", lambda units, v: int(np.searchsorted(np.cumsum(np.asarray(units, np.int64)),
+                                                                  int(np.floor(float(np.float32(v)) * int(np.sum(units)))), side="left")),
+         test_inverse_cdf_against_a_walk),
+        # units rounded up instead of down
+        ("draw_units", lambda w: np.ceil(np.asarray(w, np.float32).astype(np.float64) * S.UNIT).astype(np.int64), test_draw_units_exact),
+    ]
+    for name, bad, pin in plants:
+        monkeypatch.setattr(S, name, bad)
+        monkeypatch.setattr(oracle, name, bad)
+        with pytest.raises(AssertionError):
+            pin()
+        monkeypatch.undo()
+    assert (S.accept, S.inverse_cdf_draw, S.draw_units, S.residual) == (real_accept, real_draw, real_units, real_res)
