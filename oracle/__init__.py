@@ -14,7 +14,10 @@ It computes, plainly and slowly, what the decode linear layer computes:
   point) and their exact dequantisation;
 * ``gemm``:    y = x . dequant(W)^T in float64, rounded once to bf16;
 * ``spec``:    the speculative-sampling accept / reject step over the verify
-  pass's target and draft distributions.
+  pass's target and draft distributions;
+* ``bytes``:   the bytes a call or a step moves (codes, scales, zero points,
+  activations; KV cache per sequence) and the step's lower bound, as the
+  pages define them.
 
 Pins (tests marked ``not gpu``): exhaustive E4M3 decode against its closed
 form and against the printed maximum 448; a brute-force nearest-value encoder;
@@ -24,7 +27,11 @@ points; the products against exact rational arithmetic on tiny shapes and
 against special cases (integer matmul, identity, zero); the accept / reject
 step against the pages' worked three-token example, the theorem that its output
 is distributed as the target (integrated over a grid of the uniforms), a
-pure-Python inverse-CDF walk and its special cases.  No function here is
+pure-Python inverse-CDF walk and its special cases; the byte model against the
+byte counts and bounds the pages print (70e9 parameters in three formats, the
+KV cache of a 2,048-token sequence, the batch-1 and batch-32 floors, the CS336
+4096 x 4096 INT4 count); the FP8 dequantisation against the round-to-nearest
+error bound on the original weights.  No function here is
 "parity unpinned".
 """
 from .formats import (  # noqa: F401

@@ -123,6 +123,78 @@ def test_fp8_dequant_f32_single_rounding():
     assert np.abs(f32 - exact).max() <= np.abs(exact).max() * 2.0 ** -24
 
 
+def _e4m3_half_spacing(v):
+    """Half the spacing of the E4M3 grid around |v| (no E4M3 routine involved):
+    3 mantissa bits, so 2^(e-3) between neighbours in the binade [2^e, 2^(e+1))
+    for e >= -6, and the subnormal step 2^-9 below 2^-6."""
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = np.where(a >= 2.0 ** -6, 2.0 ** (e - 3), 2.0 ** -9)
+    return step / 2
+
+
+def _fp8_wide_rows(seed=91, N=24, K=320):
+    """Non-square W whose rows span very different magnitudes (distinct row scales)."""
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((N, K)).astype(np.float32)
+    mag = (2.0 ** rng.integers(-12, 6, size=N)) * rng.uniform(0.5, 1.0, size=N)
+    return (W * mag[:, None].astype(np.float32)).astype(np.float32)
+
+
+def check_fp8_dequant_error_bound(W, qw):
+    """Round to nearest on the scaled grid: |Wd - W| <= s_n x (half an E4M3
+    step at W / s_n + the float32 rounding of that quotient), element by
+    element, and the row's absolute maximum is hit to that bound with the
+    E4M3 maximum 448 (the per-row scale maps the row's largest weight to it)."""
+    Wd = oracle.dequant_exact(qw)
+    s = qw["scales"].astype(np.float64)
+    assert Wd.shape == W.shape and s.shape == (W.shape[0],)
+    v = W.astype(np.float64) / s[:, None]
+    bound = s[:, None] * (_e4m3_half_spacing(v) + np.abs(v) * 2.0 ** -24)
+    err = np.abs(Wd - W.astype(np.float64))
+    assert (err <= bound).all(), float((err / bound).max())
+    # round to nearest, not a looser rounding: somewhere the error is close to the bound
+    assert (err / bound).max() > 0.9
+    for n in range(W.shape[0]):
+        j = int(np.abs(W[n]).argmax())
+        assert abs(abs(Wd[n, j]) - 448 * s[n]) <= s[n] * 2.0 ** -20
+        assert abs(abs(float(W[n, j])) - 448 * s[n]) <= abs(float(W[n, j])) * 2.0 ** -22
+
+
+def test_fp8_dequant_error_bound_distinct_row_scales():
+    W = _fp8_wide_rows()
+    qw = oracle.quantize_fp8(W)
+    assert len(np.unique(qw["scales"])) == W.shape[0]
+    check_fp8_dequant_error_bound(W, qw)
+
+
+def test_fp8_dequant_bound_catches_planted_scale_mistakes(monkeypatch):
+    """Row scales reversed, or taken per column, must break the error bound."""
+    import oracle.quant as Q
+
+    W = _fp8_wide_rows()
+    real_scales = Q.fp8_row_scales
+
+    monkeypatch.setattr(Q, "fp8_row_scales", lambda A: real_scales(A)[::-1].copy())
+    with pytest.raises((AssertionError, ValueError)):
+        check_fp8_dequant_error_bound(W, Q.quantize_fp8(W))
+    monkeypatch.undo()
+
+    def column_scales(A):
+        a = np.abs(np.asarray(A, np.float32)).max(axis=0)
+        return np.where(a == 0, np.float32(1), a / np.float32(448)).astype(np.float32)
+
+    def quantize_by_column(A):
+        A = np.asarray(A, np.float32)
+        sc = column_scales(A)
+        return {"fmt": "fp8", "codes": oracle.e4m3_encode((A / sc[None, :]).astype(np.float32)), "scales": sc}
+
+    with pytest.raises((AssertionError, ValueError)):
+        check_fp8_dequant_error_bound(W, quantize_by_column(W))
+    monkeypatch.undo()
+    check_fp8_dequant_error_bound(W, Q.quantize_fp8(W))
+
+
 # ----------------------------------------------------------------- matmul
 def _brute_qgemm_bits(x_bits, qw):
     """Exact rational y = sum_k x * Wd, then nearest bf16 (ties to even), all by brute force."""
