@@ -9,16 +9,25 @@ results; 4 launches per layer instead of 7).  One step = every
 y = x . dequant(W)^T call of the stack, replayed from one HIP graph; the packed
 weights (~35.6 GB) are resident in HBM before timing starts, and the stack is
 far larger than the 256 MB last-level cache, so every step streams the
-weights from HBM.  The same stack in the separate layout (7 launches per
-layer) is timed in the same run and reported as "separate_layout".
+weights from HBM.
+
+The same run also reports, each from its own graph replays:
+  * "separate_layout": the same stack with 7 launches per layer;
+  * "targets": the rows the >= 80%-of-measured-bandwidth target names, the
+    W4A16 stack at M = 4 and 8 (the headline's packed weights, new x) and the
+    FP8-E4M3 stack at M = 1 and 8 (fused layout);
+  * "roofline": the dominant kernel (the launches of the step's costliest
+    kernel family, replayed on their own) against the 8 TB/s HBM peak;
+  * "cpu_baseline": the oracle on one full layer of the same workload on the
+    host cores, extrapolated to the stack.
 
 Prints ONE JSON line.  Options: --workload w4a16_70b | fp8_70b | bf16_7b |
 gemv4096 | verify:<fmt>:<mat>; --m (activation rows); --separate (time the
-separate layout as the headline); --no-alt (skip the other layout);
---pmc-probe (a short fixed launch sequence for hardware-counter runs).  A
-single-matrix workload (gemv4096, verify:...) is packed into identical copies
-making 1.2 GB and each call uses the next one, so that it too reads its
-weights from HBM; its step is one call.
+separate layout as the headline); --no-alt; --no-targets; --pmc-probe (a short
+fixed launch sequence for hardware-counter runs).  A single-matrix workload
+(gemv4096, verify:...) is packed into identical copies making 1.2 GB and each
+call uses the next one, so that it too reads its weights from HBM; its step is
+one call.
 """
 from __future__ import annotations
 
@@ -26,12 +35,14 @@ import argparse
 import json
 import os
 import platform
+import statistics
 import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor peak
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 MAT_INDEX = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "w": 0}
+TARGET_ROWS = (("w4a16", 4), ("w4a16", 8), ("fp8", 1), ("fp8", 8))
 
 
 def parse():
@@ -42,9 +53,9 @@ def parse():
     ap.add_argument("--workload", default="w4a16_70b")
     ap.add_argument("--m", type=int, default=1)
     ap.add_argument("--layers", type=int, default=None)
-    ap.add_argument("--fused", action="store_true", help="q/k/v and gate/up as one matrix each (the default)")
     ap.add_argument("--separate", action="store_true", help="q, k, v, gate, up as separate matrices")
     ap.add_argument("--no-alt", action="store_true", help="do not also time the other layout")
+    ap.add_argument("--no-targets", action="store_true", help="skip the target-row sub-records")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the measured HBM (and, for M >= 16, matrix-core) ceilings")
@@ -56,22 +67,29 @@ def parse():
     return ap.parse_args()
 
 
-def make_workload(args):
+def make_workload(name, fmt_m, layers, fused):
     from weight_only_quantized_decode_amd import workloads as WL
 
-    w = args.workload
-    if w == "w4a16_70b":
-        return WL.stack_70b("w4a16", args.m, args.layers or 80, args.fused)
-    if w == "fp8_70b":
-        return WL.stack_70b("fp8", args.m, args.layers or 80, args.fused)
-    if w == "bf16_7b":
-        return WL.stack_7b_bf16(args.m, args.layers or 32, args.fused)
-    if w == "gemv4096":
+    m = fmt_m
+    if name == "w4a16_70b":
+        return WL.stack_70b("w4a16", m, layers or 80, fused)
+    if name == "fp8_70b":
+        return WL.stack_70b("fp8", m, layers or 80, fused)
+    if name == "bf16_7b":
+        return WL.stack_7b_bf16(m, layers or 32, fused)
+    if name == "gemv4096":
         return WL.gemv_4096_w4a16()
-    if w.startswith("verify:"):
-        _, fmt, mat = w.split(":")
-        return WL.verify_matrix(fmt, mat, args.m)
-    raise SystemExit(f"unknown workload {w!r}")
+    if name.startswith("verify:"):
+        _, fmt, mat = name.split(":")
+        return WL.verify_matrix(fmt, mat, m)
+    raise SystemExit(f"unknown workload {name!r}")
+
+
+def with_m(wl, M):
+    """The same stack (same weights) driven by M activation rows."""
+    import dataclasses
+
+    return dataclasses.replace(wl, M=M, name=wl.name.replace(f"_m{wl.M}", f"_m{M}"))
 
 
 def log(msg):
@@ -106,7 +124,7 @@ def copies_for(wl):
     return max(2, math.ceil(COLD_BYTES / wl.weight_stream_bytes())) if wl.layers == 1 else 1
 
 
-def build_stack(wl):
+def pack_stack(wl):
     """Pack every weight matrix of the workload on the device (untimed setup).
 
     A single-matrix workload (one layer) is packed into as many identical
@@ -117,12 +135,10 @@ def build_stack(wl):
     import torch
 
     import weight_only_quantized_decode_amd as wqd
-    import wqd_inputs as I
 
     dev = torch.device("cuda", 0)
-    packed = []
     t0 = time.time()
-    copies = copies_for(wl)
+    packed = []
     for layer in range(wl.layers):
         row = []
         for name, N, K in wl.mats:
@@ -130,22 +146,128 @@ def build_stack(wl):
             row.append(wqd.pack_weights(wl.fmt, W))
             del W
         packed.append(row)
-    for _ in range(copies - 1):
-        packed.append([wqd.pack_weights(wl.fmt, weight_for(wl, 0, name, N, K, dev)) for name, N, K in wl.mats])
-        if layer % 10 == 0:
+        if layer % 20 == 19:
             torch.cuda.synchronize()
-            log(f"[bench] packed layer {layer}/{wl.layers} ({time.time() - t0:.1f}s)")
+            log(f"[bench] packed layer {layer + 1}/{wl.layers} ({time.time() - t0:.1f}s)")
+    for _ in range(copies_for(wl) - 1):
+        packed.append([wqd.pack_weights(wl.fmt, weight_for(wl, 0, name, N, K, dev)) for name, N, K in wl.mats])
     torch.cuda.synchronize()
+    return packed
+
+
+def stack_io(wl):
+    """x rows per input width, y per output width, and the largest workspace."""
+    import torch
+
+    import weight_only_quantized_decode_amd as wqd
+    import wqd_inputs as I
+
+    dev = torch.device("cuda", 0)
     xs, ys = {}, {}
     for name, N, K in wl.mats:
         if K not in xs:
-            xb = I.x_bf16(I.x_seed(wl.cfg, wl.M, K), wl.M, K, outliers=wl.outliers)
-            xs[K] = xb.to(dev)
+            xs[K] = I.x_bf16(I.x_seed(wl.cfg, wl.M, K), wl.M, K, outliers=wl.outliers).to(dev)
         if N not in ys:
             ys[N] = torch.empty((wl.M, N), dtype=torch.bfloat16, device=dev)
     need = max(wqd.workspace_bytes(wl.fmt, wl.M, N, K) for _, N, K in wl.mats)
-    ws = wqd.get_workspace(need, dev)
-    return packed, xs, ys, ws
+    return xs, ys, wqd.get_workspace(need, dev)
+
+
+def replay_timing(launch_all, stream, steps, warmup, use_graph=True):
+    """Capture launch_all() in one HIP graph (after an eager warm-up), replay it
+    `warmup` times untimed, then `steps` times between HIP events recorded on
+    the launch stream, one event before each replay and one after the last.
+    Returns (mean ms per replay over the steps, per-replay ms samples)."""
+    import torch
+
+    with torch.cuda.stream(stream):
+        launch_all()
+        torch.cuda.synchronize()
+        graph = None
+        if use_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                launch_all()
+        run = graph.replay if graph is not None else launch_all
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            run()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+    samples = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    total = ev[0].elapsed_time(ev[steps])
+    del graph
+    return total / steps, samples
+
+
+def kernel_group(wl, N, K):
+    import weight_only_quantized_decode_amd as wqd
+
+    return "%s(%d waves)" % wqd.kernel_path(wl.fmt, wl.M, N, K)
+
+
+def time_step(wl, packed, args, stream, dominant=False, shapes=False):
+    """Time the step of `wl` on its packed weights; optionally also the
+    dominant kernel family on its own and a per-matrix breakdown."""
+    import weight_only_quantized_decode_amd as wqd
+    from weight_only_quantized_decode_amd import workloads as WL
+
+    xs, ys, ws = stack_io(wl)
+    rows = len(packed) // wl.layers  # copies of a single matrix: one replay calls each once
+
+    def launches(only=None):
+        def go():
+            for row in packed:
+                for j, ((name, N, K), pw) in enumerate(zip(wl.mats, row)):
+                    if only is None or j in only:
+                        wqd.qgemm(xs[K], pw, y=ys[N], workspace=ws)
+        return go
+
+    log(f"[bench] {wl.name}: {wl.launches} launches/step, {wl.step_bytes() / 1e9:.3f} GB/step; "
+        f"timing {args.steps} steps")
+    ms, samples = replay_timing(launches(), stream, args.steps, args.warmup, not args.no_graph)
+    ms, samples = ms / rows, [s / rows for s in samples]
+    gbps = wl.step_bytes() / (ms / 1e3) / 1e9
+    res = {"workload": wl.name, "fmt": wl.fmt, "M": wl.M, "layers": wl.layers, "launches_per_step": wl.launches,
+           "ms_per_step": round(ms, 4), "GBps": round(gbps, 2),
+           "step_samples_ms": {"n": len(samples), "median": round(statistics.median(samples), 4),
+                               "min": round(min(samples), 4), "max": round(max(samples), 4)},
+           "kernels": sorted({kernel_group(wl, N, K) for _, N, K in wl.mats})}
+    if dominant:
+        groups = {}
+        for j, (_, N, K) in enumerate(wl.mats):
+            groups.setdefault(kernel_group(wl, N, K), []).append(j)
+        per = {}
+        for label, js in groups.items():
+            g_ms, _ = replay_timing(launches(set(js)), stream, args.steps, args.warmup, not args.no_graph)
+            n_launch = len(js) * len(packed)
+            g_bytes = len(packed) * sum(WL.call_bytes(wl.fmt, wl.M, wl.mats[j][1], wl.mats[j][2]) for j in js)
+            g_flops = len(packed) * sum(WL.call_flops(wl.M, wl.mats[j][1], wl.mats[j][2]) for j in js)
+            per[label] = {"matrices": [wl.mats[j][0] for j in js], "launches": n_launch, "ms": g_ms,
+                          "avg_launch_us": g_ms * 1e3 / n_launch, "bytes": g_bytes, "flops": g_flops}
+        res["groups"] = per
+    if shapes and wl.layers > 1:
+        out = {}
+        for j, (name, N, K) in enumerate(wl.mats):
+            s_ms, _ = replay_timing(launches({j}), stream, max(3, args.steps // 4), 1, not args.no_graph)
+            us = s_ms * 1e3 / wl.layers
+            b = WL.call_bytes(wl.fmt, wl.M, N, K)
+            out[name] = {"N": N, "K": K, "us": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1),
+                         "kernel": kernel_group(wl, N, K)}
+        res["shapes"] = out
+    del xs, ys, ws
+    return res
+
+
+def free_cache():
+    import torch
+
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def mfma_ceiling(iters=20000):
@@ -167,7 +289,8 @@ def mfma_ceiling(iters=20000):
 
 
 def hbm_ceiling(gib=4, reps=10):
-    """Measured HBM read and copy bandwidth (GB/s) with the library's stream kernels."""
+    """Measured HBM read and copy bandwidth (GB/s) with the library's stream
+    kernels: each the best of three timed runs of `reps` back-to-back launches."""
     import torch
 
     import weight_only_quantized_decode_amd as wqd
@@ -180,55 +303,23 @@ def hbm_ceiling(gib=4, reps=10):
     wqd.stream_copy(dst, buf[: n // 2])
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        wqd.stream_read(buf, sink)
-    e1.record()
-    torch.cuda.synchronize()
-    read = n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
-    e0.record()
-    for _ in range(reps):
-        wqd.stream_copy(dst, buf[: n // 2])
-    e1.record()
-    torch.cuda.synchronize()
-    copy = 2 * (n // 2) * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    read = copy = 0.0
+    for _ in range(3):
+        e0.record()
+        for _ in range(reps):
+            wqd.stream_read(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        read = max(read, n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9)
+        e0.record()
+        for _ in range(reps):
+            wqd.stream_copy(dst, buf[: n // 2])
+        e1.record()
+        torch.cuda.synchronize()
+        copy = max(copy, 2 * (n // 2) * reps / (e0.elapsed_time(e1) / 1e3) / 1e9)
     del buf, dst
-    torch.cuda.empty_cache()
+    free_cache()
     return read, copy
-
-
-def shape_breakdown(wl, packed, xs, ys, ws, stream):
-    """Per-matrix timing: each matrix type launched once per layer (every launch
-    on a different layer's weights, so HBM-cold), timed with events on the
-    launch stream."""
-    import torch
-
-    import weight_only_quantized_decode_amd as wqd
-    from weight_only_quantized_decode_amd import workloads as WL
-
-    out = {}
-    with torch.cuda.stream(stream):
-        for j, (name, N, K) in enumerate(wl.mats):
-            for layer in range(wl.layers):
-                wqd.qgemm(xs[K], packed[layer][j], y=ys[N], workspace=ws)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for layer in range(wl.layers):
-                wqd.qgemm(xs[K], packed[layer][j], y=ys[N], workspace=ws)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / wl.layers
-            b = WL.call_bytes(wl.fmt, wl.M, N, K)
-            out[name] = {"N": N, "K": K, "us": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1)}
-    return out
-
-
-def kernel_label(wl):
-    """Kernel family and waves per workgroup of every launch in the step."""
-    import weight_only_quantized_decode_amd as wqd
-
-    fams = sorted({"%s(%d waves)" % wqd.kernel_path(wl.fmt, wl.M, N, K) for _, N, K in wl.mats})
-    return f"{'+'.join(fams)} {wl.fmt} M={wl.M} (every launch of the timed step)"
 
 
 def profiled_traffic(wl):
@@ -255,27 +346,7 @@ def profiled_traffic(wl):
     return d["traffic_bytes_per_launch"]
 
 
-def cpu_baseline(wl):
-    """The oracle (as it stands) on a bounded sample of the same workload, on the host cores."""
-    import oracle
-    import wqd_inputs as I
-    from weight_only_quantized_decode_amd import workloads as WL
-
-    name, N, K = max(wl.mats, key=lambda m: m[1] * m[2]) if wl.layers == 1 else wl.mats[0]
-    if name in WL.FUSED_PARTS:  # time the first part of a fused matrix (the q matrix)
-        name = WL.FUSED_PARTS[name][0]
-        N = {n: Nn for n, Nn, _ in (I.LAYER_70B if K == 8192 else I.LAYER_7B)}[name]
-    W = I.w_host(I.stack_seed(wl.cfg, 0, MAT_INDEX.get(name, 0)), N, K)
-    qw = oracle.quantize(wl.fmt, W)
-    x = I.x_bf16_bits(I.x_seed(wl.cfg, wl.M, K), wl.M, K, outliers=wl.outliers)
-    reps, t_total = 0, 0.0
-    while t_total < 10.0 and reps < 50:
-        t0 = time.perf_counter()
-        oracle.qgemm_exact(x, qw)
-        t_total += time.perf_counter() - t0
-        reps += 1
-    per_call = t_total / reps
-    gbps = WL.call_bytes(wl.fmt, wl.M, N, K) / per_call / 1e9
+def host_description():
     try:
         from threadpoolctl import threadpool_info
 
@@ -289,15 +360,59 @@ def cpu_baseline(wl):
     except OSError:
         pass
     affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    desc = (f"host {model} ({platform.machine()}), {os.cpu_count()} logical CPUs, {affinity} in this "
+            f"process's affinity mask, BLAS threads {threads}")
+    return int(threads), desc
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle as it stands (exact dequantisation, float64 matmul, bf16
+    rounding: oracle.qgemm_ref) timed on the host cores on a bounded sample of
+    the same workload.  A stack is sampled as one full layer (every matrix of
+    the timed step, layer 0's weights) and extrapolated to all layers; a single
+    matrix is timed whole."""
+    import oracle
+    import wqd_inputs as I
+    from weight_only_quantized_decode_amd import workloads as WL
+
+    import numpy as np
+
+    t_setup = time.perf_counter()
+    mats = []
+    for name, N, K in wl.mats:
+        if name in WL.FUSED_PARTS:
+            shapes = {n: Nn for n, Nn, _ in (I.LAYER_70B if K == 8192 else I.LAYER_7B)}
+            W = np.concatenate([I.w_host(I.stack_seed(wl.cfg, 0, MAT_INDEX[p]), shapes[p], K)
+                                for p in WL.FUSED_PARTS[name]], axis=0)
+        else:
+            W = I.w_host(I.stack_seed(wl.cfg, 0, MAT_INDEX.get(name, 0)), N, K)
+        mats.append((oracle.quantize(wl.fmt, W), K))
+        del W
+    xs = {K: I.x_bf16_bits(I.x_seed(wl.cfg, wl.M, K), wl.M, K, outliers=wl.outliers) for _, K in mats}
+    setup_s = time.perf_counter() - t_setup
+    reps, t_total = 0, 0.0
+    while reps < 1 or (t_total < budget_s and reps < 50):
+        t0 = time.perf_counter()
+        for qw, K in mats:
+            oracle.qgemm_ref(xs[K], qw)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per_layer = t_total / reps
+    step_s = per_layer * wl.layers
+    gbps = wl.step_bytes() / step_s / 1e9
+    threads, host = host_description()
+    what = (f"one full layer ({len(mats)} matrices, layer 0) x {reps} passes, extrapolated x {wl.layers} layers"
+            if wl.layers > 1 else f"{reps} calls on one matrix")
     return {
-        "value": round(gbps, 3),
+        "value": round(gbps, 4),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{reps} calls of the float64 oracle (exact dequant, matmul, bf16 rounding) on one "
-                  f"{name} matrix {N}x{K} {wl.fmt}, M={wl.M}: {per_call * 1e3:.1f} ms per call; "
-                  f"host {model} ({platform.machine()}), {os.cpu_count()} logical CPUs, {affinity} in this "
-                  f"process's affinity mask, BLAS threads {threads}",
+        "ms_per_step": round(step_s * 1e3, 1),
+        "extrapolated": wl.layers > 1,
+        "sample": f"the float64 oracle (exact dequant, matmul, bf16 rounding) on {wl.name}: {what}; "
+                  f"{per_layer * 1e3:.1f} ms per layer ({t_total:.1f} s timed, {setup_s:.1f} s untimed "
+                  f"quantisation); {host}",
     }
 
 
@@ -332,54 +447,6 @@ def pmc_probe():
     print(json.dumps({"pmc_probe": "done", "copy_bytes_each": 2 << 30, "gemv_launches": 16, "N": N, "K": K}))
 
 
-def time_stack(wl, args, with_shapes):
-    """Build the packed stack of `wl`, replay its step args.steps times after
-    args.warmup untimed steps (HIP events on the launch stream) and free it.
-    Returns (ms per step, whether a graph was replayed, per-shape breakdown)."""
-    import torch
-
-    import weight_only_quantized_decode_amd as wqd
-
-    log(f"[bench] workload {wl.name}: {wl.launches} launches/step, {wl.step_bytes() / 1e9:.3f} GB/step")
-    packed, xs, ys, ws = build_stack(wl)
-    stream = torch.cuda.Stream()
-
-    # one graph replay runs every row of packed: the stack once, or each copy
-    # of a single matrix once (then the step time is the replay time / copies)
-    rows = len(packed) // wl.layers
-
-    def step():
-        for row in packed:
-            for (name, N, K), pw in zip(wl.mats, row):
-                wqd.qgemm(xs[K], pw, y=ys[N], workspace=ws)
-
-    with torch.cuda.stream(stream):
-        step()  # eager warm-up (also loads the kernels)
-        torch.cuda.synchronize()
-        graph = None
-        if not args.no_graph:
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                step()
-        run = graph.replay if graph is not None else step
-        for _ in range(args.warmup):
-            run()
-        torch.cuda.synchronize()
-        log(f"[bench] timing {args.steps} steps")
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps / rows
-    shapes = shape_breakdown(wl, packed, xs, ys, ws, stream) if with_shapes and wl.layers > 1 else None
-    del graph, packed, xs, ys, ws
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    return ms, not args.no_graph, shapes
-
-
 def spec_accept_timing(B=64, k=4, V=128256, reps=50):
     """The accept / reject step after a verify pass of k + 1 positions: HIP-event
     time per launch and its algorithmic bytes (the accept tests' few values,
@@ -410,9 +477,37 @@ def spec_accept_timing(B=64, k=4, V=128256, reps=50):
             "algorithmic_bytes": algo, "GBps": round(gbps, 1), "roofline_frac_hbm": round(gbps / 8000.0, 4)}
 
 
+def pct(v, ceil):
+    return None if not ceil else round(100 * v / ceil, 2)
+
+
+def roofline_of(wl, res):
+    """The dominant kernel: the kernel family whose launches, replayed on their
+    own, take the most time per step.  achieved = its algorithmic bytes (or
+    FLOPs) per launch / its average launch duration."""
+    label, g = max(res["groups"].items(), key=lambda kv: kv[1]["ms"])
+    per_launch_bytes = g["bytes"] / g["launches"]
+    per_launch_flops = g["flops"] / g["launches"]
+    avg_us = g["avg_launch_us"]
+    if per_launch_flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > per_launch_bytes / (HBM_PEAK_GBPS * 1e9):
+        tf = per_launch_flops / (avg_us / 1e6) / 1e12
+        r = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+    else:
+        a = per_launch_bytes / (avg_us / 1e6) / 1e9
+        r = {"bound": "hbm", "achieved": round(a, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": round(a / HBM_PEAK_GBPS, 4)}
+    r.update({"traffic": profiled_traffic(wl) if label.startswith("bcast") else None,
+              "kernel": f"{label} {wl.fmt} M={wl.M}: the {'/'.join(g['matrices'])} launches of every layer, "
+                        f"replayed on their own",
+              "avg_launch_us": round(avg_us, 3), "launches": g["launches"],
+              "bytes_per_launch": round(per_launch_bytes), "flops_per_launch": round(per_launch_flops),
+              "share_of_step": round(g["ms"] / res["ms_per_step"], 4)})
+    return r
+
+
 def main():
     args = parse()
-    args.fused = not args.separate
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this decode layer is measured on a single MI355X "
@@ -429,47 +524,51 @@ def main():
     if args.pmc_probe:
         pmc_probe()
         return
-    wl = make_workload(args)
+    fused = not args.separate
+    wl = make_workload(args.workload, args.m, args.layers, fused)
     ceiling = (None, None) if args.no_ceiling else hbm_ceiling()
     if ceiling[0]:
         log(f"[bench] HBM ceiling: read {ceiling[0]:.0f} GB/s, copy {ceiling[1]:.0f} GB/s")
-    ms, graph_used, shapes = time_stack(wl, args, with_shapes=not args.no_shapes)
+    stream = torch.cuda.Stream()
+
+    packed = pack_stack(wl)
+    head = time_step(wl, packed, args, stream, dominant=True, shapes=not args.no_shapes)
+    targets = []
+    is_stack = wl.layers > 1 and args.workload in ("w4a16_70b", "fp8_70b", "bf16_7b")
+    if is_stack and not args.no_targets and args.workload == "w4a16_70b" and fused:
+        for fmt, M in TARGET_ROWS:
+            if fmt == wl.fmt and M != wl.M:
+                targets.append(time_step(with_m(wl, M), packed, args, stream))
+    del packed
+    free_cache()
+
     alt = None
-    if not args.no_alt and wl.layers > 1 and args.workload in ("w4a16_70b", "fp8_70b", "bf16_7b"):
-        alt_args = argparse.Namespace(**vars(args))
-        alt_args.fused = not args.fused
-        alt_wl = make_workload(alt_args)
-        alt_ms, _, _ = time_stack(alt_wl, alt_args, with_shapes=False)
-        alt_gbps = alt_wl.step_bytes() / (alt_ms / 1e3) / 1e9
-        alt = {"workload": alt_wl.name, "launches_per_step": alt_wl.launches, "value": round(alt_gbps, 2),
-               "ms_per_step": round(alt_ms, 4), "kernel": kernel_label(alt_wl),
-               "pct_measured_read_ceiling": None if ceiling[0] is None else round(100 * alt_gbps / ceiling[0], 2)}
-    step_bytes = wl.step_bytes()
-    gbps = step_bytes / (ms / 1e3) / 1e9
-    per_launch_bytes = step_bytes / wl.launches
-    avg_launch_us = ms * 1e3 / wl.launches
-    achieved = per_launch_bytes / (avg_launch_us / 1e6) / 1e9
-    # the bound of the step: HBM bytes at the vendor bandwidth, or bf16
-    # matrix-core FLOPs at the vendor dense peak, whichever takes longer
-    flops_per_launch = wl.step_flops() / wl.launches
-    if flops_per_launch / (BF16_MFMA_PEAK_TFLOPS * 1e12) > per_launch_bytes / (HBM_PEAK_GBPS * 1e9):
-        tf = flops_per_launch / (avg_launch_us / 1e6) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": profiled_traffic(wl)}
-    else:
-        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(wl)}
-    roofline.update({"kernel": kernel_label(wl), "avg_launch_us": round(avg_launch_us, 3),
-                     "bytes_per_launch": round(per_launch_bytes), "flops_per_launch": round(flops_per_launch)})
-    graph = graph_used
+    if is_stack and not args.no_alt:
+        alt_wl = make_workload(args.workload, args.m, args.layers, not fused)
+        alt_packed = pack_stack(alt_wl)
+        alt = time_step(alt_wl, alt_packed, args, stream)
+        del alt_packed
+        free_cache()
+    if is_stack and not args.no_targets and args.workload == "w4a16_70b" and fused:
+        fp8_wl = make_workload("fp8_70b", 1, args.layers, True)
+        fp8_packed = pack_stack(fp8_wl)
+        for fmt, M in TARGET_ROWS:
+            if fmt == "fp8":
+                targets.append(time_step(with_m(fp8_wl, M), fp8_packed, args, stream))
+        del fp8_packed
+        free_cache()
+
+    ms = head["ms_per_step"]
+    gbps = head["GBps"]
+    roofline = roofline_of(wl, head)
     out = {
         "metric": "weight-stream GB/s (% of HBM peak) & us per layer-stack step, 70B W4A16/FP8/BF16",
-        "value": round(gbps, 2),
+        "value": gbps,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": ms,
         "us_per_step": round(ms * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -477,20 +576,30 @@ def main():
         "dtype": {"w4a16": "u4+bf16", "fp8": "e4m3+bf16", "bf16": "bf16"}[wl.fmt],
         "data": "synthetic",
         "config": {"workload": wl.name, "fmt": wl.fmt, "M": wl.M, "layers": wl.layers,
-                   "launches_per_step": wl.launches, "graph": graph, "fused": args.fused,
-                   "weight_copies": copies_for(wl),
-                   "algorithmic_bytes_per_step": step_bytes},
+                   "launches_per_step": wl.launches, "graph": not args.no_graph, "fused": fused,
+                   "weight_copies": copies_for(wl), "algorithmic_bytes_per_step": wl.step_bytes()},
+        "step_samples_ms": head["step_samples_ms"],
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "hbm_read_ceiling_GBps": None if ceiling[0] is None else round(ceiling[0], 1),
         "hbm_copy_ceiling_GBps": None if ceiling[1] is None else round(ceiling[1], 1),
-        "pct_measured_read_ceiling": None if ceiling[0] is None else round(100 * gbps / ceiling[0], 2),
-        "pct_measured_copy_ceiling": None if ceiling[1] is None else round(100 * gbps / ceiling[1], 2),
+        "pct_measured_read_ceiling": pct(gbps, ceiling[0]),
+        "pct_measured_copy_ceiling": pct(gbps, ceiling[1]),
         "roofline": roofline,
+        "kernel_groups": {k: {"matrices": v["matrices"], "launches": v["launches"],
+                              "avg_launch_us": round(v["avg_launch_us"], 3), "ms_replayed_alone": round(v["ms"], 4)}
+                          for k, v in head["groups"].items()},
     }
     if alt is not None:
-        out["separate_layout" if args.fused else "fused_layout"] = alt
-    if shapes is not None:
-        out["shapes"] = shapes
+        alt["pct_measured_read_ceiling"] = pct(alt["GBps"], ceiling[0])
+        out["separate_layout" if fused else "fused_layout"] = alt
+    if targets:
+        for t in targets:
+            t["pct_measured_read_ceiling"] = pct(t["GBps"], ceiling[0])
+            t["pct_measured_copy_ceiling"] = pct(t["GBps"], ceiling[1])
+            t["pct_hbm_peak"] = round(100 * t["GBps"] / HBM_PEAK_GBPS, 2)
+        out["targets"] = targets
+    if "shapes" in head:
+        out["shapes"] = head["shapes"]
     if wl.M >= 16:
         tflops = wl.step_flops() / (ms / 1e3) / 1e12
         out["mfma_util_pct"] = round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2)
@@ -504,6 +613,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"]["gpu_ms_per_step"] = ms
     print(json.dumps(out), flush=True)
 
 

@@ -48,9 +48,13 @@
  *                      All divisions float32, rint ties to even.
  *
  * Packed layout (private to the library; read it back only through
- * wqd_dequant / wqd_unpack): weights are stored in tiles of 64 output rows x
- * 4 KiB, so each lane of a 64-wide wavefront issues 16-byte loads that are
- * contiguous across the wavefront.  wqd_packed_sizes gives the buffer sizes.
+ * wqd_dequant / wqd_unpack): weights are stored in tiles of 16 output rows x
+ * 64 bytes of K (1 KiB: 32 bf16, 64 FP8 or 128 W4A16 codes per row), each row's
+ * 64 bytes split into four 16-byte slices, slice j of row r at byte
+ * (16 j + r) x 16.  Lane l of a 64-wide wavefront loads the 16 bytes at 16 l,
+ * so one wavefront load is the whole tile, contiguous, and the lane order is
+ * the B-operand order of the bf16 matrix-core multiply.  The tiles of a
+ * 16-row block are consecutive along K.  wqd_packed_sizes gives the sizes.
  */
 #ifndef WQD_H
 #define WQD_H
@@ -89,7 +93,8 @@ int wqd_last_hip_error(void);
 
 /*
  * Host-only: byte sizes of the three packed buffers for an N x K weight in
- * `fmt` (tiles padded to 64 rows and to whole K tiles).  scale_bytes and
+ * `fmt` (N padded to whole 16-row blocks and K to whole 1 KiB tiles; W4A16
+ * scales and zeros to whole sets of four groups).  scale_bytes and
  * zero_bytes are 0 where the format has none.  Any output pointer may be NULL.
  * Errors: WQD_E_ARG (fmt, N < 1, K < 1), WQD_E_SHAPE (K % 128 != 0 for W4A16,
  * K % 8 != 0 for the others).
@@ -142,9 +147,13 @@ int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* wa
 
 /*
  * Setup (not on the decode hot path): quantise W (device, float32 [N, K]
- * row-major, finite values) to `fmt` and write the packed weights, scales and
- * zero points (device buffers of the sizes wqd_packed_sizes gives; scales and
- * zeros may be NULL where the format has none).  Deterministic.
+ * row-major) to `fmt` and write the packed weights, scales and zero points
+ * (device buffers of the sizes wqd_packed_sizes gives; scales and zeros may be
+ * NULL where the format has none).  Deterministic.  W must be finite: the
+ * values are only read on the device, after the call has returned, so a NaN
+ * or infinity is not reported, and the codes, scales and zeros of a row (FP8)
+ * or group (W4A16) that holds one are unspecified (other rows and groups are
+ * unaffected).
  */
 int wqd_pack_weights(int fmt, const float* W, int64_t N, int64_t K,
                      void* w_packed, void* scales, void* zeros, void* stream);
@@ -155,9 +164,9 @@ int wqd_pack_weights(int fmt, const float* W, int64_t N, int64_t K,
  * Products are formed from exactly dequantised weights and accumulated in
  * float32 (each W4A16 group and each FP8 row scale applied in float32); y is
  * the float32 sum rounded to nearest even bfloat16.  M >= 1; any M is
- * accepted, M <= 8 takes the wavefront-per-64-rows streaming kernel, larger M
- * the matrix-core kernel.  workspace: device, >= wqd_workspace_bytes bytes
- * (may be NULL when that is 0).
+ * accepted, and the kernel family that serves a shape is the one
+ * wqd_kernel_path names (see enum wqd_path).  workspace: device, >=
+ * wqd_workspace_bytes bytes (may be NULL when that is 0).
  */
 int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K,
               const void* w_packed, const void* scales, const void* zeros,
@@ -207,6 +216,10 @@ int wqd_decode_e4m3(const uint8_t* codes, float* out, int64_t n, void* stream);
  * target_k.  A draw counts each weight in units of 2^-32 (floor(w * 2^32),
  * exact integers), takes U = floor(u_draw * T) with T the sum (the product
  * in double), and returns the smallest token whose prefix sum exceeds U.
+ * U is kept below T: a u_draw of 1 or more (a generator whose range is
+ * (0, 1]) draws the last token of positive weight, a NaN or negative u_draw
+ * counts as 0.  A weight outside [0, 1] counts as the nearest end of that
+ * range and a NaN weight as 0.
  * An empty residual draws from target_i; an all-zero row draws -1.
  * Outputs (device, caller-owned): n_kept int32 [B] (0 .. k) and out_tokens
  * int32 [B, k+1]: the kept drafts, the drawn token, then -1.  draft,

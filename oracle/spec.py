@@ -30,7 +30,12 @@ Readings where the pages leave the arithmetic open:
   order of summation.  With T = sum W_j and U = floor(v * T) (the product in
   float64, rounded to nearest), the drawn token is the smallest j whose prefix
   sum W_0 + .. + W_j exceeds U: the inverse of the cumulative distribution.
-  Mass below 2^-32 per token is dropped (at most V * 2^-32 in total);
+  Mass below 2^-32 per token is dropped (at most V * 2^-32 in total).  U is
+  kept below T: a v of 1 or more (a generator whose range is (0, 1]) draws
+  the last token of positive weight, and a NaN or negative v counts as 0.  A
+  weight outside [0, 1] counts as the nearest end of that range, a NaN weight
+  as 0 (probabilities are in [0, 1]; this only fixes what malformed input
+  gives);
 * a residual whose units sum to zero (the rejected draft had no mass under
   either distribution, and the two agree everywhere else) draws from t_i
   instead; a row of all-zero target units draws token -1.
@@ -48,6 +53,7 @@ UNIT = 2.0 ** 32
 def draw_units(w) -> np.ndarray:
     """Integer weights W_j = floor(w_j * 2^32) of float32 weights w >= 0."""
     w = np.asarray(w, dtype=np.float32)
+    w = np.clip(np.where(np.isnan(w), np.float32(0), w), 0, 1)
     return np.floor(w.astype(np.float64) * UNIT).astype(np.int64)
 
 
@@ -57,7 +63,10 @@ def inverse_cdf_draw(units, v) -> int:
     T = int(units.sum())
     if T == 0:
         return -1
-    U = int(np.floor(np.float64(np.float32(v)) * np.float64(T)))
+    v = np.float32(v)
+    p = np.float64(v) if v > 0 else np.float64(0)
+    f = np.floor(p * np.float64(T))
+    U = T - 1 if f >= T else int(f)
     return int(np.searchsorted(np.cumsum(units), U, side="right"))
 
 

@@ -26,12 +26,16 @@ def test_stream_read_checksums():
     assert got.tolist() == [int(w) for w in want]
 
 
-def test_stream_copy():
-    src = torch.randint(-2**31, 2**31 - 1, ((1 << 20) + 12,), dtype=torch.int32, device="cuda")
-    dst = torch.zeros_like(src)
+@pytest.mark.parametrize("words", [(1 << 20) + 12, (16 << 20) + 12])
+def test_stream_copy(words):
+    # the larger size runs the 8-loads-in-flight loop and a ragged remainder in
+    # every workgroup; nothing past the end is written
+    src = torch.randint(-2**31, 2**31 - 1, (words,), dtype=torch.int32, device="cuda")
+    dst = torch.full((words + 64,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
     wqd.stream_copy(dst, src)
     torch.cuda.synchronize()
-    assert torch.equal(dst, src)
+    assert torch.equal(dst[:words], src)
+    assert (dst[words:] == 0x5A5A5A5A).all()
 
 
 def test_mfma_peak():

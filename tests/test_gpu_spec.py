@@ -55,3 +55,21 @@ def test_spec_accept_degenerate_cases():
     t0, _, _, _, v0 = I.spec_inputs(78, 5, 1, 300)
     check(t0[:, :1], np.zeros((5, 0, 300), np.float32), np.zeros((5, 0), np.int32),
           np.zeros((5, 0), np.float32), v0, "k=0")
+
+
+def test_spec_accept_uniform_range_ends_and_zero_rows():
+    """u_draw at 1 (a (0, 1] generator), above 1, NaN and 0; an all-zero target
+    row after every draft is kept (token -1); NaN and out-of-range weights."""
+    B, k, V = 8, 2, 1500
+    t, d, x, u, v = I.spec_inputs(79, B, k, V)
+    t = t.copy(); d = d.copy(); v = v.copy()
+    v[0], v[1], v[2], v[3] = 1.0, 1.25, np.nan, 0.0
+    d[4] = t[4, :k]; t[4, k] = 0.0              # every draft kept, then an all-zero row: -1
+    d[5] = t[5, :k]; t[5, k] = 0.0; v[5] = 1.0
+    t[6, 0, 3] = np.nan; t[6, 0, 9] = 1.5       # malformed weights count as clamped
+    d[6, 0, 5] = np.nan
+    n, out = run(t, d, x, u, v)
+    n_ref, out_ref = oracle.spec_accept(t, d, x, u, v)
+    assert np.array_equal(n, n_ref) and np.array_equal(out, out_ref), (n, n_ref, out, out_ref)
+    assert out[4, k] == -1 and out[5, k] == -1
+    assert (out[:, :] >= -1).all() and (out < V).all()

@@ -113,6 +113,23 @@ def test_inverse_cdf_against_a_walk():
             assert got == j and units[got] > 0, (units, v, got, j)
 
 
+def test_draw_at_the_ends_of_the_uniform_range():
+    # u = 1 (a generator whose range is (0, 1]) and anything above it draws the
+    # last token of positive weight; NaN or a negative u draws like u = 0
+    units = np.array([0, 3, 0, 5, 2, 0, 0], dtype=np.int64)
+    for v in (1.0, 1.5, np.inf):
+        assert oracle.inverse_cdf_draw(units, v) == 4
+    for v in (np.nan, -0.25, 0.0):
+        assert oracle.inverse_cdf_draw(units, v) == 1
+    assert oracle.inverse_cdf_draw(units, 1 - 2.0 ** -24) == 4
+    assert oracle.inverse_cdf_draw(np.zeros(5, np.int64), 1.0) == -1
+
+
+def test_malformed_weights_count_as_clamped():
+    w = np.array([np.nan, -0.5, 2.0, 0.25], dtype=np.float32)
+    assert oracle.draw_units(w).tolist() == [0, 0, 1 << 32, 1 << 30]
+
+
 def test_draw_units_exact():
     w = np.array([0.0, 2.0 ** -32, 2.0 ** -33, 0.5, 1.0, 0.1], dtype=np.float32)
     units = oracle.draw_units(w)
@@ -145,6 +162,11 @@ def test_special_cases():
     # out-of-range draft token: rejected
     n, out = oracle.spec_accept_one(t, t[:k], np.array([V, 0, 0]), u, v)
     assert n == 0
+    # an all-zero target row (every draft kept): token -1, whatever u
+    t4 = t.copy(); t4[k] = 0.0
+    for vv in (v, np.float32(1.0)):
+        n, out = oracle.spec_accept_one(t4, t4[:k], x, u, vv)
+        assert n == k and out[k] == -1
     # k = 0: only the draw from t_0
     n, out = oracle.spec_accept_one(t[:1], np.zeros((0, V), np.float32), [], [], v)
     assert n == 0 and out.tolist() == [oracle.inverse_cdf_draw(oracle.draw_units(t[0]), v)]

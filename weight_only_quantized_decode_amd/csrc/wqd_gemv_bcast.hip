@@ -5,12 +5,13 @@
 // 16-row block over all of K, W wavefronts on contiguous shares of K, fixed
 // order reductions), but x never goes through LDS.  In a packed tile, the 16
 // lanes of one DPP row (kb fixed, n = 0..15) all multiply the same k-slice,
-// and a slice holds at most 16 dwords of x (32 bf16).  So one 32-bit x
-// register per tile covers the whole tile: lane (kb, j) holds dword j of
-// slice kb, loaded straight from L2 as one coalesced 256-byte read per
-// wavefront, and `row_newbcast:j` hands dword j to every lane of the row as
-// the first operand of v_dot2c_f32_bf16.  The DPP row broadcast exists on
-// gfx90a and later.
+// and a slice holds at most 16 dwords of x (32 bf16).  So one x register per
+// one to four tiles covers them: for W4A16 and FP8 a 64-bit register, lane
+// (kb, j) holding dwords 2j, 2j + 1 of a slice (8 lanes per W4A16 slice, 4
+// per FP8 slice), for BF16 a 32-bit one (dword j, 4 lanes per slice), loaded
+// straight from L2 as one coalesced read per wavefront.  A DPP row broadcast
+// (row_newbcast:j, gfx90a and later) hands lane j's value to every lane of
+// the row, where it feeds v_dot2c_f32_bf16.
 //
 // Why: the weights are read once per step, so the bandwidth is set by bytes
 // in flight per compute unit.  Without the staged x (registers for the
@@ -25,19 +26,13 @@
 // n, 16 + n of its wavefront's share (at most 32 tiles), and the correction
 // reads it back with the same row broadcast (v_fmac_f32 with DPP on X).
 //
-// DPP wait states.  The DPP instructions live in inline assembly, where the
-// compiler's hazard tracking cannot see them, so each block keeps its own
-// distances.  Measured on gfx950 (shorter distances gave wrong results,
-// intermittently and with no error):
-//  * a VALU write to a register read through DPP needs two wait states: every
-//    block's first instructions do not write the broadcast register, or it
-//    starts with s_nop 1;
-//  * after a DPP v_dot2c / v_fmac, the next ordinary VALU instructions must
-//    not touch its result or its operands at once (a read of the result one
-//    wait state later missed the last products; a temporary rewritten two
-//    instructions after its DPP read was read in its new state).  A DPP
-//    successor accumulating into the same register may follow at once.  So
-//    every block ends with s_nop: 1 after a word, 4 after a tile's last block.
+// DPP.  The row broadcast is a compiler builtin (a v_mov_b32 with the
+// row_newbcast control) feeding ordinary dot2 / fma builtins, so the
+// compiler's hazard recognizer inserts the wait states around it: gfx950 has
+// no folded DPP form of v_dot2c_f32_bf16 that the compiler would form, so
+// each broadcast dword costs one move.
+#include <type_traits>
+
 #include "wqd_device.h"
 #include "wqd_internal.h"
 #include "wqd_plan.h"
@@ -59,15 +54,22 @@ struct BcC {
   static constexpr int TK = FMT == kFmtBF16 ? 32 : FMT == kFmtFP8 ? 64 : 128;  // K per tile
   static constexpr int SLK = TK / 4;                                             // K per slice
   static constexpr int DPS = SLK / 2;   // x dwords per slice: 16, 8, 4
-  static constexpr int TPX = 16 / DPS;  // tiles per x register: 1, 2, 4
+  // x register width in dwords: W4A16 and FP8 broadcast two dwords per move
+  // (v_mov_b64 with row_newbcast), BF16 one
+  static constexpr int XW = FMT == kFmtBF16 ? 1 : 2;
+  static constexpr int LPS = DPS / XW;  // lanes of a row holding one slice: 8, 4, 4
+  static constexpr int TPX = 16 / LPS;  // tiles per x register: 2, 4, 4
   static constexpr int GT = 4;          // tiles per group (a W4A16 scale quad)
-  static constexpr int XR = GT / TPX;   // x registers per activation row and group
+  static constexpr int XR = GT / TPX;   // x registers per activation row and group: 2, 1, 1
 };
+
+template <int FMT>
+using XReg = typename std::conditional<BcC<FMT>::XW == 2, uint64_t, uint32_t>::type;
 
 template <int FMT, int MR>
 struct BGroup {
   uint4 w[4];
-  uint32_t x[MR][BcC<FMT>::XR];
+  XReg<FMT> x[MR][BcC<FMT>::XR];
   uint2 s;     // W4A16: 4 fp16 scales of this lane's row, one per tile
   uint32_t z;  // W4A16: 4 zero nibbles
 };
@@ -92,16 +94,18 @@ __device__ __forceinline__ void bload(BGroup<FMT, MR>& g, const BcastArgs& a, __
   }
 #pragma unroll
   for (int r = 0; r < C::XR; ++r) {
-    const int tt = min(t0 + r * C::TPX + j / C::DPS, last);
-    const int64_t k = (kt_begin + tt) * C::TK + kb * C::SLK + 2 * (j % C::DPS);
+    // lane (kb, j): x dwords XW (j % LPS) .. + XW - 1 of slice kb of tile r TPX + j / LPS
+    const int tt = min(t0 + r * C::TPX + j / C::LPS, last);
+    const int64_t k = (kt_begin + tt) * C::TK + kb * C::SLK + 2 * C::XW * (j % C::LPS);
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       if (FMT == kFmtW4) {
-        g.x[m][r] = *reinterpret_cast<const uint32_t*>(a.x + int64_t(m) * a.K + k);
+        g.x[m][r] = *reinterpret_cast<const XReg<FMT>*>(a.x + int64_t(m) * a.K + k);
       } else {
-        const int64_t kc = k < a.K ? k : a.K - 2;
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(a.x + int64_t(m) * a.K + kc);
-        g.x[m][r] = k < a.K ? v : 0u;
+        // K is a multiple of 8, so a register's 2 XW elements are all below K or all past it
+        const int64_t kc = k < a.K ? k : a.K - 2 * C::XW;
+        const XReg<FMT> v = *reinterpret_cast<const XReg<FMT>*>(a.x + int64_t(m) * a.K + kc);
+        g.x[m][r] = k < a.K ? v : XReg<FMT>(0);
       }
     }
   }
@@ -112,100 +116,96 @@ __device__ __forceinline__ void bload(BGroup<FMT, MR>& g, const BcastArgs& a, __
   }
 }
 
-// ---- inline-assembly blocks (DPP operands) --------------------------------
+// ---- row broadcast (DPP) --------------------------------------------------
+
+// Dword J of `x` as held by lane J of each 16-lane row, handed to every lane of
+// that row (row_newbcast:J, DPP control 0x150 + J on gfx90a and later).  Plain
+// builtins, so the compiler sees the data movement and places the wait states
+// the hardware needs around it (a VALU write before the DPP read of its
+// result; a VALU read after a dot product's write).
+template <int J>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
+  static_assert(J >= 0 && J < 16, "a row has 16 lanes");
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x150 + J, 0xF, 0xF, false));
+}
+
+// Dwords 2J and 2J + 1 of a row's x (held by lane J) to every lane of the row:
+// one v_mov_b64 with row_newbcast:J.
+template <int J>
+__device__ __forceinline__ uint64_t row_bcast64(uint64_t x) {
+  static_assert(J >= 0 && J < 16, "a row has 16 lanes");
+  return __builtin_amdgcn_mov_dpp(x, 0x150 + J, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t lo32(uint64_t v) { return uint32_t(v); }
+__device__ __forceinline__ uint32_t hi32(uint64_t v) { return uint32_t(v >> 32); }
+
+template <int J>
+__device__ __forceinline__ float row_bcast_f(float x) {
+  return __builtin_bit_cast(float, row_bcast<J>(__builtin_bit_cast(uint32_t, x)));
+}
 
 // One packed W4A16 word (8 nibbles = 8 consecutive k of the slice) against x
-// dwords B .. B + 3 of the row broadcast: P += sum x (128 + q).  The first
-// broadcast read comes after seven VALU instructions that do not write x;
-// the block ends with s_nop 1 before anything else may touch P or the
-// temporaries.
-template <int B>
-__device__ __forceinline__ void w4_word(float& P, uint32_t w, uint32_t x, uint32_t mask, uint32_t magic) {
-  uint32_t t0, t1, t2, t3;
-  asm("v_lshrrev_b32 %[t1], 4, %[w]\n\t"
-      "v_lshrrev_b32 %[t2], 8, %[w]\n\t"
-      "v_lshrrev_b32 %[t3], 12, %[w]\n\t"
-      "v_and_or_b32 %[t0], %[w], %[mk], %[mg]\n\t"
-      "v_and_or_b32 %[t1], %[t1], %[mk], %[mg]\n\t"
-      "v_and_or_b32 %[t2], %[t2], %[mk], %[mg]\n\t"
-      "v_and_or_b32 %[t3], %[t3], %[mk], %[mg]\n\t"
-      "v_dot2c_f32_bf16_dpp %[p], %[x], %[t0] row_newbcast:%[b0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[p], %[x], %[t1] row_newbcast:%[b1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[p], %[x], %[t2] row_newbcast:%[b2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[p], %[x], %[t3] row_newbcast:%[b3] row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 1"
-      : [p] "+v"(P), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
-      : [w] "v"(w), [x] "v"(x), [mk] "v"(mask), [mg] "v"(magic), [b0] "n"(B), [b1] "n"(B + 1), [b2] "n"(B + 2),
-        [b3] "n"(B + 3));
+// dwords 2L .. 2L + 3 of the row (held by lanes L, L + 1): P += sum x (128 + q).
+template <int L>
+__device__ __forceinline__ void w4_word(float& P, uint32_t w, uint64_t x, uint32_t mask, uint32_t magic) {
+  const uint32_t t0 = and_or_v(w, mask, magic);
+  const uint32_t t1 = and_or_v(w >> 4, mask, magic);
+  const uint32_t t2 = and_or_v(w >> 8, mask, magic);
+  const uint32_t t3 = and_or_v(w >> 12, mask, magic);
+  const uint64_t xa = row_bcast64<L>(x), xb = row_bcast64<L + 1>(x);
+  P = dot2_bf16(as_bf16x2(lo32(xa)), as_bf16x2(t0), P);
+  P = dot2_bf16(as_bf16x2(hi32(xa)), as_bf16x2(t1), P);
+  P = dot2_bf16(as_bf16x2(lo32(xb)), as_bf16x2(t2), P);
+  P = dot2_bf16(as_bf16x2(hi32(xb)), as_bf16x2(t3), P);
 }
 
 // The same for two activation rows sharing the dequantised word.
-template <int B>
-__device__ __forceinline__ void w4_word2(float& P0, float& P1, uint32_t w, uint32_t x0, uint32_t x1, uint32_t mask,
+template <int L>
+__device__ __forceinline__ void w4_word2(float& P0, float& P1, uint32_t w, uint64_t x0, uint64_t x1, uint32_t mask,
                                          uint32_t magic) {
-  uint32_t t0, t1, t2, t3;
-  asm("v_lshrrev_b32 %[t1], 4, %[w]\n\t"
-      "v_lshrrev_b32 %[t2], 8, %[w]\n\t"
-      "v_lshrrev_b32 %[t3], 12, %[w]\n\t"
-      "v_and_or_b32 %[t0], %[w], %[mk], %[mg]\n\t"
-      "v_and_or_b32 %[t1], %[t1], %[mk], %[mg]\n\t"
-      "v_and_or_b32 %[t2], %[t2], %[mk], %[mg]\n\t"
-      "v_and_or_b32 %[t3], %[t3], %[mk], %[mg]\n\t"
-      "v_dot2c_f32_bf16_dpp %[p0], %[x0], %[t0] row_newbcast:%[b0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[p1], %[x1], %[t0] row_newbcast:%[b0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[p0], %[x0], %[t1] row_newbcast:%[b1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[p1], %[x1], %[t1] row_newbcast:%[b1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[p0], %[x0], %[t2] row_newbcast:%[b2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[p1], %[x1], %[t2] row_newbcast:%[b2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[p0], %[x0], %[t3] row_newbcast:%[b3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[p1], %[x1], %[t3] row_newbcast:%[b3] row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 1"
-      : [p0] "+v"(P0), [p1] "+v"(P1), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
-      : [w] "v"(w), [x0] "v"(x0), [x1] "v"(x1), [mk] "v"(mask), [mg] "v"(magic), [b0] "n"(B), [b1] "n"(B + 1),
-        [b2] "n"(B + 2), [b3] "n"(B + 3));
+  const uint32_t t[4] = {and_or_v(w, mask, magic), and_or_v(w >> 4, mask, magic), and_or_v(w >> 8, mask, magic),
+                         and_or_v(w >> 12, mask, magic)};
+  const uint64_t a0 = row_bcast64<L>(x0), b0 = row_bcast64<L + 1>(x0);
+  const uint64_t a1 = row_bcast64<L>(x1), b1 = row_bcast64<L + 1>(x1);
+  P0 = dot2_bf16(as_bf16x2(lo32(a0)), as_bf16x2(t[0]), P0);
+  P1 = dot2_bf16(as_bf16x2(lo32(a1)), as_bf16x2(t[0]), P1);
+  P0 = dot2_bf16(as_bf16x2(hi32(a0)), as_bf16x2(t[1]), P0);
+  P1 = dot2_bf16(as_bf16x2(hi32(a1)), as_bf16x2(t[1]), P1);
+  P0 = dot2_bf16(as_bf16x2(lo32(b0)), as_bf16x2(t[2]), P0);
+  P1 = dot2_bf16(as_bf16x2(lo32(b1)), as_bf16x2(t[2]), P1);
+  P0 = dot2_bf16(as_bf16x2(hi32(b0)), as_bf16x2(t[3]), P0);
+  P1 = dot2_bf16(as_bf16x2(hi32(b1)), as_bf16x2(t[3]), P1);
 }
 
-// P += X(broadcast from lane C of the row) * nz, where nz = -(128 + z).
+// P += X(from lane C of the row) * nz, where nz = -(128 + z).
 template <int C>
 __device__ __forceinline__ void fmac_bcast(float& P, float X, float nz) {
-  asm("s_nop 1\n\t"
-      "v_fmac_f32_dpp %[p], %[X], %[nz] row_newbcast:%[c] row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 4"
-      : [p] "+v"(P)
-      : [X] "v"(X), [nz] "v"(nz), [c] "n"(C));
+  P = fmaf(row_bcast_f<C>(X), nz, P);
 }
 
-// acc += sum over 8 dwords of x (broadcast from lanes B .. B + 7) * b[0..7].
-template <int B>
-__device__ __forceinline__ void dot8_bcast(float& acc, uint32_t x, const uint32_t (&b)[8]) {
-  asm("s_nop 1\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[b0] row_newbcast:%[c0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[b1] row_newbcast:%[c1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[b2] row_newbcast:%[c2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[b3] row_newbcast:%[c3] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[b4] row_newbcast:%[c4] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[b5] row_newbcast:%[c5] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[b6] row_newbcast:%[c6] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[b7] row_newbcast:%[c7] row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 4"
-      : [a] "+v"(acc)
-      : [x] "v"(x), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]), [b4] "v"(b[4]),
-        [b5] "v"(b[5]), [b6] "v"(b[6]), [b7] "v"(b[7]), [c0] "n"(B), [c1] "n"(B + 1), [c2] "n"(B + 2),
-        [c3] "n"(B + 3), [c4] "n"(B + 4), [c5] "n"(B + 5), [c6] "n"(B + 6), [c7] "n"(B + 7));
+// acc += sum over 8 dwords of x (from lanes L .. L + 3, two each) * b[0..7].
+template <int L>
+__device__ __forceinline__ void dot8_bcast(float& acc, uint64_t x, const uint32_t (&b)[8]) {
+  const uint64_t x0 = row_bcast64<L>(x), x1 = row_bcast64<L + 1>(x);
+  const uint64_t x2 = row_bcast64<L + 2>(x), x3 = row_bcast64<L + 3>(x);
+  acc = dot2_bf16(as_bf16x2(lo32(x0)), as_bf16x2(b[0]), acc);
+  acc = dot2_bf16(as_bf16x2(hi32(x0)), as_bf16x2(b[1]), acc);
+  acc = dot2_bf16(as_bf16x2(lo32(x1)), as_bf16x2(b[2]), acc);
+  acc = dot2_bf16(as_bf16x2(hi32(x1)), as_bf16x2(b[3]), acc);
+  acc = dot2_bf16(as_bf16x2(lo32(x2)), as_bf16x2(b[4]), acc);
+  acc = dot2_bf16(as_bf16x2(hi32(x2)), as_bf16x2(b[5]), acc);
+  acc = dot2_bf16(as_bf16x2(lo32(x3)), as_bf16x2(b[6]), acc);
+  acc = dot2_bf16(as_bf16x2(hi32(x3)), as_bf16x2(b[7]), acc);
 }
 
-// acc += sum over 4 dwords of x (broadcast from lanes B .. B + 3) * w[0..3].
+// acc += sum over 4 dwords of x (from lanes B .. B + 3) * w[0..3].
 template <int B>
 __device__ __forceinline__ void dot4_bcast(float& acc, uint32_t x, uint4 w) {
-  asm("s_nop 1\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[w0] row_newbcast:%[c0] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[w1] row_newbcast:%[c1] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[w2] row_newbcast:%[c2] row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_bf16_dpp %[a], %[x], %[w3] row_newbcast:%[c3] row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 4"
-      : [a] "+v"(acc)
-      : [x] "v"(x), [w0] "v"(w.x), [w1] "v"(w.y), [w2] "v"(w.z), [w3] "v"(w.w), [c0] "n"(B), [c1] "n"(B + 1),
-        [c2] "n"(B + 2), [c3] "n"(B + 3));
+  acc = dot2_bf16(as_bf16x2(row_bcast<B>(x)), as_bf16x2(w.x), acc);
+  acc = dot2_bf16(as_bf16x2(row_bcast<B + 1>(x)), as_bf16x2(w.y), acc);
+  acc = dot2_bf16(as_bf16x2(row_bcast<B + 2>(x)), as_bf16x2(w.z), acc);
+  acc = dot2_bf16(as_bf16x2(row_bcast<B + 3>(x)), as_bf16x2(w.w), acc);
 }
 
 // ---- per-tile arithmetic ---------------------------------------------------
@@ -217,9 +217,10 @@ __device__ __forceinline__ void btile(const BGroup<FMT, MR>& g, const float (&X)
   using C = BcC<FMT>;
   const uint4 wv = g.w[I];
   constexpr int R = I / C::TPX;               // x register of this tile
-  constexpr int B = (I % C::TPX) * C::DPS;    // first broadcast lane of its dwords
+  constexpr int B = (I % C::TPX) * C::LPS;    // first lane of the row holding its x
   if constexpr (FMT == kFmtW4) {
-    const uint32_t mask = 0x000F000Fu, magic = 0x43004300u;
+    // constants in VGPRs, so each nibble pair is one v_and_or_b32
+    const uint32_t mask = vgpr_const(0x000F000Fu), magic = vgpr_const(0x43004300u);
     const uint32_t sw = (I < 2 ? g.s.x : g.s.y) >> (16 * (I & 1));
     const float s = __half2float(__ushort_as_half(uint16_t(sw & 0xFFFFu)));
     const float nz = -(128.0f + float((g.z >> (4 * I)) & 0xFu));
@@ -227,15 +228,15 @@ __device__ __forceinline__ void btile(const BGroup<FMT, MR>& g, const float (&X)
 #pragma unroll
     for (int m = 0; m < MR; ++m) P[m] = 0.f;
     if constexpr (MR == 1) {
-      w4_word<0>(P[0], wv.x, g.x[0][R], mask, magic);
-      w4_word<4>(P[0], wv.y, g.x[0][R], mask, magic);
-      w4_word<8>(P[0], wv.z, g.x[0][R], mask, magic);
-      w4_word<12>(P[0], wv.w, g.x[0][R], mask, magic);
+      w4_word<B + 0>(P[0], wv.x, g.x[0][R], mask, magic);
+      w4_word<B + 2>(P[0], wv.y, g.x[0][R], mask, magic);
+      w4_word<B + 4>(P[0], wv.z, g.x[0][R], mask, magic);
+      w4_word<B + 6>(P[0], wv.w, g.x[0][R], mask, magic);
     } else {
-      w4_word2<0>(P[0], P[1], wv.x, g.x[0][R], g.x[1][R], mask, magic);
-      w4_word2<4>(P[0], P[1], wv.y, g.x[0][R], g.x[1][R], mask, magic);
-      w4_word2<8>(P[0], P[1], wv.z, g.x[0][R], g.x[1][R], mask, magic);
-      w4_word2<12>(P[0], P[1], wv.w, g.x[0][R], g.x[1][R], mask, magic);
+      w4_word2<B + 0>(P[0], P[1], wv.x, g.x[0][R], g.x[1][R], mask, magic);
+      w4_word2<B + 2>(P[0], P[1], wv.y, g.x[0][R], g.x[1][R], mask, magic);
+      w4_word2<B + 4>(P[0], P[1], wv.z, g.x[0][R], g.x[1][R], mask, magic);
+      w4_word2<B + 6>(P[0], P[1], wv.w, g.x[0][R], g.x[1][R], mask, magic);
     }
 #pragma unroll
     for (int m = 0; m < MR; ++m) {

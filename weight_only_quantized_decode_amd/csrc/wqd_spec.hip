@@ -29,8 +29,22 @@ static_assert(kSpecMaxTiles == 4 * kSpecThreads, "each thread scans four tile su
 
 typedef unsigned long long u64;
 
-// floor(w * 2^32): exact for float32 w in [0, 1] (scaling by 2^32 is exact in double).
-__device__ inline u64 draw_unit(float w) { return u64(floor(double(w) * 4294967296.0)); }
+// floor(w * 2^32): exact for float32 w in [0, 1] (scaling by 2^32 is exact in
+// double).  A weight outside [0, 1] counts as the nearest end of it, a NaN as
+// 0 (fmaxf returns its other operand), so the unit sum cannot overflow.
+__device__ inline u64 draw_unit(float w) {
+  w = fminf(fmaxf(w, 0.0f), 1.0f);
+  return u64(floor(double(w) * 4294967296.0));
+}
+
+// The draw's threshold floor(u * T) for T > 0, kept in [0, T - 1]: a u of 1 or
+// more (a generator with range (0, 1]) takes the last token of positive
+// weight, and a NaN or negative u counts as 0.
+__device__ inline u64 draw_threshold(float u, u64 T) {
+  const double p = u > 0.0f ? double(u) : 0.0;
+  const double f = floor(p * double(T));
+  return f >= double(T) ? T - 1 : u64(f);
+}
 
 __device__ inline u64 weight_at(const float* tr, const float* dr, int64_t j, int64_t V) {
   if (j >= V) return 0;
@@ -115,7 +129,7 @@ __global__ __launch_bounds__(kSpecThreads) void spec_accept_kernel(
       if (tid == 0) o[r] = -1;
       break;
     }
-    const u64 U = u64(floor(double(u_draw[b]) * double(T)));
+    const u64 U = draw_threshold(u_draw[b], T);
     const u64 base = wbase + incl - mine;
     if (base <= U && U < base + mine) {  // the one thread whose tiles hold the threshold
       u64 acc = base;

@@ -39,10 +39,24 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
   if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+// The copy has the read kernel's structure: one contiguous range per
+// workgroup, and per iteration 8 independent non-temporal 16-byte loads per
+// thread before their 8 non-temporal stores, so that 32 KiB per workgroup are
+// in flight in each direction.
 __global__ __launch_bounds__(256) void stream_copy_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
                                                           size_t n16) {
-  const size_t stride = size_t(gridDim.x) * 256;
-  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+  const size_t per_block = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t begin = size_t(blockIdx.x) * per_block;
+  const size_t end = begin + per_block < n16 ? begin + per_block : n16;
+  size_t i = begin + threadIdx.x;
+  for (; i + (kUnroll - 1) * 256 < end; i += kUnroll * 256) {
+    u32x4_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + i + u * 256));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4_t*>(dst + i + u * 256));
+  }
+  for (; i < end; i += 256) dst[i] = src[i];
 }
 
 size_t stream_sink_words(size_t bytes) {
