@@ -173,6 +173,32 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K,
               void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * product as wqd_qgemm, with the same arguments except the workspace.  The
+ * split-K partials and W4A16 group x sums go to a scratch array of
+ * WQD_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one copy
+ * per GPU, from the first call on that GPU until the process ends.  Nothing
+ * is allocated per call (no hipMalloc, no allocating library routine).
+ *   - The scratch address is looked up on the first call on each device (the
+ *     calling thread's current device, on which `stream` must be); the
+ *     lookup makes no stream call.
+ *   - Every call on one GPU shares that GPU's array: calls that can overlap
+ *     on one GPU (other streams, other threads) race and give undefined
+ *     results.  Consecutive calls on one stream are safe; the contents left
+ *     by a call never affect the next.
+ *   - Errors: as wqd_qgemm; WQD_E_WORKSPACE when the shape needs more than
+ *     WQD_NOALLOC_SCRATCH_BYTES of workspace (wqd_workspace_bytes gives the
+ *     need; every decode and verify width of the 70B and 7B shapes up to
+ *     1024 rows fits, except BF16 above 512 rows); WQD_E_HIP if the lookup
+ *     fails.
+ */
+#define WQD_NOALLOC_SCRATCH_BYTES (64u << 20)
+int wqd_qgemm_noalloc(int fmt, const void* x, int64_t M, int64_t N, int64_t K,
+                      const void* w_packed, const void* scales, const void* zeros,
+                      void* y, void* stream);
+
+/*
  * Parity: dequantised weights in logical order, W_out device float32 [N, K]
  * row-major.  bf16 and W4A16 values are exact; FP8 values are the float32
  * product e4m3(code) * s_n rounded once.

@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
             "wqd_kernel_path": (i32, [i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "wqd_pack_weights": (i32, [i32, vp, i64, i64, vp, vp, vp, vp]),
             "wqd_qgemm": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
+            "wqd_qgemm_noalloc": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]),
             "wqd_dequant": (i32, [i32, vp, vp, vp, i64, i64, vp, vp]),
             "wqd_unpack": (i32, [i32, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
             "wqd_decode_e4m3": (i32, [vp, vp, i64, vp]),
@@ -214,6 +215,25 @@ def qgemm(x, pw: PackedWeight, y=None, workspace=None, stream=None):
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().wqd_qgemm(_fmt(pw.fmt), x.data_ptr(), M, pw.N, K, _ptr(pw.w), _ptr(pw.scales), _ptr(pw.zeros),
                            y.data_ptr(), _ptr(workspace), wsb, _stream(stream)), "wqd_qgemm")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # WQD_NOALLOC_SCRATCH_BYTES
+
+
+def qgemm_noalloc(x, pw: PackedWeight, y, stream=None):
+    """wqd_qgemm_noalloc: y = x . dequant(W)^T with the library's per-GPU
+    scratch array instead of a workspace; allocates nothing (y is the
+    caller's).  Calls that can overlap on one GPU must not use it."""
+    import torch
+
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 [M, K] tensor")
+    M, K = x.shape
+    if K != pw.K or y.dtype != torch.bfloat16 or tuple(y.shape) != (M, pw.N) or not y.is_contiguous():
+        raise ValueError("x / y shapes do not match the packed weights")
+    _check(lib().wqd_qgemm_noalloc(_fmt(pw.fmt), x.data_ptr(), M, pw.N, K, _ptr(pw.w), _ptr(pw.scales),
+                                   _ptr(pw.zeros), y.data_ptr(), _stream(stream)), "wqd_qgemm_noalloc")
     return y
 
 

@@ -33,6 +33,46 @@ int check_packed_ptrs(int fmt, const void* wp, const void* scales, const void* z
 
 }  // namespace
 
+namespace wqd {
+
+int qgemm_checked(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const void* w_packed, const void* scales,
+                  const void* zeros, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 1) return WQD_E_ARG;
+  Choice c;
+  int st = choose_path(fmt, M, N, K, &c);
+  if (st != kOK) return st;
+  if (!x || !y) return WQD_E_ARG;
+  if (!aligned16(x) || !aligned16(y)) return WQD_E_ALIGN;
+  st = check_packed_ptrs(fmt, w_packed, scales, zeros);
+  if (st != WQD_OK) return st;
+  size_t need = 0;
+  st = wqd::workspace_bytes(fmt, M, N, K, &need);
+  if (st != kOK) return st;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return WQD_E_WORKSPACE;
+    if (!aligned16(workspace)) return WQD_E_ALIGN;
+  }
+  hipStream_t s = as_stream(stream);
+  switch (c.path) {
+    case kPathBcast:
+      return hip_status(launch_gemv_bcast(fmt, c.bcast, x, M, N, K, w_packed, scales, zeros, y, s));
+    case kPathMc:
+      return hip_status(launch_gemv_mc(fmt, c.mc, x, M, N, K, w_packed, scales, zeros, y, s));
+    case kPathStaged:
+      return hip_status(launch_gemv(fmt, c.gemv, x, M, N, K, w_packed, scales, zeros, y, s));
+    case kPathGemm:
+      return hip_status(launch_gemm(fmt, c.gm, x, M, N, K, w_packed, scales, zeros, y, workspace, s));
+    case kPathSkinny:
+      return hip_status(launch_gemv_sk(fmt, c.sk, x, M, N, K, w_packed, scales, zeros, y, workspace, s));
+    default:
+      return hip_status(launch_mfma(fmt, c.mfma, M, N, K, x, w_packed, scales, zeros, y, workspace, s));
+  }
+}
+
+int record_hip_error(hipError_t e) { return hip_status(e); }
+
+}  // namespace wqd
+
 extern "C" {
 
 int wqd_version(void) { return 100; }
@@ -98,36 +138,7 @@ int wqd_pack_weights(int fmt, const float* W, int64_t N, int64_t K, void* w_pack
 
 int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const void* w_packed, const void* scales,
               const void* zeros, void* y, void* workspace, size_t workspace_bytes, void* stream) {
-  if (M < 1) return WQD_E_ARG;
-  wqd::Choice c;
-  int st = wqd::choose_path(fmt, M, N, K, &c);
-  if (st != wqd::kOK) return st;
-  if (!x || !y) return WQD_E_ARG;
-  if (!wqd::aligned16(x) || !wqd::aligned16(y)) return WQD_E_ALIGN;
-  st = check_packed_ptrs(fmt, w_packed, scales, zeros);
-  if (st != WQD_OK) return st;
-  size_t need = 0;
-  st = wqd::workspace_bytes(fmt, M, N, K, &need);
-  if (st != wqd::kOK) return st;
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need) return WQD_E_WORKSPACE;
-    if (!wqd::aligned16(workspace)) return WQD_E_ALIGN;
-  }
-  hipStream_t s = as_stream(stream);
-  switch (c.path) {
-    case wqd::kPathBcast:
-      return hip_status(wqd::launch_gemv_bcast(fmt, c.bcast, x, M, N, K, w_packed, scales, zeros, y, s));
-    case wqd::kPathMc:
-      return hip_status(wqd::launch_gemv_mc(fmt, c.mc, x, M, N, K, w_packed, scales, zeros, y, s));
-    case wqd::kPathStaged:
-      return hip_status(wqd::launch_gemv(fmt, c.gemv, x, M, N, K, w_packed, scales, zeros, y, s));
-    case wqd::kPathGemm:
-      return hip_status(wqd::launch_gemm(fmt, c.gm, x, M, N, K, w_packed, scales, zeros, y, workspace, s));
-    case wqd::kPathSkinny:
-      return hip_status(wqd::launch_gemv_sk(fmt, c.sk, x, M, N, K, w_packed, scales, zeros, y, workspace, s));
-    default:
-      return hip_status(wqd::launch_mfma(fmt, c.mfma, M, N, K, x, w_packed, scales, zeros, y, workspace, s));
-  }
+  return wqd::qgemm_checked(fmt, x, M, N, K, w_packed, scales, zeros, y, workspace, workspace_bytes, stream);
 }
 
 int wqd_dequant(int fmt, const void* w_packed, const void* scales, const void* zeros, int64_t N, int64_t K,

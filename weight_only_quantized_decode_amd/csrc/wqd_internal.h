@@ -37,6 +37,11 @@ size_t stream_sink_words(size_t bytes);
 hipError_t launch_mfma_peak(int64_t iters, float* sink, hipStream_t st);
 size_t mfma_peak_sink_words();
 double mfma_peak_flops(int64_t iters);
+// wqd_qgemm after its argument checks (shared by the entry points that call it).
+int qgemm_checked(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const void* w_packed, const void* scales,
+                  const void* zeros, void* y, void* workspace, size_t workspace_bytes, void* stream);
+// Maps a HIP error to a wqd status, keeping it for wqd_last_hip_error().
+int record_hip_error(hipError_t e);
 hipError_t launch_spec_accept(const float* target, const float* draft, const int32_t* tokens, const float* u_accept,
                               const float* u_draw, int64_t B, int64_t k, int64_t V, int32_t* n_kept, int32_t* out,
                               hipStream_t st);
