@@ -15,6 +15,9 @@ It computes, plainly and slowly, what the decode linear layer computes:
 * ``gemm``:    y = x . dequant(W)^T in float64, rounded once to bf16;
 * ``spec``:    the speculative-sampling accept / reject step over the verify
   pass's target and draft distributions;
+* ``w8a8``:    the W8A8-FP8 variant: one dynamic E4M3 scale for the whole
+  activation tensor, activation codes, and the product of the two code
+  matrices (exact in float64) times both scales;
 * ``bytes``:   the bytes a call or a step moves (codes, scales, zero points,
   activations; KV cache per sequence) and the step's lower bound, as the
   pages define them.
@@ -31,7 +34,10 @@ pure-Python inverse-CDF walk and its special cases; the byte model against the
 byte counts and bounds the pages print (70e9 parameters in three formats, the
 KV cache of a 2,048-token sequence, the batch-1 and batch-32 floors, the CS336
 4096 x 4096 INT4 count); the FP8 dequantisation against the round-to-nearest
-error bound on the original weights.  No function here is
+error bound on the original weights; the W8A8 product against exact rationals,
+activation codes against a brute-force nearest E4M3 value, activations on the
+E4M3 grid reducing to the weight-only product, and the activation rounding
+bound.  No function here is
 "parity unpinned".
 """
 from .formats import (  # noqa: F401
@@ -58,4 +64,5 @@ from .quant import (  # noqa: F401
     quantize_w4a16,
     w4a16_group_params,
 )
+from .w8a8 import act_scale, qgemm_w8a8_exact, qgemm_w8a8_ref, quantize_act  # noqa: F401
 from .spec import accept, draw_units, inverse_cdf_draw, residual, spec_accept, spec_accept_one  # noqa: F401
