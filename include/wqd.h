@@ -173,6 +173,41 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K,
               void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * W8A8-FP8: activations quantised to FP8-E4M3 too, and the product on the
+ * FP8 matrix cores, for the shapes where the matrix product, not the weight
+ * bytes, sets the time (wide verify passes, large batches, prefill).  Sources:
+ * "Making each token cheaper", "Weight quantization / Formats" (E4M3 for
+ * weights and activations; a scale applied before the cast, per channel for
+ * weights and per tensor for activations) and "What quantization saves"
+ * (only a format whose product runs at lower precision, such as FP8 W8A8,
+ * reduces that arithmetic); "LLM 推理是怎么变快的", section 4.2 B (W8A8 on the
+ * FP8 / INT8 matrix units doubles the arithmetic rate).
+ *
+ * wqd_act_quant_fp8: x device bfloat16 [M, K] row-major (finite) ->
+ *   x_scale  device float32 [1]: s_a = max |x| / 448 over the whole tensor
+ *            (float32 division; 1 if x is all zero; at least 2^-126);
+ *   x_codes  device uint8 [M, K] row-major: nearest E4M3FN of x / s_a
+ *            (float32 division, ties to even, saturating at 448).
+ *   workspace: device, >= WQD_ACT_QUANT_WORKSPACE_BYTES, contents on entry
+ *   do not matter.  K % 16 == 0 (else WQD_E_SHAPE).  Deterministic.
+ *
+ * wqd_qgemm_w8a8: y[M, N] bfloat16 = bf16(s_a * s_n * sum_k e4m3(x_codes)
+ *   e4m3(W codes)), with x_codes / x_scale as wqd_act_quant_fp8 writes them
+ *   (x_scale read on the device) and W packed by wqd_pack_weights in the FP8
+ *   format (w_packed, w_scales).  The products are exact and summed in
+ *   float32.  workspace: >= wqd_w8a8_workspace_bytes (float32 split-K
+ *   partials; may be NULL when that is 0).  K % 16 == 0, M * K < 2^31.
+ *   Errors as wqd_qgemm.
+ */
+#define WQD_ACT_QUANT_WORKSPACE_BYTES 1024u
+int wqd_act_quant_fp8(const void* x, int64_t M, int64_t K, void* x_codes, float* x_scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+int wqd_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
+int wqd_qgemm_w8a8(const void* x_codes, const float* x_scale, int64_t M, int64_t N, int64_t K,
+                   const void* w_packed, const void* w_scales, void* y,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * product as wqd_qgemm, with the same arguments except the workspace.  The

@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
             "wqd_pack_weights": (i32, [i32, vp, i64, i64, vp, vp, vp, vp]),
             "wqd_qgemm": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
             "wqd_qgemm_noalloc": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]),
+            "wqd_act_quant_fp8": (i32, [vp, i64, i64, vp, vp, vp, sz, vp]),
+            "wqd_w8a8_workspace_bytes": (i32, [i64, i64, i64, psz]),
+            "wqd_qgemm_w8a8": (i32, [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]),
             "wqd_dequant": (i32, [i32, vp, vp, vp, i64, i64, vp, vp]),
             "wqd_unpack": (i32, [i32, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
             "wqd_decode_e4m3": (i32, [vp, vp, i64, vp]),
@@ -235,6 +238,60 @@ def qgemm_noalloc(x, pw: PackedWeight, y, stream=None):
     _check(lib().wqd_qgemm_noalloc(_fmt(pw.fmt), x.data_ptr(), M, pw.N, K, _ptr(pw.w), _ptr(pw.scales),
                                    _ptr(pw.zeros), y.data_ptr(), _stream(stream)), "wqd_qgemm_noalloc")
     return y
+
+
+ACT_QUANT_WORKSPACE_BYTES = 1024  # WQD_ACT_QUANT_WORKSPACE_BYTES
+
+
+def act_quant_fp8(x, codes=None, scale=None, workspace=None, stream=None):
+    """wqd_act_quant_fp8: (codes uint8 [M, K], scale float32 [1]) of bf16 x."""
+    import torch
+
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 [M, K] tensor")
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = get_workspace(ACT_QUANT_WORKSPACE_BYTES, x.device)
+    _check(lib().wqd_act_quant_fp8(x.data_ptr(), M, K, codes.data_ptr(), scale.data_ptr(), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "wqd_act_quant_fp8")
+    return codes, scale
+
+
+def w8a8_workspace_bytes(M: int, N: int, K: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().wqd_w8a8_workspace_bytes(M, N, K, ctypes.byref(b)), "wqd_w8a8_workspace_bytes")
+    return b.value
+
+
+def qgemm_w8a8(codes, scale, pw: PackedWeight, y=None, workspace=None, stream=None):
+    """wqd_qgemm_w8a8: y[M, N] (bfloat16) from activation codes / scale and FP8 packed weights."""
+    import torch
+
+    if pw.fmt != "fp8":
+        raise ValueError("W8A8 takes FP8 packed weights")
+    M, K = codes.shape
+    if K != pw.K or codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous uint8 [M, K] tensor matching the weights")
+    if y is None:
+        y = torch.empty((M, pw.N), dtype=torch.bfloat16, device=codes.device)
+    need = w8a8_workspace_bytes(M, pw.N, K)
+    if workspace is None:
+        workspace = get_workspace(need, codes.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().wqd_qgemm_w8a8(codes.data_ptr(), scale.data_ptr(), M, pw.N, K, _ptr(pw.w), _ptr(pw.scales),
+                                y.data_ptr(), _ptr(workspace), wsb, _stream(stream)), "wqd_qgemm_w8a8")
+    return y
+
+
+def w8a8(x, pw: PackedWeight, y=None, stream=None):
+    """The W8A8-FP8 layer from bf16 x: activation quantisation, then the product."""
+    codes, scale = act_quant_fp8(x, stream=stream)
+    return qgemm_w8a8(codes, scale, pw, y=y, stream=stream)
 
 
 def dequant(pw: PackedWeight, out=None, stream=None):

@@ -141,6 +141,46 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const voi
   return wqd::qgemm_checked(fmt, x, M, N, K, w_packed, scales, zeros, y, workspace, workspace_bytes, stream);
 }
 
+int wqd_act_quant_fp8(const void* x, int64_t M, int64_t K, void* x_codes, float* x_scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int parts = 0;
+  const int st = wqd::plan_act_quant(M, K, &parts);
+  if (st != wqd::kOK) return st;
+  if (!x || !x_codes || !x_scale || !workspace) return WQD_E_ARG;
+  if (workspace_bytes < WQD_ACT_QUANT_WORKSPACE_BYTES) return WQD_E_WORKSPACE;
+  if (!wqd::aligned16(x) || !wqd::aligned16(x_codes) || !wqd::aligned16(workspace) ||
+      reinterpret_cast<uintptr_t>(x_scale) % 4)
+    return WQD_E_ALIGN;
+  return hip_status(wqd::launch_act_quant(x, M, K, parts, x_codes, x_scale, reinterpret_cast<float*>(workspace),
+                                          as_stream(stream)));
+}
+
+int wqd_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return WQD_E_ARG;
+  wqd::W8Plan p;
+  const int st = wqd::plan_w8a8(M, N, K, &p);
+  if (st != wqd::kOK) return st;
+  *bytes = p.ws_bytes;
+  return WQD_OK;
+}
+
+int wqd_qgemm_w8a8(const void* x_codes, const float* x_scale, int64_t M, int64_t N, int64_t K, const void* w_packed,
+                   const void* w_scales, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  wqd::W8Plan p;
+  int st = wqd::plan_w8a8(M, N, K, &p);
+  if (st != wqd::kOK) return st;
+  if (!x_codes || !x_scale || !y) return WQD_E_ARG;
+  if (!wqd::aligned16(x_codes) || !wqd::aligned16(y) || reinterpret_cast<uintptr_t>(x_scale) % 4) return WQD_E_ALIGN;
+  st = check_packed_ptrs(wqd::kFmtFP8, w_packed, w_scales, nullptr);
+  if (st != WQD_OK) return st;
+  if (p.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < p.ws_bytes) return WQD_E_WORKSPACE;
+    if (!wqd::aligned16(workspace)) return WQD_E_ALIGN;
+  }
+  return hip_status(wqd::launch_w8a8(p, x_codes, x_scale, M, N, K, w_packed, w_scales, y, workspace,
+                                     as_stream(stream)));
+}
+
 int wqd_dequant(int fmt, const void* w_packed, const void* scales, const void* zeros, int64_t N, int64_t K,
                 float* W_out, void* stream) {
   wqd::PackedSizes ps;

@@ -34,6 +34,32 @@ __device__ __forceinline__ bf16x2_t e4m3x2_to_bf16x2(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
 }
 
+// Nearest FP8-E4M3FN value of v, ties to even mantissa, magnitudes above 448
+// saturate to 448; the sign bit is v's sign bit.  Written from the format's
+// definition ("Making each token cheaper", "Weight quantization / Formats":
+// 4 exponent bits, 3 mantissa bits, largest normal 448): the spacing of
+// representable values in the binade [2^E, 2^(E+1)) is 2^(E-3), and below
+// 2^-6 (the subnormals) it is 2^-9.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.0f);
+  if (a == 0.0f) return sign;
+  int e;
+  (void)frexpf(a, &e);            // a = m * 2^e, m in [0.5, 1)
+  int E = e - 1;                  // binade of a
+  if (E < -6) E = -6;             // subnormals use the spacing of 2^-6's binade
+  const float r = rintf(ldexpf(a, 3 - E));  // a / 2^(E-3), exact power-of-two scaling
+  const uint32_t mr = uint32_t(r);          // in [0, 16]
+  if (E == -6 && mr < 8) return sign | mr;  // subnormal: value = mr * 2^-9
+  int Eb = E;
+  uint32_t mant = mr;
+  if (mant == 16) {  // rounded up into the next binade
+    Eb += 1;
+    mant = 8;
+  }
+  return sign | (uint32_t(Eb + 7) << 3) | (mant - 8);
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   bf16x2_t v = e4m3x2_to_bf16x2<false>(code & 0xFFu);
   return bf16_bits_to_f32(__builtin_bit_cast(uint32_t, v) & 0xFFFFu);

@@ -31,6 +31,12 @@ hipError_t launch_splitk_reduce(int fmt, const float* part, int S, int64_t M, in
                                 hipStream_t st);
 hipError_t launch_mfma(int fmt, const MfmaPlan& p, int64_t M, int64_t N, int64_t K, const void* x, const void* wp,
                        const void* scales, const void* zeros, void* y, void* ws, hipStream_t st);
+// W8A8-FP8: activation codes and scale (workspace: the G partial maxima),
+// then the product on the FP8 matrix cores.
+hipError_t launch_act_quant(const void* x, int64_t M, int64_t K, int parts, void* codes, float* scale,
+                            float* ws_part, hipStream_t st);
+hipError_t launch_w8a8(const W8Plan& p, const void* xc, const float* xscale, int64_t M, int64_t N, int64_t K,
+                       const void* wp, const void* scales, void* y, void* ws, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 size_t stream_sink_words(size_t bytes);

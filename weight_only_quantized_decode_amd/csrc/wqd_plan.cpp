@@ -386,4 +386,53 @@ int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out) {
   return kOK;
 }
 
+int plan_w8a8(int64_t M, int64_t N, int64_t K, W8Plan* out) {
+  PackedSizes ps;
+  int st = packed_sizes(kFmtFP8, N, K, &ps);
+  if (st != kOK) return st;
+  if (M < 1) return kEArg;
+  if (K % 16 != 0) return kEShape;  // activation codes move in 16-byte pieces
+  if (M * K >= (int64_t(1) << 31) - 16) return kEUnsupported;
+  W8Plan p{};
+  p.NB = ps.NB;
+  p.KT = ps.KT;
+  if (M <= 32) {
+    p.mf = 2, p.wr = 1;
+  } else if (M <= 64) {
+    p.mf = 4, p.wr = 1;
+  } else {
+    p.mf = 8, p.wr = 1;
+  }
+  const int64_t bm = 16 * int64_t(p.mf) * p.wr;
+  p.NBN = ceil_div(p.NB, 16);  // 256-column blocks
+  p.MB = ceil_div(M, bm);
+  p.nchunks = ceil_div(p.KT, 2);  // 128-k chunks
+  // fill at least one round of the 256 compute units (two workgroups each
+  // for the 4-wavefront tiles), each split at least 4 chunks, at most 8 splits
+  const int64_t tiles = ceil_div(p.NBN, 8) * 8 * p.MB;
+  const int64_t target = p.wr == 1 ? 512 : 256;
+  int64_t S = tiles >= target ? 1 : ceil_div(target, tiles);
+  const int64_t max_s = p.nchunks / 4 > 1 ? p.nchunks / 4 : 1;
+  if (S > max_s) S = max_s;
+  if (S > 8) S = 8;
+  p.cps = ceil_div(p.nchunks, S);
+  S = ceil_div(p.nchunks, p.cps);
+  p.S = int(S);
+  p.ws_bytes = p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;
+  *out = p;
+  return kOK;
+}
+
+int plan_act_quant(int64_t M, int64_t K, int* parts) {
+  if (M < 1 || K < 1) return kEArg;
+  if (K % 16 != 0) return kEShape;
+  if (M * K >= (int64_t(1) << 40)) return kEUnsupported;
+  // ranges of at least 16 KiB of x per part
+  const int64_t n16 = M * K / 8;
+  int64_t g = ceil_div(n16, 1024);
+  if (g > kActQuantParts) g = kActQuantParts;
+  *parts = int(g < 1 ? 1 : g);
+  return kOK;
+}
+
 }  // namespace wqd

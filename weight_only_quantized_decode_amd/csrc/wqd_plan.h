@@ -175,6 +175,28 @@ int choose_path(int fmt, int64_t M, int64_t N, int64_t K, Choice* out);
 // Workspace bytes for wqd_qgemm (0: no path needs scratch memory).
 int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out);
 
+// W8A8-FP8 tiled kernel: FP8 activation codes [M, K] times FP8 packed
+// weights on v_mfma_f32_16x16x128_f8f6f4.  A workgroup computes a BM x 256
+// tile of y with WR x 4 wavefronts of (16 MF rows) x (4 weight row blocks);
+// K advances in 128-k chunks (two packed tiles) through NS pipeline stages.
+// BM = 16 MF WR: 32 (MF 2), 64 (MF 4) or 128 (MF 8), WR = 1.  K is
+// split S ways over grid y when the tiles leave the compute units idle; the
+// float32 partials (already times the activation scale) go to the workspace
+// and the fixed-order split-K sum applies the row scales.
+struct W8Plan {
+  int64_t NB, KT, NBN, MB, nchunks, cps;
+  int mf, wr, S;
+  size_t ws_bytes;
+};
+
+int plan_w8a8(int64_t M, int64_t N, int64_t K, W8Plan* out);
+
+// The activation quantisation: G workgroups each reduce a contiguous range of
+// x to its largest |x| (G <= kActQuantParts, written to the workspace), then
+// every workgroup of the quantising kernel reduces the G values itself.
+constexpr int kActQuantParts = 256;
+int plan_act_quant(int64_t M, int64_t K, int* parts);
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace wqd
