@@ -41,6 +41,7 @@ import time
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor peak
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix peak
 MAT_INDEX = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "w": 0}
 TARGET_ROWS = (("w4a16", 4), ("w4a16", 8), ("fp8", 1), ("fp8", 8))
 
@@ -82,6 +83,8 @@ def make_workload(name, fmt_m, layers, fused):
     if name.startswith("verify:"):
         _, fmt, mat = name.split(":")
         return WL.verify_matrix(fmt, mat, m)
+    if name.startswith("w8a8:"):
+        return WL.verify_w8a8(name.split(":")[1], m)
     raise SystemExit(f"unknown workload {name!r}")
 
 
@@ -169,7 +172,10 @@ def stack_io(wl):
             xs[K] = I.x_bf16(I.x_seed(wl.cfg, wl.M, K), wl.M, K, outliers=wl.outliers).to(dev)
         if N not in ys:
             ys[N] = torch.empty((wl.M, N), dtype=torch.bfloat16, device=dev)
-    need = max(wqd.workspace_bytes(wl.fmt, wl.M, N, K) for _, N, K in wl.mats)
+    if wl.act == "fp8":
+        need = max(max(wqd.w8a8_workspace_bytes(wl.M, N, K) for _, N, K in wl.mats), wqd.ACT_QUANT_WORKSPACE_BYTES)
+    else:
+        need = max(wqd.workspace_bytes(wl.fmt, wl.M, N, K) for _, N, K in wl.mats)
     return xs, ys, wqd.get_workspace(need, dev)
 
 
@@ -207,6 +213,8 @@ def replay_timing(launch_all, stream, steps, warmup, use_graph=True):
 def kernel_group(wl, N, K):
     import weight_only_quantized_decode_amd as wqd
 
+    if wl.act == "fp8":
+        return "w8a8 fp8 matrix cores"
     return "%s(%d waves)" % wqd.kernel_path(wl.fmt, wl.M, N, K)
 
 
@@ -216,15 +224,26 @@ def time_step(wl, packed, args, stream, dominant=False, shapes=False):
     import weight_only_quantized_decode_amd as wqd
     from weight_only_quantized_decode_amd import workloads as WL
 
+    import torch
+
     xs, ys, ws = stack_io(wl)
     rows = len(packed) // wl.layers  # copies of a single matrix: one replay calls each once
+    # W8A8: a call is the activation quantisation, then the product (the
+    # kernel-family replays time the product alone, on codes made once)
+    codes = {K: wqd.act_quant_fp8(x, workspace=ws) for K, x in xs.items()} if wl.act == "fp8" else None
 
     def launches(only=None):
         def go():
             for row in packed:
                 for j, ((name, N, K), pw) in enumerate(zip(wl.mats, row)):
-                    if only is None or j in only:
+                    if only is not None and j not in only:
+                        continue
+                    if codes is None:
                         wqd.qgemm(xs[K], pw, y=ys[N], workspace=ws)
+                        continue
+                    if only is None:
+                        wqd.act_quant_fp8(xs[K], *codes[K], workspace=ws)
+                    wqd.qgemm_w8a8(*codes[K], pw, y=ys[N], workspace=ws)
         return go
 
     log(f"[bench] {wl.name}: {wl.launches} launches/step, {wl.step_bytes() / 1e9:.3f} GB/step; "
@@ -245,7 +264,7 @@ def time_step(wl, packed, args, stream, dominant=False, shapes=False):
         for label, js in groups.items():
             g_ms, _ = replay_timing(launches(set(js)), stream, args.steps, args.warmup, not args.no_graph)
             n_launch = len(js) * len(packed)
-            g_bytes = len(packed) * sum(WL.call_bytes(wl.fmt, wl.M, wl.mats[j][1], wl.mats[j][2]) for j in js)
+            g_bytes = len(packed) * sum(wl.call_bytes(wl.mats[j][1], wl.mats[j][2]) for j in js)
             g_flops = len(packed) * sum(WL.call_flops(wl.M, wl.mats[j][1], wl.mats[j][2]) for j in js)
             per[label] = {"matrices": [wl.mats[j][0] for j in js], "launches": n_launch, "ms": g_ms,
                           "avg_launch_us": g_ms * 1e3 / n_launch, "bytes": g_bytes, "flops": g_flops}
@@ -255,7 +274,7 @@ def time_step(wl, packed, args, stream, dominant=False, shapes=False):
         for j, (name, N, K) in enumerate(wl.mats):
             s_ms, _ = replay_timing(launches({j}), stream, max(3, args.steps // 4), 1, not args.no_graph)
             us = s_ms * 1e3 / wl.layers
-            b = WL.call_bytes(wl.fmt, wl.M, N, K)
+            b = wl.call_bytes(N, K)
             out[name] = {"N": N, "K": K, "us": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1),
                          "kernel": kernel_group(wl, N, K)}
         res["shapes"] = out
@@ -391,10 +410,11 @@ def cpu_baseline(wl, budget_s=12.0):
     xs = {K: I.x_bf16_bits(I.x_seed(wl.cfg, wl.M, K), wl.M, K, outliers=wl.outliers) for _, K in mats}
     setup_s = time.perf_counter() - t_setup
     reps, t_total = 0, 0.0
+    ref = oracle.qgemm_w8a8_ref if wl.act == "fp8" else oracle.qgemm_ref
     while reps < 1 or (t_total < budget_s and reps < 50):
         t0 = time.perf_counter()
         for qw, K in mats:
-            oracle.qgemm_ref(xs[K], qw)
+            ref(xs[K], qw)
         t_total += time.perf_counter() - t0
         reps += 1
     per_layer = t_total / reps
@@ -410,7 +430,7 @@ def cpu_baseline(wl, budget_s=12.0):
         "kind": "oracle",
         "ms_per_step": round(step_s * 1e3, 1),
         "extrapolated": wl.layers > 1,
-        "sample": f"the float64 oracle (exact dequant, matmul, bf16 rounding) on {wl.name}: {what}; "
+        "sample": f"the float64 oracle ({'activation quantisation, exact code product' if wl.act == 'fp8' else 'exact dequant, matmul'}, bf16 rounding) on {wl.name}: {what}; "
                   f"{per_layer * 1e3:.1f} ms per layer ({t_total:.1f} s timed, {setup_s:.1f} s untimed "
                   f"quantisation); {host}",
     }
@@ -489,10 +509,11 @@ def roofline_of(wl, res):
     per_launch_bytes = g["bytes"] / g["launches"]
     per_launch_flops = g["flops"] / g["launches"]
     avg_us = g["avg_launch_us"]
-    if per_launch_flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > per_launch_bytes / (HBM_PEAK_GBPS * 1e9):
+    peak_tf = FP8_MFMA_PEAK_TFLOPS if wl.act == "fp8" else BF16_MFMA_PEAK_TFLOPS
+    if per_launch_flops / (peak_tf * 1e12) > per_launch_bytes / (HBM_PEAK_GBPS * 1e9):
         tf = per_launch_flops / (avg_us / 1e6) / 1e12
-        r = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-             "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+        r = {"bound": "mfma", "achieved": round(tf, 2), "peak": peak_tf, "unit": "TFLOP/s",
+             "frac": round(tf / peak_tf, 4)}
     else:
         a = per_launch_bytes / (avg_us / 1e6) / 1e9
         r = {"bound": "hbm", "achieved": round(a, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -573,7 +594,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"w4a16": "u4+bf16", "fp8": "e4m3+bf16", "bf16": "bf16"}[wl.fmt],
+        "dtype": "e4m3" if wl.act == "fp8" else {"w4a16": "u4+bf16", "fp8": "e4m3+bf16", "bf16": "bf16"}[wl.fmt],
         "data": "synthetic",
         "config": {"workload": wl.name, "fmt": wl.fmt, "M": wl.M, "layers": wl.layers,
                    "launches_per_step": wl.launches, "graph": not args.no_graph, "fused": fused,
@@ -602,8 +623,9 @@ def main():
         out["shapes"] = head["shapes"]
     if wl.M >= 16:
         tflops = wl.step_flops() / (ms / 1e3) / 1e12
-        out["mfma_util_pct"] = round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2)
-        if not args.no_ceiling:
+        out["mfma_util_pct"] = round(100 * tflops / (FP8_MFMA_PEAK_TFLOPS if wl.act == "fp8" else
+                                                     BF16_MFMA_PEAK_TFLOPS), 2)
+        if not args.no_ceiling and wl.act != "fp8":  # the ceiling kernel runs bf16 multiplies
             peak = mfma_ceiling()
             log(f"[bench] matrix-core ceiling: {peak:.0f} TFLOP/s")
             out["mfma_ceiling_TFLOPs"] = round(peak, 1)

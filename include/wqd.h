@@ -199,7 +199,7 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K,
  *   partials; may be NULL when that is 0).  K % 16 == 0, M * K < 2^31.
  *   Errors as wqd_qgemm.
  */
-#define WQD_ACT_QUANT_WORKSPACE_BYTES 1024u
+#define WQD_ACT_QUANT_WORKSPACE_BYTES 4096u
 int wqd_act_quant_fp8(const void* x, int64_t M, int64_t K, void* x_codes, float* x_scale,
                       void* workspace, size_t workspace_bytes, void* stream);
 int wqd_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);

@@ -52,6 +52,29 @@ def test_act_quant_zero_and_tiny():
     assert ref["scale"] == np.float32(2.0 ** -126)
 
 
+def test_act_quant_rounding_cases():
+    """Scale 1 (the tensor holds 448): every finite E4M3 value, the midpoints
+    between neighbours (ties to even), one bf16 step either side of each, the
+    subnormal range and values that round to +-0 (the sign kept)."""
+    import torch as _t
+
+    fin = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = np.sort(np.unique(oracle.e4m3_decode(fin)))
+    mids = (vals[:-1] + vals[1:]) / 2
+    b = _t.from_numpy(np.concatenate([vals, mids]).astype(np.float32)).to(_t.bfloat16)
+    bits = b.view(_t.int16).numpy().view(np.uint16).astype(np.int32)
+    mid_bits = bits[len(vals):]
+    near = np.concatenate([mid_bits + 1, mid_bits - 1])
+    near = near[(near & 0x7FFF) != 0]  # keep to values next to the midpoints
+    tiny = np.array([0x0001, 0x8001, 0x3A00, 0xBA00, 0x3A80, 0xBA80, 0x8000, 0x3B00], np.int32)  # below 2^-9
+    allb = np.concatenate([bits, near, tiny, [0x43E0]]).astype(np.uint16)  # 0x43E0 = 448
+    n = (len(allb) + 15) // 16 * 16
+    xb = np.zeros(n, np.uint16)
+    xb[:len(allb)] = allb
+    codes, scale, ref = check_act(xb.reshape(n // 16, 16))
+    assert ref["scale"] == np.float32(1.0)
+
+
 def run_product(M, N, K, seed, rows=None, outl=False):
     W = I.w_device(seed, N, K, device=DEV)
     pw = wqd.pack_weights("fp8", W)

@@ -240,7 +240,7 @@ def qgemm_noalloc(x, pw: PackedWeight, y, stream=None):
     return y
 
 
-ACT_QUANT_WORKSPACE_BYTES = 1024  # WQD_ACT_QUANT_WORKSPACE_BYTES
+ACT_QUANT_WORKSPACE_BYTES = 4096  # WQD_ACT_QUANT_WORKSPACE_BYTES
 
 
 def act_quant_fp8(x, codes=None, scale=None, workspace=None, stream=None):

@@ -141,6 +141,9 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const voi
   return wqd::qgemm_checked(fmt, x, M, N, K, w_packed, scales, zeros, y, workspace, workspace_bytes, stream);
 }
 
+static_assert(WQD_ACT_QUANT_WORKSPACE_BYTES >= wqd::kActQuantParts * sizeof(float),
+              "the activation quantisation workspace holds every partial maximum");
+
 int wqd_act_quant_fp8(const void* x, int64_t M, int64_t K, void* x_codes, float* x_scale, void* workspace,
                       size_t workspace_bytes, void* stream) {
   int parts = 0;

@@ -427,9 +427,9 @@ int plan_act_quant(int64_t M, int64_t K, int* parts) {
   if (M < 1 || K < 1) return kEArg;
   if (K % 16 != 0) return kEShape;
   if (M * K >= (int64_t(1) << 40)) return kEUnsupported;
-  // ranges of at least 16 KiB of x per part
+  // ranges of at least 32 KiB of x per part (8 loads in flight per thread)
   const int64_t n16 = M * K / 8;
-  int64_t g = ceil_div(n16, 1024);
+  int64_t g = ceil_div(n16, 2048);
   if (g > kActQuantParts) g = kActQuantParts;
   *parts = int(g < 1 ? 1 : g);
   return kOK;

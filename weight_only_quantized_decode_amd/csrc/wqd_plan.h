@@ -194,7 +194,7 @@ int plan_w8a8(int64_t M, int64_t N, int64_t K, W8Plan* out);
 // The activation quantisation: G workgroups each reduce a contiguous range of
 // x to its largest |x| (G <= kActQuantParts, written to the workspace), then
 // every workgroup of the quantising kernel reduces the G values itself.
-constexpr int kActQuantParts = 256;
+constexpr int kActQuantParts = 1024;
 int plan_act_quant(int64_t M, int64_t K, int* parts);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

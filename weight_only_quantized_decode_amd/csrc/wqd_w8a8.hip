@@ -18,7 +18,8 @@
 //                      the same maximum), s_a = max / 448 (float32; 1 for an
 //                      all-zero tensor, at least 2^-126), workgroup 0 stores
 //                      it, and each thread encodes 8 activations as the
-//                      nearest E4M3 of x / s_a (ties to even, saturating).
+//                      nearest E4M3 of x / s_a (ties to even, saturating;
+//                      the hardware conversion after a clamp to +-448).
 //
 // The product (w8_gemm_kernel<MF, WR>): a workgroup computes a BM x 256 tile
 // of y, BM = 16 MF WR, with WR x 4 wavefronts, each 16 MF rows x 4 weight row
@@ -71,8 +72,16 @@ __device__ __forceinline__ float block_max_256(float a, float* red) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+__device__ __forceinline__ float absmax8(uint4 v) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a = fmaxf(a, fmaxf(fabsf(bf16_lo(u[e])), fabsf(bf16_hi(u[e]))));
+  return a;
+}
+
 // part[b] = largest |x| over the b-th of G contiguous ranges of the n16
-// 16-byte pieces (8 bf16 each) of x.
+// 16-byte pieces (8 bf16 each) of x; 8 independent loads per thread in flight.
 __global__ __launch_bounds__(256) void act_absmax_kernel(const uint4* __restrict__ x, int64_t n16,
                                                          float* __restrict__ part) {
   __shared__ float red[4];
@@ -81,37 +90,66 @@ __global__ __launch_bounds__(256) void act_absmax_kernel(const uint4* __restrict
   const int64_t begin = int64_t(blockIdx.x) * per;
   const int64_t end = begin + per < n16 ? begin + per : n16;
   float a = 0.f;
-  for (int64_t i = begin + threadIdx.x; i < end; i += 256) {
-    const uint4 v = x[i];
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  int64_t i = begin + threadIdx.x;
+  for (; i + 7 * 256 < end; i += 8 * 256) {
+    uint4 v[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a = fmaxf(a, fmaxf(fabsf(bf16_lo(u[e])), fabsf(bf16_hi(u[e]))));
+    for (int u = 0; u < 8; ++u) v[u] = x[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a = fmaxf(a, absmax8(v[u]));
   }
+  for (; i < end; i += 256) a = fmaxf(a, absmax8(x[i]));
   a = block_max_256(a, red);
   if (threadIdx.x == 0) part[blockIdx.x] = a;
 }
 
-// One 16-byte piece of x (8 activations) per thread -> 8 codes.
+constexpr int kQuantPieces = 4;  // 16-byte pieces of x per thread in act_quant_kernel
+
+// The codes of the two bf16 activations in `w` (low half first) into bytes
+// 0-1 (HI false) or 2-3 (HI true) of `old`: x / s correctly rounded in
+// float32, clamped to +-448 (the saturation; the clamp keeps the sign of
+// -0), then the hardware's round-to-nearest-even conversion to E4M3FN.
+template <bool HI>
+__device__ __forceinline__ uint32_t act_code_pair(uint32_t old, uint32_t w, float s) {
+  const float a = fminf(fmaxf(__fdiv_rn(bf16_lo(w), s), -448.0f), 448.0f);
+  const float b = fminf(fmaxf(__fdiv_rn(bf16_hi(w), s), -448.0f), 448.0f);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, int(old), HI));
+}
+
+// Each workgroup: s_a from the G partial maxima, then kQuantPieces x 256
+// consecutive pieces of x (8 activations each) -> 8 codes per piece.
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint4* __restrict__ x, int64_t n16,
                                                         const float* __restrict__ part, int G,
                                                         uint2* __restrict__ codes, float* __restrict__ scale_out) {
   __shared__ float red[4];
-  const float a = block_max_256(int(threadIdx.x) < G ? part[threadIdx.x] : 0.f, red);
+  const int64_t i0 = int64_t(blockIdx.x) * (256 * kQuantPieces) + threadIdx.x;
+  uint4 v[kQuantPieces];
+#pragma unroll
+  for (int p = 0; p < kQuantPieces; ++p) {
+    const int64_t i = i0 + p * 256;
+    v[p] = x[i < n16 ? i : n16 - 1];
+  }
+  float pm = 0.f;
+#pragma unroll
+  for (int q = 0; q < kActQuantParts / 256; ++q) {
+    const int t = threadIdx.x + 256 * q;
+    if (t < G) pm = fmaxf(pm, part[t]);
+  }
+  const float a = block_max_256(pm, red);
   float s = __fdiv_rn(a, 448.0f);
   s = fmaxf(s, 0x1p-126f);
   if (a == 0.f) s = 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= n16) return;
-  const uint4 v = x[i];
-  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-  uint32_t c[2] = {0u, 0u};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t pair = e4m3_encode(__fdiv_rn(bf16_lo(u[e]), s)) | (e4m3_encode(__fdiv_rn(bf16_hi(u[e]), s)) << 8);
-    c[e >> 1] |= pair << (16 * (e & 1));
+  for (int p = 0; p < kQuantPieces; ++p) {
+    const int64_t i = i0 + p * 256;
+    if (i >= n16) break;
+    const uint32_t u[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+    // elements 2e, 2e + 1 of the piece are the halves of u[e]; code byte j is element j
+    const uint32_t c0 = act_code_pair<true>(act_code_pair<false>(0u, u[0], s), u[1], s);
+    const uint32_t c1 = act_code_pair<true>(act_code_pair<false>(0u, u[2], s), u[3], s);
+    codes[i] = make_uint2(c0, c1);
   }
-  codes[i] = make_uint2(c[0], c[1]);
 }
 
 hipError_t launch_act_quant(const void* x, int64_t M, int64_t K, int parts, void* codes, float* scale,
@@ -121,7 +159,7 @@ hipError_t launch_act_quant(const void* x, int64_t M, int64_t K, int parts, void
                      n16, ws_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(act_quant_kernel, dim3(unsigned(ceil_div(n16, int64_t(256)))), dim3(256), 0, st,
+  hipLaunchKernelGGL(act_quant_kernel, dim3(unsigned(ceil_div(n16, int64_t(256) * kQuantPieces))), dim3(256), 0, st,
                      reinterpret_cast<const uint4*>(x), n16, ws_part, parts, reinterpret_cast<uint2*>(codes), scale);
   return hipGetLastError();
 }

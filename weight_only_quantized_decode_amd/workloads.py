@@ -33,6 +33,18 @@ def call_bytes(fmt: str, M: int, N: int, K: int) -> int:
     return wb["w"] + wb["s"] + wb["z"] + 2 * M * K + 2 * M * N
 
 
+def call_bytes_w8a8(M: int, N: int, K: int) -> int:
+    """The W8A8 product: FP8 weights and row scales, activation codes (1 B
+    each) in, y (bf16) out."""
+    wb = weight_bytes("fp8", N, K)
+    return wb["w"] + wb["s"] + M * K + 2 * M * N
+
+
+def act_quant_bytes(M: int, K: int) -> int:
+    """The activation quantisation: x read twice (maximum, then codes), codes written."""
+    return 2 * 2 * M * K + M * K
+
+
 def call_flops(M: int, N: int, K: int) -> int:
     return 2 * M * N * K
 
@@ -46,13 +58,19 @@ class Workload:
     mats: tuple  # ((name, N, K), ...) per layer
     outliers: bool
     cfg: int
+    act: str = "bf16"  # "fp8": W8A8, activations quantised per tensor before each product
 
     @property
     def launches(self) -> int:
         return self.layers * len(self.mats)
 
+    def call_bytes(self, N: int, K: int) -> int:
+        if self.act == "fp8":
+            return call_bytes_w8a8(self.M, N, K)
+        return call_bytes(self.fmt, self.M, N, K)
+
     def step_bytes(self) -> int:
-        return self.layers * sum(call_bytes(self.fmt, self.M, N, K) for _, N, K in self.mats)
+        return self.layers * sum(self.call_bytes(N, K) for _, N, K in self.mats)
 
     def step_flops(self) -> int:
         return self.layers * sum(call_flops(self.M, N, K) for _, N, K in self.mats)
@@ -105,6 +123,13 @@ def verify_matrix(fmt: str, mat: str, M: int) -> Workload:
               "down": (8192, 28672)}
     N, K = shapes[mat]
     return Workload(f"verify_{fmt}_{mat}_m{M}", fmt, M, 1, ((mat, N, K),), True, 5)
+
+
+def verify_w8a8(mat: str, M: int) -> Workload:
+    """A 70B verify-shape matrix in W8A8-FP8: FP8 weights, activations
+    quantised to FP8 per tensor, the product on the FP8 matrix cores."""
+    wl = verify_matrix("fp8", mat, M)
+    return Workload(f"verify_w8a8_{mat}_m{M}", "fp8", M, 1, wl.mats, True, 5, "fp8")
 
 
 VERIFY_M = (6, 16, 48, 128, 192, 384, 512, 1024)
