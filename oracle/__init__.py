@@ -18,6 +18,8 @@ It computes, plainly and slowly, what the decode linear layer computes:
 * ``w8a8``:    the W8A8-FP8 variant: one dynamic E4M3 scale for the whole
   activation tensor, activation codes, and the product of the two code
   matrices (exact in float64) times both scales;
+* ``attention``: decode attention over a KV cache with grouped-query heads
+  (one query per sequence, softmax over its first len positions);
 * ``bytes``:   the bytes a call or a step moves (codes, scales, zero points,
   activations; KV cache per sequence) and the step's lower bound, as the
   pages define them.
@@ -37,7 +39,9 @@ KV cache of a 2,048-token sequence, the batch-1 and batch-32 floors, the CS336
 error bound on the original weights; the W8A8 product against exact rationals,
 activation codes against a brute-force nearest E4M3 value, activations on the
 E4M3 grid reducing to the weight-only product, and the activation rounding
-bound.  No function here is
+bound; decode attention against closed forms (one position, equal keys, a
+dominant key, a 3:1 split), invariances, per-group values and torch's float64
+scaled-dot-product attention.  No function here is
 "parity unpinned".
 """
 from .formats import (  # noqa: F401
@@ -64,5 +68,6 @@ from .quant import (  # noqa: F401
     quantize_w4a16,
     w4a16_group_params,
 )
+from .attention import decode_attention_exact, decode_attention_ref  # noqa: F401
 from .w8a8 import act_scale, qgemm_w8a8_exact, qgemm_w8a8_ref, quantize_act  # noqa: F401
 from .spec import accept, draw_units, inverse_cdf_draw, residual, spec_accept, spec_accept_one  # noqa: F401
