@@ -208,6 +208,40 @@ int wqd_qgemm_w8a8(const void* x_codes, const float* x_scale, int64_t M, int64_t
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode attention over a KV cache, split along the context (Flash-Decoding),
+ * with grouped-query heads.  Sources: "Making each token cheaper", section
+ * "Why kernels matter most for long prefill" (a decode step has one query per
+ * sequence; decode attention is dominated by reading the KV cache;
+ * Flash-Decoding splits keys and values into chunks processed in parallel,
+ * since parallelising over batch and queries alone leaves most of the GPU
+ * idle) and "Why decode is usually bandwidth bound" (each sequence's KV bytes
+ * are read once per step); "LLM 推理是怎么变快的", section 2.3 (grouped-query
+ * attention: several query heads share one KV head).
+ *
+ * For each sequence b and query head h, with g = h / (Hq / Hkv):
+ *   o[b, h] = sum_{t < len[b]} softmax_t(scale * q[b, h] . K[b, g, t]) V[b, g, t]
+ * products and sums in float32 from the bf16 inputs (the softmax weights
+ * are not rounded to bf16), rounded to bf16; len[b] = 0 gives zeros.
+ *   q          device bf16 [B][Hq][D]
+ *   k_cache    device bf16 [B][Hkv][Lmax][D]   (head dimension contiguous)
+ *   v_cache_t  device bf16 [B][Hkv][D][Lmax]   (V transposed: positions
+ *              contiguous; the writer of a new position t stores V[b, g, t, d]
+ *              at [b][g][d][t])
+ *   lengths    device int32 [B]: positions used per sequence (clamped to
+ *              [0, Lmax]); cache entries at or past a length are never used,
+ *              whatever they hold
+ *   out        device bf16 [B][Hq][D]
+ *   workspace  device, >= wqd_attn_workspace_bytes (partial maxima, sums and
+ *              outputs of the splits), contents on entry do not matter.
+ * D = 128, Hq a multiple of Hkv with Hq / Hkv <= 16, Lmax a multiple of 8 and
+ * Lmax * D * 2 < 2^31 (else WQD_E_SHAPE / WQD_E_UNSUPPORTED).  Deterministic.
+ */
+int wqd_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, size_t* bytes);
+int wqd_decode_attention(const void* q, const void* k_cache, const void* v_cache_t, const int32_t* lengths,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, float scale, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * product as wqd_qgemm, with the same arguments except the workspace.  The

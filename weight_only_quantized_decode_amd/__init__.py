@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
             "wqd_qgemm": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
             "wqd_qgemm_noalloc": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]),
             "wqd_act_quant_fp8": (i32, [vp, i64, i64, vp, vp, vp, sz, vp]),
+            "wqd_attn_workspace_bytes": (i32, [i64, i64, i64, i64, i64, psz]),
+            "wqd_decode_attention": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, vp, sz,
+                                            vp]),
             "wqd_w8a8_workspace_bytes": (i32, [i64, i64, i64, psz]),
             "wqd_qgemm_w8a8": (i32, [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]),
             "wqd_dequant": (i32, [i32, vp, vp, vp, i64, i64, vp, vp]),
@@ -292,6 +295,35 @@ def w8a8(x, pw: PackedWeight, y=None, stream=None):
     """The W8A8-FP8 layer from bf16 x: activation quantisation, then the product."""
     codes, scale = act_quant_fp8(x, stream=stream)
     return qgemm_w8a8(codes, scale, pw, y=y, stream=stream)
+
+
+def attn_workspace_bytes(B: int, Hq: int, Hkv: int, Lmax: int, D: int = 128) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().wqd_attn_workspace_bytes(B, Hq, Hkv, Lmax, D, ctypes.byref(b)), "wqd_attn_workspace_bytes")
+    return b.value
+
+
+def decode_attention(q, k_cache, v_cache_t, lengths, scale: float, out=None, workspace=None, stream=None):
+    """wqd_decode_attention: q bf16 [B, Hq, D], k_cache bf16 [B, Hkv, Lmax, D],
+    v_cache_t bf16 [B, Hkv, D, Lmax] (V transposed), lengths int32 [B] ->
+    out bf16 [B, Hq, D]."""
+    import torch
+
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    for t, shape, dt in ((q, (B, Hq, D), torch.bfloat16), (k_cache, (B, Hkv, Lmax, D), torch.bfloat16),
+                         (v_cache_t, (B, Hkv, D, Lmax), torch.bfloat16), (lengths, (B,), torch.int32)):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"decode_attention: expected a contiguous {dt} tensor of shape {shape}")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        workspace = get_workspace(attn_workspace_bytes(B, Hq, Hkv, Lmax, D), q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().wqd_decode_attention(q.data_ptr(), k_cache.data_ptr(), v_cache_t.data_ptr(), lengths.data_ptr(), B,
+                                      Hq, Hkv, Lmax, D, float(scale), out.data_ptr(), workspace.data_ptr(), wsb,
+                                      _stream(stream)), "wqd_decode_attention")
+    return out
 
 
 def dequant(pw: PackedWeight, out=None, stream=None):

@@ -184,6 +184,29 @@ int wqd_qgemm_w8a8(const void* x_codes, const float* x_scale, int64_t M, int64_t
                                      as_stream(stream)));
 }
 
+int wqd_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, size_t* bytes) {
+  if (!bytes) return WQD_E_ARG;
+  wqd::AttnPlan p;
+  const int st = wqd::plan_attn(B, Hq, Hkv, Lmax, D, &p);
+  if (st != wqd::kOK) return st;
+  *bytes = p.ws_bytes;
+  return WQD_OK;
+}
+
+int wqd_decode_attention(const void* q, const void* k_cache, const void* v_cache_t, const int32_t* lengths,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, float scale, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  wqd::AttnPlan p;
+  const int st = wqd::plan_attn(B, Hq, Hkv, Lmax, D, &p);
+  if (st != wqd::kOK) return st;
+  if (!q || !k_cache || !v_cache_t || !lengths || !out || !workspace) return WQD_E_ARG;
+  if (workspace_bytes < p.ws_bytes) return WQD_E_WORKSPACE;
+  if (!wqd::aligned16(q) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache_t) || !wqd::aligned16(out) ||
+      !wqd::aligned16(workspace) || reinterpret_cast<uintptr_t>(lengths) % 4)
+    return WQD_E_ALIGN;
+  return hip_status(wqd::launch_attn(p, q, k_cache, v_cache_t, lengths, B, scale, out, workspace, as_stream(stream)));
+}
+
 int wqd_dequant(int fmt, const void* w_packed, const void* scales, const void* zeros, int64_t N, int64_t K,
                 float* W_out, void* stream) {
   wqd::PackedSizes ps;

@@ -1,0 +1,294 @@
+// Decode attention over a KV cache, split along the context (Flash-Decoding).
+//
+// A decode step has one query per sequence, so attention is a matrix-vector
+// product over the cache, and its time is the time to read the keys and
+// values ("Making each token cheaper", section "Why kernels matter most for
+// long prefill": decode attention is dominated by reading the KV cache; with
+// one query per sequence, parallelising over batch and queries alone leaves
+// most of the GPU idle, so Flash-Decoding splits the keys and values into
+// chunks processed in parallel, then merges them).  Grouped-query heads
+// ("LLM 推理是怎么变快的", section 2.3): the G = Hq / Hkv query heads of a
+// group read one KV head, so one pass over that head's cache serves all G.
+//
+// Cache layout (library-defined, caller-written): K [B][Hkv][Lmax][128] with
+// the head dimension contiguous, V [B][Hkv][128][Lmax] with positions
+// contiguous (V is stored transposed so the product over positions reads
+// contiguous 16-byte pieces, as the product over the head dimension does for K).
+//
+// attn_split_kernel: one wavefront per (sequence b, KV head g, split s); the
+// split's positions in steps of 32.  Per step, on bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16):
+//   * S^T = K Q^T as two 16-position tiles x 4 head-dimension steps.  A = key
+//     rows: tile tau's row j is position 8 (j / 4) + 4 tau + (j % 4) of the
+//     step, so that its output row 4 kb + r is position 8 kb + 4 tau + r and
+//     lane (kb, n) ends up with the 8 consecutive positions 8 kb .. 8 kb + 7
+//     of query head n; B = Q^T, lane (kb, n) holding 8 head dimensions of
+//     query head n of the group (heads G .. 15 zero);
+//   * online softmax in float32 with exp2 (scores times scale log2 e): the
+//     running maximum and sum per head, reduced over the four lanes of a head
+//     (shfl_xor 16, 32); positions at or past the sequence's length are set
+//     to -inf by selection and their values to 0, so stale cache contents
+//     never reach the sums;
+//   * O += P V as 8 head-dimension blocks of 16: A = P, which the score tiles
+//     already left in operand order (lane (kb, n): head n, positions
+//     8 kb .. 8 kb + 7), split into bf16 high and low parts (two multiplies,
+//     error ~2^-17 of each weight) so P is not rounded to 8 bits; B = V
+//     straight from the transposed cache (lane (kb, n): dimension n of the
+//     block, positions 8 kb .. 8 kb + 7, one 16-byte load);
+//   * the next step's K and V pieces are loaded before this step's arithmetic.
+// Each wavefront writes its running maximum, sum and unnormalised output per
+// head to the workspace.  attn_combine_kernel then merges the splits of each
+// (b, head) in split order: o = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s,
+// rounded to bf16 (a sequence of length 0 gives zeros).
+#include "wqd_device.h"
+#include "wqd_internal.h"
+#include "wqd_plan.h"
+
+namespace wqd {
+
+typedef __bf16 at_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float at_f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ at_f32x4_t at_mfma(uint4 a, uint4 b, at_f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(at_bf16x8_t, a), __builtin_bit_cast(at_bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+struct AttnArgs {
+  const uint16_t* q;    // [B][Hq][128]
+  const uint16_t* k;    // [B][Hkv][Lmax][128]
+  const uint16_t* vt;   // [B][Hkv][128][Lmax]
+  const int32_t* lens;  // [B]
+  uint16_t* out;        // [B][Hq][128]
+  float* part_ml;       // [B][Hq][S][2]: running maximum (log2 units), sum
+  float* part_o;        // [B][Hq][S][128]: unnormalised output
+  float scale_log2;     // softmax scale times log2 e
+  int64_t Lmax;
+  int Hq, Hkv, G, S, chunk;  // chunk: positions per split, a multiple of 32
+};
+
+struct AttnStepLoads {
+  uint4 k[2][4];  // [tile][head-dimension step]
+  uint4 v[8];     // [head-dimension block]
+};
+
+// K and V pieces of the 32 positions from t0.  Positions past Lmax lie
+// outside the resources and read zeros; the 16-byte V pieces never straddle
+// Lmax (it is a multiple of 8).
+__device__ __forceinline__ void attn_load(AttnStepLoads& ld, __amdgpu_buffer_rsrc_t kres, __amdgpu_buffer_rsrc_t vres,
+                                          int64_t Lmax, int64_t t0, int kb, int j) {
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    const int64_t t = t0 + 8 * (j >> 2) + 4 * tau + (j & 3);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t off = t < Lmax ? uint32_t((t * kHeadDim + 32 * s + 8 * kb) * 2) : 0x80000000u;
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(kres, off, 0, 0);
+      ld.k[tau][s] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+  }
+  const int64_t tv = t0 + 8 * kb;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int64_t d = 16 * c + j;
+    const uint32_t off = tv < Lmax ? uint32_t((d * Lmax + tv) * 2) : 0x80000000u;
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0);
+    ld.v[c] = make_uint4(v.x, v.y, v.z, v.w);
+  }
+}
+
+struct AttnState {
+  at_f32x4_t o[8];  // [head-dimension block]: lane (kb, n) rows 4 kb + r, column n
+  float m, l;       // running maximum (log2 units) and sum of head n (lane (kb, n))
+};
+
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+}
+
+// One step over positions t0 .. t0 + 31, of which those below `len` count.
+__device__ __forceinline__ void attn_step(AttnState& st, const AttnStepLoads& ld, const uint4 (&qf)[4], float sl2,
+                                         int64_t t0, int64_t len, int kb, int n) {
+  at_f32x4_t sc[2];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    sc[tau] = at_f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sc[tau] = at_mfma(ld.k[tau][s], qf[s], sc[tau]);
+  }
+  // lane (kb, n): head n, positions t0 + 8 kb + i, i = 4 tau + r
+  float x[8];
+  const int64_t base = t0 + 8 * kb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = sc[i >> 2][i & 3] * sl2;
+    x[i] = base + i < len ? v : -INFINITY;
+  }
+  float mt = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
+  mt = fmaxf(mt, __shfl_xor(mt, 16));
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  const float mn = fmaxf(st.m, mt);  // finite: position t0 < len is in this step
+  const float alpha = exp2f(st.m - mn);
+  float p[8], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = exp2f(x[i] - mn);
+    ps += p[i];
+  }
+  ps += __shfl_xor(ps, 16);
+  ps += __shfl_xor(ps, 32);
+  st.l = st.l * alpha + ps;
+  st.m = mn;
+  // P as operand A: high and low bf16 parts
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h = bf16_pair(p[2 * e], p[2 * e + 1]);
+    hi[e] = h;
+    lo[e] = bf16_pair(p[2 * e] - bf16_bits_to_f32(h & 0xFFFFu), p[2 * e + 1] - bf16_bits_to_f32(h >> 16));
+  }
+  const uint4 ph = make_uint4(hi[0], hi[1], hi[2], hi[3]), pl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  // V pieces of positions past the length are zeroed (stale cache slots)
+  uint4 vv[8];
+  const int64_t valid = len - base;  // positions of this lane's piece below the length
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    uint32_t w[4] = {ld.v[c].x, ld.v[c].y, ld.v[c].z, ld.v[c].w};
+    if (valid < 8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t keep = (2 * e < valid ? 0x0000FFFFu : 0u) | (2 * e + 1 < valid ? 0xFFFF0000u : 0u);
+        w[e] &= keep;
+      }
+    }
+    vv[c] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  // rescale the running output: its row 4 kb + r is head 4 kb + r, whose
+  // alpha lane 4 kb + r holds
+  float ar[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * kb + r);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st.o[c][r] *= ar[r];
+    st.o[c] = at_mfma(ph, vv[c], st.o[c]);
+    st.o[c] = at_mfma(pl, vv[c], st.o[c]);
+  }
+}
+
+__global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a) {
+  const int lane = threadIdx.x, kb = lane >> 4, n = lane & 15;
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int64_t Lmax = a.Lmax;
+  int64_t len = a.lens[b];
+  len = len < 0 ? 0 : (len > Lmax ? Lmax : len);
+  const int64_t t_begin = int64_t(s) * a.chunk;
+  const int64_t t_end = t_begin + a.chunk < len ? t_begin + a.chunk : len;
+
+  // query heads of the group as operand B (heads G .. 15 zero)
+  uint4 qf[4];
+  const int64_t hq = int64_t(g) * a.G + n;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    qf[st] = make_uint4(0u, 0u, 0u, 0u);
+    if (n < a.G) qf[st] = *reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.Hq + hq) * kHeadDim + 32 * st + 8 * kb);
+  }
+  const int64_t head = int64_t(b) * a.Hkv + g;
+  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.k + head * Lmax * kHeadDim), 0, uint32_t(Lmax * kHeadDim * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.vt + head * kHeadDim * Lmax), 0, uint32_t(Lmax * kHeadDim * 2), 0x00020000);
+
+  AttnState st;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) st.o[c] = at_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  if (t_begin < t_end) {
+    // two register sets: each step loads the next step's pieces before its
+    // own arithmetic (a step past the split reads in-bounds or zero pieces
+    // that are never used)
+    AttnStepLoads l0, l1;
+    attn_load(l0, kres, vres, Lmax, t_begin, kb, n);
+    int64_t t = t_begin;
+    for (; t + 32 < t_end; t += 64) {
+      attn_load(l1, kres, vres, Lmax, t + 32, kb, n);
+      attn_step(st, l0, qf, a.scale_log2, t, len, kb, n);
+      // unconditional: a conditional load would make the compiler wait for
+      // every load at the join, this one included
+      attn_load(l0, kres, vres, Lmax, t + 64, kb, n);
+      attn_step(st, l1, qf, a.scale_log2, t + 32, len, kb, n);
+    }
+    if (t < t_end) attn_step(st, l0, qf, a.scale_log2, t, len, kb, n);
+  }
+  if (n < a.G) {
+    const int64_t row = (int64_t(b) * a.Hq + hq) * a.S + s;
+    if (kb == 0) {
+      a.part_ml[2 * row] = st.m;
+      a.part_ml[2 * row + 1] = st.l;
+    }
+  }
+  // lane (kb, n): rows 4 kb + r (heads), column n of block c (dimension 16 c + n)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int hr = 4 * kb + r;
+    if (hr >= a.G) continue;
+    const int64_t row = (int64_t(b) * a.Hq + int64_t(g) * a.G + hr) * a.S + s;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a.part_o[row * kHeadDim + 16 * c + n] = st.o[c][r];
+  }
+}
+
+// One wavefront per (b, query head): merge the S splits in split order.
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+  const int lane = threadIdx.x;
+  const int64_t bh = int64_t(blockIdx.y) * a.Hq + blockIdx.x;
+  const float* ml = a.part_ml + bh * a.S * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < a.S; ++s) M = fmaxf(M, ml[2 * s]);
+  float o0 = 0.f, o1 = 0.f, L = 0.f;
+  if (M != -INFINITY) {
+    const float* po = a.part_o + bh * a.S * kHeadDim;
+    for (int s = 0; s < a.S; ++s) {
+      const float w = exp2f(ml[2 * s] - M);  // 0 for an empty split
+      L += w * ml[2 * s + 1];
+      o0 += w * po[s * kHeadDim + 2 * lane];
+      o1 += w * po[s * kHeadDim + 2 * lane + 1];
+    }
+    o0 /= L;
+    o1 /= L;
+  }
+  reinterpret_cast<uint32_t*>(a.out + bh * kHeadDim)[lane] = bf16_pair(o0, o1);
+}
+
+hipError_t launch_attn(const AttnPlan& p, const void* q, const void* k, const void* vt, const int32_t* lens,
+                       int64_t B, float scale, void* out, void* ws, hipStream_t st) {
+  AttnArgs a;
+  a.q = reinterpret_cast<const uint16_t*>(q);
+  a.k = reinterpret_cast<const uint16_t*>(k);
+  a.vt = reinterpret_cast<const uint16_t*>(vt);
+  a.lens = lens;
+  a.out = reinterpret_cast<uint16_t*>(out);
+  a.part_ml = reinterpret_cast<float*>(ws);
+  a.part_o = a.part_ml + B * p.Hq * p.S * 2;
+  a.scale_log2 = scale * kLog2e;
+  a.Lmax = p.Lmax;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = p.Hq / p.Hkv;
+  a.S = p.S;
+  a.chunk = p.chunk;
+  hipLaunchKernelGGL(attn_split_kernel, dim3(unsigned(p.S), unsigned(p.Hkv), unsigned(B)), dim3(64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(p.Hq), unsigned(B)), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace wqd

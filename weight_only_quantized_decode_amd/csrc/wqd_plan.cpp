@@ -435,4 +435,25 @@ int plan_act_quant(int64_t M, int64_t K, int* parts) {
   return kOK;
 }
 
+int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnPlan* out) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lmax < 1) return kEArg;
+  if (D != 128 || Hq % Hkv != 0 || Hq / Hkv > 16 || Lmax % 8 != 0) return kEShape;
+  if (Lmax * 128 * 2 >= (int64_t(1) << 31) || B > 65535 || Hkv > 65535 || Hq > 65535) return kEUnsupported;
+  AttnPlan p{};
+  p.Lmax = Lmax;
+  p.Hq = int(Hq);
+  p.Hkv = int(Hkv);
+  // about 8 wavefronts per compute unit, each split at least 64 positions
+  const int64_t pairs = B * Hkv;
+  const int64_t steps = ceil_div(Lmax, 32);
+  int64_t S = ceil_div(2048, pairs);
+  const int64_t max_s = steps / 2 > 1 ? steps / 2 : 1;
+  if (S > max_s) S = max_s;
+  p.chunk = int(32 * ceil_div(steps, S));
+  p.S = int(ceil_div(Lmax, p.chunk));
+  p.ws_bytes = size_t(B) * size_t(Hq) * size_t(p.S) * (2 + 128) * sizeof(float);
+  *out = p;
+  return kOK;
+}
+
 }  // namespace wqd

@@ -191,6 +191,17 @@ struct W8Plan {
 
 int plan_w8a8(int64_t M, int64_t N, int64_t K, W8Plan* out);
 
+// Decode attention split along the context: S splits of `chunk` positions (a
+// multiple of 32) per (sequence, KV head), one wavefront each; the partial
+// maxima, sums and outputs take B * Hq * S * (2 + 128) floats of workspace.
+struct AttnPlan {
+  int64_t Lmax;
+  int Hq, Hkv, S, chunk;
+  size_t ws_bytes;
+};
+
+int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnPlan* out);
+
 // The activation quantisation: G workgroups each reduce a contiguous range of
 // x to its largest |x| (G <= kActQuantParts, written to the workspace), then
 // every workgroup of the quantising kernel reduces the G values itself.
