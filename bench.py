@@ -497,6 +497,58 @@ def spec_accept_timing(B=64, k=4, V=128256, reps=50):
             "algorithmic_bytes": algo, "GBps": round(gbps, 1), "roofline_frac_hbm": round(gbps / 8000.0, 4)}
 
 
+ATTN_HQ, ATTN_HKV, ATTN_D = 64, 8, 128  # the 70B layer's grouped-query attention
+
+
+def attn_stack_timing(args, stream, B=32, ctx=2048, layers=80):
+    """Decode attention of every layer of the 70B-class stack for B sequences
+    of ctx positions (the pages' batch-32 snapshot: 80 layers x 8 KV heads x
+    128 x 2 bytes x 2 for keys and values = 671,088,640 bytes per sequence).
+    Each layer has its own caches, so a step reads 21.5 GB of KV from HBM.
+    One step = 80 wqd_decode_attention calls (split kernel and merge each),
+    replayed from a HIP graph."""
+    import math
+
+    import torch
+
+    import weight_only_quantized_decode_amd as wqd
+
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(2048 + B)
+    log(f"[bench] decode attention: {layers} layers, B={B}, {ctx} positions, {ATTN_HQ}/{ATTN_HKV} heads")
+    caches = []
+    for _ in range(layers):
+        c = wqd.alloc_kv_cache(B, ATTN_HKV, ctx, ATTN_D, device=dev)
+        c.k.normal_(generator=g)  # random entries: the tile order of the layout does not matter
+        c.v.normal_(generator=g)
+        caches.append(c)
+    q = torch.randn((B, ATTN_HQ, ATTN_D), generator=g, device=dev, dtype=torch.bfloat16)
+    out = torch.empty_like(q)
+    lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    ws = wqd.get_workspace(wqd.attn_workspace_bytes(B, ATTN_HQ, ATTN_HKV, ctx), dev)
+    scale = 1.0 / math.sqrt(ATTN_D)
+
+    def go():
+        for c in caches:
+            wqd.decode_attention(q, c, lens, scale, out=out, workspace=ws)
+
+    ms, samples = replay_timing(go, stream, args.steps, args.warmup, not args.no_graph)
+    kv = B * ATTN_HKV * ctx * ATTN_D * 2 * 2
+    per_layer = kv + 2 * (B * ATTN_HQ * ATTN_D * 2) + 4 * B
+    gbps = layers * per_layer / (ms / 1e3) / 1e9
+    res = {"workload": f"70b_decode_attention_{layers}l_b{B}_ctx{ctx}", "B": B, "context": ctx, "layers": layers,
+           "q_heads": ATTN_HQ, "kv_heads": ATTN_HKV, "head_dim": ATTN_D, "ms_per_step": round(ms, 4),
+           "us_per_layer": round(ms * 1e3 / layers, 2), "kv_bytes_per_step": layers * kv,
+           "algorithmic_bytes_per_step": layers * per_layer, "GBps": round(gbps, 2),
+           "step_samples_ms": {"n": len(samples), "median": round(statistics.median(samples), 4),
+                               "min": round(min(samples), 4), "max": round(max(samples), 4)},
+           "kernel": "attn_split_kernel + attn_combine_kernel per layer (both timed)"}
+    del caches
+    free_cache()
+    return res
+
+
 def pct(v, ceil):
     return None if not ceil else round(100 * v / ceil, 2)
 
@@ -527,6 +579,30 @@ def roofline_of(wl, res):
     return r
 
 
+def attn_main(args, stream, ceiling):
+    """--workload attn_70b: the stack's decode attention as the headline."""
+    B = args.m if args.m > 1 else 32
+    a = attn_stack_timing(args, stream, B=B, layers=args.layers or 80)
+    per_layer_bytes = a["algorithmic_bytes_per_step"] / a["layers"]
+    achieved = per_layer_bytes / (a["us_per_layer"] * 1e-6) / 1e9
+    out = {
+        "metric": "weight-stream GB/s (% of HBM peak) & us per layer-stack step, 70B W4A16/FP8/BF16",
+        "value": a["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": a["ms_per_step"], "us_per_step": round(a["ms_per_step"] * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": a["workload"], "B": B, "context": a["context"], "layers": a["layers"],
+                   "graph": not args.no_graph},
+        "pct_hbm_peak": round(100 * a["GBps"] / HBM_PEAK_GBPS, 2),
+        "hbm_read_ceiling_GBps": None if ceiling[0] is None else round(ceiling[0], 1),
+        "pct_measured_read_ceiling": pct(a["GBps"], ceiling[0]),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": a["kernel"],
+                     "avg_launch_us": a["us_per_layer"], "bytes_per_launch": round(per_layer_bytes)},
+        "attention": a,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -546,11 +622,14 @@ def main():
         pmc_probe()
         return
     fused = not args.separate
-    wl = make_workload(args.workload, args.m, args.layers, fused)
     ceiling = (None, None) if args.no_ceiling else hbm_ceiling()
     if ceiling[0]:
         log(f"[bench] HBM ceiling: read {ceiling[0]:.0f} GB/s, copy {ceiling[1]:.0f} GB/s")
     stream = torch.cuda.Stream()
+    if args.workload == "attn_70b":
+        attn_main(args, stream, ceiling)
+        return
+    wl = make_workload(args.workload, args.m, args.layers, fused)
 
     packed = pack_stack(wl)
     head = time_step(wl, packed, args, stream, dominant=True, shapes=not args.no_shapes)
@@ -578,6 +657,24 @@ def main():
                 targets.append(time_step(with_m(fp8_wl, M), fp8_packed, args, stream))
         del fp8_packed
         free_cache()
+
+    # the survey's next rows, each from its own replays: W8A8-FP8 at the widest
+    # verify width, and the stack's decode attention at the batch-32 snapshot
+    next_rows = {}
+    if is_stack and not args.no_targets and args.workload == "w4a16_70b" and fused:
+        w8 = make_workload("w8a8:gate", 1024, None, True)
+        w8_packed = pack_stack(w8)
+        r = time_step(w8, w8_packed, args, stream, dominant=True)
+        del w8_packed
+        free_cache()
+        rr = roofline_of(w8, r)
+        next_rows["w8a8_gate_m1024"] = {"ms_per_call": r["ms_per_step"], "product_us": rr["avg_launch_us"],
+                                        "product_TFLOPs": rr["achieved"], "frac_fp8_peak": rr["frac"],
+                                        "workload": w8.name, "weight_copies": copies_for(w8)}
+        a = attn_stack_timing(args, stream)
+        a["pct_measured_read_ceiling"] = pct(a["GBps"], ceiling[0])
+        a["frac_hbm_peak"] = round(a["GBps"] / HBM_PEAK_GBPS, 4)
+        next_rows["decode_attention"] = a
 
     ms = head["ms_per_step"]
     gbps = head["GBps"]
@@ -621,6 +718,8 @@ def main():
         out["targets"] = targets
     if "shapes" in head:
         out["shapes"] = head["shapes"]
+    if next_rows:
+        out["next_rows"] = next_rows
     if wl.M >= 16:
         tflops = wl.step_flops() / (ms / 1e3) / 1e12
         out["mfma_util_pct"] = round(100 * tflops / (FP8_MFMA_PEAK_TFLOPS if wl.act == "fp8" else

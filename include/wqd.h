@@ -223,23 +223,43 @@ int wqd_qgemm_w8a8(const void* x_codes, const float* x_scale, int64_t M, int64_t
  * products and sums in float32 from the bf16 inputs (the softmax weights
  * are not rounded to bf16), rounded to bf16; len[b] = 0 gives zeros.
  *   q          device bf16 [B][Hq][D]
- *   k_cache    device bf16 [B][Hkv][Lmax][D]   (head dimension contiguous)
- *   v_cache_t  device bf16 [B][Hkv][D][Lmax]   (V transposed: positions
- *              contiguous; the writer of a new position t stores V[b, g, t, d]
- *              at [b][g][d][t])
+ *   k_cache,   device bf16, B * Hkv * Lmax * D elements each, in the
+ *   v_cache    library's tiled layout, written by wqd_kv_pack / wqd_kv_append
+ *              (per (b, g), 1 KiB tiles in matrix-core operand order so that
+ *              every load of the kernel is one contiguous 1 KiB; the element
+ *              offsets of position t, dimension d within a (b, g) region of
+ *              Lmax * D elements are:
+ *                K: ((t / 16) * 4 + d / 32) * 512 + (((d % 32) / 8) * 16 + t % 16) * 8 + d % 8;
+ *                V: ((t / 32) * 8 + d / 16) * 512 + (kb * 16 + d % 16) * 8 + e,
+ *                   u = t % 32, kb = (u % 16) / 4, e = 4 * (u / 16) + u % 4)
  *   lengths    device int32 [B]: positions used per sequence (clamped to
  *              [0, Lmax]); cache entries at or past a length are never used,
  *              whatever they hold
  *   out        device bf16 [B][Hq][D]
  *   workspace  device, >= wqd_attn_workspace_bytes (partial maxima, sums and
  *              outputs of the splits), contents on entry do not matter.
- * D = 128, Hq a multiple of Hkv with Hq / Hkv <= 16, Lmax a multiple of 8 and
- * Lmax * D * 2 < 2^31 (else WQD_E_SHAPE / WQD_E_UNSUPPORTED).  Deterministic.
+ * D = 128, Hq a multiple of Hkv with Hq / Hkv <= 16, Lmax a multiple of 32
+ * and Lmax * D * 2 < 2^31 (else WQD_E_SHAPE / WQD_E_UNSUPPORTED).
+ * Deterministic.
+ *
+ * wqd_kv_pack: logical k, v device bf16 [B][Hkv][L][D] (L <= Lmax) into the
+ *   caches' positions 0 .. L - 1 (later positions untouched).
+ * wqd_kv_append: one new position per sequence, k_new / v_new device bf16
+ *   [B][Hkv][D] at positions[b] (device int32 [B]; a position outside
+ *   [0, Lmax) writes nothing) - the decode step's cache write.
+ * wqd_kv_unpack: the caches back to logical device bf16 [B][Hkv][Lmax][D]
+ *   (parity of the layout).
  */
 int wqd_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, size_t* bytes);
-int wqd_decode_attention(const void* q, const void* k_cache, const void* v_cache_t, const int32_t* lengths,
+int wqd_decode_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, float scale, void* out,
                          void* workspace, size_t workspace_bytes, void* stream);
+int wqd_kv_pack(const void* k, const void* v, int64_t B, int64_t Hkv, int64_t L, int64_t Lmax, int64_t D,
+                void* k_cache, void* v_cache, void* stream);
+int wqd_kv_append(const void* k_new, const void* v_new, const int32_t* positions, int64_t B, int64_t Hkv,
+                  int64_t Lmax, int64_t D, void* k_cache, void* v_cache, void* stream);
+int wqd_kv_unpack(const void* k_cache, const void* v_cache, int64_t B, int64_t Hkv, int64_t Lmax, int64_t D,
+                  void* k_out, void* v_out, void* stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

@@ -1,11 +1,13 @@
-"""GPU parity of decode attention (wqd_decode_attention) against the oracle.
+"""GPU parity of decode attention (wqd_decode_attention) against the oracle,
+and of the KV cache writers (wqd_kv_pack / wqd_kv_append / wqd_kv_unpack).
 
 Cases: grouped-query groups of 1, 4, 8 and 16 query heads per KV head;
 lengths from 0 to Lmax in one batch (ragged last steps, empty sequences,
 splits past a sequence's end); cache slots past each length filled with NaN
 and infinities (never used); the 70B layer at the pages' batch-32 snapshot
 (64 query heads, 8 KV heads of 128, 2048 positions) on sampled heads;
-determinism.  Tolerance as for the linear layer (tests/parity.py)."""
+determinism; the cache layout round trip, bit for bit, and a decode step's
+append.  Tolerance as for the linear layer (tests/parity.py)."""
 import math
 
 import numpy as np
@@ -33,10 +35,15 @@ def make(seed, B, Hq, Hkv, Lmax, lens, poison=True):
     return q, k, v
 
 
+def packed(k, v):
+    B, Hkv, Lmax, _ = k.shape
+    cache = wqd.alloc_kv_cache(B, Hkv, Lmax, device=DEV)
+    return wqd.kv_pack(k.to(DEV), v.to(DEV), cache)
+
+
 def run(q, k, v, lens, scale):
     lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
-    vt = v.transpose(2, 3).contiguous()
-    out = wqd.decode_attention(q.to(DEV), k.to(DEV), vt.to(DEV), lens_d, scale)
+    out = wqd.decode_attention(q.to(DEV), packed(k, v), lens_d, scale)
     torch.cuda.synchronize()
     return out
 
@@ -59,8 +66,8 @@ def check(q, k, v, lens, scale, what, heads=None):
 
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 2), (64, 8), (32, 2)])
 def test_groups_and_ragged_lengths(Hq, Hkv):
-    Lmax = 1000  # a multiple of 8, not of 32
-    lens = [1, 31, 32, 33, 1000, 517, 0, 64]
+    Lmax = 1024
+    lens = [1, 31, 32, 33, 1024, 517, 0, 1000]
     q, k, v = make(Hq + Hkv, len(lens), Hq, Hkv, Lmax, lens)
     out = check(q, k, v, lens, 1 / math.sqrt(128), f"attn Hq={Hq} Hkv={Hkv}")
     assert not torch.any(out[6].view(torch.int16))  # the empty sequence gives zeros
@@ -90,8 +97,38 @@ def test_deterministic_and_shape_errors():
     b = run(q, k, v, lens, 0.088)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     with pytest.raises(wqd.WqdError) as e:
-        wqd.attn_workspace_bytes(1, 64, 8, 1001)  # Lmax % 8
+        wqd.attn_workspace_bytes(1, 64, 8, 1000)  # Lmax % 32
     assert e.value.status == 2
     with pytest.raises(wqd.WqdError) as e:
         wqd.attn_workspace_bytes(1, 64, 2, 1024)  # 32 query heads per KV head
     assert e.value.status == 2
+
+
+def test_cache_layout_round_trip_and_append():
+    B, Hkv, Lmax = 3, 8, 256
+    g = torch.Generator().manual_seed(11)
+    k = torch.randn((B, Hkv, Lmax, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, Lmax, 128), generator=g).to(torch.bfloat16)
+    cache = packed(k, v)
+    k2, v2 = wqd.kv_unpack(cache)
+    torch.cuda.synchronize()
+    assert torch.equal(k2.cpu().view(torch.int16), k.view(torch.int16))
+    assert torch.equal(v2.cpu().view(torch.int16), v.view(torch.int16))
+    # a decode step: append one position per sequence, then attend over it
+    kn = torch.randn((B, Hkv, 128), generator=g).to(torch.bfloat16)
+    vn = torch.randn((B, Hkv, 128), generator=g).to(torch.bfloat16)
+    pos = [17, 255, 300]  # the last is outside the cache: nothing written
+    wqd.kv_append(kn.to(DEV), vn.to(DEV), torch.tensor(pos, dtype=torch.int32, device=DEV), cache)
+    k3, v3 = wqd.kv_unpack(cache)
+    torch.cuda.synchronize()
+    k_ref, v_ref = k.clone(), v.clone()
+    for b, t in enumerate(pos[:2]):
+        k_ref[b, :, t], v_ref[b, :, t] = kn[b], vn[b]
+    assert torch.equal(k3.cpu().view(torch.int16), k_ref.view(torch.int16))
+    assert torch.equal(v3.cpu().view(torch.int16), v_ref.view(torch.int16))
+    q = torch.randn((B, 64, 128), generator=g).to(torch.bfloat16)
+    lens = [18, 256, 200]
+    out = wqd.decode_attention(q.to(DEV), cache, torch.tensor(lens, dtype=torch.int32, device=DEV), 0.09)
+    torch.cuda.synchronize()
+    o64 = oracle.decode_attention_exact(bits(q), bits(k_ref), bits(v_ref), np.array(lens), 0.09)
+    compare_y(bf16_bits(out).reshape(-1, 128), o64.reshape(-1, 128), "attention after append")

@@ -65,6 +65,9 @@ def lib() -> ctypes.CDLL:
             "wqd_attn_workspace_bytes": (i32, [i64, i64, i64, i64, i64, psz]),
             "wqd_decode_attention": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, vp, sz,
                                             vp]),
+            "wqd_kv_pack": (i32, [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp]),
+            "wqd_kv_append": (i32, [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp]),
+            "wqd_kv_unpack": (i32, [vp, vp, i64, i64, i64, i64, vp, vp, vp]),
             "wqd_w8a8_workspace_bytes": (i32, [i64, i64, i64, psz]),
             "wqd_qgemm_w8a8": (i32, [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]),
             "wqd_dequant": (i32, [i32, vp, vp, vp, i64, i64, vp, vp]),
@@ -303,26 +306,73 @@ def attn_workspace_bytes(B: int, Hq: int, Hkv: int, Lmax: int, D: int = 128) -> 
     return b.value
 
 
-def decode_attention(q, k_cache, v_cache_t, lengths, scale: float, out=None, workspace=None, stream=None):
-    """wqd_decode_attention: q bf16 [B, Hq, D], k_cache bf16 [B, Hkv, Lmax, D],
-    v_cache_t bf16 [B, Hkv, D, Lmax] (V transposed), lengths int32 [B] ->
-    out bf16 [B, Hq, D]."""
+@dataclass
+class KVCache:
+    """One layer's KV cache in the library's tiled layout (device bf16)."""
+    B: int
+    Hkv: int
+    Lmax: int
+    k: "object"
+    v: "object"
+    D: int = 128
+
+
+def alloc_kv_cache(B: int, Hkv: int, Lmax: int, D: int = 128, device="cuda") -> KVCache:
+    import torch
+
+    n = B * Hkv * Lmax * D
+    return KVCache(B, Hkv, Lmax, torch.zeros(n, dtype=torch.bfloat16, device=device),
+                   torch.zeros(n, dtype=torch.bfloat16, device=device), D)
+
+
+def kv_pack(k, v, cache: KVCache, stream=None) -> KVCache:
+    """wqd_kv_pack: logical k, v bf16 [B, Hkv, L, D] into positions 0 .. L - 1."""
+    B, Hkv, L, D = k.shape
+    if tuple(v.shape) != (B, Hkv, L, D) or not (k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("k and v must be contiguous [B, Hkv, L, D] tensors")
+    _check(lib().wqd_kv_pack(k.data_ptr(), v.data_ptr(), B, Hkv, L, cache.Lmax, D, cache.k.data_ptr(),
+                             cache.v.data_ptr(), _stream(stream)), "wqd_kv_pack")
+    return cache
+
+
+def kv_append(k_new, v_new, positions, cache: KVCache, stream=None) -> KVCache:
+    """wqd_kv_append: k_new, v_new bf16 [B, Hkv, D] at positions int32 [B]."""
+    _check(lib().wqd_kv_append(k_new.data_ptr(), v_new.data_ptr(), positions.data_ptr(), cache.B, cache.Hkv,
+                               cache.Lmax, cache.D, cache.k.data_ptr(), cache.v.data_ptr(), _stream(stream)),
+           "wqd_kv_append")
+    return cache
+
+
+def kv_unpack(cache: KVCache, stream=None):
+    """wqd_kv_unpack: (k, v) logical bf16 [B, Hkv, Lmax, D]."""
+    import torch
+
+    shape = (cache.B, cache.Hkv, cache.Lmax, cache.D)
+    k = torch.empty(shape, dtype=torch.bfloat16, device=cache.k.device)
+    v = torch.empty(shape, dtype=torch.bfloat16, device=cache.k.device)
+    _check(lib().wqd_kv_unpack(cache.k.data_ptr(), cache.v.data_ptr(), cache.B, cache.Hkv, cache.Lmax, cache.D,
+                               k.data_ptr(), v.data_ptr(), _stream(stream)), "wqd_kv_unpack")
+    return k, v
+
+
+def decode_attention(q, cache: KVCache, lengths, scale: float, out=None, workspace=None, stream=None):
+    """wqd_decode_attention: q bf16 [B, Hq, D] against a KVCache, lengths
+    int32 [B] -> out bf16 [B, Hq, D]."""
     import torch
 
     B, Hq, D = q.shape
-    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
-    for t, shape, dt in ((q, (B, Hq, D), torch.bfloat16), (k_cache, (B, Hkv, Lmax, D), torch.bfloat16),
-                         (v_cache_t, (B, Hkv, D, Lmax), torch.bfloat16), (lengths, (B,), torch.int32)):
-        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
-            raise ValueError(f"decode_attention: expected a contiguous {dt} tensor of shape {shape}")
+    if (B, D) != (cache.B, cache.D) or q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bfloat16 [B, Hq, D] tensor matching the cache")
+    if tuple(lengths.shape) != (B,) or lengths.dtype != torch.int32:
+        raise ValueError("lengths must be int32 [B]")
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
     if workspace is None:
-        workspace = get_workspace(attn_workspace_bytes(B, Hq, Hkv, Lmax, D), q.device)
+        workspace = get_workspace(attn_workspace_bytes(B, Hq, cache.Hkv, cache.Lmax, D), q.device)
     wsb = workspace.numel() * workspace.element_size()
-    _check(lib().wqd_decode_attention(q.data_ptr(), k_cache.data_ptr(), v_cache_t.data_ptr(), lengths.data_ptr(), B,
-                                      Hq, Hkv, Lmax, D, float(scale), out.data_ptr(), workspace.data_ptr(), wsb,
-                                      _stream(stream)), "wqd_decode_attention")
+    _check(lib().wqd_decode_attention(q.data_ptr(), cache.k.data_ptr(), cache.v.data_ptr(), lengths.data_ptr(), B,
+                                      Hq, cache.Hkv, cache.Lmax, D, float(scale), out.data_ptr(),
+                                      workspace.data_ptr(), wsb, _stream(stream)), "wqd_decode_attention")
     return out
 
 

@@ -23,7 +23,9 @@ NO_PACKED_F32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Per-file flags: the tiled matrix-core kernel keeps its accumulators in VGPRs
 # (in AGPRs the compiler copied them at every loop edge, and the 4-wavefront
 # instances needed over 256 registers).
-EXTRA = {"wqd_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "wqd_w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"wqd_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "wqd_w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         # decode attention: 234 registers in VGPR form (two wavefronts per SIMD) against 272 with AGPRs
+         "wqd_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -193,18 +193,59 @@ int wqd_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, i
   return WQD_OK;
 }
 
-int wqd_decode_attention(const void* q, const void* k_cache, const void* v_cache_t, const int32_t* lengths,
+int wqd_decode_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, float scale, void* out,
                          void* workspace, size_t workspace_bytes, void* stream) {
   wqd::AttnPlan p;
   const int st = wqd::plan_attn(B, Hq, Hkv, Lmax, D, &p);
   if (st != wqd::kOK) return st;
-  if (!q || !k_cache || !v_cache_t || !lengths || !out || !workspace) return WQD_E_ARG;
+  if (!q || !k_cache || !v_cache || !lengths || !out || !workspace) return WQD_E_ARG;
   if (workspace_bytes < p.ws_bytes) return WQD_E_WORKSPACE;
-  if (!wqd::aligned16(q) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache_t) || !wqd::aligned16(out) ||
+  if (!wqd::aligned16(q) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache) || !wqd::aligned16(out) ||
       !wqd::aligned16(workspace) || reinterpret_cast<uintptr_t>(lengths) % 4)
     return WQD_E_ALIGN;
-  return hip_status(wqd::launch_attn(p, q, k_cache, v_cache_t, lengths, B, scale, out, workspace, as_stream(stream)));
+  return hip_status(wqd::launch_attn(p, q, k_cache, v_cache, lengths, B, scale, out, workspace, as_stream(stream)));
+}
+
+namespace {
+int check_kv(int64_t B, int64_t Hkv, int64_t Lmax, int64_t D) {
+  wqd::AttnPlan p;
+  return wqd::plan_attn(B, Hkv, Hkv, Lmax, D, &p);
+}
+}  // namespace
+
+int wqd_kv_pack(const void* k, const void* v, int64_t B, int64_t Hkv, int64_t L, int64_t Lmax, int64_t D,
+                void* k_cache, void* v_cache, void* stream) {
+  const int st = check_kv(B, Hkv, Lmax, D);
+  if (st != WQD_OK) return st;
+  if (L < 0 || L > Lmax) return WQD_E_ARG;
+  if (!k || !v || !k_cache || !v_cache) return WQD_E_ARG;
+  if (!wqd::aligned16(k) || !wqd::aligned16(v) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache))
+    return WQD_E_ALIGN;
+  return hip_status(wqd::launch_kv_copy(true, k, v, k_cache, v_cache, B * Hkv, L, Lmax, as_stream(stream)));
+}
+
+int wqd_kv_unpack(const void* k_cache, const void* v_cache, int64_t B, int64_t Hkv, int64_t Lmax, int64_t D,
+                  void* k_out, void* v_out, void* stream) {
+  const int st = check_kv(B, Hkv, Lmax, D);
+  if (st != WQD_OK) return st;
+  if (!k_out || !v_out || !k_cache || !v_cache) return WQD_E_ARG;
+  if (!wqd::aligned16(k_out) || !wqd::aligned16(v_out) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache))
+    return WQD_E_ALIGN;
+  return hip_status(wqd::launch_kv_copy(false, k_cache, v_cache, k_out, v_out, B * Hkv, Lmax, Lmax,
+                                        as_stream(stream)));
+}
+
+int wqd_kv_append(const void* k_new, const void* v_new, const int32_t* positions, int64_t B, int64_t Hkv,
+                  int64_t Lmax, int64_t D, void* k_cache, void* v_cache, void* stream) {
+  const int st = check_kv(B, Hkv, Lmax, D);
+  if (st != WQD_OK) return st;
+  if (!k_new || !v_new || !positions || !k_cache || !v_cache) return WQD_E_ARG;
+  if (!wqd::aligned16(k_new) || !wqd::aligned16(v_new) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache) ||
+      reinterpret_cast<uintptr_t>(positions) % 4)
+    return WQD_E_ALIGN;
+  return hip_status(wqd::launch_kv_append(k_new, v_new, positions, B, Hkv, Lmax, k_cache, v_cache,
+                                          as_stream(stream)));
 }
 
 int wqd_dequant(int fmt, const void* w_packed, const void* scales, const void* zeros, int64_t N, int64_t K,

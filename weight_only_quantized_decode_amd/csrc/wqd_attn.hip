@@ -10,32 +10,39 @@
 // ("LLM 推理是怎么变快的", section 2.3): the G = Hq / Hkv query heads of a
 // group read one KV head, so one pass over that head's cache serves all G.
 //
-// Cache layout (library-defined, caller-written): K [B][Hkv][Lmax][128] with
-// the head dimension contiguous, V [B][Hkv][128][Lmax] with positions
-// contiguous (V is stored transposed so the product over positions reads
-// contiguous 16-byte pieces, as the product over the head dimension does for K).
+// Cache layout (library-defined; wqd_kv_pack / wqd_kv_append write it): per
+// (sequence b, KV head g), 1 KiB tiles in the operand order of the matrix
+// cores, so that every wavefront load is one contiguous 1 KiB:
+//   K: tile (t / 16) * 4 + d / 32 holds positions 16 (t / 16) .. + 15 x head
+//      dimensions 32 (d / 32) .. + 31: lane 16 kb + j (kb = (d % 32) / 8,
+//      j = t % 16) holds the 8 dimensions 8 kb .. 8 kb + 7 of position j;
+//   V: tile (t / 32) * 8 + d / 16 holds positions 32 (t / 32) .. + 31 x head
+//      dimensions 16 (d / 16) .. + 15: lane 16 kb + n (n = d % 16) holds 8
+//      positions u = t % 32 of dimension n, element e = 4 (u / 16) + u % 4
+//      for kb = (u % 16) / 4, i.e. positions 4 kb .. 4 kb + 3 and
+//      16 + 4 kb .. 16 + 4 kb + 3 (the order in which the score tiles leave
+//      the softmax weights, below).
+// Both take Lmax * 128 * 2 bytes per (b, g); Lmax is a multiple of 32.
 //
 // attn_split_kernel: one wavefront per (sequence b, KV head g, split s); the
 // split's positions in steps of 32.  Per step, on bf16 matrix cores
 // (v_mfma_f32_16x16x32_bf16):
-//   * S^T = K Q^T as two 16-position tiles x 4 head-dimension steps.  A = key
-//     rows: tile tau's row j is position 8 (j / 4) + 4 tau + (j % 4) of the
-//     step, so that its output row 4 kb + r is position 8 kb + 4 tau + r and
-//     lane (kb, n) ends up with the 8 consecutive positions 8 kb .. 8 kb + 7
-//     of query head n; B = Q^T, lane (kb, n) holding 8 head dimensions of
-//     query head n of the group (heads G .. 15 zero);
+//   * S^T = K Q^T as two 16-position tiles x 4 head-dimension steps: A = one
+//     K tile (one 1 KiB load), B = Q^T, lane (kb, n) holding 8 head
+//     dimensions of query head n of the group (heads G .. 15 zero).  Output
+//     row 4 kb + r of tile tau is position 16 tau + 4 kb + r, so lane (kb, n)
+//     ends up with 8 positions of query head n;
 //   * online softmax in float32 with exp2 (scores times scale log2 e): the
 //     running maximum and sum per head, reduced over the four lanes of a head
 //     (shfl_xor 16, 32); positions at or past the sequence's length are set
 //     to -inf by selection and their values to 0, so stale cache contents
 //     never reach the sums;
 //   * O += P V as 8 head-dimension blocks of 16: A = P, which the score tiles
-//     already left in operand order (lane (kb, n): head n, positions
-//     8 kb .. 8 kb + 7), split into bf16 high and low parts (two multiplies,
-//     error ~2^-17 of each weight) so P is not rounded to 8 bits; B = V
-//     straight from the transposed cache (lane (kb, n): dimension n of the
-//     block, positions 8 kb .. 8 kb + 7, one 16-byte load);
-//   * the next step's K and V pieces are loaded before this step's arithmetic.
+//     left in operand order (lane (kb, n): head n, the 8 positions above),
+//     split into bf16 high and low parts (two multiplies, error ~2^-17 of
+//     each weight) so P is not rounded to 8 bits; B = one V tile, whose lane
+//     (kb, n) holds dimension n at the same 8 positions;
+//   * the next step's tiles are loaded before this step's arithmetic.
 // Each wavefront writes its running maximum, sum and unnormalised output per
 // head to the workspace.  attn_combine_kernel then merges the splits of each
 // (b, head) in split order: o = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s,
@@ -59,8 +66,8 @@ __device__ __forceinline__ at_f32x4_t at_mfma(uint4 a, uint4 b, at_f32x4_t c) {
 
 struct AttnArgs {
   const uint16_t* q;    // [B][Hq][128]
-  const uint16_t* k;    // [B][Hkv][Lmax][128]
-  const uint16_t* vt;   // [B][Hkv][128][Lmax]
+  const uint16_t* k;    // K tiles, Lmax * 128 per (b, g)
+  const uint16_t* v;    // V tiles, Lmax * 128 per (b, g)
   const int32_t* lens;  // [B]
   uint16_t* out;        // [B][Hq][128]
   float* part_ml;       // [B][Hq][S][2]: running maximum (log2 units), sum
@@ -75,27 +82,22 @@ struct AttnStepLoads {
   uint4 v[8];     // [head-dimension block]
 };
 
-// K and V pieces of the 32 positions from t0.  Positions past Lmax lie
-// outside the resources and read zeros; the 16-byte V pieces never straddle
-// Lmax (it is a multiple of 8).
+// The K and V tiles of the 32 positions from t0 (a multiple of 32): 16 loads
+// of one contiguous 1 KiB each.  Past Lmax the tiles lie outside the
+// resources and read zeros.
 __device__ __forceinline__ void attn_load(AttnStepLoads& ld, __amdgpu_buffer_rsrc_t kres, __amdgpu_buffer_rsrc_t vres,
-                                          int64_t Lmax, int64_t t0, int kb, int j) {
+                                          int64_t t0, int lane) {
+  const uint32_t kt = uint32_t(t0 / 16) * 4, vt = uint32_t(t0 / 32) * 8;
 #pragma unroll
-  for (int tau = 0; tau < 2; ++tau) {
-    const int64_t t = t0 + 8 * (j >> 2) + 4 * tau + (j & 3);
+  for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint32_t off = t < Lmax ? uint32_t((t * kHeadDim + 32 * s + 8 * kb) * 2) : 0x80000000u;
-      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(kres, off, 0, 0);
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(kres, lane * 16, (kt + 4 * tau + s) * 1024, 0);
       ld.k[tau][s] = make_uint4(v.x, v.y, v.z, v.w);
     }
-  }
-  const int64_t tv = t0 + 8 * kb;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const int64_t d = 16 * c + j;
-    const uint32_t off = tv < Lmax ? uint32_t((d * Lmax + tv) * 2) : 0x80000000u;
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(vres, lane * 16, (vt + c) * 1024, 0);
     ld.v[c] = make_uint4(v.x, v.y, v.z, v.w);
   }
 }
@@ -110,7 +112,7 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
 }
 
 // One step over positions t0 .. t0 + 31, of which those below `len` count.
-__device__ __forceinline__ void attn_step(AttnState& st, const AttnStepLoads& ld, const uint4 (&qf)[4], float sl2,
+__device__ __forceinline__ void attn_step(AttnState& st, AttnStepLoads& ld, const uint4 (&qf)[4], float sl2,
                                          int64_t t0, int64_t len, int kb, int n) {
   at_f32x4_t sc[2];
 #pragma unroll
@@ -119,13 +121,13 @@ __device__ __forceinline__ void attn_step(AttnState& st, const AttnStepLoads& ld
 #pragma unroll
     for (int s = 0; s < 4; ++s) sc[tau] = at_mfma(ld.k[tau][s], qf[s], sc[tau]);
   }
-  // lane (kb, n): head n, positions t0 + 8 kb + i, i = 4 tau + r
+  // lane (kb, n): head n, position t0 + 16 tau + 4 kb + r in element i = 4 tau + r
   float x[8];
-  const int64_t base = t0 + 8 * kb;
+  const int64_t rel = len - t0 - 4 * kb;  // element i counts when 16 (i / 4) + i % 4 < rel
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float v = sc[i >> 2][i & 3] * sl2;
-    x[i] = base + i < len ? v : -INFINITY;
+    x[i] = 16 * (i >> 2) + (i & 3) < rel ? v : -INFINITY;
   }
   float mt = x[0];
 #pragma unroll
@@ -153,20 +155,21 @@ __device__ __forceinline__ void attn_step(AttnState& st, const AttnStepLoads& ld
     lo[e] = bf16_pair(p[2 * e] - bf16_bits_to_f32(h & 0xFFFFu), p[2 * e + 1] - bf16_bits_to_f32(h >> 16));
   }
   const uint4 ph = make_uint4(hi[0], hi[1], hi[2], hi[3]), pl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-  // V pieces of positions past the length are zeroed (stale cache slots)
-  uint4 vv[8];
-  const int64_t valid = len - base;  // positions of this lane's piece below the length
+  // V elements of positions past the length are zeroed (stale cache slots);
+  // only a step that reaches the length has any (a wave-uniform test)
+  if (t0 + 32 > len) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint32_t w[4] = {ld.v[c].x, ld.v[c].y, ld.v[c].z, ld.v[c].w};
-    if (valid < 8) {
+    for (int c = 0; c < 8; ++c) {
+      uint32_t w[4] = {ld.v[c].x, ld.v[c].y, ld.v[c].z, ld.v[c].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t keep = (2 * e < valid ? 0x0000FFFFu : 0u) | (2 * e + 1 < valid ? 0xFFFF0000u : 0u);
+        const int i0 = 2 * e, i1 = 2 * e + 1;
+        const uint32_t keep = (16 * (i0 >> 2) + (i0 & 3) < rel ? 0x0000FFFFu : 0u) |
+                              (16 * (i1 >> 2) + (i1 & 3) < rel ? 0xFFFF0000u : 0u);
         w[e] &= keep;
       }
+      ld.v[c] = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    vv[c] = make_uint4(w[0], w[1], w[2], w[3]);
   }
   // rescale the running output: its row 4 kb + r is head 4 kb + r, whose
   // alpha lane 4 kb + r holds
@@ -177,8 +180,8 @@ __device__ __forceinline__ void attn_step(AttnState& st, const AttnStepLoads& ld
   for (int c = 0; c < 8; ++c) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) st.o[c][r] *= ar[r];
-    st.o[c] = at_mfma(ph, vv[c], st.o[c]);
-    st.o[c] = at_mfma(pl, vv[c], st.o[c]);
+    st.o[c] = at_mfma(ph, ld.v[c], st.o[c]);
+    st.o[c] = at_mfma(pl, ld.v[c], st.o[c]);
   }
 }
 
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.k + head * Lmax * kHeadDim), 0, uint32_t(Lmax * kHeadDim * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.vt + head * kHeadDim * Lmax), 0, uint32_t(Lmax * kHeadDim * 2), 0x00020000);
+      const_cast<uint16_t*>(a.v + head * Lmax * kHeadDim), 0, uint32_t(Lmax * kHeadDim * 2), 0x00020000);
 
   AttnState st;
 #pragma unroll
@@ -215,14 +218,14 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a) {
     // own arithmetic (a step past the split reads in-bounds or zero pieces
     // that are never used)
     AttnStepLoads l0, l1;
-    attn_load(l0, kres, vres, Lmax, t_begin, kb, n);
+    attn_load(l0, kres, vres, t_begin, lane);
     int64_t t = t_begin;
     for (; t + 32 < t_end; t += 64) {
-      attn_load(l1, kres, vres, Lmax, t + 32, kb, n);
+      attn_load(l1, kres, vres, t + 32, lane);
       attn_step(st, l0, qf, a.scale_log2, t, len, kb, n);
       // unconditional: a conditional load would make the compiler wait for
       // every load at the join, this one included
-      attn_load(l0, kres, vres, Lmax, t + 64, kb, n);
+      attn_load(l0, kres, vres, t + 64, lane);
       attn_step(st, l1, qf, a.scale_log2, t + 32, len, kb, n);
     }
     if (t < t_end) attn_step(st, l0, qf, a.scale_log2, t, len, kb, n);
@@ -267,12 +270,12 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   reinterpret_cast<uint32_t*>(a.out + bh * kHeadDim)[lane] = bf16_pair(o0, o1);
 }
 
-hipError_t launch_attn(const AttnPlan& p, const void* q, const void* k, const void* vt, const int32_t* lens,
+hipError_t launch_attn(const AttnPlan& p, const void* q, const void* k, const void* v, const int32_t* lens,
                        int64_t B, float scale, void* out, void* ws, hipStream_t st) {
   AttnArgs a;
   a.q = reinterpret_cast<const uint16_t*>(q);
   a.k = reinterpret_cast<const uint16_t*>(k);
-  a.vt = reinterpret_cast<const uint16_t*>(vt);
+  a.v = reinterpret_cast<const uint16_t*>(v);
   a.lens = lens;
   a.out = reinterpret_cast<uint16_t*>(out);
   a.part_ml = reinterpret_cast<float*>(ws);
@@ -288,6 +291,89 @@ hipError_t launch_attn(const AttnPlan& p, const void* q, const void* k, const vo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(p.Hq), unsigned(B)), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ cache writers
+// Element offsets (bf16 units) of position t, dimension d inside one (b, g)
+// region of the K and V tiles (layout above).
+__device__ __forceinline__ int64_t kv_k_index(int64_t t, int d) {
+  return ((t / 16) * 4 + d / 32) * 512 + (((d % 32) / 8) * 16 + (t % 16)) * 8 + (d % 8);
+}
+
+__device__ __forceinline__ int64_t kv_v_index(int64_t t, int d) {
+  const int u = int(t % 32), kb = (u % 16) / 4, e = 4 * (u / 16) + (u % 4);
+  return ((t / 32) * 8 + d / 16) * 512 + (kb * 16 + (d % 16)) * 8 + e;
+}
+
+// One thread per (b, g, t, dimension pair): logical [B][Hkv][L][128] <-> tiles.
+// DIR 0: pack (logical -> tiles), 1: unpack (tiles -> logical).
+template <int DIR>
+__global__ __launch_bounds__(256) void kv_copy_kernel(const uint16_t* __restrict__ src_k,
+                                                      const uint16_t* __restrict__ src_v, uint16_t* __restrict__ dst_k,
+                                                      uint16_t* __restrict__ dst_v, int64_t BH, int64_t L,
+                                                      int64_t Lmax) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= BH * L * (kHeadDim / 2)) return;
+  const int d = int(i % (kHeadDim / 2)) * 2;
+  const int64_t t = (i / (kHeadDim / 2)) % L, bh = i / (kHeadDim / 2) / L;
+  const int64_t lin = (bh * L + t) * kHeadDim + d;  // logical [bh][t][d] with row stride L
+  const int64_t tile = bh * Lmax * kHeadDim;
+  if (DIR == 0) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      dst_k[tile + kv_k_index(t, d + e)] = src_k[lin + e];
+      dst_v[tile + kv_v_index(t, d + e)] = src_v[lin + e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      dst_k[lin + e] = src_k[tile + kv_k_index(t, d + e)];
+      dst_v[lin + e] = src_v[tile + kv_v_index(t, d + e)];
+    }
+  }
+}
+
+// One position per sequence: k_new / v_new [B][Hkv][128] at positions[b]
+// (a position outside [0, Lmax) writes nothing).
+__global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restrict__ k_new,
+                                                        const uint16_t* __restrict__ v_new,
+                                                        const int32_t* __restrict__ positions, uint16_t* __restrict__ k,
+                                                        uint16_t* __restrict__ v, int64_t B, int64_t Hkv,
+                                                        int64_t Lmax) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= B * Hkv * kHeadDim) return;
+  const int d = int(i % kHeadDim);
+  const int64_t bh = i / kHeadDim, b = bh / Hkv;
+  const int64_t t = positions[b];
+  if (t < 0 || t >= Lmax) return;
+  const int64_t tile = bh * Lmax * kHeadDim;
+  k[tile + kv_k_index(t, d)] = k_new[i];
+  v[tile + kv_v_index(t, d)] = v_new[i];
+}
+
+hipError_t launch_kv_copy(bool pack, const void* src_k, const void* src_v, void* dst_k, void* dst_v, int64_t BH,
+                          int64_t L, int64_t Lmax, hipStream_t st) {
+  const int64_t n = BH * L * (kHeadDim / 2);
+  if (n == 0) return hipSuccess;
+  const dim3 grid(unsigned(ceil_div(n, int64_t(256))));
+  const auto* sk = reinterpret_cast<const uint16_t*>(src_k);
+  const auto* sv = reinterpret_cast<const uint16_t*>(src_v);
+  auto* dk = reinterpret_cast<uint16_t*>(dst_k);
+  auto* dv = reinterpret_cast<uint16_t*>(dst_v);
+  if (pack)
+    hipLaunchKernelGGL(kv_copy_kernel<0>, grid, dim3(256), 0, st, sk, sv, dk, dv, BH, L, Lmax);
+  else
+    hipLaunchKernelGGL(kv_copy_kernel<1>, grid, dim3(256), 0, st, sk, sv, dk, dv, BH, L, Lmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* positions, int64_t B, int64_t Hkv,
+                            int64_t Lmax, void* k, void* v, hipStream_t st) {
+  const int64_t n = B * Hkv * kHeadDim;
+  hipLaunchKernelGGL(kv_append_kernel, dim3(unsigned(ceil_div(n, int64_t(256)))), dim3(256), 0, st,
+                     reinterpret_cast<const uint16_t*>(k_new), reinterpret_cast<const uint16_t*>(v_new), positions,
+                     reinterpret_cast<uint16_t*>(k), reinterpret_cast<uint16_t*>(v), B, Hkv, Lmax);
   return hipGetLastError();
 }
 

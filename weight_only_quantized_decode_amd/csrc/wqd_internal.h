@@ -38,8 +38,13 @@ hipError_t launch_act_quant(const void* x, int64_t M, int64_t K, int parts, void
 hipError_t launch_w8a8(const W8Plan& p, const void* xc, const float* xscale, int64_t M, int64_t N, int64_t K,
                        const void* wp, const void* scales, void* y, void* ws, hipStream_t st);
 // Decode attention (split along the context, then the fixed-order merge).
-hipError_t launch_attn(const AttnPlan& p, const void* q, const void* k, const void* vt, const int32_t* lens,
+hipError_t launch_attn(const AttnPlan& p, const void* q, const void* k, const void* v, const int32_t* lens,
                        int64_t B, float scale, void* out, void* ws, hipStream_t st);
+// KV cache tiles: pack / unpack [BH][L][128] logical rows, append one position per sequence.
+hipError_t launch_kv_copy(bool pack, const void* src_k, const void* src_v, void* dst_k, void* dst_v, int64_t BH,
+                          int64_t L, int64_t Lmax, hipStream_t st);
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* positions, int64_t B, int64_t Hkv,
+                            int64_t Lmax, void* k, void* v, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 size_t stream_sink_words(size_t bytes);

@@ -437,7 +437,7 @@ int plan_act_quant(int64_t M, int64_t K, int* parts) {
 
 int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnPlan* out) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Lmax < 1) return kEArg;
-  if (D != 128 || Hq % Hkv != 0 || Hq / Hkv > 16 || Lmax % 8 != 0) return kEShape;
+  if (D != 128 || Hq % Hkv != 0 || Hq / Hkv > 16 || Lmax % 32 != 0) return kEShape;
   if (Lmax * 128 * 2 >= (int64_t(1) << 31) || B > 65535 || Hkv > 65535 || Hq > 65535) return kEUnsupported;
   AttnPlan p{};
   p.Lmax = Lmax;
