@@ -526,7 +526,7 @@ def attn_stack_timing(args, stream, B=32, ctx=2048, layers=80):
     q = torch.randn((B, ATTN_HQ, ATTN_D), generator=g, device=dev, dtype=torch.bfloat16)
     out = torch.empty_like(q)
     lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
-    ws = wqd.get_workspace(wqd.attn_workspace_bytes(B, ATTN_HQ, ATTN_HKV, ctx), dev)
+    ws = wqd.get_workspace(wqd.attn_workspace_bytes(B, ATTN_HQ, ATTN_HKV, ctx), dev)  # None when 0 bytes
     scale = 1.0 / math.sqrt(ATTN_D)
 
     def go():
@@ -543,7 +543,8 @@ def attn_stack_timing(args, stream, B=32, ctx=2048, layers=80):
            "algorithmic_bytes_per_step": layers * per_layer, "GBps": round(gbps, 2),
            "step_samples_ms": {"n": len(samples), "median": round(statistics.median(samples), 4),
                                "min": round(min(samples), 4), "max": round(max(samples), 4)},
-           "kernel": "attn_split_kernel + attn_combine_kernel per layer (both timed)"}
+           "splits": wqd.attn_workspace_bytes(B, ATTN_HQ, ATTN_HKV, ctx) // (B * ATTN_HQ * 130 * 4),
+           "kernel": "attn_split_kernel (+ attn_combine_kernel when the context is split) per layer"}
     del caches
     free_cache()
     return res

@@ -237,7 +237,9 @@ int wqd_qgemm_w8a8(const void* x_codes, const float* x_scale, int64_t M, int64_t
  *              whatever they hold
  *   out        device bf16 [B][Hq][D]
  *   workspace  device, >= wqd_attn_workspace_bytes (partial maxima, sums and
- *              outputs of the splits), contents on entry do not matter.
+ *              outputs when the context is split over several workgroups;
+ *              0 bytes, and NULL allowed, when it is not), contents on entry
+ *              do not matter.
  * D = 128, Hq a multiple of Hkv with Hq / Hkv <= 16, Lmax a multiple of 32
  * and Lmax * D * 2 < 2^31 (else WQD_E_SHAPE / WQD_E_UNSUPPORTED).
  * Deterministic.

@@ -369,10 +369,10 @@ def decode_attention(q, cache: KVCache, lengths, scale: float, out=None, workspa
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
     if workspace is None:
         workspace = get_workspace(attn_workspace_bytes(B, Hq, cache.Hkv, cache.Lmax, D), q.device)
-    wsb = workspace.numel() * workspace.element_size()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().wqd_decode_attention(q.data_ptr(), cache.k.data_ptr(), cache.v.data_ptr(), lengths.data_ptr(), B,
                                       Hq, cache.Hkv, cache.Lmax, D, float(scale), out.data_ptr(),
-                                      workspace.data_ptr(), wsb, _stream(stream)), "wqd_decode_attention")
+                                      _ptr(workspace), wsb, _stream(stream)), "wqd_decode_attention")
     return out
 
 

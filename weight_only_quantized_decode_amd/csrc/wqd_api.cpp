@@ -199,10 +199,10 @@ int wqd_decode_attention(const void* q, const void* k_cache, const void* v_cache
   wqd::AttnPlan p;
   const int st = wqd::plan_attn(B, Hq, Hkv, Lmax, D, &p);
   if (st != wqd::kOK) return st;
-  if (!q || !k_cache || !v_cache || !lengths || !out || !workspace) return WQD_E_ARG;
-  if (workspace_bytes < p.ws_bytes) return WQD_E_WORKSPACE;
+  if (!q || !k_cache || !v_cache || !lengths || !out) return WQD_E_ARG;
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return WQD_E_WORKSPACE;
   if (!wqd::aligned16(q) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache) || !wqd::aligned16(out) ||
-      !wqd::aligned16(workspace) || reinterpret_cast<uintptr_t>(lengths) % 4)
+      (p.ws_bytes > 0 && !wqd::aligned16(workspace)) || reinterpret_cast<uintptr_t>(lengths) % 4)
     return WQD_E_ALIGN;
   return hip_status(wqd::launch_attn(p, q, k_cache, v_cache, lengths, B, scale, out, workspace, as_stream(stream)));
 }

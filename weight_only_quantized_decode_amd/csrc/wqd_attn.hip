@@ -24,8 +24,9 @@
 //      the softmax weights, below).
 // Both take Lmax * 128 * 2 bytes per (b, g); Lmax is a multiple of 32.
 //
-// attn_split_kernel: one wavefront per (sequence b, KV head g, split s); the
-// split's positions in steps of 32.  Per step, on bf16 matrix cores
+// attn_split_kernel: one workgroup of 4 wavefronts per (sequence b, KV head
+// g, split s); the split's positions in steps of 32, wavefront w taking steps
+// w, w + 4, ...  Per step, on bf16 matrix cores
 // (v_mfma_f32_16x16x32_bf16):
 //   * S^T = K Q^T as two 16-position tiles x 4 head-dimension steps: A = one
 //     K tile (one 1 KiB load), B = Q^T, lane (kb, n) holding 8 head
@@ -43,10 +44,12 @@
 //     each weight) so P is not rounded to 8 bits; B = one V tile, whose lane
 //     (kb, n) holds dimension n at the same 8 positions;
 //   * the next step's tiles are loaded before this step's arithmetic.
-// Each wavefront writes its running maximum, sum and unnormalised output per
-// head to the workspace.  attn_combine_kernel then merges the splits of each
-// (b, head) in split order: o = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s,
-// rounded to bf16 (a sequence of length 0 gives zeros).
+// The 4 wavefronts merge their running maxima, sums and unnormalised outputs
+// through LDS, in wavefront order; with one split the workgroup normalises
+// and stores the output, otherwise it writes its split's partials to the
+// workspace and attn_combine_kernel merges the splits of each (b, head) in
+// split order: o = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s, rounded to
+// bf16 (a sequence of length 0 gives zeros).
 #include "wqd_device.h"
 #include "wqd_internal.h"
 #include "wqd_plan.h"
@@ -57,6 +60,7 @@ typedef __bf16 at_bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float at_f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kHeadDim = 128;
+constexpr int kAttnWaves = 4;  // wavefronts per split, interleaving its 32-position steps
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ at_f32x4_t at_mfma(uint4 a, uint4 b, at_f32x4_t c) {
@@ -185,8 +189,12 @@ __device__ __forceinline__ void attn_step(AttnState& st, AttnStepLoads& ld, cons
   }
 }
 
-__global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a) {
-  const int lane = threadIdx.x, kb = lane >> 4, n = lane & 15;
+__global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(AttnArgs a) {
+  constexpr int W = kAttnWaves;
+  __shared__ float s_ml[W][2][16];
+  __shared__ float s_o[W][16][kHeadDim];
+  const int lane = threadIdx.x & 63, kb = lane >> 4, n = lane & 15;
+  const int wave = threadIdx.x >> 6;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int64_t Lmax = a.Lmax;
   int64_t len = a.lens[b];
@@ -213,38 +221,66 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a) {
   for (int c = 0; c < 8; ++c) st.o[c] = at_f32x4_t{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
-  if (t_begin < t_end) {
-    // two register sets: each step loads the next step's pieces before its
-    // own arithmetic (a step past the split reads in-bounds or zero pieces
-    // that are never used)
+  // wavefront w takes the split's steps w, w + W, w + 2 W, ...
+  constexpr int64_t STRIDE = 32 * W;
+  const int64_t t0 = t_begin + 32 * wave;
+  if (t0 < t_end) {
+    // two register sets: each step loads the wavefront's next step before its
+    // own arithmetic (a step past the split reads in-bounds or zero tiles that
+    // are never used)
     AttnStepLoads l0, l1;
-    attn_load(l0, kres, vres, t_begin, lane);
-    int64_t t = t_begin;
-    for (; t + 32 < t_end; t += 64) {
-      attn_load(l1, kres, vres, t + 32, lane);
+    attn_load(l0, kres, vres, t0, lane);
+    int64_t t = t0;
+    for (; t + STRIDE < t_end; t += 2 * STRIDE) {
+      attn_load(l1, kres, vres, t + STRIDE, lane);
       attn_step(st, l0, qf, a.scale_log2, t, len, kb, n);
       // unconditional: a conditional load would make the compiler wait for
       // every load at the join, this one included
-      attn_load(l0, kres, vres, t + 64, lane);
-      attn_step(st, l1, qf, a.scale_log2, t + 32, len, kb, n);
+      attn_load(l0, kres, vres, t + 2 * STRIDE, lane);
+      attn_step(st, l1, qf, a.scale_log2, t + STRIDE, len, kb, n);
     }
     if (t < t_end) attn_step(st, l0, qf, a.scale_log2, t, len, kb, n);
   }
-  if (n < a.G) {
-    const int64_t row = (int64_t(b) * a.Hq + hq) * a.S + s;
-    if (kb == 0) {
-      a.part_ml[2 * row] = st.m;
-      a.part_ml[2 * row + 1] = st.l;
-    }
+
+  // merge the W wavefronts through LDS: lane (kb, n) holds head n's maximum
+  // and sum, and rows 4 kb + r (heads) of column n of each 16-dimension block
+  if (kb == 0) {
+    s_ml[wave][0][n] = st.m;
+    s_ml[wave][1][n] = st.l;
   }
-  // lane (kb, n): rows 4 kb + r (heads), column n of block c (dimension 16 c + n)
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int hr = 4 * kb + r;
-    if (hr >= a.G) continue;
-    const int64_t row = (int64_t(b) * a.Hq + int64_t(g) * a.G + hr) * a.S + s;
+  for (int c = 0; c < 8; ++c)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) a.part_o[row * kHeadDim + 16 * c + n] = st.o[c][r];
+    for (int r = 0; r < 4; ++r) s_o[wave][4 * kb + r][16 * c + n] = st.o[c][r];
+  __syncthreads();
+  // thread i: head h = i / 64 (and h + 4, + 8, + 12), dimensions 2 (i % 64), + 1
+  const int dp = threadIdx.x % 64;
+  for (int h = threadIdx.x / 64; h < a.G; h += W) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_ml[w][0][h]);
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float f = exp2f(s_ml[w][0][h] - M);  // 0 for a wavefront without positions
+        L += f * s_ml[w][1][h];
+        o0 += f * s_o[w][h][2 * dp];
+        o1 += f * s_o[w][h][2 * dp + 1];
+      }
+    }
+    const int64_t bh = int64_t(b) * a.Hq + int64_t(g) * a.G + h;
+    if (a.S == 1) {  // the whole context: normalise and store (no merge launch)
+      const float inv = M != -INFINITY ? 1.0f / L : 0.f;
+      reinterpret_cast<uint32_t*>(a.out + bh * kHeadDim)[dp] = bf16_pair(o0 * inv, o1 * inv);
+    } else {
+      const int64_t row = bh * a.S + s;
+      if (dp == 0) {
+        a.part_ml[2 * row] = M;
+        a.part_ml[2 * row + 1] = L;
+      }
+      reinterpret_cast<float2*>(a.part_o + row * kHeadDim)[dp] = make_float2(o0, o1);
+    }
   }
 }
 
@@ -287,9 +323,10 @@ hipError_t launch_attn(const AttnPlan& p, const void* q, const void* k, const vo
   a.G = p.Hq / p.Hkv;
   a.S = p.S;
   a.chunk = p.chunk;
-  hipLaunchKernelGGL(attn_split_kernel, dim3(unsigned(p.S), unsigned(p.Hkv), unsigned(B)), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(attn_split_kernel, dim3(unsigned(p.S), unsigned(p.Hkv), unsigned(B)), dim3(64 * kAttnWaves), 0,
+                     st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.S == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(p.Hq), unsigned(B)), dim3(64), 0, st, a);
   return hipGetLastError();
 }

@@ -435,6 +435,12 @@ int plan_act_quant(int64_t M, int64_t K, int* parts) {
   return kOK;
 }
 
+#ifndef WQD_ATTN_TARGET_GROUPS
+#define WQD_ATTN_TARGET_GROUPS 256
+#endif
+constexpr int64_t kAttnTargetGroups = WQD_ATTN_TARGET_GROUPS;  // workgroups of 4 wavefronts per launch
+constexpr int64_t kAttnWavesPerSplit = 4;
+
 int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnPlan* out) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Lmax < 1) return kEArg;
   if (D != 128 || Hq % Hkv != 0 || Hq / Hkv > 16 || Lmax % 32 != 0) return kEShape;
@@ -443,15 +449,17 @@ int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnP
   p.Lmax = Lmax;
   p.Hq = int(Hq);
   p.Hkv = int(Hkv);
-  // about 8 wavefronts per compute unit, each split at least 64 positions
+  // about one workgroup of 4 wavefronts per compute unit (long streams per
+  // wavefront measured faster than more, shorter splits), each wavefront at
+  // least 2 steps of 32 positions
   const int64_t pairs = B * Hkv;
   const int64_t steps = ceil_div(Lmax, 32);
-  int64_t S = ceil_div(2048, pairs);
-  const int64_t max_s = steps / 2 > 1 ? steps / 2 : 1;
+  int64_t S = ceil_div(kAttnTargetGroups, pairs);
+  const int64_t max_s = steps / (2 * kAttnWavesPerSplit) > 1 ? steps / (2 * kAttnWavesPerSplit) : 1;
   if (S > max_s) S = max_s;
   p.chunk = int(32 * ceil_div(steps, S));
   p.S = int(ceil_div(Lmax, p.chunk));
-  p.ws_bytes = size_t(B) * size_t(Hq) * size_t(p.S) * (2 + 128) * sizeof(float);
+  p.ws_bytes = p.S > 1 ? size_t(B) * size_t(Hq) * size_t(p.S) * (2 + 128) * sizeof(float) : 0;
   *out = p;
   return kOK;
 }
