@@ -12,7 +12,8 @@ It computes, plainly and slowly, what the decode linear layer computes:
 * ``quant``:   the three weight formats (bf16, FP8-E4M3 + per-row fp32 scale,
   W4A16 = uint4 codes in groups of 128 with an fp16 scale and a uint4 zero
   point) and their exact dequantisation;
-* ``gemm``:    y = x . dequant(W)^T in float64, rounded once to bf16;
+* ``gemm``:    y = x . dequant(W)^T in float64, rounded once to bf16; the
+  SwiGLU of a gate/up pair, silu(x . gate^T) * (x . up^T);
 * ``spec``:    the speculative-sampling accept / reject step over the verify
   pass's target and draft distributions;
 * ``w8a8``:    the W8A8-FP8 variant: one dynamic E4M3 scale for the whole
@@ -55,7 +56,7 @@ from .formats import (  # noqa: F401
     e4m3_encode,
     fp16_round_f32,
 )
-from .gemm import qgemm_exact, qgemm_ref  # noqa: F401
+from .gemm import qgemm_exact, qgemm_ref, silu, swiglu_exact  # noqa: F401
 from .quant import (  # noqa: F401
     FMTS,
     GROUP,

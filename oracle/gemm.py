@@ -33,3 +33,18 @@ def qgemm_ref(x_bits, qw: dict) -> dict:
     y64 = qgemm_exact(x_bits, qw)
     return {"y64": y64, "y_bits": bf16_to_bits(y64)}
 
+
+
+def silu(g) -> np.ndarray:
+    """silu(g) = g * sigmoid(g) = g / (1 + exp(-g)), float64 (an overflowing
+    exp(-g) gives -0: the limit)."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_exact(x_bits, qw_gate: dict, qw_up: dict) -> np.ndarray:
+    """h64[M, F] = silu(x . gate^T) * (x . up^T), in float64 from the exact
+    products (CS336 lecture 10 notes, section 3.2: the MLP's gate and up
+    projections of the same input, multiplied after the gate's activation)."""
+    return silu(qgemm_exact(x_bits, qw_gate)) * qgemm_exact(x_bits, qw_up)
