@@ -88,6 +88,13 @@ def make_workload(name, fmt_m, layers, fused):
     raise SystemExit(f"unknown workload {name!r}")
 
 
+def WL_stack(name, M, layers):
+    """The fused stack with gate/up packed for the SwiGLU epilogue."""
+    from weight_only_quantized_decode_amd import workloads as WL
+
+    return WL.stack_70b("w4a16" if name == "w4a16_70b" else "fp8", M, layers or 80, fused=True, swiglu=True)
+
+
 def with_m(wl, M):
     """The same stack (same weights) driven by M activation rows."""
     import dataclasses
@@ -146,7 +153,8 @@ def pack_stack(wl):
         row = []
         for name, N, K in wl.mats:
             W = weight_for(wl, layer, name, N, K, dev)
-            row.append(wqd.pack_weights(wl.fmt, W))
+            swi = wl.swiglu and name == "gate_up"  # gate rows then up rows, packed interleaved
+            row.append(wqd.pack_gate_up(wl.fmt, W) if swi else wqd.pack_weights(wl.fmt, W))
             del W
         packed.append(row)
         if layer % 20 == 19:
@@ -231,12 +239,22 @@ def time_step(wl, packed, args, stream, dominant=False, shapes=False):
     # W8A8: a call is the activation quantisation, then the product (the
     # kernel-family replays time the product alone, on codes made once)
     codes = {K: wqd.act_quant_fp8(x, workspace=ws) for K, x in xs.items()} if wl.act == "fp8" else None
+    hbuf = None
+    if wl.swiglu:
+        F = dict((name, N) for name, N, _ in wl.mats)["gate_up"] // 2
+        hbuf = torch.empty((wl.M, F), dtype=torch.bfloat16, device=ys[next(iter(ys))].device)
 
     def launches(only=None):
         def go():
             for row in packed:
                 for j, ((name, N, K), pw) in enumerate(zip(wl.mats, row)):
                     if only is not None and j not in only:
+                        continue
+                    if wl.swiglu and name == "gate_up":  # h = silu(gate) * up, read by down
+                        wqd.qgemm_swiglu(xs[K], pw, h=hbuf, workspace=ws)
+                        continue
+                    if wl.swiglu and name == "down":
+                        wqd.qgemm(hbuf, pw, y=ys[N], workspace=ws)
                         continue
                     if codes is None:
                         wqd.qgemm(xs[K], pw, y=ys[N], workspace=ws)
@@ -264,7 +282,7 @@ def time_step(wl, packed, args, stream, dominant=False, shapes=False):
         for label, js in groups.items():
             g_ms, _ = replay_timing(launches(set(js)), stream, args.steps, args.warmup, not args.no_graph)
             n_launch = len(js) * len(packed)
-            g_bytes = len(packed) * sum(wl.call_bytes(wl.mats[j][1], wl.mats[j][2]) for j in js)
+            g_bytes = len(packed) * sum(wl.call_bytes(wl.mats[j][1], wl.mats[j][2], wl.mats[j][0]) for j in js)
             g_flops = len(packed) * sum(WL.call_flops(wl.M, wl.mats[j][1], wl.mats[j][2]) for j in js)
             per[label] = {"matrices": [wl.mats[j][0] for j in js], "launches": n_launch, "ms": g_ms,
                           "avg_launch_us": g_ms * 1e3 / n_launch, "bytes": g_bytes, "flops": g_flops}
@@ -274,7 +292,7 @@ def time_step(wl, packed, args, stream, dominant=False, shapes=False):
         for j, (name, N, K) in enumerate(wl.mats):
             s_ms, _ = replay_timing(launches({j}), stream, max(3, args.steps // 4), 1, not args.no_graph)
             us = s_ms * 1e3 / wl.layers
-            b = wl.call_bytes(N, K)
+            b = wl.call_bytes(N, K, name)
             out[name] = {"N": N, "K": K, "us": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1),
                          "kernel": kernel_group(wl, N, K)}
         res["shapes"] = out
@@ -643,6 +661,13 @@ def main():
     del packed
     free_cache()
 
+    swiglu_rec = None
+    if is_stack and not args.no_alt and args.workload in ("w4a16_70b", "fp8_70b") and fused:
+        sw_wl = WL_stack(args.workload, args.m, args.layers)
+        sw_packed = pack_stack(sw_wl)
+        swiglu_rec = time_step(sw_wl, sw_packed, args, stream)
+        del sw_packed
+        free_cache()
     alt = None
     if is_stack and not args.no_alt:
         alt_wl = make_workload(args.workload, args.m, args.layers, not fused)
@@ -711,6 +736,9 @@ def main():
     if alt is not None:
         alt["pct_measured_read_ceiling"] = pct(alt["GBps"], ceiling[0])
         out["separate_layout" if fused else "fused_layout"] = alt
+    if swiglu_rec is not None:
+        swiglu_rec["pct_measured_read_ceiling"] = pct(swiglu_rec["GBps"], ceiling[0])
+        out["swiglu_layout"] = swiglu_rec
     if targets:
         for t in targets:
             t["pct_measured_read_ceiling"] = pct(t["GBps"], ceiling[0])

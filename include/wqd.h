@@ -173,6 +173,32 @@ int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K,
               void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The fused MLP input projections with a SwiGLU epilogue: the MLP's gate and
+ * up projections read the same activations and its next input is
+ * silu(gate) * up (CS336 lecture 10 notes, section 3.2: the MLP's three
+ * matrices; "Making each token cheaper", "Why decode is usually bandwidth
+ * bound": each launch and each activation byte written and read again costs
+ * time in a memory-bound step).  One launch streams both matrices and writes
+ * h = silu(g) * up once, instead of g and up.
+ *
+ * wqd_pack_gate_up: W device float32 [2F][K] row-major, gate rows 0 .. F-1
+ *   then up rows F .. 2F-1 (finite), packed in `fmt` as a 2F x K matrix whose
+ *   rows are interleaved for the epilogue (16-row block b: gate rows
+ *   8b .. 8b+7, then up rows 8b .. 8b+7); buffers of wqd_packed_sizes(fmt,
+ *   2F, K).  Each row is quantised exactly as wqd_pack_weights quantises it.
+ *   F % 8 == 0 (else WQD_E_SHAPE).
+ * wqd_qgemm_swiglu: h[M][F] bfloat16 = bf16(silu(g) * u), g = x . gate^T and
+ *   u = x . up^T formed exactly as wqd_qgemm forms y (float32 sums of exact
+ *   products), silu(g) = g / (1 + exp(-g)) in float32.  workspace >=
+ *   wqd_workspace_bytes(fmt, M, 2F, K).  Errors as wqd_qgemm.
+ */
+int wqd_pack_gate_up(int fmt, const float* W, int64_t F, int64_t K,
+                     void* w_packed, void* scales, void* zeros, void* stream);
+int wqd_qgemm_swiglu(int fmt, const void* x, int64_t M, int64_t F, int64_t K,
+                     const void* w_packed, const void* scales, const void* zeros,
+                     void* h, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * W8A8-FP8: activations quantised to FP8-E4M3 too, and the product on the
  * FP8 matrix cores, for the shapes where the matrix product, not the weight
  * bytes, sets the time (wide verify passes, large batches, prefill).  Sources:

@@ -65,3 +65,81 @@ def test_graph_replay_matches_eager(fmt, M, N, K, family):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y_buf.view(torch.int16), eager[i].view(torch.int16)), (fmt, family, M, i)
+
+
+def replay_check(run_eager, set_input, out_buf, capture, n_inputs=3):
+    """Eager results for each input, then one captured graph replayed over the
+    inputs in the order 0, 1, 2, 1, 0 with the output poisoned between
+    replays; every replay must match its eager result bit for bit."""
+    eager = []
+    for i in range(n_inputs):
+        set_input(i)
+        run_eager()
+        torch.cuda.synchronize()
+        eager.append(out_buf.clone())
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        capture()  # workspaces are allocated here, outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        capture()
+    for i in (0, 1, 2, 1, 0):
+        set_input(i)
+        out_buf.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_buf.view(torch.int16), eager[i].view(torch.int16)), i
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 8192, 4096), (48, 4096, 8192)])
+def test_graph_w8a8(M, N, K):
+    """Activation quantisation (absmax partials, codes) and the FP8 product,
+    with a K split at 48 rows."""
+    pw = wqd.pack_weights("fp8", I.w_device(41, N, K))
+    xs = [x_dev(I.x_bf16_bits(60 + i, M, K)) for i in range(3)]
+    x_buf = torch.empty_like(xs[0])
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    print(f"graph w8a8 M={M} N={N} K={K} ws={wqd.w8a8_workspace_bytes(M, N, K)}", flush=True)
+
+    def run():
+        wqd.w8a8(x_buf, pw, y=y)
+
+    replay_check(run, lambda i: x_buf.copy_(xs[i]), y, run)
+
+
+@pytest.mark.parametrize("B", [2, 32])
+def test_graph_decode_attention(B):
+    """B = 2 splits the context (partials and the merge launch); B = 32 does not."""
+    Hq, Hkv, L = 64, 8, 2048
+    cache = wqd.alloc_kv_cache(B, Hkv, L)
+    g0 = torch.Generator(device="cuda").manual_seed(3)
+    cache.k.normal_(generator=g0)
+    cache.v.normal_(generator=g0)
+    qs = [torch.randn((B, Hq, 128), generator=g0, device="cuda").to(torch.bfloat16) for _ in range(3)]
+    q_buf = torch.empty_like(qs[0])
+    lens = torch.tensor([(L * (b + 1)) // B for b in range(B)], dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q_buf)
+    print(f"graph attention B={B} ws={wqd.attn_workspace_bytes(B, Hq, Hkv, L)}", flush=True)
+
+    def run():
+        wqd.decode_attention(q_buf, cache, lens, 0.088, out=out)
+
+    replay_check(run, lambda i: q_buf.copy_(qs[i]), out, run)
+
+
+@pytest.mark.parametrize("fmt,M,F,K", [("w4a16", 1, 28672, 8192), ("fp8", 24, 200, 8192), ("w4a16", 65, 2048, 512)])
+def test_graph_swiglu(fmt, M, F, K):
+    """SwiGLU epilogue on the broadcast kernel, on the skinny kernel's split-K
+    sum, and on the tiled kernel's."""
+    pw = wqd.pack_gate_up(fmt, I.w_device(43, 2 * F, K))
+    xs = [x_dev(I.x_bf16_bits(70 + i, M, K)) for i in range(3)]
+    x_buf = torch.empty_like(xs[0])
+    h = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    print(f"graph swiglu {fmt} M={M} F={F} K={K} path={wqd.kernel_path(fmt, M, 2 * F, K)}", flush=True)
+
+    def run():
+        wqd.qgemm_swiglu(x_buf, pw, h=h)
+
+    replay_check(run, lambda i: x_buf.copy_(xs[i]), h, run)

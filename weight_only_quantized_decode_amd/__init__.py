@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
             "wqd_pack_weights": (i32, [i32, vp, i64, i64, vp, vp, vp, vp]),
             "wqd_qgemm": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
             "wqd_qgemm_noalloc": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]),
+            "wqd_pack_gate_up": (i32, [i32, vp, i64, i64, vp, vp, vp, vp]),
+            "wqd_qgemm_swiglu": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
             "wqd_act_quant_fp8": (i32, [vp, i64, i64, vp, vp, vp, sz, vp]),
             "wqd_attn_workspace_bytes": (i32, [i64, i64, i64, i64, i64, psz]),
             "wqd_decode_attention": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, vp, sz,
@@ -182,6 +184,43 @@ def pack_weights(fmt, W, out: Optional[PackedWeight] = None, stream=None) -> Pac
     _check(lib().wqd_pack_weights(_fmt(fmt), W.data_ptr(), N, K, _ptr(pw.w), _ptr(pw.scales), _ptr(pw.zeros),
                                   _stream(stream)), "wqd_pack_weights")
     return pw
+
+
+def pack_gate_up(fmt, W, out: Optional[PackedWeight] = None, stream=None) -> PackedWeight:
+    """wqd_pack_gate_up: W float32 [2F, K] (cuda; gate rows, then up rows),
+    packed for the SwiGLU epilogue.  The PackedWeight has N = 2F rows."""
+    import torch
+
+    if W.dtype != torch.float32 or not W.is_cuda or W.dim() != 2 or W.shape[0] % 2:
+        raise ValueError("W must be a cuda float32 [2F, K] tensor (gate rows, then up rows)")
+    W = W.contiguous()
+    N, K = W.shape
+    pw = out if out is not None else alloc_packed(fmt, N, K, W.device)
+    _check(lib().wqd_pack_gate_up(_fmt(fmt), W.data_ptr(), N // 2, K, _ptr(pw.w), _ptr(pw.scales), _ptr(pw.zeros),
+                                  _stream(stream)), "wqd_pack_gate_up")
+    return pw
+
+
+def qgemm_swiglu(x, pw: PackedWeight, h=None, workspace=None, stream=None):
+    """wqd_qgemm_swiglu: h[M, F] (bfloat16) = silu(x . gate^T) * (x . up^T),
+    pw packed by pack_gate_up (N = 2F)."""
+    import torch
+
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 [M, K] tensor")
+    M, K = x.shape
+    F = pw.N // 2
+    if K != pw.K:
+        raise ValueError(f"K mismatch: x has {K}, weights have {pw.K}")
+    if h is None:
+        h = torch.empty((M, F), dtype=torch.bfloat16, device=x.device)
+    need = workspace_bytes(pw.fmt, M, pw.N, K)
+    if workspace is None:
+        workspace = get_workspace(need, x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().wqd_qgemm_swiglu(_fmt(pw.fmt), x.data_ptr(), M, F, K, _ptr(pw.w), _ptr(pw.scales), _ptr(pw.zeros),
+                                  h.data_ptr(), _ptr(workspace), wsb, _stream(stream)), "wqd_qgemm_swiglu")
+    return h
 
 
 # ----------------------------------------------------------------------------- workspace

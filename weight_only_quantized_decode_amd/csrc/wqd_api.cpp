@@ -36,7 +36,7 @@ int check_packed_ptrs(int fmt, const void* wp, const void* scales, const void* z
 namespace wqd {
 
 int qgemm_checked(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const void* w_packed, const void* scales,
-                  const void* zeros, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+                  const void* zeros, void* y, void* workspace, size_t workspace_bytes, void* stream, bool swiglu) {
   if (M < 1) return WQD_E_ARG;
   Choice c;
   int st = choose_path(fmt, M, N, K, &c);
@@ -52,20 +52,21 @@ int qgemm_checked(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const
     if (!workspace || workspace_bytes < need) return WQD_E_WORKSPACE;
     if (!aligned16(workspace)) return WQD_E_ALIGN;
   }
+  if (swiglu && N % 16 != 0) return WQD_E_SHAPE;
   hipStream_t s = as_stream(stream);
   switch (c.path) {
     case kPathBcast:
-      return hip_status(launch_gemv_bcast(fmt, c.bcast, x, M, N, K, w_packed, scales, zeros, y, s));
+      return hip_status(launch_gemv_bcast(fmt, c.bcast, x, M, N, K, w_packed, scales, zeros, y, swiglu, s));
     case kPathMc:
-      return hip_status(launch_gemv_mc(fmt, c.mc, x, M, N, K, w_packed, scales, zeros, y, s));
+      return hip_status(launch_gemv_mc(fmt, c.mc, x, M, N, K, w_packed, scales, zeros, y, swiglu, s));
     case kPathStaged:
-      return hip_status(launch_gemv(fmt, c.gemv, x, M, N, K, w_packed, scales, zeros, y, s));
+      return hip_status(launch_gemv(fmt, c.gemv, x, M, N, K, w_packed, scales, zeros, y, swiglu, s));
     case kPathGemm:
-      return hip_status(launch_gemm(fmt, c.gm, x, M, N, K, w_packed, scales, zeros, y, workspace, s));
+      return hip_status(launch_gemm(fmt, c.gm, x, M, N, K, w_packed, scales, zeros, y, workspace, swiglu, s));
     case kPathSkinny:
-      return hip_status(launch_gemv_sk(fmt, c.sk, x, M, N, K, w_packed, scales, zeros, y, workspace, s));
+      return hip_status(launch_gemv_sk(fmt, c.sk, x, M, N, K, w_packed, scales, zeros, y, workspace, swiglu, s));
     default:
-      return hip_status(launch_mfma(fmt, c.mfma, M, N, K, x, w_packed, scales, zeros, y, workspace, s));
+      return hip_status(launch_mfma(fmt, c.mfma, M, N, K, x, w_packed, scales, zeros, y, workspace, swiglu, s));
   }
 }
 
@@ -133,7 +134,30 @@ int wqd_pack_weights(int fmt, const float* W, int64_t N, int64_t K, void* w_pack
   if (!wqd::aligned16(W)) return WQD_E_ALIGN;
   st = check_packed_ptrs(fmt, w_packed, scales, zeros);
   if (st != WQD_OK) return st;
-  return hip_status(wqd::launch_pack(fmt, W, N, K, ps, w_packed, scales, zeros, as_stream(stream)));
+  return hip_status(wqd::launch_pack(fmt, W, N, K, ps, w_packed, scales, zeros, 0, as_stream(stream)));
+}
+
+int wqd_pack_gate_up(int fmt, const float* W, int64_t F, int64_t K, void* w_packed, void* scales, void* zeros,
+                     void* stream) {
+  if (F < 1) return WQD_E_ARG;
+  if (F % 8 != 0) return WQD_E_SHAPE;
+  wqd::PackedSizes ps;
+  int st = wqd::packed_sizes(fmt, 2 * F, K, &ps);
+  if (st != wqd::kOK) return st;
+  if (!W) return WQD_E_ARG;
+  if (!wqd::aligned16(W)) return WQD_E_ALIGN;
+  st = check_packed_ptrs(fmt, w_packed, scales, zeros);
+  if (st != WQD_OK) return st;
+  return hip_status(wqd::launch_pack(fmt, W, 2 * F, K, ps, w_packed, scales, zeros, F, as_stream(stream)));
+}
+
+int wqd_qgemm_swiglu(int fmt, const void* x, int64_t M, int64_t F, int64_t K, const void* w_packed,
+                     const void* scales, const void* zeros, void* h, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (F < 1) return WQD_E_ARG;
+  if (F % 8 != 0) return WQD_E_SHAPE;
+  return wqd::qgemm_checked(fmt, x, M, 2 * F, K, w_packed, scales, zeros, h, workspace, workspace_bytes, stream,
+                            true);
 }
 
 int wqd_qgemm(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const void* w_packed, const void* scales,

@@ -26,6 +26,40 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Gate/up pairs packed for the SwiGLU epilogue (the MLP's gate and up
+// projections share their input, and its output is silu(gate) * up: CS336
+// lecture 10 notes, section 3.2 on the MLP's three matrices): the packed
+// matrix has N = 2F rows, 16-row block b holding gate rows 8b .. 8b + 7 and
+// then up rows 8b .. 8b + 7, from a source W = [gate rows 0 .. F - 1;
+// up rows F .. 2F - 1].  src_row gives the source row of packed row n (F = 0:
+// no interleave).
+__device__ __forceinline__ int64_t src_row(int64_t n, int64_t F) {
+  if (F == 0) return n;
+  const int64_t b = n / 16, r = n % 16;
+  return r < 8 ? 8 * b + r : F + 8 * b + (r - 8);
+}
+
+// The output of element (activation row m, packed row n) with final float32
+// value v.  Plain: y[m][n] = bf16(v), y with N columns.  SwiGLU: y has N / 2
+// columns; the gate element (n % 16 < 8) stores y[m][8 (n / 16) + n % 8] =
+// bf16(silu(v) * u), u = silu's partner value of packed row n + 8, which the
+// caller's lane `lane ^ PX` holds.  swiglu must be uniform over the
+// wavefront, and under it both lanes of a pair call this together (it
+// shuffles); `live` = this lane's element exists (the same for both of a pair).
+template <int PX>
+__device__ __forceinline__ void store_out(uint16_t* y, int64_t N, bool swiglu, int64_t m, int64_t n, float v,
+                                          bool live) {
+  if (!swiglu) {
+    if (live) y[m * N + n] = uint16_t(f32_to_bf16_rne(v));
+    return;
+  }
+  const float u = __shfl_xor(v, PX);
+  if (live && (n & 8) == 0) {
+    const float h = v / (1.0f + expf(-v)) * u;
+    y[m * (N / 2) + (n >> 4) * 8 + (n & 7)] = uint16_t(f32_to_bf16_rne(h));
+  }
+}
+
 // Two FP8-E4M3 codes (bytes 0,1 or bytes 2,3 of `w`) -> two bf16 in one register.
 // gfx950's conversion decodes the OCP E4M3FN encoding; every E4M3 value is
 // exactly representable in bf16, and a scale of 1 leaves it unchanged.

@@ -75,6 +75,7 @@ struct GmArgs {
   int nchunks;  // chunks of K
   int cps;      // chunks per split
   int S;
+  int swiglu;   // packed gate/up pairs: store silu(gate) * up (store_out)
 };
 
 template <int FMT>
@@ -517,11 +518,11 @@ __global__ __launch_bounds__((64 * GmT<FMT, WM>::WR * GmF<FMT>::WN)) void gemm_k
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = st.m0 + (st.wm * F::MF + i) * 16 + 4 * kb + r;
-        if (row >= a.M) continue;
+        if (row >= a.M) continue;  // the same for lanes n and n ^ 8
         if (a.S > 1)
           a.part[(int64_t(split) * a.M + row) * a.N + col] = st.acc[i][b][r];
         else
-          a.y[row * a.N + col] = uint16_t(f32_to_bf16_rne(st.acc[i][b][r] * cs));
+          store_out<8>(a.y, a.N, a.swiglu, row, col, st.acc[i][b][r] * cs, true);  // lane ^ 8: column ^ 8
       }
   }
 }
@@ -564,8 +565,9 @@ static hipError_t launch_gm_fmt(const GmArgs& a, const GmPlan& p, hipStream_t st
 }
 
 hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
-                       const void* scales, const void* zeros, void* y, void* ws, hipStream_t st) {
+                       const void* scales, const void* zeros, void* y, void* ws, bool swiglu, hipStream_t st) {
   GmArgs a;
+  a.swiglu = swiglu;
   a.x = reinterpret_cast<const uint16_t*>(x);
   a.y = reinterpret_cast<uint16_t*>(y);
   a.w = reinterpret_cast<const uint4*>(wp);
@@ -600,7 +602,7 @@ hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64
     if (e == hipSuccess) e = launch_gm_fmt<kFmtW4>(a, p, st);
   }
   if (e != hipSuccess || p.S == 1) return e;
-  return launch_splitk_reduce(fmt, a.part, p.S, M, N, scales, y, st);
+  return launch_splitk_reduce(fmt, a.part, p.S, M, N, scales, y, swiglu, st);
 }
 
 }  // namespace wqd

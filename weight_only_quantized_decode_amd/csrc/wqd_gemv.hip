@@ -41,6 +41,7 @@ struct GemvArgs {
   const void* scales;
   const uint16_t* zeros;
   int64_t N, K, NB, KT, G4;
+  int swiglu;  // packed gate/up pairs: store silu(gate) * up (store_out)
 };
 
 template <int FMT>
@@ -312,10 +313,9 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int w = 1; w < W; ++w) v += s_red[w][m][r];
     const int64_t row = nb * kTileRows + r;
-    if (row < a.N) {
-      if (FMT == kFmtFP8) v *= reinterpret_cast<const float*>(a.scales)[row];
-      a.y[int64_t(m) * a.N + row] = uint16_t(f32_to_bf16_rne(v));
-    }
+    const bool live = row < a.N;
+    if (FMT == kFmtFP8 && live) v *= reinterpret_cast<const float*>(a.scales)[row];
+    store_out<8>(a.y, a.N, a.swiglu, m, row, v, live);  // thread ^ 8 holds row ^ 8
   }
 }
 
@@ -344,8 +344,9 @@ static hipError_t launch_waves(const GemvArgs& a, int mr, int waves, unsigned gr
 }
 
 hipError_t launch_gemv(int fmt, const GemvPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
-                       const void* scales, const void* zeros, void* y, hipStream_t st) {
+                       const void* scales, const void* zeros, void* y, bool swiglu, hipStream_t st) {
   GemvArgs a;
+  a.swiglu = swiglu;
   a.w = reinterpret_cast<const uint4*>(wp);
   a.scales = scales;
   a.zeros = reinterpret_cast<const uint16_t*>(zeros);
@@ -359,7 +360,7 @@ hipError_t launch_gemv(int fmt, const GemvPlan& p, const void* x, int64_t M, int
     const int64_t m0 = int64_t(c) * kGemvMaxM;
     const int mr = int(M - m0 < kGemvMaxM ? M - m0 : int64_t(kGemvMaxM));
     a.x = reinterpret_cast<const uint16_t*>(x) + m0 * K;
-    a.y = reinterpret_cast<uint16_t*>(y) + m0 * N;
+    a.y = reinterpret_cast<uint16_t*>(y) + m0 * (swiglu ? N / 2 : N);  // SwiGLU output rows hold N / 2
     hipError_t e;
     if (fmt == kFmtBF16) e = launch_waves<kFmtBF16>(a, mr, p.waves, grid, st);
     else if (fmt == kFmtFP8) e = launch_waves<kFmtFP8>(a, mr, p.waves, grid, st);

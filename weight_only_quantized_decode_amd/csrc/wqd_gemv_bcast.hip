@@ -47,6 +47,7 @@ struct BcastArgs {
   const uint16_t* zeros;
   int64_t N, K, KT, G4;
   int per_wave;  // tiles per wavefront share of K (a multiple of 4)
+  int swiglu;    // packed gate/up pairs: store silu(gate) * up (store_out)
 };
 
 template <int FMT>
@@ -400,10 +401,9 @@ __global__ __launch_bounds__(64 * W) void gemv_bcast_kernel(BcastArgs a) {
 #pragma unroll
     for (int w = 1; w < W; ++w) v += s_red[w][m][r];
     const int64_t row = nb * kTileRows + r;
-    if (row < a.N) {
-      if (FMT == kFmtFP8) v *= reinterpret_cast<const float*>(a.scales)[row];
-      a.y[int64_t(m) * a.N + row] = uint16_t(f32_to_bf16_rne(v));
-    }
+    const bool live = row < a.N;
+    if (FMT == kFmtFP8 && live) v *= reinterpret_cast<const float*>(a.scales)[row];
+    store_out<8>(a.y, a.N, a.swiglu, m, row, v, live);  // thread ^ 8 holds row ^ 8
   }
 }
 
@@ -448,7 +448,8 @@ static hipError_t launch_bc_fmt(const BcastArgs& a, int mr, int waves, int ng, u
 }
 
 hipError_t launch_gemv_bcast(int fmt, const BcastPlan& p, const void* x, int64_t M, int64_t N, int64_t K,
-                             const void* wp, const void* scales, const void* zeros, void* y, hipStream_t st) {
+                             const void* wp, const void* scales, const void* zeros, void* y, bool swiglu,
+                             hipStream_t st) {
   if (M < 1 || M > (fmt == kFmtW4 ? kBcastMaxMW4 : kBcastMaxM)) return hipErrorInvalidValue;
   BcastArgs a;
   a.x = reinterpret_cast<const uint16_t*>(x);
@@ -461,6 +462,7 @@ hipError_t launch_gemv_bcast(int fmt, const BcastPlan& p, const void* x, int64_t
   a.KT = p.KT;
   a.G4 = fmt == kFmtW4 ? ceil_div(K / kGroup, kScaleQuad) : 0;
   a.per_wave = p.per_wave;
+  a.swiglu = swiglu;
   const unsigned grid = unsigned(p.NB);
   const int mr = int(M);
   if (fmt == kFmtBF16) return launch_bc_fmt<kFmtBF16>(a, mr, p.waves, p.groups, grid, st);

@@ -41,6 +41,7 @@ struct McArgs {
   const uint16_t* zeros;
   int64_t M, N, K, KT, G4, NB;
   int per_wave;
+  int swiglu;  // packed gate/up pairs: store silu(gate) * up (store_out)
 };
 
 // RB: 16-row blocks per wavefront (each x fragment feeds RB weight tiles).
@@ -254,10 +255,9 @@ __global__ __launch_bounds__(64 * W) void gemv_mc_kernel(McArgs a) {
 #pragma unroll
     for (int w = 1; w < W; ++w) v += s_red[w][b][m][r];
     const int64_t row = (nb0 + b) * kTileRows + r;
-    if (row < a.N) {
-      if (FMT == kFmtFP8) v *= reinterpret_cast<const float*>(a.scales)[row];
-      a.y[int64_t(m) * a.N + row] = uint16_t(f32_to_bf16_rne(v));
-    }
+    const bool live = row < a.N;
+    if (FMT == kFmtFP8 && live) v *= reinterpret_cast<const float*>(a.scales)[row];
+    store_out<8>(a.y, a.N, a.swiglu, m, row, v, live);  // element i ^ 8 (thread ^ 8) is row ^ 8
   }
 }
 
@@ -293,9 +293,10 @@ static hipError_t launch_mc_fmt(const McArgs& a, const McPlan& p, hipStream_t st
 }
 
 hipError_t launch_gemv_mc(int fmt, const McPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
-                          const void* scales, const void* zeros, void* y, hipStream_t st) {
+                          const void* scales, const void* zeros, void* y, bool swiglu, hipStream_t st) {
   if (M < 1 || M > kMcMaxM) return hipErrorInvalidValue;
   McArgs a;
+  a.swiglu = swiglu;
   a.x = reinterpret_cast<const uint16_t*>(x);
   a.y = reinterpret_cast<uint16_t*>(y);
   a.w = reinterpret_cast<const uint4*>(wp);

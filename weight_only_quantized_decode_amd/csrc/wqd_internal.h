@@ -8,29 +8,34 @@
 
 namespace wqd {
 
+// F > 0: W holds F gate rows then F up rows (N = 2F), packed interleaved for
+// the SwiGLU epilogue (src_row in wqd_device.h).
 hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, const PackedSizes& ps, void* wp, void* scales,
-                       void* zeros, hipStream_t st);
+                       void* zeros, int64_t F, hipStream_t st);
 hipError_t launch_dequant(int fmt, const void* wp, const void* scales, const void* zeros, int64_t N, int64_t K,
                           const PackedSizes& ps, float* out, hipStream_t st);
 hipError_t launch_unpack(int fmt, const void* wp, const void* scales, const void* zeros, int64_t N, int64_t K,
                          const PackedSizes& ps, void* codes, void* scales_out, void* zeros_out, hipStream_t st);
 hipError_t launch_decode_e4m3(const uint8_t* codes, float* out, int64_t n, hipStream_t st);
+// swiglu: the packed rows are gate/up pairs and y receives silu(gate) * up,
+// [M][N / 2] (store_out in wqd_device.h).
 hipError_t launch_gemv(int fmt, const GemvPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
-                       const void* scales, const void* zeros, void* y, hipStream_t st);
+                       const void* scales, const void* zeros, void* y, bool swiglu, hipStream_t st);
 hipError_t launch_gemv_bcast(int fmt, const BcastPlan& p, const void* x, int64_t M, int64_t N, int64_t K,
-                             const void* wp, const void* scales, const void* zeros, void* y, hipStream_t st);
+                             const void* wp, const void* scales, const void* zeros, void* y, bool swiglu,
+                             hipStream_t st);
 hipError_t launch_gemv_mc(int fmt, const McPlan& p, const void* x, int64_t M, int64_t N, int64_t K,
-                          const void* wp, const void* scales, const void* zeros, void* y, hipStream_t st);
+                          const void* wp, const void* scales, const void* zeros, void* y, bool swiglu, hipStream_t st);
 hipError_t launch_gemv_sk(int fmt, const SkPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
-                          const void* scales, const void* zeros, void* y, void* ws, hipStream_t st);
+                          const void* scales, const void* zeros, void* y, void* ws, bool swiglu, hipStream_t st);
 hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
-                       const void* scales, const void* zeros, void* y, void* ws, hipStream_t st);
+                       const void* scales, const void* zeros, void* y, void* ws, bool swiglu, hipStream_t st);
 // y = sum over s < S of part[s] (float32 [S][M][N], added in split order), FP8
 // scaled per column, rounded to bfloat16.
 hipError_t launch_splitk_reduce(int fmt, const float* part, int S, int64_t M, int64_t N, const void* scales, void* y,
-                                hipStream_t st);
+                                bool swiglu, hipStream_t st);
 hipError_t launch_mfma(int fmt, const MfmaPlan& p, int64_t M, int64_t N, int64_t K, const void* x, const void* wp,
-                       const void* scales, const void* zeros, void* y, void* ws, hipStream_t st);
+                       const void* scales, const void* zeros, void* y, void* ws, bool swiglu, hipStream_t st);
 // W8A8-FP8: activation codes and scale (workspace: the G partial maxima),
 // then the product on the FP8 matrix cores.
 hipError_t launch_act_quant(const void* x, int64_t M, int64_t K, int parts, void* codes, float* scale,
@@ -53,7 +58,8 @@ size_t mfma_peak_sink_words();
 double mfma_peak_flops(int64_t iters);
 // wqd_qgemm after its argument checks (shared by the entry points that call it).
 int qgemm_checked(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const void* w_packed, const void* scales,
-                  const void* zeros, void* y, void* workspace, size_t workspace_bytes, void* stream);
+                  const void* zeros, void* y, void* workspace, size_t workspace_bytes, void* stream,
+                  bool swiglu = false);
 // Maps a HIP error to a wqd status, keeping it for wqd_last_hip_error().
 int record_hip_error(hipError_t e);
 hipError_t launch_spec_accept(const float* target, const float* draft, const int32_t* tokens, const float* u_accept,

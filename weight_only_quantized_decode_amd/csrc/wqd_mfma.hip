@@ -51,6 +51,7 @@ struct MfmaArgs {
   int NBB, MB;  // column blocks (4 waves x BNT tiles), M-blocks
   int S;        // K splits
   int64_t cps;  // chunks per split
+  int swiglu;   // packed gate/up pairs: store silu(gate) * up (store_out)
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -264,13 +265,13 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = m0 + 16 * i + 4 * kb + r;
-        if (row < a.M) {
+        if (row < a.M) {  // the same for lanes n and n ^ 8
           float v = acc[i][j][r];
           if (a.S > 1) {
             a.part[(int64_t(split) * a.M + row) * a.N + col] = v;
           } else {
             if (FMT == kFmtFP8) v *= sc;
-            a.y[row * a.N + col] = uint16_t(f32_to_bf16_rne(v));
+            store_out<8>(a.y, a.N, a.swiglu, row, col, v, true);  // lane ^ 8: column ^ 8
           }
         }
       }
@@ -291,10 +292,10 @@ __device__ __forceinline__ float reduce_scale(float v, const float* __restrict__
 template <int FMT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t M,
                                                             int64_t N, const float* __restrict__ colscale,
-                                                            uint16_t* __restrict__ y) {
+                                                            uint16_t* __restrict__ y, int swiglu) {
   const int64_t MN = M * N;
   const int64_t i0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
-  if (i0 >= MN) return;
+  if (i0 >= MN) return;  // SwiGLU: N % 16 == 0, so a thread and its partner (^ 2) return together
   if ((MN & 3) == 0) {
     float4 v[kMaxSplits];
 #pragma unroll
@@ -309,10 +310,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         a.z += v[s].z;
         a.w += v[s].w;
       }
-    const uint32_t lo = f32_to_bf16_rne(reduce_scale<FMT>(a.x, colscale, i0, N)) |
-                        (f32_to_bf16_rne(reduce_scale<FMT>(a.y, colscale, i0 + 1, N)) << 16);
-    const uint32_t hi = f32_to_bf16_rne(reduce_scale<FMT>(a.z, colscale, i0 + 2, N)) |
-                        (f32_to_bf16_rne(reduce_scale<FMT>(a.w, colscale, i0 + 3, N)) << 16);
+    const float f[4] = {reduce_scale<FMT>(a.x, colscale, i0, N), reduce_scale<FMT>(a.y, colscale, i0 + 1, N),
+                        reduce_scale<FMT>(a.z, colscale, i0 + 2, N), reduce_scale<FMT>(a.w, colscale, i0 + 3, N)};
+    if (swiglu) {
+      // outputs i and i ^ 8 (columns n and n ^ 8 of one row) are 2 threads apart
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out<2>(y, N, true, (i0 + e) / N, (i0 + e) % N, f[e], true);
+      return;
+    }
+    const uint32_t lo = f32_to_bf16_rne(f[0]) | (f32_to_bf16_rne(f[1]) << 16);
+    const uint32_t hi = f32_to_bf16_rne(f[2]) | (f32_to_bf16_rne(f[3]) << 16);
     *reinterpret_cast<uint2*>(y + i0) = make_uint2(lo, hi);
     return;
   }
@@ -331,16 +338,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 hipError_t launch_splitk_reduce(int fmt, const float* part, int S, int64_t M, int64_t N, const void* scales, void* y,
-                                hipStream_t st) {
+                                bool swiglu, hipStream_t st) {
   if (S < 1 || S > kMaxSplits) return hipErrorInvalidValue;
+  if (swiglu && N % 16 != 0) return hipErrorInvalidValue;
   const int64_t quads = (M * N + 3) / 4;
   const dim3 grid(unsigned((quads + 255) / 256));
   const float* cs = reinterpret_cast<const float*>(scales);
   uint16_t* yo = reinterpret_cast<uint16_t*>(y);
   if (fmt == kFmtFP8)
-    hipLaunchKernelGGL(splitk_reduce_kernel<kFmtFP8>, grid, dim3(256), 0, st, part, S, M, N, cs, yo);
+    hipLaunchKernelGGL(splitk_reduce_kernel<kFmtFP8>, grid, dim3(256), 0, st, part, S, M, N, cs, yo, int(swiglu));
   else
-    hipLaunchKernelGGL(splitk_reduce_kernel<kFmtBF16>, grid, dim3(256), 0, st, part, S, M, N, cs, yo);
+    hipLaunchKernelGGL(splitk_reduce_kernel<kFmtBF16>, grid, dim3(256), 0, st, part, S, M, N, cs, yo, int(swiglu));
   return hipGetLastError();
 }
 
@@ -351,7 +359,7 @@ static hipError_t launch_mf(MfmaArgs a, hipStream_t st) {
   hipLaunchKernelGGL((mfma_kernel<FMT, BMS, BNT>), dim3(unsigned(grid), unsigned(a.S)), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.S == 1) return e;
-  return launch_splitk_reduce(FMT, a.part, a.S, a.M, a.N, a.scales, a.y, st);
+  return launch_splitk_reduce(FMT, a.part, a.S, a.M, a.N, a.scales, a.y, a.swiglu != 0, st);
 }
 
 template <int FMT>
@@ -363,8 +371,9 @@ static hipError_t launch_mf_fmt(const MfmaArgs& a, int bms, int bnt, hipStream_t
 }
 
 hipError_t launch_mfma(int fmt, const MfmaPlan& p, int64_t M, int64_t N, int64_t K, const void* x, const void* wp,
-                       const void* scales, const void* zeros, void* y, void* ws, hipStream_t st) {
+                       const void* scales, const void* zeros, void* y, void* ws, bool swiglu, hipStream_t st) {
   MfmaArgs a;
+  a.swiglu = swiglu;
   a.x = reinterpret_cast<const uint16_t*>(x);
   a.y = reinterpret_cast<uint16_t*>(y);
   a.w = reinterpret_cast<const uint4*>(wp);

@@ -33,7 +33,7 @@ __device__ __forceinline__ void store_row_slices(uint4* wp, const RowTile& rt, c
 
 // ------------------------------------------------------------------ BF16 pack
 __global__ __launch_bounds__(256) void pack_bf16_kernel(const float* __restrict__ W, int64_t N, int64_t K,
-                                                        int64_t NB, int64_t KT, uint4* __restrict__ wp) {
+                                                        int64_t NB, int64_t KT, uint4* __restrict__ wp, int64_t F) {
   RowTile rt;
   if (!row_tile(int64_t(blockIdx.x) * 256 + threadIdx.x, NB, KT, rt)) return;
   const int64_t k0 = rt.kt * 32;
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const float* __restrict_
   for (int i = 0; i < 8; ++i) {  // 8 x 4 consecutive k
     float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
     const int64_t k = k0 + 4 * i;
-    if (rt.n < N && k < K) f = *reinterpret_cast<const float4*>(W + rt.n * K + k);
+    if (rt.n < N && k < K) f = *reinterpret_cast<const float4*>(W + src_row(rt.n, F) * K + k);
     words[2 * i + 0] = f32_to_bf16_rne(f.x) | (f32_to_bf16_rne(f.y) << 16);
     words[2 * i + 1] = f32_to_bf16_rne(f.z) | (f32_to_bf16_rne(f.w) << 16);
   }
@@ -53,13 +53,13 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const float* __restrict_
 // Row scale s_n = max|W[n, :]| / 448 in float32 (1 for an all-zero row,
 // floored at 2^-126); one workgroup per (padded) row.
 __global__ __launch_bounds__(256) void fp8_rowscale_kernel(const float* __restrict__ W, int64_t N, int64_t K,
-                                                           float* __restrict__ scales) {
+                                                           float* __restrict__ scales, int64_t F) {
   __shared__ float red[4];
   const int64_t n = blockIdx.x;
   float a = 0.f;
   if (n < N) {
     for (int64_t k = int64_t(threadIdx.x) * 4; k < K; k += 1024) {
-      float4 f = *reinterpret_cast<const float4*>(W + n * K + k);
+      float4 f = *reinterpret_cast<const float4*>(W + src_row(n, F) * K + k);
       a = fmaxf(a, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
     }
   }
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void fp8_rowscale_kernel(const float* __restri
 
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const float* __restrict__ W, int64_t N, int64_t K,
                                                        int64_t NB, int64_t KT, const float* __restrict__ scales,
-                                                       uint4* __restrict__ wp) {
+                                                       uint4* __restrict__ wp, int64_t F) {
   RowTile rt;
   if (!row_tile(int64_t(blockIdx.x) * 256 + threadIdx.x, NB, KT, rt)) return;
   const int64_t k0 = rt.kt * 64;
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const float* __restrict__
     const int64_t k = k0 + 4 * i;
     uint32_t w = 0;
     if (rt.n < N && k < K) {
-      float4 f = *reinterpret_cast<const float4*>(W + rt.n * K + k);
+      float4 f = *reinterpret_cast<const float4*>(W + src_row(rt.n, F) * K + k);
       w = e4m3_encode(__fdiv_rn(f.x, s)) | (e4m3_encode(__fdiv_rn(f.y, s)) << 8) |
           (e4m3_encode(__fdiv_rn(f.z, s)) << 16) | (e4m3_encode(__fdiv_rn(f.w, s)) << 24);
     }
@@ -110,7 +110,8 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const float* __restrict__
 // (row, g4) are consecutive lanes and merge their zero nibbles into one uint16.
 __global__ __launch_bounds__(256) void pack_w4_kernel(const float* __restrict__ W, int64_t N, int64_t K,
                                                       int64_t NB, int64_t G, int64_t G4, uint4* __restrict__ wp,
-                                                      uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
+                                                      uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros,
+                                                      int64_t F) {
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t total = NB * G4 * kTileRows * kScaleQuad;
   const bool in_range = t < total;  // the grid is a multiple of 4 threads, so quads stay together
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256) void pack_w4_kernel(const float* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (valid) f = *reinterpret_cast<const float4*>(W + n * K + g * kGroup + 4 * i);
+    if (valid) f = *reinterpret_cast<const float4*>(W + src_row(n, F) * K + g * kGroup + 4 * i);
     v[4 * i + 0] = f.x;
     v[4 * i + 1] = f.y;
     v[4 * i + 2] = f.z;
@@ -267,19 +268,20 @@ __global__ __launch_bounds__(256) void decode_e4m3_kernel(const uint8_t* __restr
 static inline unsigned grid_for(int64_t threads) { return unsigned((threads + 255) / 256); }
 
 hipError_t launch_pack(int fmt, const float* W, int64_t N, int64_t K, const PackedSizes& ps, void* wp, void* scales,
-                       void* zeros, hipStream_t st) {
+                       void* zeros, int64_t F, hipStream_t st) {
   uint4* w4 = reinterpret_cast<uint4*>(wp);
   const int64_t rows_tiles = ps.NB * ps.KT * kTileRows;
   if (fmt == kFmtBF16) {
-    hipLaunchKernelGGL(pack_bf16_kernel, dim3(grid_for(rows_tiles)), dim3(256), 0, st, W, N, K, ps.NB, ps.KT, w4);
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3(grid_for(rows_tiles)), dim3(256), 0, st, W, N, K, ps.NB, ps.KT, w4, F);
   } else if (fmt == kFmtFP8) {
     float* sc = reinterpret_cast<float*>(scales);
-    hipLaunchKernelGGL(fp8_rowscale_kernel, dim3(unsigned(ps.NB * kTileRows)), dim3(256), 0, st, W, N, K, sc);
-    hipLaunchKernelGGL(pack_fp8_kernel, dim3(grid_for(rows_tiles)), dim3(256), 0, st, W, N, K, ps.NB, ps.KT, sc, w4);
+    hipLaunchKernelGGL(fp8_rowscale_kernel, dim3(unsigned(ps.NB * kTileRows)), dim3(256), 0, st, W, N, K, sc, F);
+    hipLaunchKernelGGL(pack_fp8_kernel, dim3(grid_for(rows_tiles)), dim3(256), 0, st, W, N, K, ps.NB, ps.KT, sc, w4,
+                       F);
   } else {
     const int64_t threads = ps.NB * ps.G4 * kTileRows * kScaleQuad;
     hipLaunchKernelGGL(pack_w4_kernel, dim3(grid_for(threads)), dim3(256), 0, st, W, N, K, ps.NB, ps.KT, ps.G4, w4,
-                       reinterpret_cast<uint16_t*>(scales), reinterpret_cast<uint16_t*>(zeros));
+                       reinterpret_cast<uint16_t*>(scales), reinterpret_cast<uint16_t*>(zeros), F);
   }
   return hipGetLastError();
 }

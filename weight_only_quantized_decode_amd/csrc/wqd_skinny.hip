@@ -68,6 +68,7 @@ struct SkArgs {
   int64_t M, N, K, KT, G4, NB;
   int per_split;  // tiles per split, a multiple of the ring size and of 4
   int S;
+  int swiglu;     // packed gate/up pairs: store silu(gate) * up (store_out)
 };
 
 template <int FMT>
@@ -373,11 +374,11 @@ __global__ __launch_bounds__(64 * (WN + 1)) void gemv_sk_kernel(SkArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = 16 * i + 4 * kb + r;
-        if (row >= a.M) continue;
+        if (row >= a.M) continue;  // the same for lanes n and n ^ 8
         if (a.S > 1)
           a.part[(int64_t(split) * a.M + row) * a.N + col] = st.acc[i][b][r];
         else
-          a.y[row * a.N + col] = uint16_t(f32_to_bf16_rne(st.acc[i][b][r] * cs));
+          store_out<8>(a.y, a.N, a.swiglu, row, col, st.acc[i][b][r] * cs, true);  // lane ^ 8: column ^ 8
       }
   }
 }
@@ -416,8 +417,9 @@ static hipError_t launch_sk_fmt(const SkArgs& a, const SkPlan& p, hipStream_t st
 }
 
 hipError_t launch_gemv_sk(int fmt, const SkPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
-                          const void* scales, const void* zeros, void* y, void* ws, hipStream_t st) {
+                          const void* scales, const void* zeros, void* y, void* ws, bool swiglu, hipStream_t st) {
   SkArgs a;
+  a.swiglu = swiglu;
   a.x = reinterpret_cast<const uint16_t*>(x);
   a.y = reinterpret_cast<uint16_t*>(y);
   a.part = reinterpret_cast<float*>(ws);
@@ -440,7 +442,7 @@ hipError_t launch_gemv_sk(int fmt, const SkPlan& p, const void* x, int64_t M, in
   else
     e = launch_sk_fmt<kFmtW4>(a, p, st);
   if (e != hipSuccess || p.S == 1) return e;
-  return launch_splitk_reduce(fmt, a.part, p.S, M, N, scales, y, st);
+  return launch_splitk_reduce(fmt, a.part, p.S, M, N, scales, y, swiglu, st);
 }
 
 }  // namespace wqd

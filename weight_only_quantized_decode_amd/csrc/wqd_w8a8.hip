@@ -410,7 +410,7 @@ hipError_t launch_w8a8(const W8Plan& p, const void* xc, const float* xscale, int
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
-  return launch_splitk_reduce(kFmtFP8, a.part, p.S, M, N, scales, y, st);
+  return launch_splitk_reduce(kFmtFP8, a.part, p.S, M, N, scales, y, false, st);
 }
 
 }  // namespace wqd

@@ -59,18 +59,21 @@ class Workload:
     outliers: bool
     cfg: int
     act: str = "bf16"  # "fp8": W8A8, activations quantised per tensor before each product
+    swiglu: bool = False  # gate_up writes silu(gate) * up (N / 2 columns), which down reads
 
     @property
     def launches(self) -> int:
         return self.layers * len(self.mats)
 
-    def call_bytes(self, N: int, K: int) -> int:
+    def call_bytes(self, N: int, K: int, name: str = "") -> int:
         if self.act == "fp8":
             return call_bytes_w8a8(self.M, N, K)
+        if self.swiglu and name == "gate_up":  # y holds N / 2 columns
+            return call_bytes(self.fmt, self.M, N, K) - 2 * self.M * (N // 2)
         return call_bytes(self.fmt, self.M, N, K)
 
     def step_bytes(self) -> int:
-        return self.layers * sum(self.call_bytes(N, K) for _, N, K in self.mats)
+        return self.layers * sum(self.call_bytes(N, K, name) for name, N, K in self.mats)
 
     def step_flops(self) -> int:
         return self.layers * sum(call_flops(self.M, N, K) for _, N, K in self.mats)
@@ -101,11 +104,14 @@ def fuse_layer(mats) -> tuple:
 FUSED_PARTS = {"qkv": ("q", "k", "v"), "gate_up": ("gate", "up")}
 
 
-def stack_70b(fmt: str, M: int, layers: int = 80, fused: bool = False) -> Workload:
+def stack_70b(fmt: str, M: int, layers: int = 80, fused: bool = False, swiglu: bool = False) -> Workload:
+    """swiglu: the fused layout with gate/up packed for the SwiGLU epilogue;
+    gate_up writes h = silu(gate) * up and the down projection reads h."""
     cfg = 3 if fmt == "fp8" else 4
-    mats = fuse_layer(I.LAYER_70B) if fused else I.LAYER_70B
-    tag = "_fused" if fused else ""
-    return Workload(f"70b_{fmt}_stack_{layers}l_m{M}{tag}", fmt, M, layers, mats, fmt == "w4a16", cfg)
+    mats = fuse_layer(I.LAYER_70B) if fused or swiglu else I.LAYER_70B
+    tag = "_swiglu" if swiglu else "_fused" if fused else ""
+    return Workload(f"70b_{fmt}_stack_{layers}l_m{M}{tag}", fmt, M, layers, mats, fmt == "w4a16", cfg,
+                    swiglu=swiglu)
 
 
 def stack_7b_bf16(M: int = 1, layers: int = 32, fused: bool = False) -> Workload:
