@@ -561,7 +561,7 @@ def attn_stack_timing(args, stream, B=32, ctx=2048, layers=80):
            "algorithmic_bytes_per_step": layers * per_layer, "GBps": round(gbps, 2),
            "step_samples_ms": {"n": len(samples), "median": round(statistics.median(samples), 4),
                                "min": round(min(samples), 4), "max": round(max(samples), 4)},
-           "splits": wqd.attn_workspace_bytes(B, ATTN_HQ, ATTN_HKV, ctx) // (B * ATTN_HQ * 130 * 4),
+           "splits": wqd.attn_splits(B, ATTN_HQ, ATTN_HKV, ctx),
            "kernel": "attn_split_kernel (+ attn_combine_kernel when the context is split) per layer"}
     del caches
     free_cache()

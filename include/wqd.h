@@ -279,6 +279,9 @@ int wqd_qgemm_w8a8(const void* x_codes, const float* x_scale, int64_t M, int64_t
  *   (parity of the layout).
  */
 int wqd_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, size_t* bytes);
+/* Host only: how many chunks the context of each (sequence, KV head) is split
+ * into for these sizes (1: one workgroup per pair writes the output). */
+int wqd_attn_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, int* splits);
 int wqd_decode_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, float scale, void* out,
                          void* workspace, size_t workspace_bytes, void* stream);

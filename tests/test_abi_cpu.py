@@ -101,6 +101,26 @@ def test_workspace_query():
     assert L.wqd_workspace_bytes(2, 0, 64, 128, ctypes.byref(b)) == E_ARG
 
 
+def test_attention_plan_queries():
+    # one (sequence, KV head) pair per workgroup once the pairs alone give
+    # about 256 workgroups: no split, no workspace
+    assert wqd.attn_splits(32, 64, 8, 2048) == 1
+    assert wqd.attn_workspace_bytes(32, 64, 8, 2048) == 0
+    # one sequence: the context is split, each split at least 2 steps of 32
+    # positions per wavefront of 4; partial maximum, sum and 128 outputs per split
+    for L in (128, 1024, 8192, 32768):
+        S = wqd.attn_splits(1, 64, 8, L)
+        assert 1 <= S <= max(1, L // 32 // 8) and S <= -(-256 // 8)
+        ws = wqd.attn_workspace_bytes(1, 64, 8, L)
+        assert ws == (64 * S * 130 * 4 if S > 1 else 0)
+    b, s = ctypes.c_size_t(), ctypes.c_int()
+    L = wqd.lib()
+    assert L.wqd_attn_splits(1, 64, 8, 1024, 128, None) == E_ARG
+    assert L.wqd_attn_splits(1, 64, 8, 1000, 128, ctypes.byref(s)) == E_SHAPE  # Lmax % 32
+    assert L.wqd_attn_splits(1, 64, 8, 1024, 64, ctypes.byref(s)) == E_SHAPE  # D != 128
+    assert L.wqd_attn_workspace_bytes(0, 64, 8, 1024, 128, ctypes.byref(b)) == E_ARG
+
+
 def test_kernel_path_choice():
     """Which kernel family serves each decode shape (host planning only)."""
     # broadcast kernel: 1 W4A16 row, 1-4 FP8 / BF16 rows; more waves for small N

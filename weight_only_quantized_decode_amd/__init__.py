@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "wqd_qgemm_swiglu": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
             "wqd_act_quant_fp8": (i32, [vp, i64, i64, vp, vp, vp, sz, vp]),
             "wqd_attn_workspace_bytes": (i32, [i64, i64, i64, i64, i64, psz]),
+            "wqd_attn_splits": (i32, [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int)]),
             "wqd_decode_attention": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp, vp, sz,
                                             vp]),
             "wqd_kv_pack": (i32, [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp]),
@@ -343,6 +344,12 @@ def attn_workspace_bytes(B: int, Hq: int, Hkv: int, Lmax: int, D: int = 128) -> 
     b = ctypes.c_size_t()
     _check(lib().wqd_attn_workspace_bytes(B, Hq, Hkv, Lmax, D, ctypes.byref(b)), "wqd_attn_workspace_bytes")
     return b.value
+
+
+def attn_splits(B: int, Hq: int, Hkv: int, Lmax: int, D: int = 128) -> int:
+    s = ctypes.c_int()
+    _check(lib().wqd_attn_splits(B, Hq, Hkv, Lmax, D, ctypes.byref(s)), "wqd_attn_splits")
+    return s.value
 
 
 @dataclass

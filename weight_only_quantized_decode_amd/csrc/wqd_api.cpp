@@ -217,6 +217,15 @@ int wqd_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, i
   return WQD_OK;
 }
 
+int wqd_attn_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, int* splits) {
+  if (!splits) return WQD_E_ARG;
+  wqd::AttnPlan p;
+  const int st = wqd::plan_attn(B, Hq, Hkv, Lmax, D, &p);
+  if (st != wqd::kOK) return st;
+  *splits = p.S;
+  return WQD_OK;
+}
+
 int wqd_decode_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, float scale, void* out,
                          void* workspace, size_t workspace_bytes, void* stream) {
