@@ -16,15 +16,24 @@ The same run also reports, each from its own graph replays:
   * "targets": the rows the >= 80%-of-measured-bandwidth target names, the
     W4A16 stack at M = 4 and 8 (the headline's packed weights, new x) and the
     FP8-E4M3 stack at M = 1 and 8 (fused layout);
+  * "swiglu_layout": the fused stack with gate/up packed for the SwiGLU
+    epilogue (down reads silu(gate) * up);
+  * "chain": the fused stack at M <= 2 as one persistent launch
+    (wqd_chain_run: every matrix of the step, each waiting for the output it
+    reads);
+  * "next_rows": W8A8-FP8 on the gate matrix at 1024 rows, and the stack's
+    decode attention at batch 32 over 2,048 positions;
   * "roofline": the dominant kernel (the launches of the step's costliest
     kernel family, replayed on their own) against the 8 TB/s HBM peak;
   * "cpu_baseline": the oracle on one full layer of the same workload on the
     host cores, extrapolated to the stack.
 
 Prints ONE JSON line.  Options: --workload w4a16_70b | fp8_70b | bf16_7b |
-gemv4096 | verify:<fmt>:<mat>; --m (activation rows); --separate (time the
-separate layout as the headline); --no-alt; --no-targets; --pmc-probe (a short
-fixed launch sequence for hardware-counter runs).  A single-matrix workload
+w4a16_70b_swiglu | fp8_70b_swiglu | gemv4096 | verify:<fmt>:<mat> |
+w8a8:<mat> | attn_70b; --m (activation rows); --separate (time the separate
+layout as the headline); --no-alt; --no-targets; --chain (time only the
+chain launch; --chain-workgroups sets its grid); --pmc-probe (a short fixed
+launch sequence for hardware-counter runs).  A single-matrix workload
 (gemv4096, verify:...) is packed into identical copies making 1.2 GB and each
 call uses the next one, so that it too reads its weights from HBM; its step is
 one call.
@@ -63,6 +72,10 @@ def parse():
     ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape timing breakdown")
     ap.add_argument("--spec", action="store_true",
                     help="also time the speculative accept / reject step (64 sequences x 4 drafts, 128256-token vocabulary)")
+    ap.add_argument("--chain", action="store_true",
+                    help="time the stack as one persistent chain launch (wqd_chain_run) as the headline")
+    ap.add_argument("--chain-workgroups", type=int, default=0,
+                    help="grid of the chain launch (0: the library's choice)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run 8 x 1 GiB copies and 16 launches of the dominant kernel, then exit")
     return ap.parse_args()
@@ -76,6 +89,8 @@ def make_workload(name, fmt_m, layers, fused):
         return WL.stack_70b("w4a16", m, layers or 80, fused)
     if name == "fp8_70b":
         return WL.stack_70b("fp8", m, layers or 80, fused)
+    if name in ("w4a16_70b_swiglu", "fp8_70b_swiglu"):
+        return WL_stack(name.replace("_swiglu", ""), m, layers)
     if name == "bf16_7b":
         return WL.stack_7b_bf16(m, layers or 32, fused)
     if name == "gemv4096":
@@ -297,6 +312,60 @@ def time_step(wl, packed, args, stream, dominant=False, shapes=False):
                          "kernel": kernel_group(wl, N, K)}
         res["shapes"] = out
     del xs, ys, ws
+    return res
+
+
+def chain_steps(wl, packed):
+    """The stack as a dependent chain for one persistent launch: qkv reads the
+    previous layer's down output, o the first M x 8192 of qkv's output (in
+    place of attention's), gate/up o's output, down the SwiGLU output (or, in
+    the plain fused layout, the first M x 28672 of gate/up's output in place
+    of it).  One set of buffers serves every layer: each buffer's readers are
+    ancestors of its next writer through the waits."""
+    import torch
+
+    import weight_only_quantized_decode_amd as wqd
+    import wqd_inputs as I
+
+    dev = torch.device("cuda", 0)
+    K0 = wl.mats[0][2]
+    x0 = I.x_bf16(I.x_seed(wl.cfg, wl.M, K0), wl.M, K0, outliers=wl.outliers).to(dev)
+    bufs = {}
+    steps = []
+    prev = x0
+    for layer, row in enumerate(packed):
+        for (name, N, K), pw in zip(wl.mats, row):
+            swi = wl.swiglu and name == "gate_up"
+            cols = N // 2 if swi else N
+            if name not in bufs:
+                bufs[name] = torch.empty((wl.M, cols), dtype=torch.bfloat16, device=dev)
+            x = prev if prev.shape[1] == K else prev.reshape(-1)[: wl.M * K].view(wl.M, K)
+            steps.append(wqd.ChainStep(x, pw, bufs[name], len(steps) - 1, swi))
+            prev = bufs[name]
+    return steps, x0
+
+
+def chain_timing(wl, packed, args, stream):
+    """The step as one chain launch (plus its clearing launch), replayed from a graph."""
+    import weight_only_quantized_decode_amd as wqd
+
+    steps, _ = chain_steps(wl, packed)
+    chain = wqd.chain_prepare(steps, workgroups=args.chain_workgroups)
+    log(f"[bench] chain {wl.name}: {len(steps)} calls, {chain.plan.total_items} items, "
+        f"{chain.plan.workgroups} workgroups")
+    ms, samples = replay_timing(lambda: wqd.chain_run(chain), stream, args.steps, args.warmup, not args.no_graph)
+    st = wqd.chain_status(chain, stream)
+    if st != 0:
+        raise RuntimeError(f"chain run reported status {st}")
+    gbps = wl.step_bytes() / (ms / 1e3) / 1e9
+    res = {"workload": wl.name, "fmt": wl.fmt, "M": wl.M, "layers": wl.layers, "calls": len(steps),
+           "launches_per_step": 2, "workgroups": chain.plan.workgroups, "items": chain.plan.total_items,
+           "ms_per_step": round(ms, 4), "GBps": round(gbps, 2),
+           "step_samples_ms": {"n": len(samples), "median": round(statistics.median(samples), 4),
+                               "min": round(min(samples), 4), "max": round(max(samples), 4)},
+           "kernel": "chain_kernel: every matrix of the step in one persistent launch, each waiting for "
+                     "the output it reads"}
+    del chain, steps
     return res
 
 
@@ -651,9 +720,17 @@ def main():
     wl = make_workload(args.workload, args.m, args.layers, fused)
 
     packed = pack_stack(wl)
+    if args.chain:
+        r = chain_timing(wl, packed, args, stream)
+        r["pct_measured_read_ceiling"] = pct(r["GBps"], ceiling[0])
+        print(json.dumps({"chain": r}), flush=True)
+        return
     head = time_step(wl, packed, args, stream, dominant=True, shapes=not args.no_shapes)
     targets = []
     is_stack = wl.layers > 1 and args.workload in ("w4a16_70b", "fp8_70b", "bf16_7b")
+    chain_rec = None
+    if is_stack and fused and wl.M <= 2 and not args.no_alt:
+        chain_rec = chain_timing(wl, packed, args, stream)
     if is_stack and not args.no_targets and args.workload == "w4a16_70b" and fused:
         for fmt, M in TARGET_ROWS:
             if fmt == wl.fmt and M != wl.M:
@@ -739,6 +816,9 @@ def main():
     if swiglu_rec is not None:
         swiglu_rec["pct_measured_read_ceiling"] = pct(swiglu_rec["GBps"], ceiling[0])
         out["swiglu_layout"] = swiglu_rec
+    if chain_rec is not None:
+        chain_rec["pct_measured_read_ceiling"] = pct(chain_rec["GBps"], ceiling[0])
+        out["chain"] = chain_rec
     if targets:
         for t in targets:
             t["pct_measured_read_ceiling"] = pct(t["GBps"], ceiling[0])

@@ -79,7 +79,8 @@ enum wqd_status {
     WQD_E_ALIGN = 3,        /* a pointer is not 16-byte aligned */
     WQD_E_WORKSPACE = 4,    /* workspace missing or smaller than wqd_workspace_bytes */
     WQD_E_HIP = 5,          /* a HIP runtime call failed; see wqd_last_hip_error() */
-    WQD_E_UNSUPPORTED = 6   /* a valid request this build cannot serve */
+    WQD_E_UNSUPPORTED = 6,  /* a valid request this build cannot serve */
+    WQD_E_TIMEOUT = 7       /* a chain run abandoned a wait (wqd_chain_status) */
 };
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -291,6 +292,75 @@ int wqd_kv_append(const void* k_new, const void* v_new, const int32_t* positions
                   int64_t Lmax, int64_t D, void* k_cache, void* v_cache, void* stream);
 int wqd_kv_unpack(const void* k_cache, const void* v_cache, int64_t B, int64_t Hkv, int64_t Lmax, int64_t D,
                   void* k_out, void* v_out, void* stream);
+
+/*
+ * A chain of decode linear layers in one persistent launch.  Sources: CS336
+ * lecture 10 notes, section 3.2 (a layer's matrices run in sequence, each on
+ * the previous one's output: the attention projections, then the MLP's
+ * gate/up and down); "Only Accepted Tokens Count" reading notes, on why the
+ * paired experiments turn CUDA graphs on (a step made of many small kernels
+ * pays a launch cost for each); "Making each token cheaper", "Why decode is
+ * usually bandwidth bound" (a decode step reads every weight byte once, so
+ * the step time is the weight bytes over the bandwidth).
+ *
+ * Call i computes y_i = x_i . dequant(W_i)^T, or with swiglu the SwiGLU of a
+ * wqd_pack_gate_up pair, as wqd_qgemm / wqd_qgemm_swiglu would (the
+ * broadcast streaming kernel's per-tile arithmetic, 4 wavefronts splitting K
+ * for each pair of 16-row blocks), for 1 <= M <= 2 activation rows.  A call whose x is written by an
+ * earlier call j names j in wait_for: its products start once every output
+ * of call j is stored, while the weights of later calls stream meanwhile.
+ *   wqd_chain_call, per call:
+ *     w_packed, scales, zeros  device, from wqd_pack_weights / wqd_pack_gate_up
+ *     x   device bf16 [M][K];  y  device bf16 [M][N] ([M][N / 2] with swiglu);
+ *         both 16-byte aligned
+ *     N, K      as for wqd_qgemm (swiglu: N % 16 == 0)
+ *     wait_for  an earlier call whose y x reads (0 <= wait_for < i), or -1
+ *               when x is ready before the run starts
+ *     swiglu    0, or 1 for a gate/up pair
+ *   Memory: a call may overwrite memory that another call reads only when
+ *   that reader is among its ancestors through wait_for; the library orders
+ *   nothing else.
+ *
+ * wqd_chain_workspace_bytes: host only; the device workspace a chain of
+ *   ncalls needs (the call table, completion counters and a status flag).
+ * wqd_chain_prepare (setup; synchronous copy to the device): validates every
+ *   call as wqd_qgemm would, writes the table into `workspace` (16-byte
+ *   aligned, >= wqd_chain_workspace_bytes; leave it untouched between runs)
+ *   and fills *plan (caller-owned).  workgroups: 0 for the library's choice,
+ *   else the grid size, at most the workgroups the device keeps resident at
+ *   once (WQD_E_UNSUPPORTED beyond).  Errors: as wqd_qgemm for a call;
+ *   WQD_E_ARG for M outside 1..2 (WQD_E_UNSUPPORTED above 2), ncalls < 1 or
+ *   > 65536, a wait_for outside [-1, i); WQD_E_WORKSPACE; WQD_E_HIP.
+ * wqd_chain_run: enqueues two launches on `stream` (counters cleared, then
+ *   the chain); may be captured in a graph.  The grid is persistent: nothing
+ *   else may run on the device at the same time.  Each wait is bounded by
+ *   plan->wait_ticks ticks of the GPU's 100 MHz clock (0.1 s as prepared);
+ *   past it the run is abandoned instead of hanging.
+ * wqd_chain_status: synchronizes `stream`, then reports the last run:
+ *   WQD_OK; WQD_E_TIMEOUT (a wait was abandoned: outputs are incomplete);
+ *   WQD_E_ARG (the plan passed to the run did not match the prepared table).
+ */
+typedef struct {
+    const void* w_packed;
+    const void* scales;
+    const void* zeros;
+    const void* x;
+    void* y;
+    int64_t N, K;
+    int32_t wait_for;
+    int32_t swiglu;
+} wqd_chain_call;
+
+typedef struct {
+    int32_t fmt, M, ncalls, total_items, workgroups, reserved;
+    int64_t wait_ticks;
+} wqd_chain_plan;
+
+int wqd_chain_workspace_bytes(int64_t ncalls, size_t* bytes);
+int wqd_chain_prepare(int fmt, int64_t M, int64_t ncalls, const wqd_chain_call* calls, int workgroups,
+                      void* workspace, size_t workspace_bytes, wqd_chain_plan* plan);
+int wqd_chain_run(const wqd_chain_plan* plan, void* workspace, void* stream);
+int wqd_chain_status(const void* workspace, void* stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

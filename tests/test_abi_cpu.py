@@ -265,3 +265,62 @@ def test_spec_accept_rejects_bad_arguments():
     assert call(B=0) == E_ARG and call(k=-1) == E_ARG and call(V=0) == E_ARG
     assert call(k=65) == E_SHAPE and call(V=(1 << 20) + 1) == E_SHAPE
     assert call(target=A + 2) == E_ALIGN and call(out=A + 1) == E_ALIGN
+
+
+def test_chain_rejects_bad_arguments_before_any_device_call():
+    """wqd_chain_prepare validates every call before it asks the device
+    anything; wqd_chain_run validates the plan before it enqueues."""
+    L = wqd.lib()
+    A = 0x10000
+    C, P = wqd.ChainCallC, wqd.ChainPlanC
+    b = ctypes.c_size_t()
+    assert L.wqd_chain_workspace_bytes(0, ctypes.byref(b)) == E_ARG
+    assert L.wqd_chain_workspace_bytes(2, None) == E_ARG
+    assert L.wqd_chain_workspace_bytes(3, ctypes.byref(b)) == OK
+    # 256 bytes of header and flag, 3 table entries of 128 bytes (the two
+    # rounded up to 768), then 64 counters of 128 bytes per call
+    assert b.value == 768 + 3 * 64 * 128
+    ws = b.value
+
+    def calls(**kw):
+        arr = (C * 3)()
+        for i in range(3):
+            arr[i] = C(A, A, A, A, A, 256, 512, i - 1, 0)
+        for key, (i, val) in kw.items():
+            setattr(arr[i], key, val)
+        return arr
+
+    plan = P()
+
+    def prep(arr, fmt=2, M=1, n=3, wg=0, wsb=ws, wsp=A):
+        return L.wqd_chain_prepare(fmt, M, n, arr, wg, wsp, wsb, ctypes.byref(plan))
+
+    assert prep(calls(), M=0) == E_ARG
+    assert prep(calls(), M=3) == 6  # WQD_E_UNSUPPORTED: at most 2 rows
+    assert prep(calls(), fmt=7) == E_ARG
+    assert prep(calls(), n=0) == E_ARG
+    assert prep(calls(), wg=-1) == E_ARG
+    assert prep(calls(), wsb=ws - 1) == E_WS
+    assert prep(calls(), wsp=None) == E_WS
+    assert prep(calls(), wsp=A + 4) == E_ALIGN
+    assert prep(calls(wait_for=(1, 1))) == E_ARG   # waits on itself
+    assert prep(calls(wait_for=(2, 5))) == E_ARG   # waits on a later call
+    assert prep(calls(wait_for=(0, -2))) == E_ARG
+    assert prep(calls(K=(1, 500))) == E_SHAPE      # W4A16 rows are whole groups of 128
+    assert prep(calls(x=(2, None))) == E_ARG
+    assert prep(calls(y=(0, A + 2))) == E_ALIGN
+    assert prep(calls(zeros=(1, None))) == E_ARG
+    assert prep(calls(N=(1, 40), swiglu=(1, 1))) == E_SHAPE  # gate/up pairs fill 16-row blocks
+    assert prep(calls(swiglu=(0, 2))) == E_ARG
+    # the run checks its plan before enqueueing
+    bad = P(2, 1, 3, 10, 0, 0, 10)
+    assert L.wqd_chain_run(ctypes.byref(bad), A, None) == E_ARG  # no workgroups
+    bad = P(2, 3, 3, 10, 4, 0, 10)
+    assert L.wqd_chain_run(ctypes.byref(bad), A, None) == E_ARG  # 3 rows
+    bad = P(9, 1, 3, 10, 4, 0, 10)
+    assert L.wqd_chain_run(ctypes.byref(bad), A, None) == E_ARG
+    bad = P(2, 1, 3, 10, 4, 0, -1)
+    assert L.wqd_chain_run(ctypes.byref(bad), A, None) == E_ARG
+    assert L.wqd_chain_run(None, A, None) == E_ARG
+    assert L.wqd_chain_status(None, None) == E_ARG
+    assert L.wqd_status_str(7) == b"chain run abandoned a wait"

@@ -39,6 +39,20 @@ class WqdError(RuntimeError):
 _SIGNATURE_NAMES: list = []
 
 
+class ChainCallC(ctypes.Structure):
+    """wqd_chain_call."""
+    _fields_ = [("w_packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("wait_for", ctypes.c_int32), ("swiglu", ctypes.c_int32)]
+
+
+class ChainPlanC(ctypes.Structure):
+    """wqd_chain_plan."""
+    _fields_ = [("fmt", ctypes.c_int32), ("M", ctypes.c_int32), ("ncalls", ctypes.c_int32),
+                ("total_items", ctypes.c_int32), ("workgroups", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("wait_ticks", ctypes.c_int64)]
+
+
 def lib() -> ctypes.CDLL:
     """The loaded C library (raises if it has not been built)."""
     global _lib
@@ -73,6 +87,11 @@ def lib() -> ctypes.CDLL:
             "wqd_kv_unpack": (i32, [vp, vp, i64, i64, i64, i64, vp, vp, vp]),
             "wqd_w8a8_workspace_bytes": (i32, [i64, i64, i64, psz]),
             "wqd_qgemm_w8a8": (i32, [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]),
+            "wqd_chain_workspace_bytes": (i32, [i64, psz]),
+            "wqd_chain_prepare": (i32, [i32, i64, i64, ctypes.POINTER(ChainCallC), i32, vp, sz,
+                                        ctypes.POINTER(ChainPlanC)]),
+            "wqd_chain_run": (i32, [ctypes.POINTER(ChainPlanC), vp, vp]),
+            "wqd_chain_status": (i32, [vp, vp]),
             "wqd_dequant": (i32, [i32, vp, vp, vp, i64, i64, vp, vp]),
             "wqd_unpack": (i32, [i32, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
             "wqd_decode_e4m3": (i32, [vp, vp, i64, vp]),
@@ -284,6 +303,78 @@ def qgemm_noalloc(x, pw: PackedWeight, y, stream=None):
     _check(lib().wqd_qgemm_noalloc(_fmt(pw.fmt), x.data_ptr(), M, pw.N, K, _ptr(pw.w), _ptr(pw.scales),
                                    _ptr(pw.zeros), y.data_ptr(), _stream(stream)), "wqd_qgemm_noalloc")
     return y
+
+
+# ----------------------------------------------------------------------------- chains
+@dataclass
+class ChainStep:
+    """One call of a chain: y = x . dequant(pw)^T (swiglu: the SwiGLU of a
+    pack_gate_up pair, y with N / 2 columns); wait_for = index of the earlier
+    step whose y this x is (or is part of), -1 when x is ready beforehand."""
+    x: "object"
+    pw: PackedWeight
+    y: "object"
+    wait_for: int = -1
+    swiglu: bool = False
+
+
+@dataclass
+class Chain:
+    plan: ChainPlanC
+    workspace: "object"   # torch uint8 device tensor holding the call table and counters
+    steps: list           # the ChainSteps (their tensors stay referenced)
+
+
+def chain_workspace_bytes(ncalls: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().wqd_chain_workspace_bytes(ncalls, ctypes.byref(b)), "wqd_chain_workspace_bytes")
+    return b.value
+
+
+def chain_prepare(steps, workgroups: int = 0, workspace=None) -> Chain:
+    """wqd_chain_prepare: validate the steps (one format, the same M rows of
+    x for all) and write the call table into a device workspace."""
+    import torch
+
+    if not steps:
+        raise ValueError("a chain needs at least one step")
+    fmt = _fmt(steps[0].pw.fmt)
+    M = steps[0].x.shape[0]
+    arr = (ChainCallC * len(steps))()
+    for i, st in enumerate(steps):
+        if _fmt(st.pw.fmt) != fmt:
+            raise ValueError("every step of a chain uses one weight format")
+        if st.x.dtype != torch.bfloat16 or st.x.dim() != 2 or not st.x.is_contiguous() or st.x.shape[0] != M:
+            raise ValueError(f"step {i}: x must be a contiguous bfloat16 [{M}, K] tensor")
+        if st.x.shape[1] != st.pw.K:
+            raise ValueError(f"step {i}: K mismatch: x has {st.x.shape[1]}, weights have {st.pw.K}")
+        cols = st.pw.N // 2 if st.swiglu else st.pw.N
+        if st.y.dtype != torch.bfloat16 or tuple(st.y.shape) != (M, cols) or not st.y.is_contiguous():
+            raise ValueError(f"step {i}: y must be a contiguous bfloat16 [{M}, {cols}] tensor")
+        arr[i] = ChainCallC(_ptr(st.pw.w), _ptr(st.pw.scales), _ptr(st.pw.zeros), st.x.data_ptr(), st.y.data_ptr(),
+                            st.pw.N, st.pw.K, int(st.wait_for), 1 if st.swiglu else 0)
+    need = chain_workspace_bytes(len(steps))
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=steps[0].x.device)
+    plan = ChainPlanC()
+    _check(lib().wqd_chain_prepare(fmt, M, len(steps), arr, workgroups, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), ctypes.byref(plan)),
+           "wqd_chain_prepare")
+    return Chain(plan, workspace, list(steps))
+
+
+def chain_run(chain: Chain, stream=None):
+    """wqd_chain_run: the whole chain in one persistent launch (after a small
+    clearing launch), on the current stream; graph-capturable."""
+    _check(lib().wqd_chain_run(ctypes.byref(chain.plan), chain.workspace.data_ptr(), _stream(stream)),
+           "wqd_chain_run")
+
+
+def chain_status(chain: Chain, stream=None) -> int:
+    """wqd_chain_status: synchronizes the stream; 0 when the last run
+    completed, WQD_E_TIMEOUT (7) when it abandoned a wait, WQD_E_ARG (1) when
+    the plan did not match the table."""
+    return int(lib().wqd_chain_status(chain.workspace.data_ptr(), _stream(stream)))
 
 
 ACT_QUANT_WORKSPACE_BYTES = 4096  # WQD_ACT_QUANT_WORKSPACE_BYTES

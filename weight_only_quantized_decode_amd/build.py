@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwqd.so")
-SOURCES = ["wqd_plan.cpp", "wqd_api.cpp", "wqd_pack.hip", "wqd_gemv.hip", "wqd_gemv_bcast.hip", "wqd_gemv_mc.hip", "wqd_skinny.hip", "wqd_gemm.hip", "wqd_mfma.hip", "wqd_stream.hip", "wqd_spec.hip", "wqd_noalloc.hip", "wqd_w8a8.hip", "wqd_attn.hip"]
+SOURCES = ["wqd_plan.cpp", "wqd_api.cpp", "wqd_pack.hip", "wqd_gemv.hip", "wqd_gemv_bcast.hip", "wqd_gemv_mc.hip", "wqd_skinny.hip", "wqd_gemm.hip", "wqd_mfma.hip", "wqd_stream.hip", "wqd_spec.hip", "wqd_noalloc.hip", "wqd_w8a8.hip", "wqd_attn.hip", "wqd_chain.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}"]

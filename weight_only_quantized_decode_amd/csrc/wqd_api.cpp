@@ -2,6 +2,8 @@
 // plan, then enqueue on the caller's stream.  No allocation, no host sync.
 #include <hip/hip_runtime.h>
 
+#include <vector>
+
 #include "../../include/wqd.h"
 #include "wqd_internal.h"
 #include "wqd_plan.h"
@@ -87,6 +89,7 @@ const char* wqd_status_str(int status) {
     case WQD_E_WORKSPACE: return "workspace missing or too small";
     case WQD_E_HIP: return "HIP runtime error";
     case WQD_E_UNSUPPORTED: return "unsupported request";
+    case WQD_E_TIMEOUT: return "chain run abandoned a wait";
     default: return "unknown status";
   }
 }
@@ -215,6 +218,91 @@ int wqd_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, i
   if (st != wqd::kOK) return st;
   *bytes = p.ws_bytes;
   return WQD_OK;
+}
+
+int wqd_chain_workspace_bytes(int64_t ncalls, size_t* bytes) {
+  if (!bytes || ncalls < 1 || ncalls > wqd::kChainMaxCalls) return WQD_E_ARG;
+  *bytes = wqd::chain_workspace_bytes(ncalls);
+  return WQD_OK;
+}
+
+int wqd_chain_prepare(int fmt, int64_t M, int64_t ncalls, const wqd_chain_call* calls, int workgroups,
+                      void* workspace, size_t workspace_bytes, wqd_chain_plan* plan) {
+  if (!calls || !plan || ncalls < 1 || ncalls > wqd::kChainMaxCalls || M < 1 || workgroups < 0) return WQD_E_ARG;
+  if (fmt != wqd::kFmtBF16 && fmt != wqd::kFmtFP8 && fmt != wqd::kFmtW4) return WQD_E_ARG;
+  if (M > wqd::kChainMaxM) return WQD_E_UNSUPPORTED;
+  const size_t need = wqd::chain_workspace_bytes(ncalls);
+  if (!workspace || workspace_bytes < need) return WQD_E_WORKSPACE;
+  if (!wqd::aligned16(workspace)) return WQD_E_ALIGN;
+  const size_t table_bytes = wqd::chain_table_offset() + size_t(ncalls) * sizeof(wqd::ChainCall);
+  std::vector<char> host(table_bytes, 0);
+  auto* tab = reinterpret_cast<wqd::ChainCall*>(host.data() + wqd::chain_table_offset());
+  int64_t items = 0;
+  for (int64_t i = 0; i < ncalls; ++i) {
+    const wqd_chain_call& c = calls[i];
+    int st = wqd::plan_chain_call(fmt, M, c.N, c.K, c.swiglu != 0, &tab[i]);
+    if (st != wqd::kOK) return st;
+    if (!c.x || !c.y) return WQD_E_ARG;
+    if (!wqd::aligned16(c.x) || !wqd::aligned16(c.y)) return WQD_E_ALIGN;
+    st = check_packed_ptrs(fmt, c.w_packed, c.scales, c.zeros);
+    if (st != WQD_OK) return st;
+    if (c.swiglu != 0 && c.swiglu != 1) return WQD_E_ARG;
+    if (c.wait_for < -1 || c.wait_for >= i) return WQD_E_ARG;
+    tab[i].w = c.w_packed;
+    tab[i].scales = c.scales;
+    tab[i].zeros = c.zeros;
+    tab[i].x = c.x;
+    tab[i].y = c.y;
+    tab[i].wait_for = c.wait_for;
+    tab[i].item0 = int32_t(items);
+    items += tab[i].ni;
+    if (items >= (int64_t(1) << 31)) return WQD_E_UNSUPPORTED;
+  }
+  int resident = 0, cus = 0;
+  int st = hip_status(wqd::chain_resident_workgroups(fmt, int(M), &resident));
+  if (st != WQD_OK) return st;
+  st = hip_status(wqd::chain_compute_units(&cus));
+  if (st != WQD_OK) return st;
+  const int grid = workgroups > 0 ? workgroups : (cus < resident ? cus : resident);
+  if (grid < 1 || grid > resident) return WQD_E_UNSUPPORTED;
+  auto* hdr = reinterpret_cast<wqd::ChainHeader*>(host.data());
+  hdr->magic = wqd::kChainMagic;
+  hdr->fmt = fmt;
+  hdr->M = int32_t(M);
+  hdr->ncalls = int32_t(ncalls);
+  hdr->total_items = int32_t(items);
+  hdr->grid = grid;
+  st = hip_status(hipMemcpy(workspace, host.data(), table_bytes, hipMemcpyHostToDevice));
+  if (st != WQD_OK) return st;
+  plan->fmt = fmt;
+  plan->M = int32_t(M);
+  plan->ncalls = int32_t(ncalls);
+  plan->total_items = int32_t(items);
+  plan->workgroups = grid;
+  plan->reserved = 0;
+  plan->wait_ticks = 10000000;  // 0.1 s of the 100 MHz clock
+  return WQD_OK;
+}
+
+int wqd_chain_run(const wqd_chain_plan* plan, void* workspace, void* stream) {
+  if (!plan || !workspace) return WQD_E_ARG;
+  if (plan->M < 1 || plan->M > wqd::kChainMaxM || plan->ncalls < 1 || plan->ncalls > wqd::kChainMaxCalls ||
+      plan->workgroups < 1 || plan->total_items < 1 || plan->wait_ticks < 0)
+    return WQD_E_ARG;
+  if (plan->fmt != wqd::kFmtBF16 && plan->fmt != wqd::kFmtFP8 && plan->fmt != wqd::kFmtW4) return WQD_E_ARG;
+  if (!wqd::aligned16(workspace)) return WQD_E_ALIGN;
+  return hip_status(wqd::launch_chain(plan->fmt, plan->M, plan->ncalls, plan->total_items, plan->workgroups,
+                                      plan->wait_ticks, workspace, as_stream(stream)));
+}
+
+int wqd_chain_status(const void* workspace, void* stream) {
+  if (!workspace) return WQD_E_ARG;
+  int st = hip_status(hipStreamSynchronize(as_stream(stream)));
+  if (st != WQD_OK) return st;
+  int flag = 0;
+  st = hip_status(hipMemcpy(&flag, static_cast<const char*>(workspace) + 128, sizeof(int), hipMemcpyDeviceToHost));
+  if (st != WQD_OK) return st;
+  return flag == 0 ? WQD_OK : flag == 1 ? WQD_E_TIMEOUT : WQD_E_ARG;
 }
 
 int wqd_attn_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, int* splits) {

@@ -50,6 +50,12 @@ hipError_t launch_kv_copy(bool pack, const void* src_k, const void* src_v, void*
                           int64_t L, int64_t Lmax, hipStream_t st);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* positions, int64_t B, int64_t Hkv,
                             int64_t Lmax, void* k, void* v, hipStream_t st);
+// A chain of decode layers in one persistent launch (clear, then the chain);
+// the workspace holds the table written by wqd_chain_prepare.
+hipError_t launch_chain(int fmt, int M, int ncalls, int total_items, int grid, long long ticks, void* ws,
+                        hipStream_t st);
+hipError_t chain_resident_workgroups(int fmt, int M, int* out);
+hipError_t chain_compute_units(int* out);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 size_t stream_sink_words(size_t bytes);

@@ -464,4 +464,30 @@ int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnP
   return kOK;
 }
 
+int plan_chain_call(int fmt, int64_t M, int64_t N, int64_t K, bool swiglu, ChainCall* out) {
+  PackedSizes ps;
+  int st = packed_sizes(fmt, N, K, &ps);
+  if (st != kOK) return st;
+  if (M < 1) return kEArg;
+  if (M > kChainMaxM) return kEUnsupported;
+  if (swiglu && N % 16 != 0) return kEShape;
+  if (ps.NB >= (int64_t(1) << 31) || ceil_div(ps.KT, kChainWaves) > (int64_t(1) << 20)) return kEUnsupported;
+  ChainCall c{};
+  c.N = N;
+  c.K = K;
+  c.KT = ps.KT;
+  c.G4 = fmt == kFmtW4 ? ps.G4 : 0;
+  c.per_wave = int(ceil_div(ps.KT, 8 * int64_t(kChainWaves)) * 8);
+  c.nb = int(ps.NB);
+  c.ni = int(ceil_div(ps.NB, kChainRB));
+  c.swiglu = swiglu ? 1 : 0;
+  c.wait_for = -1;
+  *out = c;
+  return kOK;
+}
+
+size_t chain_workspace_bytes(int64_t ncalls) {
+  return chain_counters_offset(ncalls) + size_t(ncalls) * kChainCounters * kChainCounterStride * sizeof(int);
+}
+
 }  // namespace wqd

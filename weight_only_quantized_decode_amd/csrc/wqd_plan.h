@@ -192,8 +192,9 @@ struct W8Plan {
 int plan_w8a8(int64_t M, int64_t N, int64_t K, W8Plan* out);
 
 // Decode attention split along the context: S splits of `chunk` positions (a
-// multiple of 32) per (sequence, KV head), one wavefront each; the partial
-// maxima, sums and outputs take B * Hq * S * (2 + 128) floats of workspace.
+// multiple of 32) per (sequence, KV head), one workgroup of 4 wavefronts
+// each; with S > 1 the partial maxima, sums and outputs take
+// B * Hq * S * (2 + 128) floats of workspace.
 struct AttnPlan {
   int64_t Lmax;
   int Hq, Hkv, S, chunk;
@@ -207,6 +208,55 @@ int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnP
 // every workgroup of the quantising kernel reduces the G values itself.
 constexpr int kActQuantParts = 1024;
 int plan_act_quant(int64_t M, int64_t K, int* parts);
+
+// A chain of decode linear layers in one persistent launch (wqd_chain.hip).
+// Items are (call, kChainRB 16-row blocks) pairs, numbered call by call and
+// dealt to the workgroups round robin; each workgroup has kChainWaves wavefronts on
+// contiguous shares of K (a multiple of 8 tiles, so the two-group register
+// ring lines up from one item to the next).  A call whose input is an earlier
+// call's output waits for that call's completion counters: kChainCounters
+// per call, each in its own 128-byte line, one atomic add per item.
+constexpr int kChainWaves = 4;
+constexpr int kChainRB = 2;  // 16-row blocks per item, sharing each x register
+constexpr int kChainMaxM = 2;
+constexpr int kChainCounters = 64;
+constexpr int kChainCounterStride = 32;  // ints: 128 bytes
+constexpr int kChainMaxCalls = 1 << 16;
+constexpr uint32_t kChainMagic = 0x43484e31u;
+constexpr size_t kChainHeaderBytes = 256;  // header, then the error flag at byte 128
+
+struct ChainCall {      // one entry of the device table (128 bytes)
+  const void* w;        // packed weights, scales, zero points
+  const void* scales;
+  const void* zeros;
+  const void* x;        // bf16 [M][K]
+  void* y;              // bf16 [M][N] ([M][N / 2] with swiglu)
+  int64_t N, K, KT, G4;
+  int32_t per_wave;     // tiles per wavefront share
+  int32_t nb;           // 16-row blocks
+  int32_t ni;           // items: kChainRB row blocks each (the last may hold fewer)
+  int32_t item0;        // number of the call's first item
+  int32_t wait_for;     // earlier call whose output x is, or -1
+  int32_t swiglu;
+  int32_t pad[8];
+};
+static_assert(sizeof(ChainCall) == 128, "chain table entries are 128 bytes");
+
+struct ChainHeader {
+  uint32_t magic;
+  int32_t fmt, M, ncalls, total_items, grid;
+  int32_t pad[10];
+};
+static_assert(sizeof(ChainHeader) == 64, "chain header is 64 bytes");
+
+// Fills the shape fields of one call (KT, G4, per_wave, nb) or returns a status.
+int plan_chain_call(int fmt, int64_t M, int64_t N, int64_t K, bool swiglu, ChainCall* out);
+// Workspace: header and flag, the table, then kChainCounters lines per call.
+size_t chain_workspace_bytes(int64_t ncalls);
+inline size_t chain_table_offset() { return kChainHeaderBytes; }
+inline size_t chain_counters_offset(int64_t ncalls) {
+  return (kChainHeaderBytes + size_t(ncalls) * sizeof(ChainCall) + 255) / 256 * 256;
+}
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
