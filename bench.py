@@ -428,11 +428,18 @@ def hbm_ceiling(gib=4, reps=10):
     return read, copy
 
 
+# The sources the broadcast kernel (the headline's dominant kernel) and its
+# kernel choice are built from: counters taken before a change to any of them
+# no longer describe the kernel.
+TRAFFIC_SOURCES = ("wqd_gemv_bcast.hip", "wqd_bcast_tile.h", "wqd_device.h", "wqd_internal.h", "wqd_plan.h",
+                   "wqd_plan.cpp")
+
+
 def profiled_traffic(wl):
     """HBM bytes per launch from the committed counter summary of this workload
     (profiles/traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE runs scaled by
-    a copy kernel of known size), or None when there is none or the kernel
-    sources changed since the counters were taken."""
+    a copy kernel of known size), or None when there is none or the kernel's
+    sources (TRAFFIC_SOURCES) changed since the counters were taken."""
     import hashlib
 
     root = os.path.dirname(os.path.abspath(__file__))
@@ -443,7 +450,7 @@ def profiled_traffic(wl):
         d = json.load(f)
     csrc = os.path.join(root, "weight_only_quantized_decode_amd", "csrc")
     recorded = d.get("kernel_sources_sha256_16", {})
-    if sorted(recorded) != sorted(os.listdir(csrc)):  # every source file, no more, no fewer
+    if sorted(recorded) != sorted(TRAFFIC_SOURCES):  # the dominant kernel's sources, no more, no fewer
         return None
     for fn, digest in recorded.items():
         with open(os.path.join(csrc, fn), "rb") as f:
