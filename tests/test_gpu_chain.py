@@ -12,9 +12,9 @@ previous call and on an earlier one, an independent call in the middle, a
 SwiGLU gate/up pair, ragged N and, for FP8 / BF16, ragged K), with the
 library's grid and with 1 and 5 workgroups (each workgroup then runs many
 items back to back); determinism and graph replays; two full 70B layers in
-the fused layout at decode width 1 (sampled rows); a plan that does not match
-the prepared table, and a wait bound of zero (runs that stop early report it
-and leave the next run correct)."""
+the fused layout (W4A16 at one row, FP8 at two; sampled rows); a plan that
+does not match the prepared table, and a wait bound of zero (runs that stop
+early report it and leave the next run correct)."""
 import numpy as np
 import pytest
 import torch
@@ -135,11 +135,12 @@ def test_deterministic_and_graph_replays():
         assert all(np.array_equal(a, b) for a, b in zip(first, case.outputs())), f"replay {r}"
 
 
-def test_70b_two_layers_fused_m1():
-    """qkv (10240 x 8192) -> o (x = the first 8192 outputs of qkv, standing in
-    for attention) -> gate/up SwiGLU (57344 x 8192 packed pairs) -> down
-    (8192 x 28672) -> the next layer's qkv on down's output; W4A16, one row."""
-    fmt, M, K = "w4a16", 1, 8192
+@pytest.mark.parametrize("fmt,M", [("w4a16", 1), ("fp8", 2)])
+def test_70b_two_layers_fused(fmt, M):
+    """qkv (10240 x 8192) -> o (x = the first M x 8192 outputs of qkv, standing
+    in for attention) -> gate/up SwiGLU (57344 x 8192 packed pairs) -> down
+    (8192 x 28672) -> the next layer's qkv on down's output."""
+    K = 8192
     shapes = [("qkv", 10240, 8192), ("o", 8192, 8192), ("gate_up", 57344, 8192), ("down", 8192, 28672)]
     rng = np.random.default_rng(9)
     steps, samples = [], []
@@ -160,13 +161,13 @@ def test_70b_two_layers_fused_m1():
             else:
                 q = oracle.quantize(fmt, W[torch.from_numpy(pick).to(DEV)].cpu().numpy())
             del W
-            x = prev if name != "o" else prev[:, :8192]
+            x = prev if name != "o" else prev.reshape(-1)[: M * 8192].view(M, 8192)
             y = torch.empty((M, cols_out), dtype=torch.bfloat16, device=DEV)
             steps.append(wqd.ChainStep(x, pw, y, i - 1, sw))
             samples.append((pick, q))
             prev = y
     steps[0].wait_for = -1
-    print("chain 70B W4A16 M=1, 2 layers (8 calls)", flush=True)
+    print(f"chain 70B {fmt} M={M}, 2 layers (8 calls)", flush=True)
     chain = wqd.chain_prepare(steps)
     for st in steps:
         st.y.view(torch.int16).fill_(NAN_BF16)
@@ -174,7 +175,7 @@ def test_70b_two_layers_fused_m1():
     assert wqd.chain_status(chain) == 0
     ys = [bf16_bits(st.y) for st in steps]
     for i, st in enumerate(steps):
-        xb = x0 if i == 0 else (ys[i - 1][:, :8192] if i % 4 == 1 else ys[i - 1])
+        xb = x0 if i == 0 else (ys[i - 1].reshape(-1)[: M * 8192].reshape(M, 8192) if i % 4 == 1 else ys[i - 1])
         pick, q = samples[i]
         ref = oracle.swiglu_exact(xb, *q) if st.swiglu else oracle.qgemm_exact(xb, q)
         s = compare_y(ys[i][:, pick], ref, f"70B chain call {i}")
