@@ -356,7 +356,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const ChainHead
   int j = blockIdx.x;
   if (j >= total_items) return;
   int c = 0;
-  while (j >= calls[c].item0 + calls[c].ni) ++c;
+  while (c + 1 < ncalls && j >= calls[c].item0 + calls[c].ni) ++c;
   CItem cur = make_item<FMT>(calls, c, j - calls[c].item0, wave, n, true);
   CGroup<FMT, MR> g0, g1;
   load_group<FMT, MR>(g0, cur, 0, lane, kb, n);
@@ -368,8 +368,10 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const ChainHead
   int done = 0;  // items of the current call this workgroup has finished
   uint4 xs0[MR][4];  // W4A16: x sums of the first 16 tiles of the current item
   while (true) {
+    // wait_for names an earlier call (the table was checked when it was
+    // written; the bound keeps a damaged table from indexing past it)
     const int d = calls[cur.call].wait_for;
-    if (d >= 0 && d != waited) {
+    if (d >= 0 && d < cur.call && d != waited) {
       if (!chain_wait(calls, d, counters, flag, &s_flag, wave, lane, ticks)) return;
       waited = d;
       x_ready = false;
