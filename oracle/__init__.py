@@ -20,7 +20,8 @@ It computes, plainly and slowly, what the decode linear layer computes:
   activation tensor, activation codes, and the product of the two code
   matrices (exact in float64) times both scales;
 * ``attention``: decode attention over a KV cache with grouped-query heads
-  (one query per sequence, softmax over its first len positions);
+  (one query per sequence, softmax over its first len positions), from a bf16
+  cache or from an FP8-E4M3 one (one scale per tensor for K and for V);
 * ``bytes``:   the bytes a call or a step moves (codes, scales, zero points,
   activations; KV cache per sequence) and the step's lower bound, as the
   pages define them.
@@ -42,7 +43,10 @@ activation codes against a brute-force nearest E4M3 value, activations on the
 E4M3 grid reducing to the weight-only product, and the activation rounding
 bound; decode attention against closed forms (one position, equal keys, a
 dominant key, a 3:1 split), invariances, per-group values and torch's float64
-scaled-dot-product attention.  No function here is
+scaled-dot-product attention; the FP8 cache's codes against a brute-force
+nearest E4M3 value and its saturation, and attention over an FP8 cache with
+power-of-two scales (every value exact in bf16) against the bf16 attention on
+the same values.  No function here is
 "parity unpinned".
 """
 from .formats import (  # noqa: F401
@@ -69,6 +73,12 @@ from .quant import (  # noqa: F401
     quantize_w4a16,
     w4a16_group_params,
 )
-from .attention import decode_attention_exact, decode_attention_ref  # noqa: F401
+from .attention import (  # noqa: F401
+    decode_attention_exact,
+    decode_attention_fp8kv_exact,
+    decode_attention_fp8kv_ref,
+    decode_attention_ref,
+    quantize_kv_fp8,
+)
 from .w8a8 import act_scale, qgemm_w8a8_exact, qgemm_w8a8_ref, quantize_act  # noqa: F401
 from .spec import accept, draw_units, inverse_cdf_draw, residual, spec_accept, spec_accept_one  # noqa: F401

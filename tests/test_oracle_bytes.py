@@ -17,6 +17,8 @@ them independently and is pinned here to the pages' own closed forms
 * same page, "Building a per-token cost calculator", the expected values:
   batch-1 23.333 / 12.104 ms, batch-32 30.492 / 19.262 ms, INT4 verify cost
   ratio 1.1629 for 5 positions per sequence.
+* same page, the hands-on lab, exercise 5 and its reference values: with a
+  1-byte FP8 KV cache (scales ignored) the INT4 batch-32 bound is 15.683 ms.
 * CS336 lecture 10 notes, section 10, exercise 4: a 4096 x 4096 INT4 matrix
   with groups of 128 and an FP16 scale takes 4.125 bits per weight, about
   8.65 MB, against 33.6 MB in BF16.
@@ -124,6 +126,12 @@ def check_bounds(g):
         close(1e3 * B.memory_time_s(wbytes, 1, 0, HBM_PAGE), f"bound_{fmt_key}_batch1_ms", g)
         close(1e3 * B.step_bound_s(wbytes, 32, 1, kv, PARAMS_70B, HBM_PAGE, PEAK_PAGE),
               f"bound_{fmt_key}_batch32_ms", g)
+    # a 1-byte (FP8) KV cache, scales ignored as the lab's exercise says: the
+    # INT4 batch-32 bound drops from 19.262 to 15.683 ms
+    kv8 = B.kv_bytes_per_sequence(layers=80, kv_heads=8, head_dim=128, bytes_per_elem=1, context=2048)
+    assert 2 * kv8 == kv
+    w4 = B.params_weight_bytes(PARAMS_70B, 4.15)
+    close(1e3 * B.step_bound_s(w4, 32, 1, kv8, PARAMS_70B, HBM_PAGE, PEAK_PAGE), "bound_int4_batch32_fp8kv_ms", g)
     # verifying 4 drafts + 1 position per sequence turns INT4's batch-32 step
     # compute bound; BF16 and FP8 stay memory bound (ratio exactly 1)
     for bits, key in ((16.0, None), (8.0, None), (4.15, "int4_verify_cost_ratio")):
