@@ -22,7 +22,8 @@ The same run also reports, each from its own graph replays:
     (wqd_chain_run: every matrix of the step, each waiting for the output it
     reads);
   * "next_rows": W8A8-FP8 on the gate matrix at 1024 rows, and the stack's
-    decode attention at batch 32 over 2,048 positions;
+    decode attention at batch 32 over 2,048 positions, over a bf16 and an FP8
+    cache;
   * "roofline": the dominant kernel (the launches of the step's costliest
     kernel family, replayed on their own) against the 8 TB/s HBM peak;
   * "cpu_baseline": the oracle on one full layer of the same workload on the
@@ -30,7 +31,7 @@ The same run also reports, each from its own graph replays:
 
 Prints ONE JSON line.  Options: --workload w4a16_70b | fp8_70b | bf16_7b |
 w4a16_70b_swiglu | fp8_70b_swiglu | gemv4096 | verify:<fmt>:<mat> |
-w8a8:<mat> | attn_70b; --m (activation rows); --separate (time the separate
+w8a8:<mat> | attn_70b | attn_fp8kv_70b; --m (activation rows); --separate (time the separate
 layout as the headline); --no-alt; --no-targets; --chain (time only the
 chain launch; --chain-workgroups sets its grid); --pmc-probe (a short fixed
 launch sequence for hardware-counter runs).  A single-matrix workload
@@ -594,12 +595,14 @@ def spec_accept_timing(B=64, k=4, V=128256, reps=50):
 ATTN_HQ, ATTN_HKV, ATTN_D = 64, 8, 128  # the 70B layer's grouped-query attention
 
 
-def attn_stack_timing(args, stream, B=32, ctx=2048, layers=80):
+def attn_stack_timing(args, stream, B=32, ctx=2048, layers=80, kv="bf16"):
     """Decode attention of every layer of the 70B-class stack for B sequences
     of ctx positions (the pages' batch-32 snapshot: 80 layers x 8 KV heads x
     128 x 2 bytes x 2 for keys and values = 671,088,640 bytes per sequence).
-    Each layer has its own caches, so a step reads 21.5 GB of KV from HBM.
-    One step = 80 wqd_decode_attention calls (split kernel and merge each),
+    Each layer has its own caches, so a step reads 21.5 GB of KV from HBM
+    (half that from an FP8 cache, kv="fp8": one byte per element, the
+    one-byte-KV case of the hands-on lab's exercise 5).  One step = 80
+    wqd_decode_attention(_fp8kv) calls (split kernel and merge each),
     replayed from a HIP graph."""
     import math
 
@@ -610,35 +613,54 @@ def attn_stack_timing(args, stream, B=32, ctx=2048, layers=80):
     dev = torch.device("cuda", 0)
     g = torch.Generator(device=dev)
     g.manual_seed(2048 + B)
-    log(f"[bench] decode attention: {layers} layers, B={B}, {ctx} positions, {ATTN_HQ}/{ATTN_HKV} heads")
+    fp8 = kv == "fp8"
+    log(f"[bench] decode attention ({kv} cache): {layers} layers, B={B}, {ctx} positions, {ATTN_HQ}/{ATTN_HKV} heads")
     caches = []
+    if fp8:
+        k_scale = v_scale = 4.0 / 448  # N(0, 1) entries, saturating past 4 sigma
+        tmp_k = torch.empty((B, ATTN_HKV, ctx, ATTN_D), dtype=torch.bfloat16, device=dev)
+        tmp_v = torch.empty_like(tmp_k)
     for _ in range(layers):
-        c = wqd.alloc_kv_cache(B, ATTN_HKV, ctx, ATTN_D, device=dev)
-        c.k.normal_(generator=g)  # random entries: the tile order of the layout does not matter
-        c.v.normal_(generator=g)
+        if fp8:
+            c = wqd.alloc_kv_cache_fp8(B, ATTN_HKV, ctx, k_scale, v_scale, ATTN_D, device=dev)
+            tmp_k.normal_(generator=g)
+            tmp_v.normal_(generator=g)
+            wqd.kv_pack_fp8(tmp_k, tmp_v, c)
+        else:
+            c = wqd.alloc_kv_cache(B, ATTN_HKV, ctx, ATTN_D, device=dev)
+            c.k.normal_(generator=g)  # random entries: the tile order of the layout does not matter
+            c.v.normal_(generator=g)
         caches.append(c)
+    if fp8:
+        del tmp_k, tmp_v
     q = torch.randn((B, ATTN_HQ, ATTN_D), generator=g, device=dev, dtype=torch.bfloat16)
     out = torch.empty_like(q)
     lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
-    ws = wqd.get_workspace(wqd.attn_workspace_bytes(B, ATTN_HQ, ATTN_HKV, ctx), dev)  # None when 0 bytes
+    wsb = (wqd.attn_fp8kv_workspace_bytes if fp8 else wqd.attn_workspace_bytes)(B, ATTN_HQ, ATTN_HKV, ctx)
+    ws = wqd.get_workspace(wsb, dev)  # None when 0 bytes
     scale = 1.0 / math.sqrt(ATTN_D)
 
     def go():
         for c in caches:
-            wqd.decode_attention(q, c, lens, scale, out=out, workspace=ws)
+            if fp8:
+                wqd.decode_attention_fp8kv(q, c, lens, scale, out=out, workspace=ws)
+            else:
+                wqd.decode_attention(q, c, lens, scale, out=out, workspace=ws)
 
     ms, samples = replay_timing(go, stream, args.steps, args.warmup, not args.no_graph)
-    kv = B * ATTN_HKV * ctx * ATTN_D * 2 * 2
-    per_layer = kv + 2 * (B * ATTN_HQ * ATTN_D * 2) + 4 * B
+    kv_bytes = B * ATTN_HKV * ctx * ATTN_D * (1 if fp8 else 2) * 2
+    per_layer = kv_bytes + 2 * (B * ATTN_HQ * ATTN_D * 2) + 4 * B
     gbps = layers * per_layer / (ms / 1e3) / 1e9
-    res = {"workload": f"70b_decode_attention_{layers}l_b{B}_ctx{ctx}", "B": B, "context": ctx, "layers": layers,
+    name = "70b_decode_attention_fp8kv" if fp8 else "70b_decode_attention"
+    res = {"workload": f"{name}_{layers}l_b{B}_ctx{ctx}", "B": B, "context": ctx, "layers": layers, "kv": kv,
            "q_heads": ATTN_HQ, "kv_heads": ATTN_HKV, "head_dim": ATTN_D, "ms_per_step": round(ms, 4),
-           "us_per_layer": round(ms * 1e3 / layers, 2), "kv_bytes_per_step": layers * kv,
+           "us_per_layer": round(ms * 1e3 / layers, 2), "kv_bytes_per_step": layers * kv_bytes,
            "algorithmic_bytes_per_step": layers * per_layer, "GBps": round(gbps, 2),
            "step_samples_ms": {"n": len(samples), "median": round(statistics.median(samples), 4),
                                "min": round(min(samples), 4), "max": round(max(samples), 4)},
-           "splits": wqd.attn_splits(B, ATTN_HQ, ATTN_HKV, ctx),
-           "kernel": "attn_split_kernel (+ attn_combine_kernel when the context is split) per layer"}
+           "splits": (wqd.attn_fp8kv_splits if fp8 else wqd.attn_splits)(B, ATTN_HQ, ATTN_HKV, ctx),
+           "kernel": f"attn_split_kernel<{'true' if fp8 else 'false'}> (+ attn_combine_kernel when the context is "
+                     "split) per layer"}
     del caches
     free_cache()
     return res
@@ -675,9 +697,11 @@ def roofline_of(wl, res):
 
 
 def attn_main(args, stream, ceiling):
-    """--workload attn_70b: the stack's decode attention as the headline."""
+    """--workload attn_70b / attn_fp8kv_70b: the stack's decode attention over
+    a bf16 / FP8 cache as the headline."""
     B = args.m if args.m > 1 else 32
-    a = attn_stack_timing(args, stream, B=B, layers=args.layers or 80)
+    a = attn_stack_timing(args, stream, B=B, layers=args.layers or 80,
+                          kv="fp8" if args.workload == "attn_fp8kv_70b" else "bf16")
     per_layer_bytes = a["algorithmic_bytes_per_step"] / a["layers"]
     achieved = per_layer_bytes / (a["us_per_layer"] * 1e-6) / 1e9
     out = {
@@ -721,7 +745,7 @@ def main():
     if ceiling[0]:
         log(f"[bench] HBM ceiling: read {ceiling[0]:.0f} GB/s, copy {ceiling[1]:.0f} GB/s")
     stream = torch.cuda.Stream()
-    if args.workload == "attn_70b":
+    if args.workload in ("attn_70b", "attn_fp8kv_70b"):
         attn_main(args, stream, ceiling)
         return
     wl = make_workload(args.workload, args.m, args.layers, fused)
@@ -781,10 +805,11 @@ def main():
         next_rows["w8a8_gate_m1024"] = {"ms_per_call": r["ms_per_step"], "product_us": rr["avg_launch_us"],
                                         "product_TFLOPs": rr["achieved"], "frac_fp8_peak": rr["frac"],
                                         "workload": w8.name, "weight_copies": copies_for(w8)}
-        a = attn_stack_timing(args, stream)
-        a["pct_measured_read_ceiling"] = pct(a["GBps"], ceiling[0])
-        a["frac_hbm_peak"] = round(a["GBps"] / HBM_PEAK_GBPS, 4)
-        next_rows["decode_attention"] = a
+        for kv, key in (("bf16", "decode_attention"), ("fp8", "decode_attention_fp8kv")):
+            a = attn_stack_timing(args, stream, kv=kv)
+            a["pct_measured_read_ceiling"] = pct(a["GBps"], ceiling[0])
+            a["frac_hbm_peak"] = round(a["GBps"] / HBM_PEAK_GBPS, 4)
+            next_rows[key] = a
 
     ms = head["ms_per_step"]
     gbps = head["GBps"]

@@ -294,6 +294,55 @@ int wqd_kv_unpack(const void* k_cache, const void* v_cache, int64_t B, int64_t H
                   void* k_out, void* v_out, void* stream);
 
 /*
+ * Decode attention over an FP8-E4M3 KV cache.  Sources: "LLM 推理是怎么变快的",
+ * section 4, C (keys and values stored in FP8 halve the cache's bytes);
+ * "Making each token cheaper", hands-on lab, exercise 5 (the step bound with
+ * a one-byte KV cache).  The pages do not fix the scales; here one float32
+ * scale per tensor for K and one for V, chosen by the caller:
+ *   code = nearest E4M3FN value of x / scale (float32 division, ties to
+ *          even, magnitudes past 448 saturate), value = e4m3(code) * scale,
+ * then the attention of wqd_decode_attention on those values:
+ *   o[b, h] = sum_{t < len[b]} softmax_t(scale * q[b, h] . K[b, g, t]) V[b, g, t]
+ * (products and sums in float32, the dequantised keys and values exact).
+ *   q, lengths, out, workspace   as wqd_decode_attention, with the sizes of
+ *              wqd_attn_fp8kv_workspace_bytes / wqd_attn_fp8kv_splits
+ *   k_cache,   device, B * Hkv * Lmax * D bytes each of E4M3 codes in the
+ *   v_cache    library's tiled layout, written by wqd_kv_pack_fp8 /
+ *              wqd_kv_append_fp8 (per (b, g), 1 KiB tiles; the byte offsets
+ *              of position t, dimension d within a (b, g) region of
+ *              Lmax * D bytes are:
+ *                K: ((t / 16) * 2 + d / 64) * 1024 + (((d % 32) / 8) * 16 + t % 16) * 16
+ *                   + 8 * ((d % 64) / 32) + d % 8;
+ *                V: ((t / 32) * 4 + d / 32) * 1024 + (kb * 16 + d % 16) * 16
+ *                   + 8 * ((d % 32) / 16) + e,
+ *                   u = t % 32, kb = (u % 16) / 4, e = 4 * (u / 16) + u % 4)
+ *              entries at or past a length are never used, whatever they hold
+ *   k_scale,   the caches' scales: finite and > 0 (else WQD_E_ARG)
+ *   v_scale
+ * Shapes and errors as wqd_decode_attention.  Deterministic.
+ *
+ * wqd_kv_pack_fp8: logical k, v device bf16 [B][Hkv][L][D] (L <= Lmax),
+ *   quantised with k_scale / v_scale, into positions 0 .. L - 1 (later
+ *   positions untouched).  NaN inputs are not meaningful (the code saturates).
+ * wqd_kv_append_fp8: one new position per sequence, quantised: k_new / v_new
+ *   device bf16 [B][Hkv][D] at positions[b] (device int32 [B]; a position
+ *   outside [0, Lmax) writes nothing).
+ * wqd_kv_unpack_fp8: the caches' codes back to logical device uint8
+ *   [B][Hkv][Lmax][D] (parity of the quantisation and the layout).
+ */
+int wqd_attn_fp8kv_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, size_t* bytes);
+int wqd_attn_fp8kv_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, int* splits);
+int wqd_decode_attention_fp8kv(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+                               const int32_t* lengths, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D,
+                               float scale, void* out, void* workspace, size_t workspace_bytes, void* stream);
+int wqd_kv_pack_fp8(const void* k, const void* v, float k_scale, float v_scale, int64_t B, int64_t Hkv, int64_t L,
+                    int64_t Lmax, int64_t D, void* k_cache, void* v_cache, void* stream);
+int wqd_kv_append_fp8(const void* k_new, const void* v_new, float k_scale, float v_scale, const int32_t* positions,
+                      int64_t B, int64_t Hkv, int64_t Lmax, int64_t D, void* k_cache, void* v_cache, void* stream);
+int wqd_kv_unpack_fp8(const void* k_cache, const void* v_cache, int64_t B, int64_t Hkv, int64_t Lmax, int64_t D,
+                      void* k_codes, void* v_codes, void* stream);
+
+/*
  * A chain of decode linear layers in one persistent launch.  Sources: CS336
  * lecture 10 notes, section 3.2 (a layer's matrices run in sequence, each on
  * the previous one's output: the attention projections, then the MLP's

@@ -64,6 +64,7 @@ def lib() -> ctypes.CDLL:
             )
         L = ctypes.CDLL(LIB_PATH)
         i64, sz, vp, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+        f32 = ctypes.c_float
         psz = ctypes.POINTER(ctypes.c_size_t)
         sig = {
             "wqd_version": (i32, []),
@@ -85,6 +86,13 @@ def lib() -> ctypes.CDLL:
             "wqd_kv_pack": (i32, [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp]),
             "wqd_kv_append": (i32, [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp]),
             "wqd_kv_unpack": (i32, [vp, vp, i64, i64, i64, i64, vp, vp, vp]),
+            "wqd_attn_fp8kv_workspace_bytes": (i32, [i64, i64, i64, i64, i64, psz]),
+            "wqd_attn_fp8kv_splits": (i32, [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int)]),
+            "wqd_decode_attention_fp8kv": (i32, [vp, vp, vp, f32, f32, vp, i64, i64, i64, i64, i64, f32, vp, vp,
+                                                 sz, vp]),
+            "wqd_kv_pack_fp8": (i32, [vp, vp, f32, f32, i64, i64, i64, i64, i64, vp, vp, vp]),
+            "wqd_kv_append_fp8": (i32, [vp, vp, f32, f32, vp, i64, i64, i64, i64, vp, vp, vp]),
+            "wqd_kv_unpack_fp8": (i32, [vp, vp, i64, i64, i64, i64, vp, vp, vp]),
             "wqd_w8a8_workspace_bytes": (i32, [i64, i64, i64, psz]),
             "wqd_qgemm_w8a8": (i32, [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]),
             "wqd_chain_workspace_bytes": (i32, [i64, psz]),
@@ -510,6 +518,95 @@ def decode_attention(q, cache: KVCache, lengths, scale: float, out=None, workspa
     _check(lib().wqd_decode_attention(q.data_ptr(), cache.k.data_ptr(), cache.v.data_ptr(), lengths.data_ptr(), B,
                                       Hq, cache.Hkv, cache.Lmax, D, float(scale), out.data_ptr(),
                                       _ptr(workspace), wsb, _stream(stream)), "wqd_decode_attention")
+    return out
+
+
+def attn_fp8kv_workspace_bytes(B: int, Hq: int, Hkv: int, Lmax: int, D: int = 128) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().wqd_attn_fp8kv_workspace_bytes(B, Hq, Hkv, Lmax, D, ctypes.byref(b)),
+           "wqd_attn_fp8kv_workspace_bytes")
+    return b.value
+
+
+def attn_fp8kv_splits(B: int, Hq: int, Hkv: int, Lmax: int, D: int = 128) -> int:
+    s = ctypes.c_int()
+    _check(lib().wqd_attn_fp8kv_splits(B, Hq, Hkv, Lmax, D, ctypes.byref(s)), "wqd_attn_fp8kv_splits")
+    return s.value
+
+
+@dataclass
+class KVCacheFP8:
+    """One layer's FP8-E4M3 KV cache in the library's tiled layout (device
+    uint8 codes) with its per-tensor scales."""
+    B: int
+    Hkv: int
+    Lmax: int
+    k: "object"
+    v: "object"
+    k_scale: float
+    v_scale: float
+    D: int = 128
+
+
+def alloc_kv_cache_fp8(B: int, Hkv: int, Lmax: int, k_scale: float, v_scale: float, D: int = 128,
+                       device="cuda") -> KVCacheFP8:
+    import torch
+
+    n = B * Hkv * Lmax * D
+    return KVCacheFP8(B, Hkv, Lmax, torch.zeros(n, dtype=torch.uint8, device=device),
+                      torch.zeros(n, dtype=torch.uint8, device=device), float(k_scale), float(v_scale), D)
+
+
+def kv_pack_fp8(k, v, cache: KVCacheFP8, stream=None) -> KVCacheFP8:
+    """wqd_kv_pack_fp8: logical k, v bf16 [B, Hkv, L, D], quantised with the
+    cache's scales, into positions 0 .. L - 1."""
+    B, Hkv, L, D = k.shape
+    if tuple(v.shape) != (B, Hkv, L, D) or not (k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("k and v must be contiguous [B, Hkv, L, D] tensors")
+    _check(lib().wqd_kv_pack_fp8(k.data_ptr(), v.data_ptr(), cache.k_scale, cache.v_scale, B, Hkv, L, cache.Lmax,
+                                 D, cache.k.data_ptr(), cache.v.data_ptr(), _stream(stream)), "wqd_kv_pack_fp8")
+    return cache
+
+
+def kv_append_fp8(k_new, v_new, positions, cache: KVCacheFP8, stream=None) -> KVCacheFP8:
+    """wqd_kv_append_fp8: k_new, v_new bf16 [B, Hkv, D] at positions int32 [B]."""
+    _check(lib().wqd_kv_append_fp8(k_new.data_ptr(), v_new.data_ptr(), cache.k_scale, cache.v_scale,
+                                   positions.data_ptr(), cache.B, cache.Hkv, cache.Lmax, cache.D,
+                                   cache.k.data_ptr(), cache.v.data_ptr(), _stream(stream)), "wqd_kv_append_fp8")
+    return cache
+
+
+def kv_unpack_fp8(cache: KVCacheFP8, stream=None):
+    """wqd_kv_unpack_fp8: (k_codes, v_codes) logical uint8 [B, Hkv, Lmax, D]."""
+    import torch
+
+    shape = (cache.B, cache.Hkv, cache.Lmax, cache.D)
+    k = torch.empty(shape, dtype=torch.uint8, device=cache.k.device)
+    v = torch.empty(shape, dtype=torch.uint8, device=cache.k.device)
+    _check(lib().wqd_kv_unpack_fp8(cache.k.data_ptr(), cache.v.data_ptr(), cache.B, cache.Hkv, cache.Lmax,
+                                   cache.D, k.data_ptr(), v.data_ptr(), _stream(stream)), "wqd_kv_unpack_fp8")
+    return k, v
+
+
+def decode_attention_fp8kv(q, cache: KVCacheFP8, lengths, scale: float, out=None, workspace=None, stream=None):
+    """wqd_decode_attention_fp8kv: q bf16 [B, Hq, D] against a KVCacheFP8,
+    lengths int32 [B] -> out bf16 [B, Hq, D]."""
+    import torch
+
+    B, Hq, D = q.shape
+    if (B, D) != (cache.B, cache.D) or q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bfloat16 [B, Hq, D] tensor matching the cache")
+    if tuple(lengths.shape) != (B,) or lengths.dtype != torch.int32:
+        raise ValueError("lengths must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        workspace = get_workspace(attn_fp8kv_workspace_bytes(B, Hq, cache.Hkv, cache.Lmax, D), q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().wqd_decode_attention_fp8kv(q.data_ptr(), cache.k.data_ptr(), cache.v.data_ptr(), cache.k_scale,
+                                            cache.v_scale, lengths.data_ptr(), B, Hq, cache.Hkv, cache.Lmax, D,
+                                            float(scale), out.data_ptr(), _ptr(workspace), wsb, _stream(stream)),
+           "wqd_decode_attention_fp8kv")
     return out
 
 

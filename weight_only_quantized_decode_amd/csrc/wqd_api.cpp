@@ -2,6 +2,7 @@
 // plan, then enqueue on the caller's stream.  No allocation, no host sync.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <vector>
 
 #include "../../include/wqd.h"
@@ -325,7 +326,46 @@ int wqd_decode_attention(const void* q, const void* k_cache, const void* v_cache
   if (!wqd::aligned16(q) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache) || !wqd::aligned16(out) ||
       (p.ws_bytes > 0 && !wqd::aligned16(workspace)) || reinterpret_cast<uintptr_t>(lengths) % 4)
     return WQD_E_ALIGN;
-  return hip_status(wqd::launch_attn(p, q, k_cache, v_cache, lengths, B, scale, out, workspace, as_stream(stream)));
+  return hip_status(wqd::launch_attn(p, q, k_cache, v_cache, lengths, B, scale, 1.0f, 1.0f, out, workspace,
+                                     as_stream(stream)));
+}
+
+namespace {
+bool kv_scale_ok(float s) { return std::isfinite(s) && s > 0.0f; }
+}  // namespace
+
+int wqd_attn_fp8kv_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, size_t* bytes) {
+  if (!bytes) return WQD_E_ARG;
+  wqd::AttnPlan p;
+  const int st = wqd::plan_attn(B, Hq, Hkv, Lmax, D, &p, true);
+  if (st != wqd::kOK) return st;
+  *bytes = p.ws_bytes;
+  return WQD_OK;
+}
+
+int wqd_attn_fp8kv_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, int* splits) {
+  if (!splits) return WQD_E_ARG;
+  wqd::AttnPlan p;
+  const int st = wqd::plan_attn(B, Hq, Hkv, Lmax, D, &p, true);
+  if (st != wqd::kOK) return st;
+  *splits = p.S;
+  return WQD_OK;
+}
+
+int wqd_decode_attention_fp8kv(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+                               const int32_t* lengths, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D,
+                               float scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  wqd::AttnPlan p;
+  const int st = wqd::plan_attn(B, Hq, Hkv, Lmax, D, &p, true);
+  if (st != wqd::kOK) return st;
+  if (!q || !k_cache || !v_cache || !lengths || !out || !kv_scale_ok(k_scale) || !kv_scale_ok(v_scale))
+    return WQD_E_ARG;
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return WQD_E_WORKSPACE;
+  if (!wqd::aligned16(q) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache) || !wqd::aligned16(out) ||
+      (p.ws_bytes > 0 && !wqd::aligned16(workspace)) || reinterpret_cast<uintptr_t>(lengths) % 4)
+    return WQD_E_ALIGN;
+  return hip_status(wqd::launch_attn(p, q, k_cache, v_cache, lengths, B, scale, k_scale, v_scale, out, workspace,
+                                     as_stream(stream)));
 }
 
 namespace {
@@ -367,6 +407,42 @@ int wqd_kv_append(const void* k_new, const void* v_new, const int32_t* positions
     return WQD_E_ALIGN;
   return hip_status(wqd::launch_kv_append(k_new, v_new, positions, B, Hkv, Lmax, k_cache, v_cache,
                                           as_stream(stream)));
+}
+
+int wqd_kv_pack_fp8(const void* k, const void* v, float k_scale, float v_scale, int64_t B, int64_t Hkv, int64_t L,
+                    int64_t Lmax, int64_t D, void* k_cache, void* v_cache, void* stream) {
+  const int st = check_kv(B, Hkv, Lmax, D);
+  if (st != WQD_OK) return st;
+  if (L < 0 || L > Lmax) return WQD_E_ARG;
+  if (!k || !v || !k_cache || !v_cache || !kv_scale_ok(k_scale) || !kv_scale_ok(v_scale)) return WQD_E_ARG;
+  if (!wqd::aligned16(k) || !wqd::aligned16(v) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache))
+    return WQD_E_ALIGN;
+  return hip_status(wqd::launch_kv8_copy(true, k, v, k_cache, v_cache, k_scale, v_scale, B * Hkv, L, Lmax,
+                                         as_stream(stream)));
+}
+
+int wqd_kv_unpack_fp8(const void* k_cache, const void* v_cache, int64_t B, int64_t Hkv, int64_t Lmax, int64_t D,
+                      void* k_codes, void* v_codes, void* stream) {
+  const int st = check_kv(B, Hkv, Lmax, D);
+  if (st != WQD_OK) return st;
+  if (!k_codes || !v_codes || !k_cache || !v_cache) return WQD_E_ARG;
+  if (!wqd::aligned16(k_codes) || !wqd::aligned16(v_codes) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache))
+    return WQD_E_ALIGN;
+  return hip_status(wqd::launch_kv8_copy(false, k_cache, v_cache, k_codes, v_codes, 1.0f, 1.0f, B * Hkv, Lmax, Lmax,
+                                         as_stream(stream)));
+}
+
+int wqd_kv_append_fp8(const void* k_new, const void* v_new, float k_scale, float v_scale, const int32_t* positions,
+                      int64_t B, int64_t Hkv, int64_t Lmax, int64_t D, void* k_cache, void* v_cache, void* stream) {
+  const int st = check_kv(B, Hkv, Lmax, D);
+  if (st != WQD_OK) return st;
+  if (!k_new || !v_new || !positions || !k_cache || !v_cache || !kv_scale_ok(k_scale) || !kv_scale_ok(v_scale))
+    return WQD_E_ARG;
+  if (!wqd::aligned16(k_new) || !wqd::aligned16(v_new) || !wqd::aligned16(k_cache) || !wqd::aligned16(v_cache) ||
+      reinterpret_cast<uintptr_t>(positions) % 4)
+    return WQD_E_ALIGN;
+  return hip_status(wqd::launch_kv8_append(k_new, v_new, k_scale, v_scale, positions, B, Hkv, Lmax, k_cache, v_cache,
+                                           as_stream(stream)));
 }
 
 int wqd_dequant(int fmt, const void* w_packed, const void* scales, const void* zeros, int64_t N, int64_t K,

@@ -24,10 +24,29 @@
 //      the softmax weights, below).
 // Both take Lmax * 128 * 2 bytes per (b, g); Lmax is a multiple of 32.
 //
+// An FP8 cache ("LLM 推理是怎么变快的", section 4, C: keys and values stored
+// as FP8 halve the cache's bytes) holds E4M3FN codes of K / k_scale and
+// V / v_scale (one float32 scale per tensor), Lmax * 128 bytes per (b, g),
+// in 1 KiB tiles that give each lane, in one 16-byte load, the codes of two
+// of the bf16 operands above (bytes 0-7 the first, 8-15 the second):
+//   K: tile (t / 16) * 2 + d / 64 holds positions 16 (t / 16) .. + 15 x
+//      dimensions 64 (d / 64) .. + 63: lane 16 kb + j (kb = (d % 32) / 8,
+//      j = t % 16), byte 8 ((d % 64) / 32) + d % 8, i.e. the operands of
+//      head-dimension steps 2 (d / 64) and 2 (d / 64) + 1;
+//   V: tile (t / 32) * 4 + d / 32 holds positions 32 (t / 32) .. + 31 x
+//      dimensions 32 (d / 32) .. + 31: lane 16 kb + n (n = d % 16), byte
+//      8 ((d % 32) / 16) + e (kb, e as for the bf16 V tile), i.e. the
+//      operands of dimension blocks 2 (d / 32) and 2 (d / 32) + 1.
+// Every E4M3 value is exact in bf16, so the kernel converts the codes to
+// bf16 operands (scale 1) and runs the bf16 arithmetic below on them: the
+// K scale joins the softmax scale, the V scale the final normalisation.  A
+// step is 64 positions (16 loads of 1 KiB, as a bf16 step), computed as two
+// halves of 32.
+//
 // attn_split_kernel: one workgroup of 4 wavefronts per (sequence b, KV head
-// g, split s); the split's positions in steps of 32, wavefront w taking steps
-// w, w + 4, ...  Per step, on bf16 matrix cores
-// (v_mfma_f32_16x16x32_bf16):
+// g, split s); the split's positions in steps of 32 (64 over an FP8 cache),
+// wavefront w taking steps w, w + 4, ...  Per 32 positions, on bf16 matrix
+// cores (v_mfma_f32_16x16x32_bf16):
 //   * S^T = K Q^T as two 16-position tiles x 4 head-dimension steps: A = one
 //     K tile (one 1 KiB load), B = Q^T, lane (kb, n) holding 8 head
 //     dimensions of query head n of the group (heads G .. 15 zero).  Output
@@ -76,9 +95,10 @@ struct AttnArgs {
   uint16_t* out;        // [B][Hq][128]
   float* part_ml;       // [B][Hq][S][2]: running maximum (log2 units), sum
   float* part_o;        // [B][Hq][S][128]: unnormalised output
-  float scale_log2;     // softmax scale times log2 e
+  float scale_log2;     // softmax scale (times the K scale of an FP8 cache) times log2 e
+  float out_scale;      // the V scale of an FP8 cache, 1 for bf16
   int64_t Lmax;
-  int Hq, Hkv, G, S, chunk;  // chunk: positions per split, a multiple of 32
+  int Hq, Hkv, G, S, chunk;  // chunk: positions per split, a multiple of the step (32 or 64)
 };
 
 struct AttnStepLoads {
@@ -104,6 +124,45 @@ __device__ __forceinline__ void attn_load(AttnStepLoads& ld, __amdgpu_buffer_rsr
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(vres, lane * 16, (vt + c) * 1024, 0);
     ld.v[c] = make_uint4(v.x, v.y, v.z, v.w);
   }
+}
+
+// FP8 cache: the K and V tiles of the 64 positions from t0 (a multiple of
+// 64): k[tau][h] = positions t0 + 16 tau .., dimensions 64 h ..;
+// v[u][c] = positions t0 + 32 u .., dimensions 32 c ...
+struct AttnStepLoads8 {
+  uint4 k[4][2];
+  uint4 v[2][4];
+};
+
+__device__ __forceinline__ void attn_load8(AttnStepLoads8& ld, __amdgpu_buffer_rsrc_t kres,
+                                           __amdgpu_buffer_rsrc_t vres, int64_t t0, int lane) {
+  const uint32_t kt = uint32_t(t0 / 16) * 2, vt = uint32_t(t0 / 32) * 4;
+#pragma unroll
+  for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(kres, lane * 16, (kt + 2 * tau + h) * 1024, 0);
+      ld.k[tau][h] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(vres, lane * 16, (vt + 4 * u + c) * 1024, 0);
+      ld.v[u][c] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+}
+
+// Eight E4M3 codes (two words) -> eight bf16, exact.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return make_uint4(__builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(w0)),
+                    __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(w0)),
+                    __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(w1)),
+                    __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(w1)));
+}
+
+__device__ __forceinline__ uint4 e4m3_half_to_bf16(const uint4& w, int half) {
+  return half == 0 ? e4m3x8_to_bf16x8(w.x, w.y) : e4m3x8_to_bf16x8(w.z, w.w);
 }
 
 struct AttnState {
@@ -189,6 +248,26 @@ __device__ __forceinline__ void attn_step(AttnState& st, AttnStepLoads& ld, cons
   }
 }
 
+// One FP8 step over positions t0 .. t0 + 63: each half of 32 positions is
+// converted to the bf16 operands of attn_step (exactly) and run through it;
+// the second half is skipped when it lies wholly at or past the length.
+__device__ __forceinline__ void attn_step8(AttnState& st, const AttnStepLoads8& l8, const uint4 (&qf)[4], float sl2,
+                                          int64_t t0, int64_t len, int kb, int n) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (u == 1 && t0 + 32 >= len) break;  // wave-uniform
+    AttnStepLoads ld;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ld.k[tau][s] = e4m3_half_to_bf16(l8.k[2 * u + tau][s >> 1], s & 1);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ld.v[c] = e4m3_half_to_bf16(l8.v[u][c >> 1], c & 1);
+    attn_step(st, ld, qf, sl2, t0 + 32 * u, len, kb, n);
+  }
+}
+
+template <bool FP8>
 __global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(AttnArgs a) {
   constexpr int W = kAttnWaves;
   __shared__ float s_ml[W][2][16];
@@ -211,10 +290,12 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(AttnArgs a)
     if (n < a.G) qf[st] = *reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.Hq + hq) * kHeadDim + 32 * st + 8 * kb);
   }
   const int64_t head = int64_t(b) * a.Hkv + g;
+  constexpr int EB = FP8 ? 1 : 2;  // bytes per cache element
+  const int64_t region = Lmax * kHeadDim * EB;
   const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.k + head * Lmax * kHeadDim), 0, uint32_t(Lmax * kHeadDim * 2), 0x00020000);
+      const_cast<char*>(reinterpret_cast<const char*>(a.k) + head * region), 0, uint32_t(region), 0x00020000);
   const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.v + head * Lmax * kHeadDim), 0, uint32_t(Lmax * kHeadDim * 2), 0x00020000);
+      const_cast<char*>(reinterpret_cast<const char*>(a.v) + head * region), 0, uint32_t(region), 0x00020000);
 
   AttnState st;
 #pragma unroll
@@ -222,9 +303,23 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(AttnArgs a)
   st.m = -INFINITY;
   st.l = 0.f;
   // wavefront w takes the split's steps w, w + W, w + 2 W, ...
-  constexpr int64_t STRIDE = 32 * W;
-  const int64_t t0 = t_begin + 32 * wave;
-  if (t0 < t_end) {
+  constexpr int64_t STEP = FP8 ? 64 : 32;
+  constexpr int64_t STRIDE = STEP * W;
+  const int64_t t0 = t_begin + STEP * wave;
+  if (FP8 && t0 < t_end) {
+    // as below, on 64-position steps (the chunk is a multiple of 64, so a
+    // step ends at or before its split's end)
+    AttnStepLoads8 l0, l1;
+    attn_load8(l0, kres, vres, t0, lane);
+    int64_t t = t0;
+    for (; t + STRIDE < t_end; t += 2 * STRIDE) {
+      attn_load8(l1, kres, vres, t + STRIDE, lane);
+      attn_step8(st, l0, qf, a.scale_log2, t, len, kb, n);
+      attn_load8(l0, kres, vres, t + 2 * STRIDE, lane);
+      attn_step8(st, l1, qf, a.scale_log2, t + STRIDE, len, kb, n);
+    }
+    if (t < t_end) attn_step8(st, l0, qf, a.scale_log2, t, len, kb, n);
+  } else if (!FP8 && t0 < t_end) {
     // two register sets: each step loads the wavefront's next step before its
     // own arithmetic (a step past the split reads in-bounds or zero tiles that
     // are never used)
@@ -271,7 +366,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_split_kernel(AttnArgs a)
     }
     const int64_t bh = int64_t(b) * a.Hq + int64_t(g) * a.G + h;
     if (a.S == 1) {  // the whole context: normalise and store (no merge launch)
-      const float inv = M != -INFINITY ? 1.0f / L : 0.f;
+      const float inv = M != -INFINITY ? a.out_scale / L : 0.f;
       reinterpret_cast<uint32_t*>(a.out + bh * kHeadDim)[dp] = bf16_pair(o0 * inv, o1 * inv);
     } else {
       const int64_t row = bh * a.S + s;
@@ -300,14 +395,15 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
       o0 += w * po[s * kHeadDim + 2 * lane];
       o1 += w * po[s * kHeadDim + 2 * lane + 1];
     }
-    o0 /= L;
-    o1 /= L;
+    const float inv = a.out_scale / L;
+    o0 *= inv;
+    o1 *= inv;
   }
   reinterpret_cast<uint32_t*>(a.out + bh * kHeadDim)[lane] = bf16_pair(o0, o1);
 }
 
 hipError_t launch_attn(const AttnPlan& p, const void* q, const void* k, const void* v, const int32_t* lens,
-                       int64_t B, float scale, void* out, void* ws, hipStream_t st) {
+                       int64_t B, float scale, float k_scale, float v_scale, void* out, void* ws, hipStream_t st) {
   AttnArgs a;
   a.q = reinterpret_cast<const uint16_t*>(q);
   a.k = reinterpret_cast<const uint16_t*>(k);
@@ -316,15 +412,19 @@ hipError_t launch_attn(const AttnPlan& p, const void* q, const void* k, const vo
   a.out = reinterpret_cast<uint16_t*>(out);
   a.part_ml = reinterpret_cast<float*>(ws);
   a.part_o = a.part_ml + B * p.Hq * p.S * 2;
-  a.scale_log2 = scale * kLog2e;
+  a.scale_log2 = scale * k_scale * kLog2e;
+  a.out_scale = v_scale;
   a.Lmax = p.Lmax;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.G = p.Hq / p.Hkv;
   a.S = p.S;
   a.chunk = p.chunk;
-  hipLaunchKernelGGL(attn_split_kernel, dim3(unsigned(p.S), unsigned(p.Hkv), unsigned(B)), dim3(64 * kAttnWaves), 0,
-                     st, a);
+  const dim3 grid(unsigned(p.S), unsigned(p.Hkv), unsigned(B));
+  if (p.fp8_kv)
+    hipLaunchKernelGGL(attn_split_kernel<true>, grid, dim3(64 * kAttnWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_split_kernel<false>, grid, dim3(64 * kAttnWaves), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(p.Hq), unsigned(B)), dim3(64), 0, st, a);
@@ -411,6 +511,95 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t*
   hipLaunchKernelGGL(kv_append_kernel, dim3(unsigned(ceil_div(n, int64_t(256)))), dim3(256), 0, st,
                      reinterpret_cast<const uint16_t*>(k_new), reinterpret_cast<const uint16_t*>(v_new), positions,
                      reinterpret_cast<uint16_t*>(k), reinterpret_cast<uint16_t*>(v), B, Hkv, Lmax);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ FP8 cache writers
+// Byte offsets of position t, dimension d inside one (b, g) region of the FP8
+// K and V tiles (layout above).
+__device__ __forceinline__ int64_t kv8_k_index(int64_t t, int d) {
+  return ((t / 16) * 2 + d / 64) * 1024 + (((d % 32) / 8) * 16 + (t % 16)) * 16 + 8 * ((d % 64) / 32) + (d % 8);
+}
+
+__device__ __forceinline__ int64_t kv8_v_index(int64_t t, int d) {
+  const int u = int(t % 32), kb = (u % 16) / 4, e = 4 * (u / 16) + (u % 4);
+  return ((t / 32) * 4 + d / 32) * 1024 + (kb * 16 + (d % 16)) * 16 + 8 * ((d % 32) / 16) + e;
+}
+
+// The E4M3 code of a bf16 value for a per-tensor scale: the nearest E4M3FN
+// value of x / scale (float32 division, ties to even, saturating at 448).
+__device__ __forceinline__ uint8_t kv8_code(uint16_t x, float scale) {
+  return uint8_t(e4m3_encode(__fdiv_rn(bf16_bits_to_f32(x), scale)));
+}
+
+// One thread per (b, g, t, dimension pair).  DIR 0: quantise logical bf16
+// [BH][L][128] into the tiles; 1: the tiles' codes back to logical uint8
+// [BH][L][128].
+template <int DIR>
+__global__ __launch_bounds__(256) void kv8_copy_kernel(const void* __restrict__ src_k, const void* __restrict__ src_v,
+                                                       uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v,
+                                                       float k_scale, float v_scale, int64_t BH, int64_t L,
+                                                       int64_t Lmax) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= BH * L * (kHeadDim / 2)) return;
+  const int d = int(i % (kHeadDim / 2)) * 2;
+  const int64_t t = (i / (kHeadDim / 2)) % L, bh = i / (kHeadDim / 2) / L;
+  const int64_t lin = (bh * L + t) * kHeadDim + d;
+  const int64_t tile = bh * Lmax * kHeadDim;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    if (DIR == 0) {
+      dst_k[tile + kv8_k_index(t, d + e)] = kv8_code(static_cast<const uint16_t*>(src_k)[lin + e], k_scale);
+      dst_v[tile + kv8_v_index(t, d + e)] = kv8_code(static_cast<const uint16_t*>(src_v)[lin + e], v_scale);
+    } else {
+      dst_k[lin + e] = static_cast<const uint8_t*>(src_k)[tile + kv8_k_index(t, d + e)];
+      dst_v[lin + e] = static_cast<const uint8_t*>(src_v)[tile + kv8_v_index(t, d + e)];
+    }
+  }
+}
+
+// One position per sequence, quantised: k_new / v_new bf16 [B][Hkv][128] at
+// positions[b] (a position outside [0, Lmax) writes nothing).
+__global__ __launch_bounds__(256) void kv8_append_kernel(const uint16_t* __restrict__ k_new,
+                                                         const uint16_t* __restrict__ v_new,
+                                                         const int32_t* __restrict__ positions,
+                                                         uint8_t* __restrict__ k, uint8_t* __restrict__ v,
+                                                         float k_scale, float v_scale, int64_t B, int64_t Hkv,
+                                                         int64_t Lmax) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= B * Hkv * kHeadDim) return;
+  const int d = int(i % kHeadDim);
+  const int64_t bh = i / kHeadDim, b = bh / Hkv;
+  const int64_t t = positions[b];
+  if (t < 0 || t >= Lmax) return;
+  const int64_t tile = bh * Lmax * kHeadDim;
+  k[tile + kv8_k_index(t, d)] = kv8_code(k_new[i], k_scale);
+  v[tile + kv8_v_index(t, d)] = kv8_code(v_new[i], v_scale);
+}
+
+hipError_t launch_kv8_copy(bool pack, const void* src_k, const void* src_v, void* dst_k, void* dst_v, float k_scale,
+                           float v_scale, int64_t BH, int64_t L, int64_t Lmax, hipStream_t st) {
+  const int64_t n = BH * L * (kHeadDim / 2);
+  if (n == 0) return hipSuccess;
+  const dim3 grid(unsigned(ceil_div(n, int64_t(256))));
+  auto* dk = reinterpret_cast<uint8_t*>(dst_k);
+  auto* dv = reinterpret_cast<uint8_t*>(dst_v);
+  if (pack)
+    hipLaunchKernelGGL(kv8_copy_kernel<0>, grid, dim3(256), 0, st, src_k, src_v, dk, dv, k_scale, v_scale, BH, L,
+                       Lmax);
+  else
+    hipLaunchKernelGGL(kv8_copy_kernel<1>, grid, dim3(256), 0, st, src_k, src_v, dk, dv, k_scale, v_scale, BH, L,
+                       Lmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv8_append(const void* k_new, const void* v_new, float k_scale, float v_scale,
+                             const int32_t* positions, int64_t B, int64_t Hkv, int64_t Lmax, void* k, void* v,
+                             hipStream_t st) {
+  const int64_t n = B * Hkv * kHeadDim;
+  hipLaunchKernelGGL(kv8_append_kernel, dim3(unsigned(ceil_div(n, int64_t(256)))), dim3(256), 0, st,
+                     reinterpret_cast<const uint16_t*>(k_new), reinterpret_cast<const uint16_t*>(v_new), positions,
+                     reinterpret_cast<uint8_t*>(k), reinterpret_cast<uint8_t*>(v), k_scale, v_scale, B, Hkv, Lmax);
   return hipGetLastError();
 }
 

@@ -44,12 +44,20 @@ hipError_t launch_w8a8(const W8Plan& p, const void* xc, const float* xscale, int
                        const void* wp, const void* scales, void* y, void* ws, hipStream_t st);
 // Decode attention (split along the context, then the fixed-order merge).
 hipError_t launch_attn(const AttnPlan& p, const void* q, const void* k, const void* v, const int32_t* lens,
-                       int64_t B, float scale, void* out, void* ws, hipStream_t st);
+                       int64_t B, float scale, float k_scale, float v_scale, void* out, void* ws, hipStream_t st);
 // KV cache tiles: pack / unpack [BH][L][128] logical rows, append one position per sequence.
 hipError_t launch_kv_copy(bool pack, const void* src_k, const void* src_v, void* dst_k, void* dst_v, int64_t BH,
                           int64_t L, int64_t Lmax, hipStream_t st);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* positions, int64_t B, int64_t Hkv,
                             int64_t Lmax, void* k, void* v, hipStream_t st);
+// The FP8 cache: pack quantises logical bf16 rows into the tiles, unpack
+// returns the tiles' codes as logical uint8 rows; append quantises one
+// position per sequence.
+hipError_t launch_kv8_copy(bool pack, const void* src_k, const void* src_v, void* dst_k, void* dst_v, float k_scale,
+                           float v_scale, int64_t BH, int64_t L, int64_t Lmax, hipStream_t st);
+hipError_t launch_kv8_append(const void* k_new, const void* v_new, float k_scale, float v_scale,
+                             const int32_t* positions, int64_t B, int64_t Hkv, int64_t Lmax, void* k, void* v,
+                             hipStream_t st);
 // A chain of decode layers in one persistent launch (clear, then the chain);
 // the workspace holds the table written by wqd_chain_prepare.
 hipError_t launch_chain(int fmt, int M, int ncalls, int total_items, int grid, long long ticks, void* ws,

@@ -441,7 +441,7 @@ int plan_act_quant(int64_t M, int64_t K, int* parts) {
 constexpr int64_t kAttnTargetGroups = WQD_ATTN_TARGET_GROUPS;  // workgroups of 4 wavefronts per launch
 constexpr int64_t kAttnWavesPerSplit = 4;
 
-int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnPlan* out) {
+int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnPlan* out, bool fp8_kv) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Lmax < 1) return kEArg;
   if (D != 128 || Hq % Hkv != 0 || Hq / Hkv > 16 || Lmax % 32 != 0) return kEShape;
   if (Lmax * 128 * 2 >= (int64_t(1) << 31) || B > 65535 || Hkv > 65535 || Hq > 65535) return kEUnsupported;
@@ -451,14 +451,17 @@ int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnP
   p.Hkv = int(Hkv);
   // about one workgroup of 4 wavefronts per compute unit (long streams per
   // wavefront measured faster than more, shorter splits), each wavefront at
-  // least 2 steps of 32 positions
+  // least 2 steps; a step is 32 positions of a bf16 cache, 64 of an FP8 one
+  // (the same 16 KiB of keys and values)
+  const int64_t step = fp8_kv ? 64 : 32;
   const int64_t pairs = B * Hkv;
-  const int64_t steps = ceil_div(Lmax, 32);
+  const int64_t steps = ceil_div(Lmax, step);
   int64_t S = ceil_div(kAttnTargetGroups, pairs);
   const int64_t max_s = steps / (2 * kAttnWavesPerSplit) > 1 ? steps / (2 * kAttnWavesPerSplit) : 1;
   if (S > max_s) S = max_s;
-  p.chunk = int(32 * ceil_div(steps, S));
+  p.chunk = int(step * ceil_div(steps, S));
   p.S = int(ceil_div(Lmax, p.chunk));
+  p.fp8_kv = fp8_kv ? 1 : 0;
   p.ws_bytes = p.S > 1 ? size_t(B) * size_t(Hq) * size_t(p.S) * (2 + 128) * sizeof(float) : 0;
   *out = p;
   return kOK;

@@ -192,16 +192,18 @@ struct W8Plan {
 int plan_w8a8(int64_t M, int64_t N, int64_t K, W8Plan* out);
 
 // Decode attention split along the context: S splits of `chunk` positions (a
-// multiple of 32) per (sequence, KV head), one workgroup of 4 wavefronts
-// each; with S > 1 the partial maxima, sums and outputs take
-// B * Hq * S * (2 + 128) floats of workspace.
+// multiple of the kernel's step: 32 positions over a bf16 cache, 64 over an
+// FP8 one) per (sequence, KV head), one workgroup of 4 wavefronts each; with
+// S > 1 the partial maxima, sums and outputs take B * Hq * S * (2 + 128)
+// floats of workspace.
 struct AttnPlan {
   int64_t Lmax;
   int Hq, Hkv, S, chunk;
+  int fp8_kv;  // 1: E4M3 codes, one byte per element
   size_t ws_bytes;
 };
 
-int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnPlan* out);
+int plan_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t D, AttnPlan* out, bool fp8_kv = false);
 
 // The activation quantisation: G workgroups each reduce a contiguous range of
 // x to its largest |x| (G <= kActQuantParts, written to the workspace), then
