@@ -136,7 +136,8 @@ enum wqd_path {
     WQD_PATH_MFMA = 2,    /* bf16 matrix cores, x staged in LDS, dequant on load */
     WQD_PATH_MC = 3,      /* streaming, bf16 matrix cores, x fragments read per tile */
     WQD_PATH_SKINNY = 4,  /* bf16 matrix cores, x staged in LDS by a producer wavefront, shared by 7-14 row blocks */
-    WQD_PATH_GEMM = 5     /* bf16 matrix cores, 64 or 256 x 256 tiles of y, x staged in LDS, dequant on load */
+    WQD_PATH_GEMM = 5,    /* bf16 matrix cores, 64 or 256 x 256 tiles of y, x staged in LDS, dequant on load */
+    WQD_PATH_GEMM_LDS = 6 /* bf16 matrix cores, 256 x 256 tiles of y, x and the weights staged in LDS (BF16) */
 };
 
 /*

@@ -171,8 +171,18 @@ def test_kernel_path_choice():
         assert wqd.kernel_path(fmt, 257, 8192, 8192) == ("gemm", 4)   # a 5th 64-row block, no 2nd 256-row round
         assert wqd.kernel_path(fmt, 512, 4096, 4096) == ("gemm", 4)   # 256-row tiles: too few workgroups
     assert wqd.kernel_path("bf16", 129, 8192, 8192) == ("gemm", 8)    # 256-row tiles with an 8-way K split
-    assert wqd.kernel_path("bf16", 1024, 28672, 8192) == ("gemm", 8)
     assert wqd.kernel_path("fp8", 1024, 28672, 8192) == ("gemm", 4)
+    # BF16 from 192 rows on the 70B verify shapes: the tiled kernel that stages
+    # the weights in LDS as well (its time model is the faster one there) ...
+    for M in (192, 257, 512, 1024):
+        assert wqd.kernel_path("bf16", M, 28672, 8192) == ("gemm_lds", 8)
+        assert wqd.kernel_path("bf16", M, 8192, 28672) == ("gemm_lds", 8)
+    # ... never below 192 rows, for K not a whole number of 32-k tiles, nor for FP8 / W4A16
+    assert wqd.kernel_path("bf16", 191, 28672, 8192)[0] == "gemm"
+    assert wqd.kernel_path("bf16", 1024, 28672, 8208)[0] == "gemm"
+    for fmt in ("fp8", "w4a16"):
+        for M in (192, 512, 1024):
+            assert wqd.kernel_path(fmt, M, 28672, 8192)[0] == "gemm"
     for M in (65, 1024):
         assert wqd.kernel_path("w4a16", M, 8192, 8192) == ("gemm", 8)
     # otherwise above 64 rows (N under 16 x 256): the LDS matrix-core kernel
@@ -181,11 +191,11 @@ def test_kernel_path_choice():
     assert wqd.kernel_path("fp8", 256, 3840, 8192)[0] == "mfma"
     # the tiled kernel's K split: whole splits of M x N float32 partials, at most 8
     for fmt, M, N, K in (("bf16", 128, 8192, 28672), ("fp8", 384, 8192, 8192), ("bf16", 1024, 28672, 8192),
-                         ("fp8", 96, 4096, 4096)):
+                         ("fp8", 96, 4096, 4096), ("bf16", 512, 8192, 28672), ("bf16", 256, 8192, 8192)):
         ws = wqd.workspace_bytes(fmt, M, N, K)
         assert ws % (M * N * 4) == 0 and ws // (M * N * 4) in (0, 2, 3, 4, 5, 6, 7, 8)
     assert wqd.workspace_bytes("bf16", 128, 8192, 28672) == 4 * 128 * 8192 * 4  # 64 tiles: 4 splits fill the GPU
-    assert wqd.workspace_bytes("bf16", 1024, 28672, 8192) == 0                  # 896 tiles: no split
+    assert wqd.workspace_bytes("bf16", 1024, 28672, 8192) == 0                  # 448 tiles of 256 x 256: no split
     # x rows spanning 2 GiB: the LDS matrix-core kernel
     assert wqd.kernel_path("bf16", 65536, 64, 16384)[0] == "mfma"
     L = wqd.lib()

@@ -304,6 +304,31 @@ def test_qgemm_tiled_256_rows_padded(fmt, N, K, M):
     compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("N,K,M,S", [(8208, 8224, 513, 2), (16392, 2048, 513, 1), (28672, 1056, 300, 1),
+                                     (12296, 4096, 777, 1), (11008, 4096, 777, 1)])
+def test_qgemm_tiled_lds(N, K, M, S):
+    """BF16 on the tiled kernel that stages x and the weights in LDS (256 x 256
+    tiles): ragged N inside a 16-row block and a last column block of one row
+    block, ragged M (a last row block of 1 or 9 rows), chunk counts leaving
+    each remainder of the 4-chunk loop (257 chunks split 129 + 128, 33, 64,
+    128), and a K split.  The oracle checks a sample of output columns,
+    the first and last ones included, over every row."""
+    fmt = "bf16"
+    assert wqd.kernel_path(fmt, M, N, K) == ("gemm_lds", 8)
+    ws = wqd.workspace_bytes(fmt, M, N, K)
+    assert (ws // (M * N * 4) if ws else 1) == S
+    W = I.w_host(6300 + N + K, N, K)
+    rng = np.random.default_rng(N + K)
+    cols = np.unique(np.concatenate([rng.choice(N, 48, replace=False), [0, 15, 255, 256, N - 17, N - 9, N - 1]]))
+    qw = oracle.quantize(fmt, W[cols])
+    pw = wqd.pack_weights(fmt, to_dev(W))
+    print(f"qgemm lds M={M} N={N} K={K} S={S}", flush=True)
+    x = I.x_bf16_bits(43 * M + K, M, K)
+    y = wqd.qgemm(x_dev(x), pw)
+    torch.cuda.synchronize()
+    compare_y(bf16_bits(y)[:, cols], oracle.qgemm_exact(x, qw), f"{fmt} lds M={M} N={N} K={K}")
+
+
 def mfma_wide_shapes(fmt):
     # (N, K) that the LDS matrix-core kernel takes above 64 rows (below 16
     # column blocks of 256): ragged N, ragged K tiles where the format allows

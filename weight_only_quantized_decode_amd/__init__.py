@@ -165,7 +165,7 @@ def workspace_bytes(fmt, M: int, N: int, K: int) -> int:
     return b.value
 
 
-KERNEL_PATHS = ("bcast", "staged", "mfma", "mc", "skinny", "gemm")
+KERNEL_PATHS = ("bcast", "staged", "mfma", "mc", "skinny", "gemm", "gemm_lds")
 
 
 def kernel_path(fmt, M: int, N: int, K: int):

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwqd.so")
-SOURCES = ["wqd_plan.cpp", "wqd_api.cpp", "wqd_pack.hip", "wqd_gemv.hip", "wqd_gemv_bcast.hip", "wqd_gemv_mc.hip", "wqd_skinny.hip", "wqd_gemm.hip", "wqd_mfma.hip", "wqd_stream.hip", "wqd_spec.hip", "wqd_noalloc.hip", "wqd_w8a8.hip", "wqd_attn.hip", "wqd_chain.hip"]
+SOURCES = ["wqd_plan.cpp", "wqd_api.cpp", "wqd_pack.hip", "wqd_gemv.hip", "wqd_gemv_bcast.hip", "wqd_gemv_mc.hip", "wqd_skinny.hip", "wqd_gemm.hip", "wqd_gemm_lds.hip", "wqd_mfma.hip", "wqd_stream.hip", "wqd_spec.hip", "wqd_noalloc.hip", "wqd_w8a8.hip", "wqd_attn.hip", "wqd_chain.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}"]
@@ -23,7 +23,8 @@ NO_PACKED_F32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Per-file flags: the tiled matrix-core kernel keeps its accumulators in VGPRs
 # (in AGPRs the compiler copied them at every loop edge, and the 4-wavefront
 # instances needed over 256 registers).
-EXTRA = {"wqd_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "wqd_w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+EXTRA = {"wqd_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "wqd_gemm_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "wqd_w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          # decode attention: 234 registers in VGPR form (two wavefronts per SIMD) against 272 with AGPRs
          "wqd_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

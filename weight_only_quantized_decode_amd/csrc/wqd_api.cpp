@@ -65,6 +65,7 @@ int qgemm_checked(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const
     case kPathStaged:
       return hip_status(launch_gemv(fmt, c.gemv, x, M, N, K, w_packed, scales, zeros, y, swiglu, s));
     case kPathGemm:
+    case kPathGemmLds:
       return hip_status(launch_gemm(fmt, c.gm, x, M, N, K, w_packed, scales, zeros, y, workspace, swiglu, s));
     case kPathSkinny:
       return hip_status(launch_gemv_sk(fmt, c.sk, x, M, N, K, w_packed, scales, zeros, y, workspace, swiglu, s));
@@ -124,6 +125,7 @@ int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* wa
            : c.path == wqd::kPathStaged ? c.gemv.waves
            : c.path == wqd::kPathSkinny ? c.sk.waves + 1
            : c.path == wqd::kPathGemm   ? (fmt == wqd::kFmtW4 ? 8 : 4 * c.gm.wm)
+           : c.path == wqd::kPathGemmLds ? 8
                                         : 4;
   }
   return WQD_OK;

@@ -592,7 +592,9 @@ hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64
   a.xsum = reinterpret_cast<const float*>(ws);
   a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.xs_bytes);
   hipError_t e;
-  if (fmt == kFmtBF16) {
+  if (p.wm == 3) {
+    e = launch_gemm_lds(fmt, p, x, M, N, K, wp, y, a.part, swiglu, st);
+  } else if (fmt == kFmtBF16) {
     e = launch_gm_fmt<kFmtBF16>(a, p, st);
   } else if (fmt == kFmtFP8) {
     e = launch_gm_fmt<kFmtFP8>(a, p, st);

@@ -276,13 +276,76 @@ static int plan_gemm_wm(int fmt, int64_t M, int64_t N, int64_t K, const PackedSi
   return kOK;
 }
 
+// The tiled kernel with both operands staged in LDS (wm = 3, BF16): 256 x 256
+// tiles, one workgroup per compute unit, chunks of one packed tile (32 k)
+// along K.  Time model t = c0 + cps * a * rounds + the split partials
+// (written and read once at bw), fitted by least squares to the kernel on the
+// 70B q, gate and down shapes at 192-1024 rows (rms error ~10%).  An FP8 form
+// (64-k chunks, three 48 KiB stages) measured 7-38% slower than the tiled
+// kernel that takes FP8 weights straight into registers, so FP8 keeps that.
+constexpr double kGlC0 = 13.0, kGlA = 0.89, kGlBw = 3.75;
+constexpr int64_t kGlMinM = 192;
+
+static int plan_gemm_lds(int fmt, int64_t M, int64_t N, int64_t K, const PackedSizes& ps, GmPlan* out,
+                         double* t_us) {
+  if (fmt != kFmtBF16) return kEUnsupported;
+  // fitted and measured from 192 rows (below, most of a 256-row tile is padding)
+  if (M < kGlMinM) return kEUnsupported;
+  // K a whole number of tiles (no x piece of a tile lies past K)
+  if (K % tile_k(fmt) != 0) return kEUnsupported;
+  // weight offsets of 16 row blocks stay below 2^31
+  if (16 * ps.KT * kTileBytes >= (int64_t(1) << 31)) return kEUnsupported;
+  GmPlan p{};
+  p.NB = ps.NB;
+  p.KT = ps.KT;
+  p.wm = 3;
+  p.NBN = ceil_div(p.NB, 16);
+  p.MB = ceil_div(M, 256);
+  p.Mp = p.MB * 256;
+  p.nchunks = p.KT;
+  const int64_t tiles = p.NBN * p.MB;
+  const double mn8 = double(M) * double(N) * 8.0;
+  const int64_t max_s = p.nchunks / 8 < 1 ? 1 : (p.nchunks / 8 > 8 ? 8 : p.nchunks / 8);
+  double best = 0.0;
+  int64_t S = 1;
+  for (int64_t s = 1; s <= max_s; ++s) {
+    const int64_t cps = ceil_div(p.nchunks, s), se = ceil_div(p.nchunks, cps);
+    const int64_t rounds = ceil_div(tiles * se, kComputeUnits);
+    const double t = kGlC0 + double(cps) * kGlA * double(rounds) + (se > 1 ? double(se) * mn8 / (kGlBw * 1.0e6) : 0.0);
+    if (s == 1 || t < 0.98 * best) {
+      best = t;
+      S = se;
+    }
+  }
+  p.cps = ceil_div(p.nchunks, S);
+  p.S = int(ceil_div(p.nchunks, p.cps));
+  p.ws_bytes = p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;
+  *out = p;
+  *t_us = best;
+  return kOK;
+}
+
 int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   PackedSizes ps;
   int st = packed_sizes(fmt, N, K, &ps);
   if (st != kOK) return st;
   if (M < 1) return kEArg;
   if (M * K * 2 >= (int64_t(1) << 31)) return kEUnsupported;
-  double t1 = 0.0, t2 = 0.0;
+#ifdef WQD_GEMM_FORCE_WM
+  {
+    // measurement builds only: one tile shape regardless of the models
+    double t = 0.0;
+    GmPlan pf;
+    const int wf = WQD_GEMM_FORCE_WM;
+    if ((wf == 3 ? plan_gemm_lds(fmt, M, N, K, ps, &pf, &t) : plan_gemm_wm(fmt, M, N, K, ps, wf, &pf, &t)) == kOK) {
+      *out = pf;
+      return kOK;
+    }
+  }
+#endif
+  double t1 = 0.0, t2 = 0.0, t3 = 0.0;
+  GmPlan p3;
+  const bool lds_ok = plan_gemm_lds(fmt, M, N, K, ps, &p3, &t3) == kOK;
   // 64-row tiles or the taller ones, whichever the model puts faster (within
   // 2%: 64).  Taller tiles read each weight chunk for more rows (W4A16: half
   // the dequantisation per multiply) but pad M and quantise the launch into
@@ -292,11 +355,14 @@ int plan_gemm(int fmt, int64_t M, int64_t N, int64_t K, GmPlan* out) {
   GmPlan p1, p2;
   st = plan_gemm_wm(fmt, M, N, K, ps, 1, &p1, &t1);
   if (st != kOK) return st;
-  if (plan_gemm_wm(fmt, M, N, K, ps, 2, &p2, &t2) == kOK && t2 < 0.98 * t1) {
-    *out = p2;
-    return kOK;
+  GmPlan best = p1;
+  double tb = t1;
+  if (plan_gemm_wm(fmt, M, N, K, ps, 2, &p2, &t2) == kOK && t2 < 0.98 * tb) {
+    best = p2;
+    tb = t2;
   }
-  *out = p1;
+  if (lds_ok && t3 < 0.98 * tb) best = p3;
+  *out = best;
   return kOK;
 }
 
@@ -365,7 +431,7 @@ int choose_path(int fmt, int64_t M, int64_t N, int64_t K, Choice* out) {
   } else if (M <= kSkMaxM && sk_ok) {
     c.path = kPathSkinny;
   } else if (M > kGmMinM && ceil_div(N, int64_t(256)) >= kGmMinNBN && plan_gemm(fmt, M, N, K, &c.gm) == kOK) {
-    c.path = kPathGemm;
+    c.path = c.gm.wm == 3 ? kPathGemmLds : kPathGemm;
   } else {
     st = plan_mfma(fmt, M, N, K, &c.mfma);
     if (st != kOK) return st;
@@ -381,7 +447,7 @@ int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out) {
   if (st != kOK) return st;
   *out = c.path == kPathMfma     ? c.mfma.ws_bytes
          : c.path == kPathSkinny ? c.sk.ws_bytes
-         : c.path == kPathGemm   ? c.gm.ws_bytes
+         : c.path == kPathGemm || c.path == kPathGemmLds ? c.gm.ws_bytes
                                  : 0;
   return kOK;
 }

@@ -157,8 +157,10 @@ int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out);
 // the streaming matrix-core kernel on matrices up to 8192 x 8192 that the
 // skinny kernel would split over K; the skinny kernel otherwise up to 64
 // rows; above that the tiled matrix-core kernel where N has at least
-// kGmMinNBN column blocks of 256, else the LDS matrix-core kernel.
-enum Path { kPathBcast = 0, kPathStaged = 1, kPathMfma = 2, kPathMc = 3, kPathSkinny = 4, kPathGemm = 5 };
+// kGmMinNBN column blocks of 256 (for BF16 and FP8, where its time model
+// says so, in the form that stages the weights in LDS as well), else the LDS
+// matrix-core kernel.
+enum Path { kPathBcast = 0, kPathStaged = 1, kPathMfma = 2, kPathMc = 3, kPathSkinny = 4, kPathGemm = 5, kPathGemmLds = 6 };
 
 struct Choice {
   int path;
