@@ -489,14 +489,18 @@ int wqd_decode_e4m3(const uint8_t* codes, float* out, int64_t n, void* stream);
  * An empty residual draws from target_i; an all-zero row draws -1.
  * Outputs (device, caller-owned): n_kept int32 [B] (0 .. k) and out_tokens
  * int32 [B, k+1]: the kept drafts, the drawn token, then -1.  draft,
- * draft_tokens and u_accept may be NULL when k = 0.  Deterministic; all
- * arrays contiguous row-major, 4-byte aligned.
+ * draft_tokens and u_accept may be NULL when k = 0.  workspace: device,
+ * >= wqd_spec_workspace_bytes(B, V) (per sequence, two 64-bit unit sums per
+ * 256 tokens), 8-byte aligned, contents on entry do not matter.
+ * Deterministic; all arrays contiguous row-major, 4-byte aligned.
  * Errors: WQD_E_ARG (NULL pointer, B < 1, k < 0, V < 1), WQD_E_SHAPE (k > 64,
- * V > 2^20), WQD_E_ALIGN.
+ * V > 2^20), WQD_E_ALIGN, WQD_E_WORKSPACE.
  */
+int wqd_spec_workspace_bytes(int64_t B, int64_t V, size_t* bytes);
 int wqd_spec_accept(const float* target, const float* draft, const int32_t* draft_tokens,
                     const float* u_accept, const float* u_draw, int64_t B, int64_t k, int64_t V,
-                    int32_t* n_kept, int32_t* out_tokens, void* stream);
+                    int32_t* n_kept, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /*
  * Measurement: read `bytes` (multiple of 16) from device `src` with 16-byte

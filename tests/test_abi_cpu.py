@@ -261,11 +261,18 @@ def test_spec_accept_rejects_bad_arguments():
     """Validation happens before any device work (no GPU needed)."""
     L = wqd.lib()
     A = 0x10000
-    args = [A, A, A, A, A, 4, 3, 100, A, A, None]  # target, draft, tokens, u_accept, u_draw, B, k, V, n, out
+    # target, draft, tokens, u_accept, u_draw, B, k, V, n, out, workspace, workspace_bytes, stream
+    b = ctypes.c_size_t()
+    assert L.wqd_spec_workspace_bytes(4, 100, ctypes.byref(b)) == OK
+    assert b.value == 4 * 1 * 2 * 8  # one tile of 256 tokens, two 64-bit sums, per sequence
+    assert L.wqd_spec_workspace_bytes(64, 128256, ctypes.byref(b)) == OK and b.value == 64 * 501 * 16
+    assert L.wqd_spec_workspace_bytes(0, 100, ctypes.byref(b)) == E_ARG
+    assert L.wqd_spec_workspace_bytes(1, (1 << 20) + 1, ctypes.byref(b)) == E_SHAPE
+    args = [A, A, A, A, A, 4, 3, 100, A, A, A, 64, None]
 
     def call(**kw):
         a = list(args)
-        names = ["target", "draft", "tokens", "u_accept", "u_draw", "B", "k", "V", "n", "out"]
+        names = ["target", "draft", "tokens", "u_accept", "u_draw", "B", "k", "V", "n", "out", "ws", "wsb"]
         for key, val in kw.items():
             a[names.index(key)] = val
         return L.wqd_spec_accept(*a)
@@ -275,6 +282,7 @@ def test_spec_accept_rejects_bad_arguments():
     assert call(B=0) == E_ARG and call(k=-1) == E_ARG and call(V=0) == E_ARG
     assert call(k=65) == E_SHAPE and call(V=(1 << 20) + 1) == E_SHAPE
     assert call(target=A + 2) == E_ALIGN and call(out=A + 1) == E_ALIGN
+    assert call(ws=None) == E_WS and call(wsb=63) == E_WS and call(ws=A + 4) == E_ALIGN
 
 
 def test_chain_rejects_bad_arguments_before_any_device_call():

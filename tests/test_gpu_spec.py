@@ -34,7 +34,8 @@ def check(target, draft, tokens, u, v, what):
     return n
 
 
-@pytest.mark.parametrize("B,k,V", [(64, 1, 3), (64, 4, 1000), (32, 7, 32000), (8, 16, 4099), (8, 4, 128256)])
+@pytest.mark.parametrize("B,k,V", [(64, 1, 3), (64, 4, 1000), (32, 7, 32000), (8, 16, 4099), (8, 4, 128256),
+                                   (1, 4, 128256), (1024, 2, 1000)])
 def test_spec_accept_matches_oracle(B, k, V):
     n = check(*I.spec_inputs(900 + V + k, B, k, V), f"random V={V}")
     assert 0 < n.mean() < k or k == 1  # a mix of early rejections and kept drafts

@@ -103,7 +103,8 @@ def lib() -> ctypes.CDLL:
             "wqd_dequant": (i32, [i32, vp, vp, vp, i64, i64, vp, vp]),
             "wqd_unpack": (i32, [i32, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
             "wqd_decode_e4m3": (i32, [vp, vp, i64, vp]),
-            "wqd_spec_accept": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]),
+            "wqd_spec_workspace_bytes": (i32, [i64, i64, psz]),
+            "wqd_spec_accept": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]),
             "wqd_stream_read": (i32, [vp, sz, vp, vp]),
             "wqd_stream_sink_words": (sz, [sz]),
             "wqd_stream_copy": (i32, [vp, vp, sz, vp]),
@@ -651,7 +652,7 @@ def decode_e4m3(codes, stream=None):
     return out
 
 
-def spec_accept(target, draft, draft_tokens, u_accept, u_draw, stream=None):
+def spec_accept(target, draft, draft_tokens, u_accept, u_draw, workspace=None, stream=None):
     """Speculative accept / reject on the device (``wqd_spec_accept``).
 
     target float32 [B, k+1, V], draft float32 [B, k, V], draft_tokens int32
@@ -670,9 +671,19 @@ def spec_accept(target, draft, draft_tokens, u_accept, u_draw, stream=None):
     n_kept = torch.empty(B, dtype=torch.int32, device=target.device)
     out = torch.empty((B, k1), dtype=torch.int32, device=target.device)
     ptr = lambda t: t.data_ptr() if t.numel() else None  # noqa: E731
+    if workspace is None:
+        workspace = get_workspace(spec_workspace_bytes(B, V), target.device)
+    wsb = workspace.numel() * workspace.element_size()
     _check(lib().wqd_spec_accept(target.data_ptr(), ptr(draft), ptr(draft_tokens), ptr(u_accept), u_draw.data_ptr(),
-                                 B, k, V, n_kept.data_ptr(), out.data_ptr(), _stream(stream)), "wqd_spec_accept")
+                                 B, k, V, n_kept.data_ptr(), out.data_ptr(), workspace.data_ptr(), wsb,
+                                 _stream(stream)), "wqd_spec_accept")
     return n_kept, out
+
+
+def spec_workspace_bytes(B: int, V: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().wqd_spec_workspace_bytes(B, V, ctypes.byref(b)), "wqd_spec_workspace_bytes")
+    return b.value
 
 
 def stream_read(buf, sink=None, stream=None):

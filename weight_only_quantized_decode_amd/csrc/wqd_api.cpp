@@ -478,17 +478,26 @@ int wqd_decode_e4m3(const uint8_t* codes, float* out, int64_t n, void* stream) {
   return hip_status(wqd::launch_decode_e4m3(codes, out, n, as_stream(stream)));
 }
 
+int wqd_spec_workspace_bytes(int64_t B, int64_t V, size_t* bytes) {
+  if (!bytes || B < 1 || V < 1) return WQD_E_ARG;
+  if (V > (int64_t(1) << 20) || B > 0x7fffffff) return WQD_E_SHAPE;
+  *bytes = wqd::spec_workspace_bytes(B, V);
+  return WQD_OK;
+}
+
 int wqd_spec_accept(const float* target, const float* draft, const int32_t* draft_tokens, const float* u_accept,
                     const float* u_draw, int64_t B, int64_t k, int64_t V, int32_t* n_kept, int32_t* out_tokens,
-                    void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 1 || k < 0 || V < 1 || !target || !u_draw || !n_kept || !out_tokens) return WQD_E_ARG;
   if (k > 0 && (!draft || !draft_tokens || !u_accept)) return WQD_E_ARG;
   if (k > 64 || V > (int64_t(1) << 20) || B > 0x7fffffff) return WQD_E_SHAPE;
   const void* ptrs[] = {target, draft, draft_tokens, u_accept, u_draw, n_kept, out_tokens};
   for (const void* q : ptrs)
     if (reinterpret_cast<uintptr_t>(q) % 4) return WQD_E_ALIGN;
+  if (!workspace || workspace_bytes < wqd::spec_workspace_bytes(B, V)) return WQD_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 8) return WQD_E_ALIGN;
   return hip_status(wqd::launch_spec_accept(target, k > 0 ? draft : nullptr, draft_tokens, u_accept, u_draw, B, k,
-                                            V, n_kept, out_tokens, as_stream(stream)));
+                                            V, n_kept, out_tokens, workspace, as_stream(stream)));
 }
 
 size_t wqd_stream_sink_words(size_t bytes) { return wqd::stream_sink_words(bytes); }

@@ -82,6 +82,8 @@ int qgemm_checked(int fmt, const void* x, int64_t M, int64_t N, int64_t K, const
 int record_hip_error(hipError_t e);
 hipError_t launch_spec_accept(const float* target, const float* draft, const int32_t* tokens, const float* u_accept,
                               const float* u_draw, int64_t B, int64_t k, int64_t V, int32_t* n_kept, int32_t* out,
-                              hipStream_t st);
+                              void* ws, hipStream_t st);
+// Workspace of the accept / reject step: two 64-bit tile sums per 256 tokens and sequence.
+size_t spec_workspace_bytes(int64_t B, int64_t V);
 
 }  // namespace wqd

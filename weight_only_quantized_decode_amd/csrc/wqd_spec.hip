@@ -5,14 +5,19 @@
 // last target row when every draft is kept; section 6.2: the output is then an
 // exact sample of the target).
 //
-// One workgroup of 16 wavefronts per sequence.  The accept tests are a
-// handful of loads, taken by every thread alike.  The draw reads one row (two
-// for a residual) of V float32 probabilities in tiles of 256 tokens: a
-// wavefront sums a tile's weights in integer units of 2^-32 from four
-// coalesced loads per lane and row, the tile sums are scanned in LDS to find
-// the tile that holds the threshold, and one wavefront scans that tile's
-// tokens in order to the drawn one.  Integer units make the draw exact and
-// independent of the order of summation.
+// Two launches, so that the row reads spread over the whole GPU:
+//   * spec_sums_kernel, P workgroups of 4 wavefronts per sequence: each takes
+//     the accept tests (a handful of loads, the same for every thread) and
+//     sums its share of the row's tiles of 256 tokens - each wavefront four
+//     tiles at a time, from four coalesced loads per lane, tile and row - in integer
+//     units of 2^-32, both the residual max(target - draft, 0) and the target
+//     itself from the same loads (the residual may be empty), into the
+//     workspace; workgroup 0 writes the kept count and tokens;
+//   * spec_draw_kernel, one workgroup of 16 wavefronts per sequence: scans
+//     the tile sums in LDS to find the tile that holds the threshold, and one
+//     wavefront scans that tile's tokens in order to the drawn one.
+// Integer units make the draw exact and independent of the order of
+// summation.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -59,51 +64,99 @@ __device__ inline u64 wave_inclusive_scan(u64 v, int lane) {
   return v;
 }
 
-__global__ __launch_bounds__(kSpecThreads) void spec_accept_kernel(
-    const float* __restrict__ target, const float* __restrict__ draft, const int32_t* __restrict__ tokens,
-    const float* __restrict__ u_accept, const float* __restrict__ u_draw, int64_t k, int64_t V,
-    int32_t* __restrict__ n_kept, int32_t* __restrict__ out) {
+// Accept tests of sequence b, left to right: keep x while u * d(x) < t(x) in
+// float32; the first rejected position (k when every draft is kept).
+__device__ inline int64_t spec_first_rejection(const float* t, const float* d, const int32_t* tokens,
+                                               const float* u_accept, int64_t b, int64_t k, int64_t V) {
+  for (int64_t i = 0; i < k; ++i) {
+    const int32_t x = tokens[b * k + i];
+    const bool keep = x >= 0 && x < V && u_accept[b * k + i] * d[i * V + x] < t[i * V + x];
+    if (!keep) return i;
+  }
+  return k;
+}
+
+// Workgroup (b, p): the tile sums of sequence b's draw rows, tiles
+// p * 4 + w + 4 P i for wavefront w; ws[b][tile] = {residual units, target units}.
+__global__ __launch_bounds__(256) void spec_sums_kernel(const float* __restrict__ target,
+                                                        const float* __restrict__ draft,
+                                                        const int32_t* __restrict__ tokens,
+                                                        const float* __restrict__ u_accept, int64_t k, int64_t V,
+                                                        int64_t NT, int32_t* __restrict__ n_kept,
+                                                        int32_t* __restrict__ out, u64* __restrict__ ws) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t b = blockIdx.x, P = gridDim.y, p = blockIdx.y;
+  const float* t = target + b * (k + 1) * V;
+  const float* d = draft ? draft + b * k * V : nullptr;
+  const int64_t r = spec_first_rejection(t, d, tokens, u_accept, b, k, V);
+  if (p == 0) {
+    int32_t* o = out + b * (k + 1);
+    for (int64_t i = tid; i <= k; i += 256)
+      if (i != r) o[i] = i < r ? tokens[b * k + i] : -1;
+    if (tid == 0) n_kept[b] = int32_t(r);
+  }
+  const float* tr = t + r * V;
+  const float* dr = r < k ? d + r * V : nullptr;
+  u64* wsb = ws + b * NT * 2;
+  // four of the wavefront's tiles per round, all their loads issued before any sum
+  for (int64_t t0 = p * 4 + wave; t0 < NT; t0 += 16 * P) {
+    float tv[4][4], dv[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t jq = (t0 + 4 * P * u) * kSpecTile + lane + 64 * q;
+        const bool in = t0 + 4 * P * u < NT && jq < V;
+        tv[u][q] = in ? tr[jq] : 0.0f;
+        dv[u][q] = in && dr ? dr[jq] : 0.0f;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t ti = t0 + 4 * P * u;
+      u64 sr = 0, st = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        st += draw_unit(tv[u][q]);
+        if (dr) sr += draw_unit(fmaxf(tv[u][q] - dv[u][q], 0.0f));
+      }
+      for (int m = 32; m > 0; m >>= 1) {
+        sr += __shfl_xor(sr, m);
+        st += __shfl_xor(st, m);
+      }
+      if (lane == 0 && ti < NT) {
+        wsb[2 * ti] = sr;
+        wsb[2 * ti + 1] = st;
+      }
+    }
+  }
+}
+
+// One workgroup per sequence: the draw from the tile sums.
+__global__ __launch_bounds__(kSpecThreads) void spec_draw_kernel(const float* __restrict__ target,
+                                                                 const float* __restrict__ draft,
+                                                                 const float* __restrict__ u_draw, int64_t k,
+                                                                 int64_t V, int64_t NT,
+                                                                 const int32_t* __restrict__ n_kept,
+                                                                 int32_t* __restrict__ out,
+                                                                 const u64* __restrict__ ws) {
   __shared__ u64 s_tile[kSpecMaxTiles];
   __shared__ u64 s_wave[kSpecWaves];
   __shared__ u64 s_pick[2];  // picked tile, units before it
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t b = blockIdx.x;
-  const float* t = target + b * (k + 1) * V;
-  const float* d = draft ? draft + b * k * V : nullptr;
+  const int64_t r = n_kept[b];
   int32_t* o = out + b * (k + 1);
-
-  // accept tests, left to right: keep x while u * d(x) < t(x) in float32
-  int64_t r = k;
-  for (int64_t i = 0; i < k; ++i) {
-    const int32_t x = tokens[b * k + i];
-    const bool keep = x >= 0 && x < V && u_accept[b * k + i] * d[i * V + x] < t[i * V + x];
-    if (!keep) {
-      r = i;
-      break;
-    }
-  }
-  for (int64_t i = tid; i <= k; i += kSpecThreads)
-    if (i != r) o[i] = i < r ? tokens[b * k + i] : -1;
+  const float* tr = target + (b * (k + 1) + r) * V;
+  const float* dr = r < k ? draft + (b * k + r) * V : nullptr;
+  const u64* wsb = ws + b * NT * 2;
   if (tid == 0) {
-    n_kept[b] = int32_t(r);
     s_pick[0] = 0;  // read only after a barrier; always overwritten when T > 0
     s_pick[1] = 0;
   }
-
-  // the draw: residual of row r, else (empty residual, or every draft kept) target row r
-  const float* tr = t + r * V;
-  const float* dr = r < k ? d + r * V : nullptr;
-  const int64_t NT = (V + kSpecTile - 1) / kSpecTile;
+  // the residual's sums (rejection), the target's (every draft kept, or an empty residual)
   for (int pass = 0; pass < 2; ++pass) {
-    // tile sums: wavefront w takes tiles w, w + 16, ...
-#pragma unroll 4
-    for (int64_t ti = wave; ti < NT; ti += kSpecWaves) {
-      const int64_t j = ti * kSpecTile + lane;
-      u64 s = weight_at(tr, dr, j, V) + weight_at(tr, dr, j + 64, V) + weight_at(tr, dr, j + 128, V) +
-              weight_at(tr, dr, j + 192, V);
-      for (int m = 32; m > 0; m >>= 1) s += __shfl_xor(s, m);
-      if (lane == 0) s_tile[ti] = s;
-    }
+    const int which = dr ? 0 : 1;
+    for (int64_t i = tid; i < NT; i += kSpecThreads) s_tile[i] = wsb[2 * i + which];
     __syncthreads();
     // scan of the tile sums: thread t owns tiles 4t .. 4t + 3
     u64 mine = 0;
@@ -116,9 +169,9 @@ __global__ __launch_bounds__(kSpecThreads) void spec_accept_kernel(
     __syncthreads();
     u64 wbase = 0, T = 0;
     for (int w = 0; w < kSpecWaves; ++w) {
-      const u64 s = s_wave[w];
-      if (w < wave) wbase += s;
-      T += s;
+      const u64 sw = s_wave[w];
+      if (w < wave) wbase += sw;
+      T += sw;
     }
     if (T == 0 && dr) {  // empty residual: draw from the target row
       dr = nullptr;
@@ -135,13 +188,13 @@ __global__ __launch_bounds__(kSpecThreads) void spec_accept_kernel(
       u64 acc = base;
       for (int q = 0; q < 4; ++q) {
         const int64_t i = 4 * tid + q;
-        const u64 s = i < NT ? s_tile[i] : 0;
-        if (acc + s > U) {
+        const u64 sq = i < NT ? s_tile[i] : 0;
+        if (acc + sq > U) {
           s_pick[0] = u64(i);
           s_pick[1] = acc;
           break;
         }
-        acc += s;
+        acc += sq;
       }
     }
     __syncthreads();
@@ -168,11 +221,25 @@ __global__ __launch_bounds__(kSpecThreads) void spec_accept_kernel(
   }
 }
 
+int64_t spec_tiles(int64_t V) { return (V + kSpecTile - 1) / kSpecTile; }
+
+size_t spec_workspace_bytes(int64_t B, int64_t V) { return size_t(B) * size_t(spec_tiles(V)) * 2 * sizeof(u64); }
+
 hipError_t launch_spec_accept(const float* target, const float* draft, const int32_t* tokens, const float* u_accept,
                               const float* u_draw, int64_t B, int64_t k, int64_t V, int32_t* n_kept, int32_t* out,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(spec_accept_kernel, dim3(unsigned(B)), dim3(kSpecThreads), 0, st, target, draft, tokens,
-                     u_accept, u_draw, k, V, n_kept, out);
+                              void* ws, hipStream_t st) {
+  const int64_t NT = spec_tiles(V);
+  // about 2048 workgroups of 4 wavefronts in all, each at least one tile per wavefront
+  int64_t P = (2048 + B - 1) / B;
+  const int64_t pmax = (NT + 3) / 4;
+  if (P > pmax) P = pmax;
+  if (P < 1) P = 1;
+  hipLaunchKernelGGL(spec_sums_kernel, dim3(unsigned(B), unsigned(P)), dim3(256), 0, st, target, draft, tokens,
+                     u_accept, k, V, NT, n_kept, out, reinterpret_cast<u64*>(ws));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(spec_draw_kernel, dim3(unsigned(B)), dim3(kSpecThreads), 0, st, target, draft, u_draw, k, V, NT,
+                     n_kept, out, reinterpret_cast<const u64*>(ws));
   return hipGetLastError();
 }
 
