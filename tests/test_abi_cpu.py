@@ -171,18 +171,22 @@ def test_kernel_path_choice():
         assert wqd.kernel_path(fmt, 257, 8192, 8192) == ("gemm", 4)   # a 5th 64-row block, no 2nd 256-row round
         assert wqd.kernel_path(fmt, 512, 4096, 4096) == ("gemm", 4)   # 256-row tiles: too few workgroups
     assert wqd.kernel_path("bf16", 129, 8192, 8192) == ("gemm", 8)    # 256-row tiles with an 8-way K split
-    assert wqd.kernel_path("fp8", 1024, 28672, 8192) == ("gemm", 4)
-    # BF16 from 192 rows on the 70B verify shapes: the tiled kernel that stages
-    # the weights in LDS as well (its time model is the faster one there) ...
+    # BF16 from 192 rows on the 70B verify shapes, FP8 where its time model puts
+    # it ahead (gate / down from 512 rows): the tiled kernel that stages the
+    # weights in LDS as well ...
     for M in (192, 257, 512, 1024):
         assert wqd.kernel_path("bf16", M, 28672, 8192) == ("gemm_lds", 8)
         assert wqd.kernel_path("bf16", M, 8192, 28672) == ("gemm_lds", 8)
-    # ... never below 192 rows, for K not a whole number of 32-k tiles, nor for FP8 / W4A16
+    for M in (512, 1024):
+        assert wqd.kernel_path("fp8", M, 28672, 8192) == ("gemm_lds", 8)
+        assert wqd.kernel_path("fp8", M, 8192, 28672) == ("gemm_lds", 8)
+    assert wqd.kernel_path("fp8", 1024, 8192, 8192) == ("gemm", 4)
+    # ... never below 192 rows, for K not a whole number of tiles, nor for W4A16
     assert wqd.kernel_path("bf16", 191, 28672, 8192)[0] == "gemm"
     assert wqd.kernel_path("bf16", 1024, 28672, 8208)[0] == "gemm"
-    for fmt in ("fp8", "w4a16"):
-        for M in (192, 512, 1024):
-            assert wqd.kernel_path(fmt, M, 28672, 8192)[0] == "gemm"
+    assert wqd.kernel_path("fp8", 1024, 28672, 8224)[0] == "gemm"
+    for M in (192, 512, 1024):
+        assert wqd.kernel_path("w4a16", M, 28672, 8192)[0] == "gemm"
     for M in (65, 1024):
         assert wqd.kernel_path("w4a16", M, 8192, 8192) == ("gemm", 8)
     # otherwise above 64 rows (N under 16 x 256): the LDS matrix-core kernel

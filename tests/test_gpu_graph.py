@@ -27,6 +27,7 @@ CASES = [
     ("w4a16", 300, 4104, 4096, "gemm"),      # x sums, K split
     ("bf16", 200, 4000, 1160, "gemm"),
     ("bf16", 513, 8208, 8224, "gemm_lds"),   # weights staged in LDS too, K split, ragged M and N
+    ("fp8", 1000, 8208, 8256, "gemm_lds"),   # the FP8 form: 3-way K split, ragged M and N
     ("w4a16", 100, 1000, 1152, "mfma"),
 ]
 

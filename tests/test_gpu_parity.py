@@ -304,16 +304,19 @@ def test_qgemm_tiled_256_rows_padded(fmt, N, K, M):
     compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("N,K,M,S", [(8208, 8224, 513, 2), (16392, 2048, 513, 1), (28672, 1056, 300, 1),
-                                     (12296, 4096, 777, 1), (11008, 4096, 777, 1)])
-def test_qgemm_tiled_lds(N, K, M, S):
-    """BF16 on the tiled kernel that stages x and the weights in LDS (256 x 256
-    tiles): ragged N inside a 16-row block and a last column block of one row
-    block, ragged M (a last row block of 1 or 9 rows), chunk counts leaving
-    each remainder of the 4-chunk loop (257 chunks split 129 + 128, 33, 64,
-    128), and a K split.  The oracle checks a sample of output columns,
-    the first and last ones included, over every row."""
-    fmt = "bf16"
+@pytest.mark.parametrize("fmt,N,K,M,S", [("bf16", 8208, 8224, 513, 2), ("bf16", 16392, 2048, 513, 1),
+                                         ("bf16", 28672, 1056, 300, 1), ("bf16", 12296, 4096, 777, 1),
+                                         ("bf16", 11008, 4096, 777, 1),
+                                         ("fp8", 8208, 8256, 1000, 3), ("fp8", 28672, 1088, 1023, 1),
+                                         ("fp8", 28680, 4096, 900, 1), ("fp8", 8200, 28672, 1024, 5),
+                                         ("fp8", 20488, 8192, 1023, 2)])
+def test_qgemm_tiled_lds(fmt, N, K, M, S):
+    """BF16 and FP8 on the tiled kernel that stages x and the weights in LDS
+    (256 x 256 tiles): ragged N inside a 16-row block and a last column block
+    of one row block, ragged M (last row blocks of 1 to 255 rows), chunk
+    counts leaving each remainder of the loop (BF16: 4 chunks of 32 k, FP8: 3
+    of 64 k), and K splits of 2 to 5.  The oracle checks a sample of output
+    columns, the first and last ones included, over every row."""
     assert wqd.kernel_path(fmt, M, N, K) == ("gemm_lds", 8)
     ws = wqd.workspace_bytes(fmt, M, N, K)
     assert (ws // (M * N * 4) if ws else 1) == S
@@ -327,6 +330,10 @@ def test_qgemm_tiled_lds(N, K, M, S):
     y = wqd.qgemm(x_dev(x), pw)
     torch.cuda.synchronize()
     compare_y(bf16_bits(y)[:, cols], oracle.qgemm_exact(x, qw), f"{fmt} lds M={M} N={N} K={K}")
+    if fmt == "fp8":  # the row scales of the sampled columns, bit for bit
+        _, sc, _ = wqd.unpack(pw)
+        torch.cuda.synchronize()
+        assert np.array_equal(sc.cpu().numpy()[cols].view(np.uint32), qw["scales"].view(np.uint32))
 
 
 def mfma_wide_shapes(fmt):

@@ -593,7 +593,7 @@ hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64
   a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.xs_bytes);
   hipError_t e;
   if (p.wm == 3) {
-    e = launch_gemm_lds(fmt, p, x, M, N, K, wp, y, a.part, swiglu, st);
+    e = launch_gemm_lds(fmt, p, x, M, N, K, wp, scales, y, a.part, swiglu, st);
   } else if (fmt == kFmtBF16) {
     e = launch_gm_fmt<kFmtBF16>(a, p, st);
   } else if (fmt == kFmtFP8) {

@@ -256,9 +256,166 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GlArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- FP8 weights
+// The same tile and wavefront layout; a chunk is one packed FP8 tile along K
+// (64 k, two matrix-core steps): 16 weight fragments (one per row block,
+// bytes 8 s .. 8 s + 7 of each lane's 16 codes are step s's 8 k) and 32 x
+// fragments (row block i, step s) in one 48 KiB stage, 3 stages.  With three
+// stages a chunk's operands are read from LDS at its start (no register copy
+// of the next chunk), so that each wavefront waits at the end of chunk c for
+// its loads of chunk c + 1, issued a whole chunk earlier.
+struct GlF8 {
+  static constexpr int TK = 64;
+  static constexpr int BUF = (16 + 32) * 64;  // uint4 per stage
+  static constexpr int DX = 4;                // x loads per wavefront and chunk (2 row blocks x 2 steps)
+  static constexpr int DPC = 2 + DX;
+  static constexpr int NS = 3;
+};
+
+struct GlState8 {
+  gl_f32x4_t acc[4][8];
+  uint4 w[8];
+  uint4 x[2][4];  // steps 0 and 1
+  __amdgpu_buffer_rsrc_t wres, xres;
+  uint32_t wvo[2];
+  uint32_t xvo[GlF8::DX];
+  int64_t kt0;
+  int lane, wave, wm, wn;
+};
+
+__device__ __forceinline__ void gl8_load_chunk(const GlState8& st, int c, uint4* buf) {
+  const uint32_t kt = uint32_t(st.kt0) + uint32_t(c);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) gl_dma(st.wres, buf + (2 * st.wave + u) * 64, st.wvo[u], kt * kTileBytes);
+#pragma unroll
+  for (int u = 0; u < GlF8::DX; ++u)
+    gl_dma(st.xres, buf + (16 + GlF8::DX * st.wave + u) * 64, st.xvo[u], kt * (GlF8::TK * 2));
+}
+
+template <int S>
+__device__ __forceinline__ void gl8_read_x(GlState8& st, const uint4* buf) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.x[S][i] = buf[(16 + (4 * st.wm + i) * 2 + S) * 64 + st.lane];
+}
+
+template <int S>
+__device__ __forceinline__ void gl8_mfmas(GlState8& st) {
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint4 wv = st.w[b];
+    const uint32_t w0 = S == 0 ? wv.x : wv.z, w1 = S == 0 ? wv.y : wv.w;
+    const uint4 bm = make_uint4(__builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(w0)),
+                                __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(w0)),
+                                __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(w1)),
+                                __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<true>(w1)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.acc[i][b] = gl_mfma(st.x[S][i], bm, st.acc[i][b]);
+  }
+}
+
+// Chunk c = (loop body start) + H: issue the loads of chunk c + 2 (into the
+// stage of chunk c - 1), read this chunk's weights and step-0 x, multiply
+// step 0 while reading step 1's x, multiply step 1, then wait for chunk c + 1
+// and meet the other wavefronts.
+template <int H>
+__device__ __forceinline__ void gl8_chunk(GlState8& st, uint4* const* sb, int c) {
+  constexpr int NS = GlF8::NS;
+  gl8_load_chunk(st, c + NS - 1, sb[(H + NS - 1) % NS]);
+  const uint4* buf = sb[H % NS];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) st.w[b] = buf[(8 * st.wn + b) * 64 + st.lane];
+  gl8_read_x<0>(st, buf);
+  gl8_read_x<1>(st, buf);
+  gl8_mfmas<0>(st);
+  gl8_mfmas<1>(st);
+  __builtin_amdgcn_sched_barrier(0);
+  gl_wait_barrier<GlF8::DPC * (NS - 2)>();
+}
+
+__global__ __launch_bounds__(512) void gemm_lds8_kernel(GlArgs a, const float* __restrict__ scales) {
+  constexpr int NS = GlF8::NS;
+  __shared__ uint4 s0[GlF8::BUF], s1[GlF8::BUF], s2[GlF8::BUF];
+  uint4* const sb[3] = {s0, s1, s2};
+  const int Lb = blockIdx.x, xcd = Lb & 7, wi = Lb >> 3;
+  const int nbn = (wi / a.MB) * 8 + xcd, mb = wi % a.MB;
+  if (nbn >= a.NBN) return;
+
+  GlState8 st;
+  st.lane = threadIdx.x & 63;
+  st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  st.wm = st.wave & 3;
+  st.wn = st.wave >> 2;
+  const int split = blockIdx.y;
+  const int c0 = split * a.cps;
+  const int nch = int(a.KT) - c0 < a.cps ? int(a.KT) - c0 : a.cps;
+  st.kt0 = c0;
+  const int64_t nb0 = int64_t(nbn) * 16, m0 = int64_t(mb) * 256;
+  const int64_t nbl = a.NB - nb0 < 16 ? a.NB - nb0 : 16;
+  st.wres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(a.w + nb0 * a.KT * (kTileBytes / 16)), 0,
+                                              uint32_t(nbl * a.KT * kTileBytes), 0x00020000);
+  st.xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, uint32_t(a.M * a.K * 2), 0x00020000);
+  {
+    const int kb = st.lane >> 4, j = st.lane & 15;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) st.wvo[u] = uint32_t((2 * st.wave + u) * a.KT * kTileBytes) + st.lane * 16;
+#pragma unroll
+    for (int u = 0; u < GlF8::DX; ++u) {
+      // fragment f = (x row block i, step s): lane (kb, j) holds the 8 k of
+      // row 16 i + j that pair with bytes 8 s .. 8 s + 7 of weight slice kb
+      const int f = GlF8::DX * st.wave + u, i = f / 2, sx = f % 2;
+      const int64_t row = m0 + 16 * i + j;
+      st.xvo[u] = row < a.M ? uint32_t((row * a.K + kb * 16 + 8 * sx) * 2) : 0x80000000u;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) st.acc[i][b] = gl_f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < NS; ++h)
+    for (int i = threadIdx.x; i < GlF8::BUF; i += 512) sb[h][i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+
+  // prologue: chunks 0 and 1 requested, chunk 0 landed
+  gl8_load_chunk(st, 0, sb[0]);
+  gl8_load_chunk(st, 1, sb[1]);
+  gl_wait_barrier<GlF8::DPC>();
+  int c = 0;
+  for (; c + NS <= nch; c += NS) {
+    gl8_chunk<0>(st, sb, c);
+    gl8_chunk<1>(st, sb, c + 1);
+    gl8_chunk<2>(st, sb, c + 2);
+  }
+  const int rest = nch - c;
+  if (rest > 0) gl8_chunk<0>(st, sb, c);
+  if (rest > 1) gl8_chunk<1>(st, sb, c + 1);
+  __builtin_amdgcn_s_waitcnt(0x7 << 4);
+
+  const int kb = st.lane >> 4, n = st.lane & 15;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int64_t nb = nb0 + 8 * st.wn + b;
+    const int64_t col = nb * kTileRows + n;
+    if (nb >= a.NB || col >= a.N) continue;
+    const float cs = a.S == 1 ? scales[col] : 1.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + (4 * st.wm + i) * 16 + 4 * kb + r;
+        if (row >= a.M) continue;
+        if (a.S > 1)
+          a.part[(int64_t(split) * a.M + row) * a.N + col] = st.acc[i][b][r];
+        else
+          store_out<8>(a.y, a.N, a.swiglu, row, col, st.acc[i][b][r] * cs, true);
+      }
+  }
+}
+
 hipError_t launch_gemm_lds(int fmt, const GmPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
-                           void* y, void* part, bool swiglu, hipStream_t st) {
-  if (fmt != kFmtBF16 || p.wm != 3 || K != p.KT * GlF::TK) return hipErrorInvalidValue;
+                           const void* scales, void* y, void* part, bool swiglu, hipStream_t st) {
+  if (p.wm != 3 || (fmt != kFmtBF16 && fmt != kFmtFP8) || K != p.KT * (fmt == kFmtFP8 ? GlF8::TK : GlF::TK))
+    return hipErrorInvalidValue;
   GlArgs a;
   a.x = reinterpret_cast<const uint16_t*>(x);
   a.y = reinterpret_cast<uint16_t*>(y);
@@ -275,7 +432,10 @@ hipError_t launch_gemm_lds(int fmt, const GmPlan& p, const void* x, int64_t M, i
   a.S = p.S;
   a.swiglu = swiglu;
   const dim3 grid(unsigned(ceil_div(p.NBN, int64_t(8)) * 8 * p.MB), unsigned(p.S));
-  hipLaunchKernelGGL(gemm_lds_kernel, grid, dim3(512), 0, st, a);
+  if (fmt == kFmtFP8)
+    hipLaunchKernelGGL(gemm_lds8_kernel, grid, dim3(512), 0, st, a, reinterpret_cast<const float*>(scales));
+  else
+    hipLaunchKernelGGL(gemm_lds_kernel, grid, dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ hipError_t launch_gemv_sk(int fmt, const SkPlan& p, const void* x, int64_t M, in
 // The tiled kernel with the weights staged in LDS as well (GmPlan::wm == 3,
 // BF16); launch_gemm calls it.
 hipError_t launch_gemm_lds(int fmt, const GmPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
-                           void* y, void* part, bool swiglu, hipStream_t st);
+                           const void* scales, void* y, void* part, bool swiglu, hipStream_t st);
 hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64_t N, int64_t K, const void* wp,
                        const void* scales, const void* zeros, void* y, void* ws, bool swiglu, hipStream_t st);
 // y = sum over s < S of part[s] (float32 [S][M][N], added in split order), FP8

@@ -276,19 +276,24 @@ static int plan_gemm_wm(int fmt, int64_t M, int64_t N, int64_t K, const PackedSi
   return kOK;
 }
 
-// The tiled kernel with both operands staged in LDS (wm = 3, BF16): 256 x 256
-// tiles, one workgroup per compute unit, chunks of one packed tile (32 k)
-// along K.  Time model t = c0 + cps * a * rounds + the split partials
-// (written and read once at bw), fitted by least squares to the kernel on the
-// 70B q, gate and down shapes at 192-1024 rows (rms error ~10%).  An FP8 form
-// (64-k chunks, three 48 KiB stages) measured 7-38% slower than the tiled
-// kernel that takes FP8 weights straight into registers, so FP8 keeps that.
-constexpr double kGlC0 = 13.0, kGlA = 0.89, kGlBw = 3.75;
+// The tiled kernel with both operands staged in LDS (wm = 3; BF16 and FP8):
+// 256 x 256 tiles, one workgroup per compute unit, chunks of one packed tile
+// along K (32 k BF16, 64 k FP8).  Time model t = c0 + cps * a * rounds + the
+// split partials (written and read once at bw), fitted by least squares to
+// the kernel on the 70B q, gate and down shapes at 192-1024 rows (rms error
+// ~10% BF16, ~4% FP8).
+struct GlCost {
+  double c0, a, bw;
+};
+static constexpr GlCost kGlCost[2] = {
+    {13.0, 0.89, 3.75},   // BF16
+    {12.07, 1.53, 5.15},  // FP8
+};
 constexpr int64_t kGlMinM = 192;
 
 static int plan_gemm_lds(int fmt, int64_t M, int64_t N, int64_t K, const PackedSizes& ps, GmPlan* out,
                          double* t_us) {
-  if (fmt != kFmtBF16) return kEUnsupported;
+  if (fmt != kFmtBF16 && fmt != kFmtFP8) return kEUnsupported;
   // fitted and measured from 192 rows (below, most of a 256-row tile is padding)
   if (M < kGlMinM) return kEUnsupported;
   // K a whole number of tiles (no x piece of a tile lies past K)
@@ -311,7 +316,8 @@ static int plan_gemm_lds(int fmt, int64_t M, int64_t N, int64_t K, const PackedS
   for (int64_t s = 1; s <= max_s; ++s) {
     const int64_t cps = ceil_div(p.nchunks, s), se = ceil_div(p.nchunks, cps);
     const int64_t rounds = ceil_div(tiles * se, kComputeUnits);
-    const double t = kGlC0 + double(cps) * kGlA * double(rounds) + (se > 1 ? double(se) * mn8 / (kGlBw * 1.0e6) : 0.0);
+    const GlCost& gc = kGlCost[fmt == kFmtFP8];
+    const double t = gc.c0 + double(cps) * gc.a * double(rounds) + (se > 1 ? double(se) * mn8 / (gc.bw * 1.0e6) : 0.0);
     if (s == 1 || t < 0.98 * best) {
       best = t;
       S = se;
