@@ -137,7 +137,7 @@ enum wqd_path {
     WQD_PATH_MC = 3,      /* streaming, bf16 matrix cores, x fragments read per tile */
     WQD_PATH_SKINNY = 4,  /* bf16 matrix cores, x staged in LDS by a producer wavefront, shared by 7-14 row blocks */
     WQD_PATH_GEMM = 5,    /* bf16 matrix cores, 64 or 256 x 256 tiles of y, x staged in LDS, dequant on load */
-    WQD_PATH_GEMM_LDS = 6 /* bf16 matrix cores, 256 x 256 tiles of y, x and the weights staged in LDS (BF16) */
+    WQD_PATH_GEMM_LDS = 6 /* bf16 matrix cores, 256 x 256 tiles of y (FP8 also 256 x 224), x and the weights staged in LDS */
 };
 
 /*
@@ -146,6 +146,17 @@ enum wqd_path {
  * NULL).  Same validation as wqd_qgemm's shape checks.
  */
 int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* waves);
+
+/*
+ * Host-only: for a shape that wqd_qgemm serves with a tiled matrix-core kernel
+ * (WQD_PATH_GEMM or WQD_PATH_GEMM_LDS), the tile of y each workgroup computes
+ * (*rows x *cols: 64, 128 or 256 rows; 256 columns, or 224 on the FP8
+ * LDS-staged kernel where those fill the compute units' rounds better) and
+ * the number of K splits (*splits; 1 when K is not split).  Any output pointer
+ * may be NULL.  Errors: those of wqd_kernel_path, and WQD_E_UNSUPPORTED for a
+ * shape served by another kernel family.
+ */
+int wqd_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K, int* rows, int* cols, int* splits);
 
 /*
  * Setup (not on the decode hot path): quantise W (device, float32 [N, K]

@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "wqd.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(wqd.LIB_PATH), reason="libwqd.so not built")
 
-OK, E_ARG, E_SHAPE, E_ALIGN, E_WS = 0, 1, 2, 3, 4
+OK, E_ARG, E_SHAPE, E_ALIGN, E_WS, E_UNSUPPORTED = 0, 1, 2, 3, 4, 6
 
 
 def header_functions():
@@ -202,6 +202,25 @@ def test_kernel_path_choice():
     assert wqd.workspace_bytes("bf16", 1024, 28672, 8192) == 0                  # 448 tiles of 256 x 256: no split
     # x rows spanning 2 GiB: the LDS matrix-core kernel
     assert wqd.kernel_path("bf16", 65536, 64, 16384)[0] == "mfma"
+    # the tiled kernels' tile of y and K split: FP8 on the LDS-staged kernel
+    # takes 224-column tiles where they fill the rounds of 256 compute units
+    # better (the 70B gate: 512 tiles of 256 x 224 in two whole rounds instead
+    # of 448 of 256 x 256 in 1.75), 256 columns elsewhere
+    assert wqd.gemm_tile("fp8", 1024, 28672, 8192) == (256, 224, 1)
+    assert wqd.gemm_tile("fp8", 512, 28672, 8192) == (256, 224, 1)
+    assert wqd.gemm_tile("fp8", 1024, 8192, 28672) == (256, 256, 2)
+    assert wqd.gemm_tile("fp8", 1024, 8192, 8192) == (64, 256, 1)
+    assert wqd.gemm_tile("bf16", 1024, 28672, 8192) == (256, 256, 1)
+    assert wqd.gemm_tile("w4a16", 1024, 28672, 8192)[:2] == (128, 256)
+    assert wqd.gemm_tile("w4a16", 100, 28672, 8192)[:2] == (64, 256)
+    for fmt, M, N, K in (("fp8", 1024, 28672, 8192), ("bf16", 128, 8192, 28672), ("w4a16", 384, 8192, 28672)):
+        ws = wqd.workspace_bytes(fmt, M, N, K)
+        S = wqd.gemm_tile(fmt, M, N, K)[2]
+        assert S >= 1 and ws - (ws % (M * N * 4)) == (S * M * N * 4 if S > 1 else 0)
+    r = ctypes.c_int()
+    assert wqd.lib().wqd_gemm_tile(2, 1, 8192, 8192, ctypes.byref(r), None, None) == E_UNSUPPORTED  # broadcast
+    assert wqd.lib().wqd_gemm_tile(9, 1024, 8192, 8192, None, None, None) == E_ARG
+    assert wqd.lib().wqd_gemm_tile(0, 1024, 28672, 8192, None, None, None) == 0
     L = wqd.lib()
     p = ctypes.c_int()
     assert L.wqd_kernel_path(2, 1, 64, 128, None, None) == E_ARG

@@ -131,6 +131,18 @@ int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* wa
   return WQD_OK;
 }
 
+int wqd_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K, int* rows, int* cols, int* splits) {
+  wqd::Choice c;
+  int st = wqd::choose_path(fmt, M, N, K, &c);
+  if (st != wqd::kOK) return st;
+  if (c.path != wqd::kPathGemm && c.path != wqd::kPathGemmLds) return WQD_E_UNSUPPORTED;
+  const wqd::GmPlan& p = c.gm;
+  if (rows) *rows = p.wm == 3 ? 256 : p.wm == 2 ? (fmt == wqd::kFmtW4 ? 128 : 256) : 64;
+  if (cols) *cols = p.wm == 3 ? 32 * p.rbw : 256;
+  if (splits) *splits = p.S;
+  return WQD_OK;
+}
+
 int wqd_pack_weights(int fmt, const float* W, int64_t N, int64_t K, void* w_packed, void* scales, void* zeros,
                      void* stream) {
   wqd::PackedSizes ps;

@@ -257,7 +257,10 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GlArgs a) {
 }
 
 // ---------------------------------------------------------------- FP8 weights
-// The same tile and wavefront layout; a chunk is one packed FP8 tile along K
+// The same tile and wavefront layout, 256 columns (RBW = 8 weight row blocks
+// per wavefront) or 224 (RBW = 7, where those fill the compute units' rounds
+// better: the loads of the two unused weight slots lie outside the weight
+// resource and read nothing); a chunk is one packed FP8 tile along K
 // (64 k, two matrix-core steps): 16 weight fragments (one per row block,
 // bytes 8 s .. 8 s + 7 of each lane's 16 codes are step s's 8 k) and 32 x
 // fragments (row block i, step s) in one 48 KiB stage, 3 stages.  With three
@@ -272,9 +275,10 @@ struct GlF8 {
   static constexpr int NS = 3;
 };
 
+template <int RBW>
 struct GlState8 {
-  gl_f32x4_t acc[4][8];
-  uint4 w[8];
+  gl_f32x4_t acc[4][RBW];
+  uint4 w[RBW];
   uint4 x[2][4];  // steps 0 and 1
   __amdgpu_buffer_rsrc_t wres, xres;
   uint32_t wvo[2];
@@ -283,7 +287,8 @@ struct GlState8 {
   int lane, wave, wm, wn;
 };
 
-__device__ __forceinline__ void gl8_load_chunk(const GlState8& st, int c, uint4* buf) {
+template <int RBW>
+__device__ __forceinline__ void gl8_load_chunk(const GlState8<RBW>& st, int c, uint4* buf) {
   const uint32_t kt = uint32_t(st.kt0) + uint32_t(c);
 #pragma unroll
   for (int u = 0; u < 2; ++u) gl_dma(st.wres, buf + (2 * st.wave + u) * 64, st.wvo[u], kt * kTileBytes);
@@ -292,16 +297,16 @@ __device__ __forceinline__ void gl8_load_chunk(const GlState8& st, int c, uint4*
     gl_dma(st.xres, buf + (16 + GlF8::DX * st.wave + u) * 64, st.xvo[u], kt * (GlF8::TK * 2));
 }
 
-template <int S>
-__device__ __forceinline__ void gl8_read_x(GlState8& st, const uint4* buf) {
+template <int S, int RBW>
+__device__ __forceinline__ void gl8_read_x(GlState8<RBW>& st, const uint4* buf) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.x[S][i] = buf[(16 + (4 * st.wm + i) * 2 + S) * 64 + st.lane];
 }
 
-template <int S>
-__device__ __forceinline__ void gl8_mfmas(GlState8& st) {
+template <int S, int RBW>
+__device__ __forceinline__ void gl8_mfmas(GlState8<RBW>& st) {
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
+  for (int b = 0; b < RBW; ++b) {
     const uint4 wv = st.w[b];
     const uint32_t w0 = S == 0 ? wv.x : wv.z, w1 = S == 0 ? wv.y : wv.w;
     const uint4 bm = make_uint4(__builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(w0)),
@@ -317,13 +322,13 @@ __device__ __forceinline__ void gl8_mfmas(GlState8& st) {
 // stage of chunk c - 1), read this chunk's weights and step-0 x, multiply
 // step 0 while reading step 1's x, multiply step 1, then wait for chunk c + 1
 // and meet the other wavefronts.
-template <int H>
-__device__ __forceinline__ void gl8_chunk(GlState8& st, uint4* const* sb, int c) {
+template <int H, int RBW>
+__device__ __forceinline__ void gl8_chunk(GlState8<RBW>& st, uint4* const* sb, int c) {
   constexpr int NS = GlF8::NS;
   gl8_load_chunk(st, c + NS - 1, sb[(H + NS - 1) % NS]);
   const uint4* buf = sb[H % NS];
 #pragma unroll
-  for (int b = 0; b < 8; ++b) st.w[b] = buf[(8 * st.wn + b) * 64 + st.lane];
+  for (int b = 0; b < RBW; ++b) st.w[b] = buf[(RBW * st.wn + b) * 64 + st.lane];
   gl8_read_x<0>(st, buf);
   gl8_read_x<1>(st, buf);
   gl8_mfmas<0>(st);
@@ -332,6 +337,7 @@ __device__ __forceinline__ void gl8_chunk(GlState8& st, uint4* const* sb, int c)
   gl_wait_barrier<GlF8::DPC * (NS - 2)>();
 }
 
+template <int RBW>
 __global__ __launch_bounds__(512) void gemm_lds8_kernel(GlArgs a, const float* __restrict__ scales) {
   constexpr int NS = GlF8::NS;
   __shared__ uint4 s0[GlF8::BUF], s1[GlF8::BUF], s2[GlF8::BUF];
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(512) void gemm_lds8_kernel(GlArgs a, const float* _
   const int nbn = (wi / a.MB) * 8 + xcd, mb = wi % a.MB;
   if (nbn >= a.NBN) return;
 
-  GlState8 st;
+  GlState8<RBW> st;
   st.lane = threadIdx.x & 63;
   st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   st.wm = st.wave & 3;
@@ -349,8 +355,11 @@ __global__ __launch_bounds__(512) void gemm_lds8_kernel(GlArgs a, const float* _
   const int c0 = split * a.cps;
   const int nch = int(a.KT) - c0 < a.cps ? int(a.KT) - c0 : a.cps;
   st.kt0 = c0;
-  const int64_t nb0 = int64_t(nbn) * 16, m0 = int64_t(mb) * 256;
-  const int64_t nbl = a.NB - nb0 < 16 ? a.NB - nb0 : 16;
+  // the tile's 2 RBW weight row blocks (slots past them, and row blocks past
+  // the matrix, are out of range of the resource: their loads read nothing
+  // and their LDS slots are never multiplied)
+  const int64_t nb0 = int64_t(nbn) * (2 * RBW), m0 = int64_t(mb) * 256;
+  const int64_t nbl = a.NB - nb0 < 2 * RBW ? a.NB - nb0 : 2 * RBW;
   st.wres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(a.w + nb0 * a.KT * (kTileBytes / 16)), 0,
                                               uint32_t(nbl * a.KT * kTileBytes), 0x00020000);
   st.xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, uint32_t(a.M * a.K * 2), 0x00020000);
@@ -370,7 +379,7 @@ __global__ __launch_bounds__(512) void gemm_lds8_kernel(GlArgs a, const float* _
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) st.acc[i][b] = gl_f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < RBW; ++b) st.acc[i][b] = gl_f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int h = 0; h < NS; ++h)
     for (int i = threadIdx.x; i < GlF8::BUF; i += 512) sb[h][i] = make_uint4(0u, 0u, 0u, 0u);
@@ -382,19 +391,19 @@ __global__ __launch_bounds__(512) void gemm_lds8_kernel(GlArgs a, const float* _
   gl_wait_barrier<GlF8::DPC>();
   int c = 0;
   for (; c + NS <= nch; c += NS) {
-    gl8_chunk<0>(st, sb, c);
-    gl8_chunk<1>(st, sb, c + 1);
-    gl8_chunk<2>(st, sb, c + 2);
+    gl8_chunk<0, RBW>(st, sb, c);
+    gl8_chunk<1, RBW>(st, sb, c + 1);
+    gl8_chunk<2, RBW>(st, sb, c + 2);
   }
   const int rest = nch - c;
-  if (rest > 0) gl8_chunk<0>(st, sb, c);
-  if (rest > 1) gl8_chunk<1>(st, sb, c + 1);
+  if (rest > 0) gl8_chunk<0, RBW>(st, sb, c);
+  if (rest > 1) gl8_chunk<1, RBW>(st, sb, c + 1);
   __builtin_amdgcn_s_waitcnt(0x7 << 4);
 
   const int kb = st.lane >> 4, n = st.lane & 15;
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int64_t nb = nb0 + 8 * st.wn + b;
+  for (int b = 0; b < RBW; ++b) {
+    const int64_t nb = nb0 + RBW * st.wn + b;
     const int64_t col = nb * kTileRows + n;
     if (nb >= a.NB || col >= a.N) continue;
     const float cs = a.S == 1 ? scales[col] : 1.f;
@@ -416,6 +425,9 @@ hipError_t launch_gemm_lds(int fmt, const GmPlan& p, const void* x, int64_t M, i
                            const void* scales, void* y, void* part, bool swiglu, hipStream_t st) {
   if (p.wm != 3 || (fmt != kFmtBF16 && fmt != kFmtFP8) || K != p.KT * (fmt == kFmtFP8 ? GlF8::TK : GlF::TK))
     return hipErrorInvalidValue;
+  // column blocks of 2 rbw weight row blocks: 16 for BF16, 16 or 14 for FP8
+  if (!(p.rbw == 8 || (fmt == kFmtFP8 && p.rbw == 7)) || p.NBN != ceil_div(p.NB, int64_t(2 * p.rbw)))
+    return hipErrorInvalidValue;
   GlArgs a;
   a.x = reinterpret_cast<const uint16_t*>(x);
   a.y = reinterpret_cast<uint16_t*>(y);
@@ -432,8 +444,10 @@ hipError_t launch_gemm_lds(int fmt, const GmPlan& p, const void* x, int64_t M, i
   a.S = p.S;
   a.swiglu = swiglu;
   const dim3 grid(unsigned(ceil_div(p.NBN, int64_t(8)) * 8 * p.MB), unsigned(p.S));
-  if (fmt == kFmtFP8)
-    hipLaunchKernelGGL(gemm_lds8_kernel, grid, dim3(512), 0, st, a, reinterpret_cast<const float*>(scales));
+  if (fmt == kFmtFP8 && p.rbw == 7)
+    hipLaunchKernelGGL(gemm_lds8_kernel<7>, grid, dim3(512), 0, st, a, reinterpret_cast<const float*>(scales));
+  else if (fmt == kFmtFP8)
+    hipLaunchKernelGGL(gemm_lds8_kernel<8>, grid, dim3(512), 0, st, a, reinterpret_cast<const float*>(scales));
   else
     hipLaunchKernelGGL(gemm_lds_kernel, grid, dim3(512), 0, st, a);
   return hipGetLastError();

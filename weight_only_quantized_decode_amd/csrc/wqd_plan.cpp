@@ -291,6 +291,13 @@ static constexpr GlCost kGlCost[2] = {
 };
 constexpr int64_t kGlMinM = 192;
 
+// Relative time of a chunk on 224-column tiles (14 weight row blocks, 7 per
+// wavefront) against 256-column ones (FP8 only).
+#ifndef WQD_GL_W7
+#define WQD_GL_W7 0.95
+#endif
+constexpr double kGlW7 = WQD_GL_W7;
+
 static int plan_gemm_lds(int fmt, int64_t M, int64_t N, int64_t K, const PackedSizes& ps, GmPlan* out,
                          double* t_us) {
   if (fmt != kFmtBF16 && fmt != kFmtFP8) return kEUnsupported;
@@ -304,25 +311,41 @@ static int plan_gemm_lds(int fmt, int64_t M, int64_t N, int64_t K, const PackedS
   p.NB = ps.NB;
   p.KT = ps.KT;
   p.wm = 3;
-  p.NBN = ceil_div(p.NB, 16);
   p.MB = ceil_div(M, 256);
   p.Mp = p.MB * 256;
   p.nchunks = p.KT;
-  const int64_t tiles = p.NBN * p.MB;
   const double mn8 = double(M) * double(N) * 8.0;
   const int64_t max_s = p.nchunks / 8 < 1 ? 1 : (p.nchunks / 8 > 8 ? 8 : p.nchunks / 8);
+  const GlCost& gc = kGlCost[fmt == kFmtFP8];
+  // the tile width (FP8: 256 or 224 columns, whichever fills the compute
+  // units' rounds better) and the K split
   double best = 0.0;
   int64_t S = 1;
-  for (int64_t s = 1; s <= max_s; ++s) {
-    const int64_t cps = ceil_div(p.nchunks, s), se = ceil_div(p.nchunks, cps);
-    const int64_t rounds = ceil_div(tiles * se, kComputeUnits);
-    const GlCost& gc = kGlCost[fmt == kFmtFP8];
-    const double t = gc.c0 + double(cps) * gc.a * double(rounds) + (se > 1 ? double(se) * mn8 / (gc.bw * 1.0e6) : 0.0);
-    if (s == 1 || t < 0.98 * best) {
-      best = t;
-      S = se;
+  int rbw = 8;
+  bool first = true;
+#ifdef WQD_GL_FORCE_RBW
+  const int w_hi = fmt == kFmtFP8 ? WQD_GL_FORCE_RBW : 8, w_lo = w_hi;  // measurement builds only
+#else
+  const int w_hi = 8, w_lo = fmt == kFmtFP8 ? 7 : 8;
+#endif
+  for (int w = w_hi; w >= w_lo; --w) {
+    const int64_t tiles = ceil_div(p.NB, int64_t(2 * w)) * p.MB;
+    const double fw = w == 8 ? 1.0 : kGlW7;
+    for (int64_t s = 1; s <= max_s; ++s) {
+      const int64_t cps = ceil_div(p.nchunks, s), se = ceil_div(p.nchunks, cps);
+      const int64_t rounds = ceil_div(tiles * se, kComputeUnits);
+      const double t =
+          gc.c0 + double(cps) * gc.a * fw * double(rounds) + (se > 1 ? double(se) * mn8 / (gc.bw * 1.0e6) : 0.0);
+      if (first || t < 0.98 * best) {
+        best = t;
+        S = se;
+        rbw = w;
+        first = false;
+      }
     }
   }
+  p.rbw = rbw;
+  p.NBN = ceil_div(p.NB, int64_t(2 * rbw));
   p.cps = ceil_div(p.nchunks, S);
   p.S = int(ceil_div(p.nchunks, p.cps));
   p.ws_bytes = p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;

@@ -127,6 +127,7 @@ constexpr int64_t kGmMinNBN = 16;
 struct GmPlan {
   int64_t NB, KT, NBN, MB, nchunks, cps, Mp;
   int wm, S;
+  int rbw;  // LDS-staged form (wm 3): weight row blocks per wavefront, a column block being 2 rbw of them
   size_t xs_bytes, ws_bytes;
 };
 
