@@ -203,10 +203,10 @@ def test_kernel_path_choice():
     # x rows spanning 2 GiB: the LDS matrix-core kernel
     assert wqd.kernel_path("bf16", 65536, 64, 16384)[0] == "mfma"
     # the tiled kernels' tile of y and K split: FP8 on the LDS-staged kernel
-    # takes 224-column tiles where they fill the rounds of 256 compute units
-    # better (the 70B gate: 512 tiles of 256 x 224 in two whole rounds instead
-    # of 448 of 256 x 256 in 1.75), 256 columns elsewhere
-    assert wqd.gemm_tile("fp8", 1024, 28672, 8192) == (256, 224, 1)
+    # takes 256 x 224 or 128 x 448 tiles where they fill the rounds of the 8
+    # XCDs' 32 compute units better (the 70B gate at 1024 rows: 512 tiles in
+    # two whole rounds instead of 448 of 256 x 256 in 1.75), 256 x 256 elsewhere
+    assert wqd.gemm_tile("fp8", 1024, 28672, 8192) == (128, 448, 1)
     assert wqd.gemm_tile("fp8", 512, 28672, 8192) == (256, 224, 1)
     assert wqd.gemm_tile("fp8", 1024, 8192, 28672) == (256, 256, 2)
     assert wqd.gemm_tile("fp8", 1024, 8192, 8192) == (64, 256, 1)

@@ -304,24 +304,26 @@ def test_qgemm_tiled_256_rows_padded(fmt, N, K, M):
     compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("fmt,N,K,M,S,C", [("bf16", 8208, 8224, 513, 2, 256), ("bf16", 16392, 2048, 513, 1, 256),
-                                           ("bf16", 28672, 1056, 300, 1, 256), ("bf16", 12296, 4096, 777, 1, 256),
-                                           ("bf16", 11008, 4096, 777, 1, 256),
-                                           ("fp8", 8208, 8256, 1000, 3, 224), ("fp8", 28672, 1088, 1023, 1, 224),
-                                           ("fp8", 28680, 4096, 900, 1, 256), ("fp8", 8200, 28672, 1024, 5, 224),
-                                           ("fp8", 20488, 8192, 1023, 2, 224), ("fp8", 28672, 8192, 1024, 1, 224),
-                                           ("fp8", 13456, 2048, 1000, 1, 224)])
-def test_qgemm_tiled_lds(fmt, N, K, M, S, C):
+@pytest.mark.parametrize("fmt,N,K,M,S,R,C", [
+    ("bf16", 8208, 8224, 513, 2, 256, 256), ("bf16", 16392, 2048, 513, 1, 256, 256),
+    ("bf16", 28672, 1056, 300, 1, 256, 256), ("bf16", 12296, 4096, 777, 1, 256, 256),
+    ("bf16", 11008, 4096, 777, 1, 256, 256),
+    ("fp8", 8208, 8256, 1000, 3, 256, 224), ("fp8", 28672, 1088, 1023, 1, 256, 224),
+    ("fp8", 28680, 4096, 900, 1, 256, 256), ("fp8", 8200, 28672, 1024, 3, 256, 224),
+    ("fp8", 20488, 8192, 1023, 2, 256, 224), ("fp8", 13456, 2048, 1000, 1, 256, 224),
+    ("fp8", 28672, 8192, 1024, 1, 128, 448), ("fp8", 28664, 8192, 1000, 1, 128, 448),
+    ("fp8", 29104, 4096, 777, 1, 128, 448), ("fp8", 57352, 2048, 777, 1, 128, 448)])
+def test_qgemm_tiled_lds(fmt, N, K, M, S, R, C):
     """BF16 and FP8 on the tiled kernel that stages x and the weights in LDS
-    (256-row tiles, 256 columns or for FP8 224): ragged N inside a 16-row
-    block, last column blocks of one row block (of 16 and of 14) and of 7 or 9,
-    ragged M (last row blocks of 1 to 255 rows), chunk counts leaving each
-    remainder of the loop (BF16: 4 chunks of 32 k, FP8: 3 of 64 k), and K
-    splits of 2 to 5.  The oracle checks a sample of output columns, the first
-    and last ones and those on either side of the first column blocks' edges
-    included, over every row."""
+    (R x C tiles: 256 x 256, for FP8 also 256 x 224 and 128 x 448): ragged N
+    inside a 16-row block, last column blocks of one row block (of 16, 14 and
+    28) and of 7, 9 or 27, ragged M (last row blocks of 1 to 255 rows), chunk
+    counts leaving each remainder of the loop (BF16: 4 chunks of 32 k, FP8: 3
+    of 64 k), and K splits of 2 and 3.  The oracle checks a sample of output
+    columns, the first and last ones and those on either side of the first
+    column blocks' edges included, over every row."""
     assert wqd.kernel_path(fmt, M, N, K) == ("gemm_lds", 8)
-    assert wqd.gemm_tile(fmt, M, N, K) == (256, C, S)
+    assert wqd.gemm_tile(fmt, M, N, K) == (R, C, S)
     ws = wqd.workspace_bytes(fmt, M, N, K)
     assert (ws // (M * N * 4) if ws else 1) == S
     W = I.w_host(6300 + N + K, N, K)

@@ -137,8 +137,8 @@ int wqd_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K, int* rows, int* cols
   if (st != wqd::kOK) return st;
   if (c.path != wqd::kPathGemm && c.path != wqd::kPathGemmLds) return WQD_E_UNSUPPORTED;
   const wqd::GmPlan& p = c.gm;
-  if (rows) *rows = p.wm == 3 ? 256 : p.wm == 2 ? (fmt == wqd::kFmtW4 ? 128 : 256) : 64;
-  if (cols) *cols = p.wm == 3 ? 32 * p.rbw : 256;
+  if (rows) *rows = p.wm == 3 ? 64 * p.lwr : p.wm == 2 ? (fmt == wqd::kFmtW4 ? 128 : 256) : 64;
+  if (cols) *cols = p.wm == 3 ? 16 * (8 / p.lwr) * p.rbw : 256;
   if (splits) *splits = p.S;
   return WQD_OK;
 }

@@ -269,42 +269,59 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GlArgs a) {
 // its loads of chunk c + 1, issued a whole chunk earlier.
 struct GlF8 {
   static constexpr int TK = 64;
-  static constexpr int BUF = (16 + 32) * 64;  // uint4 per stage
-  static constexpr int DX = 4;                // x loads per wavefront and chunk (2 row blocks x 2 steps)
-  static constexpr int DPC = 2 + DX;
+  static constexpr int BUF = 48 * 64;  // uint4 per stage: weight slots, then x fragments
+  static constexpr int DPC = 6;        // loads per wavefront and chunk
   static constexpr int NS = 3;
 };
 
-template <int RBW>
+// Tile shapes: WRM wavefront rows of 64 rows (4: 256-row tiles, 2: 128-row
+// tiles) by 8 / WRM wavefront columns of RBW weight row blocks.  A stage holds
+// WS weight slots (the tile's WN RBW row blocks, the rest out of range) and
+// the 2 XR x fragments of the tile's rows, filled by DW weight and DX x loads
+// per wavefront.
+template <int RBW, int WRM>
+struct GlT8 {
+  static constexpr int WN = 8 / WRM;
+  static constexpr int XR = 4 * WRM;         // x row blocks per tile
+  static constexpr int DX = XR / 4;          // x loads per wavefront and chunk (XR blocks x 2 steps)
+  static constexpr int DW = GlF8::DPC - DX;  // weight loads per wavefront and chunk
+  static constexpr int WS = 8 * DW;          // weight slots per stage
+  static_assert(WN * RBW <= WS && (WS + 2 * XR) * 64 == GlF8::BUF, "stage layout");
+};
+
+template <int RBW, int WRM>
 struct GlState8 {
+  using T = GlT8<RBW, WRM>;
   gl_f32x4_t acc[4][RBW];
   uint4 w[RBW];
   uint4 x[2][4];  // steps 0 and 1
   __amdgpu_buffer_rsrc_t wres, xres;
-  uint32_t wvo[2];
-  uint32_t xvo[GlF8::DX];
+  uint32_t wvo[T::DW];
+  uint32_t xvo[T::DX];
   int64_t kt0;
   int lane, wave, wm, wn;
 };
 
-template <int RBW>
-__device__ __forceinline__ void gl8_load_chunk(const GlState8<RBW>& st, int c, uint4* buf) {
+template <int RBW, int WRM>
+__device__ __forceinline__ void gl8_load_chunk(const GlState8<RBW, WRM>& st, int c, uint4* buf) {
+  using T = GlT8<RBW, WRM>;
   const uint32_t kt = uint32_t(st.kt0) + uint32_t(c);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) gl_dma(st.wres, buf + (2 * st.wave + u) * 64, st.wvo[u], kt * kTileBytes);
+  for (int u = 0; u < T::DW; ++u) gl_dma(st.wres, buf + (T::DW * st.wave + u) * 64, st.wvo[u], kt * kTileBytes);
 #pragma unroll
-  for (int u = 0; u < GlF8::DX; ++u)
-    gl_dma(st.xres, buf + (16 + GlF8::DX * st.wave + u) * 64, st.xvo[u], kt * (GlF8::TK * 2));
+  for (int u = 0; u < T::DX; ++u)
+    gl_dma(st.xres, buf + (T::WS + T::DX * st.wave + u) * 64, st.xvo[u], kt * (GlF8::TK * 2));
 }
 
-template <int S, int RBW>
-__device__ __forceinline__ void gl8_read_x(GlState8<RBW>& st, const uint4* buf) {
+template <int S, int RBW, int WRM>
+__device__ __forceinline__ void gl8_read_x(GlState8<RBW, WRM>& st, const uint4* buf) {
+  using T = GlT8<RBW, WRM>;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) st.x[S][i] = buf[(16 + (4 * st.wm + i) * 2 + S) * 64 + st.lane];
+  for (int i = 0; i < 4; ++i) st.x[S][i] = buf[(T::WS + (4 * st.wm + i) * 2 + S) * 64 + st.lane];
 }
 
-template <int S, int RBW>
-__device__ __forceinline__ void gl8_mfmas(GlState8<RBW>& st) {
+template <int S, int RBW, int WRM>
+__device__ __forceinline__ void gl8_mfmas(GlState8<RBW, WRM>& st) {
 #pragma unroll
   for (int b = 0; b < RBW; ++b) {
     const uint4 wv = st.w[b];
@@ -322,8 +339,8 @@ __device__ __forceinline__ void gl8_mfmas(GlState8<RBW>& st) {
 // stage of chunk c - 1), read this chunk's weights and step-0 x, multiply
 // step 0 while reading step 1's x, multiply step 1, then wait for chunk c + 1
 // and meet the other wavefronts.
-template <int H, int RBW>
-__device__ __forceinline__ void gl8_chunk(GlState8<RBW>& st, uint4* const* sb, int c) {
+template <int H, int RBW, int WRM>
+__device__ __forceinline__ void gl8_chunk(GlState8<RBW, WRM>& st, uint4* const* sb, int c) {
   constexpr int NS = GlF8::NS;
   gl8_load_chunk(st, c + NS - 1, sb[(H + NS - 1) % NS]);
   const uint4* buf = sb[H % NS];
@@ -337,8 +354,9 @@ __device__ __forceinline__ void gl8_chunk(GlState8<RBW>& st, uint4* const* sb, i
   gl_wait_barrier<GlF8::DPC * (NS - 2)>();
 }
 
-template <int RBW>
+template <int RBW, int WRM>
 __global__ __launch_bounds__(512) void gemm_lds8_kernel(GlArgs a, const float* __restrict__ scales) {
+  using T = GlT8<RBW, WRM>;
   constexpr int NS = GlF8::NS;
   __shared__ uint4 s0[GlF8::BUF], s1[GlF8::BUF], s2[GlF8::BUF];
   uint4* const sb[3] = {s0, s1, s2};
@@ -346,32 +364,32 @@ __global__ __launch_bounds__(512) void gemm_lds8_kernel(GlArgs a, const float* _
   const int nbn = (wi / a.MB) * 8 + xcd, mb = wi % a.MB;
   if (nbn >= a.NBN) return;
 
-  GlState8<RBW> st;
+  GlState8<RBW, WRM> st;
   st.lane = threadIdx.x & 63;
   st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  st.wm = st.wave & 3;
-  st.wn = st.wave >> 2;
+  st.wm = st.wave % WRM;
+  st.wn = st.wave / WRM;
   const int split = blockIdx.y;
   const int c0 = split * a.cps;
   const int nch = int(a.KT) - c0 < a.cps ? int(a.KT) - c0 : a.cps;
   st.kt0 = c0;
-  // the tile's 2 RBW weight row blocks (slots past them, and row blocks past
+  // the tile's WN RBW weight row blocks (slots past them, and row blocks past
   // the matrix, are out of range of the resource: their loads read nothing
   // and their LDS slots are never multiplied)
-  const int64_t nb0 = int64_t(nbn) * (2 * RBW), m0 = int64_t(mb) * 256;
-  const int64_t nbl = a.NB - nb0 < 2 * RBW ? a.NB - nb0 : 2 * RBW;
+  const int64_t nb0 = int64_t(nbn) * (T::WN * RBW), m0 = int64_t(mb) * (64 * WRM);
+  const int64_t nbl = a.NB - nb0 < T::WN * RBW ? a.NB - nb0 : T::WN * RBW;
   st.wres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(a.w + nb0 * a.KT * (kTileBytes / 16)), 0,
                                               uint32_t(nbl * a.KT * kTileBytes), 0x00020000);
   st.xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, uint32_t(a.M * a.K * 2), 0x00020000);
   {
     const int kb = st.lane >> 4, j = st.lane & 15;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) st.wvo[u] = uint32_t((2 * st.wave + u) * a.KT * kTileBytes) + st.lane * 16;
+    for (int u = 0; u < T::DW; ++u) st.wvo[u] = uint32_t((T::DW * st.wave + u) * a.KT * kTileBytes) + st.lane * 16;
 #pragma unroll
-    for (int u = 0; u < GlF8::DX; ++u) {
+    for (int u = 0; u < T::DX; ++u) {
       // fragment f = (x row block i, step s): lane (kb, j) holds the 8 k of
       // row 16 i + j that pair with bytes 8 s .. 8 s + 7 of weight slice kb
-      const int f = GlF8::DX * st.wave + u, i = f / 2, sx = f % 2;
+      const int f = T::DX * st.wave + u, i = f / 2, sx = f % 2;
       const int64_t row = m0 + 16 * i + j;
       st.xvo[u] = row < a.M ? uint32_t((row * a.K + kb * 16 + 8 * sx) * 2) : 0x80000000u;
     }
@@ -391,13 +409,13 @@ __global__ __launch_bounds__(512) void gemm_lds8_kernel(GlArgs a, const float* _
   gl_wait_barrier<GlF8::DPC>();
   int c = 0;
   for (; c + NS <= nch; c += NS) {
-    gl8_chunk<0, RBW>(st, sb, c);
-    gl8_chunk<1, RBW>(st, sb, c + 1);
-    gl8_chunk<2, RBW>(st, sb, c + 2);
+    gl8_chunk<0>(st, sb, c);
+    gl8_chunk<1>(st, sb, c + 1);
+    gl8_chunk<2>(st, sb, c + 2);
   }
   const int rest = nch - c;
-  if (rest > 0) gl8_chunk<0, RBW>(st, sb, c);
-  if (rest > 1) gl8_chunk<1, RBW>(st, sb, c + 1);
+  if (rest > 0) gl8_chunk<0>(st, sb, c);
+  if (rest > 1) gl8_chunk<1>(st, sb, c + 1);
   __builtin_amdgcn_s_waitcnt(0x7 << 4);
 
   const int kb = st.lane >> 4, n = st.lane & 15;
@@ -425,8 +443,11 @@ hipError_t launch_gemm_lds(int fmt, const GmPlan& p, const void* x, int64_t M, i
                            const void* scales, void* y, void* part, bool swiglu, hipStream_t st) {
   if (p.wm != 3 || (fmt != kFmtBF16 && fmt != kFmtFP8) || K != p.KT * (fmt == kFmtFP8 ? GlF8::TK : GlF::TK))
     return hipErrorInvalidValue;
-  // column blocks of 2 rbw weight row blocks: 16 for BF16, 16 or 14 for FP8
-  if (!(p.rbw == 8 || (fmt == kFmtFP8 && p.rbw == 7)) || p.NBN != ceil_div(p.NB, int64_t(2 * p.rbw)))
+  // tiles of 64 lwr rows by (8 / lwr) rbw weight row blocks: BF16 256 x 256,
+  // FP8 256 x 256, 256 x 224 or 128 x 448
+  const bool shape_ok = fmt == kFmtBF16 ? (p.rbw == 8 && p.lwr == 4)
+                                        : ((p.rbw == 8 && p.lwr == 4) || (p.rbw == 7 && (p.lwr == 4 || p.lwr == 2)));
+  if (!shape_ok || p.NBN != ceil_div(p.NB, int64_t(8 / p.lwr * p.rbw)) || p.MB != ceil_div(M, int64_t(64 * p.lwr)))
     return hipErrorInvalidValue;
   GlArgs a;
   a.x = reinterpret_cast<const uint16_t*>(x);
@@ -444,10 +465,13 @@ hipError_t launch_gemm_lds(int fmt, const GmPlan& p, const void* x, int64_t M, i
   a.S = p.S;
   a.swiglu = swiglu;
   const dim3 grid(unsigned(ceil_div(p.NBN, int64_t(8)) * 8 * p.MB), unsigned(p.S));
-  if (fmt == kFmtFP8 && p.rbw == 7)
-    hipLaunchKernelGGL(gemm_lds8_kernel<7>, grid, dim3(512), 0, st, a, reinterpret_cast<const float*>(scales));
+  const float* sc = reinterpret_cast<const float*>(scales);
+  if (fmt == kFmtFP8 && p.lwr == 4 && p.rbw == 7)
+    hipLaunchKernelGGL((gemm_lds8_kernel<7, 4>), grid, dim3(512), 0, st, a, sc);
+  else if (fmt == kFmtFP8 && p.lwr == 4)
+    hipLaunchKernelGGL((gemm_lds8_kernel<8, 4>), grid, dim3(512), 0, st, a, sc);
   else if (fmt == kFmtFP8)
-    hipLaunchKernelGGL(gemm_lds8_kernel<8>, grid, dim3(512), 0, st, a, reinterpret_cast<const float*>(scales));
+    hipLaunchKernelGGL((gemm_lds8_kernel<7, 2>), grid, dim3(512), 0, st, a, sc);
   else
     hipLaunchKernelGGL(gemm_lds_kernel, grid, dim3(512), 0, st, a);
   return hipGetLastError();

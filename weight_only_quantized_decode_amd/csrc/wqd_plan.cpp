@@ -291,12 +291,21 @@ static constexpr GlCost kGlCost[2] = {
 };
 constexpr int64_t kGlMinM = 192;
 
-// Relative time of a chunk on 224-column tiles (14 weight row blocks, 7 per
-// wavefront) against 256-column ones (FP8 only).
-#ifndef WQD_GL_W7
-#define WQD_GL_W7 0.95
+// FP8 tile shapes of the LDS-staged kernel: (weight row blocks per wavefront,
+// wavefront rows of 64 rows) and the time of one of its 64-k chunks relative
+// to the 256 x 256 tile's.
+struct GlShape {
+  int rbw, lwr;
+  double f;
+};
+#ifndef WQD_GL_F72
+#define WQD_GL_F72 0.93
 #endif
-constexpr double kGlW7 = WQD_GL_W7;
+#ifndef WQD_GL_FORCE_SHAPE
+static constexpr GlShape kGlShapes[] = {{8, 4, 1.0}, {7, 4, 0.95}, {7, 2, WQD_GL_F72}};
+#else
+static constexpr GlShape kGlShapes[] = {WQD_GL_FORCE_SHAPE};  // measurement builds only
+#endif
 
 static int plan_gemm_lds(int fmt, int64_t M, int64_t N, int64_t K, const PackedSizes& ps, GmPlan* out,
                          double* t_us) {
@@ -305,47 +314,50 @@ static int plan_gemm_lds(int fmt, int64_t M, int64_t N, int64_t K, const PackedS
   if (M < kGlMinM) return kEUnsupported;
   // K a whole number of tiles (no x piece of a tile lies past K)
   if (K % tile_k(fmt) != 0) return kEUnsupported;
-  // weight offsets of 16 row blocks stay below 2^31
-  if (16 * ps.KT * kTileBytes >= (int64_t(1) << 31)) return kEUnsupported;
+  // weight offsets of 32 row blocks stay below 2^31
+  if (32 * ps.KT * kTileBytes >= (int64_t(1) << 31)) return kEUnsupported;
   GmPlan p{};
   p.NB = ps.NB;
   p.KT = ps.KT;
   p.wm = 3;
-  p.MB = ceil_div(M, 256);
-  p.Mp = p.MB * 256;
   p.nchunks = p.KT;
   const double mn8 = double(M) * double(N) * 8.0;
   const int64_t max_s = p.nchunks / 8 < 1 ? 1 : (p.nchunks / 8 > 8 ? 8 : p.nchunks / 8);
   const GlCost& gc = kGlCost[fmt == kFmtFP8];
-  // the tile width (FP8: 256 or 224 columns, whichever fills the compute
-  // units' rounds better) and the K split
+  // the tile shape (BF16: 256 x 256; FP8: the one that fills the compute
+  // units' rounds best) and the K split
+  static constexpr GlShape kBf16Shape[] = {{8, 4, 1.0}};
+  const GlShape* shapes = fmt == kFmtFP8 ? kGlShapes : kBf16Shape;
+  const int nshapes = fmt == kFmtFP8 ? int(sizeof(kGlShapes) / sizeof(kGlShapes[0])) : 1;
   double best = 0.0;
   int64_t S = 1;
-  int rbw = 8;
+  GlShape pick = shapes[0];
   bool first = true;
-#ifdef WQD_GL_FORCE_RBW
-  const int w_hi = fmt == kFmtFP8 ? WQD_GL_FORCE_RBW : 8, w_lo = w_hi;  // measurement builds only
-#else
-  const int w_hi = 8, w_lo = fmt == kFmtFP8 ? 7 : 8;
-#endif
-  for (int w = w_hi; w >= w_lo; --w) {
-    const int64_t tiles = ceil_div(p.NB, int64_t(2 * w)) * p.MB;
-    const double fw = w == 8 ? 1.0 : kGlW7;
+  for (int h = 0; h < nshapes; ++h) {
+    const GlShape& sh = shapes[h];
+    // column block j runs on XCD j % 8 (workgroups are dispatched round-robin
+    // over the 8 XCDs and the kernel maps them so), so the busiest XCD holds
+    // ceil(NBN / 8) column blocks' workgroups for its 32 compute units
+    const int64_t nbn_xcd = ceil_div(ceil_div(p.NB, int64_t(8 / sh.lwr * sh.rbw)), int64_t(8));
+    const int64_t per_xcd = nbn_xcd * ceil_div(M, int64_t(64 * sh.lwr));
     for (int64_t s = 1; s <= max_s; ++s) {
       const int64_t cps = ceil_div(p.nchunks, s), se = ceil_div(p.nchunks, cps);
-      const int64_t rounds = ceil_div(tiles * se, kComputeUnits);
+      const int64_t rounds = ceil_div(per_xcd * se, kComputeUnits / 8);
       const double t =
-          gc.c0 + double(cps) * gc.a * fw * double(rounds) + (se > 1 ? double(se) * mn8 / (gc.bw * 1.0e6) : 0.0);
+          gc.c0 + double(cps) * gc.a * sh.f * double(rounds) + (se > 1 ? double(se) * mn8 / (gc.bw * 1.0e6) : 0.0);
       if (first || t < 0.98 * best) {
         best = t;
         S = se;
-        rbw = w;
+        pick = sh;
         first = false;
       }
     }
   }
-  p.rbw = rbw;
-  p.NBN = ceil_div(p.NB, int64_t(2 * rbw));
+  p.rbw = pick.rbw;
+  p.lwr = pick.lwr;
+  p.NBN = ceil_div(p.NB, int64_t(8 / pick.lwr * pick.rbw));
+  p.MB = ceil_div(M, int64_t(64 * pick.lwr));
+  p.Mp = p.MB * 64 * pick.lwr;
   p.cps = ceil_div(p.nchunks, S);
   p.S = int(ceil_div(p.nchunks, p.cps));
   p.ws_bytes = p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;

@@ -127,7 +127,8 @@ constexpr int64_t kGmMinNBN = 16;
 struct GmPlan {
   int64_t NB, KT, NBN, MB, nchunks, cps, Mp;
   int wm, S;
-  int rbw;  // LDS-staged form (wm 3): weight row blocks per wavefront, a column block being 2 rbw of them
+  int rbw;  // LDS-staged form (wm 3): weight row blocks per wavefront ...
+  int lwr;  // ... and wavefront rows of 64 rows: tiles of 64 lwr rows by (8 / lwr) rbw row blocks
   size_t xs_bytes, ws_bytes;
 };
 
