@@ -199,18 +199,19 @@ def test_kernel_path_choice():
         ws = wqd.workspace_bytes(fmt, M, N, K)
         assert ws % (M * N * 4) == 0 and ws // (M * N * 4) in (0, 2, 3, 4, 5, 6, 7, 8)
     assert wqd.workspace_bytes("bf16", 128, 8192, 28672) == 4 * 128 * 8192 * 4  # 64 tiles: 4 splits fill the GPU
-    assert wqd.workspace_bytes("bf16", 1024, 28672, 8192) == 0                  # 448 tiles of 256 x 256: no split
+    assert wqd.workspace_bytes("bf16", 1024, 28672, 8192) == 0                  # 512 tiles of 256 x 224: no split
     # x rows spanning 2 GiB: the LDS matrix-core kernel
     assert wqd.kernel_path("bf16", 65536, 64, 16384)[0] == "mfma"
-    # the tiled kernels' tile of y and K split: FP8 on the LDS-staged kernel
-    # takes 256 x 224 or 128 x 448 tiles where they fill the rounds of the 8
+    # the tiled kernels' tile of y and K split: the LDS-staged kernel takes
+    # 256 x 224 (FP8 also 128 x 448) tiles where they fill the rounds of the 8
     # XCDs' 32 compute units better (the 70B gate at 1024 rows: 512 tiles in
     # two whole rounds instead of 448 of 256 x 256 in 1.75), 256 x 256 elsewhere
     assert wqd.gemm_tile("fp8", 1024, 28672, 8192) == (128, 448, 1)
     assert wqd.gemm_tile("fp8", 512, 28672, 8192) == (256, 224, 1)
     assert wqd.gemm_tile("fp8", 1024, 8192, 28672) == (256, 256, 2)
     assert wqd.gemm_tile("fp8", 1024, 8192, 8192) == (64, 256, 1)
-    assert wqd.gemm_tile("bf16", 1024, 28672, 8192) == (256, 256, 1)
+    assert wqd.gemm_tile("bf16", 1024, 28672, 8192) == (256, 224, 1)
+    assert wqd.gemm_tile("bf16", 1024, 8192, 28672) == (256, 256, 2)
     assert wqd.gemm_tile("w4a16", 1024, 28672, 8192)[:2] == (128, 256)
     assert wqd.gemm_tile("w4a16", 100, 28672, 8192)[:2] == (64, 256)
     for fmt, M, N, K in (("fp8", 1024, 28672, 8192), ("bf16", 128, 8192, 28672), ("w4a16", 384, 8192, 28672)):

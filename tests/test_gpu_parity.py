@@ -305,9 +305,10 @@ def test_qgemm_tiled_256_rows_padded(fmt, N, K, M):
 
 
 @pytest.mark.parametrize("fmt,N,K,M,S,R,C", [
-    ("bf16", 8208, 8224, 513, 2, 256, 256), ("bf16", 16392, 2048, 513, 1, 256, 256),
-    ("bf16", 28672, 1056, 300, 1, 256, 256), ("bf16", 12296, 4096, 777, 1, 256, 256),
-    ("bf16", 11008, 4096, 777, 1, 256, 256),
+    ("bf16", 8208, 8224, 513, 2, 256, 224), ("bf16", 16392, 2048, 513, 1, 256, 224),
+    ("bf16", 28672, 1056, 300, 1, 256, 224), ("bf16", 12296, 4096, 777, 1, 256, 224),
+    ("bf16", 11008, 4096, 777, 1, 256, 224), ("bf16", 13456, 2048, 1000, 1, 256, 224),
+    ("bf16", 8192, 28704, 513, 5, 256, 256), ("bf16", 12288, 28672, 700, 5, 256, 256),
     ("fp8", 8208, 8256, 1000, 3, 256, 224), ("fp8", 28672, 1088, 1023, 1, 256, 224),
     ("fp8", 28680, 4096, 900, 1, 256, 256), ("fp8", 8200, 28672, 1024, 3, 256, 224),
     ("fp8", 20488, 8192, 1023, 2, 256, 224), ("fp8", 13456, 2048, 1000, 1, 256, 224),
@@ -315,11 +316,11 @@ def test_qgemm_tiled_256_rows_padded(fmt, N, K, M):
     ("fp8", 29104, 4096, 777, 1, 128, 448), ("fp8", 57352, 2048, 777, 1, 128, 448)])
 def test_qgemm_tiled_lds(fmt, N, K, M, S, R, C):
     """BF16 and FP8 on the tiled kernel that stages x and the weights in LDS
-    (R x C tiles: 256 x 256, for FP8 also 256 x 224 and 128 x 448): ragged N
+    (R x C tiles: 256 x 256, 256 x 224, for FP8 also 128 x 448): ragged N
     inside a 16-row block, last column blocks of one row block (of 16, 14 and
     28) and of 7, 9 or 27, ragged M (last row blocks of 1 to 255 rows), chunk
     counts leaving each remainder of the loop (BF16: 4 chunks of 32 k, FP8: 3
-    of 64 k), and K splits of 2 and 3.  The oracle checks a sample of output
+    of 64 k), and K splits of 2, 3 and 5.  The oracle checks a sample of output
     columns, the first and last ones and those on either side of the first
     column blocks' edges included, over every row."""
     assert wqd.kernel_path(fmt, M, N, K) == ("gemm_lds", 8)

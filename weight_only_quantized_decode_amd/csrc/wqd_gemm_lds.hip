@@ -72,9 +72,10 @@ struct GlF {
   static constexpr int NS = 4;             // stages (128 KiB of LDS)
 };
 
+template <int RBW>
 struct GlState {
-  gl_f32x4_t acc[4][8];  // [x row block][weight row block]
-  uint4 w[2][8];         // weight fragments of the current and the next chunk
+  gl_f32x4_t acc[4][RBW];  // [x row block][weight row block]
+  uint4 w[2][RBW];         // weight fragments of the current and the next chunk
   uint4 x[2][4];         // x fragments of the current and the next chunk
   __amdgpu_buffer_rsrc_t wres, xres;
   uint32_t wvo[2];         // this lane's byte offsets of its two weight loads (chunk 0 of the matrix)
@@ -95,7 +96,8 @@ __device__ __forceinline__ void gl_dma(__amdgpu_buffer_rsrc_t r, uint4* dst, uin
 // inside the matrix lies past K; chunks past the matrix read weights of the
 // next row block, or nothing past the last one, into stages that are never
 // multiplied).
-__device__ __forceinline__ void gl_load_chunk(const GlState& st, int c, uint4* buf) {
+template <int RBW>
+__device__ __forceinline__ void gl_load_chunk(const GlState<RBW>& st, int c, uint4* buf) {
   const uint32_t kt = uint32_t(st.kt0) + uint32_t(c);
 #pragma unroll
   for (int u = 0; u < 2; ++u) gl_dma(st.wres, buf + (2 * st.wave + u) * 64, st.wvo[u], kt * kTileBytes);
@@ -106,19 +108,19 @@ __device__ __forceinline__ void gl_load_chunk(const GlState& st, int c, uint4* b
 
 // The operands of the chunk in buf into set H: weight fragments of row blocks
 // 8 wn .. 8 wn + 7, x fragments of row blocks 4 wm .. 4 wm + 3.
-template <int H>
-__device__ __forceinline__ void gl_read_ops(GlState& st, const uint4* buf) {
+template <int H, int RBW>
+__device__ __forceinline__ void gl_read_ops(GlState<RBW>& st, const uint4* buf) {
 #pragma unroll
-  for (int b = 0; b < 8; ++b) st.w[H][b] = buf[(8 * st.wn + b) * 64 + st.lane];
+  for (int b = 0; b < RBW; ++b) st.w[H][b] = buf[(RBW * st.wn + b) * 64 + st.lane];
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.x[H][i] = buf[(16 + 4 * st.wm + i) * 64 + st.lane];
 }
 
 // The 32 multiplies of the operands in set H.
-template <int H>
-__device__ __forceinline__ void gl_mfmas(GlState& st) {
+template <int H, int RBW>
+__device__ __forceinline__ void gl_mfmas(GlState<RBW>& st) {
 #pragma unroll
-  for (int b = 0; b < 8; ++b)
+  for (int b = 0; b < RBW; ++b)
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.acc[i][b] = gl_mfma(st.x[H][i], st.w[H][b], st.acc[i][b]);
 }
@@ -137,15 +139,16 @@ __device__ __forceinline__ void gl_wait_barrier() {
 // released by the last barrier), multiply while reading chunk c + 1's
 // operands (landed before the last barrier) into the other set, then wait
 // for chunk c + 2 and meet the other wavefronts.
-template <int H>
-__device__ __forceinline__ void gl_chunk(GlState& st, uint4* const* sb, int c) {
+template <int H, int RBW>
+__device__ __forceinline__ void gl_chunk(GlState<RBW>& st, uint4* const* sb, int c) {
   constexpr int NS = GlF::NS, P = H % 2;
   gl_load_chunk(st, c + NS - 1, sb[(H + NS - 1) % NS]);
   gl_read_ops<1 - P>(st, sb[(H + 1) % NS]);
   gl_mfmas<P>(st);
-  // spread the 12 LDS reads and 4 loads over the 32 multiplies (left to
-  // itself the scheduler reads the next operands into the registers of the
+  // spread the RBW + 4 LDS reads and 4 loads over the 4 RBW multiplies (left
+  // to itself the scheduler reads the next operands into the registers of the
   // current ones after their last multiply, and waits for them at once)
+  static_assert(RBW >= 7 && RBW <= 8, "pattern for 7 or 8 weight row blocks");
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
@@ -154,13 +157,14 @@ __device__ __forceinline__ void gl_chunk(GlState& st, uint4* const* sb, int c) {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, RBW - 6, 0);
     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 load into LDS
   }
   __builtin_amdgcn_sched_barrier(0);
   gl_wait_barrier<GlF::DPC * (NS - 3)>();
 }
 
+template <int RBW>
 __global__ __launch_bounds__(512) void gemm_lds_kernel(GlArgs a) {
   constexpr int NS = GlF::NS;
   __shared__ uint4 s0[GlF::BUF], s1[GlF::BUF], s2[GlF::BUF], s3[GlF::BUF];
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GlArgs a) {
   const int nbn = (wi / a.MB) * 8 + xcd, mb = wi % a.MB;
   if (nbn >= a.NBN) return;  // whole workgroup, before any barrier
 
-  GlState st;
+  GlState<RBW> st;
   st.lane = threadIdx.x & 63;
   st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   st.wm = st.wave & 3;
@@ -182,9 +186,10 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GlArgs a) {
   const int c0 = split * a.cps;
   const int nch = int(a.KT) - c0 < a.cps ? int(a.KT) - c0 : a.cps;  // >= 1: the planner sizes S so
   st.kt0 = c0;
-  const int64_t nb0 = int64_t(nbn) * 16, m0 = int64_t(mb) * 256;
-  // the tile's weight row blocks (those past the matrix are out of range)
-  const int64_t nbl = a.NB - nb0 < 16 ? a.NB - nb0 : 16;
+  const int64_t nb0 = int64_t(nbn) * (2 * RBW), m0 = int64_t(mb) * 256;
+  // the tile's 2 RBW weight row blocks (slots past them, and row blocks past
+  // the matrix, are out of range: their loads read nothing)
+  const int64_t nbl = a.NB - nb0 < 2 * RBW ? a.NB - nb0 : 2 * RBW;
   st.wres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(a.w + nb0 * a.KT * (kTileBytes / 16)), 0,
                                               uint32_t(nbl * a.KT * kTileBytes), 0x00020000);
   st.xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, uint32_t(a.M * a.K * 2), 0x00020000);
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GlArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) st.acc[i][b] = gl_f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < RBW; ++b) st.acc[i][b] = gl_f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // the stages start as zeros: lanes out of range of their resource may leave
   // their LDS bytes unwritten (those bytes then only ever hold zeros)
@@ -238,8 +243,8 @@ __global__ __launch_bounds__(512) void gemm_lds_kernel(GlArgs a) {
   // lane (kb, n) holds rows 4 kb + r of each x row block, column n of each weight row block
   const int kb = st.lane >> 4, n = st.lane & 15;
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int64_t nb = nb0 + 8 * st.wn + b;
+  for (int b = 0; b < RBW; ++b) {
+    const int64_t nb = nb0 + RBW * st.wn + b;
     const int64_t col = nb * kTileRows + n;
     if (nb >= a.NB || col >= a.N) continue;  // the same for lanes n and n ^ 8 (N % 16 == 0 with SwiGLU)
 #pragma unroll
@@ -445,7 +450,7 @@ hipError_t launch_gemm_lds(int fmt, const GmPlan& p, const void* x, int64_t M, i
     return hipErrorInvalidValue;
   // tiles of 64 lwr rows by (8 / lwr) rbw weight row blocks: BF16 256 x 256,
   // FP8 256 x 256, 256 x 224 or 128 x 448
-  const bool shape_ok = fmt == kFmtBF16 ? (p.rbw == 8 && p.lwr == 4)
+  const bool shape_ok = fmt == kFmtBF16 ? ((p.rbw == 8 || p.rbw == 7) && p.lwr == 4)
                                         : ((p.rbw == 8 && p.lwr == 4) || (p.rbw == 7 && (p.lwr == 4 || p.lwr == 2)));
   if (!shape_ok || p.NBN != ceil_div(p.NB, int64_t(8 / p.lwr * p.rbw)) || p.MB != ceil_div(M, int64_t(64 * p.lwr)))
     return hipErrorInvalidValue;
@@ -472,8 +477,10 @@ hipError_t launch_gemm_lds(int fmt, const GmPlan& p, const void* x, int64_t M, i
     hipLaunchKernelGGL((gemm_lds8_kernel<8, 4>), grid, dim3(512), 0, st, a, sc);
   else if (fmt == kFmtFP8)
     hipLaunchKernelGGL((gemm_lds8_kernel<7, 2>), grid, dim3(512), 0, st, a, sc);
+  else if (p.rbw == 7)
+    hipLaunchKernelGGL(gemm_lds_kernel<7>, grid, dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL(gemm_lds_kernel, grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL(gemm_lds_kernel<8>, grid, dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

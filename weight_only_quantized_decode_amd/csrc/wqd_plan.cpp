@@ -301,10 +301,15 @@ struct GlShape {
 #ifndef WQD_GL_F72
 #define WQD_GL_F72 0.93
 #endif
+#ifndef WQD_GL_BF16_F74
+#define WQD_GL_BF16_F74 0.965
+#endif
 #ifndef WQD_GL_FORCE_SHAPE
 static constexpr GlShape kGlShapes[] = {{8, 4, 1.0}, {7, 4, 0.95}, {7, 2, WQD_GL_F72}};
+static constexpr GlShape kGlShapesBf16[] = {{8, 4, 1.0}, {7, 4, WQD_GL_BF16_F74}};
 #else
 static constexpr GlShape kGlShapes[] = {WQD_GL_FORCE_SHAPE};  // measurement builds only
+static constexpr GlShape kGlShapesBf16[] = {WQD_GL_FORCE_SHAPE};
 #endif
 
 static int plan_gemm_lds(int fmt, int64_t M, int64_t N, int64_t K, const PackedSizes& ps, GmPlan* out,
@@ -324,11 +329,10 @@ static int plan_gemm_lds(int fmt, int64_t M, int64_t N, int64_t K, const PackedS
   const double mn8 = double(M) * double(N) * 8.0;
   const int64_t max_s = p.nchunks / 8 < 1 ? 1 : (p.nchunks / 8 > 8 ? 8 : p.nchunks / 8);
   const GlCost& gc = kGlCost[fmt == kFmtFP8];
-  // the tile shape (BF16: 256 x 256; FP8: the one that fills the compute
-  // units' rounds best) and the K split
-  static constexpr GlShape kBf16Shape[] = {{8, 4, 1.0}};
-  const GlShape* shapes = fmt == kFmtFP8 ? kGlShapes : kBf16Shape;
-  const int nshapes = fmt == kFmtFP8 ? int(sizeof(kGlShapes) / sizeof(kGlShapes[0])) : 1;
+  // the tile shape that fills the compute units' rounds best and the K split
+  const GlShape* shapes = fmt == kFmtFP8 ? kGlShapes : kGlShapesBf16;
+  const int nshapes = fmt == kFmtFP8 ? int(sizeof(kGlShapes) / sizeof(kGlShapes[0]))
+                                     : int(sizeof(kGlShapesBf16) / sizeof(kGlShapesBf16[0]));
   double best = 0.0;
   int64_t S = 1;
   GlShape pick = shapes[0];
