@@ -117,7 +117,8 @@ int wqd_packed_sizes(int fmt, int64_t N, int64_t K,
 int wqd_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes);
 
 /* Kernel families behind wqd_qgemm (wqd_kernel_path).  Which one serves a
- * shape: the broadcast kernel for 1 W4A16 row or up to 4 FP8 / BF16 rows; up
+ * shape: the broadcast kernel for 1 W4A16 row or up to 4 FP8 / BF16 rows
+ * (FP8 at 4 rows only where the skinny kernel's shares are not long); up
  * to 8 rows the skinny matrix-core kernel for long shares of K (large N, or
  * long K at 8 rows), else the streaming matrix-core kernel; otherwise, up to
  * 8 rows, the broadcast kernel, then the staged one; from 9 to 64 rows the skinny

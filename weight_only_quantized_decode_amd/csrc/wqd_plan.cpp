@@ -457,7 +457,11 @@ int choose_path(int fmt, int64_t M, int64_t N, int64_t K, Choice* out) {
   // start and, with a K split, the second launch are amortised), measured
   // on the 70B shapes: gate/up from 2 rows, down at 8
   const bool sk_long = sk_ok && c.sk.per_split >= 48 && (c.sk.S == 1 || M >= kGemvMaxM);
-  if (M <= bcast_first && plan_bcast(fmt, M, N, K, &c.bcast) == kOK) {
+  // FP8 at 4 rows: the skinny kernel ahead of the broadcast one where its
+  // shares are long (70B gate/up 82.7 -> 74.4 us; at 2 and 3 rows the
+  // broadcast kernel is as fast or faster, measured on the same box)
+  const bool sk_first = fmt == kFmtFP8 && M >= 4 && sk_long;
+  if (!sk_first && M <= bcast_first && plan_bcast(fmt, M, N, K, &c.bcast) == kOK) {
     c.path = kPathBcast;
   } else if (M <= kGemvMaxM && sk_long) {
     c.path = kPathSkinny;

@@ -152,7 +152,8 @@ int plan_mfma(int fmt, int64_t M, int64_t N, int64_t K, MfmaPlan* out);
 
 // The kernel family for a shape, in order of preference (measured on the
 // 70B shapes): the broadcast kernel for 1 W4A16 row or up to 4 FP8 / BF16
-// rows; up to 8 rows the skinny matrix-core kernel where its K shares are
+// rows (FP8 at 4 rows only where the skinny kernel's shares are not long);
+// up to 8 rows the skinny matrix-core kernel where its K shares are
 // at least 48 tiles long and unsplit (or split, at 8 rows), else the
 // streaming matrix-core kernel; the broadcast kernel again, then the staged
 // one, up to 8 rows where those cannot take the shape; from 9 to 16 rows
