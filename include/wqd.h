@@ -160,6 +160,16 @@ int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* wa
 int wqd_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K, int* rows, int* cols, int* splits);
 
 /*
+ * Host-only: the tile of y each workgroup of wqd_qgemm_w8a8 computes for this
+ * shape (*rows x *cols: 32, 64 or 128 x 256 with the weights taken into
+ * registers; 256 x 256, 256 x 224 or 128 x 448 with both operands staged in
+ * LDS, from 256 rows where K is a whole number of 128-k chunks) and its
+ * number of K splits.  Any output pointer may be NULL.  Errors: those of
+ * wqd_w8a8_workspace_bytes.
+ */
+int wqd_w8a8_tile(int64_t M, int64_t N, int64_t K, int* rows, int* cols, int* splits);
+
+/*
  * Setup (not on the decode hot path): quantise W (device, float32 [N, K]
  * row-major) to `fmt` and write the packed weights, scales and zero points
  * (device buffers of the sizes wqd_packed_sizes gives; scales and zeros may be

@@ -218,6 +218,16 @@ def test_kernel_path_choice():
         ws = wqd.workspace_bytes(fmt, M, N, K)
         S = wqd.gemm_tile(fmt, M, N, K)[2]
         assert S >= 1 and ws - (ws % (M * N * 4)) == (S * M * N * 4 if S > 1 else 0)
+    # W8A8: register-operand tiles of 32 / 64 / 128 rows, the LDS-staged ones
+    # from 256 rows where they fill the compute units' rounds (not the 70B gate
+    # at 768 rows: three quarters)
+    assert wqd.w8a8_tile(16, 8192, 8192)[:2] == (32, 256)
+    assert wqd.w8a8_tile(128, 8192, 8192)[:2] == (128, 256)
+    assert wqd.w8a8_tile(1024, 28672, 8192) == (256, 224, 1)
+    assert wqd.w8a8_tile(1024, 8192, 28672) == (256, 256, 2)
+    assert wqd.w8a8_tile(768, 28672, 8192) == (128, 256, 1)
+    assert wqd.w8a8_tile(300, 300, 1040)[:2] == (128, 256)  # K not a whole number of 128-k chunks
+    assert wqd.lib().wqd_w8a8_tile(256, 8192, 8200, None, None, None) == E_SHAPE
     r = ctypes.c_int()
     assert wqd.lib().wqd_gemm_tile(2, 1, 8192, 8192, ctypes.byref(r), None, None) == E_UNSUPPORTED  # broadcast
     assert wqd.lib().wqd_gemm_tile(9, 1024, 8192, 8192, None, None, None) == E_ARG

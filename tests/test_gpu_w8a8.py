@@ -105,6 +105,26 @@ def test_verify_shapes_sampled(M, N, K):
     run_product(M, N, K, 600 + M, rows=rows, outl=K == 8192)
 
 
+@pytest.mark.parametrize("M,N,K,R,C,S", [(513, 43008, 2176, 128, 448, 1), (256, 16400, 4224, 128, 448, 3),
+                                         (257, 8200, 28672, 128, 448, 7), (257, 28672, 2176, 256, 224, 1),
+                                         (256, 13456, 8192, 256, 224, 4), (256, 8200, 28672, 256, 224, 6),
+                                         (256, 57352, 2176, 256, 256, 1), (300, 8200, 2176, 256, 256, 3),
+                                         (1000, 29104, 4096, 256, 256, 1)])
+def test_lds_staged_ragged(M, N, K, R, C, S):
+    """From 256 rows (K a whole number of 128-k chunks, tiles that fill the
+    compute units' rounds) both operands are staged in LDS on 256 x 256,
+    256 x 224 or 128 x 448 tiles: ragged N inside
+    a 16-row block and last column blocks of 1 to 27 row blocks, ragged M (last
+    row blocks of 1 to 127 rows), odd and even chunk counts per split (the
+    two-stage loop's remainder) and K splits of 2 to 7.  Sampled columns
+    include the first column blocks' edges."""
+    assert wqd.w8a8_tile(M, N, K) == (R, C, S)
+    rng = np.random.default_rng(N + K + M)
+    edges = {0, 15, C - 1, C, 2 * C - 1, 2 * C, N - 17, N - 9, N - 1}
+    rows = np.array(sorted(set(rng.choice(N, 40, replace=False).tolist()) | edges))
+    run_product(M, N, K, 700 + M, rows=rows)
+
+
 def test_deterministic():
     M, N, K = 256, 4096, 4096
     pw = wqd.pack_weights("fp8", I.w_device(77, N, K, device=DEV))

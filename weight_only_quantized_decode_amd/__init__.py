@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "wqd_kernel_path": (i32, [i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "wqd_gemm_tile": (i32, [i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                     ctypes.POINTER(i32)]),
+            "wqd_w8a8_tile": (i32, [i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "wqd_pack_weights": (i32, [i32, vp, i64, i64, vp, vp, vp, vp]),
             "wqd_qgemm": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
             "wqd_qgemm_noalloc": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]),
@@ -185,6 +186,14 @@ def gemm_tile(fmt, M: int, N: int, K: int):
     r, c, s = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     _check(lib().wqd_gemm_tile(_fmt(fmt), M, N, K, ctypes.byref(r), ctypes.byref(c), ctypes.byref(s)),
            "wqd_gemm_tile")
+    return r.value, c.value, s.value
+
+
+def w8a8_tile(M: int, N: int, K: int):
+    """(rows, columns, K splits) of the tile of y each workgroup of qgemm_w8a8
+    computes for this shape."""
+    r, c, s = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().wqd_w8a8_tile(M, N, K, ctypes.byref(r), ctypes.byref(c), ctypes.byref(s)), "wqd_w8a8_tile")
     return r.value, c.value, s.value
 
 

@@ -143,6 +143,16 @@ int wqd_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K, int* rows, int* cols
   return WQD_OK;
 }
 
+int wqd_w8a8_tile(int64_t M, int64_t N, int64_t K, int* rows, int* cols, int* splits) {
+  wqd::W8Plan p;
+  const int st = wqd::plan_w8a8(M, N, K, &p);
+  if (st != wqd::kOK) return st;
+  if (rows) *rows = p.lds ? 64 * p.lwr : 16 * p.mf * p.wr;
+  if (cols) *cols = p.lds ? 16 * (8 / p.lwr) * p.rbw : 256;
+  if (splits) *splits = p.S;
+  return WQD_OK;
+}
+
 int wqd_pack_weights(int fmt, const float* W, int64_t N, int64_t K, void* w_packed, void* scales, void* zeros,
                      void* stream) {
   wqd::PackedSizes ps;

@@ -501,6 +501,19 @@ int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out) {
   return kOK;
 }
 
+// W8A8 LDS-staged form: from this many rows; per-chunk cost model and the
+// relative chunk times of its tile shapes.
+#ifndef WQD_W8_LDS_MIN_M
+#define WQD_W8_LDS_MIN_M 256
+#endif
+constexpr int64_t kW8LdsMinM = WQD_W8_LDS_MIN_M;
+static constexpr GlCost kW8Cost = {12.0, 1.53, 5.15};
+#ifndef WQD_W8_FORCE_SHAPE
+static constexpr GlShape kW8Shapes[] = {{8, 4, 1.0}, {7, 4, 0.95}, {7, 2, 0.93}};
+#else
+static constexpr GlShape kW8Shapes[] = {WQD_W8_FORCE_SHAPE};  // measurement builds only
+#endif
+
 int plan_w8a8(int64_t M, int64_t N, int64_t K, W8Plan* out) {
   PackedSizes ps;
   int st = packed_sizes(kFmtFP8, N, K, &ps);
@@ -518,10 +531,48 @@ int plan_w8a8(int64_t M, int64_t N, int64_t K, W8Plan* out) {
   } else {
     p.mf = 8, p.wr = 1;
   }
+  p.nchunks = ceil_div(p.KT, 2);  // 128-k chunks
+  if (M >= kW8LdsMinM && K % 128 == 0 && 32 * p.KT * kTileBytes < (int64_t(1) << 31)) {
+    // the LDS-staged form: the tile shape and K split by the busiest XCD's
+    // rounds (as for the weight-only FP8 LDS-staged kernel)
+    const double mn8 = double(M) * double(N) * 8.0;
+    const int64_t max_s = p.nchunks / 4 < 1 ? 1 : (p.nchunks / 4 > 8 ? 8 : p.nchunks / 4);
+    double best = 0.0, fill = 0.0;
+    bool first = true;
+    for (const GlShape& sh : kW8Shapes) {
+      const int64_t nbn = ceil_div(p.NB, int64_t(8 / sh.lwr * sh.rbw)), mb = ceil_div(M, int64_t(64 * sh.lwr));
+      const int64_t per_xcd = ceil_div(nbn, int64_t(8)) * mb;
+      for (int64_t s = 1; s <= max_s; ++s) {
+        const int64_t cps = ceil_div(p.nchunks, s), se = ceil_div(p.nchunks, cps);
+        const int64_t rounds = ceil_div(per_xcd * se, kComputeUnits / 8);
+        const double t = kW8Cost.c0 + double(cps) * kW8Cost.a * sh.f * double(rounds) +
+                         (se > 1 ? double(se) * mn8 / (kW8Cost.bw * 1.0e6) : 0.0);
+        if (first || t < 0.98 * best) {
+          best = t;
+          first = false;
+          p.rbw = sh.rbw;
+          p.lwr = sh.lwr;
+          p.NBN = nbn;
+          p.MB = mb;
+          p.cps = cps;
+          p.S = int(se);
+          fill = double(per_xcd * se) / double(rounds * (kComputeUnits / 8));
+        }
+      }
+    }
+    // where the rounds are not nearly full (e.g. the 70B gate at 768 rows:
+    // 3/4), the 4-wavefront register-operand tiles measured faster
+    if (fill >= 0.9) {
+      p.lds = 1;
+      p.ws_bytes = p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;
+      *out = p;
+      return kOK;
+    }
+    p.rbw = p.lwr = 0;
+  }
   const int64_t bm = 16 * int64_t(p.mf) * p.wr;
   p.NBN = ceil_div(p.NB, 16);  // 256-column blocks
   p.MB = ceil_div(M, bm);
-  p.nchunks = ceil_div(p.KT, 2);  // 128-k chunks
   // fill at least one round of the 256 compute units (two workgroups each
   // for the 4-wavefront tiles), each split at least 4 chunks, at most 8 splits
   const int64_t tiles = ceil_div(p.NBN, 8) * 8 * p.MB;

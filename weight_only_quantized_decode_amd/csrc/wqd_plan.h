@@ -191,6 +191,7 @@ int workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* out);
 struct W8Plan {
   int64_t NB, KT, NBN, MB, nchunks, cps;
   int mf, wr, S;
+  int lds, rbw, lwr;  // LDS-staged form: tiles of 64 lwr rows by (8 / lwr) rbw weight row blocks
   size_t ws_bytes;
 };
 

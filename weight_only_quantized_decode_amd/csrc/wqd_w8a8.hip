@@ -21,7 +21,8 @@
 //                      nearest E4M3 of x / s_a (ties to even, saturating;
 //                      the hardware conversion after a clamp to +-448).
 //
-// The product (w8_gemm_kernel<MF, WR>): a workgroup computes a BM x 256 tile
+// The product, up to 255 rows (and where the LDS-staged form below would fill
+// the compute units' rounds poorly) w8_gemm_kernel<MF, WR>: a workgroup computes a BM x 256 tile
 // of y, BM = 16 MF WR, with WR x 4 wavefronts, each 16 MF rows x 4 weight row
 // blocks (64 columns); instantiated for MF = 2, 4, 8 and WR = 1 (at WR = 2
 // the 128-row wavefront tiles need one register more than the 256 a lane has).  K advances in 128-k chunks, one multiply per (x row
@@ -375,6 +376,178 @@ __global__ __launch_bounds__((64 * W8T<MF, WR>::NW)) void w8_gemm_kernel(W8Args 
   }
 }
 
+// ------------------------------------------------------------------ the product, LDS-staged form
+// For wide verify batches: both operands of a 128-k chunk go from memory
+// straight into one LDS stage (16-byte loads that write LDS, every
+// wavefront issuing its share), so every operand byte crosses from memory to
+// the compute unit once per workgroup.  A workgroup of 8 wavefronts computes
+// a tile of WRM wavefront rows of 64 rows by 8 / WRM wavefront columns of RBW
+// weight row blocks (256 x 256, 256 x 224 or 128 x 448); a stage holds the
+// tile's weight slots (two packed tiles per row block, the B operand's
+// halves; slots past the tile's row blocks lie outside the weight resource,
+// so their loads read nothing) and its x fragment halves.  Two stages: at the
+// start of chunk c the loads of chunk c + 1 are issued into the stage of
+// chunk c - 1 (released at the last barrier), the chunk's operands are read
+// from its stage and multiplied, and each wavefront then waits for its loads
+// and meets the others at a bare barrier.  K is a whole number of chunks.
+template <int RBW, int WRM>
+struct W8L {
+  static constexpr int WN = 8 / WRM;              // wavefront columns
+  static constexpr int XR = 4 * WRM;              // x row blocks per tile
+  static constexpr int XH = 2 * XR;               // x fragment halves per chunk
+  static constexpr int NWS = 2 * WN * RBW;        // weight slots in use
+  static constexpr int LPW = (NWS + XH + 7) / 8;  // loads per wavefront and chunk
+  static constexpr int DX = XH / 8;               // of which x
+  static constexpr int DW = LPW - DX;             // of which weights
+  static constexpr int WS = 8 * DW;               // weight slots per stage
+  static constexpr int BUF = (WS + XH) * 64;      // uint4 per stage
+  static_assert(XH % 8 == 0 && WS >= NWS && 2 * BUF * 16 <= 160 * 1024, "stage layout");
+};
+
+template <int RBW, int WRM>
+struct W8LState {
+  using T = W8L<RBW, WRM>;
+  w8_f32x4_t acc[4][RBW];
+  __amdgpu_buffer_rsrc_t wres, xres;
+  uint32_t wvo[T::DW], xvo[T::DX];
+  int64_t c0;
+  int lane, wave, wm, wn;
+};
+
+__device__ __forceinline__ void w8l_dma(__amdgpu_buffer_rsrc_t r, uint4* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
+
+// All loads of chunk c of the split into buf: this wavefront's weight slots,
+// then its x halves; the chunk's part of every address is a scalar offset.
+template <int RBW, int WRM>
+__device__ __forceinline__ void w8l_load_chunk(const W8LState<RBW, WRM>& st, int c, uint4* buf) {
+  using T = W8L<RBW, WRM>;
+  const uint32_t ch = uint32_t(st.c0) + uint32_t(c);
+#pragma unroll
+  for (int u = 0; u < T::DW; ++u) w8l_dma(st.wres, buf + (T::DW * st.wave + u) * 64, st.wvo[u], ch * 2 * kTileBytes);
+#pragma unroll
+  for (int u = 0; u < T::DX; ++u) w8l_dma(st.xres, buf + (T::WS + T::DX * st.wave + u) * 64, st.xvo[u], ch * 128);
+}
+
+template <int N>
+__device__ __forceinline__ void w8l_wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));  // vmcnt(N) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Chunk c = (loop body start) + H, in stage H: request chunk c + 1 (if the
+// split has one) into the other stage, multiply chunk c, wait for chunk
+// c + 1 and meet the others.
+template <int H, int RBW, int WRM>
+__device__ __forceinline__ void w8l_chunk(W8LState<RBW, WRM>& st, uint4* const* sb, int c, int nch) {
+  using T = W8L<RBW, WRM>;
+  if (c + 1 < nch) w8l_load_chunk(st, c + 1, sb[1 - H]);
+  const uint4* buf = sb[H];
+  uint4 a[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) a[i][h] = buf[(T::WS + 2 * (4 * st.wm + i) + h) * 64 + st.lane];
+#pragma unroll
+  for (int b = 0; b < RBW; ++b) {
+    const int rb = RBW * st.wn + b;
+    const uint4 b0 = buf[(2 * rb) * 64 + st.lane], b1 = buf[(2 * rb + 1) * 64 + st.lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.acc[i][b] = w8_mfma(a[i][0], a[i][1], b0, b1, st.acc[i][b]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  w8l_wait_barrier<0>();
+}
+
+template <int RBW, int WRM>
+__global__ __launch_bounds__(512) void w8_lds_kernel(W8Args a) {
+  using T = W8L<RBW, WRM>;
+  __shared__ uint4 s0[T::BUF], s1[T::BUF];
+  uint4* const sb[2] = {s0, s1};
+  // XCD-aware order: the workgroups of one XCD sweep the row blocks of x of
+  // one column block back to back
+  const int Lb = blockIdx.x, xcd = Lb & 7, wi = Lb >> 3;
+  const int nbn = (wi / a.MB) * 8 + xcd, mb = wi % a.MB;
+  if (nbn >= a.NBN) return;  // whole workgroup, before any barrier
+
+  W8LState<RBW, WRM> st;
+  st.lane = threadIdx.x & 63;
+  st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  st.wm = st.wave % WRM;
+  st.wn = st.wave / WRM;
+  const int split = blockIdx.y;
+  const int c0 = split * a.cps;
+  const int nch = a.nchunks - c0 < a.cps ? a.nchunks - c0 : a.cps;  // >= 1: the planner sizes S so
+  st.c0 = c0;
+  const int64_t nb0 = int64_t(nbn) * (T::WN * RBW), m0 = int64_t(mb) * (64 * WRM);
+  const int64_t nbl = a.NB - nb0 < T::WN * RBW ? a.NB - nb0 : T::WN * RBW;
+  st.wres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(a.w + nb0 * a.KT * (kTileBytes / 16)), 0,
+                                              uint32_t(nbl * a.KT * kTileBytes), 0x00020000);
+  st.xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.xc), 0, uint32_t(a.M * a.K), 0x00020000);
+  {
+    const int g = st.lane >> 4, j = st.lane & 15;
+#pragma unroll
+    for (int u = 0; u < T::DW; ++u) {
+      // slot q: tile q % 2 of the chunk of the tile's weight row block q / 2
+      const int q = T::DW * st.wave + u;
+      st.wvo[u] = uint32_t((q / 2) * a.KT * kTileBytes + (q % 2) * kTileBytes) + st.lane * 16;
+    }
+#pragma unroll
+    for (int u = 0; u < T::DX; ++u) {
+      // half f = (x row block i, h): lane (g, j) holds the codes k = 16 g ..
+      // 16 g + 15 (h = 0) or 64 + 16 g .. (h = 1) of the chunk of row 16 i + j
+      const int f = T::DX * st.wave + u, i = f / 2, h = f % 2;
+      const int64_t row = m0 + 16 * i + j;
+      st.xvo[u] = row < a.M ? uint32_t(row * a.K + 16 * g + 64 * h) : 0x80000000u;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int b = 0; b < RBW; ++b) st.acc[i][b] = w8_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the stages start as zeros (lanes out of range write nothing)
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    for (int i = threadIdx.x; i < T::BUF; i += 512) sb[h][i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+
+  w8l_load_chunk(st, 0, sb[0]);
+  w8l_wait_barrier<0>();
+  int c = 0;
+  for (; c + 2 <= nch; c += 2) {
+    w8l_chunk<0>(st, sb, c, nch);
+    w8l_chunk<1>(st, sb, c + 1, nch);
+  }
+  if (c < nch) w8l_chunk<0>(st, sb, c, nch);
+
+  // lane (g, n) holds rows 4 g + r of each x row block, column n of each row block
+  const float sa = *a.xscale;
+  const int g = st.lane >> 4, n = st.lane & 15;
+#pragma unroll
+  for (int b = 0; b < RBW; ++b) {
+    const int64_t nb = nb0 + RBW * st.wn + b;
+    const int64_t col = nb * kTileRows + n;
+    if (nb >= a.NB || col >= a.N) continue;
+    const float cs = a.S == 1 ? a.scales[col] : 1.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + (4 * st.wm + i) * 16 + 4 * g + r;
+        if (row >= a.M) continue;
+        const float v = st.acc[i][b][r] * sa;
+        if (a.S > 1)
+          a.part[(int64_t(split) * a.M + row) * a.N + col] = v;
+        else
+          a.y[row * a.N + col] = uint16_t(f32_to_bf16_rne(v * cs));
+      }
+  }
+}
+
 template <int MF, int WR>
 static void launch_w8_tile(const W8Args& a, const W8Plan& p, hipStream_t st) {
   const unsigned grid = unsigned(ceil_div(p.NBN, 8) * 8 * p.MB);
@@ -400,7 +573,18 @@ hipError_t launch_w8a8(const W8Plan& p, const void* xc, const float* xscale, int
   a.nchunks = int(p.nchunks);
   a.cps = int(p.cps);
   a.S = p.S;
-  if (p.wr == 1 && p.mf == 8)
+  if (p.lds) {
+    if (K != p.nchunks * 128 || !((p.rbw == 8 && p.lwr == 4) || (p.rbw == 7 && (p.lwr == 4 || p.lwr == 2))) ||
+        p.NBN != ceil_div(p.NB, int64_t(8 / p.lwr * p.rbw)) || p.MB != ceil_div(M, int64_t(64 * p.lwr)))
+      return hipErrorInvalidValue;
+    const dim3 grid(unsigned(ceil_div(p.NBN, int64_t(8)) * 8 * p.MB), unsigned(p.S));
+    if (p.lwr == 2)
+      hipLaunchKernelGGL((w8_lds_kernel<7, 2>), grid, dim3(512), 0, st, a);
+    else if (p.rbw == 7)
+      hipLaunchKernelGGL((w8_lds_kernel<7, 4>), grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((w8_lds_kernel<8, 4>), grid, dim3(512), 0, st, a);
+  } else if (p.wr == 1 && p.mf == 8)
     launch_w8_tile<8, 1>(a, p, st);
   else if (p.wr == 1 && p.mf == 4)
     launch_w8_tile<4, 1>(a, p, st);
