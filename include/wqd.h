@@ -151,13 +151,16 @@ int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* wa
 /*
  * Host-only: for a shape that wqd_qgemm serves with a tiled matrix-core kernel
  * (WQD_PATH_GEMM or WQD_PATH_GEMM_LDS), the tile of y each workgroup computes
- * (*rows x *cols: 64, 128 or 256 rows; 256 columns, or 224 on the FP8
- * LDS-staged kernel where those fill the compute units' rounds better) and
- * the number of K splits (*splits; 1 when K is not split).  Any output pointer
- * may be NULL.  Errors: those of wqd_kernel_path, and WQD_E_UNSUPPORTED for a
- * shape served by another kernel family.
+ * (*rows x *cols: 64, 128 or 256 rows; 256 columns, or on the LDS-staged
+ * kernel 224 or (FP8) 448 where those fill the compute units' rounds better),
+ * the number of K splits (*splits; 1 when K is not split), and a tail split
+ * (*tail_cols: the last columns of y, computed as *tail_splits K splits after
+ * the others so that they fill the launch's last round; 0 and 0 when there is
+ * none).  Any output pointer may be NULL.  Errors: those of wqd_kernel_path,
+ * and WQD_E_UNSUPPORTED for a shape served by another kernel family.
  */
-int wqd_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K, int* rows, int* cols, int* splits);
+int wqd_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K, int* rows, int* cols, int* splits, int* tail_cols,
+                  int* tail_splits);
 
 /*
  * Host-only: the tile of y each workgroup of wqd_qgemm_w8a8 computes for this

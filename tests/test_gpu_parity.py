@@ -304,6 +304,32 @@ def test_qgemm_tiled_256_rows_padded(fmt, N, K, M):
     compare_y(bf16_bits(y), oracle.qgemm_exact(x, qw), f"{fmt} M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("N,K,M,R,TC,TS", [(28680, 2048, 300, 64, 4104, 2), (36872, 8192, 700, 128, 4104, 3),
+                                          (24584, 2048, 1024, 128, 8, 4), (28672, 8192, 777, 128, 2048, 4),
+                                          (10240, 8192, 1024, 64, 2048, 2)])
+def test_qgemm_tiled_tail_split(N, K, M, R, TC, TS):
+    """W4A16 on the tiled kernel with a tail split: the last TC columns of y
+    run as TS K splits after the other column blocks (filling the launch's
+    last round) and a second launch sums their partials.  Ragged N (the tail
+    ending inside a 16-row block, or a tail of 8 columns), ragged M, 64- and
+    128-row tiles, 2 to 4 splits; the oracle checks sampled columns on both
+    sides of the tail's edge and the last ones, over every row."""
+    assert wqd.kernel_path("w4a16", M, N, K)[0] == "gemm"
+    assert wqd.gemm_tile("w4a16", M, N, K, tail=True) == (R, 256, 1, TC, TS)
+    W = I.w_host(6500 + N + K, N, K)
+    rng = np.random.default_rng(N + K + M)
+    edge = N - TC
+    fixed = [0, 15, 255, edge - 9, edge - 1, edge, edge + 7, edge + 8, N - 17, N - 9, N - 1]
+    cols = np.unique(np.concatenate([rng.choice(N, 48, replace=False), [c for c in fixed if 0 <= c < N]]))
+    qw = oracle.quantize("w4a16", W[cols])
+    pw = wqd.pack_weights("w4a16", to_dev(W))
+    print(f"qgemm tail M={M} N={N} K={K} tail {TC} x {TS}", flush=True)
+    x = I.x_bf16_bits(47 * M + K, M, K)
+    y = wqd.qgemm(x_dev(x), pw)
+    torch.cuda.synchronize()
+    compare_y(bf16_bits(y)[:, cols], oracle.qgemm_exact(x, qw), f"w4a16 tail M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("fmt,N,K,M,S,R,C", [
     ("bf16", 8208, 8224, 513, 2, 256, 224), ("bf16", 16392, 2048, 513, 1, 256, 224),
     ("bf16", 28672, 1056, 300, 1, 256, 224), ("bf16", 12296, 4096, 777, 1, 256, 224),

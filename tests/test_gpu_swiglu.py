@@ -67,7 +67,7 @@ def test_every_kernel_family(fmt, M, F, K):
     run(fmt, M, F, K, 100 + M + F % 97 + K % 89)
 
 
-@pytest.mark.parametrize("fmt,Ms", [("w4a16", [1, 4, 8, 16, 32, 128, 1024]), ("fp8", [1, 8, 32, 512, 1024]),
+@pytest.mark.parametrize("fmt,Ms", [("w4a16", [1, 4, 8, 16, 32, 128, 512, 1024]), ("fp8", [1, 8, 32, 512, 1024]),
                                     ("bf16", [1, 4, 192, 512])])
 def test_70b_gate_up(fmt, Ms):
     F, K = 28672, 8192

@@ -73,8 +73,7 @@ def lib() -> ctypes.CDLL:
             "wqd_packed_sizes": (i32, [i32, i64, i64, psz, psz, psz]),
             "wqd_workspace_bytes": (i32, [i32, i64, i64, i64, psz]),
             "wqd_kernel_path": (i32, [i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
-            "wqd_gemm_tile": (i32, [i32, i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
-                                    ctypes.POINTER(i32)]),
+            "wqd_gemm_tile": (i32, [i32, i64, i64, i64] + [ctypes.POINTER(i32)] * 5),
             "wqd_w8a8_tile": (i32, [i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "wqd_pack_weights": (i32, [i32, vp, i64, i64, vp, vp, vp, vp]),
             "wqd_qgemm": (i32, [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]),
@@ -179,14 +178,15 @@ def kernel_path(fmt, M: int, N: int, K: int):
     return KERNEL_PATHS[p.value], w.value
 
 
-def gemm_tile(fmt, M: int, N: int, K: int):
+def gemm_tile(fmt, M: int, N: int, K: int, tail: bool = False):
     """(rows, columns, K splits) of the tile of y each workgroup computes, for
     shapes on a tiled matrix-core kernel (WqdError with WQD_E_UNSUPPORTED for
-    the others)."""
-    r, c, s = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(lib().wqd_gemm_tile(_fmt(fmt), M, N, K, ctypes.byref(r), ctypes.byref(c), ctypes.byref(s)),
-           "wqd_gemm_tile")
-    return r.value, c.value, s.value
+    the others); with tail=True also (tail columns, tail splits), (0, 0) when
+    there is no tail split."""
+    r, c, s, tc, ts = (ctypes.c_int() for _ in range(5))
+    _check(lib().wqd_gemm_tile(_fmt(fmt), M, N, K, ctypes.byref(r), ctypes.byref(c), ctypes.byref(s),
+                               ctypes.byref(tc), ctypes.byref(ts)), "wqd_gemm_tile")
+    return (r.value, c.value, s.value) + ((tc.value, ts.value) if tail else ())
 
 
 def w8a8_tile(M: int, N: int, K: int):

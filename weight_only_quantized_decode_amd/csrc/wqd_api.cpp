@@ -131,7 +131,8 @@ int wqd_kernel_path(int fmt, int64_t M, int64_t N, int64_t K, int* path, int* wa
   return WQD_OK;
 }
 
-int wqd_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K, int* rows, int* cols, int* splits) {
+int wqd_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K, int* rows, int* cols, int* splits, int* tail_cols,
+                  int* tail_splits) {
   wqd::Choice c;
   int st = wqd::choose_path(fmt, M, N, K, &c);
   if (st != wqd::kOK) return st;
@@ -140,6 +141,8 @@ int wqd_gemm_tile(int fmt, int64_t M, int64_t N, int64_t K, int* rows, int* cols
   if (rows) *rows = p.wm == 3 ? 64 * p.lwr : p.wm == 2 ? (fmt == wqd::kFmtW4 ? 128 : 256) : 64;
   if (cols) *cols = p.wm == 3 ? 16 * (8 / p.lwr) * p.rbw : 256;
   if (splits) *splits = p.S;
+  if (tail_cols) *tail_cols = p.S2 > 0 ? int(N - p.nbn1 * 256) : 0;
+  if (tail_splits) *tail_splits = p.S2;
   return WQD_OK;
 }
 

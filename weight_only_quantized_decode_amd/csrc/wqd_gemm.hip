@@ -76,6 +76,11 @@ struct GmArgs {
   int cps;      // chunks per split
   int S;
   int swiglu;   // packed gate/up pairs: store silu(gate) * up (store_out)
+  // tail split (S2 > 0, S == 1): the column blocks from nbn1 run as S2 K
+  // splits of cps2 chunks after the unsplit ones, their float32 partials to
+  // tpart [S2][M][N - 256 nbn1]
+  int nbn1, S2, cps2;
+  float* tpart;
 };
 
 template <int FMT>
@@ -424,9 +429,14 @@ __global__ __launch_bounds__((64 * GmT<FMT, WM>::WR * GmF<FMT>::WN)) void gemm_k
   uint4* const s_x[4] = {s_x0, s_x1, s_x2, s_x3};
 
   // XCD-aware order: the workgroups of one XCD sweep the row blocks of x of
-  // one column block back to back
-  const int Lb = blockIdx.x, xcd = Lb & 7, wi = Lb >> 3;
-  const int nbn = (wi / a.MB) * 8 + xcd, mb = wi % a.MB;
+  // one column block back to back.  With a tail split the workgroups past
+  // the unsplit column blocks' take the tail's (column block, row block,
+  // split) in the same order.
+  const int Lb = blockIdx.x, g1 = a.nbn1 * a.MB;
+  const bool tail = a.S2 > 0 && Lb >= g1;
+  const int Lt = tail ? Lb - g1 : Lb, xcd = Lt & 7, wi = Lt >> 3;
+  const int per = tail ? a.MB * a.S2 : a.MB;  // workgroups per column block
+  const int nbn = (tail ? a.nbn1 : 0) + (wi / per) * 8 + xcd, mb = (wi % per) % a.MB;
   if (nbn >= a.NBN) return;  // whole workgroup, before any barrier
 
   GmState<FMT, WM> st;
@@ -434,9 +444,10 @@ __global__ __launch_bounds__((64 * GmT<FMT, WM>::WR * GmF<FMT>::WN)) void gemm_k
   st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   st.wm = st.wave / F::WN;
   const int wn = st.wave % F::WN;
-  const int split = blockIdx.y;
-  const int c0 = split * a.cps;
-  const int nch = a.nchunks - c0 < a.cps ? a.nchunks - c0 : a.cps;  // >= 1: the planner sizes S so
+  const int split = tail ? (wi % per) / a.MB : int(blockIdx.y);
+  const int cps = tail ? a.cps2 : a.cps;
+  const int c0 = split * cps;
+  const int nch = a.nchunks - c0 < cps ? a.nchunks - c0 : cps;  // >= 1: the planner sizes the splits so
   st.kt0 = int64_t(c0) * F::TPC;
   st.m0 = int64_t(mb) * 16 * F::MF * F::WR;
   const int64_t tiles = a.KT - st.kt0 < int64_t(nch) * F::TPC ? a.KT - st.kt0 : int64_t(nch) * F::TPC;
@@ -515,14 +526,17 @@ __global__ __launch_bounds__((64 * GmT<FMT, WM>::WR * GmF<FMT>::WN)) void gemm_k
   for (int b = 0; b < F::RB; ++b) {
     const int64_t col = (st.nb0 + b) * kTileRows + n;
     if (st.nb0 + b >= a.NB || col >= a.N) continue;
-    const float cs = FMT == kFmtFP8 && a.S == 1 ? reinterpret_cast<const float*>(a.scales)[col] : 1.f;
+    const float cs = FMT == kFmtFP8 && a.S == 1 && !tail ? reinterpret_cast<const float*>(a.scales)[col] : 1.f;
+    const int64_t nt = a.N - int64_t(a.nbn1) * 256, ct = col - int64_t(a.nbn1) * 256;  // tail: width, column
 #pragma unroll
     for (int i = 0; i < F::MF; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = st.m0 + (st.wm * F::MF + i) * 16 + 4 * kb + r;
         if (row >= a.M) continue;  // the same for lanes n and n ^ 8
-        if (a.S > 1)
+        if (tail)
+          a.tpart[(int64_t(split) * a.M + row) * nt + ct] = st.acc[i][b][r];
+        else if (a.S > 1)
           a.part[(int64_t(split) * a.M + row) * a.N + col] = st.acc[i][b][r];
         else
           store_out<8>(a.y, a.N, a.swiglu, row, col, st.acc[i][b][r] * cs, true);  // lane ^ 8: column ^ 8
@@ -554,10 +568,36 @@ __global__ __launch_bounds__(256) void gm_xsum_kernel(const uint16_t* __restrict
   xs[i] = s;
 }
 
+// The tail split's sum: y[m][256 nbn1 + c] for the tail's nt columns, in
+// split order (FP8: times the row scale), one output per thread; SwiGLU pairs
+// columns c and c ^ 8 of 16-aligned groups (nt % 16 == 0 then), 8 lanes apart.
+template <int FMT>
+__global__ __launch_bounds__(256) void gm_tail_reduce_kernel(const float* __restrict__ tpart, int S2, int64_t M,
+                                                             int64_t N, int64_t col0, const float* __restrict__ colscale,
+                                                             uint16_t* __restrict__ y, int swiglu) {
+  const int64_t nt = N - col0;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const bool live = i < M * nt;  // SwiGLU: 16-aligned groups of threads are all live or all not
+  if (!live && !swiglu) return;
+  const int64_t row = live ? i / nt : 0, c = live ? i % nt : 0;
+  float v = 0.f;
+  if (live) {
+    for (int s = 0; s < S2; ++s) v += tpart[(int64_t(s) * M + row) * nt + c];
+    if (FMT == kFmtFP8) v *= colscale[col0 + c];
+  }
+  if (swiglu) {
+    if (i - (i & 15) >= M * nt) return;
+    store_out<8>(y, N, true, row, col0 + c, v, true);  // lane ^ 8: column ^ 8
+    return;
+  }
+  y[row * N + col0 + c] = uint16_t(f32_to_bf16_rne(v));
+}
+
 template <int FMT>
 static hipError_t launch_gm_fmt(const GmArgs& a, const GmPlan& p, hipStream_t st) {
   constexpr int WN = GmF<FMT>::WN;
-  const unsigned grid = unsigned(ceil_div(p.NBN, 8) * 8 * p.MB);
+  const unsigned grid = unsigned(p.S2 > 0 ? p.nbn1 * p.MB + ceil_div(p.NBN - p.nbn1, int64_t(8)) * 8 * p.MB * p.S2
+                                          : ceil_div(p.NBN, 8) * 8 * p.MB);
   if (p.wm == 2)
     hipLaunchKernelGGL((gemm_kernel<FMT, 2>), dim3(grid, unsigned(p.S)), dim3(64 * GmT<FMT, 2>::WR * WN), 0, st, a);
   else if (p.wm == 1)
@@ -588,9 +628,15 @@ hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64
   a.nchunks = int(p.nchunks);
   a.cps = int(p.cps);
   a.S = p.S;
-  // workspace: [W4A16 x sums][split partials]
+  a.nbn1 = int(p.nbn1);
+  a.S2 = p.S2;
+  a.cps2 = int(p.cps2);
+  // workspace: [W4A16 x sums][split partials, or the tail split's]
   a.xsum = reinterpret_cast<const float*>(ws);
   a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.xs_bytes);
+  a.tpart = a.part;
+  if (p.S2 > 0 && (p.S != 1 || p.nbn1 % 8 != 0 || p.nbn1 <= 0 || p.nbn1 >= p.NBN || p.S2 > 8))
+    return hipErrorInvalidValue;
   hipError_t e;
   if (p.wm == 3) {
     e = launch_gemm_lds(fmt, p, x, M, N, K, wp, scales, y, a.part, swiglu, st);
@@ -606,7 +652,21 @@ hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64
     e = hipGetLastError();
     if (e == hipSuccess) e = launch_gm_fmt<kFmtW4>(a, p, st);
   }
-  if (e != hipSuccess || p.S == 1) return e;
+  if (e != hipSuccess) return e;
+  if (p.S2 > 0) {
+    const int64_t col0 = p.nbn1 * 256, n = M * (N - col0);
+    const dim3 g(unsigned(ceil_div(n, int64_t(256))));
+    const float* cs = reinterpret_cast<const float*>(scales);
+    uint16_t* yo = reinterpret_cast<uint16_t*>(y);
+    if (fmt == kFmtFP8)
+      hipLaunchKernelGGL(gm_tail_reduce_kernel<kFmtFP8>, g, dim3(256), 0, st, a.tpart, p.S2, M, N, col0, cs, yo,
+                         int(swiglu));
+    else
+      hipLaunchKernelGGL(gm_tail_reduce_kernel<kFmtBF16>, g, dim3(256), 0, st, a.tpart, p.S2, M, N, col0, cs, yo,
+                         int(swiglu));
+    return hipGetLastError();
+  }
+  if (p.S == 1) return e;
   return launch_splitk_reduce(fmt, a.part, p.S, M, N, scales, y, swiglu, st);
 }
 

@@ -271,6 +271,35 @@ static int plan_gemm_wm(int fmt, int64_t M, int64_t N, int64_t K, const PackedSi
   p.cps = ceil_div(p.nchunks, S);
   p.S = int(ceil_div(p.nchunks, p.cps));
   p.ws_bytes = p.xs_bytes + (p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0);
+  if (fmt == kFmtW4 && p.S == 1 && p.NBN > 8) {
+    // tail split: the column blocks from nbn1 (a multiple of 8, so that
+    // every XCD keeps whole column blocks) run as S2 K splits after the
+    // others, filling the last round that whole tiles would leave part idle
+    // (the 70B gate at 1024 rows: 896 tiles, 3.5 rounds); their partials
+    // take a small second launch.  Rounds on the busiest XCD (32 compute
+    // units, one workgroup each).
+    const double k = wide ? 2.26 : 1.33;
+    const int64_t per_cu = kComputeUnits / 8;
+    for (int64_t nbn1 = 8; nbn1 < p.NBN; nbn1 += 8) {
+      const int64_t r1 = ceil_div(nbn1 / 8 * p.MB, per_cu);
+      for (int s2 = 2; s2 <= 4; ++s2) {
+        const int64_t cps2 = ceil_div(p.nchunks, int64_t(s2));
+        if (ceil_div(p.nchunks, cps2) != s2 || cps2 < 4) continue;
+        const int64_t r2 = ceil_div(ceil_div(p.NBN - nbn1, int64_t(8)) * p.MB * s2, per_cu);
+        const double nt = double(N - nbn1 * 256);
+        const double t = (double(r1) * double(p.nchunks) + double(r2) * double(cps2)) * k +
+                         double(s2) * double(M) * nt * 8.0 / 4.0e6 + 4.0;
+        if (t < 0.98 * best) {
+          best = t;
+          p.nbn1 = nbn1;
+          p.S2 = s2;
+          p.cps2 = int(cps2);
+        }
+      }
+    }
+    if (p.S2 > 0)
+      p.ws_bytes = p.xs_bytes + size_t(p.S2) * size_t(M) * size_t(N - p.nbn1 * 256) * sizeof(float);
+  }
   *out = p;
   *t_us = best;
   return kOK;

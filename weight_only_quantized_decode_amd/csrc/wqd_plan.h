@@ -127,6 +127,8 @@ constexpr int64_t kGmMinNBN = 16;
 struct GmPlan {
   int64_t NB, KT, NBN, MB, nchunks, cps, Mp;
   int wm, S;
+  int64_t nbn1;  // tail split (S2 > 0, S == 1): column blocks from nbn1 split S2 ways (cps2 chunks each)
+  int S2, cps2;
   int rbw;  // LDS-staged form (wm 3): weight row blocks per wavefront ...
   int lwr;  // ... and wavefront rows of 64 rows: tiles of 64 lwr rows by (8 / lwr) rbw row blocks
   size_t xs_bytes, ws_bytes;
