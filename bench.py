@@ -732,7 +732,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this decode layer is measured on a single MI355X "
-              "(multi-GPU sharding is a design note, not part of this build).", file=sys.stderr)
+              "(sharding the layer across GPUs is not implemented).", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -806,7 +806,7 @@ def main():
         del fp8_packed
         free_cache()
 
-    # the survey's next rows, each from its own replays: W8A8-FP8 at the widest
+    # the adjacent parts of the step, each from its own replays: W8A8-FP8 at the widest
     # verify width, and the stack's decode attention at the batch-32 snapshot
     next_rows = {}
     if is_stack and not args.no_targets and args.workload == "w4a16_70b" and fused:

@@ -79,7 +79,7 @@ enum wqd_status {
     WQD_E_ALIGN = 3,        /* a pointer is not 16-byte aligned */
     WQD_E_WORKSPACE = 4,    /* workspace missing or smaller than wqd_workspace_bytes */
     WQD_E_HIP = 5,          /* a HIP runtime call failed; see wqd_last_hip_error() */
-    WQD_E_UNSUPPORTED = 6,  /* a valid request this build cannot serve */
+    WQD_E_UNSUPPORTED = 6,  /* a valid request the library cannot serve */
     WQD_E_TIMEOUT = 7       /* a chain run abandoned a wait (wqd_chain_status) */
 };
 

@@ -18,7 +18,7 @@ channel, k = input channel):
   scale and a zero point).  The stored format is uint4 codes q in [0, 15], an
   fp16 scale s and a uint4 zero z per (row, group); the weight is (q - z) * s.
 
-Readings where the pages leave a step open (each also listed in the design doc):
+Readings where the pages leave a step open:
 
 * FP8 row scale s_n = max_k |W[n, k]| / 448 in float32 (the page fixes one
   32-bit scale per row and the E4M3 maximum 448; absmax-to-max is the plain
