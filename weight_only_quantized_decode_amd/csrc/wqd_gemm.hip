@@ -569,27 +569,45 @@ __global__ __launch_bounds__(256) void gm_xsum_kernel(const uint16_t* __restrict
 }
 
 // The tail split's sum: y[m][256 nbn1 + c] for the tail's nt columns, in
-// split order (FP8: times the row scale), one output per thread; SwiGLU pairs
-// columns c and c ^ 8 of 16-aligned groups (nt % 16 == 0 then), 8 lanes apart.
+// split order (FP8: times the row scale).  Four consecutive outputs of a row
+// per thread where nt % 4 == 0 (SwiGLU: columns c and c ^ 8 are then two
+// threads apart, nt % 16 == 0), else one.
 template <int FMT>
 __global__ __launch_bounds__(256) void gm_tail_reduce_kernel(const float* __restrict__ tpart, int S2, int64_t M,
                                                              int64_t N, int64_t col0, const float* __restrict__ colscale,
                                                              uint16_t* __restrict__ y, int swiglu) {
-  const int64_t nt = N - col0;
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const bool live = i < M * nt;  // SwiGLU: 16-aligned groups of threads are all live or all not
-  if (!live && !swiglu) return;
-  const int64_t row = live ? i / nt : 0, c = live ? i % nt : 0;
-  float v = 0.f;
-  if (live) {
-    for (int s = 0; s < S2; ++s) v += tpart[(int64_t(s) * M + row) * nt + c];
-    if (FMT == kFmtFP8) v *= colscale[col0 + c];
-  }
-  if (swiglu) {
-    if (i - (i & 15) >= M * nt) return;
-    store_out<8>(y, N, true, row, col0 + c, v, true);  // lane ^ 8: column ^ 8
+  const int64_t nt = N - col0, MN = M * nt;
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if ((nt & 3) == 0) {
+    const int64_t i0 = t * 4;
+    if (i0 >= MN) return;  // SwiGLU: 4-thread groups (16 outputs) are all live or all not
+    float4 a = *reinterpret_cast<const float4*>(tpart + i0);
+    for (int s = 1; s < S2; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(tpart + int64_t(s) * MN + i0);
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    const int64_t row = i0 / nt, c = i0 % nt;
+    float f[4] = {a.x, a.y, a.z, a.w};
+    if (FMT == kFmtFP8)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] *= colscale[col0 + c + e];
+    if (swiglu) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out<2>(y, N, true, row, col0 + c + e, f[e], true);  // thread ^ 2: column ^ 8
+      return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[row * N + col0 + c + e] = uint16_t(f32_to_bf16_rne(f[e]));
     return;
   }
+  if (t >= MN) return;  // (no SwiGLU here: it needs nt % 16 == 0)
+  const int64_t row = t / nt, c = t % nt;
+  float v = 0.f;
+  for (int s = 0; s < S2; ++s) v += tpart[int64_t(s) * MN + t];
+  if (FMT == kFmtFP8) v *= colscale[col0 + c];
   y[row * N + col0 + c] = uint16_t(f32_to_bf16_rne(v));
 }
 
@@ -655,7 +673,7 @@ hipError_t launch_gemm(int fmt, const GmPlan& p, const void* x, int64_t M, int64
   if (e != hipSuccess) return e;
   if (p.S2 > 0) {
     const int64_t col0 = p.nbn1 * 256, n = M * (N - col0);
-    const dim3 g(unsigned(ceil_div(n, int64_t(256))));
+    const dim3 g(unsigned(ceil_div((N - col0) % 4 == 0 ? n / 4 : n, int64_t(256))));
     const float* cs = reinterpret_cast<const float*>(scales);
     uint16_t* yo = reinterpret_cast<uint16_t*>(y);
     if (fmt == kFmtFP8)
