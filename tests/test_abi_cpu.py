@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import weight_only_quantized_decode_amd as wqd
@@ -240,6 +241,40 @@ def test_kernel_path_choice():
     assert L.wqd_kernel_path(2, 1, 64, 128, None, None) == E_ARG
     assert L.wqd_kernel_path(2, 1, 64, 100, ctypes.byref(p), None) == E_SHAPE
     assert L.wqd_kernel_path(2, 1, 64, 128, ctypes.byref(p), None) == 0 and p.value == 0
+
+
+def test_tiled_plans_are_consistent():
+    """Over a grid of formats and shapes on the tiled kernels, the reported
+    tile, K split and tail split agree with the workspace the call asks for:
+    the W4A16 x sums (float32 per 128-k group and row of the padded row
+    blocks), then the split partials (S x M x N float32) or the tail split's
+    (S2 x M x tail columns); a tail split leaves the unsplit part whole
+    multiples of 8 column blocks of 256 and never comes with a K split."""
+    rng = np.random.default_rng(5)
+    shapes = [(int(rng.integers(65, 1100)), int(rng.integers(16, 3600)) * 16, int(rng.integers(8, 224)) * 128)
+              for _ in range(120)]
+    shapes += [(M, N, K) for M in (65, 128, 192, 384, 512, 768, 1024)
+               for N, K in ((8192, 8192), (28672, 8192), (57344, 8192), (8192, 28672), (10240, 8192))]
+    seen_tail = 0
+    for fmt in ("bf16", "fp8", "w4a16"):
+        for M, N, K in shapes:
+            if wqd.kernel_path(fmt, M, N, K)[0] not in ("gemm", "gemm_lds"):
+                continue
+            R, C, S, TC, TS = wqd.gemm_tile(fmt, M, N, K, tail=True)
+            assert R in (64, 128, 256) and C in (224, 256, 448) and 1 <= S <= 8
+            rows = -(-M // R) * R
+            xs = (K // 128) * rows * 4 if fmt == "w4a16" else 0
+            xs = -(-xs // 256) * 256
+            ws = wqd.workspace_bytes(fmt, M, N, K)
+            if TS:
+                seen_tail += 1
+                assert fmt == "w4a16" and S == 1 and 2 <= TS <= 4 and C == 256
+                assert 0 < TC < N and (N - TC) % (8 * 256) == 0
+                assert ws == xs + TS * M * TC * 4, (fmt, M, N, K)
+            else:
+                assert TC == 0
+                assert ws == xs + (S * M * N * 4 if S > 1 else 0), (fmt, M, N, K)
+    assert seen_tail >= 3
 
 
 def test_qgemm_rejects_bad_arguments_before_enqueue():
