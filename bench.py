@@ -21,6 +21,11 @@ The same run also reports, each from its own graph replays:
   * "chain": the fused stack at M <= 2 as one persistent launch
     (wqd_chain_run: every matrix of the step, each waiting for the output it
     reads);
+  * "config_rows": the remaining measured configurations: the W4A16 stack
+    at M = 16 and 32 and the FP8 stack at M = 32 (with matrix-core
+    utilisation), the 7B BF16 stack at M = 1, the 4096 x 4096 W4A16 GEMV
+    (cold), and the gate matrix at 1024 verify rows in BF16, FP8 and W4A16
+    (the product's TFLOP/s against the 2.5 PFLOP/s bf16 peak);
   * "next_rows": W8A8-FP8 on the gate matrix at 1024 rows, and the stack's
     decode attention at batch 32 over 2,048 positions, over a bf16 and an FP8
     cache;
@@ -54,6 +59,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix peak
 MAT_INDEX = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "w": 0}
 TARGET_ROWS = (("w4a16", 4), ("w4a16", 8), ("fp8", 1), ("fp8", 8))
+WIDE_ROWS = (("w4a16", 16), ("w4a16", 32), ("fp8", 32))  # stack rows past the target's M <= 8
 
 
 def parse():
@@ -701,6 +707,48 @@ def roofline_of(wl, res):
     return r
 
 
+def wide_row(wl, packed, args, stream, ceiling):
+    """A stack row past the M <= 8 target: GB/s against the ceilings and the
+    matrix-core utilisation of its 2MNK FLOPs."""
+    r = time_step(wl, packed, args, stream)
+    r["pct_measured_read_ceiling"] = pct(r["GBps"], ceiling[0])
+    r["pct_measured_copy_ceiling"] = pct(r["GBps"], ceiling[1])
+    r["pct_hbm_peak"] = round(100 * r["GBps"] / HBM_PEAK_GBPS, 2)
+    tflops = wl.step_flops() / (r["ms_per_step"] / 1e3) / 1e12
+    r["mfma_util_pct"] = round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2)
+    return r
+
+
+def other_configs(args, stream, ceiling):
+    """The 7B BF16 stack at M = 1, the 4096^2 W4A16 GEMV read cold, and the gate
+    matrix at 1024 verify rows in each weight format (its product alone
+    against the bf16 matrix peak), each from its own replays."""
+    rows = []
+    for name, M in (("bf16_7b", 1), ("gemv4096", 1)):
+        wl = make_workload(name, M, None, True)
+        packed = pack_stack(wl)
+        r = time_step(wl, packed, args, stream)
+        del packed
+        free_cache()
+        r["pct_measured_read_ceiling"] = pct(r["GBps"], ceiling[0])
+        r["weight_copies"] = copies_for(wl)
+        if wl.layers == 1:
+            r["us_per_call"] = round(wl.step_bytes() / (r["GBps"] * 1e9) * 1e6, 2)
+        rows.append(r)
+    for fmt in ("bf16", "fp8", "w4a16"):
+        wl = make_workload(f"verify:{fmt}:gate", 1024, None, True)
+        packed = pack_stack(wl)
+        r = time_step(wl, packed, args, stream, dominant=True)
+        del packed
+        free_cache()
+        rr = roofline_of(wl, r)
+        rows.append({"workload": wl.name, "fmt": fmt, "M": wl.M, "ms_per_call": r["ms_per_step"],
+                     "product_us": rr["avg_launch_us"], "product_TFLOPs": rr["achieved"],
+                     "frac_bf16_peak": rr["frac"], "kernel": kernel_group(wl, wl.mats[0][1], wl.mats[0][2]),
+                     "weight_copies": copies_for(wl)})
+    return rows
+
+
 def attn_main(args, stream, ceiling):
     """--workload attn_70b / attn_fp8kv_70b: the stack's decode attention over
     a bf16 / FP8 cache as the headline."""
@@ -776,10 +824,15 @@ def main():
     chain_rec = None
     if is_stack and fused and wl.M <= 2 and not args.no_alt:
         chain_rec = chain_timing(wl, packed, args, stream)
-    if is_stack and not args.no_targets and args.workload == "w4a16_70b" and fused:
+    config_rows = []
+    default_run = is_stack and not args.no_targets and args.workload == "w4a16_70b" and fused
+    if default_run:
         for fmt, M in TARGET_ROWS:
             if fmt == wl.fmt and M != wl.M:
                 targets.append(time_step(with_m(wl, M), packed, args, stream))
+        for fmt, M in WIDE_ROWS:
+            if fmt == wl.fmt and M != wl.M:
+                config_rows.append(wide_row(with_m(wl, M), packed, args, stream, ceiling))
     del packed
     free_cache()
 
@@ -803,8 +856,12 @@ def main():
         for fmt, M in TARGET_ROWS:
             if fmt == "fp8":
                 targets.append(time_step(with_m(fp8_wl, M), fp8_packed, args, stream))
+        for fmt, M in WIDE_ROWS:
+            if fmt == "fp8":
+                config_rows.append(wide_row(with_m(fp8_wl, M), fp8_packed, args, stream, ceiling))
         del fp8_packed
         free_cache()
+        config_rows.extend(other_configs(args, stream, ceiling))
 
     # the adjacent parts of the step, each from its own replays: W8A8-FP8 at the widest
     # verify width, and the stack's decode attention at the batch-32 snapshot
@@ -874,6 +931,8 @@ def main():
         out["targets"] = targets
     if "shapes" in head:
         out["shapes"] = head["shapes"]
+    if config_rows:
+        out["config_rows"] = config_rows
     if next_rows:
         out["next_rows"] = next_rows
     if wl.M >= 16:
