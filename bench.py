@@ -707,19 +707,22 @@ def roofline_of(wl, res):
     return r
 
 
-def wide_row(wl, packed, args, stream, ceiling):
+def wide_row(wl, packed, args, stream, ceiling, mpeak):
     """A stack row past the M <= 8 target: GB/s against the ceilings and the
-    matrix-core utilisation of its 2MNK FLOPs."""
+    matrix-core utilisation of its 2MNK FLOPs (against the vendor peak and,
+    when measured, the back-to-back multiply ceiling)."""
     r = time_step(wl, packed, args, stream)
     r["pct_measured_read_ceiling"] = pct(r["GBps"], ceiling[0])
     r["pct_measured_copy_ceiling"] = pct(r["GBps"], ceiling[1])
     r["pct_hbm_peak"] = round(100 * r["GBps"] / HBM_PEAK_GBPS, 2)
     tflops = wl.step_flops() / (r["ms_per_step"] / 1e3) / 1e12
     r["mfma_util_pct"] = round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2)
+    if mpeak:
+        r["mfma_util_pct_measured_ceiling"] = round(100 * tflops / mpeak, 2)
     return r
 
 
-def other_configs(args, stream, ceiling):
+def other_configs(args, stream, ceiling, mpeak):
     """The 7B BF16 stack at M = 1, the 4096^2 W4A16 GEMV read cold, and the gate
     matrix at 1024 verify rows in each weight format (its product alone
     against the bf16 matrix peak), each from its own replays."""
@@ -745,6 +748,7 @@ def other_configs(args, stream, ceiling):
         rows.append({"workload": wl.name, "fmt": fmt, "M": wl.M, "ms_per_call": r["ms_per_step"],
                      "product_us": rr["avg_launch_us"], "product_TFLOPs": rr["achieved"],
                      "frac_bf16_peak": rr["frac"], "kernel": kernel_group(wl, wl.mats[0][1], wl.mats[0][2]),
+                     "frac_measured_mfma_ceiling": round(rr["achieved"] / mpeak, 4) if mpeak else None,
                      "weight_copies": copies_for(wl)})
     return rows
 
@@ -826,13 +830,16 @@ def main():
         chain_rec = chain_timing(wl, packed, args, stream)
     config_rows = []
     default_run = is_stack and not args.no_targets and args.workload == "w4a16_70b" and fused
+    mpeak = mfma_ceiling() if default_run and not args.no_ceiling else None
+    if mpeak:
+        log(f"[bench] matrix-core ceiling: {mpeak:.0f} TFLOP/s")
     if default_run:
         for fmt, M in TARGET_ROWS:
             if fmt == wl.fmt and M != wl.M:
                 targets.append(time_step(with_m(wl, M), packed, args, stream))
         for fmt, M in WIDE_ROWS:
             if fmt == wl.fmt and M != wl.M:
-                config_rows.append(wide_row(with_m(wl, M), packed, args, stream, ceiling))
+                config_rows.append(wide_row(with_m(wl, M), packed, args, stream, ceiling, mpeak))
     del packed
     free_cache()
 
@@ -858,10 +865,10 @@ def main():
                 targets.append(time_step(with_m(fp8_wl, M), fp8_packed, args, stream))
         for fmt, M in WIDE_ROWS:
             if fmt == "fp8":
-                config_rows.append(wide_row(with_m(fp8_wl, M), fp8_packed, args, stream, ceiling))
+                config_rows.append(wide_row(with_m(fp8_wl, M), fp8_packed, args, stream, ceiling, mpeak))
         del fp8_packed
         free_cache()
-        config_rows.extend(other_configs(args, stream, ceiling))
+        config_rows.extend(other_configs(args, stream, ceiling, mpeak))
 
     # the adjacent parts of the step, each from its own replays: W8A8-FP8 at the widest
     # verify width, and the stack's decode attention at the batch-32 snapshot
@@ -933,6 +940,8 @@ def main():
         out["shapes"] = head["shapes"]
     if config_rows:
         out["config_rows"] = config_rows
+    if mpeak:
+        out["mfma_ceiling_TFLOPs"] = round(mpeak, 1)
     if next_rows:
         out["next_rows"] = next_rows
     if wl.M >= 16:
