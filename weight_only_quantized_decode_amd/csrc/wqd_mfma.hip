@@ -337,10 +337,62 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// The common case (N a multiple of 8, plain store): eight outputs of one row
+// per thread, every split's 32 bytes requested before the first add (twice
+// the bytes in flight per thread of the four-output form, and one column
+// index per thread).  The sum runs in split order, as above.
+template <int FMT>
+__global__ __launch_bounds__(256) void splitk_reduce8_kernel(const float* __restrict__ part, int S, int64_t MN,
+                                                             int64_t N, const float* __restrict__ colscale,
+                                                             uint16_t* __restrict__ y) {
+  const int64_t i0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i0 >= MN) return;
+  float4 v[kMaxSplits][2];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < S) {
+      v[s][0] = *reinterpret_cast<const float4*>(part + int64_t(s) * MN + i0);
+      v[s][1] = *reinterpret_cast<const float4*>(part + int64_t(s) * MN + i0 + 4);
+    }
+  float4 a = v[0][0], b = v[0][1];
+#pragma unroll
+  for (int s = 1; s < kMaxSplits; ++s)
+    if (s < S) {
+      a.x += v[s][0].x;
+      a.y += v[s][0].y;
+      a.z += v[s][0].z;
+      a.w += v[s][0].w;
+      b.x += v[s][1].x;
+      b.y += v[s][1].y;
+      b.z += v[s][1].z;
+      b.w += v[s][1].w;
+    }
+  float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  if constexpr (FMT == kFmtFP8) {
+    const int64_t n0 = i0 % N;  // the eight outputs share a row: N % 8 == 0
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] *= colscale[n0 + e];
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16_rne(f[2 * e]) | (f32_to_bf16_rne(f[2 * e + 1]) << 16);
+  *reinterpret_cast<uint4*>(y + i0) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 hipError_t launch_splitk_reduce(int fmt, const float* part, int S, int64_t M, int64_t N, const void* scales, void* y,
                                 bool swiglu, hipStream_t st) {
   if (S < 1 || S > kMaxSplits) return hipErrorInvalidValue;
   if (swiglu && N % 16 != 0) return hipErrorInvalidValue;
+  if (!swiglu && N % 8 == 0) {
+    const dim3 grid8(unsigned((M * N / 8 + 255) / 256));
+    const float* cs8 = reinterpret_cast<const float*>(scales);
+    uint16_t* yo8 = reinterpret_cast<uint16_t*>(y);
+    if (fmt == kFmtFP8)
+      hipLaunchKernelGGL(splitk_reduce8_kernel<kFmtFP8>, grid8, dim3(256), 0, st, part, S, M * N, N, cs8, yo8);
+    else
+      hipLaunchKernelGGL(splitk_reduce8_kernel<kFmtBF16>, grid8, dim3(256), 0, st, part, S, M * N, N, cs8, yo8);
+    return hipGetLastError();
+  }
   const int64_t quads = (M * N + 3) / 4;
   const dim3 grid(unsigned((quads + 255) / 256));
   const float* cs = reinterpret_cast<const float*>(scales);
